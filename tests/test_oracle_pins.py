@@ -1,0 +1,408 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix.
+
+Each check is written as a function of the oracle routine it pins, so that the
+mutation tests at the bottom can hand it a plausibly wrong variant (a dropped
+term, a wrong index, a reversed tie rule, the union's rows instead of a query's
+own rows) and show that the pin fails on it.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import dualkv_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ----------------------------------------------------------------------------
+# landmarks: mean key of each chunk
+# ----------------------------------------------------------------------------
+
+def check_landmarks(fn):
+    fx = golden("landmarks_hand.json")
+    lm = fn(np.array(fx["K"], dtype=np.float64), fx["chunk"])
+    np.testing.assert_array_equal(lm, np.array(fx["expected_lm"], dtype=np.float64))
+    rng = np.random.default_rng(1)
+    K = rng.standard_normal((2, 3, 12, 5))
+    # chunk = 1: every key is its own landmark
+    np.testing.assert_array_equal(fn(K, 1), K)
+    # keys constant inside each chunk: the landmark is that constant
+    vals = rng.integers(-9, 9, size=(2, 3, 3, 5)).astype(np.float64)
+    Kc = np.repeat(vals, 4, axis=2)
+    np.testing.assert_array_equal(fn(Kc, 4), vals)
+    # one chunk spanning L: the landmark is the mean over all keys (numpy's mean)
+    np.testing.assert_allclose(fn(K, 12)[:, :, 0], np.mean(K, axis=2), rtol=0, atol=1e-14)
+
+
+def test_landmarks_pins():
+    check_landmarks(O.chunk_landmarks)
+
+
+def test_landmarks_reject_ragged_length():
+    with pytest.raises(ValueError):
+        O.chunk_landmarks(np.zeros((1, 1, 10, 2)), 4)
+
+
+# ----------------------------------------------------------------------------
+# scores
+# ----------------------------------------------------------------------------
+
+def check_scores(fn):
+    fx = golden("scores_hand.json")
+    q = np.array(fx["q"], dtype=np.float64)
+    lm = np.array(fx["lm"], dtype=np.float64)
+    np.testing.assert_allclose(fn(q, lm, fx["scale"], "mean"), np.array(fx["expected_mean"]), atol=1e-15)
+    np.testing.assert_allclose(fn(q, lm, fx["scale"], "max"), np.array(fx["expected_max"]), atol=1e-15)
+    rng = np.random.default_rng(2)
+    # G = 1: mean and max of one head agree
+    q1 = rng.standard_normal((2, 2, 3, 7))
+    lm1 = rng.standard_normal((2, 3, 11, 7))
+    np.testing.assert_array_equal(fn(q1, lm1, 0.3, "mean"), fn(q1, lm1, 0.3, "max"))
+    # group of 4 heads, rectangular shapes: compare with a brute-force triple loop
+    q4 = rng.standard_normal((2, 2, 8, 6))
+    lm4 = rng.standard_normal((2, 2, 9, 6))
+    s = fn(q4, lm4, 0.25, "mean")
+    sm = fn(q4, lm4, 0.25, "max")
+    for b, g, t, c in itertools.product(range(2), range(2), range(2), range(9)):
+        dots = [0.25 * sum(q4[b, t, h, i] * lm4[b, g, c, i] for i in range(6))
+                for h in range(4 * g, 4 * g + 4)]
+        assert abs(s[b, g, t, c] - sum(dots) / 4) < 1e-12
+        assert abs(sm[b, g, t, c] - max(dots)) < 1e-12
+
+
+def test_scores_pins():
+    check_scores(O.chunk_scores)
+
+
+# ----------------------------------------------------------------------------
+# top-k
+# ----------------------------------------------------------------------------
+
+def brute_force_topk(row, k):
+    """Among all k-subsets with the largest score sum, the lexicographically smallest."""
+    best = None
+    for sub in itertools.combinations(range(len(row)), k):
+        key = (-sum(row[i] for i in sub), sub)
+        if best is None or key < best:
+            best = key
+    return list(best[1])
+
+
+def check_topk(fn):
+    fx = golden("topk_ties_hand.json")
+    for k, want in fx["cases"]:
+        assert list(fn(np.array(fx["scores"], dtype=np.float64), k)) == want
+    rng = np.random.default_rng(3)
+    for trial in range(60):
+        C = int(rng.integers(1, 11))
+        k = int(rng.integers(1, C + 1))
+        if trial % 2:
+            row = rng.integers(0, 4, size=C).astype(np.float64)   # many ties
+        else:
+            row = rng.standard_normal(C)
+        assert list(fn(row, k)) == brute_force_topk(row, k), (row, k)
+    # distinct scores: the same set as torch.topk
+    s = rng.standard_normal((4, 3, 200))
+    got = fn(s, 17)
+    ref = torch.topk(torch.from_numpy(s), 17, dim=-1).indices.sort(dim=-1).values.numpy()
+    np.testing.assert_array_equal(got, ref)
+    # k = C keeps everything
+    np.testing.assert_array_equal(fn(s[0, 0], 200), np.arange(200))
+
+
+def test_topk_pins():
+    check_topk(O.topk_chunks)
+
+
+# ----------------------------------------------------------------------------
+# union
+# ----------------------------------------------------------------------------
+
+def check_union(fn):
+    fx = golden("union_hand.json")
+    u, m, c, o = fn(np.array(fx["idx"]))
+    np.testing.assert_array_equal(u, fx["expected_union"])
+    np.testing.assert_array_equal(m, fx["expected_member"])
+    np.testing.assert_array_equal(c, fx["expected_count"])
+    np.testing.assert_array_equal(o, fx["expected_overlap"])
+    rng = np.random.default_rng(4)
+    C, k = 40, 9
+    idx = np.stack([np.stack([np.sort(rng.choice(C, k, replace=False)) for _ in range(2)])
+                    for _ in range(6)]).reshape(2, 3, 2, k)
+    u, m, c, o = fn(idx)
+    for b, g in itertools.product(range(2), range(3)):
+        n = c[b, g]
+        ids = u[b, g, :n]
+        assert n == 2 * k - o[b, g]
+        assert k <= n <= min(2 * k, C)
+        assert np.all(np.diff(ids) > 0)
+        assert np.all(u[b, g, n:] == -1) and np.all(m[b, g, n:] == 0)
+        for t in range(2):
+            assert set(ids[(m[b, g, :n] >> t) & 1 == 1].tolist()) == set(idx[b, g, t].tolist())
+        assert np.all(m[b, g, :n] > 0)
+    # identical selections: union = each set, full overlap, accuracy exactly 1
+    same = np.repeat(idx[:, :, :1], 2, axis=2)
+    u, m, c, o = fn(same)
+    assert np.all(c == k) and np.all(o == k) and np.all(m[:, :, :k] == 3)
+    assert O.prediction_accuracy(o, k) == 1.0
+
+
+def test_union_pins():
+    check_union(O.union_select)
+
+
+def test_union_single_query():
+    idx = np.array([[[[2, 5, 6]]]])
+    u, m, c, o = O.union_select(idx)
+    assert u.tolist() == [[[2, 5, 6]]] and m.tolist() == [[[1, 1, 1]]]
+    assert c.tolist() == [[3]] and o.tolist() == [[3]]
+
+
+# ----------------------------------------------------------------------------
+# attention over each query's own rows
+# ----------------------------------------------------------------------------
+
+def sdpa_masked(q, K, V, rows_mask, scale):
+    """torch's scaled_dot_product_attention in fp64 on CPU with a boolean row mask."""
+    out = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None, None, None, :], torch.from_numpy(K)[None, None],
+        torch.from_numpy(V)[None, None], attn_mask=torch.from_numpy(rows_mask)[None, None, None, :],
+        scale=scale)
+    return out[0, 0, 0].numpy()
+
+
+def check_attention(fn):
+    fx = golden("attention_hand.json")
+    out, lse = fn(np.array(fx["q"]), np.array(fx["K"]), np.array(fx["V"]), np.array(fx["sel"]),
+                  fx["chunk"], fx["scale"])
+    np.testing.assert_allclose(out, fx["expected_out"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, fx["expected_lse"], rtol=0, atol=1e-12)
+
+    rng = np.random.default_rng(5)
+    B, T, Hq, Hkv, dk, dv, chunk, C = 2, 2, 4, 2, 6, 5, 3, 7
+    L = C * chunk
+    q = rng.standard_normal((B, T, Hq, dk))
+    K = rng.standard_normal((B, Hkv, L, dk))
+    V = rng.standard_normal((B, Hkv, L, dv))
+    G = Hq // Hkv
+    # k = C: sparse attention is dense attention (library routine, fp64)
+    sel_all = np.broadcast_to(np.arange(C), (B, Hkv, T, C))
+    out, lse = fn(q, K, V, sel_all, chunk, 0.4)
+    for b, t, h in itertools.product(range(B), range(T), range(Hq)):
+        ref = sdpa_masked(q[b, t, h], K[b, h // G], V[b, h // G], np.ones(L, dtype=bool), 0.4)
+        np.testing.assert_allclose(out[b, t, h], ref, rtol=0, atol=1e-12)
+        z = 0.4 * K[b, h // G] @ q[b, t, h]
+        assert abs(lse[b, t, h] - math.log(np.sum(np.exp(z)))) < 1e-12
+    # own sets differ per query: masked library attention over exactly those rows
+    sel = np.zeros((B, Hkv, T, 3), dtype=np.int64)
+    for b, g, t in itertools.product(range(B), range(Hkv), range(T)):
+        sel[b, g, t] = np.sort(rng.choice(C, 3, replace=False))
+    out, lse = fn(q, K, V, sel, chunk, 0.4)
+    for b, t, h in itertools.product(range(B), range(T), range(Hq)):
+        mask = np.zeros(L, dtype=bool)
+        for c in sel[b, h // G, t]:
+            mask[c * chunk:(c + 1) * chunk] = True
+        ref = sdpa_masked(q[b, t, h], K[b, h // G], V[b, h // G], mask, 0.4)
+        np.testing.assert_allclose(out[b, t, h], ref, rtol=0, atol=1e-12)
+    # one selected row: the output is that row's value, lse its logit
+    sel1 = np.full((B, Hkv, T, 1), 4)
+    out, lse = fn(q, K, V, sel1, 1, 0.4)
+    for b, t, h in itertools.product(range(B), range(T), range(Hq)):
+        np.testing.assert_array_equal(out[b, t, h], V[b, h // G, 4])
+        assert abs(lse[b, t, h] - 0.4 * K[b, h // G, 4] @ q[b, t, h]) < 1e-14
+    # zero keys: uniform weights over the own rows, lse = log(#rows)
+    out, lse = fn(q, np.zeros_like(K), V, sel, chunk, 0.4)
+    for b, t, h in itertools.product(range(B), range(T), range(Hq)):
+        rows = np.concatenate([np.arange(c * chunk, (c + 1) * chunk) for c in sel[b, h // G, t]])
+        np.testing.assert_allclose(out[b, t, h], V[b, h // G, rows].mean(axis=0), atol=1e-14)
+        assert abs(lse[b, t, h] - math.log(len(rows))) < 1e-14
+
+
+def test_attention_pins():
+    check_attention(O.sparse_attention)
+
+
+# ----------------------------------------------------------------------------
+# hot-cache plan
+# ----------------------------------------------------------------------------
+
+def check_cache_plan(fn):
+    fx = golden("cache_plan_hand.json")
+    p = fn(np.array(fx["resident"]), np.array(fx["union"]), np.array(fx["count"]))
+    for key in ("new_resident", "slot_of_union", "miss_chunk", "miss_slot", "miss_count", "hit_count"):
+        np.testing.assert_array_equal(p[key], fx["expected_" + key], err_msg=key)
+    rng = np.random.default_rng(6)
+    S, C, n = 12, 30, 8
+    res = np.full((2, 2, S), -1)
+    for step in range(6):
+        u = np.full((2, 2, S), -1)
+        cnt = np.zeros((2, 2), dtype=np.int64)
+        for b, g in itertools.product(range(2), range(2)):
+            m = int(rng.integers(1, n + 1))
+            u[b, g, :m] = np.sort(rng.choice(C, m, replace=False))
+            cnt[b, g] = m
+        p = fn(res, u, cnt)
+        for b, g in itertools.product(range(2), range(2)):
+            m = cnt[b, g]
+            ids = u[b, g, :m]
+            new = p["new_resident"][b, g]
+            assert sorted(new[new >= 0].tolist()) == sorted(ids.tolist())
+            assert p["hit_count"][b, g] + p["miss_count"][b, g] == m
+            old = {int(c): s for s, c in enumerate(res[b, g]) if c >= 0}
+            for i, c in enumerate(ids):
+                s = p["slot_of_union"][b, g, i]
+                assert new[s] == c
+                if c in old:
+                    assert s == old[c]
+            for j in range(p["miss_count"][b, g]):
+                c, s = p["miss_chunk"][b, g, j], p["miss_slot"][b, g, j]
+                assert c not in old and (res[b, g, s] < 0 or res[b, g, s] not in ids)
+        # the same union again: every chunk is a hit
+        p2 = fn(p["new_resident"], u, cnt)
+        assert np.all(p2["miss_count"] == 0) and np.all(p2["hit_count"] == cnt)
+        res = p["new_resident"]
+
+
+def test_cache_plan_pins():
+    check_cache_plan(O.cache_plan)
+
+
+# ----------------------------------------------------------------------------
+# whole step: sizes and composition
+# ----------------------------------------------------------------------------
+
+def test_pool_size_closed_form():
+    from sparse_kv_retrieval_amd.workloads import WORKLOADS
+    # OasisKV summary Eq. (1) for one layer: B * L * 2 * N_kv * d_h * s bytes
+    w = WORKLOADS["b64_l128k"]
+    assert w.pool_bytes() == 64 * 131072 * 2 * 8 * 128 * 2 == 34_359_738_368
+    assert WORKLOADS["llama8b_l32k"].landmark_bytes() == 16 * 8 * 1024 * 128 * 4
+
+
+def test_decode_step_identical_queries_full_accuracy():
+    rng = np.random.default_rng(7)
+    q1 = rng.standard_normal((2, 1, 4, 8))
+    q = np.concatenate([q1, q1], axis=1)
+    K = rng.standard_normal((2, 2, 64, 8))
+    V = rng.standard_normal((2, 2, 64, 8))
+    r = O.decode_step(q, K, V, chunk=4, k=5)
+    assert r["accuracy"] == 1.0
+    np.testing.assert_array_equal(r["out"][:, 0], r["out"][:, 1])
+
+
+# ----------------------------------------------------------------------------
+# the pins bite: each fails on a plausibly wrong oracle
+# ----------------------------------------------------------------------------
+
+def _landmarks_off_by_one(K, chunk):
+    B, H, L, d = K.shape
+    return K.reshape(B, H, L // chunk, chunk, d)[:, :, :, 1:, :].sum(axis=3) / chunk
+
+
+def _landmarks_wrong_divisor(K, chunk):
+    B, H, L, d = K.shape
+    return K.reshape(B, H, L // chunk, chunk, d).sum(axis=3) / max(chunk - 1, 1)
+
+
+def _scores_wrong_group(q, lm, scale, reduce="mean"):
+    # query head h read against KV head h % Hkv instead of h // G
+    B, T, Hq, d = q.shape
+    Hkv = lm.shape[1]
+    perm = np.concatenate([np.arange(g, Hq, Hkv) for g in range(Hkv)])
+    return O.chunk_scores(q[:, :, perm], lm, scale, reduce)
+
+
+def _scores_no_scale(q, lm, scale, reduce="mean"):
+    return O.chunk_scores(q, lm, 1.0, reduce)
+
+
+def _topk_ties_high_id(s, k):
+    s = np.asarray(s, dtype=np.float64)
+    C = s.shape[-1]
+    flat = s.reshape(-1, C)
+    out = np.zeros((flat.shape[0], k), dtype=np.int64)
+    for r in range(flat.shape[0]):
+        order = np.lexsort((-np.arange(C), -flat[r]))
+        out[r] = np.sort(order[:k])
+    return out.reshape(s.shape[:-1] + (k,))
+
+
+def _union_overlap_wrong(idx):
+    u, m, c, o = O.union_select(idx)
+    return u, m, c, c - idx.shape[-1]
+
+
+def _attention_over_union(q, K, V, sel, chunk, scale):
+    # every query reads the union of the two sets instead of its own set
+    B, T, Hq, dk = q.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    out = np.zeros((B, T, Hq, V.shape[3]))
+    lse = np.zeros((B, T, Hq))
+    for b, t, h in itertools.product(range(B), range(T), range(Hq)):
+        ids = sorted(set(sel[b, h // G].reshape(-1).tolist()))
+        rows = np.concatenate([np.arange(c * chunk, (c + 1) * chunk) for c in ids])
+        z = scale * K[b, h // G, rows] @ q[b, t, h]
+        p = np.exp(z - z.max())
+        out[b, t, h] = p @ V[b, h // G, rows] / p.sum()
+        lse[b, t, h] = z.max() + math.log(p.sum())
+    return out, lse
+
+
+def _attention_lse_missing_max(q, K, V, sel, chunk, scale):
+    out, lse = O.sparse_attention(q, K, V, sel, chunk, scale)
+    return out, lse * 0.5
+
+
+def _cache_plan_misses_descending_slots(resident, union_ids, count):
+    # misses fill the free slots from the highest slot down
+    B, H, S = resident.shape
+    new = np.full((B, H, S), -1)
+    sou = np.full(union_ids.shape, -1)
+    mc = np.full(union_ids.shape, -1)
+    ms = np.full(union_ids.shape, -1)
+    mn = np.zeros((B, H), dtype=np.int64)
+    hn = np.zeros((B, H), dtype=np.int64)
+    for b, g in itertools.product(range(B), range(H)):
+        u = [int(c) for c in union_ids[b, g, :int(count[b, g])]]
+        where = {int(c): s for s, c in enumerate(resident[b, g]) if c >= 0}
+        free = [s for s in range(S - 1, -1, -1) if int(resident[b, g, s]) not in set(u)]
+        for i, c in enumerate(u):
+            if c in where:
+                s = where[c]
+                hn[b, g] += 1
+            else:
+                s = free[mn[b, g]]
+                mc[b, g, mn[b, g]] = c
+                ms[b, g, mn[b, g]] = s
+                mn[b, g] += 1
+            sou[b, g, i] = s
+            new[b, g, s] = c
+    return dict(new_resident=new, slot_of_union=sou, miss_chunk=mc, miss_slot=ms,
+                miss_count=mn, hit_count=hn)
+
+
+@pytest.mark.parametrize("check,bad", [
+    (check_landmarks, _landmarks_off_by_one),
+    (check_landmarks, _landmarks_wrong_divisor),
+    (check_scores, _scores_wrong_group),
+    (check_scores, _scores_no_scale),
+    (check_topk, _topk_ties_high_id),
+    (check_union, _union_overlap_wrong),
+    (check_attention, _attention_over_union),
+    (check_attention, _attention_lse_missing_max),
+    (check_cache_plan, _cache_plan_misses_descending_slots),
+])
+def test_pins_reject_planted_mistakes(check, bad):
+    with pytest.raises(AssertionError):
+        check(bad)
