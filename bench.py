@@ -1,0 +1,222 @@
+"""Benchmark: dual-query sparse decode steps/s and selected-KV GB/s on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload b64_l128k]
+
+A step is one pass of the whole hot path over every layer of the workload: per
+layer, chunk scores and top-k of both queries (dk_score_topk), their union
+(dk_union_select) and attention of both queries over their own chunks, read
+once per union chunk straight from the HBM pool (dk_sparse_decode_attn).
+Landmarks are built once before timing (they are fixed for the whole decode).
+Inputs are seeded synthetic tensors resident in HBM before the timed region.
+
+Prints one JSON line.  `roofline` covers the kernel family that takes the most
+time per step; `kernels` lists every call's measured duration and algorithmic
+bytes; `cpu_baseline` times the CPU oracle on a bounded sample of the same
+workload (single thread).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, 8 TB/s
+METRIC = "dual-query sparse decode steps/s + selected-KV GB/s (% HBM peak), B=64 L=128K"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="b64_l128k")
+    ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--layers", type=int, default=None, help="override the layer count")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="CPU oracle sample budget (0 disables the CPU baseline)")
+    ap.add_argument("--no-events", action="store_true",
+                    help="time only whole steps (no per-call events inside the step)")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, qs_host, K, V, budget_s, seed):
+    """Time the fp64 CPU oracle on sampled (request, KV head, layer) units."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import dualkv_oracle as O
+    from sparse_kv_retrieval_amd import synth
+
+    rng = np.random.default_rng(seed)
+    pairs = [(int(rng.integers(w.B)), int(rng.integers(w.Hkv))) for _ in range(4)]
+    per_pair = budget_s / len(pairs)
+    units, spent = 0, 0.0
+    with threadpool_limits(1):
+        for b, g in pairs:
+            Kh = synth.to_numpy_f64(K[b:b + 1, g:g + 1])
+            Vh = synth.to_numpy_f64(V[b:b + 1, g:g + 1])
+            lm = O.chunk_landmarks(Kh, w.chunk)            # built once per prefill: not timed
+            pair_spent, layer = 0.0, 0
+            while pair_spent < per_pair:
+                qh = qs_host[layer % len(qs_host)][b:b + 1, :, g * w.G:(g + 1) * w.G]
+                t0 = time.perf_counter()
+                s = O.chunk_scores(qh, lm, w.scale, "mean")
+                sel = O.topk_chunks(s, w.k)
+                O.union_select(sel)
+                O.sparse_attention(qh, Kh, Vh, sel, w.chunk, w.scale)
+                pair_spent += time.perf_counter() - t0
+                units += 1
+                layer += 1
+            spent += pair_spent
+    per_unit = spent / units
+    per_step = per_unit * w.B * w.Hkv * len(qs_host)
+    return {"value": 1.0 / per_step, "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{units} (request, KV head, layer) units of the {w.name} step "
+                      f"({spent:.1f} s, {per_unit * 1e3:.1f} ms each), scaled to "
+                      f"{w.B * w.Hkv * len(qs_host)} units per step; landmarks precomputed"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the decode step has no "
+              "cross-GPU exchange and this build measures a single MI355X.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from sparse_kv_retrieval_amd import binding as dkb   # fails loudly without libdualkv.so
+    from sparse_kv_retrieval_amd import synth
+    from sparse_kv_retrieval_amd.workloads import WORKLOADS
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w = WORKLOADS[args.workload]
+    if args.layers:
+        w = w.with_(layers=args.layers)
+    dev = "cuda"
+    torch.cuda.set_device(0)
+
+    t0 = time.time()
+    qs = [synth.make_queries(w, args.seed, layer=l, device=dev) for l in range(w.layers)]
+    K, V = synth.make_kv_pool(w, args.seed, device=dev, q0=qs[0])
+    lm = dkb.build_landmarks(K, w.chunk)
+    st = dkb.DecodeStep(w.B, w.T, w.Hq, w.Hkv, w.d, w.C, w.chunk, w.k, w.scale, dev, want_scores=False)
+    torch.cuda.synchronize()
+    print(f"[bench] inputs ready in {time.time() - t0:.1f} s: pool {2 * K.nbytes / 1e9:.2f} GB, "
+          f"landmarks {lm.nbytes / 1e9:.3f} GB", file=sys.stderr, flush=True)
+
+    # Per-layer union sizes (deterministic): the selected-KV bytes of each layer.
+    sel_chunks, overlap = [], []
+    for l in range(w.layers):
+        st.run(qs[l], lm, K, V)
+        sel_chunks.append(int(st.count.sum().item()))
+        overlap.append(st.overlap.double().mean().item())
+    torch.cuda.synchronize()
+    chunk_bytes = w.chunk_kv_bytes()
+    sel_bytes_step = sum(sel_chunks) * chunk_bytes
+    lm_bytes_layer = w.landmark_bytes()
+    accuracy = float(np.mean(overlap)) / w.k
+
+    calls = ("score_topk", "union_select", "sparse_decode_attn")
+    use_events = not args.no_events
+    # one set of events per (step, layer), read only after the timed region
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(w.layers)]
+          for _ in range(args.steps)] if use_events else None
+    call_ms = {c: 0.0 for c in calls}
+
+    def step(record):
+        for l in range(w.layers):
+            q = qs[l]
+            e = ev[record - 1][l] if record else None
+            if record:
+                e[0].record()
+            dkb.score_topk(q, lm, w.k, w.scale, dkb.DK_REDUCE_MEAN, st.topk_idx, None, st.ws_topk)
+            if record:
+                e[1].record()
+            dkb.union_select(st.topk_idx, w.C, st.union_ids, st.member, st.count, st.overlap)
+            if record:
+                e[2].record()
+            dkb.sparse_decode_attn(q, K, V, st.union_ids, st.member, st.count, w.chunk, w.scale,
+                                   out=st.out, lse=st.lse, ws=st.ws_attn)
+            if record:
+                e[3].record()
+
+    for _ in range(args.warmup):
+        step(0)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for s in range(args.steps):
+        step(s + 1 if use_events else 0)
+    end.record()
+    torch.cuda.synchronize()
+    if use_events:
+        for s in range(args.steps):
+            for l in range(w.layers):
+                for i, c in enumerate(calls):
+                    call_ms[c] += ev[s][l][i].elapsed_time(ev[s][l][i + 1])
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    steps_per_s = 1000.0 / ms_per_step
+
+    kernels = {}
+    n_launch = args.steps * w.layers
+    per_call_bytes = {
+        "score_topk": lm_bytes_layer + w.B * w.T * w.Hq * w.d * 4,
+        "union_select": w.B * w.Hkv * w.T * w.k * 4 * 3,
+        "sparse_decode_attn": sel_bytes_step / w.layers,
+    }
+    for c in calls:
+        if not use_events:
+            break
+        avg_ms = call_ms[c] / n_launch
+        gbps = per_call_bytes[c] / (avg_ms * 1e-3) / 1e9
+        kernels[c] = {"avg_us": round(avg_ms * 1e3, 2), "bytes_per_launch": int(per_call_bytes[c]),
+                      "GBps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+    attn_ms_step = call_ms["sparse_decode_attn"] / args.steps if use_events else float("nan")
+    sel_gbps = sel_bytes_step / (attn_ms_step * 1e-3) / 1e9 if use_events else float("nan")
+
+    dominant = max(kernels, key=lambda c: kernels[c]["avg_us"]) if kernels else None
+    roofline = None
+    if dominant:
+        kd = kernels[dominant]
+        roofline = {"bound": "hbm", "kernel": dominant, "achieved": kd["GBps"], "peak": HBM_PEAK_GBPS,
+                    "unit": "GB/s", "frac": round(kd["GBps"] / HBM_PEAK_GBPS, 4), "traffic": None}
+
+    out = {
+        "metric": METRIC,
+        "value": round(steps_per_s, 3),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "L": w.L, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d,
+                   "chunk": w.chunk, "k": w.k, "T": w.T, "layers": w.layers, "seed": args.seed},
+        "selected_kv_GBps": round(sel_gbps, 1),
+        "selected_kv_frac_hbm_peak": round(sel_gbps / HBM_PEAK_GBPS, 4),
+        "selected_kv_bytes_per_step": int(sel_bytes_step),
+        "mean_union_chunks": round(sum(sel_chunks) / (w.layers * w.B * w.Hkv), 2),
+        "prediction_accuracy": round(accuracy, 5),
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    if args.cpu_seconds > 0:
+        qs_host = [q.cpu().numpy().astype(np.float64) for q in qs]
+        out["cpu_baseline"] = cpu_baseline(w, qs_host, K, V, args.cpu_seconds, args.seed)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

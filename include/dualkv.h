@@ -1,0 +1,243 @@
+/*
+ * dualkv.h - C ABI of libdualkv: one decode step of dual-query sparse KV-cache
+ * retrieval attention on MI355X (gfx950).
+ *
+ * The step, per request b, KV head g and query t (t = 0 the real token, t = 1
+ * the speculative look-ahead token), is:
+ *   landmarks  -> dk_build_landmarks     (once per prefilled pool)
+ *   scores     -> dk_score_topk          (chunk scores and the k best chunks)
+ *   union      -> dk_union_select        (one list of distinct chunks, plus an
+ *                                         optional hot-cache transfer plan)
+ *   gather     -> dk_gather_kv           (chunk copies; fused into attention on
+ *                                         the HBM-pool path)
+ *   attention  -> dk_sparse_decode_attn  (each query over its own chunks)
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All pointers are owned by the caller.  The library never allocates or frees
+ *   memory; calls that need scratch space take a workspace pointer whose size
+ *   comes from the matching *_workspace_size function.
+ * - `stream` is a hipStream_t passed as void*; NULL is the null stream.  Every
+ *   call only enqueues work on `stream` and returns, except dk_gather_kv in
+ *   host mode, which reads its host-side lists while it enqueues copies.
+ * - Arguments are checked before anything is enqueued.  A call that returns
+ *   anything other than DK_OK has enqueued nothing and written nothing; the
+ *   reason is in dk_last_error().  HIP failures return DK_ERR_HIP with the HIP
+ *   error string.
+ * - Tensors are dense in their last dimension.  KV pools are described by a
+ *   base pointer and dk_strides {b, h, t}: the element offset of row n of
+ *   (request b, head g) is b*s.b + g*s.h + n*s.t.  Pool and landmark rows must
+ *   start on 16-byte boundaries (base pointer and every stride, in bytes, are
+ *   multiples of 16).
+ * - Chunk ids, slot ids and counts are int32.  Ids that fall outside the range
+ *   a call is told about (pool_blocks, C, slots) are skipped on the device,
+ *   never dereferenced.
+ * - The library keeps no global state besides the thread-local error string;
+ *   calls on different streams may run concurrently.
+ */
+#ifndef DUALKV_H
+#define DUALKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DK_ABI_VERSION 1
+
+typedef enum {
+    DK_OK = 0,
+    DK_ERR_INVALID_ARG = 1,   /* a size, pointer or stride is out of range       */
+    DK_ERR_UNSUPPORTED = 2,   /* valid, but a shape or alignment v1 does not run */
+    DK_ERR_HIP = 3            /* the HIP runtime reported an error               */
+} dk_status;
+
+typedef enum { DK_F32 = 0, DK_BF16 = 1 } dk_dtype;
+
+/* How the G query heads of one KV head combine into one chunk score. */
+typedef enum { DK_REDUCE_MEAN = 0, DK_REDUCE_MAX = 1 } dk_group_reduce;
+
+typedef struct { int64_t b, h, t; } dk_strides;   /* element strides of dims 0, 1, 2 */
+
+/* ABI version of the loaded library (DK_ABI_VERSION it was built with). */
+int dk_abi_version(void);
+
+/* Text of the last failure on the calling thread; valid until its next dk_* call. */
+const char* dk_last_error(void);
+
+/*
+ * dk_build_landmarks - the mean key of every chunk.
+ *
+ * DualDecoder (arXiv 2607.26475), "2.2 Dynamic Sparse KV Cache": adjacent KV
+ * entries are grouped into chunks, each summarised by a GPU-resident landmark;
+ * "4.1 KV Retrieval Predictability": landmarks are built before decoding and
+ * stay fixed.  The landmark is the arithmetic mean of the chunk's keys.
+ *
+ *   lm[b, g, c, :] = (1 / chunk) * sum_{n = c*chunk}^{c*chunk + chunk - 1} K[b, g, n, :]
+ *
+ * K       : keys, k_dtype (DK_F32 or DK_BF16), rows [B, Hkv, L] of d elements,
+ *           strides ks.  Read only.
+ * lm      : out, fp32 [B, Hkv, C, d] contiguous, C = L / chunk.  Sums are kept in fp32.
+ * Errors  : DK_ERR_INVALID_ARG unless B, Hkv, L, d, chunk >= 1, L % chunk == 0 and
+ *           K, lm non-NULL; DK_ERR_UNSUPPORTED unless d % 8 == 0, d <= 512 and
+ *           the 16-byte alignment rule holds.
+ */
+dk_status dk_build_landmarks(const void* K, dk_dtype k_dtype, dk_strides ks,
+                             int B, int Hkv, int L, int d, int chunk,
+                             float* lm, void* stream);
+
+/*
+ * dk_score_topk - chunk scores of both queries and each query's k best chunks.
+ *
+ * DualDecoder "4.1": the retrieval index of a step comes from the current query
+ * and the landmarks, and the speculative token with the same landmarks predicts
+ * the next step's index; the sparse budget is a fixed number of chunks per KV
+ * head (OasisKV summary, "Look-ahead Attention": blocks are ranked per KV head).
+ *
+ *   s[b, g, t, c] = reduce_{h in group g} scale * <q[b, t, h, :], lm[b, g, c, :]>
+ *   topk_idx[b, g, t, :] = the k chunk ids with the largest s, ties to the lower
+ *                          id, written in ascending id order.
+ *
+ * q          : fp32 [B, T, Hq, d] contiguous; query head h belongs to KV head h / (Hq/Hkv).
+ * lm         : landmarks, lm_dtype (v1: DK_F32), rows [B, Hkv, C] of d, strides ls.
+ * reduce     : DK_REDUCE_MEAN (mean over the group's heads) or DK_REDUCE_MAX.
+ * topk_idx   : out, int32 [B, Hkv, T, k].
+ * topk_score : out, fp32 [B, Hkv, T, k] (the selected scores, same order) or NULL.
+ * ws         : workspace of dk_score_topk_workspace_size(B, Hkv, T, C, k) bytes
+ *              (may be NULL when that size is 0).  Contents on entry are ignored.
+ * Errors     : DK_ERR_INVALID_ARG unless 1 <= T <= 2, Hq % Hkv == 0, 1 <= k <= C,
+ *              pointers non-NULL and ws_bytes large enough; DK_ERR_UNSUPPORTED
+ *              unless lm_dtype == DK_F32, d is 64 or 128, C <= 65536, the number
+ *              of query vectors (T for mean, G*T for max) is at most 16 and
+ *              the 16-byte alignment rule holds.
+ */
+size_t dk_score_topk_workspace_size(int B, int Hkv, int T, int C, int k);
+dk_status dk_score_topk(const float* q, int B, int T, int Hq,
+                        const void* lm, dk_dtype lm_dtype, dk_strides ls, int Hkv, int C, int d,
+                        int k, float scale, dk_group_reduce reduce,
+                        int32_t* topk_idx, float* topk_score,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Hot-cache plan for the host-pool path (NULL in HBM-pool mode).
+ *
+ * Adaptive DHiSparse, Figure 2: a selected row that the hot cache does not hold
+ * is copied from host DRAM into the hot cache before attention reads it.
+ * OasisKV summary, "Asynchronous Prefetch Pipeline": the selection stage
+ * compares the predicted set with the resident set and builds a transfer plan.
+ *
+ * Rule: union chunks already resident are hits and keep their slot; misses, in
+ * ascending chunk order, take the free slots (slots whose chunk is not in the
+ * new union, or empty) in ascending slot order; afterwards the cache holds
+ * exactly the new union and every other slot is -1.
+ */
+typedef struct {
+    int32_t* resident;       /* in/out [B, Hkv, slots]: chunk held by each slot, -1 = empty */
+    int      slots;          /* slots per (b, g); must be >= T*k                            */
+    int32_t* slot_of_union;  /* out [B, Hkv, T*k]: slot of each union entry, -1 padded      */
+    int32_t* miss_chunk;     /* out [B, Hkv, T*k]: chunk id of each miss, -1 padded         */
+    int32_t* miss_slot;      /* out [B, Hkv, T*k]: destination slot of each miss            */
+    int32_t* miss_count;     /* out [B, Hkv]                                                */
+    int32_t* hit_count;      /* out [B, Hkv]                                                */
+} dk_cache_plan;
+
+/*
+ * dk_union_select - the distinct chunks of the T selections of every (b, g).
+ *
+ * Adaptive DHiSparse, Figure 3 (2): the top-k selections of several queries of
+ * one request and KV source are resolved together, so each distinct chunk is
+ * moved once, and each query still attends over its own selection.  DualDecoder
+ * "6.3 Accuracy Analysis": the overlap of the predicted (speculative) and true
+ * (real) sets is the prediction accuracy.
+ *
+ * topk_idx    : int32 [B, Hkv, T, k], each row strictly ascending in [0, C)
+ *               (as written by dk_score_topk).
+ * union_ids   : out int32 [B, Hkv, T*k]: ascending distinct ids, -1 padded.
+ * member      : out uint8 [B, Hkv, T*k]: bit t set iff the chunk is in query t's set, 0 padded.
+ * union_count : out int32 [B, Hkv].
+ * overlap     : out int32 [B, Hkv]: |S_0 & S_1| (k when T == 1), or NULL.
+ * plan        : hot-cache plan (see above) or NULL.
+ * Errors      : DK_ERR_INVALID_ARG unless 1 <= T <= 2, 1 <= k <= C <= 2^30, outputs
+ *               non-NULL and, with a plan, all its arrays non-NULL and slots >= T*k;
+ *               DK_ERR_UNSUPPORTED if T*k > 8192 or slots > 8192.
+ */
+dk_status dk_union_select(const int32_t* topk_idx, int B, int Hkv, int T, int k, int C,
+                          int32_t* union_ids, uint8_t* member, int32_t* union_count,
+                          int32_t* overlap, const dk_cache_plan* plan, void* stream);
+
+/*
+ * dk_gather_kv - copy selected chunks of a KV pool into destination slots.
+ *
+ * DualDecoder "5.4 Layer-Scoped KV Memory Management", GPU-side sparse KV
+ * assembly: selected blocks are moved into GPU memory and placed into the
+ * attention layout by a GPU kernel; Adaptive DHiSparse, Figure 2 step 3: missed
+ * rows are copied from host DRAM into the hot cache.
+ *
+ * For every (b, g) and j < count[b, g]: rows [c*chunk, (c+1)*chunk) of K_src and
+ * V_src, c = src_chunk[b, g, j], go to rows [s*chunk, (s+1)*chunk) of K_dst and
+ * V_dst, s = dst_slot[b, g, j] (s = j when dst_slot is NULL).
+ *
+ * src_chunk, dst_slot : int32 [B, Hkv, N].   count : int32 [B, Hkv] (NULL: N each).
+ * src_blocks          : chunks in the source pool; ids outside [0, src_blocks) are skipped.
+ * dst_blocks          : slots in the destination; ids outside [0, dst_blocks) are skipped.
+ * src_is_host = 0     : K_src/V_src and the lists are device memory; one kernel on `stream`.
+ * src_is_host = 1     : K_src/V_src are pinned host memory (hipHostMalloc) and
+ *                       src_chunk, dst_slot, count are host-readable and final
+ *                       when the call is made; the call issues one
+ *                       hipMemcpyAsync (2-D when rows are strided) per run of
+ *                       consecutive chunks on `stream` and returns after issuing.
+ * Errors              : DK_ERR_INVALID_ARG unless sizes >= 1, N >= 0, pointers
+ *                       non-NULL (dst_slot and count may be NULL); DK_ERR_UNSUPPORTED
+ *                       unless the 16-byte alignment rule holds.
+ */
+dk_status dk_gather_kv(const void* K_src, const void* V_src, dk_dtype dt, dk_strides src_s,
+                       int B, int Hkv, int chunk, int d,
+                       const int32_t* src_chunk, const int32_t* dst_slot, const int32_t* count,
+                       int N, int src_blocks,
+                       void* K_dst, void* V_dst, dk_strides dst_s, int dst_blocks,
+                       int src_is_host, void* stream);
+
+/*
+ * dk_sparse_decode_attn - attention of every query head over its own chunks,
+ * both queries in one pass over the union.
+ *
+ * DualDecoder "4.2" and "5.3": the result must equal attention over the true
+ * retrieval index; "5.2" and "6.4": the real and speculative tokens are
+ * processed by one attention launch instead of two.  Adaptive DHiSparse Figure 3
+ * (2): each query attends over its own selection.
+ *
+ * For query head h (KV head g = h / G) and query t, with R the rows of the chunks
+ * i < count[b, g] whose member bit t is set:
+ *   z = scale * K[b, g, R] q[b, t, h],  out[b, t, h] = softmax(z) V[b, g, R],
+ *   lse[b, t, h] = log sum exp z   (out = 0 and lse = -inf when R is empty).
+ * Each union chunk is read once for all G*T query rows.
+ *
+ * q          : fp32 [B, T, Hq, dk] contiguous.  With bf16 K, q is read as bf16
+ *              (exact for bf16-valued queries); fp32 K uses q as is.
+ * K, V       : pools (kv_dtype) with strides ks, vs; block_ids index chunks of
+ *              `chunk` rows in them (pool chunk ids, or hot-cache slot ids).
+ * block_ids  : int32 [B, Hkv, N]; ids outside [0, pool_blocks) are skipped.
+ * member     : uint8 [B, Hkv, N] query bits, or NULL when T == 1 (all rows belong).
+ * count      : int32 [B, Hkv] valid entries (<= N), or NULL for N.
+ * out, lse   : out fp32 [B, T, Hq, dv] and [B, T, Hq] (lse may be NULL).
+ * ws         : workspace of dk_attn_workspace_size(...) bytes (NULL when 0).
+ * Errors     : DK_ERR_INVALID_ARG unless sizes >= 1, Hq % Hkv == 0, 1 <= T <= 2,
+ *              pointers non-NULL as stated and ws_bytes large enough;
+ *              DK_ERR_UNSUPPORTED unless dk == dv in {64, 128}, G*T <= 16 and
+ *              the 16-byte alignment rule holds.
+ */
+size_t dk_attn_workspace_size(int B, int Hkv, int T, int Hq, int dv, int N, int chunk);
+dk_status dk_sparse_decode_attn(const float* q, int B, int T, int Hq, int Hkv,
+                                const void* K, const void* V, dk_dtype kv_dtype,
+                                dk_strides ks, dk_strides vs, int dk, int dv, int chunk,
+                                const int32_t* block_ids, const uint8_t* member,
+                                const int32_t* count, int N, int pool_blocks, float scale,
+                                float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DUALKV_H */

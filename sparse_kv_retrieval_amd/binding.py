@@ -1,0 +1,296 @@
+"""ctypes binding of libdualkv for torch tensors and torch streams.
+
+Argument marshalling only: each function checks that tensors have the layout
+the C ABI states, passes their data pointers and the current HIP stream, and
+raises ``DualKVError`` when the library returns anything but DK_OK.  Every step
+of the computation runs in the library's HIP kernels; torch provides memory and
+streams.  Importing this module fails loudly if ``libdualkv.so`` has not been
+built (``python -m sparse_kv_retrieval_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdualkv.so")
+
+DK_OK, DK_ERR_INVALID_ARG, DK_ERR_UNSUPPORTED, DK_ERR_HIP = 0, 1, 2, 3
+DK_F32, DK_BF16 = 0, 1
+DK_REDUCE_MEAN, DK_REDUCE_MAX = 0, 1
+ABI_VERSION = 1
+
+_STATUS = {0: "DK_OK", 1: "DK_ERR_INVALID_ARG", 2: "DK_ERR_UNSUPPORTED", 3: "DK_ERR_HIP"}
+
+
+class DualKVError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class dk_strides(ctypes.Structure):
+    _fields_ = [("b", ctypes.c_int64), ("h", ctypes.c_int64), ("t", ctypes.c_int64)]
+
+
+class dk_cache_plan(ctypes.Structure):
+    _fields_ = [("resident", ctypes.c_void_p), ("slots", ctypes.c_int),
+                ("slot_of_union", ctypes.c_void_p), ("miss_chunk", ctypes.c_void_p),
+                ("miss_slot", ctypes.c_void_p), ("miss_count", ctypes.c_void_p),
+                ("hit_count", ctypes.c_void_p)]
+
+
+# (name, restype, argtypes) of every exported function
+_P, _I, _Z, _F, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float, dk_strides
+EXPORTS = [
+    ("dk_abi_version", ctypes.c_int, []),
+    ("dk_last_error", ctypes.c_char_p, []),
+    ("dk_build_landmarks", _I, [_P, _I, _S, _I, _I, _I, _I, _I, _P, _P]),
+    ("dk_score_topk_workspace_size", _Z, [_I, _I, _I, _I, _I]),
+    ("dk_score_topk", _I, [_P, _I, _I, _I, _P, _I, _S, _I, _I, _I, _I, _F, _I, _P, _P, _P, _Z, _P]),
+    ("dk_union_select", _I, [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, ctypes.POINTER(dk_cache_plan), _P]),
+    ("dk_gather_kv", _I, [_P, _P, _I, _S, _I, _I, _I, _I, _P, _P, _P, _I, _I, _P, _P, _S, _I, _I, _P]),
+    ("dk_attn_workspace_size", _Z, [_I, _I, _I, _I, _I, _I, _I]),
+    ("dk_sparse_decode_attn", _I, [_P, _I, _I, _I, _I, _P, _P, _I, _S, _S, _I, _I, _I, _P, _P, _P,
+                                   _I, _I, _F, _P, _P, _P, _Z, _P]),
+]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libdualkv.so not found at {LIB_PATH}; build it with "
+                          "`python -m sparse_kv_retrieval_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, res, args in EXPORTS:
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if lib.dk_abi_version() != ABI_VERSION:
+        raise ImportError(f"libdualkv ABI {lib.dk_abi_version()} != binding ABI {ABI_VERSION}")
+    return lib
+
+
+lib = _load()
+
+
+def _check(status: int):
+    if status != DK_OK:
+        raise DualKVError(status, lib.dk_last_error().decode(errors="replace"))
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DK_BF16
+    if t.dtype == torch.float32:
+        return DK_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def pool_strides(t: torch.Tensor) -> dk_strides:
+    """dk_strides of a [B, H, rows, d] tensor whose last dimension is dense."""
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("pool tensors must be 4-D [B, H, rows, d] with a dense last dimension")
+    s = t.stride()
+    return dk_strides(s[0], s[1], s[2])
+
+
+def _need(t: torch.Tensor, dtype, shape, name, device=True):
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name}: need contiguous {dtype} {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+
+
+# ----------------------------------------------------------------------------
+# one wrapper per C entry point
+# ----------------------------------------------------------------------------
+
+def build_landmarks(K: torch.Tensor, chunk: int, lm: torch.Tensor | None = None, stream=None):
+    B, H, L, d = K.shape
+    C = L // chunk if chunk > 0 else 0
+    if lm is None:
+        lm = torch.empty(B, H, C, d, dtype=torch.float32, device=K.device)
+    _need(lm, torch.float32, (B, H, C, d), "lm")
+    _check(lib.dk_build_landmarks(_ptr(K), _dtype(K), pool_strides(K), B, H, L, d, chunk,
+                                  _ptr(lm), _stream(stream)))
+    return lm
+
+
+def score_topk_workspace_size(B, Hkv, T, C, k) -> int:
+    return int(lib.dk_score_topk_workspace_size(B, Hkv, T, C, k))
+
+
+def score_topk(q: torch.Tensor, lm: torch.Tensor, k: int, scale: float, reduce: int = DK_REDUCE_MEAN,
+               topk_idx=None, topk_score=None, ws=None, want_scores=True, stream=None):
+    B, T, Hq, d = q.shape
+    _, Hkv, C, _ = lm.shape
+    _need(q, torch.float32, (B, T, Hq, d), "q")
+    if topk_idx is None:
+        topk_idx = torch.empty(B, Hkv, T, k, dtype=torch.int32, device=q.device)
+    if topk_score is None and want_scores:
+        topk_score = torch.empty(B, Hkv, T, k, dtype=torch.float32, device=q.device)
+    nbytes = score_topk_workspace_size(B, Hkv, T, C, k)
+    if ws is None and nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    _check(lib.dk_score_topk(_ptr(q), B, T, Hq, _ptr(lm), _dtype(lm), pool_strides(lm), Hkv, C, d, k,
+                             float(scale), int(reduce), _ptr(topk_idx), _ptr(topk_score), _ptr(ws),
+                             0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+    return topk_idx, topk_score
+
+
+@dataclass
+class CachePlan:
+    """Device buffers of the hot-cache transfer plan for one layer."""
+    resident: torch.Tensor        # [B, Hkv, slots] int32, -1 = empty
+    slot_of_union: torch.Tensor   # [B, Hkv, T*k]
+    miss_chunk: torch.Tensor
+    miss_slot: torch.Tensor
+    miss_count: torch.Tensor      # [B, Hkv]
+    hit_count: torch.Tensor
+
+    @staticmethod
+    def empty(B, Hkv, T, k, slots, device):
+        i32 = dict(dtype=torch.int32, device=device)
+        return CachePlan(torch.full((B, Hkv, slots), -1, **i32), torch.empty(B, Hkv, T * k, **i32),
+                         torch.empty(B, Hkv, T * k, **i32), torch.empty(B, Hkv, T * k, **i32),
+                         torch.empty(B, Hkv, **i32), torch.empty(B, Hkv, **i32))
+
+    def as_c(self) -> dk_cache_plan:
+        return dk_cache_plan(self.resident.data_ptr(), self.resident.shape[2],
+                             self.slot_of_union.data_ptr(), self.miss_chunk.data_ptr(),
+                             self.miss_slot.data_ptr(), self.miss_count.data_ptr(),
+                             self.hit_count.data_ptr())
+
+
+def union_select(topk_idx: torch.Tensor, C: int, union_ids=None, member=None, count=None,
+                 overlap=None, plan: CachePlan | None = None, stream=None):
+    B, Hkv, T, k = topk_idx.shape
+    _need(topk_idx, torch.int32, (B, Hkv, T, k), "topk_idx")
+    dev = topk_idx.device
+    if union_ids is None:
+        union_ids = torch.empty(B, Hkv, T * k, dtype=torch.int32, device=dev)
+    if member is None:
+        member = torch.empty(B, Hkv, T * k, dtype=torch.uint8, device=dev)
+    if count is None:
+        count = torch.empty(B, Hkv, dtype=torch.int32, device=dev)
+    if overlap is None:
+        overlap = torch.empty(B, Hkv, dtype=torch.int32, device=dev)
+    cplan = ctypes.byref(plan.as_c()) if plan is not None else None
+    _check(lib.dk_union_select(_ptr(topk_idx), B, Hkv, T, k, C, _ptr(union_ids), _ptr(member),
+                               _ptr(count), _ptr(overlap), cplan, _stream(stream)))
+    return union_ids, member, count, overlap
+
+
+def gather_kv(K_src, V_src, src_chunk, count, chunk, K_dst, V_dst, dst_slot=None,
+              src_blocks=None, dst_blocks=None, stream=None):
+    """Copy chunks src_chunk[b, g, j] (j < count[b, g]) into slots of K_dst / V_dst.
+
+    With device pools this is one kernel; with pinned host pools the lists must
+    be host tensors and the copies are hipMemcpyAsync calls on `stream`.
+    """
+    B, Hkv, L, d = K_src.shape
+    N = src_chunk.shape[2]
+    host = not K_src.is_cuda
+    if host and not K_src.is_pinned():
+        raise ValueError("a host KV pool must be in pinned memory")
+    for name, t in (("src_chunk", src_chunk), ("dst_slot", dst_slot), ("count", count)):
+        if t is not None and (t.is_cuda == host or t.dtype != torch.int32 or not t.is_contiguous()):
+            raise ValueError(f"{name}: int32 contiguous, on the {'host' if host else 'device'}")
+    if src_blocks is None:
+        src_blocks = L // chunk
+    if dst_blocks is None:
+        dst_blocks = K_dst.shape[2] // chunk
+    _check(lib.dk_gather_kv(_ptr(K_src), _ptr(V_src), _dtype(K_src), pool_strides(K_src), B, Hkv,
+                            chunk, d, _ptr(src_chunk), _ptr(dst_slot), _ptr(count), N, src_blocks,
+                            _ptr(K_dst), _ptr(V_dst), pool_strides(K_dst), dst_blocks, int(host),
+                            _stream(stream)))
+
+
+def attn_workspace_size(B, Hkv, T, Hq, dv, N, chunk) -> int:
+    return int(lib.dk_attn_workspace_size(B, Hkv, T, Hq, dv, N, chunk))
+
+
+def sparse_decode_attn(q, K, V, block_ids, member, count, chunk: int, scale: float,
+                       pool_blocks: int | None = None, out=None, lse=None, ws=None, want_lse=True,
+                       stream=None):
+    B, T, Hq, dk = q.shape
+    Hkv = K.shape[1]
+    dv = V.shape[3]
+    N = block_ids.shape[2]
+    _need(q, torch.float32, (B, T, Hq, dk), "q")
+    _need(block_ids, torch.int32, (B, Hkv, N), "block_ids")
+    if member is not None:
+        _need(member, torch.uint8, (B, Hkv, N), "member")
+    if count is not None:
+        _need(count, torch.int32, (B, Hkv), "count")
+    if out is None:
+        out = torch.empty(B, T, Hq, dv, dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty(B, T, Hq, dtype=torch.float32, device=q.device)
+    if pool_blocks is None:
+        pool_blocks = K.shape[2] // chunk
+    nbytes = attn_workspace_size(B, Hkv, T, Hq, dv, N, chunk)
+    if ws is None and nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    if K.dtype != V.dtype:
+        raise ValueError("K and V must share a dtype")
+    _check(lib.dk_sparse_decode_attn(_ptr(q), B, T, Hq, Hkv, _ptr(K), _ptr(V), _dtype(K),
+                                     pool_strides(K), pool_strides(V), dk, dv, chunk,
+                                     _ptr(block_ids), _ptr(member), _ptr(count), N, pool_blocks,
+                                     float(scale), _ptr(out), _ptr(lse), _ptr(ws),
+                                     0 if ws is None else ws.numel() * ws.element_size(),
+                                     _stream(stream)))
+    return out, lse
+
+
+# ----------------------------------------------------------------------------
+# one layer of the HBM-pool step with buffers allocated once
+# ----------------------------------------------------------------------------
+
+class DecodeStep:
+    """Preallocated buffers for score_topk -> union_select -> sparse_decode_attn.
+
+    ``run(q, lm, K, V)`` enqueues the three calls on the current stream and
+    returns the output buffers (reused across calls).
+    """
+
+    def __init__(self, B, T, Hq, Hkv, d, C, chunk, k, scale, device, reduce=DK_REDUCE_MEAN,
+                 want_scores=True):
+        self.B, self.T, self.Hq, self.Hkv, self.d, self.C = B, T, Hq, Hkv, d, C
+        self.chunk, self.k, self.scale, self.reduce = chunk, k, scale, reduce
+        i32 = dict(dtype=torch.int32, device=device)
+        self.topk_idx = torch.empty(B, Hkv, T, k, **i32)
+        self.topk_score = torch.empty(B, Hkv, T, k, dtype=torch.float32, device=device) \
+            if want_scores else None
+        n = score_topk_workspace_size(B, Hkv, T, C, k)
+        self.ws_topk = torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+        self.union_ids = torch.empty(B, Hkv, T * k, **i32)
+        self.member = torch.empty(B, Hkv, T * k, dtype=torch.uint8, device=device)
+        self.count = torch.empty(B, Hkv, **i32)
+        self.overlap = torch.empty(B, Hkv, **i32)
+        n = attn_workspace_size(B, Hkv, T, Hq, d, T * k, chunk)
+        self.ws_attn = torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+        self.out = torch.empty(B, T, Hq, d, dtype=torch.float32, device=device)
+        self.lse = torch.empty(B, T, Hq, dtype=torch.float32, device=device)
+
+    def run(self, q, lm, K, V, stream=None):
+        score_topk(q, lm, self.k, self.scale, self.reduce, self.topk_idx, self.topk_score,
+                   self.ws_topk, stream=stream)
+        union_select(self.topk_idx, self.C, self.union_ids, self.member, self.count, self.overlap,
+                     stream=stream)
+        sparse_decode_attn(q, K, V, self.union_ids, self.member, self.count, self.chunk, self.scale,
+                           out=self.out, lse=self.lse, ws=self.ws_attn, stream=stream)
+        return self.out, self.lse

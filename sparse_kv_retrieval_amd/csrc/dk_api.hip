@@ -1,0 +1,251 @@
+// libdualkv C ABI: argument checks, workspace sizing, launches, error text.
+// Every check runs before anything is enqueued; a failing call enqueues nothing.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "dk_common.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+dk_status fail(dk_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+dk_status hip_fail(hipError_t e, const char* what) {
+    return fail(DK_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int dtype_size(dk_dtype dt) { return dt == DK_BF16 ? 2 : (dt == DK_F32 ? 4 : 0); }
+
+bool strides_ok(dk_strides s, int esz) {
+    if (s.b < 0 || s.h < 0 || s.t < 0) return false;
+    return (s.b * esz) % 16 == 0 && (s.h * esz) % 16 == 0 && (s.t * esz) % 16 == 0;
+}
+
+#define DK_REQUIRE(cond, status, ...) \
+    do {                              \
+        if (!(cond)) return fail(status, __VA_ARGS__); \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int dk_abi_version(void) { return DK_ABI_VERSION; }
+
+const char* dk_last_error(void) { return g_err.c_str(); }
+
+dk_status dk_build_landmarks(const void* K, dk_dtype k_dtype, dk_strides ks, int B, int Hkv, int L,
+                             int d, int chunk, float* lm, void* stream) {
+    g_err.clear();
+    const int esz = dtype_size(k_dtype);
+    DK_REQUIRE(K && lm, DK_ERR_INVALID_ARG, "dk_build_landmarks: K and lm must be non-NULL");
+    DK_REQUIRE(esz != 0, DK_ERR_INVALID_ARG, "dk_build_landmarks: unknown k_dtype %d", (int)k_dtype);
+    DK_REQUIRE(B >= 1 && Hkv >= 1 && L >= 1 && d >= 1 && chunk >= 1, DK_ERR_INVALID_ARG,
+               "dk_build_landmarks: B, Hkv, L, d, chunk must be >= 1");
+    DK_REQUIRE(L % chunk == 0, DK_ERR_INVALID_ARG, "dk_build_landmarks: L (%d) %% chunk (%d) != 0", L,
+               chunk);
+    DK_REQUIRE(d % 8 == 0 && d <= 512, DK_ERR_UNSUPPORTED,
+               "dk_build_landmarks: d must be a multiple of 8 and <= 512 (got %d)", d);
+    DK_REQUIRE(aligned16(K) && aligned16(lm) && strides_ok(ks, esz), DK_ERR_UNSUPPORTED,
+               "dk_build_landmarks: K, lm and K's strides must be 16-byte aligned");
+    DK_REQUIRE((int64_t)B * Hkv * (L / chunk) < (int64_t)1 << 40, DK_ERR_INVALID_ARG,
+               "dk_build_landmarks: too many chunks");
+    hipError_t e = dk::launch_landmarks(K, k_dtype, ks, B, Hkv, L, d, chunk, lm, (hipStream_t)stream);
+    return e == hipSuccess ? DK_OK : hip_fail(e, "dk_build_landmarks");
+}
+
+size_t dk_score_topk_workspace_size(int B, int Hkv, int T, int C, int k) {
+    if (B < 1 || Hkv < 1 || T < 1 || T > 2 || k < 1 || C < k) return 0;
+    return dk::plan_topk(B, Hkv, T, C, k).ws_bytes;
+}
+
+dk_status dk_score_topk(const float* q, int B, int T, int Hq, const void* lm, dk_dtype lm_dtype,
+                        dk_strides ls, int Hkv, int C, int d, int k, float scale,
+                        dk_group_reduce reduce, int32_t* topk_idx, float* topk_score, void* ws,
+                        size_t ws_bytes, void* stream) {
+    g_err.clear();
+    DK_REQUIRE(q && lm && topk_idx, DK_ERR_INVALID_ARG, "dk_score_topk: q, lm, topk_idx must be non-NULL");
+    DK_REQUIRE(B >= 1 && Hq >= 1 && Hkv >= 1 && C >= 1 && d >= 1, DK_ERR_INVALID_ARG,
+               "dk_score_topk: B, Hq, Hkv, C, d must be >= 1");
+    DK_REQUIRE(T == 1 || T == 2, DK_ERR_INVALID_ARG, "dk_score_topk: T must be 1 or 2 (got %d)", T);
+    DK_REQUIRE(Hq % Hkv == 0, DK_ERR_INVALID_ARG, "dk_score_topk: Hq (%d) %% Hkv (%d) != 0", Hq, Hkv);
+    DK_REQUIRE(k >= 1 && k <= C, DK_ERR_INVALID_ARG, "dk_score_topk: need 1 <= k (%d) <= C (%d)", k, C);
+    DK_REQUIRE(reduce == DK_REDUCE_MEAN || reduce == DK_REDUCE_MAX, DK_ERR_INVALID_ARG,
+               "dk_score_topk: unknown reduce %d", (int)reduce);
+    DK_REQUIRE(std::isfinite(scale), DK_ERR_INVALID_ARG, "dk_score_topk: scale must be finite");
+    DK_REQUIRE(lm_dtype == DK_F32, DK_ERR_UNSUPPORTED, "dk_score_topk: landmarks must be DK_F32");
+    DK_REQUIRE(d == 64 || d == 128, DK_ERR_UNSUPPORTED, "dk_score_topk: d must be 64 or 128 (got %d)", d);
+    DK_REQUIRE(C <= 65536, DK_ERR_UNSUPPORTED, "dk_score_topk: C must be <= 65536 (got %d)", C);
+    const int G = Hq / Hkv;
+    if (reduce == DK_REDUCE_MAX) {
+        const int nq = G * T;
+        DK_REQUIRE(nq <= 16 && (nq & (nq - 1)) == 0, DK_ERR_UNSUPPORTED,
+                   "dk_score_topk: max reduction needs G*T a power of two <= 16 (got %d)", nq);
+    }
+    DK_REQUIRE(aligned16(q) && aligned16(lm) && strides_ok(ls, 4), DK_ERR_UNSUPPORTED,
+               "dk_score_topk: q, lm and lm's strides must be 16-byte aligned");
+    const dk::TopkPlan plan = dk::plan_topk(B, Hkv, T, C, k);
+    DK_REQUIRE(plan.splits > 0, DK_ERR_UNSUPPORTED, "dk_score_topk: no split plan for C=%d k=%d", C, k);
+    DK_REQUIRE(ws_bytes >= plan.ws_bytes && (plan.ws_bytes == 0 || ws), DK_ERR_INVALID_ARG,
+               "dk_score_topk: workspace needs %zu bytes (got %zu)", plan.ws_bytes, ws_bytes);
+    hipError_t e = dk::launch_score_topk(q, B, T, Hq, (const float*)lm, ls, Hkv, C, d, k, scale, reduce,
+                                         topk_idx, topk_score, ws, plan, (hipStream_t)stream);
+    return e == hipSuccess ? DK_OK : hip_fail(e, "dk_score_topk");
+}
+
+dk_status dk_union_select(const int32_t* topk_idx, int B, int Hkv, int T, int k, int C,
+                          int32_t* union_ids, uint8_t* member, int32_t* union_count,
+                          int32_t* overlap, const dk_cache_plan* plan, void* stream) {
+    g_err.clear();
+    DK_REQUIRE(topk_idx && union_ids && member && union_count, DK_ERR_INVALID_ARG,
+               "dk_union_select: topk_idx, union_ids, member, union_count must be non-NULL");
+    DK_REQUIRE(B >= 1 && Hkv >= 1, DK_ERR_INVALID_ARG, "dk_union_select: B, Hkv must be >= 1");
+    DK_REQUIRE(T == 1 || T == 2, DK_ERR_INVALID_ARG, "dk_union_select: T must be 1 or 2 (got %d)", T);
+    DK_REQUIRE(k >= 1 && k <= C && C <= (1 << 30), DK_ERR_INVALID_ARG,
+               "dk_union_select: need 1 <= k (%d) <= C (%d) <= 2^30", k, C);
+    const int N = T * k;
+    int slots = 0;
+    if (plan) {
+        DK_REQUIRE(plan->resident && plan->slot_of_union && plan->miss_chunk && plan->miss_slot &&
+                       plan->miss_count && plan->hit_count,
+                   DK_ERR_INVALID_ARG, "dk_union_select: every cache-plan array must be non-NULL");
+        DK_REQUIRE(plan->slots >= N, DK_ERR_INVALID_ARG,
+                   "dk_union_select: cache slots (%d) must be >= T*k (%d)", plan->slots, N);
+        slots = plan->slots;
+    }
+    DK_REQUIRE(N <= 8192 && slots <= 8192, DK_ERR_UNSUPPORTED,
+               "dk_union_select: T*k and slots must be <= 8192");
+    const int64_t lds = (int64_t)(3 * k + 1 + N + 8 + (plan ? 2 * slots + N : 0)) * 4;
+    DK_REQUIRE(lds <= 65536, DK_ERR_UNSUPPORTED, "dk_union_select: k and slots too large for one block");
+    hipError_t e = dk::launch_union(topk_idx, B, Hkv, T, k, C, union_ids, member, union_count, overlap,
+                                    plan, (hipStream_t)stream);
+    return e == hipSuccess ? DK_OK : hip_fail(e, "dk_union_select");
+}
+
+dk_status dk_gather_kv(const void* K_src, const void* V_src, dk_dtype dt, dk_strides src_s, int B,
+                       int Hkv, int chunk, int d, const int32_t* src_chunk, const int32_t* dst_slot,
+                       const int32_t* count, int N, int src_blocks, void* K_dst, void* V_dst,
+                       dk_strides dst_s, int dst_blocks, int src_is_host, void* stream) {
+    g_err.clear();
+    const int esz = dtype_size(dt);
+    DK_REQUIRE(K_src && V_src && K_dst && V_dst && src_chunk, DK_ERR_INVALID_ARG,
+               "dk_gather_kv: K_src, V_src, K_dst, V_dst, src_chunk must be non-NULL");
+    DK_REQUIRE(esz != 0, DK_ERR_INVALID_ARG, "dk_gather_kv: unknown dtype %d", (int)dt);
+    DK_REQUIRE(B >= 1 && Hkv >= 1 && chunk >= 1 && d >= 1 && N >= 0 && src_blocks >= 0 && dst_blocks >= 0,
+               DK_ERR_INVALID_ARG, "dk_gather_kv: sizes out of range");
+    DK_REQUIRE(src_is_host == 0 || src_is_host == 1, DK_ERR_INVALID_ARG,
+               "dk_gather_kv: src_is_host must be 0 or 1");
+    DK_REQUIRE(src_s.b >= 0 && src_s.h >= 0 && src_s.t >= 0 && dst_s.b >= 0 && dst_s.h >= 0 && dst_s.t >= 0,
+               DK_ERR_INVALID_ARG, "dk_gather_kv: strides must be >= 0");
+    DK_REQUIRE(aligned16(K_src) && aligned16(V_src) && aligned16(K_dst) && aligned16(V_dst) &&
+                   strides_ok(src_s, esz) && strides_ok(dst_s, esz) && (d * esz) % 16 == 0,
+               DK_ERR_UNSUPPORTED, "dk_gather_kv: pools, strides and rows must be 16-byte aligned");
+    hipStream_t st = (hipStream_t)stream;
+    if (N == 0) return DK_OK;
+    if (!src_is_host) {
+        hipError_t e = dk::launch_gather(K_src, V_src, dt, src_s, B, Hkv, chunk, d, src_chunk, dst_slot,
+                                         count, N, src_blocks, K_dst, V_dst, dst_s, dst_blocks, st);
+        return e == hipSuccess ? DK_OK : hip_fail(e, "dk_gather_kv");
+    }
+    // Host pool: one copy per run of consecutive source chunks going to
+    // consecutive slots (rows of consecutive chunks are adjacent when the row
+    // stride equals the row width; otherwise every chunk is its own 2-D copy).
+    const size_t row_bytes = (size_t)d * esz;
+    const size_t spitch = (size_t)src_s.t * esz, dpitch = (size_t)dst_s.t * esz;
+    const bool merge_runs = spitch == row_bytes && dpitch == row_bytes;
+    for (int b = 0; b < B; ++b) {
+        for (int g = 0; g < Hkv; ++g) {
+            const int64_t bg = (int64_t)b * Hkv + g;
+            int n = count ? count[bg] : N;
+            n = n < 0 ? 0 : (n > N ? N : n);
+            int j = 0;
+            while (j < n) {
+                const int c = src_chunk[bg * N + j];
+                const int s = dst_slot ? dst_slot[bg * N + j] : j;
+                if (c < 0 || c >= src_blocks || s < 0 || s >= dst_blocks) { ++j; continue; }
+                int run = 1;
+                if (merge_runs) {
+                    while (j + run < n) {
+                        const int c2 = src_chunk[bg * N + j + run];
+                        const int s2 = dst_slot ? dst_slot[bg * N + j + run] : j + run;
+                        if (c2 != c + run || s2 != s + run || c2 >= src_blocks || s2 >= dst_blocks) break;
+                        ++run;
+                    }
+                }
+                const int64_t so = ((int64_t)b * src_s.b + (int64_t)g * src_s.h + (int64_t)c * chunk * src_s.t) * esz;
+                const int64_t dof = ((int64_t)b * dst_s.b + (int64_t)g * dst_s.h + (int64_t)s * chunk * dst_s.t) * esz;
+                const size_t rows = (size_t)run * chunk;
+                hipError_t e;
+                if (merge_runs) {
+                    e = hipMemcpyAsync((char*)K_dst + dof, (const char*)K_src + so, rows * row_bytes,
+                                       hipMemcpyHostToDevice, st);
+                    if (e == hipSuccess)
+                        e = hipMemcpyAsync((char*)V_dst + dof, (const char*)V_src + so, rows * row_bytes,
+                                           hipMemcpyHostToDevice, st);
+                } else {
+                    e = hipMemcpy2DAsync((char*)K_dst + dof, dpitch, (const char*)K_src + so, spitch,
+                                         row_bytes, rows, hipMemcpyHostToDevice, st);
+                    if (e == hipSuccess)
+                        e = hipMemcpy2DAsync((char*)V_dst + dof, dpitch, (const char*)V_src + so, spitch,
+                                             row_bytes, rows, hipMemcpyHostToDevice, st);
+                }
+                if (e != hipSuccess) return hip_fail(e, "dk_gather_kv (host)");
+                j += run;
+            }
+        }
+    }
+    return DK_OK;
+}
+
+size_t dk_attn_workspace_size(int B, int Hkv, int T, int Hq, int dv, int N, int chunk) {
+    if (B < 1 || Hkv < 1 || T < 1 || T > 2 || Hq < 1 || Hq % Hkv || dv < 1 || N < 1 || chunk < 1)
+        return 0;
+    return dk::plan_attn(B, Hkv, T, Hq, dv, N, chunk).ws_bytes;
+}
+
+dk_status dk_sparse_decode_attn(const float* q, int B, int T, int Hq, int Hkv, const void* K,
+                                const void* V, dk_dtype kv_dtype, dk_strides ks, dk_strides vs, int dk,
+                                int dv, int chunk, const int32_t* block_ids, const uint8_t* member,
+                                const int32_t* count, int N, int pool_blocks, float scale, float* out,
+                                float* lse, void* ws, size_t ws_bytes, void* stream) {
+    g_err.clear();
+    const int esz = dtype_size(kv_dtype);
+    DK_REQUIRE(q && K && V && block_ids && out, DK_ERR_INVALID_ARG,
+               "dk_sparse_decode_attn: q, K, V, block_ids, out must be non-NULL");
+    DK_REQUIRE(esz != 0, DK_ERR_INVALID_ARG, "dk_sparse_decode_attn: unknown kv_dtype %d", (int)kv_dtype);
+    DK_REQUIRE(B >= 1 && Hq >= 1 && Hkv >= 1 && dk >= 1 && dv >= 1 && chunk >= 1 && N >= 1 &&
+                   pool_blocks >= 0,
+               DK_ERR_INVALID_ARG, "dk_sparse_decode_attn: sizes out of range");
+    DK_REQUIRE(T == 1 || T == 2, DK_ERR_INVALID_ARG, "dk_sparse_decode_attn: T must be 1 or 2 (got %d)", T);
+    DK_REQUIRE(Hq % Hkv == 0, DK_ERR_INVALID_ARG, "dk_sparse_decode_attn: Hq (%d) %% Hkv (%d) != 0", Hq, Hkv);
+    DK_REQUIRE(member || T == 1, DK_ERR_INVALID_ARG, "dk_sparse_decode_attn: member is required when T == 2");
+    DK_REQUIRE(std::isfinite(scale), DK_ERR_INVALID_ARG, "dk_sparse_decode_attn: scale must be finite");
+    DK_REQUIRE(dk == dv && (dk == 64 || dk == 128), DK_ERR_UNSUPPORTED,
+               "dk_sparse_decode_attn: needs dk == dv in {64, 128} (got %d, %d)", dk, dv);
+    DK_REQUIRE((Hq / Hkv) * T <= 16, DK_ERR_UNSUPPORTED, "dk_sparse_decode_attn: G*T must be <= 16");
+    DK_REQUIRE(aligned16(q) && aligned16(out) && aligned16(K) && aligned16(V) && strides_ok(ks, esz) &&
+                   strides_ok(vs, esz),
+               DK_ERR_UNSUPPORTED, "dk_sparse_decode_attn: q, out, K, V and strides must be 16-byte aligned");
+    const dk::AttnPlan plan = dk::plan_attn(B, Hkv, T, Hq, dv, N, chunk);
+    DK_REQUIRE(ws_bytes >= plan.ws_bytes && (plan.ws_bytes == 0 || ws), DK_ERR_INVALID_ARG,
+               "dk_sparse_decode_attn: workspace needs %zu bytes (got %zu)", plan.ws_bytes, ws_bytes);
+    hipError_t e = dk::launch_attention(q, B, T, Hq, Hkv, K, V, kv_dtype, ks, vs, dk, chunk, block_ids,
+                                        member, count, N, pool_blocks, scale, out, lse, ws, plan,
+                                        (hipStream_t)stream);
+    return e == hipSuccess ? DK_OK : hip_fail(e, "dk_sparse_decode_attn");
+}
+
+}  // extern "C"

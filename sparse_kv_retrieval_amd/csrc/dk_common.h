@@ -1,0 +1,137 @@
+// Internal helpers shared by the libdualkv kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dualkv.h"
+
+namespace dk {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// bf16 words: a dword holds two bf16 values, the lower element in bits 0..15.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 with round-to-nearest-even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// a.lo*b.lo + a.hi*b.hi + c in fp32 (v_dot2c_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// ---------------------------------------------------------------------------
+// Order-preserving uint32 key of an fp32 score: a > b  <=>  key(a) > key(b).
+// -0 is folded onto +0 so equal scores give equal keys.  Finite inputs; every
+// finite score (and -inf) maps to a key above 0, so 0 marks an empty slot.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t score_key(float f) {
+    if (f == 0.0f) f = 0.0f;
+    uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_score(uint32_t k) {
+    uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+    return __uint_as_float(u);
+}
+
+// ---------------------------------------------------------------------------
+// Block-wide exclusive prefix sum of one int per thread.  `scratch` holds at
+// least blockDim.x / 64 + 1 ints of LDS.  Returns the exclusive prefix and
+// writes the block total to *total.  Every thread of the block must call it.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        int t = __shfl_up(v, off, kWave);
+        if (lane >= off) v += t;
+    }
+    return v;
+}
+
+__device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* total) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int nwaves = (blockDim.x + kWave - 1) / kWave;
+    int inc = wave_inclusive_scan(v);
+    if (lane == kWave - 1) scratch[wave] = inc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int run = 0;
+        for (int w = 0; w < nwaves; ++w) {
+            int t = scratch[w];
+            scratch[w] = run;
+            run += t;
+        }
+        scratch[nwaves] = run;
+    }
+    __syncthreads();
+    int excl = scratch[wave] + inc - v;
+    *total = scratch[nwaves];
+    __syncthreads();
+    return excl;
+}
+
+// ---------------------------------------------------------------------------
+// 16-byte global loads/stores.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
+}  // namespace dk
+
+// ---------------------------------------------------------------------------
+// Launchers (one per kernel family).  Arguments are already validated.
+// ---------------------------------------------------------------------------
+namespace dk {
+
+hipError_t launch_landmarks(const void* K, dk_dtype dt, dk_strides ks, int B, int Hkv, int L,
+                            int d, int chunk, float* lm, hipStream_t st);
+
+struct TopkPlan {
+    int splits;        // chunk-range splits per (b, g)
+    int rows;          // chunks per split (last split may have fewer)
+    size_t ws_bytes;   // candidate buffer bytes (0 when splits == 1)
+};
+TopkPlan plan_topk(int B, int Hkv, int T, int C, int k);
+hipError_t launch_score_topk(const float* q, int B, int T, int Hq, const float* lm, dk_strides ls,
+                             int Hkv, int C, int d, int k, float scale, dk_group_reduce reduce,
+                             int32_t* topk_idx, float* topk_score, void* ws, const TopkPlan& plan,
+                             hipStream_t st);
+
+hipError_t launch_union(const int32_t* topk_idx, int B, int Hkv, int T, int k, int C,
+                        int32_t* union_ids, uint8_t* member, int32_t* union_count, int32_t* overlap,
+                        const dk_cache_plan* plan, hipStream_t st);
+
+hipError_t launch_gather(const void* K_src, const void* V_src, dk_dtype dt, dk_strides ss, int B,
+                         int Hkv, int chunk, int d, const int32_t* src_chunk, const int32_t* dst_slot,
+                         const int32_t* count, int N, int src_blocks, void* K_dst, void* V_dst,
+                         dk_strides ds, int dst_blocks, hipStream_t st);
+
+struct AttnPlan {
+    int splits;        // union-range splits per (b, g)
+    size_t ws_bytes;   // partial results (0 when splits == 1)
+};
+AttnPlan plan_attn(int B, int Hkv, int T, int Hq, int dv, int N, int chunk);
+hipError_t launch_attention(const float* q, int B, int T, int Hq, int Hkv, const void* K,
+                            const void* V, dk_dtype dt, dk_strides ks, dk_strides vs, int D,
+                            int chunk, const int32_t* block_ids, const uint8_t* member,
+                            const int32_t* count, int N, int pool_blocks, float scale, float* out,
+                            float* lse, void* ws, const AttnPlan& plan, hipStream_t st);
+
+}  // namespace dk

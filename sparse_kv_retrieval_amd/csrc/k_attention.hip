@@ -1,0 +1,459 @@
+// Sparse decode attention of both queries in one pass over the union.
+//
+// DualDecoder (arXiv 2607.26475), "4.2" and "5.3": the result must equal
+// attention over the true retrieval index; "5.2" and "6.4": the real and the
+// speculative token share one attention launch.  Adaptive DHiSparse Figure 3
+// (2): each query attends over its own selection, so a union chunk is masked out
+// for a query whose membership bit is clear.
+//
+// Split-K flash decoding: a block owns one (b, g) and one contiguous range of
+// its union entries (the ranges split the entry count evenly, so the work
+// follows the ragged union sizes), keeps a running max m, sum l and weighted
+// value sum per query row, and either writes the normalised result (one range)
+// or its (m, l, acc) partial for k_attn_merge, which combines the ranges with
+// the online-softmax rule.  Logits are kept in log2 units (scale * log2 e).
+//
+// Fast path (bf16 K/V, d = 128, G = 4, T = 2, chunk a multiple of 32): four
+// waves, wave w owning query head g*4 + w for both tokens.  A 32-row tile of K
+// and V (16 KiB) is read once from HBM with 16-byte loads into a double-buffered
+// LDS stage and used by all eight query rows.  Q.K: two lanes per key, each
+// lane holding its 64-dim half of both queries as packed bf16 in registers and
+// using v_dot2c_f32_bf16; one lane swap leaves lane (key, t) with its logit.
+// K rows are stored with their 16-byte pieces XOR-swizzled by row and the odd
+// lanes walk their half in rotated order, so the eight lanes served per LDS
+// cycle hit distinct banks.  P.V: lane (piece s, key group kg) accumulates 8
+// value dims of keys kg, kg+4, ... in fp32; the key groups are summed at the end.
+#include "dk_common.h"
+
+namespace dk {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct AttnArgs {
+    const float* q;
+    int Hq, Hkv, T, G;
+    const void* K;
+    const void* V;
+    dk_strides ks, vs;
+    int chunk;
+    const int32_t* block_ids;
+    const uint8_t* member;
+    const int32_t* count;
+    int N, pool_blocks;
+    float scale_log2;
+    int splits;
+    float* out;
+    float* lse;
+    float* part_acc;   // [bg][split][R][D]
+    float* part_ml;    // [bg][split][R][2]
+};
+
+__device__ __forceinline__ void entry_range(const AttnArgs& a, int bg, int split, int& u0, int& u1) {
+    int n = a.count ? a.count[bg] : a.N;
+    n = n < 0 ? 0 : (n > a.N ? a.N : n);
+    u0 = (int)((int64_t)split * n / a.splits);
+    u1 = (int)((int64_t)(split + 1) * n / a.splits);
+}
+
+// Write one query row's result: normalised output (single range) or its partial.
+template <int D>
+__device__ __forceinline__ void emit_row(const AttnArgs& a, int b, int bg, int split, int t, int h,
+                                         int r, int R, float m, float l, const float* acc,
+                                         int dim0, int ndim, bool lead) {
+    if (a.splits == 1) {
+        float* o = a.out + (((int64_t)b * a.T + t) * a.Hq + h) * D + dim0;
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        for (int e = 0; e < ndim; ++e) o[e] = acc[e] * inv;
+        if (lead && a.lse)
+            a.lse[((int64_t)b * a.T + t) * a.Hq + h] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+    } else {
+        const int64_t slot = ((int64_t)bg * a.splits + split) * R + r;
+        float* p = a.part_acc + slot * D + dim0;
+        for (int e = 0; e < ndim; ++e) p[e] = acc[e];
+        if (lead) {
+            a.part_ml[slot * 2] = m;
+            a.part_ml[slot * 2 + 1] = l;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Fast path: bf16, D = 128, G = 4, T = 2.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void k_attn_bf16_d128_g4t2(AttnArgs a) {
+    constexpr int D = 128, G = 4, T = 2, R = G * T, KT = 32;
+    __shared__ uint4 kbuf[2][KT * 16];
+    __shared__ uint4 vbuf[2][KT * 16];
+    __shared__ float pbuf[4][KT * 2];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int split = blockIdx.x % a.splits;
+    const int bg = blockIdx.x / a.splits;
+    const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+    int u0, u1;
+    entry_range(a, bg, split, u0, u1);
+    const int tpc = a.chunk / KT;
+    const int ntiles = (u1 - u0) * tpc;
+    const int h = g * G + w;
+
+    // Q in registers: lane (key j, half hd) holds its half of both queries as
+    // bf16 pairs, in the rotated order it reads its K half.
+    const int j = lane >> 1, hd = lane & 1;
+    uint4 qr[T][8];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        const float* qp = a.q + (((int64_t)b * T + t) * a.Hq + h) * D;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int ls = 8 * hd + ((i + 4 * hd) & 7);
+            const float4 x0 = *reinterpret_cast<const float4*>(qp + ls * 8);
+            const float4 x1 = *reinterpret_cast<const float4*>(qp + ls * 8 + 4);
+            qr[t][i] = make_uint4(pack_bf16x2(x0.x, x0.y), pack_bf16x2(x0.z, x0.w),
+                                  pack_bf16x2(x1.x, x1.y), pack_bf16x2(x1.z, x1.w));
+        }
+    }
+
+    const uint16_t* Kb = (const uint16_t*)a.K + (int64_t)b * a.ks.b + (int64_t)g * a.ks.h;
+    const uint16_t* Vb = (const uint16_t*)a.V + (int64_t)b * a.vs.b + (int64_t)g * a.vs.h;
+    const int32_t* ids = a.block_ids + (int64_t)bg * a.N;
+    const uint8_t* mem = a.member + (int64_t)bg * a.N;
+
+    // tile loader: thread owns 16-byte piece (tid & 15) of rows (tid >> 4) and +16
+    const int lr = tid >> 4, lsl = tid & 15;
+    auto tile_info = [&](int it, int& c, int& row0, uint32_t& m) {
+        const int u = u0 + it / tpc;
+        c = ids[u];
+        m = mem[u];
+        if (c < 0 || c >= a.pool_blocks) m = 0;
+        row0 = (m ? c : 0) * a.chunk + (it % tpc) * KT;
+    };
+    uint4 rk0, rk1, rv0, rv1;
+    auto load_tile = [&](int it) {
+        int c, row0;
+        uint32_t m;
+        tile_info(it, c, row0, m);
+        if (m) {
+            rk0 = ld16(Kb + (int64_t)(row0 + lr) * a.ks.t + lsl * 8);
+            rk1 = ld16(Kb + (int64_t)(row0 + lr + 16) * a.ks.t + lsl * 8);
+            rv0 = ld16(Vb + (int64_t)(row0 + lr) * a.vs.t + lsl * 8);
+            rv1 = ld16(Vb + (int64_t)(row0 + lr + 16) * a.vs.t + lsl * 8);
+        }
+    };
+    auto store_tile = [&](int bi) {
+        kbuf[bi][lr * 16 + (lsl ^ (lr & 7))] = rk0;
+        kbuf[bi][(lr + 16) * 16 + (lsl ^ ((lr + 16) & 7))] = rk1;
+        vbuf[bi][lr * 16 + lsl] = rv0;
+        vbuf[bi][(lr + 16) * 16 + lsl] = rv1;
+    };
+
+    float m_run = -INFINITY, l_run = 0.f;     // this lane's query t = hd
+    float acc[T][8];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[t][e] = 0.f;
+    const int ps = lane & 15, kg = lane >> 4;
+
+    if (ntiles > 0) load_tile(0);
+    for (int it = 0; it < ntiles; ++it) {
+        const int bi = it & 1;
+        int c_cur, row_cur;
+        uint32_t m_cur;
+        tile_info(it, c_cur, row_cur, m_cur);
+        if (m_cur) store_tile(bi);
+        if (it + 1 < ntiles) load_tile(it + 1);
+        __syncthreads();
+        if (m_cur == 0) continue;
+
+        // ---- logits ----
+        float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int ls = 8 * hd + ((i + 4 * hd) & 7);
+            const uint4 kv = kbuf[bi][j * 16 + (ls ^ (j & 7))];
+            a0 = dot2_bf16(qr[0][i].x, kv.x, a0);
+            a0 = dot2_bf16(qr[0][i].y, kv.y, a0);
+            a0 = dot2_bf16(qr[0][i].z, kv.z, a0);
+            a0 = dot2_bf16(qr[0][i].w, kv.w, a0);
+            a1 = dot2_bf16(qr[1][i].x, kv.x, a1);
+            a1 = dot2_bf16(qr[1][i].y, kv.y, a1);
+            a1 = dot2_bf16(qr[1][i].z, kv.z, a1);
+            a1 = dot2_bf16(qr[1][i].w, kv.w, a1);
+        }
+        const float send = hd ? a0 : a1;
+        const float keep = hd ? a1 : a0;
+        float z = (keep + __shfl_xor(send, 1, kWave)) * a.scale_log2;
+        if (!((m_cur >> hd) & 1u)) z = -INFINITY;
+
+        // ---- online softmax over this tile, per query t = lane parity ----
+        float cm = z;
+#pragma unroll
+        for (int off = 2; off < kWave; off <<= 1) cm = fmaxf(cm, __shfl_xor(cm, off, kWave));
+        const float mn = fmaxf(m_run, cm);
+        const float alpha = mn == -INFINITY ? 1.f : exp2f(m_run - mn);
+        const float p = mn == -INFINITY ? 0.f : exp2f(z - mn);
+        l_run = l_run * alpha + p;
+        m_run = mn;
+        pbuf[w][lane] = p;   // = pbuf[w][2 * j + hd]
+        const float al0 = __shfl(alpha, 0, kWave);
+        const float al1 = __shfl(alpha, 1, kWave);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        // ---- P.V ----
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            acc[0][e] *= al0;
+            acc[1][e] *= al1;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int jj = kg + 4 * i;
+            const uint4 vv = vbuf[bi][jj * 16 + ps];
+            const float2 pp = *reinterpret_cast<const float2*>(&pbuf[w][2 * jj]);
+            const float v[8] = {bf16_lo(vv.x), bf16_hi(vv.x), bf16_lo(vv.y), bf16_hi(vv.y),
+                                bf16_lo(vv.z), bf16_hi(vv.z), bf16_lo(vv.w), bf16_hi(vv.w)};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                acc[0][e] = fmaf(pp.x, v[e], acc[0][e]);
+                acc[1][e] = fmaf(pp.y, v[e], acc[1][e]);
+            }
+        }
+        // pbuf is rewritten next tile only after every lane read it (program order)
+        __builtin_amdgcn_wave_barrier();
+    }
+
+    // ---- combine lanes ----
+#pragma unroll
+    for (int off = 2; off < kWave; off <<= 1) l_run += __shfl_xor(l_run, off, kWave);
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            acc[t][e] += __shfl_xor(acc[t][e], 16, kWave);
+            acc[t][e] += __shfl_xor(acc[t][e], 32, kWave);
+        }
+    const float m0 = __shfl(m_run, 0, kWave), m1 = __shfl(m_run, 1, kWave);
+    const float l0 = __shfl(l_run, 0, kWave), l1 = __shfl(l_run, 1, kWave);
+    if (kg == 0) {
+        emit_row<D>(a, b, bg, split, 0, h, 0 * G + w, R, m0, l0, acc[0], ps * 8, 8, ps == 0);
+        emit_row<D>(a, b, bg, split, 1, h, 1 * G + w, R, m1, l1, acc[1], ps * 8, 8, ps == 0);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Generic path: fp32 or bf16 K/V, D in {64, 128}, any G*T <= 16, any chunk.
+// Correct and simple; used off the fast path's shapes.
+// ---------------------------------------------------------------------------
+template <typename KVT, int D>
+__device__ __forceinline__ float kv_elem(const KVT* p, int64_t i);
+template <>
+__device__ __forceinline__ float kv_elem<float, 64>(const float* p, int64_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float kv_elem<float, 128>(const float* p, int64_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float kv_elem<uint16_t, 64>(const uint16_t* p, int64_t i) {
+    return __uint_as_float((uint32_t)p[i] << 16);
+}
+template <>
+__device__ __forceinline__ float kv_elem<uint16_t, 128>(const uint16_t* p, int64_t i) {
+    return __uint_as_float((uint32_t)p[i] << 16);
+}
+
+template <typename KVT, int D>
+__global__ __launch_bounds__(kThreads) void k_attn_generic(AttnArgs a) {
+    constexpr int TR = 32, RMAX = 16, DPL = D / kWave;
+    __shared__ float qs[RMAX][D];
+    __shared__ float kt[TR][D + 1];
+    __shared__ float vt[TR][D];
+    __shared__ float zs[RMAX][TR];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int split = blockIdx.x % a.splits;
+    const int bg = blockIdx.x / a.splits;
+    const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+    const int G = a.G, T = a.T, R = G * T;
+    int u0, u1;
+    entry_range(a, bg, split, u0, u1);
+
+    // q rows r = t * G + hh, with bf16 K/V the query is read as bf16 (RNE)
+    for (int i = tid; i < R * D; i += kThreads) {
+        const int r = i / D, dd = i - r * D;
+        const int t = r / G, hh = r - t * G;
+        float x = a.q[(((int64_t)b * T + t) * a.Hq + g * G + hh) * D + dd];
+        if (sizeof(KVT) == 2) x = __uint_as_float(f32_to_bf16_rne(x) << 16);
+        qs[r][dd] = x;
+    }
+    const KVT* Kb = (const KVT*)a.K + (int64_t)b * a.ks.b + (int64_t)g * a.ks.h;
+    const KVT* Vb = (const KVT*)a.V + (int64_t)b * a.vs.b + (int64_t)g * a.vs.h;
+
+    float m_run[4], l_run[4], acc[4][DPL];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+        m_run[x] = -INFINITY;
+        l_run[x] = 0.f;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc[x][e] = 0.f;
+    }
+    const int tiles_per_chunk = (a.chunk + TR - 1) / TR;
+    for (int u = u0; u < u1; ++u) {
+        const int c = a.block_ids[(int64_t)bg * a.N + u];
+        uint32_t m = a.member ? a.member[(int64_t)bg * a.N + u] : 0xffu;
+        if (c < 0 || c >= a.pool_blocks) m = 0;
+        if (m == 0) continue;
+        for (int st = 0; st < tiles_per_chunk; ++st) {
+            const int r0 = st * TR;
+            const int nr = min(TR, a.chunk - r0);
+            __syncthreads();
+            for (int i = tid; i < nr * D; i += kThreads) {
+                const int rr = i / D, dd = i - rr * D;
+                const int64_t row = (int64_t)c * a.chunk + r0 + rr;
+                kt[rr][dd] = kv_elem<KVT, D>(Kb, row * a.ks.t + dd);
+                vt[rr][dd] = kv_elem<KVT, D>(Vb, row * a.vs.t + dd);
+            }
+            __syncthreads();
+            for (int i = tid; i < R * TR; i += kThreads) {
+                const int r = i / TR, jj = i - r * TR;
+                float z = -INFINITY;
+                if (jj < nr && ((m >> (r / G)) & 1u)) {
+                    float s = 0.f;
+                    for (int dd = 0; dd < D; ++dd) s = fmaf(qs[r][dd], kt[jj][dd], s);
+                    z = s * a.scale_log2;
+                }
+                zs[r][jj] = z;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int r = w + 4 * x;
+                if (r >= R) break;
+                const float z = lane < TR ? zs[r][lane] : -INFINITY;
+                float cm = z;
+#pragma unroll
+                for (int off = 1; off < kWave; off <<= 1) cm = fmaxf(cm, __shfl_xor(cm, off, kWave));
+                const float mn = fmaxf(m_run[x], cm);
+                const float alpha = mn == -INFINITY ? 1.f : exp2f(m_run[x] - mn);
+                const float p = mn == -INFINITY ? 0.f : exp2f(z - mn);
+                float ps = p;
+#pragma unroll
+                for (int off = 1; off < kWave; off <<= 1) ps += __shfl_xor(ps, off, kWave);
+                l_run[x] = l_run[x] * alpha + ps;
+                m_run[x] = mn;
+#pragma unroll
+                for (int e = 0; e < DPL; ++e) acc[x][e] *= alpha;
+                for (int jj = 0; jj < nr; ++jj) {
+                    const float pj = __shfl(p, jj, kWave);
+#pragma unroll
+                    for (int e = 0; e < DPL; ++e) acc[x][e] = fmaf(pj, vt[jj][lane * DPL + e], acc[x][e]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+        const int r = w + 4 * x;
+        if (r >= R) break;
+        const int t = r / G, hh = r - t * G;
+        emit_row<D>(a, b, bg, split, t, g * G + hh, r, R, m_run[x], l_run[x], acc[x], lane * DPL,
+                    DPL, lane == 0);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Merge of the split partials (online-softmax combination), one block per (b, g).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_attn_merge(AttnArgs a) {
+    const int bg = blockIdx.x;
+    const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+    const int R = a.G * a.T;
+    constexpr int D4 = D / 4;
+    for (int i = threadIdx.x; i < R * D4; i += kThreads) {
+        const int r = i / D4, d4 = i - r * D4;
+        float M = -INFINITY;
+        for (int s = 0; s < a.splits; ++s)
+            M = fmaxf(M, a.part_ml[(((int64_t)bg * a.splits + s) * R + r) * 2]);
+        float L = 0.f;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (M != -INFINITY) {
+            for (int s = 0; s < a.splits; ++s) {
+                const int64_t slot = ((int64_t)bg * a.splits + s) * R + r;
+                const float ms = a.part_ml[slot * 2];
+                if (ms == -INFINITY) continue;
+                const float f = exp2f(ms - M);
+                L += a.part_ml[slot * 2 + 1] * f;
+                const float4 x = *reinterpret_cast<const float4*>(a.part_acc + slot * D + d4 * 4);
+                acc.x += x.x * f; acc.y += x.y * f; acc.z += x.z * f; acc.w += x.w * f;
+            }
+        }
+        const int t = r / a.G, hh = r - t * a.G;
+        const int h = g * a.G + hh;
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        float* o = a.out + (((int64_t)b * a.T + t) * a.Hq + h) * D + d4 * 4;
+        *reinterpret_cast<float4*>(o) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+        if (d4 == 0 && a.lse)
+            a.lse[((int64_t)b * a.T + t) * a.Hq + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+    }
+}
+
+bool use_fast_path(dk_dtype dt, int D, int G, int T, int chunk) {
+    return dt == DK_BF16 && D == 128 && G == 4 && T == 2 && chunk % 32 == 0;
+}
+
+}  // namespace
+
+AttnPlan plan_attn(int B, int Hkv, int T, int Hq, int dv, int N, int chunk) {
+    AttnPlan p{1, 0};
+    const int64_t bg = (int64_t)B * Hkv;
+    const int R = (Hq / Hkv) * T;
+    const int64_t tiles = (int64_t)N * ((chunk + 31) / 32);
+    int64_t want = (2048 + bg - 1) / bg;
+    int64_t by_work = tiles / 4;
+    if (by_work < 1) by_work = 1;
+    int64_t s = want < by_work ? want : by_work;
+    if (s > 64) s = 64;
+    if (s < 1) s = 1;
+    p.splits = (int)s;
+    p.ws_bytes = s > 1 ? (size_t)(bg * s * R) * (size_t)(dv + 2) * 4 : 0;
+    return p;
+}
+
+hipError_t launch_attention(const float* q, int B, int T, int Hq, int Hkv, const void* K,
+                            const void* V, dk_dtype dt, dk_strides ks, dk_strides vs, int D,
+                            int chunk, const int32_t* block_ids, const uint8_t* member,
+                            const int32_t* count, int N, int pool_blocks, float scale, float* out,
+                            float* lse, void* ws, const AttnPlan& plan, hipStream_t st) {
+    AttnArgs a;
+    a.q = q; a.Hq = Hq; a.Hkv = Hkv; a.T = T; a.G = Hq / Hkv;
+    a.K = K; a.V = V; a.ks = ks; a.vs = vs; a.chunk = chunk;
+    a.block_ids = block_ids; a.member = member; a.count = count;
+    a.N = N; a.pool_blocks = pool_blocks;
+    a.scale_log2 = scale * kLog2e;
+    a.splits = plan.splits;
+    a.out = out; a.lse = lse;
+    const int64_t bg = (int64_t)B * Hkv;
+    const int R = a.G * T;
+    a.part_acc = plan.splits > 1 ? (float*)ws : nullptr;
+    a.part_ml = plan.splits > 1 ? (float*)ws + bg * plan.splits * R * D : nullptr;
+    const unsigned grid = (unsigned)(bg * plan.splits);
+    if (use_fast_path(dt, D, a.G, T, chunk)) {
+        hipLaunchKernelGGL(k_attn_bf16_d128_g4t2, dim3(grid), dim3(kThreads), 0, st, a);
+    } else if (dt == DK_BF16) {
+        if (D == 128) hipLaunchKernelGGL((k_attn_generic<uint16_t, 128>), dim3(grid), dim3(kThreads), 0, st, a);
+        else hipLaunchKernelGGL((k_attn_generic<uint16_t, 64>), dim3(grid), dim3(kThreads), 0, st, a);
+    } else {
+        if (D == 128) hipLaunchKernelGGL((k_attn_generic<float, 128>), dim3(grid), dim3(kThreads), 0, st, a);
+        else hipLaunchKernelGGL((k_attn_generic<float, 64>), dim3(grid), dim3(kThreads), 0, st, a);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || plan.splits == 1) return e;
+    if (D == 128) hipLaunchKernelGGL(k_attn_merge<128>, dim3((unsigned)bg), dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL(k_attn_merge<64>, dim3((unsigned)bg), dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace dk

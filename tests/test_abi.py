@@ -1,0 +1,150 @@
+"""The C ABI: the library loads, exports every declared entry point, and rejects
+bad arguments before it touches the device (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dualkv.h")
+
+b = pytest.importorskip("sparse_kv_retrieval_amd.binding",
+                        reason="libdualkv.so not built (python -m sparse_kv_retrieval_amd.build)")
+lib = b.lib
+
+FAKE = ctypes.c_void_p(0x1000)        # 16-byte aligned, never dereferenced by a failing call
+MIS = ctypes.c_void_p(0x1004)         # misaligned
+NULL = None
+S0 = b.dk_strides(0, 0, 0)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dk_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) == 9, names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert {n for n, _, _ in b.EXPORTS} == set(names)
+
+
+def test_abi_version():
+    assert lib.dk_abi_version() == 1
+
+
+def err():
+    return lib.dk_last_error().decode()
+
+
+def landmarks(K=FAKE, dt=1, ks=b.dk_strides(1 << 20, 1 << 16, 128), B=1, H=1, L=64, d=128, chunk=32,
+              lm=FAKE):
+    return lib.dk_build_landmarks(K, dt, ks, B, H, L, d, chunk, lm, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=NULL), 1), (dict(lm=NULL), 1), (dict(dt=7), 1), (dict(B=0), 1), (dict(chunk=0), 1),
+    (dict(L=65), 1), (dict(d=12), 2), (dict(d=1024), 2), (dict(K=MIS), 2),
+    (dict(ks=b.dk_strides(1 << 20, 1 << 16, 100)), 2),
+])
+def test_landmarks_rejects(kw, status):
+    assert landmarks(**kw) == status
+    assert err().startswith("dk_build_landmarks")
+
+
+def score(q=FAKE, B=2, T=2, Hq=32, lm=FAKE, lmdt=0, ls=b.dk_strides(1 << 22, 1 << 19, 128), Hkv=8,
+          C=1024, d=128, k=64, scale=0.088, reduce=0, idx=FAKE, sc=FAKE, ws=FAKE, wsb=1 << 30):
+    return lib.dk_score_topk(q, B, T, Hq, lm, lmdt, ls, Hkv, C, d, k, scale, reduce, idx, sc, ws, wsb,
+                             None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=NULL), 1), (dict(idx=NULL), 1), (dict(T=3), 1), (dict(T=0), 1), (dict(Hq=30), 1),
+    (dict(k=0), 1), (dict(k=1025), 1), (dict(reduce=5), 1), (dict(scale=float("nan")), 1),
+    (dict(lmdt=1), 2), (dict(d=96), 2), (dict(C=70000, k=64), 2), (dict(reduce=1, Hq=24), 2),
+    (dict(ws=NULL), 1), (dict(wsb=16), 1), (dict(lm=MIS), 2),
+])
+def test_score_topk_rejects(kw, status):
+    assert score(**kw) == status, err()
+    assert err().startswith("dk_score_topk")
+
+
+def test_score_topk_workspace_sizes():
+    # 64 x 8 (b, g) rows over 4096 chunks: 4 ranges of 1024, 64 candidates each
+    assert lib.dk_score_topk_workspace_size(64, 8, 2, 4096, 64) == 64 * 8 * 2 * 4 * 64 * 8
+    assert lib.dk_score_topk_workspace_size(1, 1, 2, 128, 8) > 0
+    assert lib.dk_score_topk_workspace_size(1, 1, 2, 128, 0) == 0
+
+
+def union(idx=FAKE, B=2, H=8, T=2, k=64, C=1024, uo=FAKE, mo=FAKE, cnt=FAKE, ov=FAKE, plan=None):
+    return lib.dk_union_select(idx, B, H, T, k, C, uo, mo, cnt, ov, plan, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(idx=NULL), 1), (dict(uo=NULL), 1), (dict(T=3), 1), (dict(k=0), 1), (dict(k=2000), 1),
+    (dict(k=5000, C=100000), 2),
+])
+def test_union_rejects(kw, status):
+    assert union(**kw) == status
+    assert err().startswith("dk_union_select")
+
+
+def test_union_plan_rejects_small_cache():
+    p = b.dk_cache_plan(0x1000, 100, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
+    assert union(plan=ctypes.byref(p)) == 1 and "slots" in err()
+    p = b.dk_cache_plan(0x1000, 128, 0, 0x1000, 0x1000, 0x1000, 0x1000)
+    assert union(plan=ctypes.byref(p)) == 1
+
+
+def attn(q=FAKE, B=2, T=2, Hq=32, Hkv=8, K=FAKE, V=FAKE, dt=1, ks=b.dk_strides(1 << 22, 1 << 19, 128),
+         vs=b.dk_strides(1 << 22, 1 << 19, 128), dk=128, dv=128, chunk=32, ids=FAKE, mem=FAKE, cnt=FAKE,
+         N=128, pool=1024, scale=0.088, out=FAKE, lse=FAKE, ws=FAKE, wsb=1 << 30):
+    return lib.dk_sparse_decode_attn(q, B, T, Hq, Hkv, K, V, dt, ks, vs, dk, dv, chunk, ids, mem, cnt, N,
+                                     pool, scale, out, lse, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=NULL), 1), (dict(ids=NULL), 1), (dict(out=NULL), 1), (dict(mem=NULL), 1), (dict(T=3), 1),
+    (dict(Hq=33), 1), (dict(N=0), 1), (dict(dt=9), 1), (dict(scale=float("inf")), 1),
+    (dict(dk=96, dv=96), 2), (dict(dk=128, dv=64), 2), (dict(Hq=80, Hkv=8), 2), (dict(K=MIS), 2),
+    (dict(vs=b.dk_strides(1 << 22, 1 << 19, 100)), 2), (dict(ws=NULL), 1), (dict(wsb=8), 1),
+])
+def test_attention_rejects(kw, status):
+    assert attn(**kw) == status, err()
+    assert err().startswith("dk_sparse_decode_attn")
+
+
+def test_attention_member_optional_for_one_query():
+    # T == 1 without a member array gets past the member check and stops at the
+    # (deliberately too small) workspace, so nothing is launched.
+    assert attn(T=1, mem=NULL, wsb=8) == 1
+    assert "workspace" in err()
+
+
+def gather(Ks=FAKE, Vs=FAKE, dt=1, ss=b.dk_strides(1 << 22, 1 << 19, 128), B=2, H=8, chunk=32, d=128,
+           src=FAKE, dst=NULL, cnt=NULL, N=16, sb=1024, Kd=FAKE, Vd=FAKE, ds=b.dk_strides(1 << 16, 1 << 13, 128),
+           db=64, host=0):
+    return lib.dk_gather_kv(Ks, Vs, dt, ss, B, H, chunk, d, src, dst, cnt, N, sb, Kd, Vd, ds, db, host, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Ks=NULL), 1), (dict(src=NULL), 1), (dict(N=-1), 1), (dict(host=2), 1), (dict(dt=3), 1),
+    (dict(Kd=MIS), 2), (dict(d=4), 2), (dict(ss=b.dk_strides(-8, 0, 128)), 1),
+])
+def test_gather_rejects(kw, status):
+    assert gather(**kw) == status
+    assert err().startswith("dk_gather_kv")
+
+
+def test_gather_empty_is_ok():
+    assert gather(N=0) == 0
+
+
+def test_attention_workspace_sizes():
+    # 64 x 8 (b, g) rows, 4 ranges each, 8 query rows of 128 values plus (m, l)
+    assert lib.dk_attn_workspace_size(64, 8, 2, 32, 128, 128, 32) == 64 * 8 * 4 * 8 * 130 * 4
+    assert lib.dk_attn_workspace_size(64, 8, 2, 30, 128, 128, 32) == 0
