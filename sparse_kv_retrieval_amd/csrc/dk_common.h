@@ -88,6 +88,42 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* to
 }
 
 // ---------------------------------------------------------------------------
+// Cross-lane helpers.
+// ---------------------------------------------------------------------------
+// value of lane i ^ 1 (DPP quad_perm [1,0,3,2]; a VALU op, no LDS round trip)
+__device__ __forceinline__ float dpp_xor1(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+
+// ---------------------------------------------------------------------------
+// Global -> LDS DMA (gfx950 global_load_lds_dwordx4).  Lane i's 16 bytes land
+// at lds_base + 16 * i; lds_base must be wave-uniform.  The load is issued from
+// inline asm so that the compiler does not insert its own (conservative)
+// vmcnt waits; callers wait with lds_dma_wait<N>() (N = loads that may still be
+// in flight) and must issue no other vector-memory loads between a DMA and its
+// wait.  Non-temporal: the streamed KV is not reused.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) char lds_char_t;
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)((lds_char_t*)(p));
+}
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+                 :: "v"(g), "s"(lds_base) : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void lds_dma_wait() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" :: "n"(N) : "memory");
+}
+// s_barrier without the compiler's release fence (which would wait for every
+// outstanding DMA); ordering of LDS accesses is kept by the asm memory clobbers.
+__device__ __forceinline__ void raw_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// ---------------------------------------------------------------------------
 // 16-byte global loads/stores.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }

@@ -14,15 +14,19 @@
 // the online-softmax rule.  Logits are kept in log2 units (scale * log2 e).
 //
 // Fast path (bf16 K/V, d = 128, G = 4, T = 2, chunk a multiple of 32): four
-// waves, wave w owning query head g*4 + w for both tokens.  A 32-row tile of K
-// and V (16 KiB) is read once from HBM with 16-byte loads into a double-buffered
-// LDS stage and used by all eight query rows.  Q.K: two lanes per key, each
-// lane holding its 64-dim half of both queries as packed bf16 in registers and
-// using v_dot2c_f32_bf16; one lane swap leaves lane (key, t) with its logit.
-// K rows are stored with their 16-byte pieces XOR-swizzled by row and the odd
-// lanes walk their half in rotated order, so the eight lanes served per LDS
-// cycle hit distinct banks.  P.V: lane (piece s, key group kg) accumulates 8
-// value dims of keys kg, kg+4, ... in fp32; the key groups are summed at the end.
+// waves, wave w owning query head g*4 + w for both tokens.  32-row tiles of K
+// and V (16 KiB) stream from HBM straight into a three-stage LDS ring with
+// global_load_lds_dwordx4 (non-temporal; no register staging), so two tiles are
+// in flight while one is computed, and each tile is read from HBM once for all
+// eight query rows.  Q.K: two lanes per key, each holding its 64-dim half of
+// both queries as packed bf16 in registers (v_dot2c_f32_bf16); one DPP lane swap
+// leaves lane (key, t) with its logit.  K pieces are XOR-swizzled by row in LDS
+// and odd lanes walk their half in rotated order, so the lanes served per LDS
+// cycle hit distinct banks.  The running max only moves when a logit exceeds it
+// (a ballot), so most tiles need no cross-lane reduction.  P.V: the weights
+// are rounded to bf16 and keys j, j + 4 are paired along v_dot2c_f32_bf16
+// (V words re-paired with v_perm_b32); the row sums use the same rounded
+// weights, so each output stays an exact convex combination of its values.
 #include "dk_common.h"
 
 namespace dk {
@@ -81,13 +85,21 @@ __device__ __forceinline__ void emit_row(const AttnArgs& a, int b, int bg, int s
 }
 
 // ---------------------------------------------------------------------------
-// Fast path: bf16, D = 128, G = 4, T = 2.
+// Fast path: bf16, D = 128, G = 4, T = 2, chunk % 32 == 0.
 // ---------------------------------------------------------------------------
+constexpr int kFastStages = 3;     // LDS ring: one tile computed, two in flight
+constexpr int kFastMaxEntries = 256;
+
+struct __align__(16) FastSmem {
+    uint4 kv[kFastStages][2][32 * 16];     // [stage][K|V][row * 16 + 16-byte piece]
+    int32_t erow[kFastMaxEntries];         // first pool row of each entry's chunk
+    uint32_t ebits[kFastMaxEntries];       // membership bits (0: skip the entry)
+    uint32_t p16[4][16][2];                // [wave][key pair][t]: bf16 weights of keys j, j + 4
+};
+
 __global__ __launch_bounds__(kThreads) void k_attn_bf16_d128_g4t2(AttnArgs a) {
-    constexpr int D = 128, G = 4, T = 2, R = G * T, KT = 32;
-    __shared__ uint4 kbuf[2][KT * 16];
-    __shared__ uint4 vbuf[2][KT * 16];
-    __shared__ float pbuf[4][KT * 2];
+    constexpr int D = 128, G = 4, T = 2, R = G * T, KT = 32, NS = kFastStages;
+    __shared__ FastSmem sm;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int split = blockIdx.x % a.splits;
@@ -96,11 +108,11 @@ __global__ __launch_bounds__(kThreads) void k_attn_bf16_d128_g4t2(AttnArgs a) {
     int u0, u1;
     entry_range(a, bg, split, u0, u1);
     const int tpc = a.chunk / KT;
-    const int ntiles = (u1 - u0) * tpc;
+    const int ntiles = a.pool_blocks > 0 ? (u1 - u0) * tpc : 0;
     const int h = g * G + w;
 
-    // Q in registers: lane (key j, half hd) holds its half of both queries as
-    // bf16 pairs, in the rotated order it reads its K half.
+    // Q in registers: lane (key j, half hd) holds its 64-dim half of both queries
+    // as bf16 pairs, in the rotated order in which it reads its K half.
     const int j = lane >> 1, hd = lane & 1;
     uint4 qr[T][8];
 #pragma unroll
@@ -115,38 +127,49 @@ __global__ __launch_bounds__(kThreads) void k_attn_bf16_d128_g4t2(AttnArgs a) {
                                   pack_bf16x2(x1.x, x1.y), pack_bf16x2(x1.z, x1.w));
         }
     }
-
-    const uint16_t* Kb = (const uint16_t*)a.K + (int64_t)b * a.ks.b + (int64_t)g * a.ks.h;
-    const uint16_t* Vb = (const uint16_t*)a.V + (int64_t)b * a.vs.b + (int64_t)g * a.vs.h;
+    // This block's entries go to LDS, so the tile loop issues no vector loads of
+    // its own besides the DMA (keeps the explicit vmcnt accounting exact).
     const int32_t* ids = a.block_ids + (int64_t)bg * a.N;
     const uint8_t* mem = a.member + (int64_t)bg * a.N;
-
-    // tile loader: thread owns 16-byte piece (tid & 15) of rows (tid >> 4) and +16
-    const int lr = tid >> 4, lsl = tid & 15;
-    auto tile_info = [&](int it, int& c, int& row0, uint32_t& m) {
-        const int u = u0 + it / tpc;
-        c = ids[u];
-        m = mem[u];
+    for (int e = tid; e < u1 - u0; e += kThreads) {
+        const int c = ids[u0 + e];
+        uint32_t m = mem[u0 + e];
         if (c < 0 || c >= a.pool_blocks) m = 0;
-        row0 = (m ? c : 0) * a.chunk + (it % tpc) * KT;
-    };
-    uint4 rk0, rk1, rv0, rv1;
-    auto load_tile = [&](int it) {
-        int c, row0;
-        uint32_t m;
-        tile_info(it, c, row0, m);
-        if (m) {
-            rk0 = ld16(Kb + (int64_t)(row0 + lr) * a.ks.t + lsl * 8);
-            rk1 = ld16(Kb + (int64_t)(row0 + lr + 16) * a.ks.t + lsl * 8);
-            rv0 = ld16(Vb + (int64_t)(row0 + lr) * a.vs.t + lsl * 8);
-            rv1 = ld16(Vb + (int64_t)(row0 + lr + 16) * a.vs.t + lsl * 8);
-        }
-    };
-    auto store_tile = [&](int bi) {
-        kbuf[bi][lr * 16 + (lsl ^ (lr & 7))] = rk0;
-        kbuf[bi][(lr + 16) * 16 + (lsl ^ ((lr + 16) & 7))] = rk1;
-        vbuf[bi][lr * 16 + lsl] = rv0;
-        vbuf[bi][(lr + 16) * 16 + lsl] = rv1;
+        sm.erow[e] = (m ? c : 0) * a.chunk;
+        sm.ebits[e] = m;
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            asm volatile("" : "+v"(qr[t][i].x), "+v"(qr[t][i].y), "+v"(qr[t][i].z), "+v"(qr[t][i].w));
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    // DMA geometry: wave w fills rows 8w..8w+7 of the K tile (pieces XOR-swizzled
+    // by row) and of the V tile (plain), two 1 KiB wave-loads each.
+    const uint16_t* Kb = (const uint16_t*)a.K + (int64_t)b * a.ks.b + (int64_t)g * a.ks.h;
+    const uint16_t* Vb = (const uint16_t*)a.V + (int64_t)b * a.vs.b + (int64_t)g * a.vs.h;
+    int koff[2], voff[2];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+        const int p = (2 * w + jj) * 64 + lane;
+        const int row = p >> 4, phys = p & 15;
+        koff[jj] = row * (int)a.ks.t + (phys ^ (row & 7)) * 8;
+        voff[jj] = row * (int)a.vs.t + phys * 8;
+    }
+    auto issue = [&](int it) {
+        const int e = it / tpc;
+        const int row0 = sm.erow[e] + (it - e * tpc) * KT;
+        const int s = it % NS;
+        const uint16_t* kp = Kb + (int64_t)row0 * a.ks.t;
+        const uint16_t* vp = Vb + (int64_t)row0 * a.vs.t;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+            lds_dma16(kp + koff[jj], __builtin_amdgcn_readfirstlane(lds_addr(&sm.kv[s][0][(2 * w + jj) * 64])));
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+            lds_dma16(vp + voff[jj], __builtin_amdgcn_readfirstlane(lds_addr(&sm.kv[s][1][(2 * w + jj) * 64])));
     };
 
     float m_run = -INFINITY, l_run = 0.f;     // this lane's query t = hd
@@ -157,23 +180,29 @@ __global__ __launch_bounds__(kThreads) void k_attn_bf16_d128_g4t2(AttnArgs a) {
         for (int e = 0; e < 8; ++e) acc[t][e] = 0.f;
     const int ps = lane & 15, kg = lane >> 4;
 
-    if (ntiles > 0) load_tile(0);
-    for (int it = 0; it < ntiles; ++it) {
-        const int bi = it & 1;
-        int c_cur, row_cur;
-        uint32_t m_cur;
-        tile_info(it, c_cur, row_cur, m_cur);
-        if (m_cur) store_tile(bi);
-        if (it + 1 < ntiles) load_tile(it + 1);
-        __syncthreads();
-        if (m_cur == 0) continue;
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s)
+        if (s < ntiles) issue(s);
 
-        // ---- logits ----
+    for (int it = 0; it < ntiles; ++it) {
+        // tile `it` has landed when at most the 4 loads of tile it + 1 are pending
+        if (it + 1 < ntiles) lds_dma_wait<4>();
+        else lds_dma_wait<0>();
+        raw_barrier();
+        // the stage computed in the previous iteration is free for tile it + 2
+        if (it + NS - 1 < ntiles) issue(it + NS - 1);
+
+        const uint32_t m_cur = sm.ebits[it / tpc];
+        if (m_cur == 0) continue;
+        const uint4* kb = sm.kv[it % NS][0];
+        const uint4* vb = sm.kv[it % NS][1];
+
+        // ---- logits of both queries ----
         float a0 = 0.f, a1 = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int ls = 8 * hd + ((i + 4 * hd) & 7);
-            const uint4 kv = kbuf[bi][j * 16 + (ls ^ (j & 7))];
+            const uint4 kv = kb[j * 16 + (ls ^ (j & 7))];
             a0 = dot2_bf16(qr[0][i].x, kv.x, a0);
             a0 = dot2_bf16(qr[0][i].y, kv.y, a0);
             a0 = dot2_bf16(qr[0][i].z, kv.z, a0);
@@ -185,47 +214,62 @@ __global__ __launch_bounds__(kThreads) void k_attn_bf16_d128_g4t2(AttnArgs a) {
         }
         const float send = hd ? a0 : a1;
         const float keep = hd ? a1 : a0;
-        float z = (keep + __shfl_xor(send, 1, kWave)) * a.scale_log2;
+        float z = (keep + dpp_xor1(send)) * a.scale_log2;
         if (!((m_cur >> hd) & 1u)) z = -INFINITY;
 
-        // ---- online softmax over this tile, per query t = lane parity ----
-        float cm = z;
+        // ---- online softmax; the running max moves only when a logit exceeds it ----
+        float p;
+        if (__builtin_amdgcn_ballot_w64(z > m_run) == 0ull) {
+            p = z == -INFINITY ? 0.f : exp2f(z - m_run);
+        } else {
+            float cm = z;
 #pragma unroll
-        for (int off = 2; off < kWave; off <<= 1) cm = fmaxf(cm, __shfl_xor(cm, off, kWave));
-        const float mn = fmaxf(m_run, cm);
-        const float alpha = mn == -INFINITY ? 1.f : exp2f(m_run - mn);
-        const float p = mn == -INFINITY ? 0.f : exp2f(z - mn);
-        l_run = l_run * alpha + p;
-        m_run = mn;
-        pbuf[w][lane] = p;   // = pbuf[w][2 * j + hd]
-        const float al0 = __shfl(alpha, 0, kWave);
-        const float al1 = __shfl(alpha, 1, kWave);
+            for (int off = 2; off < kWave; off <<= 1) cm = fmaxf(cm, __shfl_xor(cm, off, kWave));
+            const float mn = fmaxf(m_run, cm);
+            const float alpha = mn == -INFINITY ? 1.f : exp2f(m_run - mn);
+            p = mn == -INFINITY ? 0.f : exp2f(z - mn);
+            l_run *= alpha;
+            m_run = mn;
+            const float al0 = __shfl(alpha, 0, kWave);
+            const float al1 = __shfl(alpha, 1, kWave);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                acc[0][e] *= al0;
+                acc[1][e] *= al1;
+            }
+        }
+        // weights go to P.V as bf16; the row sum uses the same rounded weights
+        const uint32_t pb = f32_to_bf16_rne(p);
+        l_run += __uint_as_float(pb << 16);
+        reinterpret_cast<uint16_t*>(&sm.p16[w][(j >> 3) * 4 + (j & 3)][hd])[(j >> 2) & 1] = (uint16_t)pb;
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-        // ---- P.V ----
+        // ---- P.V: keys j1 = 8i + kg and j2 = j1 + 4 paired along the bf16 dot ----
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            acc[0][e] *= al0;
-            acc[1][e] *= al1;
-        }
+        for (int i = 0; i < 4; ++i) {
+            const int j1 = 8 * i + kg, j2 = j1 + 4;
+            const uint4 va = vb[j1 * 16 + ps];
+            const uint4 vc = vb[j2 * 16 + ps];
+            const uint2 pp = *reinterpret_cast<const uint2*>(&sm.p16[w][i * 4 + kg][0]);
+            const uint32_t av[4] = {va.x, va.y, va.z, va.w};
+            const uint32_t cv[4] = {vc.x, vc.y, vc.z, vc.w};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int jj = kg + 4 * i;
-            const uint4 vv = vbuf[bi][jj * 16 + ps];
-            const float2 pp = *reinterpret_cast<const float2*>(&pbuf[w][2 * jj]);
-            const float v[8] = {bf16_lo(vv.x), bf16_hi(vv.x), bf16_lo(vv.y), bf16_hi(vv.y),
-                                bf16_lo(vv.z), bf16_hi(vv.z), bf16_lo(vv.w), bf16_hi(vv.w)};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                acc[0][e] = fmaf(pp.x, v[e], acc[0][e]);
-                acc[1][e] = fmaf(pp.y, v[e], acc[1][e]);
+            for (int e = 0; e < 4; ++e) {
+                // (V[j1][d], V[j2][d]) for the even and the odd dim of this word
+                const uint32_t lo = __builtin_amdgcn_perm(cv[e], av[e], 0x05040100u);
+                const uint32_t hi = __builtin_amdgcn_perm(cv[e], av[e], 0x07060302u);
+                acc[0][2 * e] = dot2_bf16(pp.x, lo, acc[0][2 * e]);
+                acc[0][2 * e + 1] = dot2_bf16(pp.x, hi, acc[0][2 * e + 1]);
+                acc[1][2 * e] = dot2_bf16(pp.y, lo, acc[1][2 * e]);
+                acc[1][2 * e + 1] = dot2_bf16(pp.y, hi, acc[1][2 * e + 1]);
             }
         }
-        // pbuf is rewritten next tile only after every lane read it (program order)
+        // p16 is rewritten next tile only after every lane has read it
         __builtin_amdgcn_wave_barrier();
     }
+    lds_dma_wait<0>();
 
     // ---- combine lanes ----
 #pragma unroll
@@ -400,8 +444,9 @@ __global__ __launch_bounds__(kThreads) void k_attn_merge(AttnArgs a) {
     }
 }
 
-bool use_fast_path(dk_dtype dt, int D, int G, int T, int chunk) {
-    return dt == DK_BF16 && D == 128 && G == 4 && T == 2 && chunk % 32 == 0;
+bool use_fast_path(dk_dtype dt, int D, int G, int T, int chunk, dk_strides ks, dk_strides vs) {
+    return dt == DK_BF16 && D == 128 && G == 4 && T == 2 && chunk % 32 == 0 &&
+           ks.t < (1 << 26) && vs.t < (1 << 26);
 }
 
 }  // namespace
@@ -411,11 +456,15 @@ AttnPlan plan_attn(int B, int Hkv, int T, int Hq, int dv, int N, int chunk) {
     const int64_t bg = (int64_t)B * Hkv;
     const int R = (Hq / Hkv) * T;
     const int64_t tiles = (int64_t)N * ((chunk + 31) / 32);
-    int64_t want = (2048 + bg - 1) / bg;
-    int64_t by_work = tiles / 4;
+    // about two rounds of three resident blocks per CU, at least ~6 tiles per
+    // range, and never more entries per range than the fast path stages in LDS
+    int64_t want = (1536 + bg - 1) / bg;
+    int64_t by_work = tiles / 6;
     if (by_work < 1) by_work = 1;
     int64_t s = want < by_work ? want : by_work;
-    if (s > 64) s = 64;
+    const int64_t min_s = (N + kFastMaxEntries - 1) / kFastMaxEntries;
+    if (s < min_s) s = min_s;
+    if (s > 64 && min_s <= 64) s = 64;
     if (s < 1) s = 1;
     p.splits = (int)s;
     p.ws_bytes = s > 1 ? (size_t)(bg * s * R) * (size_t)(dv + 2) * 4 : 0;
@@ -440,7 +489,7 @@ hipError_t launch_attention(const float* q, int B, int T, int Hq, int Hkv, const
     a.part_acc = plan.splits > 1 ? (float*)ws : nullptr;
     a.part_ml = plan.splits > 1 ? (float*)ws + bg * plan.splits * R * D : nullptr;
     const unsigned grid = (unsigned)(bg * plan.splits);
-    if (use_fast_path(dt, D, a.G, T, chunk)) {
+    if (use_fast_path(dt, D, a.G, T, chunk, ks, vs)) {
         hipLaunchKernelGGL(k_attn_bf16_d128_g4t2, dim3(grid), dim3(kThreads), 0, st, a);
     } else if (dt == DK_BF16) {
         if (D == 128) hipLaunchKernelGGL((k_attn_generic<uint16_t, 128>), dim3(grid), dim3(kThreads), 0, st, a);

@@ -145,6 +145,8 @@ def test_gather_empty_is_ok():
 
 
 def test_attention_workspace_sizes():
-    # 64 x 8 (b, g) rows, 4 ranges each, 8 query rows of 128 values plus (m, l)
-    assert lib.dk_attn_workspace_size(64, 8, 2, 32, 128, 128, 32) == 64 * 8 * 4 * 8 * 130 * 4
+    # 64 x 8 (b, g) rows, 3 ranges each, 8 query rows of 128 values plus (m, l)
+    assert lib.dk_attn_workspace_size(64, 8, 2, 32, 128, 128, 32) == 64 * 8 * 3 * 8 * 130 * 4
+    # a single (b, g) with few entries: one range, no workspace
+    assert lib.dk_attn_workspace_size(1, 1, 2, 4, 128, 4, 32) == 0
     assert lib.dk_attn_workspace_size(64, 8, 2, 30, 128, 128, 32) == 0

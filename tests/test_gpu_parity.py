@@ -285,7 +285,7 @@ def run_attention(dkb, w, seed, mutate=None):
     ("llama8b_l32k", 2, 4096, dict(Hq=64)),                      # G = 8 (generic)
     ("llama8b_l32k", 2, 4096, dict(d=64)),                       # d = 64 bf16 (generic)
     ("llama8b_l32k", 2, 4096, dict(chunk=16, k=64)),             # chunk 16 bf16 (generic)
-    ("tiny", None, None, dict(Hq=8, Hkv=2, B=3)),                # fp32, several (b, g)
+    ("tiny", 3, None, dict(Hq=8, Hkv=2)),                     # fp32, several (b, g)
 ])
 def test_attention(dkb, name, B, L, kw):
     run_attention(dkb, workload(name, B, L, **kw), 31)
