@@ -6,7 +6,8 @@ A step is one pass of the whole hot path over every layer of the workload: per
 layer, chunk scores and top-k of both queries (dk_score_topk), their union
 (dk_union_select) and attention of both queries over their own chunks, read
 once per union chunk straight from the HBM pool (dk_sparse_decode_attn).
-Landmarks are built once before timing (they are fixed for the whole decode).
+Landmarks (and their fp16 shadow) are built once before timing: they are fixed
+for the whole decode.
 Inputs are seeded synthetic tensors resident in HBM before the timed region.
 
 Prints one JSON line.  `roofline` covers the kernel family that takes the most
@@ -39,6 +40,8 @@ def parse():
                     help="CPU oracle sample budget (0 disables the CPU baseline)")
     ap.add_argument("--no-events", action="store_true",
                     help="time only whole steps (no per-call events inside the step)")
+    ap.add_argument("--no-shadow", action="store_true",
+                    help="score from the fp32 landmarks only (no fp16 landmark shadow)")
     return ap.parse_args()
 
 
@@ -104,7 +107,9 @@ def main():
     qs = [synth.make_queries(w, args.seed, layer=l, device=dev) for l in range(w.layers)]
     K, V = synth.make_kv_pool(w, args.seed, device=dev, q0=qs[0])
     lm = dkb.build_landmarks(K, w.chunk)
-    st = dkb.DecodeStep(w.B, w.T, w.Hq, w.Hkv, w.d, w.C, w.chunk, w.k, w.scale, dev, want_scores=False)
+    shadow = None if args.no_shadow else dkb.build_landmark_shadow(lm)
+    st = dkb.DecodeStep(w.B, w.T, w.Hq, w.Hkv, w.d, w.C, w.chunk, w.k, w.scale, dev, want_scores=False,
+                        shadow=shadow)
     torch.cuda.synchronize()
     print(f"[bench] inputs ready in {time.time() - t0:.1f} s: pool {2 * K.nbytes / 1e9:.2f} GB, "
           f"landmarks {lm.nbytes / 1e9:.3f} GB", file=sys.stderr, flush=True)
@@ -134,7 +139,8 @@ def main():
             e = ev[record - 1][l] if record else None
             if record:
                 e[0].record()
-            dkb.score_topk(q, lm, w.k, w.scale, dkb.DK_REDUCE_MEAN, st.topk_idx, None, st.ws_topk)
+            dkb.score_topk(q, lm, w.k, w.scale, dkb.DK_REDUCE_MEAN, st.topk_idx, None, st.ws_topk,
+                           shadow=shadow)
             if record:
                 e[1].record()
             dkb.union_select(st.topk_idx, w.C, st.union_ids, st.member, st.count, st.overlap)
@@ -165,8 +171,16 @@ def main():
 
     kernels = {}
     n_launch = args.steps * w.layers
+    q_bytes = w.B * w.T * w.Hq * w.d * 4
+    if shadow is None:
+        score_bytes = lm_bytes_layer + q_bytes
+    else:
+        # fp16 landmarks + the fp32 scores written and read back + at least k fp32
+        # landmark rows re-scored per (b, g, t)
+        score_bytes = (lm_bytes_layer // 2 + 2 * w.B * w.Hkv * w.T * w.C * 4
+                       + w.B * w.Hkv * w.T * w.k * w.d * 4 + q_bytes)
     per_call_bytes = {
-        "score_topk": lm_bytes_layer + w.B * w.T * w.Hq * w.d * 4,
+        "score_topk": score_bytes,
         "union_select": w.B * w.Hkv * w.T * w.k * 4 * 3,
         "sparse_decode_attn": sel_bytes_step / w.layers,
     }
@@ -201,7 +215,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "L": w.L, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d,
-                   "chunk": w.chunk, "k": w.k, "T": w.T, "layers": w.layers, "seed": args.seed},
+                   "chunk": w.chunk, "k": w.k, "T": w.T, "layers": w.layers, "seed": args.seed,
+                   "landmark_shadow": shadow is not None},
         "selected_kv_GBps": round(sel_gbps, 1),
         "selected_kv_frac_hbm_peak": round(sel_gbps / HBM_PEAK_GBPS, 4),
         "selected_kv_bytes_per_step": int(sel_bytes_step),

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define DK_ABI_VERSION 1
+#define DK_ABI_VERSION 2
 
 typedef enum {
     DK_OK = 0,
@@ -89,6 +89,34 @@ dk_status dk_build_landmarks(const void* K, dk_dtype k_dtype, dk_strides ks,
                              float* lm, void* stream);
 
 /*
+ * Landmark shadow: an fp16 copy of the landmarks plus, per (b, g), an upper
+ * bound of the largest landmark norm.  It lets dk_score_topk stream half the
+ * landmark bytes and still return exactly the k chunks that scoring with the
+ * fp32 landmarks returns: every chunk whose shadow score is within a proven
+ * error bound of the k-th shadow score is re-scored from the fp32 landmarks
+ * before the final selection.  Made once per pool by dk_build_landmark_shadow.
+ */
+typedef struct {
+    const uint16_t* lm16;     /* fp16 landmarks [B, Hkv, C, d], contiguous   */
+    const float*    norm_max; /* [B, Hkv]: >= max_c ||lm[b, g, c, :]||_2, or +inf */
+} dk_landmark_shadow;
+
+/*
+ * dk_build_landmark_shadow - fp16 copy and norm bound of fp32 landmarks.
+ *
+ * lm       : fp32 landmarks, rows [B, Hkv, C] of d, strides ls (as written by
+ *            dk_build_landmarks).
+ * lm16     : out, fp16 [B, Hkv, C, d] contiguous, round-to-nearest-even.
+ * norm_max : out, fp32 [B, Hkv]; +inf when a landmark does not fit fp16 (the
+ *            scoring then re-scores every chunk of that (b, g) exactly).
+ * Errors   : DK_ERR_INVALID_ARG unless sizes >= 1 and pointers non-NULL;
+ *            DK_ERR_UNSUPPORTED unless d is 64 or 128 and the 16-byte alignment
+ *            rule holds.
+ */
+dk_status dk_build_landmark_shadow(const float* lm, dk_strides ls, int B, int Hkv, int C, int d,
+                                   uint16_t* lm16, float* norm_max, void* stream);
+
+/*
  * dk_score_topk - chunk scores of both queries and each query's k best chunks.
  *
  * DualDecoder "4.1": the retrieval index of a step comes from the current query
@@ -103,20 +131,24 @@ dk_status dk_build_landmarks(const void* K, dk_dtype k_dtype, dk_strides ks,
  * q          : fp32 [B, T, Hq, d] contiguous; query head h belongs to KV head h / (Hq/Hkv).
  * lm         : landmarks, lm_dtype (v1: DK_F32), rows [B, Hkv, C] of d, strides ls.
  * reduce     : DK_REDUCE_MEAN (mean over the group's heads) or DK_REDUCE_MAX.
+ * shadow     : the landmarks' shadow (see above) or NULL.  With a shadow the
+ *              result is the same; the call reads about half the bytes.
  * topk_idx   : out, int32 [B, Hkv, T, k].
  * topk_score : out, fp32 [B, Hkv, T, k] (the selected scores, same order) or NULL.
- * ws         : workspace of dk_score_topk_workspace_size(B, Hkv, T, C, k) bytes
- *              (may be NULL when that size is 0).  Contents on entry are ignored.
+ * ws         : workspace of dk_score_topk_workspace_size(B, Hkv, T, C, k,
+ *              shadow != NULL) bytes (may be NULL when that size is 0).
+ *              Contents on entry are ignored.
  * Errors     : DK_ERR_INVALID_ARG unless 1 <= T <= 2, Hq % Hkv == 0, 1 <= k <= C,
  *              pointers non-NULL and ws_bytes large enough; DK_ERR_UNSUPPORTED
- *              unless lm_dtype == DK_F32, d is 64 or 128, C <= 65536, the number
- *              of query vectors (T for mean, G*T for max) is at most 16 and
- *              the 16-byte alignment rule holds.
+ *              unless lm_dtype == DK_F32, d is 64 or 128, C <= 65536 (C <= 6144
+ *              with a shadow), the number of query vectors (T for mean, G*T for
+ *              max) is at most 16 and the 16-byte alignment rule holds.
  */
-size_t dk_score_topk_workspace_size(int B, int Hkv, int T, int C, int k);
+size_t dk_score_topk_workspace_size(int B, int Hkv, int T, int C, int k, int with_shadow);
 dk_status dk_score_topk(const float* q, int B, int T, int Hq,
                         const void* lm, dk_dtype lm_dtype, dk_strides ls, int Hkv, int C, int d,
                         int k, float scale, dk_group_reduce reduce,
+                        const dk_landmark_shadow* shadow,
                         int32_t* topk_idx, float* topk_score,
                         void* ws, size_t ws_bytes, void* stream);
 

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libdualkv.so")
 DK_OK, DK_ERR_INVALID_ARG, DK_ERR_UNSUPPORTED, DK_ERR_HIP = 0, 1, 2, 3
 DK_F32, DK_BF16 = 0, 1
 DK_REDUCE_MEAN, DK_REDUCE_MAX = 0, 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 _STATUS = {0: "DK_OK", 1: "DK_ERR_INVALID_ARG", 2: "DK_ERR_UNSUPPORTED", 3: "DK_ERR_HIP"}
 
@@ -34,6 +34,10 @@ class DualKVError(RuntimeError):
 
 class dk_strides(ctypes.Structure):
     _fields_ = [("b", ctypes.c_int64), ("h", ctypes.c_int64), ("t", ctypes.c_int64)]
+
+
+class dk_landmark_shadow(ctypes.Structure):
+    _fields_ = [("lm16", ctypes.c_void_p), ("norm_max", ctypes.c_void_p)]
 
 
 class dk_cache_plan(ctypes.Structure):
@@ -49,8 +53,10 @@ EXPORTS = [
     ("dk_abi_version", ctypes.c_int, []),
     ("dk_last_error", ctypes.c_char_p, []),
     ("dk_build_landmarks", _I, [_P, _I, _S, _I, _I, _I, _I, _I, _P, _P]),
-    ("dk_score_topk_workspace_size", _Z, [_I, _I, _I, _I, _I]),
-    ("dk_score_topk", _I, [_P, _I, _I, _I, _P, _I, _S, _I, _I, _I, _I, _F, _I, _P, _P, _P, _Z, _P]),
+    ("dk_build_landmark_shadow", _I, [_P, _S, _I, _I, _I, _I, _P, _P, _P]),
+    ("dk_score_topk_workspace_size", _Z, [_I, _I, _I, _I, _I, _I]),
+    ("dk_score_topk", _I, [_P, _I, _I, _I, _P, _I, _S, _I, _I, _I, _I, _F, _I,
+                           ctypes.POINTER(dk_landmark_shadow), _P, _P, _P, _Z, _P]),
     ("dk_union_select", _I, [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, ctypes.POINTER(dk_cache_plan), _P]),
     ("dk_gather_kv", _I, [_P, _P, _I, _S, _I, _I, _I, _I, _P, _P, _P, _I, _I, _P, _P, _S, _I, _I, _P]),
     ("dk_attn_workspace_size", _Z, [_I, _I, _I, _I, _I, _I, _I]),
@@ -129,12 +135,32 @@ def build_landmarks(K: torch.Tensor, chunk: int, lm: torch.Tensor | None = None,
     return lm
 
 
-def score_topk_workspace_size(B, Hkv, T, C, k) -> int:
-    return int(lib.dk_score_topk_workspace_size(B, Hkv, T, C, k))
+@dataclass
+class Shadow:
+    """fp16 copy of the landmarks and the per-(b, g) norm bound (dk_landmark_shadow)."""
+    lm16: torch.Tensor       # [B, Hkv, C, d] float16
+    norm_max: torch.Tensor   # [B, Hkv] float32
+
+    def as_c(self) -> dk_landmark_shadow:
+        return dk_landmark_shadow(self.lm16.data_ptr(), self.norm_max.data_ptr())
+
+
+def build_landmark_shadow(lm: torch.Tensor, stream=None) -> Shadow:
+    B, H, C, d = lm.shape
+    sh = Shadow(torch.empty(B, H, C, d, dtype=torch.float16, device=lm.device),
+                torch.empty(B, H, dtype=torch.float32, device=lm.device))
+    _check(lib.dk_build_landmark_shadow(_ptr(lm), pool_strides(lm), B, H, C, d, _ptr(sh.lm16),
+                                        _ptr(sh.norm_max), _stream(stream)))
+    return sh
+
+
+def score_topk_workspace_size(B, Hkv, T, C, k, with_shadow=False) -> int:
+    return int(lib.dk_score_topk_workspace_size(B, Hkv, T, C, k, int(bool(with_shadow))))
 
 
 def score_topk(q: torch.Tensor, lm: torch.Tensor, k: int, scale: float, reduce: int = DK_REDUCE_MEAN,
-               topk_idx=None, topk_score=None, ws=None, want_scores=True, stream=None):
+               topk_idx=None, topk_score=None, ws=None, want_scores=True, shadow: Shadow | None = None,
+               stream=None):
     B, T, Hq, d = q.shape
     _, Hkv, C, _ = lm.shape
     _need(q, torch.float32, (B, T, Hq, d), "q")
@@ -142,12 +168,14 @@ def score_topk(q: torch.Tensor, lm: torch.Tensor, k: int, scale: float, reduce: 
         topk_idx = torch.empty(B, Hkv, T, k, dtype=torch.int32, device=q.device)
     if topk_score is None and want_scores:
         topk_score = torch.empty(B, Hkv, T, k, dtype=torch.float32, device=q.device)
-    nbytes = score_topk_workspace_size(B, Hkv, T, C, k)
+    nbytes = score_topk_workspace_size(B, Hkv, T, C, k, shadow is not None)
     if ws is None and nbytes:
         ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    csh = ctypes.byref(shadow.as_c()) if shadow is not None else None
     _check(lib.dk_score_topk(_ptr(q), B, T, Hq, _ptr(lm), _dtype(lm), pool_strides(lm), Hkv, C, d, k,
-                             float(scale), int(reduce), _ptr(topk_idx), _ptr(topk_score), _ptr(ws),
-                             0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+                             float(scale), int(reduce), csh, _ptr(topk_idx), _ptr(topk_score),
+                             _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                             _stream(stream)))
     return topk_idx, topk_score
 
 
@@ -268,14 +296,15 @@ class DecodeStep:
     """
 
     def __init__(self, B, T, Hq, Hkv, d, C, chunk, k, scale, device, reduce=DK_REDUCE_MEAN,
-                 want_scores=True):
+                 want_scores=True, shadow: Shadow | None = None):
         self.B, self.T, self.Hq, self.Hkv, self.d, self.C = B, T, Hq, Hkv, d, C
         self.chunk, self.k, self.scale, self.reduce = chunk, k, scale, reduce
         i32 = dict(dtype=torch.int32, device=device)
         self.topk_idx = torch.empty(B, Hkv, T, k, **i32)
         self.topk_score = torch.empty(B, Hkv, T, k, dtype=torch.float32, device=device) \
             if want_scores else None
-        n = score_topk_workspace_size(B, Hkv, T, C, k)
+        self.shadow = shadow
+        n = score_topk_workspace_size(B, Hkv, T, C, k, shadow is not None)
         self.ws_topk = torch.empty(max(n, 1), dtype=torch.uint8, device=device)
         self.union_ids = torch.empty(B, Hkv, T * k, **i32)
         self.member = torch.empty(B, Hkv, T * k, dtype=torch.uint8, device=device)
@@ -288,7 +317,7 @@ class DecodeStep:
 
     def run(self, q, lm, K, V, stream=None):
         score_topk(q, lm, self.k, self.scale, self.reduce, self.topk_idx, self.topk_score,
-                   self.ws_topk, stream=stream)
+                   self.ws_topk, shadow=self.shadow, stream=stream)
         union_select(self.topk_idx, self.C, self.union_ids, self.member, self.count, self.overlap,
                      stream=stream)
         sparse_decode_attn(q, K, V, self.union_ids, self.member, self.count, self.chunk, self.scale,

@@ -67,15 +67,29 @@ dk_status dk_build_landmarks(const void* K, dk_dtype k_dtype, dk_strides ks, int
     return e == hipSuccess ? DK_OK : hip_fail(e, "dk_build_landmarks");
 }
 
-size_t dk_score_topk_workspace_size(int B, int Hkv, int T, int C, int k) {
+dk_status dk_build_landmark_shadow(const float* lm, dk_strides ls, int B, int Hkv, int C, int d,
+                                   uint16_t* lm16, float* norm_max, void* stream) {
+    g_err.clear();
+    DK_REQUIRE(lm && lm16 && norm_max, DK_ERR_INVALID_ARG,
+               "dk_build_landmark_shadow: lm, lm16, norm_max must be non-NULL");
+    DK_REQUIRE(B >= 1 && Hkv >= 1 && C >= 1 && d >= 1, DK_ERR_INVALID_ARG,
+               "dk_build_landmark_shadow: B, Hkv, C, d must be >= 1");
+    DK_REQUIRE(d == 64 || d == 128, DK_ERR_UNSUPPORTED, "dk_build_landmark_shadow: d must be 64 or 128");
+    DK_REQUIRE(aligned16(lm) && aligned16(lm16) && strides_ok(ls, 4), DK_ERR_UNSUPPORTED,
+               "dk_build_landmark_shadow: lm, lm16 and lm's strides must be 16-byte aligned");
+    hipError_t e = dk::launch_build_shadow(lm, ls, B, Hkv, C, d, lm16, norm_max, (hipStream_t)stream);
+    return e == hipSuccess ? DK_OK : hip_fail(e, "dk_build_landmark_shadow");
+}
+
+size_t dk_score_topk_workspace_size(int B, int Hkv, int T, int C, int k, int with_shadow) {
     if (B < 1 || Hkv < 1 || T < 1 || T > 2 || k < 1 || C < k) return 0;
-    return dk::plan_topk(B, Hkv, T, C, k).ws_bytes;
+    return dk::plan_topk(B, Hkv, T, C, k, with_shadow != 0).ws_bytes;
 }
 
 dk_status dk_score_topk(const float* q, int B, int T, int Hq, const void* lm, dk_dtype lm_dtype,
                         dk_strides ls, int Hkv, int C, int d, int k, float scale,
-                        dk_group_reduce reduce, int32_t* topk_idx, float* topk_score, void* ws,
-                        size_t ws_bytes, void* stream) {
+                        dk_group_reduce reduce, const dk_landmark_shadow* shadow, int32_t* topk_idx,
+                        float* topk_score, void* ws, size_t ws_bytes, void* stream) {
     g_err.clear();
     DK_REQUIRE(q && lm && topk_idx, DK_ERR_INVALID_ARG, "dk_score_topk: q, lm, topk_idx must be non-NULL");
     DK_REQUIRE(B >= 1 && Hq >= 1 && Hkv >= 1 && C >= 1 && d >= 1, DK_ERR_INVALID_ARG,
@@ -86,6 +100,8 @@ dk_status dk_score_topk(const float* q, int B, int T, int Hq, const void* lm, dk
     DK_REQUIRE(reduce == DK_REDUCE_MEAN || reduce == DK_REDUCE_MAX, DK_ERR_INVALID_ARG,
                "dk_score_topk: unknown reduce %d", (int)reduce);
     DK_REQUIRE(std::isfinite(scale), DK_ERR_INVALID_ARG, "dk_score_topk: scale must be finite");
+    DK_REQUIRE(!shadow || (shadow->lm16 && shadow->norm_max), DK_ERR_INVALID_ARG,
+               "dk_score_topk: shadow->lm16 and shadow->norm_max must be non-NULL");
     DK_REQUIRE(lm_dtype == DK_F32, DK_ERR_UNSUPPORTED, "dk_score_topk: landmarks must be DK_F32");
     DK_REQUIRE(d == 64 || d == 128, DK_ERR_UNSUPPORTED, "dk_score_topk: d must be 64 or 128 (got %d)", d);
     DK_REQUIRE(C <= 65536, DK_ERR_UNSUPPORTED, "dk_score_topk: C must be <= 65536 (got %d)", C);
@@ -95,14 +111,15 @@ dk_status dk_score_topk(const float* q, int B, int T, int Hq, const void* lm, dk
         DK_REQUIRE(nq <= 16 && (nq & (nq - 1)) == 0, DK_ERR_UNSUPPORTED,
                    "dk_score_topk: max reduction needs G*T a power of two <= 16 (got %d)", nq);
     }
-    DK_REQUIRE(aligned16(q) && aligned16(lm) && strides_ok(ls, 4), DK_ERR_UNSUPPORTED,
-               "dk_score_topk: q, lm and lm's strides must be 16-byte aligned");
-    const dk::TopkPlan plan = dk::plan_topk(B, Hkv, T, C, k);
-    DK_REQUIRE(plan.splits > 0, DK_ERR_UNSUPPORTED, "dk_score_topk: no split plan for C=%d k=%d", C, k);
+    DK_REQUIRE(aligned16(q) && aligned16(lm) && strides_ok(ls, 4) && (!shadow || aligned16(shadow->lm16)),
+               DK_ERR_UNSUPPORTED, "dk_score_topk: q, lm, lm's strides and lm16 must be 16-byte aligned");
+    const dk::TopkPlan plan = dk::plan_topk(B, Hkv, T, C, k, shadow != nullptr);
+    DK_REQUIRE(plan.splits > 0, DK_ERR_UNSUPPORTED, "dk_score_topk: no plan for C=%d k=%d%s", C, k,
+               shadow ? " with a shadow (C <= 6144)" : "");
     DK_REQUIRE(ws_bytes >= plan.ws_bytes && (plan.ws_bytes == 0 || ws), DK_ERR_INVALID_ARG,
                "dk_score_topk: workspace needs %zu bytes (got %zu)", plan.ws_bytes, ws_bytes);
     hipError_t e = dk::launch_score_topk(q, B, T, Hq, (const float*)lm, ls, Hkv, C, d, k, scale, reduce,
-                                         topk_idx, topk_score, ws, plan, (hipStream_t)stream);
+                                         shadow, topk_idx, topk_score, ws, plan, (hipStream_t)stream);
     return e == hipSuccess ? DK_OK : hip_fail(e, "dk_score_topk");
 }
 

@@ -144,11 +144,13 @@ struct TopkPlan {
     int rows;          // chunks per split (last split may have fewer)
     size_t ws_bytes;   // candidate buffer bytes (0 when splits == 1)
 };
-TopkPlan plan_topk(int B, int Hkv, int T, int C, int k);
+TopkPlan plan_topk(int B, int Hkv, int T, int C, int k, bool shadow);
 hipError_t launch_score_topk(const float* q, int B, int T, int Hq, const float* lm, dk_strides ls,
                              int Hkv, int C, int d, int k, float scale, dk_group_reduce reduce,
-                             int32_t* topk_idx, float* topk_score, void* ws, const TopkPlan& plan,
-                             hipStream_t st);
+                             const dk_landmark_shadow* shadow, int32_t* topk_idx, float* topk_score,
+                             void* ws, const TopkPlan& plan, hipStream_t st);
+hipError_t launch_build_shadow(const float* lm, dk_strides ls, int B, int Hkv, int C, int d,
+                               uint16_t* lm16, float* norm_max, hipStream_t st);
 
 hipError_t launch_union(const int32_t* topk_idx, int B, int Hkv, int T, int k, int C,
                         int32_t* union_ids, uint8_t* member, int32_t* union_count, int32_t* overlap,

@@ -29,23 +29,77 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxRows = 4096;       // landmark rows per range (LDS: T * 16 KiB)
 constexpr int kMaxCand = 8192;       // candidates per (b, g, t) in the merge
+constexpr int kShadowMaxC = 6144;    // chunks per (b, g) with a shadow (pass-2 LDS <= 64 KiB)
 
-// Select the k largest keys of keys[0..n) (k <= n), ties to the lower position,
-// and call emit(j, position, key) for j = 0..k-1 in ascending position order.
-// Uses `hist` (256 uint), `scratch` (>= 5 int) and `bc` (2 int) of LDS.  Every
-// thread of the block must call it.
-template <typename Emit>
-__device__ void block_topk(const uint32_t* keys, int n, int k, uint32_t* hist, int* scratch,
-                           int* bc, Emit emit) {
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// streamed once: non-temporal 16-byte loads
+__device__ __forceinline__ float4 nt_load_f4(const float* p) {
+    const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ u32x4_t nt_load_u4(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+__device__ __forceinline__ uint32_t f16_bits(float x) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+}
+// a.lo*b.lo + a.hi*b.hi + c in fp32 (v_dot2_f32_f16; fp16 products are exact in fp32)
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c,
+                                  false);
+}
+// sum over the aligned group of LPR (8 or 16) lanes, every lane gets the total
+template <int LPR>
+__device__ __forceinline__ float dpp_group_sum(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+    if constexpr (LPR == 8) {
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+    } else {
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+    }
+    return v;
+}
+
+// The k-th largest of keys[0..n) (1 <= k <= n) by an 8-bit radix select; also
+// returns how many of the keys equal to it belong to the k largest (*need).
+// Uses `hist` (256 uint) and `bc` (2 int) of LDS.  Every thread must call it.
+__device__ uint32_t block_kth_key(const uint32_t* keys, int n, int k, uint32_t* hist, int* bc,
+                                  int* need_out) {
     const int tid = threadIdx.x;
     uint32_t prefix = 0, pmask = 0;
     int need = k;
     for (int shift = 24; shift >= 0; shift -= 8) {
         for (int i = tid; i < 256; i += kThreads) hist[i] = 0;
         __syncthreads();
-        for (int i = tid; i < n; i += kThreads) {
-            uint32_t key = keys[i];
-            if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+        if (shift == 24) {
+            // The top byte (sign and high exponent bits) takes few distinct values
+            // within a wave: add one count per distinct digit instead of one LDS
+            // atomic per key on the same few bins.
+            const int lane = tid & (kWave - 1);
+            for (int i0 = 0; i0 < n; i0 += kThreads) {
+                const int i = i0 + tid;
+                bool active = i < n;
+                const uint32_t digit = active ? keys[i] >> 24 : 0u;
+                uint64_t act = __builtin_amdgcn_ballot_w64(active);
+                while (act) {
+                    const int leader = (int)__builtin_ctzll(act);
+                    const uint32_t ld = (uint32_t)__builtin_amdgcn_readlane((int)digit, leader);
+                    const uint64_t same = __builtin_amdgcn_ballot_w64(active && digit == ld);
+                    if (lane == leader) atomicAdd(&hist[ld], (uint32_t)__builtin_popcountll(same));
+                    act &= ~same;
+                    active = active && digit != ld;
+                }
+            }
+        } else {
+            for (int i = tid; i < n; i += kThreads) {
+                uint32_t key = keys[i];
+                if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+            }
         }
         __syncthreads();
         if (tid < kWave) {
@@ -74,7 +128,100 @@ __device__ void block_topk(const uint32_t* keys, int n, int k, uint32_t* hist, i
         pmask |= 0xffu << shift;
         need = bc[1];
     }
-    const uint32_t thr = prefix;
+    *need_out = need;
+    return prefix;
+}
+
+// ---------------------------------------------------------------------------
+// Wave-level selection over at most 256 keys held 4 per lane (value v of lane l
+// is position l + 64 v).  No block barriers: one wave owns the work and a
+// 256-bin histogram in LDS.
+// ---------------------------------------------------------------------------
+// inclusive prefix sum over the wave (DPP row shifts, then row broadcasts)
+__device__ __forceinline__ int wave_prefix_sum(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);   // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    return v;
+}
+
+// The k-th largest of up to 256 keys held 4 per lane (1 <= k <= number of keys;
+// unused slots hold 0, below every real key) by a bitwise search over the key
+// space with wave-wide ballot counts; also how many keys equal to it are among
+// the k largest.  No LDS, no barriers.
+__device__ uint32_t wave_kth_key_bisect(const uint32_t (&x)[4], int k, int* need_out) {
+    uint32_t r = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t c = r | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(x[v] >= c));
+        if (cnt >= k) r = c;
+    }
+    int greater = 0;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) greater += __builtin_popcountll(__builtin_amdgcn_ballot_w64(x[v] > r));
+    *need_out = k - greater;
+    return r;
+}
+
+// The k-th largest of the keys (1 <= k <= number of non-zero keys; empty slots
+// hold 0) and how many keys equal to it belong to the k largest.
+__device__ uint32_t wave_kth_key(const uint32_t (&x)[4], int k, uint32_t* hist, int* need_out) {
+    const int lane = threadIdx.x & (kWave - 1);
+    uint32_t prefix = 0, pmask = 0;
+    int need = k;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        reinterpret_cast<uint4*>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            if ((x[v] & pmask) == prefix) atomicAdd(&hist[(x[v] >> shift) & 255u], 1u);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // lane l owns digits 255 - 4l - j, j = 0..3 (descending), so the count of
+        // keys above its digits is the exclusive prefix over lanes below it
+        const uint4 h4 = reinterpret_cast<const uint4*>(hist)[63 - lane];
+        const int c[4] = {(int)h4.w, (int)h4.z, (int)h4.y, (int)h4.x};
+        const int tot = c[0] + c[1] + c[2] + c[3];
+        int above = wave_prefix_sum(tot) - tot;
+        int digit = -1, nneed = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (above < need && need <= above + c[j]) {
+                digit = 255 - 4 * lane - j;
+                nneed = need - above;
+            }
+            above += c[j];
+        }
+        const uint64_t found = __builtin_amdgcn_ballot_w64(digit >= 0);
+        const int src = (int)__builtin_ctzll(found);
+        digit = __builtin_amdgcn_readlane(digit, src);
+        need = __builtin_amdgcn_readlane(nneed, src);
+        prefix |= (uint32_t)digit << shift;
+        pmask |= 0xffu << shift;
+        __builtin_amdgcn_wave_barrier();
+    }
+    *need_out = need;
+    return prefix;
+}
+
+// Select the k largest keys of keys[0..n) (k <= n), ties to the lower position,
+// and call emit(j, position, key) for j = 0..k-1 in ascending position order.
+// Uses `hist` (256 uint), `scratch` (>= 5 int) and `bc` (2 int) of LDS.  Every
+// thread of the block must call it.
+template <typename Emit>
+__device__ void block_topk(const uint32_t* keys, int n, int k, uint32_t* hist, int* scratch,
+                           int* bc, Emit emit) {
+    const int tid = threadIdx.x;
+    int need;
+    const uint32_t thr = block_kth_key(keys, n, k, hist, bc, &need);
     // keys > thr are all taken; of the keys == thr, the `need` lowest positions.
     const int per = (n + kThreads - 1) / kThreads;
     const int lo = min(n, tid * per), hi = min(n, lo + per);
@@ -173,8 +320,7 @@ __global__ __launch_bounds__(kThreads) void k_score_split(
             const float* p = base + (int64_t)(ok ? rr[u] : 0) * ls.t;
 #pragma unroll
             for (int i = 0; i < S::NLD; ++i)
-                x[u][i] = ok ? *reinterpret_cast<const float4*>(p + i * 4 * S::LPR)
-                             : make_float4(0.f, 0.f, 0.f, 0.f);
+                x[u][i] = ok ? nt_load_f4(p + i * 4 * S::LPR) : make_float4(0.f, 0.f, 0.f, 0.f);
         }
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
@@ -267,6 +413,355 @@ __global__ __launch_bounds__(kThreads) void k_topk_merge(const uint32_t* __restr
     }
 }
 
+// ---------------------------------------------------------------------------
+// Landmark shadow: fp16 copy (round to nearest even) and a per-(b, g) upper
+// bound of the largest landmark norm.  One block per (b, g).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_build_shadow(const float* __restrict__ lm, dk_strides ls,
+                                                          int Hkv, int C, uint16_t* __restrict__ lm16,
+                                                          float* __restrict__ norm_max) {
+    constexpr int TPR = D / 4;                 // threads per row, one float4 each
+    constexpr int RPB = kThreads / TPR;        // rows per block pass
+    __shared__ float smax[kThreads / kWave];
+    __shared__ int sinf;
+    const int bg = blockIdx.x;
+    const int b = bg / Hkv, g = bg - b * Hkv;
+    const int tr = threadIdx.x / TPR, part = threadIdx.x % TPR;
+    if (threadIdx.x == 0) sinf = 0;
+    __syncthreads();
+    float vmax = 0.f;
+    bool overflow = false;
+    const float* base = lm + (int64_t)b * ls.b + (int64_t)g * ls.h + part * 4;
+    uint16_t* obase = lm16 + (int64_t)bg * C * D + part * 4;
+    for (int r0 = 0; r0 < C; r0 += RPB) {
+        const int r = r0 + tr;
+        float ss = 0.f;
+        if (r < C) {
+            const float4 x = *reinterpret_cast<const float4*>(base + (int64_t)r * ls.t);
+            const uint32_t h0 = f16_bits(x.x), h1 = f16_bits(x.y), h2 = f16_bits(x.z), h3 = f16_bits(x.w);
+            // an fp16 infinity (or NaN) means the shadow cannot bound this (b, g)
+            overflow |= (h0 & 0x7c00u) == 0x7c00u || (h1 & 0x7c00u) == 0x7c00u ||
+                        (h2 & 0x7c00u) == 0x7c00u || (h3 & 0x7c00u) == 0x7c00u;
+            *reinterpret_cast<uint2*>(obase + (int64_t)r * D) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+            ss = x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
+        }
+        // squared norm of the row: sum over its TPR threads (aligned lane groups)
+        for (int off = 1; off < TPR; off <<= 1) ss += __shfl_xor(ss, off, kWave);
+        vmax = fmaxf(vmax, ss);
+    }
+    if (overflow) sinf = 1;
+    for (int off = 1; off < kWave; off <<= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, off, kWave));
+    if ((threadIdx.x & (kWave - 1)) == 0) smax[threadIdx.x / kWave] = vmax;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float m = 0.f;
+        for (int w = 0; w < kThreads / kWave; ++w) m = fmaxf(m, smax[w]);
+        // sum of D squares and a square root in fp32: relative error below (D + 4) u
+        const float bound = sqrtf(m) * (1.0f + (float)(D + 8) * 5.9604645e-8f);
+        norm_max[bg] = sinf ? INFINITY : bound;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Shadow pass 1: fp16 scores of every chunk, streamed with non-temporal 16-byte
+// loads; LPR = D / 8 lanes per row, 8 fp16 dims per lane; the row sums use DPP
+// only.  Scores of one block's rows are staged in LDS and stored coalesced to
+// s_lo [B * Hkv, T, C] (fp32).
+// ---------------------------------------------------------------------------
+template <int D, int NQ, int T, bool MAXRED>
+__global__ __launch_bounds__(kThreads) void k_score_lo(const float* __restrict__ q, int Hq,
+                                                      const uint16_t* __restrict__ lm16, int Hkv, int C,
+                                                      float scale, int rows_per_block, int blocks_per_bg,
+                                                      float* __restrict__ s_lo) {
+    constexpr int LPR = D / 8, RPW = kWave / LPR, U = 8;
+    constexpr int G = MAXRED ? NQ / T : 0;
+    extern __shared__ float sres[];    // [T][rows_per_block]
+    const int blk = blockIdx.x % blocks_per_bg;
+    const int bg = blockIdx.x / blocks_per_bg;
+    const int b = bg / Hkv, g = bg - b * Hkv;
+    const int row0 = blk * rows_per_block;
+    const int nrows = min(rows_per_block, C - row0);
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int rp = lane / LPR, part = lane % LPR;
+    const int Gq = Hq / Hkv;
+
+    uint32_t qh[NQ][4];
+#pragma unroll
+    for (int v = 0; v < NQ; ++v) {
+        float x[8];
+        if constexpr (MAXRED) {
+            const float* src = q + (((int64_t)b * T + v / G) * Hq + g * Gq + v % G) * D + part * 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = src[e];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = 0.f;
+            for (int h = 0; h < Gq; ++h) {
+                const float* src = q + (((int64_t)b * T + v) * Hq + g * Gq + h) * D + part * 8;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] += src[e];
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = x[e] / (float)Gq;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qh[v][e] = f16_bits(x[2 * e]) | (f16_bits(x[2 * e + 1]) << 16);
+    }
+
+    const uint16_t* base = lm16 + ((int64_t)bg * C + row0) * D + part * 8;
+    constexpr int ROWS_PER_ITER = 4 * RPW * U;
+    for (int it = 0; it < nrows; it += ROWS_PER_ITER) {
+        u32x4_t x[U];
+        int rr[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            rr[u] = it + (u * 4 + wave) * RPW + rp;
+            x[u] = rr[u] < nrows ? nt_load_u4(base + (int64_t)rr[u] * D) : u32x4_t{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float dot[NQ];
+#pragma unroll
+            for (int v = 0; v < NQ; ++v) {
+                float a = dot2_f16(qh[v][0], x[u].x, 0.f);
+                a = dot2_f16(qh[v][1], x[u].y, a);
+                a = dot2_f16(qh[v][2], x[u].z, a);
+                a = dot2_f16(qh[v][3], x[u].w, a);
+                dot[v] = dpp_group_sum<LPR>(a);
+            }
+            // per-query scores with compile-time register indices
+            float sct[T];
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                if constexpr (MAXRED) {
+                    sct[t] = scale * dot[t * G];
+#pragma unroll
+                    for (int h = 1; h < G; ++h) sct[t] = fmaxf(sct[t], scale * dot[t * G + h]);
+                } else {
+                    sct[t] = scale * dot[t];
+                }
+            }
+            if (part < T && rr[u] < nrows)
+                sres[part * rows_per_block + rr[u]] = (part == 0) ? sct[0] : sct[T - 1];
+        }
+    }
+    __syncthreads();
+    for (int t = 0; t < T; ++t) {
+        float* dst = s_lo + ((int64_t)bg * T + t) * C + row0;
+        for (int i = threadIdx.x; i < nrows; i += kThreads) dst[i] = sres[t * rows_per_block + i];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Shadow pass 2, one block per (b, g, t): the k-th largest fp16 score tau, the
+// candidates {c : s_lo[c] >= tau - 2 delta} (delta bounds |s_lo - s| for every
+// chunk, s the fp32 score this kernel computes), their fp32 re-scores, and the
+// exact top-k among them (ties to the lower id), written in ascending order.
+// ---------------------------------------------------------------------------
+template <int D, bool MAXRED>
+__global__ __launch_bounds__(kThreads) void k_select_exact(
+    const float* __restrict__ q, int T, int Hq, const float* __restrict__ lm, dk_strides ls,
+    const float* __restrict__ norm_max, const float* __restrict__ s_lo, int Hkv, int C, int k,
+    float scale, int32_t* __restrict__ topk_idx, float* __restrict__ topk_score) {
+    constexpr int LPR = D / 8;                 // lanes per fp32 row, 8 floats each
+    constexpr int RPW = kWave / LPR;
+    extern __shared__ uint32_t smem2[];
+    // LDS: keys [Cp] | cand [max(Cp, 256)] | qv [nvec][D] | hist [256] | scratch | bc | sf,
+    // Cp = C rounded up to 4 so that every array starts on 16 bytes
+    const int Cp = (C + 3) & ~3;
+    uint32_t* keys = smem2;
+    int32_t* cand = (int32_t*)(keys + Cp);
+    uint32_t* cand_u = (uint32_t*)cand;
+    float* qv = (float*)(cand + (Cp > kThreads ? Cp : kThreads));
+    const int Gq = Hq / Hkv;
+    const int nvec = MAXRED ? Gq : 1;
+    uint32_t* hist = (uint32_t*)(qv + nvec * D);     // [256]
+    int* scratch = (int*)(hist + 256);               // [8]
+    int* bc = scratch + 8;                           // [2]
+    float* sf = (float*)(bc + 2);                    // [2] norm, threshold
+
+    const int t = blockIdx.x % T;
+    const int bg = blockIdx.x / T;
+    const int b = bg / Hkv, g = bg - b * Hkv;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+
+    // Every independent global load first: this thread's contiguous range of
+    // fp16-pass scores (kept in registers), the norm bound, the query rows.
+    constexpr int KPT = kShadowMaxC / kThreads;      // scores per thread, at most
+    const int per = (C + kThreads - 1) / kThreads;
+    const int lo = min(C, tid * per), hi = min(C, lo + per);
+    const float* sl = s_lo + ((int64_t)bg * T + t) * C;
+    // coalesced 16-byte loads into LDS (s_lo rows start on 16 bytes when C % 4 == 0)
+    if ((C & 3) == 0) {
+        for (int i = tid; i < (C >> 2); i += kThreads) {
+            const float4 x = *reinterpret_cast<const float4*>(sl + 4 * i);
+            reinterpret_cast<uint4*>(keys)[i] =
+                make_uint4(score_key(x.x), score_key(x.y), score_key(x.z), score_key(x.w));
+        }
+    } else {
+        for (int i = tid; i < C; i += kThreads) keys[i] = score_key(sl[i]);
+    }
+    const float M = norm_max[bg];
+    for (int i = tid; i < nvec * D; i += kThreads) {
+        const int v = i / D, e = i - v * D;
+        float x;
+        if (MAXRED) {
+            x = q[(((int64_t)b * T + t) * Hq + g * Gq + v) * D + e];
+        } else {
+            x = 0.f;
+            for (int h = 0; h < Gq; ++h) x += q[(((int64_t)b * T + t) * Hq + g * Gq + h) * D + e];
+            x = x / (float)Gq;
+        }
+        qv[i] = x;
+    }
+    __syncthreads();
+    uint32_t kr[KPT];
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) kr[i] = lo + i < hi ? keys[lo + i] : 0u;
+    uint32_t tmax = 0u;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) tmax = max(tmax, kr[i]);
+    uint32_t* tmaxs = cand_u;                     // [256] scratch (cand[] is not used yet)
+    tmaxs[tid] = tmax;
+    __syncthreads();
+    if (wave == 0) {
+        // largest query-vector norm, rounded up
+        float nmax = 0.f;
+        for (int v = 0; v < nvec; ++v) {
+            float ss = 0.f;
+            for (int e = lane; e < D; e += kWave) ss += qv[v * D + e] * qv[v * D + e];
+            for (int off = 1; off < kWave; off <<= 1) ss += __shfl_xor(ss, off, kWave);
+            nmax = fmaxf(nmax, ss);
+        }
+        // A lower bound of the k-th largest fp16 score: the k-th largest of the
+        // per-thread maxima (at least k scores reach it).  For k > 256 the
+        // bound is 0, i.e. every chunk is a candidate.
+        uint32_t kb = 0u;
+        if (k <= kThreads) {
+            uint32_t x[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) x[v] = tmaxs[lane + 64 * v];
+            int nd;
+            kb = wave_kth_key_bisect(x, k, &nd);
+        }
+        if (lane == 0) {
+            sf[0] = sqrtf(nmax) * (1.0f + (float)(D + 8) * 5.9604645e-8f);
+            bc[0] = (int)kb;
+        }
+    }
+    __syncthreads();
+    const uint32_t kth = (uint32_t)bc[0];
+    const float nq = sf[0];
+    const float u16 = 4.8828125e-4f, u32 = 5.9604645e-8f;
+    const float A = nq * M;   // >= sum_i |q_i lm_ci| for every chunk (Cauchy-Schwarz)
+    const float sqd = sqrtf((float)D);
+    const float e1 = (2.f * u16 + u16 * u16 + (D + 2) * u32 * 1.01f) * A +
+                     2.9802322e-8f * 1.01f * sqd * (M + nq) + (float)D * 8.9e-16f;
+    const float e2 = (D + 2) * u32 * 1.01f * A;
+    const float delta = fabsf(scale) * (e1 + e2) * 1.01f;
+    const float tau = key_score(kth);
+    float thr = tau - 2.f * delta;
+    thr -= (fabsf(tau) + 2.f * delta) * 2.4e-7f;     // round the bound down
+    const uint32_t thr_key =
+        (M != M || M == INFINITY || thr != thr || kth == 0u) ? 0u : score_key(thr);
+
+    // candidates in ascending chunk order
+    int mine = 0;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) mine += (lo + i < hi) && kr[i] >= thr_key;
+    int ncand;
+    int pos = block_exclusive_scan(mine, scratch, &ncand);
+#pragma unroll
+    for (int i = 0; i < KPT; ++i)
+        if ((lo + i < hi) && kr[i] >= thr_key) cand[pos++] = lo + i;
+    __syncthreads();
+
+    // exact fp32 scores of the candidates (keys[] is reused for them); UG rows
+    // per lane group are loaded before any is used, so the gathers overlap
+    constexpr int UG = 8;
+    const int rp = lane / LPR, part = lane % LPR;
+    const float* lb = lm + (int64_t)b * ls.b + (int64_t)g * ls.h + part * 8;
+    float qm[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qm[e] = qv[part * 8 + e];
+    for (int j0 = 0; j0 < ncand; j0 += 4 * RPW * UG) {
+        float x[UG][8];
+        int jj[UG];
+#pragma unroll
+        for (int u = 0; u < UG; ++u) {
+            jj[u] = j0 + (u * 4 + wave) * RPW + rp;
+            if (jj[u] < ncand) {
+                const float* src = lb + (int64_t)cand[jj[u]] * ls.t;
+                const float4 x0 = *reinterpret_cast<const float4*>(src);
+                const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
+                x[u][0] = x0.x; x[u][1] = x0.y; x[u][2] = x0.z; x[u][3] = x0.w;
+                x[u][4] = x1.x; x[u][5] = x1.y; x[u][6] = x1.z; x[u][7] = x1.w;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[u][e] = 0.f;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UG; ++u) {
+            float best;
+            if (MAXRED) {
+                best = -INFINITY;
+                for (int v = 0; v < nvec; ++v) {
+                    float a = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) a = fmaf(qv[v * D + part * 8 + e], x[u][e], a);
+                    a = dpp_group_sum<LPR>(a);
+                    best = fmaxf(best, scale * a);
+                }
+            } else {
+                float a = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) a = fmaf(qm[e], x[u][e], a);
+                best = scale * dpp_group_sum<LPR>(a);
+            }
+            if (jj[u] < ncand && part == 0) keys[jj[u]] = score_key(best);
+        }
+    }
+    __syncthreads();
+    int32_t* oi = topk_idx + ((int64_t)bg * T + t) * k;
+    float* os = topk_score ? topk_score + ((int64_t)bg * T + t) * k : nullptr;
+    if (ncand <= kThreads) {
+        // one wave: exact k-th key, then the winners in ascending position order
+        if (wave == 0) {
+            uint32_t x[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) x[v] = lane + 64 * v < ncand ? keys[lane + 64 * v] : 0u;
+            int need;
+            const uint32_t thr2 = wave_kth_key_bisect(x, k, &need);
+            const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+            int base = 0, eq_base = 0;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const bool eq = x[v] == thr2 && lane + 64 * v < ncand;
+                const uint64_t eqm = __builtin_amdgcn_ballot_w64(eq);
+                const int eq_rank = eq_base + __builtin_popcountll(eqm & below);
+                const bool take = (x[v] > thr2 && lane + 64 * v < ncand) || (eq && eq_rank < need);
+                const uint64_t tm = __builtin_amdgcn_ballot_w64(take);
+                if (take) {
+                    const int jpos = base + __builtin_popcountll(tm & below);
+                    if (jpos < k) {
+                        oi[jpos] = cand[lane + 64 * v];
+                        if (os) os[jpos] = key_score(x[v]);
+                    }
+                }
+                base += __builtin_popcountll(tm);
+                eq_base += __builtin_popcountll(eqm);
+            }
+        }
+    } else {
+        block_topk(keys, ncand, k, hist, scratch, bc, [&](int jpos, int i, uint32_t key) {
+            oi[jpos] = cand[i];
+            if (os) os[jpos] = key_score(key);
+        });
+    }
+}
+
 template <int D, int NQ, int T, bool MAXRED>
 hipError_t launch_split(const float* q, int B, int Hq, const float* lm, dk_strides ls, int Hkv,
                         int C, int k, float scale, const TopkPlan& p, uint32_t* ck, int32_t* ci,
@@ -303,12 +798,60 @@ hipError_t dispatch_split(int nq, int T, bool maxred, const float* q, int B, int
     return hipErrorInvalidValue;
 }
 
+template <int D, int NQ, int T, bool MAXRED>
+hipError_t launch_lo(const float* q, int B, int Hq, const uint16_t* lm16, int Hkv, int C, float scale,
+                     const TopkPlan& p, float* s_lo, hipStream_t st) {
+    const size_t lds = (size_t)T * p.rows * 4;
+    const unsigned grid = (unsigned)((int64_t)B * Hkv * p.splits);
+    hipLaunchKernelGGL((k_score_lo<D, NQ, T, MAXRED>), dim3(grid), dim3(kThreads), lds, st, q, Hq, lm16,
+                       Hkv, C, scale, p.rows, p.splits, s_lo);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t dispatch_lo(int nq, int T, bool maxred, const float* q, int B, int Hq, const uint16_t* lm16,
+                       int Hkv, int C, float scale, const TopkPlan& p, float* s_lo, hipStream_t st) {
+#define DK_LO(NQ_, T_, MX_) \
+    if (nq == NQ_ && T == T_ && maxred == MX_) return launch_lo<D, NQ_, T_, MX_>(q, B, Hq, lm16, Hkv, C, scale, p, s_lo, st);
+    DK_LO(1, 1, false)
+    DK_LO(2, 2, false)
+    DK_LO(1, 1, true)
+    DK_LO(2, 1, true)
+    DK_LO(4, 1, true)
+    DK_LO(8, 1, true)
+    DK_LO(16, 1, true)
+    DK_LO(2, 2, true)
+    DK_LO(4, 2, true)
+    DK_LO(8, 2, true)
+    DK_LO(16, 2, true)
+#undef DK_LO
+    return hipErrorInvalidValue;
+}
+
 }  // namespace
 
-TopkPlan plan_topk(int B, int Hkv, int T, int C, int k) {
-    (void)T;
+TopkPlan plan_topk(int B, int Hkv, int T, int C, int k, bool shadow) {
     TopkPlan p{0, 0, 0};
     const int64_t bg = (int64_t)B * Hkv;
+    if (shadow) {
+        // pass 1: ranges of rows for ~2048 blocks, at least 256 rows each, at most
+        // kMaxRows (LDS staging); pass 2 keeps every score of a (b, g) in LDS.
+        if (C > kShadowMaxC) return p;
+        int64_t s = (2048 + bg - 1) / bg;
+        int64_t by_rows = C / 256;
+        if (by_rows < 1) by_rows = 1;
+        if (s > by_rows) s = by_rows;
+        const int64_t min_s = (C + kMaxRows - 1) / kMaxRows;
+        if (s < min_s) s = min_s;
+        p.splits = (int)s;
+        p.rows = (int)((C + s - 1) / s);
+        while (p.splits > 1 && (int64_t)(p.splits - 1) * p.rows >= C) {
+            p.splits -= 1;
+            p.rows = (C + p.splits - 1) / p.splits;
+        }
+        p.ws_bytes = (size_t)bg * T * C * 4;
+        return p;
+    }
     int64_t want = (2048 + bg - 1) / bg;
     int64_t by_rows = C / (2 * (int64_t)k);
     if (by_rows < 1) by_rows = 1;
@@ -333,13 +876,44 @@ TopkPlan plan_topk(int B, int Hkv, int T, int C, int k) {
     return p;
 }
 
+size_t select_lds_bytes(int C, int D, int nvec) {
+    const int Cp = (C + 3) & ~3;
+    return (size_t)(Cp + (Cp > 256 ? Cp : 256) + nvec * D + 256 + 12) * 4;
+}
+
+hipError_t launch_build_shadow(const float* lm, dk_strides ls, int B, int Hkv, int C, int d,
+                               uint16_t* lm16, float* norm_max, hipStream_t st) {
+    const unsigned grid = (unsigned)((int64_t)B * Hkv);
+    if (d == 128)
+        hipLaunchKernelGGL(k_build_shadow<128>, dim3(grid), dim3(kThreads), 0, st, lm, ls, Hkv, C, lm16, norm_max);
+    else
+        hipLaunchKernelGGL(k_build_shadow<64>, dim3(grid), dim3(kThreads), 0, st, lm, ls, Hkv, C, lm16, norm_max);
+    return hipGetLastError();
+}
+
 hipError_t launch_score_topk(const float* q, int B, int T, int Hq, const float* lm, dk_strides ls,
                              int Hkv, int C, int d, int k, float scale, dk_group_reduce reduce,
-                             int32_t* topk_idx, float* topk_score, void* ws, const TopkPlan& p,
-                             hipStream_t st) {
+                             const dk_landmark_shadow* shadow, int32_t* topk_idx, float* topk_score,
+                             void* ws, const TopkPlan& p, hipStream_t st) {
     const bool maxred = reduce == DK_REDUCE_MAX;
     const int G = Hq / Hkv;
     const int nq = maxred ? G * T : T;
+    if (shadow) {
+        float* s_lo = (float*)ws;
+        hipError_t e = d == 128
+            ? dispatch_lo<128>(nq, T, maxred, q, B, Hq, shadow->lm16, Hkv, C, scale, p, s_lo, st)
+            : dispatch_lo<64>(nq, T, maxred, q, B, Hq, shadow->lm16, Hkv, C, scale, p, s_lo, st);
+        if (e != hipSuccess) return e;
+        const unsigned grid = (unsigned)((int64_t)B * Hkv * T);
+        const size_t lds = select_lds_bytes(C, d, maxred ? G : 1);
+#define DK_SEL(D_, MX_)                                                                            \
+    hipLaunchKernelGGL((k_select_exact<D_, MX_>), dim3(grid), dim3(kThreads), lds, st, q, T, Hq, lm, ls, \
+                       shadow->norm_max, s_lo, Hkv, C, k, scale, topk_idx, topk_score)
+        if (d == 128) { if (maxred) DK_SEL(128, true); else DK_SEL(128, false); }
+        else { if (maxred) DK_SEL(64, true); else DK_SEL(64, false); }
+#undef DK_SEL
+        return hipGetLastError();
+    }
     const int64_t ncand = (int64_t)B * Hkv * T * p.splits * k;
     uint32_t* ck = p.splits > 1 ? (uint32_t*)ws : nullptr;
     int32_t* ci = p.splits > 1 ? (int32_t*)((char*)ws + ncand * 4) : nullptr;

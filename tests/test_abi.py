@@ -27,14 +27,14 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     for n in names:
         assert hasattr(lib, n), n
     assert {n for n, _, _ in b.EXPORTS} == set(names)
 
 
 def test_abi_version():
-    assert lib.dk_abi_version() == 1
+    assert lib.dk_abi_version() == 2
 
 
 def err():
@@ -57,9 +57,15 @@ def test_landmarks_rejects(kw, status):
 
 
 def score(q=FAKE, B=2, T=2, Hq=32, lm=FAKE, lmdt=0, ls=b.dk_strides(1 << 22, 1 << 19, 128), Hkv=8,
-          C=1024, d=128, k=64, scale=0.088, reduce=0, idx=FAKE, sc=FAKE, ws=FAKE, wsb=1 << 30):
-    return lib.dk_score_topk(q, B, T, Hq, lm, lmdt, ls, Hkv, C, d, k, scale, reduce, idx, sc, ws, wsb,
-                             None)
+          C=1024, d=128, k=64, scale=0.088, reduce=0, shadow=None, idx=FAKE, sc=FAKE, ws=FAKE,
+          wsb=1 << 30):
+    return lib.dk_score_topk(q, B, T, Hq, lm, lmdt, ls, Hkv, C, d, k, scale, reduce, shadow, idx, sc,
+                             ws, wsb, None)
+
+
+SH_OK = b.dk_landmark_shadow(0x1000, 0x1000)
+SH_NULL = b.dk_landmark_shadow(0x1000, 0)
+SH_MIS = b.dk_landmark_shadow(0x1008, 0x1000)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -67,6 +73,8 @@ def score(q=FAKE, B=2, T=2, Hq=32, lm=FAKE, lmdt=0, ls=b.dk_strides(1 << 22, 1 <
     (dict(k=0), 1), (dict(k=1025), 1), (dict(reduce=5), 1), (dict(scale=float("nan")), 1),
     (dict(lmdt=1), 2), (dict(d=96), 2), (dict(C=70000, k=64), 2), (dict(reduce=1, Hq=24), 2),
     (dict(ws=NULL), 1), (dict(wsb=16), 1), (dict(lm=MIS), 2),
+    (dict(shadow=ctypes.byref(SH_NULL)), 1), (dict(shadow=ctypes.byref(SH_MIS)), 2),
+    (dict(shadow=ctypes.byref(SH_OK), C=8192), 2), (dict(shadow=ctypes.byref(SH_OK), wsb=1024), 1),
 ])
 def test_score_topk_rejects(kw, status):
     assert score(**kw) == status, err()
@@ -75,9 +83,22 @@ def test_score_topk_rejects(kw, status):
 
 def test_score_topk_workspace_sizes():
     # 64 x 8 (b, g) rows over 4096 chunks: 4 ranges of 1024, 64 candidates each
-    assert lib.dk_score_topk_workspace_size(64, 8, 2, 4096, 64) == 64 * 8 * 2 * 4 * 64 * 8
-    assert lib.dk_score_topk_workspace_size(1, 1, 2, 128, 8) > 0
-    assert lib.dk_score_topk_workspace_size(1, 1, 2, 128, 0) == 0
+    assert lib.dk_score_topk_workspace_size(64, 8, 2, 4096, 64, 0) == 64 * 8 * 2 * 4 * 64 * 8
+    # with a shadow: every fp16 score of every (b, g, t)
+    assert lib.dk_score_topk_workspace_size(64, 8, 2, 4096, 64, 1) == 64 * 8 * 2 * 4096 * 4
+    assert lib.dk_score_topk_workspace_size(1, 1, 2, 128, 8, 0) > 0
+    assert lib.dk_score_topk_workspace_size(1, 1, 2, 128, 0, 0) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(lm=NULL), 1), (dict(C=0), 1), (dict(d=96), 2), (dict(lm16=MIS), 2),
+])
+def test_shadow_rejects(kw, status):
+    a = dict(lm=FAKE, ls=b.dk_strides(1 << 22, 1 << 19, 128), B=2, H=8, C=1024, d=128, lm16=FAKE, nm=FAKE)
+    a.update(kw)
+    assert lib.dk_build_landmark_shadow(a["lm"], a["ls"], a["B"], a["H"], a["C"], a["d"], a["lm16"],
+                                        a["nm"], None) == status
+    assert err().startswith("dk_build_landmark_shadow")
 
 
 def union(idx=FAKE, B=2, H=8, T=2, k=64, C=1024, uo=FAKE, mo=FAKE, cnt=FAKE, ov=FAKE, plan=None):

@@ -94,11 +94,16 @@ def test_landmarks_strided_pool(dkb):
 # scores and top-k
 # ----------------------------------------------------------------------------
 
-def check_score_topk(dkb, qh, lm32, k, scale, reduce, G):
-    """GPU scores/top-k on fp32 landmarks lm32 against the oracle on the same values."""
+def check_score_topk(dkb, qh, lm32, k, scale, reduce, G, shadow=False):
+    """GPU scores/top-k on fp32 landmarks lm32 against the oracle on the same values.
+
+    With shadow=True the call streams the fp16 shadow and re-scores candidates;
+    the bar is the same (the selected set and the reported scores)."""
     q = torch.from_numpy(qh.astype(np.float32)).cuda()
     lm = torch.from_numpy(lm32).cuda()
-    idx, sc = dkb.score_topk(q, lm, k, scale, dkb.DK_REDUCE_MAX if reduce == "max" else dkb.DK_REDUCE_MEAN)
+    sh = dkb.build_landmark_shadow(lm) if shadow else None
+    idx, sc = dkb.score_topk(q, lm, k, scale, dkb.DK_REDUCE_MAX if reduce == "max" else dkb.DK_REDUCE_MEAN,
+                             shadow=sh)
     torch.cuda.synchronize()
     s_ref = O.chunk_scores(qh, lm32.astype(np.float64), scale, reduce)
     idx_ref = O.topk_chunks(s_ref, k)
@@ -122,6 +127,7 @@ def check_score_topk(dkb, qh, lm32, k, scale, reduce, G):
     return rows_diff, near
 
 
+@pytest.mark.parametrize("shadow", [False, True])
 @pytest.mark.parametrize("name,B,L,T,reduce", [
     ("tiny", None, None, 2, "mean"),
     ("tiny", None, None, 1, "mean"),
@@ -130,34 +136,70 @@ def check_score_topk(dkb, qh, lm32, k, scale, reduce, G):
     ("llama8b_l32k", 2, 8192, 1, "max"),
     ("llama8b_l32k", None, None, 2, "mean"),
 ])
-def test_score_topk(dkb, name, B, L, T, reduce):
+def test_score_topk(dkb, name, B, L, T, reduce, shadow):
     w = workload(name, B, L, T=T)
     q, K, V = make(w, 21)
     qh = q.cpu().numpy().astype(np.float64)
     lm32 = O.chunk_landmarks(synth.to_numpy_f64(K), w.chunk).astype(np.float32)
-    rows_diff, near = check_score_topk(dkb, qh, lm32, w.k, w.scale, reduce, w.G)
+    rows_diff, near = check_score_topk(dkb, qh, lm32, w.k, w.scale, reduce, w.G, shadow)
     print(f"rows differing only by near-ties: {rows_diff}, near-tie chunks: {near}")
 
 
-def test_score_topk_full_128k_shape(dkb):
+@pytest.mark.parametrize("shadow", [False, True])
+def test_score_topk_full_128k_shape(dkb, shadow):
     # landmarks of the 128K workload shape (B=64, Hkv=8, C=4096), drawn directly
     w = WORKLOADS["b64_l128k"]
     g = torch.Generator().manual_seed(3)
     lm32 = (torch.randn(w.B, w.Hkv, w.C, w.d, generator=g) / math.sqrt(w.chunk)).numpy()
     qh = synth.make_queries(w, 3).numpy().astype(np.float64)
-    rows_diff, near = check_score_topk(dkb, qh, lm32, w.k, w.scale, "mean", w.G)
+    rows_diff, near = check_score_topk(dkb, qh, lm32, w.k, w.scale, "mean", w.G, shadow)
     print(f"rows differing only by near-ties: {rows_diff}, near-tie chunks: {near}")
 
 
-def test_score_topk_exact_ties_and_k_equals_c(dkb):
+@pytest.mark.parametrize("shadow", [False, True])
+def test_score_topk_exact_ties_and_k_equals_c(dkb, shadow):
     # duplicated landmark rows give bit-identical scores: the lower id must win
     g = torch.Generator().manual_seed(4)
     base = torch.randn(2, 2, 40, 64, generator=g)
     lm32 = torch.cat([base, base, base[:, :, :16]], dim=2).contiguous().numpy()   # C = 96
     qh = synth.round_bf16(torch.randn(2, 2, 8, 64, generator=g)).numpy().astype(np.float64)
     for k in (1, 7, 40, 41, 96):
-        rows_diff, near = check_score_topk(dkb, qh, lm32, k, 0.125, "mean", 4)
+        rows_diff, near = check_score_topk(dkb, qh, lm32, k, 0.125, "mean", 4, shadow)
         assert rows_diff == 0
+
+
+def test_landmark_shadow_builder(dkb):
+    g = torch.Generator().manual_seed(6)
+    lm = torch.randn(3, 2, 200, 128, generator=g) * torch.rand(3, 2, 200, 1, generator=g) * 3
+    lm[1, 1, 17] *= 1e5                      # beyond fp16: that (b, g) gets an infinite bound
+    sh = dkb.build_landmark_shadow(lm.cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(sh.lm16.cpu(), lm.half())          # round to nearest even, per element
+    nm = sh.norm_max.cpu().numpy()
+    true = np.linalg.norm(lm.numpy().astype(np.float64), axis=-1).max(axis=-1)
+    assert np.isinf(nm[1, 1])
+    fin = np.isfinite(nm)
+    assert np.all(nm[fin] >= true[fin]) and np.all(nm[fin] <= true[fin] * (1 + 1e-5))
+
+
+def test_score_topk_shadow_degenerate(dkb):
+    g = torch.Generator().manual_seed(7)
+    qh = synth.round_bf16(torch.randn(1, 2, 4, 128, generator=g)).numpy().astype(np.float64)
+    # every landmark equal: all chunks tie, the k lowest ids win (every chunk is a candidate)
+    lm_eq = np.broadcast_to(torch.randn(128, generator=g).numpy(), (1, 1, 300, 128)).astype(np.float32).copy()
+    rows_diff, near = check_score_topk(dkb, qh, lm_eq, 37, 0.09, "mean", 4, True)
+    assert rows_diff == 0
+    # near-ties finer than fp16 can see: a base row plus perturbations of 1e-5
+    base = torch.randn(128, generator=g)
+    pert = torch.randn(1, 1, 600, 128, generator=g) * 1e-5
+    lm_nt = (base + pert).numpy().astype(np.float32)
+    rows_diff, near = check_score_topk(dkb, qh, lm_nt, 50, 0.09, "mean", 4, True)
+    print(f"near-tie stress: rows differing {rows_diff}, near-tie chunks {near}")
+    # a landmark beyond fp16 range: the (b, g) is re-scored exactly
+    lm_big = torch.randn(1, 1, 256, 128, generator=g).numpy().astype(np.float32)
+    lm_big[0, 0, 100] = 7e4
+    rows_diff, near = check_score_topk(dkb, qh, lm_big, 9, 0.09, "mean", 4, True)
+    assert rows_diff == 0
 
 
 # ----------------------------------------------------------------------------
@@ -399,11 +441,13 @@ def check_step_sampled(dkb, w, q, K, V, st, samples):
     return total_near
 
 
-def test_step_tiny_full(dkb):
+@pytest.mark.parametrize("shadow", [False, True])
+def test_step_tiny_full(dkb, shadow):
     w = WORKLOADS["tiny"]
     q, K, V = make(w, 0)
     lm = dkb.build_landmarks(K, w.chunk)
-    st = dkb.DecodeStep(w.B, w.T, w.Hq, w.Hkv, w.d, w.C, w.chunk, w.k, w.scale, "cuda")
+    sh = dkb.build_landmark_shadow(lm) if shadow else None
+    st = dkb.DecodeStep(w.B, w.T, w.Hq, w.Hkv, w.d, w.C, w.chunk, w.k, w.scale, "cuda", shadow=sh)
     st.run(q, lm, K, V)
     torch.cuda.synchronize()
     check_step_sampled(dkb, w, q, K, V, st, [(0, 0)])
@@ -418,7 +462,8 @@ def test_step_full_size_sampled(dkb, name, samples):
     w = WORKLOADS[name]
     q, K, V = make(w, 1)
     lm = dkb.build_landmarks(K, w.chunk)
-    st = dkb.DecodeStep(w.B, w.T, w.Hq, w.Hkv, w.d, w.C, w.chunk, w.k, w.scale, "cuda")
+    sh = dkb.build_landmark_shadow(lm)
+    st = dkb.DecodeStep(w.B, w.T, w.Hq, w.Hkv, w.d, w.C, w.chunk, w.k, w.scale, "cuda", shadow=sh)
     st.run(q, lm, K, V)
     torch.cuda.synchronize()
     near = check_step_sampled(dkb, w, q, K, V, st, samples)
