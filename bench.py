@@ -25,7 +25,9 @@ import sys
 import time
 
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, 8 TB/s
+PCIE_PEAK_GBPS = 64.0    # PCIe 5.0 x16, one direction
 METRIC = "dual-query sparse decode steps/s + selected-KV GB/s (% HBM peak), B=64 L=128K"
+METRIC_HOST = "dual-query sparse decode steps/s, KV pool in pinned host memory, B=32 L=128K"
 
 
 def parse():
@@ -42,6 +44,13 @@ def parse():
                     help="time only whole steps (no per-call events inside the step)")
     ap.add_argument("--no-shadow", action="store_true",
                     help="score from the fp32 landmarks only (no fp16 landmark shadow)")
+    ap.add_argument("--host-copy", choices=("mapped", "copy"), default="mapped",
+                    help="host-pool workloads: gather kernel over the mapped pool, or hipMemcpyAsync")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB + 1 GiB device copy (dk_gather_kv over consecutive "
+                         "chunks) three times: the known-size reference for HBM byte counters")
+    ap.add_argument("--lookahead", type=int, default=2,
+                    help="host-pool workloads: layers between a selection/transfer and its attention")
     return ap.parse_args()
 
 
@@ -81,6 +90,157 @@ def cpu_baseline(w, qs_host, K, V, budget_s, seed):
                       f"{w.B * w.Hkv * len(qs_host)} units per step; landmarks precomputed"}
 
 
+def h2d_peak_gbps(torch, nbytes=1 << 28, reps=5):
+    """Contiguous pinned-host -> HBM copy rate (the link's practical peak)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    best = 0.0
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src, non_blocking=True)
+        b.record()
+        b.synchronize()
+        best = max(best, nbytes / (a.elapsed_time(b) * 1e-3) / 1e9)
+    return best
+
+
+def bench_host_pool(args, w):
+    """Decode steps with the KV pool in pinned host memory and a hot cache per layer."""
+    import numpy as np
+    import torch
+
+    from sparse_kv_retrieval_amd import binding as dkb
+    from sparse_kv_retrieval_amd import synth
+    from sparse_kv_retrieval_amd.host_pool import HostPoolDecoder, StageTimer
+
+    dev = "cuda"
+    total = 1 + args.warmup + args.steps           # one cold step, warm-up, timed steps
+    t0 = time.time()
+    qseq = [synth.make_query_sequence(w, args.seed, total, layer=l, device=dev) for l in range(w.layers)]
+    K, V = synth.make_kv_pool(w, args.seed, device=dev, q0=qseq[0][0])
+    lm = dkb.build_landmarks(K, w.chunk)                # prefill: built before the pool moves out
+    shadow = None if args.no_shadow else dkb.build_landmark_shadow(lm)
+    Kh = torch.empty(K.shape, dtype=K.dtype, pin_memory=True)
+    Vh = torch.empty(V.shape, dtype=V.dtype, pin_memory=True)
+    Kh.copy_(K)
+    Vh.copy_(V)
+    del K, V
+    torch.cuda.empty_cache()
+    dec = HostPoolDecoder(Kh, Vh, lm, shadow, T=w.T, Hq=w.Hq, k=w.k, scale=w.scale, layers=w.layers,
+                          mode=args.host_copy, lookahead=args.lookahead)
+    link_gbps = h2d_peak_gbps(torch)
+    torch.cuda.synchronize()
+    print(f"[bench] inputs ready in {time.time() - t0:.1f} s: host pool {2 * Kh.nbytes / 1e9:.2f} GB pinned, "
+          f"hot caches {2 * dec.Kc.nbytes / 1e9:.2f} GB, contiguous H2D {link_gbps:.1f} GB/s",
+          file=sys.stderr, flush=True)
+
+    def qs_at(s):
+        return [qseq[l][s] for l in range(w.layers)]
+
+    for s in range(1 + args.warmup):
+        dec.step(qs_at(s))
+    torch.cuda.synchronize()
+    timer = None if args.no_events else StageTimer()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for s in range(1 + args.warmup, total):
+        dec.step(qs_at(s), timer)
+    end.record()
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / args.steps
+
+    # Statistics from a deterministic replay of the same steps (untimed).
+    dec.reset()
+    prev_spec = [None] * w.layers
+    hits = unions = misses = overlap_sum = temporal_hits = 0
+    n_units = 0
+    for s in range(total):
+        dec.step(qs_at(s))
+        torch.cuda.synchronize()
+        for l in range(w.layers):
+            idx = dec.topk_idx[l]
+            if s >= 1 + args.warmup:
+                p = dec.plans[l]
+                hits += int(p.hit_count.sum())
+                misses += int(p.miss_count.sum())
+                unions += int(dec.count[l].sum())
+                overlap_sum += int(dec.overlap[l].sum())
+                real = idx[:, :, 0]
+                temporal_hits += int((real.unsqueeze(-1) == prev_spec[l].unsqueeze(-2)).any(-1).sum())
+                n_units += w.B * w.Hkv
+            prev_spec[l] = idx[:, :, w.T - 1].clone()
+    chunk_bytes = w.chunk_kv_bytes()
+    miss_bytes_step = misses * chunk_bytes / args.steps
+    union_bytes_step = unions * chunk_bytes / args.steps
+    out = {
+        "metric": METRIC_HOST, "value": round(1000.0 / ms_per_step, 3), "unit": "steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "L": w.L, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d,
+                   "chunk": w.chunk, "k": w.k, "T": w.T, "layers": w.layers, "seed": args.seed,
+                   "landmark_shadow": shadow is not None, "host_copy": args.host_copy,
+                   "hot_cache_slots": dec.slots, "drift": 0.05, "lookahead": dec.lookahead},
+        "hit_rate": round(hits / max(unions, 1), 5),
+        "misses_per_bg_layer": round(misses / max(n_units, 1), 3),
+        "miss_bytes_per_step": int(miss_bytes_step),
+        "prediction_accuracy": round(overlap_sum / max(n_units, 1) / w.k, 5),
+        "temporal_prediction_accuracy": round(temporal_hits / max(n_units, 1) / w.k, 5),
+        "h2d_contiguous_GBps": round(link_gbps, 1),
+    }
+    if timer:
+        g_ms = timer.total_ms("gather") / args.steps
+        sel_ms = timer.total_ms("select") / args.steps
+        att_ms = timer.total_ms("attn") / args.steps
+        pcie = miss_bytes_step / (g_ms * 1e-3) / 1e9
+        hidden = (g_ms + sel_ms + att_ms - ms_per_step) / g_ms if g_ms > 0 else 0.0
+        out["pcie_GBps"] = round(pcie, 2)
+        out["pcie_frac_of_contiguous"] = round(pcie / link_gbps, 4)
+        out["copy_ms_per_step"] = round(g_ms, 3)
+        out["compute_ms_per_step"] = round(sel_ms + att_ms, 3)
+        out["copy_hidden_frac"] = round(min(max(hidden, 0.0), 1.0), 4)
+        out["hot_cache_attn_GBps"] = round(union_bytes_step / (att_ms * 1e-3) / 1e9, 1)
+        out["roofline"] = {"bound": "pcie", "kernel": "gather_kv", "achieved": round(pcie, 2),
+                           "peak": PCIE_PEAK_GBPS, "unit": "GB/s", "frac": round(pcie / PCIE_PEAK_GBPS, 4),
+                           "traffic": None}
+        out["kernels"] = {
+            "select (score_topk + union_select)": {"avg_us": round(sel_ms * 1e3 / w.layers, 2)},
+            "gather_kv": {"avg_us": round(g_ms * 1e3 / w.layers, 2),
+                          "bytes_per_launch": int(miss_bytes_step / w.layers)},
+            "sparse_decode_attn": {"avg_us": round(att_ms * 1e3 / w.layers, 2),
+                                   "bytes_per_launch": int(union_bytes_step / w.layers)},
+        }
+    else:
+        out["roofline"] = None
+    if args.cpu_seconds > 0:
+        qs_host = [q.cpu().numpy().astype(np.float64) for q in qs_at(total - 1)]
+        out["cpu_baseline"] = cpu_baseline(w, qs_host, Kh, Vh, args.cpu_seconds, args.seed)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+def calibrate_copy():
+    """Three plain copies of 512 MiB K + 512 MiB V (1 GiB read, 1 GiB written each)."""
+    import torch
+
+    from sparse_kv_retrieval_amd import binding as dkb
+
+    rows, d, chunk = 1 << 21, 128, 32
+    C = rows // chunk
+    src = [torch.ones(1, 1, rows, d, dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    dst = [torch.empty_like(src[0]) for _ in range(2)]
+    ids = torch.arange(C, dtype=torch.int32, device="cuda").reshape(1, 1, C)
+    for _ in range(3):
+        dkb.gather_kv(src[0], src[1], ids, None, chunk, dst[0], dst[1])
+    torch.cuda.synchronize()
+    assert torch.equal(dst[0], src[0]) and torch.equal(dst[1], src[1])
+    nbytes = 2 * src[0].nbytes
+    print(json.dumps({"calibration": "copy", "kernel": "k_gather", "launches": 3,
+                      "bytes_read_per_launch": nbytes, "bytes_written_per_launch": nbytes}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -102,6 +262,12 @@ def main():
         w = w.with_(layers=args.layers)
     dev = "cuda"
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    if w.host_pool:
+        bench_host_pool(args, w)
+        return
 
     t0 = time.time()
     qs = [synth.make_queries(w, args.seed, layer=l, device=dev) for l in range(w.layers)]

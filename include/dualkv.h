@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define DK_ABI_VERSION 2
+#define DK_ABI_VERSION 3
 
 typedef enum {
     DK_OK = 0,
@@ -58,6 +58,14 @@ typedef enum { DK_F32 = 0, DK_BF16 = 1 } dk_dtype;
 
 /* How the G query heads of one KV head combine into one chunk score. */
 typedef enum { DK_REDUCE_MEAN = 0, DK_REDUCE_MAX = 1 } dk_group_reduce;
+
+/* Where dk_gather_kv reads its source pool from. */
+typedef enum {
+    DK_SRC_DEVICE = 0,       /* device memory; one kernel                                  */
+    DK_SRC_HOST_COPY = 1,    /* pinned host memory; one hipMemcpyAsync per run of chunks   */
+    DK_SRC_HOST_MAPPED = 2   /* pinned host memory read by the gather kernel through its
+                                device mapping (zero-copy over PCIe); one kernel            */
+} dk_src_kind;
 
 typedef struct { int64_t b, h, t; } dk_strides;   /* element strides of dims 0, 1, 2 */
 
@@ -214,22 +222,31 @@ dk_status dk_union_select(const int32_t* topk_idx, int B, int Hkv, int T, int k,
  * src_chunk, dst_slot : int32 [B, Hkv, N].   count : int32 [B, Hkv] (NULL: N each).
  * src_blocks          : chunks in the source pool; ids outside [0, src_blocks) are skipped.
  * dst_blocks          : slots in the destination; ids outside [0, dst_blocks) are skipped.
- * src_is_host = 0     : K_src/V_src and the lists are device memory; one kernel on `stream`.
- * src_is_host = 1     : K_src/V_src are pinned host memory (hipHostMalloc) and
- *                       src_chunk, dst_slot, count are host-readable and final
- *                       when the call is made; the call issues one
- *                       hipMemcpyAsync (2-D when rows are strided) per run of
- *                       consecutive chunks on `stream` and returns after issuing.
+ * src_kind = DK_SRC_DEVICE      : K_src/V_src and the lists are device memory;
+ *                                 one kernel on `stream`.
+ * src_kind = DK_SRC_HOST_COPY   : K_src/V_src are pinned host memory (hipHostMalloc)
+ *                                 and src_chunk, dst_slot, count are host-readable and
+ *                                 final when the call is made; the call issues one
+ *                                 hipMemcpyAsync (2-D when rows are strided) per run of
+ *                                 consecutive chunks on `stream` and returns after
+ *                                 issuing.  Every copy costs a few microseconds of host
+ *                                 time, so scattered misses are API-bound.
+ * src_kind = DK_SRC_HOST_MAPPED : K_src/V_src are pinned host memory, the lists are
+ *                                 device memory; one kernel on `stream` reads the pool
+ *                                 through its device mapping over PCIe.  Fully
+ *                                 asynchronous: no host synchronisation on the lists.
  * Errors              : DK_ERR_INVALID_ARG unless sizes >= 1, N >= 0, pointers
- *                       non-NULL (dst_slot and count may be NULL); DK_ERR_UNSUPPORTED
- *                       unless the 16-byte alignment rule holds.
+ *                       non-NULL (dst_slot and count may be NULL), src_kind is one
+ *                       of the above and, for the host kinds, K_src and V_src are
+ *                       pinned host memory known to HIP; DK_ERR_UNSUPPORTED unless
+ *                       the 16-byte alignment rule holds.
  */
 dk_status dk_gather_kv(const void* K_src, const void* V_src, dk_dtype dt, dk_strides src_s,
                        int B, int Hkv, int chunk, int d,
                        const int32_t* src_chunk, const int32_t* dst_slot, const int32_t* count,
                        int N, int src_blocks,
                        void* K_dst, void* V_dst, dk_strides dst_s, int dst_blocks,
-                       int src_is_host, void* stream);
+                       int src_kind, void* stream);
 
 /*
  * dk_sparse_decode_attn - attention of every query head over its own chunks,

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libdualkv.so")
 DK_OK, DK_ERR_INVALID_ARG, DK_ERR_UNSUPPORTED, DK_ERR_HIP = 0, 1, 2, 3
 DK_F32, DK_BF16 = 0, 1
 DK_REDUCE_MEAN, DK_REDUCE_MAX = 0, 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 _STATUS = {0: "DK_OK", 1: "DK_ERR_INVALID_ARG", 2: "DK_ERR_UNSUPPORTED", 3: "DK_ERR_HIP"}
 
@@ -222,29 +222,41 @@ def union_select(topk_idx: torch.Tensor, C: int, union_ids=None, member=None, co
     return union_ids, member, count, overlap
 
 
+DK_SRC_DEVICE, DK_SRC_HOST_COPY, DK_SRC_HOST_MAPPED = 0, 1, 2
+
+
 def gather_kv(K_src, V_src, src_chunk, count, chunk, K_dst, V_dst, dst_slot=None,
               src_blocks=None, dst_blocks=None, stream=None):
     """Copy chunks src_chunk[b, g, j] (j < count[b, g]) into slots of K_dst / V_dst.
 
-    With device pools this is one kernel; with pinned host pools the lists must
-    be host tensors and the copies are hipMemcpyAsync calls on `stream`.
+    The source kind follows from where the tensors live:
+      device pool                          -> one gather kernel;
+      pinned host pool, host (CPU) lists   -> hipMemcpyAsync per run of chunks;
+      pinned host pool, device lists       -> one gather kernel reading the pool
+                                              through its device mapping (zero-copy).
     """
     B, Hkv, L, d = K_src.shape
     N = src_chunk.shape[2]
-    host = not K_src.is_cuda
-    if host and not K_src.is_pinned():
+    host_pool = not K_src.is_cuda
+    if host_pool and not (K_src.is_pinned() and V_src.is_pinned()):
         raise ValueError("a host KV pool must be in pinned memory")
+    lists_on_host = not src_chunk.is_cuda
+    if not host_pool and lists_on_host:
+        raise ValueError("a device KV pool needs device lists")
+    kind = (DK_SRC_DEVICE if not host_pool else
+            DK_SRC_HOST_COPY if lists_on_host else DK_SRC_HOST_MAPPED)
     for name, t in (("src_chunk", src_chunk), ("dst_slot", dst_slot), ("count", count)):
-        if t is not None and (t.is_cuda == host or t.dtype != torch.int32 or not t.is_contiguous()):
-            raise ValueError(f"{name}: int32 contiguous, on the {'host' if host else 'device'}")
+        if t is not None and (t.is_cuda == lists_on_host or t.dtype != torch.int32 or not t.is_contiguous()):
+            raise ValueError(f"{name}: int32 contiguous, on the same side as src_chunk")
     if src_blocks is None:
         src_blocks = L // chunk
     if dst_blocks is None:
         dst_blocks = K_dst.shape[2] // chunk
     _check(lib.dk_gather_kv(_ptr(K_src), _ptr(V_src), _dtype(K_src), pool_strides(K_src), B, Hkv,
                             chunk, d, _ptr(src_chunk), _ptr(dst_slot), _ptr(count), N, src_blocks,
-                            _ptr(K_dst), _ptr(V_dst), pool_strides(K_dst), dst_blocks, int(host),
+                            _ptr(K_dst), _ptr(V_dst), pool_strides(K_dst), dst_blocks, kind,
                             _stream(stream)))
+    return kind
 
 
 def attn_workspace_size(B, Hkv, T, Hq, dv, N, chunk) -> int:

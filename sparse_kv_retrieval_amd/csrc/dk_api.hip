@@ -34,6 +34,17 @@ bool strides_ok(dk_strides s, int esz) {
     return (s.b * esz) % 16 == 0 && (s.h * esz) % 16 == 0 && (s.t * esz) % 16 == 0;
 }
 
+// Device address of pinned host memory, or nullptr when `p` is not host memory
+// that HIP has pinned (pageable memory, device memory, unknown pointers).
+void* mapped_host_ptr(const void* p) {
+    hipPointerAttribute_t a{};
+    if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+        (void)hipGetLastError();   // the query's failure is an answer, not a sticky error
+        return nullptr;
+    }
+    return a.type == hipMemoryTypeHost ? a.devicePointer : nullptr;
+}
+
 #define DK_REQUIRE(cond, status, ...) \
     do {                              \
         if (!(cond)) return fail(status, __VA_ARGS__); \
@@ -155,7 +166,7 @@ dk_status dk_union_select(const int32_t* topk_idx, int B, int Hkv, int T, int k,
 dk_status dk_gather_kv(const void* K_src, const void* V_src, dk_dtype dt, dk_strides src_s, int B,
                        int Hkv, int chunk, int d, const int32_t* src_chunk, const int32_t* dst_slot,
                        const int32_t* count, int N, int src_blocks, void* K_dst, void* V_dst,
-                       dk_strides dst_s, int dst_blocks, int src_is_host, void* stream) {
+                       dk_strides dst_s, int dst_blocks, int src_kind, void* stream) {
     g_err.clear();
     const int esz = dtype_size(dt);
     DK_REQUIRE(K_src && V_src && K_dst && V_dst && src_chunk, DK_ERR_INVALID_ARG,
@@ -163,8 +174,8 @@ dk_status dk_gather_kv(const void* K_src, const void* V_src, dk_dtype dt, dk_str
     DK_REQUIRE(esz != 0, DK_ERR_INVALID_ARG, "dk_gather_kv: unknown dtype %d", (int)dt);
     DK_REQUIRE(B >= 1 && Hkv >= 1 && chunk >= 1 && d >= 1 && N >= 0 && src_blocks >= 0 && dst_blocks >= 0,
                DK_ERR_INVALID_ARG, "dk_gather_kv: sizes out of range");
-    DK_REQUIRE(src_is_host == 0 || src_is_host == 1, DK_ERR_INVALID_ARG,
-               "dk_gather_kv: src_is_host must be 0 or 1");
+    DK_REQUIRE(src_kind == DK_SRC_DEVICE || src_kind == DK_SRC_HOST_COPY || src_kind == DK_SRC_HOST_MAPPED,
+               DK_ERR_INVALID_ARG, "dk_gather_kv: src_kind must be 0, 1 or 2 (got %d)", src_kind);
     DK_REQUIRE(src_s.b >= 0 && src_s.h >= 0 && src_s.t >= 0 && dst_s.b >= 0 && dst_s.h >= 0 && dst_s.t >= 0,
                DK_ERR_INVALID_ARG, "dk_gather_kv: strides must be >= 0");
     DK_REQUIRE(aligned16(K_src) && aligned16(V_src) && aligned16(K_dst) && aligned16(V_dst) &&
@@ -172,9 +183,24 @@ dk_status dk_gather_kv(const void* K_src, const void* V_src, dk_dtype dt, dk_str
                DK_ERR_UNSUPPORTED, "dk_gather_kv: pools, strides and rows must be 16-byte aligned");
     hipStream_t st = (hipStream_t)stream;
     if (N == 0) return DK_OK;
-    if (!src_is_host) {
-        hipError_t e = dk::launch_gather(K_src, V_src, dt, src_s, B, Hkv, chunk, d, src_chunk, dst_slot,
+    const void* Ks = K_src;
+    const void* Vs = V_src;
+    if (src_kind != DK_SRC_DEVICE) {
+        void* km = mapped_host_ptr(K_src);
+        void* vm = mapped_host_ptr(V_src);
+        DK_REQUIRE(km && vm, DK_ERR_INVALID_ARG,
+                   "dk_gather_kv: a host source pool must be pinned host memory (hipHostMalloc)");
+        Ks = km;
+        Vs = vm;
+    }
+    if (src_kind == DK_SRC_DEVICE) {
+        hipError_t e = dk::launch_gather(Ks, Vs, dt, src_s, B, Hkv, chunk, d, src_chunk, dst_slot,
                                          count, N, src_blocks, K_dst, V_dst, dst_s, dst_blocks, st);
+        return e == hipSuccess ? DK_OK : hip_fail(e, "dk_gather_kv");
+    }
+    if (src_kind == DK_SRC_HOST_MAPPED) {
+        hipError_t e = dk::launch_gather_stream(Ks, Vs, dt, src_s, B, Hkv, chunk, d, src_chunk, dst_slot,
+                                                count, N, src_blocks, K_dst, V_dst, dst_s, dst_blocks, st);
         return e == hipSuccess ? DK_OK : hip_fail(e, "dk_gather_kv");
     }
     // Host pool: one copy per run of consecutive source chunks going to

@@ -160,6 +160,10 @@ hipError_t launch_gather(const void* K_src, const void* V_src, dk_dtype dt, dk_s
                          int Hkv, int chunk, int d, const int32_t* src_chunk, const int32_t* dst_slot,
                          const int32_t* count, int N, int src_blocks, void* K_dst, void* V_dst,
                          dk_strides ds, int dst_blocks, hipStream_t st);
+hipError_t launch_gather_stream(const void* K_src, const void* V_src, dk_dtype dt, dk_strides ss, int B,
+                         int Hkv, int chunk, int d, const int32_t* src_chunk, const int32_t* dst_slot,
+                         const int32_t* count, int N, int src_blocks, void* K_dst, void* V_dst,
+                         dk_strides ds, int dst_blocks, hipStream_t st);
 
 struct AttnPlan {
     int splits;        // union-range splits per (b, g)

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version():
-    assert lib.dk_abi_version() == 2
+    assert lib.dk_abi_version() == 3
 
 
 def err():
@@ -153,7 +153,8 @@ def gather(Ks=FAKE, Vs=FAKE, dt=1, ss=b.dk_strides(1 << 22, 1 << 19, 128), B=2, 
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(Ks=NULL), 1), (dict(src=NULL), 1), (dict(N=-1), 1), (dict(host=2), 1), (dict(dt=3), 1),
+    (dict(Ks=NULL), 1), (dict(src=NULL), 1), (dict(N=-1), 1), (dict(host=3), 1), (dict(host=-1), 1),
+    (dict(dt=3), 1),
     (dict(Kd=MIS), 2), (dict(d=4), 2), (dict(ss=b.dk_strides(-8, 0, 128)), 1),
 ])
 def test_gather_rejects(kw, status):
@@ -163,6 +164,14 @@ def test_gather_rejects(kw, status):
 
 def test_gather_empty_is_ok():
     assert gather(N=0) == 0
+
+
+@pytest.mark.parametrize("host", [1, 2])
+def test_gather_host_kinds_need_pinned_host_memory(host):
+    # FAKE is no pinned host allocation: both host kinds refuse it before any copy
+    # or launch (with or without a GPU present).
+    assert gather(host=host) == 1
+    assert "pinned host memory" in err()
 
 
 def test_attention_workspace_sizes():

@@ -369,8 +369,8 @@ def expected_gather(Ks, src, cnt, dst, Kd0, chunk):
     return out
 
 
-@pytest.mark.parametrize("host", [False, True])
-def test_gather(dkb, host):
+@pytest.mark.parametrize("kind", ["device", "host_copy", "host_mapped"])
+def test_gather(dkb, kind):
     rng = np.random.default_rng(9)
     B, H, L, d, chunk, N, S = 2, 3, 2048, 128, 32, 12, 24
     C = L // chunk
@@ -392,13 +392,21 @@ def test_gather(dkb, host):
             cnt[b, g] = n
     Kd = torch.zeros(B, H, S * chunk, d, dtype=torch.bfloat16, device="cuda")
     Vd = torch.zeros_like(Kd)
-    if host:
-        Ksrc, Vsrc = Ks.pin_memory(), Vs.pin_memory()
-        lists = [torch.from_numpy(x) for x in (src, cnt, dst)]
-    else:
+    if kind == "device":
         Ksrc, Vsrc = Ks.cuda(), Vs.cuda()
-        lists = [torch.from_numpy(x).cuda() for x in (src, cnt, dst)]
-    dkb.gather_kv(Ksrc, Vsrc, lists[0], lists[1], chunk, Kd, Vd, dst_slot=lists[2])
+    else:
+        # interior views of pinned allocations: the source pointers are not the
+        # allocation bases
+        Kp = torch.empty(B + 1, H, L, d, dtype=torch.bfloat16, pin_memory=True)
+        Vp = torch.empty(B + 1, H, L, d, dtype=torch.bfloat16, pin_memory=True)
+        Kp[1:].copy_(Ks)
+        Vp[1:].copy_(Vs)
+        Ksrc, Vsrc = Kp[1:], Vp[1:]
+    lists = [torch.from_numpy(x) for x in (src, cnt, dst)]
+    if kind != "host_copy":
+        lists = [x.cuda() for x in lists]
+    got_kind = dkb.gather_kv(Ksrc, Vsrc, lists[0], lists[1], chunk, Kd, Vd, dst_slot=lists[2])
+    assert got_kind == {"device": 0, "host_copy": 1, "host_mapped": 2}[kind]
     torch.cuda.synchronize()
     z = torch.zeros(B, H, S * chunk, d, dtype=torch.bfloat16)
     assert torch.equal(Kd.cpu(), expected_gather(Ks, src, cnt, dst, z, chunk))
@@ -474,4 +482,93 @@ def test_step_full_size_sampled(dkb, name, samples):
     ov = st.overlap.cpu().numpy()
     assert np.all(c == 2 * w.k - ov) and np.all((c >= w.k) & (c <= 2 * w.k))
     del K, V, lm
+    torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------------------
+# host-resident pool: hot cache, misses copied from pinned host memory
+# ----------------------------------------------------------------------------
+
+def run_host_pool_steps(dkb, w, steps, mode, seed, check_pairs=None):
+    """Run `steps` decode steps of the host-pool path and check every layer of every
+    step against the oracle: selection (near-ties counted), the hot-cache plan
+    (oracle state machine over the GPU's sets), the cache contents, attention."""
+    from sparse_kv_retrieval_amd.host_pool import HostPoolDecoder
+
+    qseq = [synth.make_query_sequence(w, seed, steps, layer=l, device="cuda") for l in range(w.layers)]
+    K, V = synth.make_kv_pool(w, seed, device="cuda", q0=qseq[0][0])
+    lm = dkb.build_landmarks(K, w.chunk)
+    sh = dkb.build_landmark_shadow(lm)
+    Kh_pin, Vh_pin = K.cpu().pin_memory(), V.cpu().pin_memory()
+    dec = HostPoolDecoder(Kh_pin, Vh_pin, lm, sh, T=w.T, Hq=w.Hq, k=w.k, scale=w.scale, layers=w.layers,
+                          mode=mode)
+    pairs = check_pairs or [(b, g) for b in range(w.B) for g in range(w.Hkv)]
+    Kf = {bg: synth.to_numpy_f64(K[bg[0]:bg[0] + 1, bg[1]:bg[1] + 1]) for bg in pairs}
+    Vf = {bg: synth.to_numpy_f64(V[bg[0]:bg[0] + 1, bg[1]:bg[1] + 1]) for bg in pairs}
+    res = [np.full((w.B, w.Hkv, dec.slots), -1) for _ in range(w.layers)]
+    near_total, hits, unions = 0, 0, 0
+    tol = ATOL[w.kv_dtype]
+    for s in range(steps):
+        dec.step([qseq[l][s] for l in range(w.layers)])
+        torch.cuda.synchronize()
+        for l in range(w.layers):
+            idx = dec.topk_idx[l].cpu().numpy()
+            plan = dec.plans[l]
+            # the plan, bit-exact, from the oracle's state machine on the GPU's sets
+            ru, rm, rc, ro = O.union_select(idx)
+            ref = O.cache_plan(res[l], ru, rc)
+            np.testing.assert_array_equal(dec.union_ids[l].cpu().numpy(), ru)
+            np.testing.assert_array_equal(dec.member[l].cpu().numpy(), rm)
+            for name in ("slot_of_union", "miss_chunk", "miss_slot", "miss_count", "hit_count"):
+                np.testing.assert_array_equal(getattr(plan, name).cpu().numpy(), ref[name], err_msg=name)
+            np.testing.assert_array_equal(plan.resident.cpu().numpy(), ref["new_resident"])
+            res[l] = ref["new_resident"]
+            if s:
+                hits += int(ref["hit_count"].sum())
+                unions += int(rc.sum())
+            # the hot cache holds exactly the union's chunks in their slots
+            sl = torch.from_numpy(ref["slot_of_union"]).cuda()
+            uid = torch.from_numpy(ru).cuda()
+            for b, g in pairs:
+                n = int(rc[b, g])
+                rows_c = (sl[b, g, :n, None] * w.chunk + torch.arange(w.chunk, device="cuda")).reshape(-1)
+                rows_p = (uid[b, g, :n, None] * w.chunk + torch.arange(w.chunk, device="cuda")).reshape(-1)
+                assert torch.equal(dec.Kc[l, b, g, rows_c], K[b, g, rows_p]), (s, l, b, g)
+                assert torch.equal(dec.Vc[l, b, g, rows_c], V[b, g, rows_p]), (s, l, b, g)
+            # selection and attention against the oracle
+            q = qseq[l][s]
+            qh_all = q.cpu().numpy().astype(np.float64)
+            out, lse = dec.out[l].cpu().numpy(), dec.lse[l].cpu().numpy()
+            for b, g in pairs:
+                qh = qh_all[b:b + 1, :, g * w.G:(g + 1) * w.G]
+                r = O.decode_step(qh, Kf[(b, g)], Vf[(b, g)], w.chunk, w.k, w.scale)
+                rows_diff, near, hard = compare_topk(idx[b:b + 1, g:g + 1], r["topk"], r["scores"])
+                assert not hard, (s, l, b, g, hard[:5])
+                near_total += near
+                if rows_diff == 0:
+                    ro_, rl_ = r["out"], r["lse"]
+                else:
+                    ro_, rl_ = O.sparse_attention(qh, Kf[(b, g)], Vf[(b, g)],
+                                                  idx[b:b + 1, g:g + 1].astype(np.int64), w.chunk, w.scale)
+                e1 = max_abs(out[b:b + 1, :, g * w.G:(g + 1) * w.G], ro_)
+                e2 = max_abs(lse[b:b + 1, :, g * w.G:(g + 1) * w.G], rl_)
+                assert e1 <= tol and e2 <= tol, (s, l, b, g, e1, e2)
+    return near_total, hits / max(unions, 1)
+
+
+@pytest.mark.parametrize("mode", ["mapped", "copy"])
+def test_host_pool_steps(dkb, mode):
+    w = shrink(WORKLOADS["host_b32_l128k"], B=2, L=8192, layers=2)
+    near, hit_rate = run_host_pool_steps(dkb, w, steps=4, mode=mode, seed=3)
+    print(f"host pool ({mode}): near-tie chunks {near}, steady-state hit rate {hit_rate:.3f}")
+    assert 0.0 < hit_rate < 1.0
+
+
+def test_host_pool_full_size_sampled(dkb):
+    """The host-pool workload at full size (B=32, L=128K) for two layers and three
+    steps, in the bench's launch configuration; oracle on sampled (b, g)."""
+    w = WORKLOADS["host_b32_l128k"].with_(layers=2)
+    near, hit_rate = run_host_pool_steps(dkb, w, steps=3, mode="mapped", seed=1,
+                                         check_pairs=[(0, 0), (17, 4), (31, 7)])
+    print(f"host_b32_l128k: near-tie chunks {near}, steady-state hit rate {hit_rate:.3f}")
     torch.cuda.empty_cache()
