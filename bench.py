@@ -54,6 +54,35 @@ def parse():
     return ap.parse_args()
 
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "sparse_kv_retrieval_amd", "csrc")
+
+
+def source_digest(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(files):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, call):
+    """HBM bytes per launch of `call` from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE passes, each scaled by the same counter's reading
+    for a plain copy of known size), or None when there is no summary for this
+    workload or the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = next((json.loads(line[5:]) for line in fh if line.startswith("json:")), None)
+    c = (rec or {}).get("calls", {}).get(call)
+    if not c or source_digest(c["sources"]) != c["digest"]:
+        return None
+    return c["bytes_per_launch"]
+
+
 def cpu_baseline(w, qs_host, K, V, budget_s, seed):
     """Time the fp64 CPU oracle on sampled (request, KV head, layer) units."""
     import numpy as np
@@ -364,8 +393,10 @@ def main():
     roofline = None
     if dominant:
         kd = kernels[dominant]
+        traffic = measured_traffic(w.name, dominant)
         roofline = {"bound": "hbm", "kernel": dominant, "achieved": kd["GBps"], "peak": HBM_PEAK_GBPS,
-                    "unit": "GB/s", "frac": round(kd["GBps"] / HBM_PEAK_GBPS, 4), "traffic": None}
+                    "unit": "GB/s", "frac": round(kd["GBps"] / HBM_PEAK_GBPS, 4),
+                    "traffic": None if traffic is None else int(traffic)}
 
     out = {
         "metric": METRIC,
