@@ -111,21 +111,17 @@ __global__ __launch_bounds__(kThreads) void k_attn_bf16_d128_g4t2(AttnArgs a) {
     const int ntiles = a.pool_blocks > 0 ? (u1 - u0) * tpc : 0;
     const int h = g * G + w;
 
-    // Q in registers: lane (key j, half hd) holds its 64-dim half of both queries
-    // as bf16 pairs, in the rotated order in which it reads its K half.
-    const int j = lane >> 1, hd = lane & 1;
-    uint4 qr[T][8];
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-        const float* qp = a.q + (((int64_t)b * T + t) * a.Hq + h) * D;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int ls = 8 * hd + ((i + 4 * hd) & 7);
-            const float4 x0 = *reinterpret_cast<const float4*>(qp + ls * 8);
-            const float4 x1 = *reinterpret_cast<const float4*>(qp + ls * 8 + 4);
-            qr[t][i] = make_uint4(pack_bf16x2(x0.x, x0.y), pack_bf16x2(x0.z, x0.w),
-                                  pack_bf16x2(x1.x, x1.y), pack_bf16x2(x1.z, x1.w));
-        }
+    // The block's eight query rows (row t * G + w) go through LDS once: one
+    // 16-byte load per thread, instead of every key lane fetching its own copy.
+    // They borrow the last ring stage, which the first DMA into it (issued after
+    // the first barrier of the tile loop) overwrites only once every wave has
+    // taken its rows into registers.
+    float* qs = reinterpret_cast<float*>(&sm.kv[NS - 1][0][0]);   // [R][D]
+    {
+        const int r = tid >> 5, c4 = tid & 31;   // 256 threads: 8 rows x 32 float4
+        const int t = r / G, hh = r - t * G;
+        *reinterpret_cast<float4*>(qs + r * D + c4 * 4) =
+            *reinterpret_cast<const float4*>(a.q + (((int64_t)b * T + t) * a.Hq + g * G + hh) * D + c4 * 4);
     }
     // This block's entries go to LDS, so the tile loop issues no vector loads of
     // its own besides the DMA (keeps the explicit vmcnt accounting exact).
@@ -138,13 +134,30 @@ __global__ __launch_bounds__(kThreads) void k_attn_bf16_d128_g4t2(AttnArgs a) {
         sm.erow[e] = (m ? c : 0) * a.chunk;
         sm.ebits[e] = m;
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    // Q in registers: lane (key j, half hd) holds its 64-dim half of both queries
+    // as bf16 pairs, in the rotated order in which it reads its K half.
+    const int j = lane >> 1, hd = lane & 1;
+    uint4 qr[T][8];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        const float* qp = qs + (t * G + w) * D;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int ls = 8 * hd + ((i + 4 * hd) & 7);
+            const float4 x0 = *reinterpret_cast<const float4*>(qp + ls * 8);
+            const float4 x1 = *reinterpret_cast<const float4*>(qp + ls * 8 + 4);
+            qr[t][i] = make_uint4(pack_bf16x2(x0.x, x0.y), pack_bf16x2(x0.z, x0.w),
+                                  pack_bf16x2(x1.x, x1.y), pack_bf16x2(x1.z, x1.w));
+        }
+    }
 #pragma unroll
     for (int t = 0; t < T; ++t)
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             asm volatile("" : "+v"(qr[t][i].x), "+v"(qr[t][i].y), "+v"(qr[t][i].z), "+v"(qr[t][i].w));
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
 
     // DMA geometry: wave w fills rows 8w..8w+7 of the K tile (pieces XOR-swizzled
     // by row) and of the V tile (plain), two 1 KiB wave-loads each.

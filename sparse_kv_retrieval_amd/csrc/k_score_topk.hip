@@ -41,7 +41,11 @@ __device__ __forceinline__ float4 nt_load_f4(const float* p) {
     return make_float4(v.x, v.y, v.z, v.w);
 }
 __device__ __forceinline__ u32x4_t nt_load_u4(const void* p) {
+#ifdef DK_SCORE_PLAIN_LOADS
+    return *reinterpret_cast<const u32x4_t*>(p);
+#else
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+#endif
 }
 __device__ __forceinline__ uint32_t f16_bits(float x) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
@@ -469,14 +473,18 @@ __global__ __launch_bounds__(kThreads) void k_build_shadow(const float* __restri
 // only.  Scores of one block's rows are staged in LDS and stored coalesced to
 // s_lo [B * Hkv, T, C] (fp32).
 // ---------------------------------------------------------------------------
+#ifndef DK_SCORE_LO_UNROLL
+#define DK_SCORE_LO_UNROLL 8   // 16-byte landmark loads in flight per lane
+#endif
+
 template <int D, int NQ, int T, bool MAXRED>
 __global__ __launch_bounds__(kThreads) void k_score_lo(const float* __restrict__ q, int Hq,
                                                       const uint16_t* __restrict__ lm16, int Hkv, int C,
                                                       float scale, int rows_per_block, int blocks_per_bg,
                                                       float* __restrict__ s_lo) {
-    constexpr int LPR = D / 8, RPW = kWave / LPR, U = 8;
+    constexpr int LPR = D / 8, RPW = kWave / LPR, U = DK_SCORE_LO_UNROLL;
     constexpr int G = MAXRED ? NQ / T : 0;
-    extern __shared__ float sres[];    // [T][rows_per_block]
+    extern __shared__ float sres[];    // [T][rows_per_block], then [NQ][D] query vectors
     const int blk = blockIdx.x % blocks_per_bg;
     const int bg = blockIdx.x / blocks_per_bg;
     const int b = bg / Hkv, g = bg - b * Hkv;
@@ -486,27 +494,31 @@ __global__ __launch_bounds__(kThreads) void k_score_lo(const float* __restrict__
     const int rp = lane / LPR, part = lane % LPR;
     const int Gq = Hq / Hkv;
 
+    // The query vectors of this (b, g) go through LDS once per block (one 16-byte
+    // global load per lane would otherwise be repeated by every row-lane group).
+    float* qs = sres + ((T * rows_per_block + 3) & ~3);   // [NQ][D], 16-byte aligned
+    for (int i = threadIdx.x; i < NQ * D; i += kThreads) {
+        const int v = i / D, e = i - v * D;
+        float x;
+        if constexpr (MAXRED) {
+            x = q[(((int64_t)b * T + v / G) * Hq + g * Gq + v % G) * D + e];
+        } else {
+            x = 0.f;
+            for (int h = 0; h < Gq; ++h) x += q[(((int64_t)b * T + v) * Hq + g * Gq + h) * D + e];
+            x = x / (float)Gq;
+        }
+        qs[i] = x;
+    }
+    __syncthreads();
     uint32_t qh[NQ][4];
 #pragma unroll
     for (int v = 0; v < NQ; ++v) {
-        float x[8];
-        if constexpr (MAXRED) {
-            const float* src = q + (((int64_t)b * T + v / G) * Hq + g * Gq + v % G) * D + part * 8;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = src[e];
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = 0.f;
-            for (int h = 0; h < Gq; ++h) {
-                const float* src = q + (((int64_t)b * T + v) * Hq + g * Gq + h) * D + part * 8;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] += src[e];
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = x[e] / (float)Gq;
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) qh[v][e] = f16_bits(x[2 * e]) | (f16_bits(x[2 * e + 1]) << 16);
+        const float4 x0 = *reinterpret_cast<const float4*>(qs + v * D + part * 8);
+        const float4 x1 = *reinterpret_cast<const float4*>(qs + v * D + part * 8 + 4);
+        qh[v][0] = f16_bits(x0.x) | (f16_bits(x0.y) << 16);
+        qh[v][1] = f16_bits(x0.z) | (f16_bits(x0.w) << 16);
+        qh[v][2] = f16_bits(x1.x) | (f16_bits(x1.y) << 16);
+        qh[v][3] = f16_bits(x1.z) | (f16_bits(x1.w) << 16);
     }
 
     const uint16_t* base = lm16 + ((int64_t)bg * C + row0) * D + part * 8;
@@ -801,7 +813,7 @@ hipError_t dispatch_split(int nq, int T, bool maxred, const float* q, int B, int
 template <int D, int NQ, int T, bool MAXRED>
 hipError_t launch_lo(const float* q, int B, int Hq, const uint16_t* lm16, int Hkv, int C, float scale,
                      const TopkPlan& p, float* s_lo, hipStream_t st) {
-    const size_t lds = (size_t)T * p.rows * 4;
+    const size_t lds = (((size_t)T * p.rows + 3) & ~(size_t)3) * 4 + (size_t)NQ * D * 4;
     const unsigned grid = (unsigned)((int64_t)B * Hkv * p.splits);
     hipLaunchKernelGGL((k_score_lo<D, NQ, T, MAXRED>), dim3(grid), dim3(kThreads), lds, st, q, Hq, lm16,
                        Hkv, C, scale, p.rows, p.splits, s_lo);
@@ -830,15 +842,23 @@ hipError_t dispatch_lo(int nq, int T, bool maxred, const float* q, int B, int Hq
 
 }  // namespace
 
+#ifndef DK_SCORE_LO_BLOCKS
+#define DK_SCORE_LO_BLOCKS 2048
+#endif
+#ifndef DK_SCORE_LO_MIN_ROWS
+#define DK_SCORE_LO_MIN_ROWS 256
+#endif
+
 TopkPlan plan_topk(int B, int Hkv, int T, int C, int k, bool shadow) {
     TopkPlan p{0, 0, 0};
     const int64_t bg = (int64_t)B * Hkv;
     if (shadow) {
-        // pass 1: ranges of rows for ~2048 blocks, at least 256 rows each, at most
-        // kMaxRows (LDS staging); pass 2 keeps every score of a (b, g) in LDS.
+        // pass 1: ranges of rows for about DK_SCORE_LO_BLOCKS blocks, at least
+        // DK_SCORE_LO_MIN_ROWS rows each, at most kMaxRows (LDS staging); pass 2
+        // keeps every score of a (b, g) in LDS.
         if (C > kShadowMaxC) return p;
-        int64_t s = (2048 + bg - 1) / bg;
-        int64_t by_rows = C / 256;
+        int64_t s = (DK_SCORE_LO_BLOCKS + bg - 1) / bg;
+        int64_t by_rows = C / DK_SCORE_LO_MIN_ROWS;
         if (by_rows < 1) by_rows = 1;
         if (s > by_rows) s = by_rows;
         const int64_t min_s = (C + kMaxRows - 1) / kMaxRows;
