@@ -3,9 +3,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload b64_l128k]
 
 A step is one pass of the whole hot path over every layer of the workload: per
-layer, chunk scores and top-k of both queries (dk_score_topk), their union
-(dk_union_select) and attention of both queries over their own chunks, read
-once per union chunk straight from the HBM pool (dk_sparse_decode_attn).
+layer, chunk scores, top-k of both queries and their union in one call
+(dk_score_topk_union), and attention of both queries over their own chunks,
+read once per union chunk straight from the HBM pool (dk_sparse_decode_attn).
 Landmarks (and their fp16 shadow) are built once before timing: they are fixed
 for the whole decode.
 Inputs are seeded synthetic tensors resident in HBM before the timed region.
@@ -321,10 +321,10 @@ def main():
     lm_bytes_layer = w.landmark_bytes()
     accuracy = float(np.mean(overlap)) / w.k
 
-    calls = ("score_topk", "union_select", "sparse_decode_attn")
+    calls = ("score_topk_union", "sparse_decode_attn")
     use_events = not args.no_events
     # one set of events per (step, layer), read only after the timed region
-    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(w.layers)]
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(w.layers)]
           for _ in range(args.steps)] if use_events else None
     call_ms = {c: 0.0 for c in calls}
 
@@ -334,17 +334,14 @@ def main():
             e = ev[record - 1][l] if record else None
             if record:
                 e[0].record()
-            dkb.score_topk(q, lm, w.k, w.scale, dkb.DK_REDUCE_MEAN, st.topk_idx, None, st.ws_topk,
-                           shadow=shadow)
+            dkb.score_topk_union(q, lm, w.k, w.scale, dkb.DK_REDUCE_MEAN, st.topk_idx, None, st.union_ids,
+                                 st.member, st.count, st.overlap, st.ws_topk, shadow=shadow)
             if record:
                 e[1].record()
-            dkb.union_select(st.topk_idx, w.C, st.union_ids, st.member, st.count, st.overlap)
-            if record:
-                e[2].record()
             dkb.sparse_decode_attn(q, K, V, st.union_ids, st.member, st.count, w.chunk, w.scale,
                                    out=st.out, lse=st.lse, ws=st.ws_attn)
             if record:
-                e[3].record()
+                e[2].record()
 
     for _ in range(args.warmup):
         step(0)
@@ -375,8 +372,8 @@ def main():
         score_bytes = (lm_bytes_layer // 2 + 2 * w.B * w.Hkv * w.T * w.C * 4
                        + w.B * w.Hkv * w.T * w.k * w.d * 4 + q_bytes)
     per_call_bytes = {
-        "score_topk": score_bytes,
-        "union_select": w.B * w.Hkv * w.T * w.k * 4 * 3,
+        # scores and selection, then the union: both sets read back, ids + bits written
+        "score_topk_union": score_bytes + w.B * w.Hkv * w.T * w.k * 4 * 3,
         "sparse_decode_attn": sel_bytes_step / w.layers,
     }
     for c in calls:

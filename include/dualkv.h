@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define DK_ABI_VERSION 3
+#define DK_ABI_VERSION 4
 
 typedef enum {
     DK_OK = 0,
@@ -159,6 +159,32 @@ dk_status dk_score_topk(const float* q, int B, int T, int Hq,
                         const dk_landmark_shadow* shadow,
                         int32_t* topk_idx, float* topk_score,
                         void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * dk_score_topk_union - dk_score_topk and dk_union_select (without a cache
+ * plan) of the same step in one call.
+ *
+ * DualDecoder "4.1": the index comes from the queries and the landmarks;
+ * Adaptive DHiSparse, Figure 3 (2): the queries' selections are resolved
+ * together.  With a landmark shadow the last of the T selection blocks of each
+ * (b, g) merges the union itself, so the step needs no separate union launch;
+ * otherwise the union runs as dk_union_select would.  Every output equals what
+ * dk_score_topk followed by dk_union_select(plan = NULL) writes.
+ *
+ * Arguments: as dk_score_topk, plus the union outputs of dk_union_select
+ * (union_ids int32 [B, Hkv, T*k], member uint8 [B, Hkv, T*k], union_count
+ * int32 [B, Hkv], overlap int32 [B, Hkv] or NULL).  ws: the same
+ * dk_score_topk_workspace_size bytes; contents on entry are ignored.
+ * Errors: those of dk_score_topk; DK_ERR_INVALID_ARG if a union output other
+ * than overlap is NULL; DK_ERR_UNSUPPORTED beyond dk_union_select's limits.
+ */
+dk_status dk_score_topk_union(const float* q, int B, int T, int Hq,
+                              const void* lm, dk_dtype lm_dtype, dk_strides ls, int Hkv, int C,
+                              int d, int k, float scale, dk_group_reduce reduce,
+                              const dk_landmark_shadow* shadow,
+                              int32_t* topk_idx, float* topk_score,
+                              int32_t* union_ids, uint8_t* member, int32_t* union_count,
+                              int32_t* overlap, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Hot-cache plan for the host-pool path (NULL in HBM-pool mode).

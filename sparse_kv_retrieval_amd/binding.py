@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libdualkv.so")
 DK_OK, DK_ERR_INVALID_ARG, DK_ERR_UNSUPPORTED, DK_ERR_HIP = 0, 1, 2, 3
 DK_F32, DK_BF16 = 0, 1
 DK_REDUCE_MEAN, DK_REDUCE_MAX = 0, 1
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 _STATUS = {0: "DK_OK", 1: "DK_ERR_INVALID_ARG", 2: "DK_ERR_UNSUPPORTED", 3: "DK_ERR_HIP"}
 
@@ -57,6 +57,8 @@ EXPORTS = [
     ("dk_score_topk_workspace_size", _Z, [_I, _I, _I, _I, _I, _I]),
     ("dk_score_topk", _I, [_P, _I, _I, _I, _P, _I, _S, _I, _I, _I, _I, _F, _I,
                            ctypes.POINTER(dk_landmark_shadow), _P, _P, _P, _Z, _P]),
+    ("dk_score_topk_union", _I, [_P, _I, _I, _I, _P, _I, _S, _I, _I, _I, _I, _F, _I,
+                                 ctypes.POINTER(dk_landmark_shadow), _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     ("dk_union_select", _I, [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, ctypes.POINTER(dk_cache_plan), _P]),
     ("dk_gather_kv", _I, [_P, _P, _I, _S, _I, _I, _I, _I, _P, _P, _P, _I, _I, _P, _P, _S, _I, _I, _P]),
     ("dk_attn_workspace_size", _Z, [_I, _I, _I, _I, _I, _I, _I]),
@@ -177,6 +179,39 @@ def score_topk(q: torch.Tensor, lm: torch.Tensor, k: int, scale: float, reduce: 
                              _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
                              _stream(stream)))
     return topk_idx, topk_score
+
+
+def score_topk_union(q: torch.Tensor, lm: torch.Tensor, k: int, scale: float,
+                     reduce: int = DK_REDUCE_MEAN, topk_idx=None, topk_score=None, union_ids=None,
+                     member=None, count=None, overlap=None, ws=None, want_scores=False,
+                     shadow: Shadow | None = None, stream=None):
+    """score_topk followed by union_select (no cache plan), as one library call."""
+    B, T, Hq, d = q.shape
+    _, Hkv, C, _ = lm.shape
+    _need(q, torch.float32, (B, T, Hq, d), "q")
+    dev = q.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    if topk_idx is None:
+        topk_idx = torch.empty(B, Hkv, T, k, **i32)
+    if topk_score is None and want_scores:
+        topk_score = torch.empty(B, Hkv, T, k, dtype=torch.float32, device=dev)
+    if union_ids is None:
+        union_ids = torch.empty(B, Hkv, T * k, **i32)
+    if member is None:
+        member = torch.empty(B, Hkv, T * k, dtype=torch.uint8, device=dev)
+    if count is None:
+        count = torch.empty(B, Hkv, **i32)
+    if overlap is None:
+        overlap = torch.empty(B, Hkv, **i32)
+    nbytes = score_topk_workspace_size(B, Hkv, T, C, k, shadow is not None)
+    if ws is None and nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    csh = ctypes.byref(shadow.as_c()) if shadow is not None else None
+    _check(lib.dk_score_topk_union(_ptr(q), B, T, Hq, _ptr(lm), _dtype(lm), pool_strides(lm), Hkv, C, d,
+                                   k, float(scale), int(reduce), csh, _ptr(topk_idx), _ptr(topk_score),
+                                   _ptr(union_ids), _ptr(member), _ptr(count), _ptr(overlap), _ptr(ws),
+                                   0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+    return topk_idx, topk_score, union_ids, member, count, overlap
 
 
 @dataclass
@@ -301,9 +336,9 @@ def sparse_decode_attn(q, K, V, block_ids, member, count, chunk: int, scale: flo
 # ----------------------------------------------------------------------------
 
 class DecodeStep:
-    """Preallocated buffers for score_topk -> union_select -> sparse_decode_attn.
+    """Preallocated buffers for score_topk_union -> sparse_decode_attn.
 
-    ``run(q, lm, K, V)`` enqueues the three calls on the current stream and
+    ``run(q, lm, K, V)`` enqueues the two calls on the current stream and
     returns the output buffers (reused across calls).
     """
 
@@ -328,10 +363,9 @@ class DecodeStep:
         self.lse = torch.empty(B, T, Hq, dtype=torch.float32, device=device)
 
     def run(self, q, lm, K, V, stream=None):
-        score_topk(q, lm, self.k, self.scale, self.reduce, self.topk_idx, self.topk_score,
-                   self.ws_topk, shadow=self.shadow, stream=stream)
-        union_select(self.topk_idx, self.C, self.union_ids, self.member, self.count, self.overlap,
-                     stream=stream)
+        score_topk_union(q, lm, self.k, self.scale, self.reduce, self.topk_idx, self.topk_score,
+                         self.union_ids, self.member, self.count, self.overlap, self.ws_topk,
+                         shadow=self.shadow, stream=stream)
         sparse_decode_attn(q, K, V, self.union_ids, self.member, self.count, self.chunk, self.scale,
                            out=self.out, lse=self.lse, ws=self.ws_attn, stream=stream)
         return self.out, self.lse

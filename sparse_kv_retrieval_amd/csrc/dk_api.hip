@@ -97,41 +97,94 @@ size_t dk_score_topk_workspace_size(int B, int Hkv, int T, int C, int k, int wit
     return dk::plan_topk(B, Hkv, T, C, k, with_shadow != 0).ws_bytes;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by dk_score_topk and dk_score_topk_union; `fn` names
+// the entry point in the messages.
+dk_status check_score_topk(const char* fn, const float* q, int B, int T, int Hq, const void* lm,
+                           dk_dtype lm_dtype, dk_strides ls, int Hkv, int C, int d, int k, float scale,
+                           dk_group_reduce reduce, const dk_landmark_shadow* shadow, int32_t* topk_idx,
+                           void* ws, size_t ws_bytes, dk::TopkPlan* plan_out) {
+    DK_REQUIRE(q && lm && topk_idx, DK_ERR_INVALID_ARG, "%s: q, lm, topk_idx must be non-NULL", fn);
+    DK_REQUIRE(B >= 1 && Hq >= 1 && Hkv >= 1 && C >= 1 && d >= 1, DK_ERR_INVALID_ARG,
+               "%s: B, Hq, Hkv, C, d must be >= 1", fn);
+    DK_REQUIRE(T == 1 || T == 2, DK_ERR_INVALID_ARG, "%s: T must be 1 or 2 (got %d)", fn, T);
+    DK_REQUIRE(Hq % Hkv == 0, DK_ERR_INVALID_ARG, "%s: Hq (%d) %% Hkv (%d) != 0", fn, Hq, Hkv);
+    DK_REQUIRE(k >= 1 && k <= C, DK_ERR_INVALID_ARG, "%s: need 1 <= k (%d) <= C (%d)", fn, k, C);
+    DK_REQUIRE(reduce == DK_REDUCE_MEAN || reduce == DK_REDUCE_MAX, DK_ERR_INVALID_ARG,
+               "%s: unknown reduce %d", fn, (int)reduce);
+    DK_REQUIRE(std::isfinite(scale), DK_ERR_INVALID_ARG, "%s: scale must be finite", fn);
+    DK_REQUIRE(!shadow || (shadow->lm16 && shadow->norm_max), DK_ERR_INVALID_ARG,
+               "%s: shadow->lm16 and shadow->norm_max must be non-NULL", fn);
+    DK_REQUIRE(lm_dtype == DK_F32, DK_ERR_UNSUPPORTED, "%s: landmarks must be DK_F32", fn);
+    DK_REQUIRE(d == 64 || d == 128, DK_ERR_UNSUPPORTED, "%s: d must be 64 or 128 (got %d)", fn, d);
+    DK_REQUIRE(C <= 65536, DK_ERR_UNSUPPORTED, "%s: C must be <= 65536 (got %d)", fn, C);
+    const int G = Hq / Hkv;
+    if (reduce == DK_REDUCE_MAX) {
+        const int nq = G * T;
+        DK_REQUIRE(nq <= 16 && (nq & (nq - 1)) == 0, DK_ERR_UNSUPPORTED,
+                   "%s: max reduction needs G*T a power of two <= 16 (got %d)", fn, nq);
+    }
+    DK_REQUIRE(aligned16(q) && aligned16(lm) && strides_ok(ls, 4) && (!shadow || aligned16(shadow->lm16)),
+               DK_ERR_UNSUPPORTED, "%s: q, lm, lm's strides and lm16 must be 16-byte aligned", fn);
+    const dk::TopkPlan plan = dk::plan_topk(B, Hkv, T, C, k, shadow != nullptr);
+    DK_REQUIRE(plan.splits > 0, DK_ERR_UNSUPPORTED, "%s: no plan for C=%d k=%d%s", fn, C, k,
+               shadow ? " with a shadow (C <= 6144)" : "");
+    DK_REQUIRE(ws_bytes >= plan.ws_bytes && (plan.ws_bytes == 0 || ws), DK_ERR_INVALID_ARG,
+               "%s: workspace needs %zu bytes (got %zu)", fn, plan.ws_bytes, ws_bytes);
+    *plan_out = plan;
+    return DK_OK;
+}
+
+// Limits of the union stage (one block per (b, g), everything in LDS).
+dk_status check_union(const char* fn, int T, int k, int slots, bool with_plan) {
+    const int N = T * k;
+    DK_REQUIRE(N <= 8192 && slots <= 8192, DK_ERR_UNSUPPORTED, "%s: T*k and slots must be <= 8192", fn);
+    const int64_t lds = (int64_t)(3 * k + 1 + N + 8 + (with_plan ? 2 * slots + N : 0)) * 4;
+    DK_REQUIRE(lds <= 65536, DK_ERR_UNSUPPORTED, "%s: k and slots too large for one block", fn);
+    return DK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 dk_status dk_score_topk(const float* q, int B, int T, int Hq, const void* lm, dk_dtype lm_dtype,
                         dk_strides ls, int Hkv, int C, int d, int k, float scale,
                         dk_group_reduce reduce, const dk_landmark_shadow* shadow, int32_t* topk_idx,
                         float* topk_score, void* ws, size_t ws_bytes, void* stream) {
     g_err.clear();
-    DK_REQUIRE(q && lm && topk_idx, DK_ERR_INVALID_ARG, "dk_score_topk: q, lm, topk_idx must be non-NULL");
-    DK_REQUIRE(B >= 1 && Hq >= 1 && Hkv >= 1 && C >= 1 && d >= 1, DK_ERR_INVALID_ARG,
-               "dk_score_topk: B, Hq, Hkv, C, d must be >= 1");
-    DK_REQUIRE(T == 1 || T == 2, DK_ERR_INVALID_ARG, "dk_score_topk: T must be 1 or 2 (got %d)", T);
-    DK_REQUIRE(Hq % Hkv == 0, DK_ERR_INVALID_ARG, "dk_score_topk: Hq (%d) %% Hkv (%d) != 0", Hq, Hkv);
-    DK_REQUIRE(k >= 1 && k <= C, DK_ERR_INVALID_ARG, "dk_score_topk: need 1 <= k (%d) <= C (%d)", k, C);
-    DK_REQUIRE(reduce == DK_REDUCE_MEAN || reduce == DK_REDUCE_MAX, DK_ERR_INVALID_ARG,
-               "dk_score_topk: unknown reduce %d", (int)reduce);
-    DK_REQUIRE(std::isfinite(scale), DK_ERR_INVALID_ARG, "dk_score_topk: scale must be finite");
-    DK_REQUIRE(!shadow || (shadow->lm16 && shadow->norm_max), DK_ERR_INVALID_ARG,
-               "dk_score_topk: shadow->lm16 and shadow->norm_max must be non-NULL");
-    DK_REQUIRE(lm_dtype == DK_F32, DK_ERR_UNSUPPORTED, "dk_score_topk: landmarks must be DK_F32");
-    DK_REQUIRE(d == 64 || d == 128, DK_ERR_UNSUPPORTED, "dk_score_topk: d must be 64 or 128 (got %d)", d);
-    DK_REQUIRE(C <= 65536, DK_ERR_UNSUPPORTED, "dk_score_topk: C must be <= 65536 (got %d)", C);
-    const int G = Hq / Hkv;
-    if (reduce == DK_REDUCE_MAX) {
-        const int nq = G * T;
-        DK_REQUIRE(nq <= 16 && (nq & (nq - 1)) == 0, DK_ERR_UNSUPPORTED,
-                   "dk_score_topk: max reduction needs G*T a power of two <= 16 (got %d)", nq);
-    }
-    DK_REQUIRE(aligned16(q) && aligned16(lm) && strides_ok(ls, 4) && (!shadow || aligned16(shadow->lm16)),
-               DK_ERR_UNSUPPORTED, "dk_score_topk: q, lm, lm's strides and lm16 must be 16-byte aligned");
-    const dk::TopkPlan plan = dk::plan_topk(B, Hkv, T, C, k, shadow != nullptr);
-    DK_REQUIRE(plan.splits > 0, DK_ERR_UNSUPPORTED, "dk_score_topk: no plan for C=%d k=%d%s", C, k,
-               shadow ? " with a shadow (C <= 6144)" : "");
-    DK_REQUIRE(ws_bytes >= plan.ws_bytes && (plan.ws_bytes == 0 || ws), DK_ERR_INVALID_ARG,
-               "dk_score_topk: workspace needs %zu bytes (got %zu)", plan.ws_bytes, ws_bytes);
+    dk::TopkPlan plan{};
+    const dk_status s = check_score_topk("dk_score_topk", q, B, T, Hq, lm, lm_dtype, ls, Hkv, C, d, k, scale,
+                                         reduce, shadow, topk_idx, ws, ws_bytes, &plan);
+    if (s != DK_OK) return s;
     hipError_t e = dk::launch_score_topk(q, B, T, Hq, (const float*)lm, ls, Hkv, C, d, k, scale, reduce,
-                                         shadow, topk_idx, topk_score, ws, plan, (hipStream_t)stream);
+                                         shadow, topk_idx, topk_score, ws, plan, nullptr, (hipStream_t)stream);
     return e == hipSuccess ? DK_OK : hip_fail(e, "dk_score_topk");
+}
+
+dk_status dk_score_topk_union(const float* q, int B, int T, int Hq, const void* lm, dk_dtype lm_dtype,
+                              dk_strides ls, int Hkv, int C, int d, int k, float scale,
+                              dk_group_reduce reduce, const dk_landmark_shadow* shadow,
+                              int32_t* topk_idx, float* topk_score, int32_t* union_ids, uint8_t* member,
+                              int32_t* union_count, int32_t* overlap, void* ws, size_t ws_bytes,
+                              void* stream) {
+    g_err.clear();
+    const char* fn = "dk_score_topk_union";
+    dk::TopkPlan plan{};
+    dk_status s = check_score_topk(fn, q, B, T, Hq, lm, lm_dtype, ls, Hkv, C, d, k, scale, reduce, shadow,
+                                   topk_idx, ws, ws_bytes, &plan);
+    if (s != DK_OK) return s;
+    DK_REQUIRE(union_ids && member && union_count, DK_ERR_INVALID_ARG,
+               "%s: union_ids, member, union_count must be non-NULL", fn);
+    s = check_union(fn, T, k, 0, false);
+    if (s != DK_OK) return s;
+    const dk::UnionOut un{union_ids, member, union_count, overlap};
+    hipError_t e = dk::launch_score_topk(q, B, T, Hq, (const float*)lm, ls, Hkv, C, d, k, scale, reduce,
+                                         shadow, topk_idx, topk_score, ws, plan, &un, (hipStream_t)stream);
+    return e == hipSuccess ? DK_OK : hip_fail(e, fn);
 }
 
 dk_status dk_union_select(const int32_t* topk_idx, int B, int Hkv, int T, int k, int C,
@@ -154,10 +207,8 @@ dk_status dk_union_select(const int32_t* topk_idx, int B, int Hkv, int T, int k,
                    "dk_union_select: cache slots (%d) must be >= T*k (%d)", plan->slots, N);
         slots = plan->slots;
     }
-    DK_REQUIRE(N <= 8192 && slots <= 8192, DK_ERR_UNSUPPORTED,
-               "dk_union_select: T*k and slots must be <= 8192");
-    const int64_t lds = (int64_t)(3 * k + 1 + N + 8 + (plan ? 2 * slots + N : 0)) * 4;
-    DK_REQUIRE(lds <= 65536, DK_ERR_UNSUPPORTED, "dk_union_select: k and slots too large for one block");
+    const dk_status s = check_union("dk_union_select", T, k, slots, plan != nullptr);
+    if (s != DK_OK) return s;
     hipError_t e = dk::launch_union(topk_idx, B, Hkv, T, k, C, union_ids, member, union_count, overlap,
                                     plan, (hipStream_t)stream);
     return e == hipSuccess ? DK_OK : hip_fail(e, "dk_union_select");

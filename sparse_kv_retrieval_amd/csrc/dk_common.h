@@ -145,10 +145,17 @@ struct TopkPlan {
     size_t ws_bytes;   // candidate buffer bytes (0 when splits == 1)
 };
 TopkPlan plan_topk(int B, int Hkv, int T, int C, int k, bool shadow);
+// Union outputs computed in the same call as the top-k (dk_score_topk_union).
+struct UnionOut {
+    int32_t* ids;        // [B, Hkv, T*k]
+    uint8_t* member;     // [B, Hkv, T*k]
+    int32_t* count;      // [B, Hkv]
+    int32_t* overlap;    // [B, Hkv] or null
+};
 hipError_t launch_score_topk(const float* q, int B, int T, int Hq, const float* lm, dk_strides ls,
                              int Hkv, int C, int d, int k, float scale, dk_group_reduce reduce,
                              const dk_landmark_shadow* shadow, int32_t* topk_idx, float* topk_score,
-                             void* ws, const TopkPlan& plan, hipStream_t st);
+                             void* ws, const TopkPlan& plan, const UnionOut* un, hipStream_t st);
 hipError_t launch_build_shadow(const float* lm, dk_strides ls, int B, int Hkv, int C, int d,
                                uint16_t* lm16, float* norm_max, hipStream_t st);
 

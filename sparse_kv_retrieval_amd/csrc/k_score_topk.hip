@@ -22,6 +22,7 @@
 // products = dot product with the mean query), so each landmark row costs
 // T dot products; the max reduction keeps all G*T vectors.
 #include "dk_common.h"
+#include "dk_union_core.h"
 
 namespace dk {
 namespace {
@@ -481,7 +482,7 @@ template <int D, int NQ, int T, bool MAXRED>
 __global__ __launch_bounds__(kThreads) void k_score_lo(const float* __restrict__ q, int Hq,
                                                       const uint16_t* __restrict__ lm16, int Hkv, int C,
                                                       float scale, int rows_per_block, int blocks_per_bg,
-                                                      float* __restrict__ s_lo) {
+                                                      float* __restrict__ s_lo, uint32_t* __restrict__ arrivals) {
     constexpr int LPR = D / 8, RPW = kWave / LPR, U = DK_SCORE_LO_UNROLL;
     constexpr int G = MAXRED ? NQ / T : 0;
     extern __shared__ float sres[];    // [T][rows_per_block], then [NQ][D] query vectors
@@ -493,6 +494,8 @@ __global__ __launch_bounds__(kThreads) void k_score_lo(const float* __restrict__
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int rp = lane / LPR, part = lane % LPR;
     const int Gq = Hq / Hkv;
+    // the selection kernel that follows counts its (b, g, t) blocks from zero
+    if (arrivals && blk == 0 && threadIdx.x == 0) arrivals[bg] = 0u;
 
     // The query vectors of this (b, g) go through LDS once per block (one 16-byte
     // global load per lane would otherwise be repeated by every row-lane group).
@@ -571,11 +574,22 @@ __global__ __launch_bounds__(kThreads) void k_score_lo(const float* __restrict__
 // chunk, s the fp32 score this kernel computes), their fp32 re-scores, and the
 // exact top-k among them (ties to the lower id), written in ascending order.
 // ---------------------------------------------------------------------------
+// Agent-scope relaxed store / load: written through to, and read from, the
+// device-coherent level, so another block (on any XCD) that reads the value
+// after a device-scope atomic sees it without a whole-cache fence.
+__device__ __forceinline__ void store_agent(int32_t* p, int32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t load_agent(const int32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int D, bool MAXRED>
 __global__ __launch_bounds__(kThreads) void k_select_exact(
     const float* __restrict__ q, int T, int Hq, const float* __restrict__ lm, dk_strides ls,
     const float* __restrict__ norm_max, const float* __restrict__ s_lo, int Hkv, int C, int k,
-    float scale, int32_t* __restrict__ topk_idx, float* __restrict__ topk_score) {
+    float scale, int32_t* __restrict__ topk_idx, float* __restrict__ topk_score, UnionOut un,
+    uint32_t* __restrict__ arrivals) {
     constexpr int LPR = D / 8;                 // lanes per fp32 row, 8 floats each
     constexpr int RPW = kWave / LPR;
     extern __shared__ uint32_t smem2[];
@@ -758,7 +772,7 @@ __global__ __launch_bounds__(kThreads) void k_select_exact(
                 if (take) {
                     const int jpos = base + __builtin_popcountll(tm & below);
                     if (jpos < k) {
-                        oi[jpos] = cand[lane + 64 * v];
+                        store_agent(oi + jpos, cand[lane + 64 * v]);
                         if (os) os[jpos] = key_score(x[v]);
                     }
                 }
@@ -768,9 +782,41 @@ __global__ __launch_bounds__(kThreads) void k_select_exact(
         }
     } else {
         block_topk(keys, ncand, k, hist, scratch, bc, [&](int jpos, int i, uint32_t key) {
-            oi[jpos] = cand[i];
+            store_agent(oi + jpos, cand[i]);
             if (os) os[jpos] = key_score(key);
         });
+    }
+    if (un.ids == nullptr) return;
+
+    // Union of the (b, g)'s T sets, by the last of its T blocks to finish.  The
+    // ids above were stored at agent scope; once every lane's stores have
+    // completed the block counts itself in, and the last block reads all T sets
+    // back at agent scope.  The score pass of the same call zeroed the counter;
+    // the last block rezeroes it.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0)
+        scratch[7] = __hip_atomic_fetch_add(&arrivals[bg], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                     (unsigned)(T - 1);
+    __syncthreads();
+    if (!scratch[7]) return;
+    int32_t* s0 = (int32_t*)keys;        // keys[] and cand[] are free now
+    int32_t* s1 = s0 + k;
+    int32_t* dup_pre = s1 + k;
+    const int32_t* src = topk_idx + (int64_t)bg * T * k;
+    for (int i = tid; i < k; i += kThreads) {
+        s0[i] = load_agent(src + i);
+        s1[i] = T == 2 ? load_agent(src + k + i) : 0;
+    }
+    __syncthreads();
+    const int N = T * k;
+    int nshared;
+    const int count = block_union_two(s0, s1, T, k, un.ids + (int64_t)bg * N, un.member + (int64_t)bg * N,
+                                      dup_pre, scratch, nullptr, &nshared);
+    if (tid == 0) {
+        un.count[bg] = count;
+        if (un.overlap) un.overlap[bg] = nshared;
+        arrivals[bg] = 0u;
     }
 }
 
@@ -812,19 +858,21 @@ hipError_t dispatch_split(int nq, int T, bool maxred, const float* q, int B, int
 
 template <int D, int NQ, int T, bool MAXRED>
 hipError_t launch_lo(const float* q, int B, int Hq, const uint16_t* lm16, int Hkv, int C, float scale,
-                     const TopkPlan& p, float* s_lo, hipStream_t st) {
+                     const TopkPlan& p, float* s_lo, uint32_t* arrivals, hipStream_t st) {
     const size_t lds = (((size_t)T * p.rows + 3) & ~(size_t)3) * 4 + (size_t)NQ * D * 4;
     const unsigned grid = (unsigned)((int64_t)B * Hkv * p.splits);
     hipLaunchKernelGGL((k_score_lo<D, NQ, T, MAXRED>), dim3(grid), dim3(kThreads), lds, st, q, Hq, lm16,
-                       Hkv, C, scale, p.rows, p.splits, s_lo);
+                       Hkv, C, scale, p.rows, p.splits, s_lo, arrivals);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t dispatch_lo(int nq, int T, bool maxred, const float* q, int B, int Hq, const uint16_t* lm16,
-                       int Hkv, int C, float scale, const TopkPlan& p, float* s_lo, hipStream_t st) {
+                       int Hkv, int C, float scale, const TopkPlan& p, float* s_lo, uint32_t* arrivals,
+                       hipStream_t st) {
 #define DK_LO(NQ_, T_, MX_) \
-    if (nq == NQ_ && T == T_ && maxred == MX_) return launch_lo<D, NQ_, T_, MX_>(q, B, Hq, lm16, Hkv, C, scale, p, s_lo, st);
+    if (nq == NQ_ && T == T_ && maxred == MX_) \
+        return launch_lo<D, NQ_, T_, MX_>(q, B, Hq, lm16, Hkv, C, scale, p, s_lo, arrivals, st);
     DK_LO(1, 1, false)
     DK_LO(2, 2, false)
     DK_LO(1, 1, true)
@@ -869,7 +917,8 @@ TopkPlan plan_topk(int B, int Hkv, int T, int C, int k, bool shadow) {
             p.splits -= 1;
             p.rows = (C + p.splits - 1) / p.splits;
         }
-        p.ws_bytes = (size_t)bg * T * C * 4;
+        // fp16-pass scores, then one arrival counter per (b, g) for the fused union
+        p.ws_bytes = (((size_t)bg * T * C * 4 + 15) & ~(size_t)15) + (size_t)bg * 4;
         return p;
     }
     int64_t want = (2048 + bg - 1) / bg;
@@ -914,27 +963,39 @@ hipError_t launch_build_shadow(const float* lm, dk_strides ls, int B, int Hkv, i
 hipError_t launch_score_topk(const float* q, int B, int T, int Hq, const float* lm, dk_strides ls,
                              int Hkv, int C, int d, int k, float scale, dk_group_reduce reduce,
                              const dk_landmark_shadow* shadow, int32_t* topk_idx, float* topk_score,
-                             void* ws, const TopkPlan& p, hipStream_t st) {
+                             void* ws, const TopkPlan& p, const UnionOut* un, hipStream_t st) {
     const bool maxred = reduce == DK_REDUCE_MAX;
     const int G = Hq / Hkv;
     const int nq = maxred ? G * T : T;
+    const int64_t bg = (int64_t)B * Hkv;
     if (shadow) {
         float* s_lo = (float*)ws;
+        // the selection kernel merges the union itself when s0, s1 and the scan
+        // prefix (3k + 1 ints) fit where its keys and candidates were
+        const int Cp = (C + 3) & ~3;
+        const bool fuse = un && 3 * (int64_t)k + 1 <= (int64_t)Cp + (Cp > kThreads ? Cp : kThreads);
+        uint32_t* arrivals =
+            fuse ? (uint32_t*)((char*)ws + (((size_t)bg * T * C * 4 + 15) & ~(size_t)15)) : nullptr;
         hipError_t e = d == 128
-            ? dispatch_lo<128>(nq, T, maxred, q, B, Hq, shadow->lm16, Hkv, C, scale, p, s_lo, st)
-            : dispatch_lo<64>(nq, T, maxred, q, B, Hq, shadow->lm16, Hkv, C, scale, p, s_lo, st);
+            ? dispatch_lo<128>(nq, T, maxred, q, B, Hq, shadow->lm16, Hkv, C, scale, p, s_lo, arrivals, st)
+            : dispatch_lo<64>(nq, T, maxred, q, B, Hq, shadow->lm16, Hkv, C, scale, p, s_lo, arrivals, st);
         if (e != hipSuccess) return e;
-        const unsigned grid = (unsigned)((int64_t)B * Hkv * T);
+        const unsigned grid = (unsigned)(bg * T);
         const size_t lds = select_lds_bytes(C, d, maxred ? G : 1);
+        const UnionOut none{nullptr, nullptr, nullptr, nullptr};
+        const UnionOut uo = fuse ? *un : none;
 #define DK_SEL(D_, MX_)                                                                            \
     hipLaunchKernelGGL((k_select_exact<D_, MX_>), dim3(grid), dim3(kThreads), lds, st, q, T, Hq, lm, ls, \
-                       shadow->norm_max, s_lo, Hkv, C, k, scale, topk_idx, topk_score)
+                       shadow->norm_max, s_lo, Hkv, C, k, scale, topk_idx, topk_score, uo, arrivals)
         if (d == 128) { if (maxred) DK_SEL(128, true); else DK_SEL(128, false); }
         else { if (maxred) DK_SEL(64, true); else DK_SEL(64, false); }
 #undef DK_SEL
-        return hipGetLastError();
+        e = hipGetLastError();
+        if (e != hipSuccess || !un || fuse) return e;
+        return launch_union(topk_idx, B, Hkv, T, k, C, un->ids, un->member, un->count, un->overlap,
+                            nullptr, st);
     }
-    const int64_t ncand = (int64_t)B * Hkv * T * p.splits * k;
+    const int64_t ncand = bg * T * p.splits * k;
     uint32_t* ck = p.splits > 1 ? (uint32_t*)ws : nullptr;
     int32_t* ci = p.splits > 1 ? (int32_t*)((char*)ws + ncand * 4) : nullptr;
     hipError_t e = d == 128
@@ -942,11 +1003,17 @@ hipError_t launch_score_topk(const float* q, int B, int T, int Hq, const float* 
                               topk_score, st)
         : dispatch_split<64>(nq, T, maxred, q, B, Hq, lm, ls, Hkv, C, k, scale, p, ck, ci, topk_idx,
                              topk_score, st);
-    if (e != hipSuccess || p.splits == 1) return e;
-    const size_t lds = (size_t)(p.splits * k + 256 + 10) * 4;
-    hipLaunchKernelGGL(k_topk_merge, dim3((unsigned)((int64_t)B * Hkv)), dim3(kThreads), lds, st,
-                       ck, ci, T, k, p.splits, topk_idx, topk_score);
-    return hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (p.splits > 1) {
+        const size_t lds = (size_t)(p.splits * k + 256 + 10) * 4;
+        hipLaunchKernelGGL(k_topk_merge, dim3((unsigned)bg), dim3(kThreads), lds, st, ck, ci, T, k,
+                           p.splits, topk_idx, topk_score);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (!un) return hipSuccess;
+    return launch_union(topk_idx, B, Hkv, T, k, C, un->ids, un->member, un->count, un->overlap, nullptr,
+                        st);
 }
 
 }  // namespace dk

@@ -8,25 +8,14 @@
 // the OasisKV summary's "KV selection" stage: compare the new set with the
 // resident set and plan the copies of the missing chunks.
 //
-// One block per (b, g).  Both inputs are strictly ascending, so the union is a
-// merge: S0[i] lands at i + |{S1 < S0[i]}| - |{S0 & S1 below it}| and a chunk
-// of S1 that S0 lacks lands at |{S0 < y}| + j - |{S0 & S1 below it}|.  The
-// shared-chunk counts come from one block scan over S0's "also in S1" flags.
+// One block per (b, g); the merge itself is block_union_two (dk_union_core.h).
 #include "dk_common.h"
+#include "dk_union_core.h"
 
 namespace dk {
 namespace {
 
 constexpr int kThreads = 256;
-
-__device__ __forceinline__ int lower_bound(const int32_t* a, int n, int32_t x) {
-    int lo = 0, hi = n;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (a[mid] < x) lo = mid + 1; else hi = mid;
-    }
-    return lo;
-}
 
 __global__ __launch_bounds__(kThreads) void k_union(
     const int32_t* __restrict__ topk_idx, int T, int k, int32_t* __restrict__ union_ids,
@@ -53,60 +42,8 @@ __global__ __launch_bounds__(kThreads) void k_union(
     }
     __syncthreads();
 
-    int count, nshared;
-    if (T == 1) {
-        for (int i = tid; i < k; i += kThreads) {
-            uo[i] = s0[i];
-            mo[i] = 1;
-            u_ids[i] = s0[i];
-        }
-        count = k;
-        nshared = k;
-    } else {
-        // flags of S0 entries that S1 also holds, scanned in S0 order
-        const int per = (k + kThreads - 1) / kThreads;
-        const int lo = min(k, tid * per), hi = min(k, lo + per);
-        int mine = 0;
-        for (int i = lo; i < hi; ++i) {
-            const int j = lower_bound(s1, k, s0[i]);
-            mine += (j < k && s1[j] == s0[i]);
-        }
-        int total;
-        int run = block_exclusive_scan(mine, scratch, &total);
-        for (int i = lo; i < hi; ++i) {
-            dup_pre[i] = run;
-            const int j = lower_bound(s1, k, s0[i]);
-            run += (j < k && s1[j] == s0[i]);
-        }
-        if (tid == 0) dup_pre[k] = total;
-        __syncthreads();
-        nshared = total;
-        count = 2 * k - total;
-        for (int i = tid; i < k; i += kThreads) {
-            const int32_t x = s0[i];
-            const int j = lower_bound(s1, k, x);
-            const bool both = j < k && s1[j] == x;
-            const int pos = i + j - dup_pre[i];
-            if (pos < 0 || pos >= N) continue;   // only for rows that are not ascending
-            uo[pos] = x;
-            mo[pos] = both ? 3 : 1;
-            u_ids[pos] = x;
-        }
-        for (int j = tid; j < k; j += kThreads) {
-            const int32_t y = s1[j];
-            const int i = lower_bound(s0, k, y);
-            if (i < k && s0[i] == y) continue;
-            const int pos = i + j - dup_pre[i];
-            if (pos < 0 || pos >= N) continue;
-            uo[pos] = y;
-            mo[pos] = 2;
-            u_ids[pos] = y;
-        }
-    }
-    for (int i = count + tid; i < N; i += kThreads) {
-        uo[i] = -1;
-        mo[i] = 0;
-    }
+    int nshared;
+    const int count = block_union_two(s0, s1, T, k, uo, mo, dup_pre, scratch, u_ids, &nshared);
     if (tid == 0) {
         union_count[bg] = count;
         if (overlap) overlap[bg] = nshared;
@@ -132,7 +69,7 @@ __global__ __launch_bounds__(kThreads) void k_union(
         int mine = 0;
         for (int s = lo; s < hi; ++s) {
             const int32_t c = res[s];
-            const int p = c >= 0 ? lower_bound(u_ids, count, c) : count;
+            const int p = c >= 0 ? lower_bound_i32(u_ids, count, c) : count;
             mine += !(p < count && u_ids[p] == c);
         }
         int total;
@@ -140,7 +77,7 @@ __global__ __launch_bounds__(kThreads) void k_union(
         nfree = total;
         for (int s = lo; s < hi; ++s) {
             const int32_t c = res[s];
-            const int p = c >= 0 ? lower_bound(u_ids, count, c) : count;
+            const int p = c >= 0 ? lower_bound_i32(u_ids, count, c) : count;
             if (!(p < count && u_ids[p] == c)) free_list[r++] = s;
         }
     }
@@ -150,7 +87,7 @@ __global__ __launch_bounds__(kThreads) void k_union(
     for (int s = tid; s < slots; s += kThreads) {
         const int32_t c = res[s];
         if (c < 0) continue;
-        const int p = lower_bound(u_ids, count, c);
+        const int p = lower_bound_i32(u_ids, count, c);
         if (p < count && u_ids[p] == c) u_slot[p] = s;
     }
     __syncthreads();

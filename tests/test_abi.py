@@ -27,14 +27,14 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(lib, n), n
     assert {n for n, _, _ in b.EXPORTS} == set(names)
 
 
 def test_abi_version():
-    assert lib.dk_abi_version() == 3
+    assert lib.dk_abi_version() == 4
 
 
 def err():
@@ -81,11 +81,34 @@ def test_score_topk_rejects(kw, status):
     assert err().startswith("dk_score_topk")
 
 
+def score_union(uid=FAKE, mem=FAKE, cnt=FAKE, ov=NULL, **kw):
+    a = dict(q=FAKE, B=2, T=2, Hq=32, lm=FAKE, lmdt=0, ls=b.dk_strides(1 << 22, 1 << 19, 128), Hkv=8,
+             C=1024, d=128, k=64, scale=0.088, reduce=0, shadow=None, idx=FAKE, sc=FAKE, ws=FAKE,
+             wsb=1 << 30)
+    a.update(kw)
+    return lib.dk_score_topk_union(a["q"], a["B"], a["T"], a["Hq"], a["lm"], a["lmdt"], a["ls"], a["Hkv"],
+                                   a["C"], a["d"], a["k"], a["scale"], a["reduce"], a["shadow"], a["idx"],
+                                   a["sc"], uid, mem, cnt, ov, a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(uid=NULL), 1), (dict(mem=NULL), 1), (dict(cnt=NULL), 1), (dict(q=NULL), 1), (dict(T=3), 1),
+    (dict(k=0), 1), (dict(wsb=16), 1), (dict(d=96), 2), (dict(lm=MIS), 2),
+    (dict(shadow=ctypes.byref(SH_NULL)), 1), (dict(shadow=ctypes.byref(SH_OK), C=8192), 2),
+    (dict(C=65536, k=4097), 2),
+])
+def test_score_topk_union_rejects(kw, status):
+    # every case fails its checks, so nothing is launched
+    assert score_union(**kw) == status, err()
+    assert err().startswith("dk_score_topk_union")
+
+
 def test_score_topk_workspace_sizes():
     # 64 x 8 (b, g) rows over 4096 chunks: 4 ranges of 1024, 64 candidates each
     assert lib.dk_score_topk_workspace_size(64, 8, 2, 4096, 64, 0) == 64 * 8 * 2 * 4 * 64 * 8
-    # with a shadow: every fp16 score of every (b, g, t)
-    assert lib.dk_score_topk_workspace_size(64, 8, 2, 4096, 64, 1) == 64 * 8 * 2 * 4096 * 4
+    # with a shadow: every fp16 score of every (b, g, t), then one arrival
+    # counter per (b, g) for the fused union
+    assert lib.dk_score_topk_workspace_size(64, 8, 2, 4096, 64, 1) == 64 * 8 * 2 * 4096 * 4 + 64 * 8 * 4
     assert lib.dk_score_topk_workspace_size(1, 1, 2, 128, 8, 0) > 0
     assert lib.dk_score_topk_workspace_size(1, 1, 2, 128, 0, 0) == 0
 

@@ -242,6 +242,45 @@ def test_union(dkb, T, k, C, mode):
     np.testing.assert_array_equal(o.cpu().numpy(), ro)
 
 
+@pytest.mark.parametrize("name,B,L,kw,shadow", [
+    ("llama8b_l32k", 4, 8192, {}, True),            # fused into the selection kernel
+    ("llama8b_l32k", 4, 8192, {}, False),           # fp32 path: separate union kernel
+    ("llama8b_l32k", 2, 16384, dict(k=400), True),  # 3k + 1 beyond the selection LDS: separate kernel
+    ("tiny", None, None, dict(T=1), True),          # one query: the union is S_0
+    ("tiny", None, None, {}, True),
+])
+def test_score_topk_union(dkb, name, B, L, kw, shadow):
+    w = workload(name, B, L, **kw)
+    q, K, V = make(w, 4)
+    lm = dkb.build_landmarks(K, w.chunk)
+    sh = dkb.build_landmark_shadow(lm) if shadow else None
+    ws = torch.empty(dkb.score_topk_workspace_size(w.B, w.Hkv, w.T, w.C, w.k, shadow), dtype=torch.uint8,
+                     device="cuda")
+    # Two different query sets through the same workspace and output buffers:
+    # the arrival counters restart from zero, and the union of the second call
+    # must come from its own sets, not from what the first call left behind.
+    q2 = synth.make_queries(w, 5, device="cuda")
+    outs = dkb.score_topk_union(q2, lm, w.k, w.scale, ws=ws, want_scores=True, shadow=sh)
+    for qq in (q2, q):
+        if qq is q:
+            outs = dkb.score_topk_union(qq, lm, w.k, w.scale, dkb.DK_REDUCE_MEAN, *outs, ws=ws, shadow=sh)
+        idx_f, sc_f, uid, mem, cnt, ov = outs
+        idx_s, sc_s = dkb.score_topk(qq, lm, w.k, w.scale, shadow=sh)
+        torch.cuda.synchronize()
+        assert torch.equal(idx_f, idx_s) and torch.equal(sc_f, sc_s)
+        ru, rm, rc, ro = O.union_select(idx_f.cpu().numpy())
+        np.testing.assert_array_equal(uid.cpu().numpy(), ru)
+        np.testing.assert_array_equal(mem.cpu().numpy(), rm)
+        np.testing.assert_array_equal(cnt.cpu().numpy(), rc)
+        np.testing.assert_array_equal(ov.cpu().numpy(), ro)
+    # and the sets themselves against the oracle (near-ties counted)
+    qh = q.cpu().numpy().astype(np.float64)
+    Kh = synth.to_numpy_f64(K)
+    _, sref, selref = oracle_selection(w, qh, Kh)
+    _, _, hard = compare_topk(idx_f.cpu().numpy(), selref, sref)
+    assert not hard, hard[:5]
+
+
 def test_cache_plan_sequence(dkb):
     rng = np.random.default_rng(8)
     B, H, T, k, C = 2, 3, 2, 16, 200
@@ -477,10 +516,15 @@ def test_step_full_size_sampled(dkb, name, samples):
     near = check_step_sampled(dkb, w, q, K, V, st, samples)
     acc = st.overlap.float().mean().item() / w.k
     print(f"{name}: near-tie chunks {near}, prediction accuracy {acc:.4f}")
-    # union invariants over every (b, g)
+    # union invariants over every (b, g), and the union itself from the GPU's sets
     c = st.count.cpu().numpy()
     ov = st.overlap.cpu().numpy()
     assert np.all(c == 2 * w.k - ov) and np.all((c >= w.k) & (c <= 2 * w.k))
+    ru, rm, rc, ro = O.union_select(st.topk_idx.cpu().numpy())
+    np.testing.assert_array_equal(st.union_ids.cpu().numpy(), ru)
+    np.testing.assert_array_equal(st.member.cpu().numpy(), rm)
+    np.testing.assert_array_equal(c, rc)
+    np.testing.assert_array_equal(ov, ro)
     del K, V, lm
     torch.cuda.empty_cache()
 
