@@ -497,20 +497,34 @@ __global__ __launch_bounds__(kThreads) void k_score_lo(const float* __restrict__
     // the selection kernel that follows counts its (b, g, t) blocks from zero
     if (arrivals && blk == 0 && threadIdx.x == 0) arrivals[bg] = 0u;
 
+    // The first rows are requested before anything else: their loads overlap
+    // the query staging below.
+    const uint16_t* base = lm16 + ((int64_t)bg * C + row0) * D + part * 8;
+    constexpr int ROWS_PER_ITER = 4 * RPW * U;
+    u32x4_t x[U];
+    auto load_rows = [&](int it) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int r = it + (u * 4 + wave) * RPW + rp;
+            x[u] = r < nrows ? nt_load_u4(base + (int64_t)r * D) : u32x4_t{0u, 0u, 0u, 0u};
+        }
+    };
+    load_rows(0);
+
     // The query vectors of this (b, g) go through LDS once per block (one 16-byte
     // global load per lane would otherwise be repeated by every row-lane group).
     float* qs = sres + ((T * rows_per_block + 3) & ~3);   // [NQ][D], 16-byte aligned
     for (int i = threadIdx.x; i < NQ * D; i += kThreads) {
         const int v = i / D, e = i - v * D;
-        float x;
+        float xq;
         if constexpr (MAXRED) {
-            x = q[(((int64_t)b * T + v / G) * Hq + g * Gq + v % G) * D + e];
+            xq = q[(((int64_t)b * T + v / G) * Hq + g * Gq + v % G) * D + e];
         } else {
-            x = 0.f;
-            for (int h = 0; h < Gq; ++h) x += q[(((int64_t)b * T + v) * Hq + g * Gq + h) * D + e];
-            x = x / (float)Gq;
+            xq = 0.f;
+            for (int h = 0; h < Gq; ++h) xq += q[(((int64_t)b * T + v) * Hq + g * Gq + h) * D + e];
+            xq = xq / (float)Gq;
         }
-        qs[i] = x;
+        qs[i] = xq;
     }
     __syncthreads();
     uint32_t qh[NQ][4];
@@ -524,16 +538,11 @@ __global__ __launch_bounds__(kThreads) void k_score_lo(const float* __restrict__
         qh[v][3] = f16_bits(x1.z) | (f16_bits(x1.w) << 16);
     }
 
-    const uint16_t* base = lm16 + ((int64_t)bg * C + row0) * D + part * 8;
-    constexpr int ROWS_PER_ITER = 4 * RPW * U;
     for (int it = 0; it < nrows; it += ROWS_PER_ITER) {
-        u32x4_t x[U];
+        if (it) load_rows(it);
         int rr[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            rr[u] = it + (u * 4 + wave) * RPW + rp;
-            x[u] = rr[u] < nrows ? nt_load_u4(base + (int64_t)rr[u] * D) : u32x4_t{0u, 0u, 0u, 0u};
-        }
+        for (int u = 0; u < U; ++u) rr[u] = it + (u * 4 + wave) * RPW + rp;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             float dot[NQ];

@@ -372,6 +372,26 @@ def test_attention(dkb, name, B, L, kw):
     run_attention(dkb, workload(name, B, L, **kw), 31)
 
 
+def test_attention_workspace_reuse(dkb):
+    """One workspace serves calls of different shapes (and range splits) in turn."""
+    cases = [workload("llama8b_l32k", 4, 8192), workload("tiny", 3, None, Hq=8, Hkv=2),
+             workload("llama8b_l32k", 2, 8192), workload("llama8b_l32k", 4, 8192)]
+    need = max(dkb.attn_workspace_size(w.B, w.Hkv, w.T, w.Hq, w.d, w.T * w.k, w.chunk) for w in cases)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for i, w in enumerate(cases):
+        q, K, V = make(w, 20 + i)
+        qh = q.cpu().numpy().astype(np.float64)
+        Kh, Vh = synth.to_numpy_f64(K), synth.to_numpy_f64(V)
+        _, _, sel = oracle_selection(w, qh, Kh)
+        ru, rm, rc, _ = O.union_select(sel)
+        out, lse = dkb.sparse_decode_attn(q, K, V, to_dev(ru), to_dev(rm, torch.uint8), to_dev(rc), w.chunk,
+                                          w.scale, ws=ws)
+        torch.cuda.synchronize()
+        ro_, rl_ = O.sparse_attention(qh, Kh, Vh, sel, w.chunk, w.scale)
+        tol = ATOL[w.kv_dtype]
+        assert max_abs(out.cpu().numpy(), ro_) <= tol and max_abs(lse.cpu().numpy(), rl_) <= tol, (i, w.name)
+
+
 def test_attention_ragged_and_empty(dkb):
     def mutate(ru, rm, rc, lists, w):
         # (0, 0): empty; (0, 1): one chunk, real query only; (1, 2): out-of-range id skipped
