@@ -83,8 +83,32 @@ def measured_traffic(workload, call):
     return c["bytes_per_launch"]
 
 
-def cpu_baseline(w, qs_host, K, V, budget_s, seed):
-    """Time the fp64 CPU oracle on sampled (request, KV head, layer) units."""
+def near_tie_report(gpu_sel, ref_sel, scores):
+    """Compare GPU and oracle top-k rows: a chunk in one set but not the other is
+    a near-tie when its oracle score is within 1e-5 * max(|s_(k)|, rms(row)) of
+    the k-th largest oracle score s_(k); any other difference is a mismatch."""
+    import numpy as np
+    rows = diff_rows = near = hard = 0
+    for gi, oi, sc in zip(gpu_sel.reshape(-1, gpu_sel.shape[-1]), ref_sel.reshape(-1, ref_sel.shape[-1]),
+                          scores.reshape(-1, scores.shape[-1])):
+        rows += 1
+        sym = set(gi.tolist()) ^ set(oi.tolist())
+        if not sym:
+            continue
+        diff_rows += 1
+        sk = sc[oi].min()
+        tol = 1e-5 * max(abs(sk), float(np.sqrt(np.mean(sc ** 2))))
+        for c in sym:
+            if abs(sc[c] - sk) <= tol:
+                near += 1
+            else:
+                hard += 1
+    return rows, diff_rows, near, hard
+
+
+def cpu_baseline(w, qs_host, K, V, budget_s, seed, gpu_topk=None):
+    """Time the fp64 CPU oracle on sampled (request, KV head, layer) units; with the
+    GPU's top-k of every layer, also compare the sampled selections."""
     import numpy as np
     from threadpoolctl import threadpool_limits
     from oracle import dualkv_oracle as O
@@ -94,6 +118,8 @@ def cpu_baseline(w, qs_host, K, V, budget_s, seed):
     pairs = [(int(rng.integers(w.B)), int(rng.integers(w.Hkv))) for _ in range(4)]
     per_pair = budget_s / len(pairs)
     units, spent = 0, 0.0
+    cmp = [0, 0, 0, 0]
+    overlap_gpu = overlap_ref = 0
     with threadpool_limits(1):
         for b, g in pairs:
             Kh = synth.to_numpy_f64(K[b:b + 1, g:g + 1])
@@ -101,7 +127,8 @@ def cpu_baseline(w, qs_host, K, V, budget_s, seed):
             lm = O.chunk_landmarks(Kh, w.chunk)            # built once per prefill: not timed
             pair_spent, layer = 0.0, 0
             while pair_spent < per_pair:
-                qh = qs_host[layer % len(qs_host)][b:b + 1, :, g * w.G:(g + 1) * w.G]
+                li = layer % len(qs_host)
+                qh = qs_host[li][b:b + 1, :, g * w.G:(g + 1) * w.G]
                 t0 = time.perf_counter()
                 s = O.chunk_scores(qh, lm, w.scale, "mean")
                 sel = O.topk_chunks(s, w.k)
@@ -109,14 +136,48 @@ def cpu_baseline(w, qs_host, K, V, budget_s, seed):
                 O.sparse_attention(qh, Kh, Vh, sel, w.chunk, w.scale)
                 pair_spent += time.perf_counter() - t0
                 units += 1
+                if gpu_topk is not None and layer < len(qs_host):
+                    gsel = gpu_topk[li][b:b + 1, g:g + 1]
+                    for i, x in enumerate(near_tie_report(gsel, sel, s)):
+                        cmp[i] += x
+                    if w.T == 2:
+                        overlap_gpu += len(set(gsel[0, 0, 0].tolist()) & set(gsel[0, 0, 1].tolist()))
+                        overlap_ref += len(set(sel[0, 0, 0].tolist()) & set(sel[0, 0, 1].tolist()))
                 layer += 1
             spent += pair_spent
     per_unit = spent / units
     per_step = per_unit * w.B * w.Hkv * len(qs_host)
-    return {"value": 1.0 / per_step, "unit": "steps/s", "cores": 1, "kind": "oracle",
-            "sample": f"{units} (request, KV head, layer) units of the {w.name} step "
-                      f"({spent:.1f} s, {per_unit * 1e3:.1f} ms each), scaled to "
-                      f"{w.B * w.Hkv * len(qs_host)} units per step; landmarks precomputed"}
+    out = {"value": 1.0 / per_step, "unit": "steps/s", "cores": 1, "kind": "oracle",
+           "sample": f"{units} (request, KV head, layer) units of the {w.name} step "
+                     f"({spent:.1f} s, {per_unit * 1e3:.1f} ms each), scaled to "
+                     f"{w.B * w.Hkv * len(qs_host)} units per step; landmarks precomputed"}
+    if gpu_topk is not None:
+        out["selection_check"] = {"rows": cmp[0], "rows_differing": cmp[1], "near_tie_chunks": cmp[2],
+                                  "mismatched_chunks": cmp[3], "overlap_gpu": overlap_gpu,
+                                  "overlap_oracle": overlap_ref}
+    return out
+
+
+def hbm_copy_gbps(torch, dkb, reps=5):
+    """Plain device copy rate (1 GiB read + 1 GiB written per launch) through
+    dk_gather_kv over consecutive chunks; bytes moved (read + written) per second."""
+    rows, d, chunk = 1 << 21, 128, 32
+    C = rows // chunk
+    src = [torch.ones(1, 1, rows, d, dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    dst = [torch.empty_like(src[0]) for _ in range(2)]
+    ids = torch.arange(C, dtype=torch.int32, device="cuda").reshape(1, 1, C)
+    dkb.gather_kv(src[0], src[1], ids, None, chunk, dst[0], dst[1])
+    best = 0.0
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dkb.gather_kv(src[0], src[1], ids, None, chunk, dst[0], dst[1])
+        b.record()
+        b.synchronize()
+        best = max(best, 4 * src[0].nbytes / (a.elapsed_time(b) * 1e-3) / 1e9)
+    del src, dst
+    torch.cuda.empty_cache()
+    return best
 
 
 def h2d_peak_gbps(torch, nbytes=1 << 28, reps=5):
@@ -310,11 +371,12 @@ def main():
           f"landmarks {lm.nbytes / 1e9:.3f} GB", file=sys.stderr, flush=True)
 
     # Per-layer union sizes (deterministic): the selected-KV bytes of each layer.
-    sel_chunks, overlap = [], []
+    sel_chunks, overlap, gpu_topk = [], [], []
     for l in range(w.layers):
         st.run(qs[l], lm, K, V)
         sel_chunks.append(int(st.count.sum().item()))
         overlap.append(st.overlap.double().mean().item())
+        gpu_topk.append(st.topk_idx.cpu().numpy())
     torch.cuda.synchronize()
     chunk_bytes = w.chunk_kv_bytes()
     sel_bytes_step = sum(sel_chunks) * chunk_bytes
@@ -352,11 +414,13 @@ def main():
         step(s + 1 if use_events else 0)
     end.record()
     torch.cuda.synchronize()
+    step_ms = []
     if use_events:
         for s in range(args.steps):
             for l in range(w.layers):
                 for i, c in enumerate(calls):
                     call_ms[c] += ev[s][l][i].elapsed_time(ev[s][l][i + 1])
+            step_ms.append(ev[s][0][0].elapsed_time(ev[s][w.layers - 1][len(calls)]))
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
     steps_per_s = 1000.0 / ms_per_step
@@ -386,6 +450,11 @@ def main():
     attn_ms_step = call_ms["sparse_decode_attn"] / args.steps if use_events else float("nan")
     sel_gbps = sel_bytes_step / (attn_ms_step * 1e-3) / 1e9 if use_events else float("nan")
 
+    # every byte the step moves: landmark scoring, union chunks, queries, outputs, indices
+    out_bytes = w.B * w.T * w.Hq * (w.d + 1) * 4          # out and lse
+    full_bytes_step = w.layers * (per_call_bytes["score_topk_union"] + q_bytes + out_bytes) + sel_bytes_step
+    copy_gbps = hbm_copy_gbps(torch, dkb)
+
     dominant = max(kernels, key=lambda c: kernels[c]["avg_us"]) if kernels else None
     roofline = None
     if dominant:
@@ -411,8 +480,14 @@ def main():
         "config": {"workload": w.name, "B": w.B, "L": w.L, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d,
                    "chunk": w.chunk, "k": w.k, "T": w.T, "layers": w.layers, "seed": args.seed,
                    "landmark_shadow": shadow is not None},
+        "ms_per_step_median": round(float(np.median(step_ms)), 4) if step_ms else None,
+        "ms_per_step_min": round(float(np.min(step_ms)), 4) if step_ms else None,
         "selected_kv_GBps": round(sel_gbps, 1),
         "selected_kv_frac_hbm_peak": round(sel_gbps / HBM_PEAK_GBPS, 4),
+        "hbm_copy_GBps": round(copy_gbps, 1),
+        "selected_kv_frac_of_copy": round(sel_gbps / copy_gbps, 4),
+        "full_step_GBps": round(full_bytes_step / (ms_per_step * 1e-3) / 1e9, 1),
+        "full_step_frac_hbm_peak": round(full_bytes_step / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "selected_kv_bytes_per_step": int(sel_bytes_step),
         "mean_union_chunks": round(sum(sel_chunks) / (w.layers * w.B * w.Hkv), 2),
         "prediction_accuracy": round(accuracy, 5),
@@ -421,7 +496,7 @@ def main():
     }
     if args.cpu_seconds > 0:
         qs_host = [q.cpu().numpy().astype(np.float64) for q in qs]
-        out["cpu_baseline"] = cpu_baseline(w, qs_host, K, V, args.cpu_seconds, args.seed)
+        out["cpu_baseline"] = cpu_baseline(w, qs_host, K, V, args.cpu_seconds, args.seed, gpu_topk)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
