@@ -35,6 +35,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNoLogit = -1e30f;   // running-max floor of the fast path (log2 units)
 
 struct AttnArgs {
     const float* q;
@@ -171,21 +172,26 @@ __global__ __launch_bounds__(kThreads) void k_attn_bf16_d128_g4t2(AttnArgs a) {
         koff[jj] = row * (int)a.ks.t + (phys ^ (row & 7)) * 8;
         voff[jj] = row * (int)a.vs.t + phys * 8;
     }
-    auto issue = [&](int it) {
+    // the wave index as a scalar: the DMA's LDS bases (M0) are then plain SALU math
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    auto tile_row = [&](int it) {
         const int e = it / tpc;
-        const int row0 = sm.erow[e] + (it - e * tpc) * KT;
+        return sm.erow[e] + (it - e * tpc) * KT;
+    };
+    auto issue = [&](int it, int row0) {
         const int s = it % NS;
         const uint16_t* kp = Kb + (int64_t)row0 * a.ks.t;
         const uint16_t* vp = Vb + (int64_t)row0 * a.vs.t;
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-            lds_dma16(kp + koff[jj], __builtin_amdgcn_readfirstlane(lds_addr(&sm.kv[s][0][(2 * w + jj) * 64])));
+        for (int jj = 0; jj < 2; ++jj) lds_dma16(kp + koff[jj], lds_addr(&sm.kv[s][0][(2 * wu + jj) * 64]));
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-            lds_dma16(vp + voff[jj], __builtin_amdgcn_readfirstlane(lds_addr(&sm.kv[s][1][(2 * w + jj) * 64])));
+        for (int jj = 0; jj < 2; ++jj) lds_dma16(vp + voff[jj], lds_addr(&sm.kv[s][1][(2 * wu + jj) * 64]));
     };
 
-    float m_run = -INFINITY, l_run = 0.f;     // this lane's query t = hd
+    // Running max in log2 units.  It starts at a finite floor far below every
+    // logit, so exp2 of (masked logit = -inf) - max is 0 without a guard, and a
+    // range with no valid key ends with l = 0 (reported as out 0, lse -inf).
+    float m_run = kNoLogit, l_run = 0.f;     // this lane's query t = hd
     float acc[T][8];
 #pragma unroll
     for (int t = 0; t < T; ++t)
@@ -195,7 +201,10 @@ __global__ __launch_bounds__(kThreads) void k_attn_bf16_d128_g4t2(AttnArgs a) {
 
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s)
-        if (s < ntiles) issue(s);
+        if (s < ntiles) issue(s, tile_row(s));
+    // per-tile metadata is read one iteration ahead, off the critical path
+    int row_next = NS - 1 < ntiles ? tile_row(NS - 1) : 0;
+    uint32_t bits_next = ntiles > 0 ? sm.ebits[0] : 0u;
 
     for (int it = 0; it < ntiles; ++it) {
         // tile `it` has landed when at most the 4 loads of tile it + 1 are pending
@@ -203,9 +212,10 @@ __global__ __launch_bounds__(kThreads) void k_attn_bf16_d128_g4t2(AttnArgs a) {
         else lds_dma_wait<0>();
         raw_barrier();
         // the stage computed in the previous iteration is free for tile it + 2
-        if (it + NS - 1 < ntiles) issue(it + NS - 1);
-
-        const uint32_t m_cur = sm.ebits[it / tpc];
+        if (it + NS - 1 < ntiles) issue(it + NS - 1, row_next);
+        const uint32_t m_cur = bits_next;
+        row_next = it + NS < ntiles ? tile_row(it + NS) : 0;
+        bits_next = it + 1 < ntiles ? sm.ebits[(it + 1) / tpc] : 0u;
         if (m_cur == 0) continue;
         const uint4* kb = sm.kv[it % NS][0];
         const uint4* vb = sm.kv[it % NS][1];
@@ -230,17 +240,14 @@ __global__ __launch_bounds__(kThreads) void k_attn_bf16_d128_g4t2(AttnArgs a) {
         float z = (keep + dpp_xor1(send)) * a.scale_log2;
         if (!((m_cur >> hd) & 1u)) z = -INFINITY;
 
-        // ---- online softmax; the running max moves only when a logit exceeds it ----
-        float p;
-        if (__builtin_amdgcn_ballot_w64(z > m_run) == 0ull) {
-            p = z == -INFINITY ? 0.f : exp2f(z - m_run);
-        } else {
+        // ---- online softmax; the running max moves only when a logit exceeds it,
+        // and then the accumulators are rescaled in place ----
+        if (__builtin_amdgcn_ballot_w64(z > m_run) != 0ull) {
             float cm = z;
 #pragma unroll
             for (int off = 2; off < kWave; off <<= 1) cm = fmaxf(cm, __shfl_xor(cm, off, kWave));
             const float mn = fmaxf(m_run, cm);
-            const float alpha = mn == -INFINITY ? 1.f : exp2f(m_run - mn);
-            p = mn == -INFINITY ? 0.f : exp2f(z - mn);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
             l_run *= alpha;
             m_run = mn;
             const float al0 = __shfl(alpha, 0, kWave);
@@ -251,6 +258,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_bf16_d128_g4t2(AttnArgs a) {
                 acc[1][e] *= al1;
             }
         }
+        const float p = __builtin_amdgcn_exp2f(z - m_run);
         // weights go to P.V as bf16; the row sum uses the same rounded weights
         const uint32_t pb = f32_to_bf16_rne(p);
         l_run += __uint_as_float(pb << 16);
