@@ -627,15 +627,24 @@ __global__ __launch_bounds__(kThreads) void k_select_exact(
     const int per = (C + kThreads - 1) / kThreads;
     const int lo = min(C, tid * per), hi = min(C, lo + per);
     const float* sl = s_lo + ((int64_t)bg * T + t) * C;
-    // coalesced 16-byte loads into LDS (s_lo rows start on 16 bytes when C % 4 == 0)
-    if ((C & 3) == 0) {
-        for (int i = tid; i < (C >> 2); i += kThreads) {
-            const float4 x = *reinterpret_cast<const float4*>(sl + 4 * i);
-            reinterpret_cast<uint4*>(keys)[i] =
-                make_uint4(score_key(x.x), score_key(x.y), score_key(x.z), score_key(x.w));
+    // straight into registers: 16-byte loads when the ranges are 4-aligned
+    uint32_t kr[KPT];
+    if ((per & 3) == 0 && (C & 3) == 0) {
+#pragma unroll
+        for (int i = 0; i < KPT / 4; ++i) {
+            if (lo + 4 * i < hi) {
+                const float4 x = *reinterpret_cast<const float4*>(sl + lo + 4 * i);
+                kr[4 * i] = score_key(x.x);
+                kr[4 * i + 1] = score_key(x.y);
+                kr[4 * i + 2] = score_key(x.z);
+                kr[4 * i + 3] = score_key(x.w);
+            } else {
+                kr[4 * i] = kr[4 * i + 1] = kr[4 * i + 2] = kr[4 * i + 3] = 0u;
+            }
         }
     } else {
-        for (int i = tid; i < C; i += kThreads) keys[i] = score_key(sl[i]);
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) kr[i] = lo + i < hi ? score_key(sl[lo + i]) : 0u;
     }
     const float M = norm_max[bg];
     for (int i = tid; i < nvec * D; i += kThreads) {
@@ -651,9 +660,6 @@ __global__ __launch_bounds__(kThreads) void k_select_exact(
         qv[i] = x;
     }
     __syncthreads();
-    uint32_t kr[KPT];
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) kr[i] = lo + i < hi ? keys[lo + i] : 0u;
     uint32_t tmax = 0u;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) tmax = max(tmax, kr[i]);
