@@ -335,7 +335,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the decode step has no "
-              "cross-GPU exchange and this build measures a single MI355X.", file=sys.stderr)
+              "cross-GPU exchange and this benchmark measures a single MI355X.", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch

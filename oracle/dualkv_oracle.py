@@ -30,7 +30,7 @@ The overlap of the real and speculative chunk sets is the prediction accuracy
 (DualDecoder, "6.3 Accuracy Analysis": overlap ratio of predicted and
 ground-truth sparse indices).
 
-Readings where the pages are silent (each one listed in the design doc):
+Readings where the pages are silent:
 * a landmark is the arithmetic mean of the chunk's keys;
 * the G query heads of one KV head are combined by the mean of their scaled
   dot products ("max" is offered as an alternative);
