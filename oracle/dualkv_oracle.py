@@ -220,6 +220,61 @@ def sparse_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, sel: np.ndarra
     return out, lse
 
 
+def sparse_attention_tail(q: np.ndarray, K: np.ndarray, V: np.ndarray, sel: np.ndarray, chunk: int,
+                          scale: float, K_tail=None, V_tail=None, tail_len=None, K_new=None, V_new=None):
+    """sparse_attention plus the rows every query attends besides its chunks.
+
+    DualDecoder "5.2 Dual-Token Decoding Pipeline": the step's real token T_i and
+    speculative token T'_{i+1} are placed one after the other along the sequence,
+    and a mask keeps the real token from using the speculative token's data,
+    while the speculative token sees every earlier token, the real one included.
+    Adaptive DHiSparse, Figure 2: a per-request tail of recent rows is resolved
+    for every lookup, besides the selected rows.
+
+    K_tail, V_tail: [B, Hkv, Lt, d] and tail_len [B]: the first tail_len[b] rows
+    are attended by every query of request b (None: no tail).
+    K_new, V_new: [B, T, Hkv, d]: the step's own tokens; query t attends the rows
+    of tokens t' <= t (None: no fresh rows).
+    For query head h (KV head g = h // G) and query t the key rows are the rows of
+    its chunks, then the tail rows, then the allowed fresh rows; the softmax is
+    the same dense one as in sparse_attention over all of them.
+    Returns out [B, T, Hq, dv] and lse [B, T, Hq].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    B, T, Hq, dk = q.shape
+    Hkv = K.shape[1]
+    dv = V.shape[3]
+    G = Hq // Hkv
+    out = np.zeros((B, T, Hq, dv), dtype=np.float64)
+    lse = np.zeros((B, T, Hq), dtype=np.float64)
+    for b in range(B):
+        for t in range(T):
+            for h in range(Hq):
+                g = h // G
+                keys, vals = [], []
+                for c in sel[b, g, t]:
+                    keys.append(K[b, g, int(c) * chunk:(int(c) + 1) * chunk])
+                    vals.append(V[b, g, int(c) * chunk:(int(c) + 1) * chunk])
+                if K_tail is not None:
+                    n = int(tail_len[b])
+                    keys.append(np.asarray(K_tail[b, g, :n], dtype=np.float64))
+                    vals.append(np.asarray(V_tail[b, g, :n], dtype=np.float64))
+                if K_new is not None:
+                    for tp in range(t + 1):           # tokens up to and including t
+                        keys.append(np.asarray(K_new[b, tp, g], dtype=np.float64)[None, :])
+                        vals.append(np.asarray(V_new[b, tp, g], dtype=np.float64)[None, :])
+                Kr = np.concatenate(keys, axis=0)
+                Vr = np.concatenate(vals, axis=0)
+                z = scale * (Kr @ q[b, t, h])
+                m = z.max()
+                p = np.exp(z - m)
+                out[b, t, h] = (p @ Vr) / p.sum()
+                lse[b, t, h] = m + math.log(p.sum())
+    return out, lse
+
+
 # ----------------------------------------------------------------------------
 # host-pool hot cache: which union chunks are already resident
 # ----------------------------------------------------------------------------

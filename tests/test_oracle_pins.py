@@ -233,6 +233,80 @@ def test_attention_pins():
 
 
 # ----------------------------------------------------------------------------
+# attention with the tail and the step's own (fresh) rows
+# ----------------------------------------------------------------------------
+
+def tail_inputs(rng, B=2, T=2, Hq=4, Hkv=2, dk=6, dv=5, chunk=3, C=7, Lt=5):
+    q = rng.standard_normal((B, T, Hq, dk))
+    K = rng.standard_normal((B, Hkv, C * chunk, dk))
+    V = rng.standard_normal((B, Hkv, C * chunk, dv))
+    sel = np.zeros((B, Hkv, T, 3), dtype=np.int64)
+    for b, g, t in itertools.product(range(B), range(Hkv), range(T)):
+        sel[b, g, t] = np.sort(rng.choice(C, 3, replace=False))
+    Kt = rng.standard_normal((B, Hkv, Lt, dk))
+    Vt = rng.standard_normal((B, Hkv, Lt, dv))
+    tl = np.array([Lt, 2][:B])
+    Kn = rng.standard_normal((B, T, Hkv, dk))
+    Vn = rng.standard_normal((B, T, Hkv, dv))
+    return q, K, V, sel, chunk, Kt, Vt, tl, Kn, Vn
+
+
+def check_attention_tail(fn):
+    fx = golden("attention_tail_hand.json")
+    out, lse = fn(np.array(fx["q"]), np.array(fx["K"]), np.array(fx["V"]), np.array(fx["sel"]), fx["chunk"],
+                  fx["scale"], np.array(fx["K_tail"]), np.array(fx["V_tail"]), np.array(fx["tail_len"]),
+                  np.array(fx["K_new"]), np.array(fx["V_new"]))
+    np.testing.assert_allclose(out, fx["expected_out"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, fx["expected_lse"], rtol=0, atol=1e-12)
+
+    rng = np.random.default_rng(11)
+    q, K, V, sel, chunk, Kt, Vt, tl, Kn, Vn = tail_inputs(rng)
+    B, T, Hq, _ = q.shape
+    G = Hq // K.shape[1]
+    out, lse = fn(q, K, V, sel, chunk, 0.4, Kt, Vt, tl, Kn, Vn)
+    # the same rows laid out as one sequence (pool, tail, real, speculative) with a
+    # boolean mask, through the library's masked attention in fp64
+    for b, t, h in itertools.product(range(B), range(T), range(Hq)):
+        g = h // G
+        Kall = np.concatenate([K[b, g], Kt[b, g], Kn[b, :, g]])
+        Vall = np.concatenate([V[b, g], Vt[b, g], Vn[b, :, g]])
+        L, Lt = K.shape[2], Kt.shape[2]
+        mask = np.zeros(len(Kall), dtype=bool)
+        for c in sel[b, g, t]:
+            mask[c * chunk:(c + 1) * chunk] = True
+        mask[L:L + tl[b]] = True
+        mask[L + Lt:L + Lt + t + 1] = True        # causal: tokens up to t
+        ref = sdpa_masked(q[b, t, h], Kall, Vall, mask, 0.4)
+        np.testing.assert_allclose(out[b, t, h], ref, rtol=0, atol=1e-12)
+        z = 0.4 * Kall[mask] @ q[b, t, h]
+        assert abs(lse[b, t, h] - math.log(np.sum(np.exp(z)))) < 1e-12
+    # causality: the speculative token's fresh row never reaches the real query ...
+    Kn2, Vn2 = Kn.copy(), Vn.copy()
+    Kn2[:, 1] = 50.0 * rng.standard_normal(Kn2[:, 1].shape)
+    Vn2[:, 1] = 9.0
+    out2, lse2 = fn(q, K, V, sel, chunk, 0.4, Kt, Vt, tl, Kn2, Vn2)
+    np.testing.assert_array_equal(out2[:, 0], out[:, 0])
+    np.testing.assert_array_equal(lse2[:, 0], lse[:, 0])
+    # ... while the real token's fresh row reaches both
+    Vn3 = Vn.copy()
+    Vn3[:, 0] += 1.0
+    out3, _ = fn(q, K, V, sel, chunk, 0.4, Kt, Vt, tl, Kn, Vn3)
+    assert np.all(np.abs(out3[:, 0] - out[:, 0]) > 1e-9) and np.all(np.abs(out3[:, 1] - out[:, 1]) > 1e-9)
+    # no tail and no fresh rows: plain sparse attention; an empty tail adds nothing
+    o0, l0 = fn(q, K, V, sel, chunk, 0.4)
+    r0, rl0 = O.sparse_attention(q, K, V, sel, chunk, 0.4)
+    np.testing.assert_allclose(o0, r0, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l0, rl0, rtol=0, atol=1e-13)
+    o1, l1 = fn(q, K, V, sel, chunk, 0.4, Kt, Vt, np.zeros(B, dtype=np.int64))
+    np.testing.assert_allclose(o1, r0, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l1, rl0, rtol=0, atol=1e-13)
+
+
+def test_attention_tail_pins():
+    check_attention_tail(O.sparse_attention_tail)
+
+
+# ----------------------------------------------------------------------------
 # hot-cache plan
 # ----------------------------------------------------------------------------
 
@@ -392,7 +466,49 @@ def _cache_plan_misses_descending_slots(resident, union_ids, count):
                 miss_count=mn, hit_count=hn)
 
 
+def _tail_no_causal_mask(q, K, V, sel, chunk, scale, K_tail=None, V_tail=None, tail_len=None, K_new=None,
+                         V_new=None):
+    # every query sees every fresh row: the speculative token leaks into the real one
+    if K_new is None:
+        return O.sparse_attention_tail(q, K, V, sel, chunk, scale, K_tail, V_tail, tail_len)
+    out = np.zeros(q.shape[:3] + (V.shape[3],))
+    lse = np.zeros(q.shape[:3])
+    for t in range(q.shape[1]):
+        o, l = _tail_all_fresh(q[:, [t]], K, V, sel[:, :, [t]], chunk, scale, K_tail, V_tail, tail_len, K_new,
+                               V_new)
+        out[:, t], lse[:, t] = o[:, 0], l[:, 0]
+    return out, lse
+
+
+def _tail_all_fresh(q, K, V, sel, chunk, scale, K_tail, V_tail, tail_len, K_new, V_new):
+    B, T1, Hq, dk = q.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    out = np.zeros((B, 1, Hq, V.shape[3]))
+    lse = np.zeros((B, 1, Hq))
+    for b, h in itertools.product(range(B), range(Hq)):
+        g = h // G
+        rows = np.concatenate([np.arange(c * chunk, (c + 1) * chunk) for c in sel[b, g, 0]])
+        Kr = np.concatenate([K[b, g, rows]] + ([K_tail[b, g, :tail_len[b]]] if K_tail is not None else [])
+                            + [K_new[b, :, g]])
+        Vr = np.concatenate([V[b, g, rows]] + ([V_tail[b, g, :tail_len[b]]] if K_tail is not None else [])
+                            + [V_new[b, :, g]])
+        z = scale * Kr @ q[b, 0, h]
+        p = np.exp(z - z.max())
+        out[b, 0, h] = p @ Vr / p.sum()
+        lse[b, 0, h] = z.max() + math.log(p.sum())
+    return out, lse
+
+
+def _tail_ignores_tail_len(q, K, V, sel, chunk, scale, K_tail=None, V_tail=None, tail_len=None, K_new=None,
+                           V_new=None):
+    full = None if tail_len is None else np.full_like(np.asarray(tail_len), K_tail.shape[2])
+    return O.sparse_attention_tail(q, K, V, sel, chunk, scale, K_tail, V_tail, full, K_new, V_new)
+
+
 @pytest.mark.parametrize("check,bad", [
+    (check_attention_tail, _tail_no_causal_mask),
+    (check_attention_tail, _tail_ignores_tail_len),
     (check_landmarks, _landmarks_off_by_one),
     (check_landmarks, _landmarks_wrong_divisor),
     (check_scores, _scores_wrong_group),
