@@ -46,6 +46,10 @@ def parse():
                     help="score from the fp32 landmarks only (no fp16 landmark shadow)")
     ap.add_argument("--host-copy", choices=("mapped", "copy"), default="mapped",
                     help="host-pool workloads: gather kernel over the mapped pool, or hipMemcpyAsync")
+    ap.add_argument("--tail", type=int, default=0,
+                    help="attend, besides the chunks, a per-request tail of up to this many rows "
+                         "(lengths drawn in [tail/2, tail]) and the step's two fresh rows "
+                         "(dk_sparse_decode_attn_tail)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB + 1 GiB device copy (dk_gather_kv over consecutive "
                          "chunks) three times: the known-size reference for HBM byte counters")
@@ -383,7 +387,22 @@ def main():
     lm_bytes_layer = w.landmark_bytes()
     accuracy = float(np.mean(overlap)) / w.k
 
-    calls = ("score_topk_union", "sparse_decode_attn")
+    attn_call = "sparse_decode_attn_tail" if args.tail else "sparse_decode_attn"
+    calls = ("score_topk_union", attn_call)
+    if args.tail:
+        # one tail and one pair of fresh rows, shared by the layers like the pool
+        gt = torch.Generator(device=dev)
+        gt.manual_seed(args.seed + 7)
+        kvdt = K.dtype
+        K_tail = torch.randn(w.B, w.Hkv, args.tail, w.d, generator=gt, device=dev).to(kvdt)
+        V_tail = torch.randn(w.B, w.Hkv, args.tail, w.d, generator=gt, device=dev).to(kvdt)
+        tail_len = torch.randint(args.tail // 2, args.tail + 1, (w.B,), generator=gt, device=dev,
+                                 dtype=torch.int32)
+        K_new = torch.randn(w.B, w.T, w.Hkv, w.d, generator=gt, device=dev).to(kvdt)
+        V_new = torch.randn(w.B, w.T, w.Hkv, w.d, generator=gt, device=dev).to(kvdt)
+        ws_tail = torch.empty(dkb.attn_tail_workspace_size(w.B, w.Hkv, w.T, w.Hq, w.d, w.T * w.k, w.chunk),
+                              dtype=torch.uint8, device=dev)
+        tail_rows = int(tail_len.sum().item())
     use_events = not args.no_events
     # one set of events per (step, layer), read only after the timed region
     ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(w.layers)]
@@ -400,8 +419,13 @@ def main():
                                  st.member, st.count, st.overlap, st.ws_topk, shadow=shadow)
             if record:
                 e[1].record()
-            dkb.sparse_decode_attn(q, K, V, st.union_ids, st.member, st.count, w.chunk, w.scale,
-                                   out=st.out, lse=st.lse, ws=st.ws_attn)
+            if args.tail:
+                dkb.sparse_decode_attn_tail(q, K, V, st.union_ids, st.member, st.count, w.chunk, w.scale,
+                                            K_tail=K_tail, V_tail=V_tail, tail_len=tail_len, K_new=K_new,
+                                            V_new=V_new, out=st.out, lse=st.lse, ws=ws_tail)
+            else:
+                dkb.sparse_decode_attn(q, K, V, st.union_ids, st.member, st.count, w.chunk, w.scale,
+                                       out=st.out, lse=st.lse, ws=st.ws_attn)
             if record:
                 e[2].record()
 
@@ -438,7 +462,8 @@ def main():
     per_call_bytes = {
         # scores and selection, then the union: both sets read back, ids + bits written
         "score_topk_union": score_bytes + w.B * w.Hkv * w.T * w.k * 4 * 3,
-        "sparse_decode_attn": sel_bytes_step / w.layers,
+        attn_call: sel_bytes_step / w.layers
+        + (w.Hkv * (tail_rows + w.B * w.T) * w.d * 2 * K.element_size() if args.tail else 0),
     }
     for c in calls:
         if not use_events:
@@ -447,7 +472,7 @@ def main():
         gbps = per_call_bytes[c] / (avg_ms * 1e-3) / 1e9
         kernels[c] = {"avg_us": round(avg_ms * 1e3, 2), "bytes_per_launch": int(per_call_bytes[c]),
                       "GBps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
-    attn_ms_step = call_ms["sparse_decode_attn"] / args.steps if use_events else float("nan")
+    attn_ms_step = call_ms[attn_call] / args.steps if use_events else float("nan")
     sel_gbps = sel_bytes_step / (attn_ms_step * 1e-3) / 1e9 if use_events else float("nan")
 
     # every byte the step moves: landmark scoring, union chunks, queries, outputs, indices
@@ -479,7 +504,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "L": w.L, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d,
                    "chunk": w.chunk, "k": w.k, "T": w.T, "layers": w.layers, "seed": args.seed,
-                   "landmark_shadow": shadow is not None},
+                   "landmark_shadow": shadow is not None, "tail_max": args.tail},
         "ms_per_step_median": round(float(np.median(step_ms)), 4) if step_ms else None,
         "ms_per_step_min": round(float(np.min(step_ms)), 4) if step_ms else None,
         "selected_kv_GBps": round(sel_gbps, 1),

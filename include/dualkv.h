@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define DK_ABI_VERSION 4
+#define DK_ABI_VERSION 5
 
 typedef enum {
     DK_OK = 0,
@@ -310,6 +310,50 @@ dk_status dk_sparse_decode_attn(const float* q, int B, int T, int Hq, int Hkv,
                                 const int32_t* block_ids, const uint8_t* member,
                                 const int32_t* count, int N, int pool_blocks, float scale,
                                 float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * dk_sparse_decode_attn_tail - dk_sparse_decode_attn plus the rows every query
+ * attends besides its chunks.
+ *
+ * DualDecoder "5.2 Dual-Token Decoding Pipeline": the step's real and
+ * speculative tokens lie one after the other along the sequence, and a mask
+ * keeps the real token from the speculative token's data while the speculative
+ * token sees every earlier token, the real one included.  Adaptive DHiSparse
+ * Figure 2: each request's tail of recent rows is resolved for every lookup,
+ * besides the selected rows.
+ *
+ * For query head h (KV head g) and query t the key rows are its own chunks' rows
+ * (as in dk_sparse_decode_attn), the first tail_len[b] rows of the tail, and the
+ * new rows of the step's tokens t' <= t; the softmax runs over all of them.
+ *
+ * extra->K_tail, V_tail : [B, Hkv, tail_max, dk] pools (kv_dtype) with element
+ *                         strides tail_k_s, tail_v_s, or both NULL (no tail).
+ * extra->tail_len       : int32 [B], clamped to [0, tail_max], or NULL (tail_max).
+ * extra->K_new, V_new   : [B, T, Hkv, dk] contiguous (kv_dtype): the step's own
+ *                         tokens' keys and values, or both NULL.
+ * ws                    : dk_attn_tail_workspace_size(...) bytes; contents on
+ *                         entry are ignored.  The tail goes to a partial result of
+ *                         its own that is merged with the chunks' partials.
+ * Other arguments and errors: as dk_sparse_decode_attn; DK_ERR_INVALID_ARG also
+ * for a NULL extra, a half-given K/V pair or negative tail sizes.
+ */
+typedef struct {
+    const void* K_tail;
+    const void* V_tail;
+    dk_strides tail_k_s, tail_v_s;
+    const int32_t* tail_len;
+    int tail_max;
+    const void* K_new;
+    const void* V_new;
+} dk_attn_extra;
+size_t dk_attn_tail_workspace_size(int B, int Hkv, int T, int Hq, int dv, int N, int chunk);
+dk_status dk_sparse_decode_attn_tail(const float* q, int B, int T, int Hq, int Hkv,
+                                     const void* K, const void* V, dk_dtype kv_dtype,
+                                     dk_strides ks, dk_strides vs, int dk, int dv, int chunk,
+                                     const int32_t* block_ids, const uint8_t* member,
+                                     const int32_t* count, int N, int pool_blocks,
+                                     const dk_attn_extra* extra, float scale,
+                                     float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libdualkv.so")
 DK_OK, DK_ERR_INVALID_ARG, DK_ERR_UNSUPPORTED, DK_ERR_HIP = 0, 1, 2, 3
 DK_F32, DK_BF16 = 0, 1
 DK_REDUCE_MEAN, DK_REDUCE_MAX = 0, 1
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 _STATUS = {0: "DK_OK", 1: "DK_ERR_INVALID_ARG", 2: "DK_ERR_UNSUPPORTED", 3: "DK_ERR_HIP"}
 
@@ -47,6 +47,12 @@ class dk_cache_plan(ctypes.Structure):
                 ("hit_count", ctypes.c_void_p)]
 
 
+class dk_attn_extra(ctypes.Structure):
+    _fields_ = [("K_tail", ctypes.c_void_p), ("V_tail", ctypes.c_void_p), ("tail_k_s", dk_strides),
+                ("tail_v_s", dk_strides), ("tail_len", ctypes.c_void_p), ("tail_max", ctypes.c_int),
+                ("K_new", ctypes.c_void_p), ("V_new", ctypes.c_void_p)]
+
+
 # (name, restype, argtypes) of every exported function
 _P, _I, _Z, _F, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float, dk_strides
 EXPORTS = [
@@ -64,6 +70,9 @@ EXPORTS = [
     ("dk_attn_workspace_size", _Z, [_I, _I, _I, _I, _I, _I, _I]),
     ("dk_sparse_decode_attn", _I, [_P, _I, _I, _I, _I, _P, _P, _I, _S, _S, _I, _I, _I, _P, _P, _P,
                                    _I, _I, _F, _P, _P, _P, _Z, _P]),
+    ("dk_attn_tail_workspace_size", _Z, [_I, _I, _I, _I, _I, _I, _I]),
+    ("dk_sparse_decode_attn_tail", _I, [_P, _I, _I, _I, _I, _P, _P, _I, _S, _S, _I, _I, _I, _P, _P, _P,
+                                        _I, _I, ctypes.POINTER(dk_attn_extra), _F, _P, _P, _P, _Z, _P]),
 ]
 
 
@@ -334,6 +343,57 @@ def sparse_decode_attn(q, K, V, block_ids, member, count, chunk: int, scale: flo
 # ----------------------------------------------------------------------------
 # one layer of the HBM-pool step with buffers allocated once
 # ----------------------------------------------------------------------------
+
+def attn_tail_workspace_size(B, Hkv, T, Hq, dv, N, chunk) -> int:
+    return int(lib.dk_attn_tail_workspace_size(B, Hkv, T, Hq, dv, N, chunk))
+
+
+def sparse_decode_attn_tail(q, K, V, block_ids, member, count, chunk: int, scale: float, K_tail=None,
+                            V_tail=None, tail_len=None, K_new=None, V_new=None, pool_blocks: int | None = None,
+                            out=None, lse=None, ws=None, stream=None):
+    """sparse_decode_attn plus the tail rows [B, Hkv, tail_max, d] (first tail_len[b]
+    rows of request b) and the step's own rows K_new, V_new [B, T, Hkv, d] under the
+    dual-token causal rule."""
+    B, T, Hq, dk = q.shape
+    Hkv = K.shape[1]
+    dv = V.shape[3]
+    N = block_ids.shape[2]
+    _need(q, torch.float32, (B, T, Hq, dk), "q")
+    _need(block_ids, torch.int32, (B, Hkv, N), "block_ids")
+    if member is not None:
+        _need(member, torch.uint8, (B, Hkv, N), "member")
+    if count is not None:
+        _need(count, torch.int32, (B, Hkv), "count")
+    for name, t in (("K_tail", K_tail), ("V_tail", V_tail), ("K_new", K_new), ("V_new", V_new)):
+        if t is not None and t.dtype != K.dtype:
+            raise ValueError(f"{name} must have the pools' dtype")
+    if K_new is not None:
+        _need(K_new, K.dtype, (B, T, Hkv, dk), "K_new")
+        _need(V_new, V.dtype, (B, T, Hkv, dv), "V_new")
+    if tail_len is not None:
+        _need(tail_len, torch.int32, (B,), "tail_len")
+    if out is None:
+        out = torch.empty(B, T, Hq, dv, dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty(B, T, Hq, dtype=torch.float32, device=q.device)
+    if pool_blocks is None:
+        pool_blocks = K.shape[2] // chunk
+    nbytes = attn_tail_workspace_size(B, Hkv, T, Hq, dv, N, chunk)
+    if ws is None and nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    zero = dk_strides(0, 0, 0)
+    extra = dk_attn_extra(_ptr(K_tail), _ptr(V_tail),
+                          pool_strides(K_tail) if K_tail is not None else zero,
+                          pool_strides(V_tail) if V_tail is not None else zero,
+                          _ptr(tail_len), K_tail.shape[2] if K_tail is not None else 0,
+                          _ptr(K_new), _ptr(V_new))
+    _check(lib.dk_sparse_decode_attn_tail(_ptr(q), B, T, Hq, Hkv, _ptr(K), _ptr(V), _dtype(K),
+                                          pool_strides(K), pool_strides(V), dk, dv, chunk, _ptr(block_ids),
+                                          _ptr(member), _ptr(count), N, pool_blocks, ctypes.byref(extra),
+                                          float(scale), _ptr(out), _ptr(lse), _ptr(ws),
+                                          0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+    return out, lse
+
 
 class DecodeStep:
     """Preallocated buffers for score_topk_union -> sparse_decode_attn.

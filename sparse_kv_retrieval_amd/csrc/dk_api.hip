@@ -337,9 +337,63 @@ dk_status dk_sparse_decode_attn(const float* q, int B, int T, int Hq, int Hkv, c
     DK_REQUIRE(ws_bytes >= plan.ws_bytes && (plan.ws_bytes == 0 || ws), DK_ERR_INVALID_ARG,
                "dk_sparse_decode_attn: workspace needs %zu bytes (got %zu)", plan.ws_bytes, ws_bytes);
     hipError_t e = dk::launch_attention(q, B, T, Hq, Hkv, K, V, kv_dtype, ks, vs, dk, chunk, block_ids,
-                                        member, count, N, pool_blocks, scale, out, lse, ws, plan,
+                                        member, count, N, pool_blocks, scale, out, lse, ws, plan, nullptr,
                                         (hipStream_t)stream);
     return e == hipSuccess ? DK_OK : hip_fail(e, "dk_sparse_decode_attn");
+}
+
+size_t dk_attn_tail_workspace_size(int B, int Hkv, int T, int Hq, int dv, int N, int chunk) {
+    if (B < 1 || Hkv < 1 || T < 1 || T > 2 || Hq < 1 || Hq % Hkv || dv < 1 || N < 1 || chunk < 1)
+        return 0;
+    return dk::plan_attn(B, Hkv, T, Hq, dv, N, chunk, true).ws_bytes;
+}
+
+dk_status dk_sparse_decode_attn_tail(const float* q, int B, int T, int Hq, int Hkv, const void* K,
+                                     const void* V, dk_dtype kv_dtype, dk_strides ks, dk_strides vs,
+                                     int dk, int dv, int chunk, const int32_t* block_ids,
+                                     const uint8_t* member, const int32_t* count, int N, int pool_blocks,
+                                     const dk_attn_extra* extra, float scale, float* out, float* lse,
+                                     void* ws, size_t ws_bytes, void* stream) {
+    g_err.clear();
+    const char* fn = "dk_sparse_decode_attn_tail";
+    const int esz = dtype_size(kv_dtype);
+    DK_REQUIRE(q && K && V && block_ids && out && extra, DK_ERR_INVALID_ARG,
+               "%s: q, K, V, block_ids, out, extra must be non-NULL", fn);
+    DK_REQUIRE(esz != 0, DK_ERR_INVALID_ARG, "%s: unknown kv_dtype %d", fn, (int)kv_dtype);
+    DK_REQUIRE(B >= 1 && Hq >= 1 && Hkv >= 1 && dk >= 1 && dv >= 1 && chunk >= 1 && N >= 1 &&
+                   pool_blocks >= 0,
+               DK_ERR_INVALID_ARG, "%s: sizes out of range", fn);
+    DK_REQUIRE(T == 1 || T == 2, DK_ERR_INVALID_ARG, "%s: T must be 1 or 2 (got %d)", fn, T);
+    DK_REQUIRE(Hq % Hkv == 0, DK_ERR_INVALID_ARG, "%s: Hq (%d) %% Hkv (%d) != 0", fn, Hq, Hkv);
+    DK_REQUIRE(member || T == 1, DK_ERR_INVALID_ARG, "%s: member is required when T == 2", fn);
+    DK_REQUIRE(std::isfinite(scale), DK_ERR_INVALID_ARG, "%s: scale must be finite", fn);
+    DK_REQUIRE(!extra->K_tail == !extra->V_tail, DK_ERR_INVALID_ARG,
+               "%s: K_tail and V_tail must both be given or both be NULL", fn);
+    DK_REQUIRE(!extra->K_new == !extra->V_new, DK_ERR_INVALID_ARG,
+               "%s: K_new and V_new must both be given or both be NULL", fn);
+    DK_REQUIRE(!extra->K_tail || (extra->tail_max >= 0 && extra->tail_k_s.b >= 0 && extra->tail_k_s.h >= 0 &&
+                                  extra->tail_k_s.t >= 0 && extra->tail_v_s.b >= 0 && extra->tail_v_s.h >= 0 &&
+                                  extra->tail_v_s.t >= 0),
+               DK_ERR_INVALID_ARG, "%s: tail_max and the tail strides must be >= 0", fn);
+    DK_REQUIRE(dk == dv && (dk == 64 || dk == 128), DK_ERR_UNSUPPORTED,
+               "%s: needs dk == dv in {64, 128} (got %d, %d)", fn, dk, dv);
+    DK_REQUIRE((Hq / Hkv) * T <= 16, DK_ERR_UNSUPPORTED, "%s: G*T must be <= 16", fn);
+    DK_REQUIRE(aligned16(q) && aligned16(out) && aligned16(K) && aligned16(V) && strides_ok(ks, esz) &&
+                   strides_ok(vs, esz) &&
+                   (!extra->K_tail || (aligned16(extra->K_tail) && aligned16(extra->V_tail) &&
+                                       strides_ok(extra->tail_k_s, esz) && strides_ok(extra->tail_v_s, esz))) &&
+                   (!extra->K_new || (aligned16(extra->K_new) && aligned16(extra->V_new))),
+               DK_ERR_UNSUPPORTED, "%s: q, out, K, V, the tail and new rows and their strides must be 16-byte aligned",
+               fn);
+    const dk::AttnPlan plan = dk::plan_attn(B, Hkv, T, Hq, dv, N, chunk, true);
+    DK_REQUIRE(ws_bytes >= plan.ws_bytes && (plan.ws_bytes == 0 || ws), DK_ERR_INVALID_ARG,
+               "%s: workspace needs %zu bytes (got %zu)", fn, plan.ws_bytes, ws_bytes);
+    const dk::AttnTail tail{extra->K_tail, extra->V_tail, extra->tail_k_s, extra->tail_v_s, extra->tail_len,
+                            extra->K_tail ? extra->tail_max : 0, extra->K_new, extra->V_new};
+    hipError_t e = dk::launch_attention(q, B, T, Hq, Hkv, K, V, kv_dtype, ks, vs, dk, chunk, block_ids,
+                                        member, count, N, pool_blocks, scale, out, lse, ws, plan, &tail,
+                                        (hipStream_t)stream);
+    return e == hipSuccess ? DK_OK : hip_fail(e, fn);
 }
 
 }  // extern "C"

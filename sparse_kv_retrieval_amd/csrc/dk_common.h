@@ -174,13 +174,25 @@ hipError_t launch_gather_stream(const void* K_src, const void* V_src, dk_dtype d
 
 struct AttnPlan {
     int splits;        // union-range splits per (b, g)
-    size_t ws_bytes;   // partial results (0 when splits == 1)
+    int nparts;        // partial slots per (b, g): splits, plus one for tail rows
+    size_t ws_bytes;   // partial results (0 when nparts == 1)
 };
-AttnPlan plan_attn(int B, int Hkv, int T, int Hq, int dv, int N, int chunk);
+// Rows every query attends besides its chunks (dk_sparse_decode_attn_tail).
+struct AttnTail {
+    const void* K_tail;       // [B, Hkv, tail_max, D] with strides kts / vts, or null
+    const void* V_tail;
+    dk_strides kts, vts;
+    const int32_t* tail_len;  // [B] or null (tail_max rows each)
+    int tail_max;
+    const void* K_new;        // [B, T, Hkv, D] contiguous, or null
+    const void* V_new;
+};
+AttnPlan plan_attn(int B, int Hkv, int T, int Hq, int dv, int N, int chunk, bool tail = false);
 hipError_t launch_attention(const float* q, int B, int T, int Hq, int Hkv, const void* K,
                             const void* V, dk_dtype dt, dk_strides ks, dk_strides vs, int D,
                             int chunk, const int32_t* block_ids, const uint8_t* member,
                             const int32_t* count, int N, int pool_blocks, float scale, float* out,
-                            float* lse, void* ws, const AttnPlan& plan, hipStream_t st);
+                            float* lse, void* ws, const AttnPlan& plan, const AttnTail* tail,
+                            hipStream_t st);
 
 }  // namespace dk

@@ -52,8 +52,17 @@ struct AttnArgs {
     int splits;
     float* out;
     float* lse;
-    float* part_acc;   // [bg][split][R][D]
-    float* part_ml;    // [bg][split][R][2]
+    float* part_acc;   // [bg][part][R][D]
+    float* part_ml;    // [bg][part][R][2]
+    int nparts;        // partial slots per (b, g): the ranges, plus one for the tail rows
+    // rows every query attends besides its chunks (k_attn_tail)
+    const void* Kt;
+    const void* Vt;
+    dk_strides kts, vts;
+    const int32_t* tail_len;
+    int tail_max;
+    const void* Kn;    // [B, T, Hkv, D]: the step's own tokens
+    const void* Vn;
 };
 
 __device__ __forceinline__ void entry_range(const AttnArgs& a, int bg, int split, int& u0, int& u1) {
@@ -68,14 +77,14 @@ template <int D>
 __device__ __forceinline__ void emit_row(const AttnArgs& a, int b, int bg, int split, int t, int h,
                                          int r, int R, float m, float l, const float* acc,
                                          int dim0, int ndim, bool lead) {
-    if (a.splits == 1) {
+    if (a.nparts == 1) {
         float* o = a.out + (((int64_t)b * a.T + t) * a.Hq + h) * D + dim0;
         const float inv = l > 0.f ? 1.f / l : 0.f;
         for (int e = 0; e < ndim; ++e) o[e] = acc[e] * inv;
         if (lead && a.lse)
             a.lse[((int64_t)b * a.T + t) * a.Hq + h] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
     } else {
-        const int64_t slot = ((int64_t)bg * a.splits + split) * R + r;
+        const int64_t slot = ((int64_t)bg * a.nparts + split) * R + r;
         float* p = a.part_acc + slot * D + dim0;
         for (int e = 0; e < ndim; ++e) p[e] = acc[e];
         if (lead) {
@@ -314,28 +323,197 @@ __global__ __launch_bounds__(kThreads) void k_attn_bf16_d128_g4t2(AttnArgs a) {
 // Generic path: fp32 or bf16 K/V, D in {64, 128}, any G*T <= 16, any chunk.
 // Correct and simple; used off the fast path's shapes.
 // ---------------------------------------------------------------------------
-template <typename KVT, int D>
-__device__ __forceinline__ float kv_elem(const KVT* p, int64_t i);
-template <>
-__device__ __forceinline__ float kv_elem<float, 64>(const float* p, int64_t i) { return p[i]; }
-template <>
-__device__ __forceinline__ float kv_elem<float, 128>(const float* p, int64_t i) { return p[i]; }
-template <>
-__device__ __forceinline__ float kv_elem<uint16_t, 64>(const uint16_t* p, int64_t i) {
-    return __uint_as_float((uint32_t)p[i] << 16);
-}
-template <>
-__device__ __forceinline__ float kv_elem<uint16_t, 128>(const uint16_t* p, int64_t i) {
-    return __uint_as_float((uint32_t)p[i] << 16);
+// One tile of up to TR K and V rows staged through registers: every thread
+// issues all of its 16-byte loads before any is waited on, so a tile costs one
+// memory latency; the values are widened to fp32 when written to LDS.  K rows
+// in LDS are padded to D + 4 floats (16-byte aligned rows, float4 reads spread
+// over the banks).
+template <typename KVT, int D, int TR>
+struct TileRegs {
+    static constexpr int kEpv = 16 / (int)sizeof(KVT);          // elements per 16-byte vector
+    static constexpr int kVpr = D / kEpv;                        // vectors per row
+    static constexpr int kPer = (TR * kVpr + kThreads - 1) / kThreads;
+    uint4 k[kPer], v[kPer];
+};
+
+struct RowPair {
+    const void* k;
+    const void* v;
+};
+
+// rows(rr) gives the addresses of K and V row rr of the tile (16-byte aligned)
+template <typename KVT, int D, int TR, typename Rows>
+__device__ __forceinline__ void tile_load(TileRegs<KVT, D, TR>& t, int nr, Rows rows) {
+    using TT = TileRegs<KVT, D, TR>;
+#pragma unroll
+    for (int p = 0; p < TT::kPer; ++p) {
+        const int i = threadIdx.x + p * kThreads;
+        const int rr = i / TT::kVpr, x = i - rr * TT::kVpr;
+        if (rr < nr) {
+            const RowPair rp = rows(rr);
+            t.k[p] = ((const uint4*)rp.k)[x];
+            t.v[p] = ((const uint4*)rp.v)[x];
+        }
+    }
 }
 
-template <typename KVT, int D>
+__device__ __forceinline__ void widen(const uint4& u, float* f, uint16_t) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        f[2 * j] = __uint_as_float(w[j] << 16);
+        f[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void widen(const uint4& u, float* f, float) {
+    f[0] = __uint_as_float(u.x);
+    f[1] = __uint_as_float(u.y);
+    f[2] = __uint_as_float(u.z);
+    f[3] = __uint_as_float(u.w);
+}
+
+template <typename KVT, int D, int TR>
+__device__ __forceinline__ void tile_store(const TileRegs<KVT, D, TR>& t, int nr, float (*kt)[D + 4],
+                                           float (*vt)[D]) {
+    using TT = TileRegs<KVT, D, TR>;
+    constexpr int E = TT::kEpv;
+#pragma unroll
+    for (int p = 0; p < TT::kPer; ++p) {
+        const int i = threadIdx.x + p * kThreads;
+        const int rr = i / TT::kVpr, x = i - rr * TT::kVpr;
+        if (rr < nr) {
+            float f[E];
+            widen(t.k[p], f, KVT{});
+#pragma unroll
+            for (int e = 0; e < E; e += 4) *(float4*)&kt[rr][x * E + e] = make_float4(f[e], f[e + 1], f[e + 2], f[e + 3]);
+            widen(t.v[p], f, KVT{});
+#pragma unroll
+            for (int e = 0; e < E; e += 4) *(float4*)&vt[rr][x * E + e] = make_float4(f[e], f[e + 1], f[e + 2], f[e + 3]);
+        }
+    }
+}
+
+// One tile of nr (<= TR) key rows already in kt / vt.  Wave w owns query rows
+// r = w + 4x (x < XR): it computes their logits with one lane per key row, so a
+// K row is read from LDS once for all of the wave's rows, updates (m, l, acc)
+// by online softmax, and forms the weighted value sum, reading each V row once
+// for all of its rows.  The probabilities pass through the wave's own zs rows,
+// four per LDS read.  vis(r, jj) says whether query row r may use key row jj.
+// Only the wave's own LDS rows are written: no block barrier inside.
+template <int D, int TR, int XR, typename Vis>
+__device__ __forceinline__ void attend_tile(const AttnArgs& a, int nr, const float (*qs)[D],
+                                            const float (*kt)[D + 4], const float (*vt)[D], float (*zs)[TR],
+                                            Vis vis, float* m_run, float* l_run, float (*acc)[D / kWave]) {
+    static_assert(TR == 32 || TR == 64, "tile rows");
+    constexpr int DPL = D / kWave;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    float s[XR][4];
+#pragma unroll
+    for (int x = 0; x < XR; ++x)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) s[x][c] = 0.f;
+    const int jr = lane < nr ? lane : 0;       // lanes past the tile are masked below
+#pragma unroll 4
+    for (int dd = 0; dd < D; dd += 4) {
+        const float4 kv = *(const float4*)&kt[jr][dd];
+#pragma unroll
+        for (int x = 0; x < XR; ++x) {
+            const float4 qv = *(const float4*)&qs[w + 4 * x][dd];
+            s[x][0] = fmaf(qv.x, kv.x, s[x][0]);
+            s[x][1] = fmaf(qv.y, kv.y, s[x][1]);
+            s[x][2] = fmaf(qv.z, kv.z, s[x][2]);
+            s[x][3] = fmaf(qv.w, kv.w, s[x][3]);
+        }
+    }
+#pragma unroll
+    for (int x = 0; x < XR; ++x) {
+        const int r = w + 4 * x;
+        float z = ((s[x][0] + s[x][1]) + (s[x][2] + s[x][3])) * a.scale_log2;
+        if (!(lane < nr && vis(r, lane))) z = -INFINITY;
+        float cm = z;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) cm = fmaxf(cm, __shfl_xor(cm, off, kWave));
+        const float mn = fmaxf(m_run[x], cm);
+        const float alpha = mn == -INFINITY ? 1.f : exp2f(m_run[x] - mn);
+        const float p = mn == -INFINITY ? 0.f : exp2f(z - mn);
+        float ps = p;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) ps += __shfl_xor(ps, off, kWave);
+        l_run[x] = l_run[x] * alpha + ps;
+        m_run[x] = mn;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc[x][e] *= alpha;
+        if (lane < TR) zs[r][lane] = p;
+    }
+    __builtin_amdgcn_wave_barrier();
+    for (int j4 = 0; j4 < nr; j4 += 4) {
+        float pj[XR][4];
+#pragma unroll
+        for (int x = 0; x < XR; ++x) {
+            const float4 p4 = *(const float4*)&zs[w + 4 * x][j4];
+            pj[x][0] = p4.x;
+            pj[x][1] = p4.y;
+            pj[x][2] = p4.z;
+            pj[x][3] = p4.w;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (j4 + q < nr) {
+                float v[DPL];
+#pragma unroll
+                for (int e = 0; e < DPL; ++e) v[e] = vt[j4 + q][lane * DPL + e];
+#pragma unroll
+                for (int x = 0; x < XR; ++x)
+#pragma unroll
+                    for (int e = 0; e < DPL; ++e) acc[x][e] = fmaf(pj[x][q], v[e], acc[x][e]);
+            }
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
+// The block's query rows r = t * G + hh of (b, g) into qs, all loads issued
+// before the first is used; with bf16 K/V the query is read as bf16 (RNE).
+// Rows R .. 4 * XR - 1 are zero: they are computed and dropped.
+template <typename KVT, int D, int XR>
+__device__ __forceinline__ void stage_q(const AttnArgs& a, int b, int g, float (*qs)[D]) {
+    constexpr int VPR = D / 4, NV = 4 * XR * VPR, PER = (NV + kThreads - 1) / kThreads;
+    const int G = a.G, R = G * a.T;
+    float4 v[PER];
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+        const int i = threadIdx.x + p * kThreads;
+        const int r = i / VPR, x = i - r * VPR;
+        v[p] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (i < NV && r < R) {
+            const int t = r / G, hh = r - t * G;
+            v[p] = *(const float4*)&a.q[(((int64_t)b * a.T + t) * a.Hq + g * G + hh) * D + 4 * x];
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+        const int i = threadIdx.x + p * kThreads;
+        const int r = i / VPR, x = i - r * VPR;
+        if (i < NV) {
+            float4 u = v[p];
+            if (sizeof(KVT) == 2) {
+                u.x = __uint_as_float(f32_to_bf16_rne(u.x) << 16);
+                u.y = __uint_as_float(f32_to_bf16_rne(u.y) << 16);
+                u.z = __uint_as_float(f32_to_bf16_rne(u.z) << 16);
+                u.w = __uint_as_float(f32_to_bf16_rne(u.w) << 16);
+            }
+            *(float4*)&qs[r][4 * x] = u;
+        }
+    }
+}
+
+template <typename KVT, int D, int XR>
 __global__ __launch_bounds__(kThreads) void k_attn_generic(AttnArgs a) {
     constexpr int TR = 32, RMAX = 16, DPL = D / kWave;
-    __shared__ float qs[RMAX][D];
-    __shared__ float kt[TR][D + 1];
-    __shared__ float vt[TR][D];
-    __shared__ float zs[RMAX][TR];
+    __shared__ __align__(16) float qs[RMAX][D];
+    __shared__ __align__(16) float kt[TR][D + 4];
+    __shared__ __align__(16) float vt[TR][D];
+    __shared__ __align__(16) float zs[RMAX][TR];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int split = blockIdx.x % a.splits;
@@ -345,20 +523,13 @@ __global__ __launch_bounds__(kThreads) void k_attn_generic(AttnArgs a) {
     int u0, u1;
     entry_range(a, bg, split, u0, u1);
 
-    // q rows r = t * G + hh, with bf16 K/V the query is read as bf16 (RNE)
-    for (int i = tid; i < R * D; i += kThreads) {
-        const int r = i / D, dd = i - r * D;
-        const int t = r / G, hh = r - t * G;
-        float x = a.q[(((int64_t)b * T + t) * a.Hq + g * G + hh) * D + dd];
-        if (sizeof(KVT) == 2) x = __uint_as_float(f32_to_bf16_rne(x) << 16);
-        qs[r][dd] = x;
-    }
+    stage_q<KVT, D, XR>(a, b, g, qs);
     const KVT* Kb = (const KVT*)a.K + (int64_t)b * a.ks.b + (int64_t)g * a.ks.h;
     const KVT* Vb = (const KVT*)a.V + (int64_t)b * a.vs.b + (int64_t)g * a.vs.h;
 
-    float m_run[4], l_run[4], acc[4][DPL];
+    float m_run[XR], l_run[XR], acc[XR][DPL];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
+    for (int x = 0; x < XR; ++x) {
         m_run[x] = -INFINITY;
         l_run[x] = 0.f;
 #pragma unroll
@@ -373,58 +544,97 @@ __global__ __launch_bounds__(kThreads) void k_attn_generic(AttnArgs a) {
         for (int st = 0; st < tiles_per_chunk; ++st) {
             const int r0 = st * TR;
             const int nr = min(TR, a.chunk - r0);
-            __syncthreads();
-            for (int i = tid; i < nr * D; i += kThreads) {
-                const int rr = i / D, dd = i - rr * D;
+            TileRegs<KVT, D, TR> tr;
+            tile_load(tr, nr, [&](int rr) {
                 const int64_t row = (int64_t)c * a.chunk + r0 + rr;
-                kt[rr][dd] = kv_elem<KVT, D>(Kb, row * a.ks.t + dd);
-                vt[rr][dd] = kv_elem<KVT, D>(Vb, row * a.vs.t + dd);
-            }
+                return RowPair{Kb + row * a.ks.t, Vb + row * a.vs.t};
+            });
             __syncthreads();
-            for (int i = tid; i < R * TR; i += kThreads) {
-                const int r = i / TR, jj = i - r * TR;
-                float z = -INFINITY;
-                if (jj < nr && ((m >> (r / G)) & 1u)) {
-                    float s = 0.f;
-                    for (int dd = 0; dd < D; ++dd) s = fmaf(qs[r][dd], kt[jj][dd], s);
-                    z = s * a.scale_log2;
-                }
-                zs[r][jj] = z;
-            }
+            tile_store(tr, nr, kt, vt);
             __syncthreads();
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const int r = w + 4 * x;
-                if (r >= R) break;
-                const float z = lane < TR ? zs[r][lane] : -INFINITY;
-                float cm = z;
-#pragma unroll
-                for (int off = 1; off < kWave; off <<= 1) cm = fmaxf(cm, __shfl_xor(cm, off, kWave));
-                const float mn = fmaxf(m_run[x], cm);
-                const float alpha = mn == -INFINITY ? 1.f : exp2f(m_run[x] - mn);
-                const float p = mn == -INFINITY ? 0.f : exp2f(z - mn);
-                float ps = p;
-#pragma unroll
-                for (int off = 1; off < kWave; off <<= 1) ps += __shfl_xor(ps, off, kWave);
-                l_run[x] = l_run[x] * alpha + ps;
-                m_run[x] = mn;
-#pragma unroll
-                for (int e = 0; e < DPL; ++e) acc[x][e] *= alpha;
-                for (int jj = 0; jj < nr; ++jj) {
-                    const float pj = __shfl(p, jj, kWave);
-#pragma unroll
-                    for (int e = 0; e < DPL; ++e) acc[x][e] = fmaf(pj, vt[jj][lane * DPL + e], acc[x][e]);
-                }
-            }
+            attend_tile<D, TR, XR>(a, nr, qs, kt, vt, zs, [&](int r, int) { return ((m >> (r / G)) & 1u) != 0; },
+                                   m_run, l_run, acc);
         }
     }
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
+    for (int x = 0; x < XR; ++x) {
         const int r = w + 4 * x;
         if (r >= R) break;
         const int t = r / G, hh = r - t * G;
         emit_row<D>(a, b, bg, split, t, g * G + hh, r, R, m_run[x], l_run[x], acc[x], lane * DPL,
                     DPL, lane == 0);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Tail rows and the step's own rows, one block per (b, g), written as the last
+// partial of the (b, g) (DualDecoder "5.2": the real token is masked from the
+// speculative token's row, the speculative token sees the real one; Adaptive
+// DHiSparse Figure 2: the request's tail rows are resolved for every lookup).
+// Rows 0 .. nt-1 are the tail, rows nt .. nt+T-1 the step's tokens; 64-row
+// tiles go through LDS as in the generic kernel, so a tail shorter than a
+// 32-row chunk and the step's two rows take one tile.
+// ---------------------------------------------------------------------------
+template <typename KVT, int D, int XR>
+__global__ __launch_bounds__(kThreads) void k_attn_tail(AttnArgs a) {
+    constexpr int TR = 64, RMAX = 16, DPL = D / kWave;
+    __shared__ __align__(16) float qs[RMAX][D];
+    __shared__ __align__(16) float kt[TR][D + 4];
+    __shared__ __align__(16) float vt[TR][D];
+    __shared__ __align__(16) float zs[RMAX][TR];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int bg = blockIdx.x;
+    const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+    const int G = a.G, T = a.T, R = G * T;
+    int nt = 0;
+    if (a.Kt) {
+        nt = a.tail_len ? a.tail_len[b] : a.tail_max;
+        nt = nt < 0 ? 0 : (nt > a.tail_max ? a.tail_max : nt);
+    }
+    const int nrows = nt + (a.Kn ? T : 0);
+    const KVT* Ktb = (const KVT*)a.Kt + (int64_t)b * a.kts.b + (int64_t)g * a.kts.h;
+    const KVT* Vtb = (const KVT*)a.Vt + (int64_t)b * a.vts.b + (int64_t)g * a.vts.h;
+    auto rows_at = [&](int base) {
+        return [=](int rr) {
+            const int row = base + rr;
+            if (row < nt) return RowPair{Ktb + (int64_t)row * a.kts.t, Vtb + (int64_t)row * a.vts.t};
+            const int64_t off = (((int64_t)b * T + (row - nt)) * a.Hkv + g) * D;
+            return RowPair{(const KVT*)a.Kn + off, (const KVT*)a.Vn + off};
+        };
+    };
+    // the first tile is on its way while the queries are staged; later, the
+    // next tile's loads are in flight while the current one is used
+    TileRegs<KVT, D, TR> tr;
+    if (nrows > 0) tile_load(tr, min(TR, nrows), rows_at(0));
+    stage_q<KVT, D, XR>(a, b, g, qs);
+    float m_run[XR], l_run[XR], acc[XR][DPL];
+#pragma unroll
+    for (int x = 0; x < XR; ++x) {
+        m_run[x] = -INFINITY;
+        l_run[x] = 0.f;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc[x][e] = 0.f;
+    }
+    for (int base = 0; base < nrows; base += TR) {
+        const int nr = min(TR, nrows - base);
+        __syncthreads();
+        tile_store(tr, nr, kt, vt);
+        __syncthreads();
+        if (base + TR < nrows) tile_load(tr, min(TR, nrows - base - TR), rows_at(base + TR));
+        // a tail row is seen by every query; the fresh row of token t' only by
+        // queries t >= t'
+        attend_tile<D, TR, XR>(a, nr, qs, kt, vt, zs,
+                               [&](int r, int jj) { return base + jj < nt || base + jj - nt <= r / G; },
+                               m_run, l_run, acc);
+    }
+#pragma unroll
+    for (int x = 0; x < XR; ++x) {
+        const int r = w + 4 * x;
+        if (r >= R) break;
+        const int t = r / G, hh = r - t * G;
+        emit_row<D>(a, b, bg, a.nparts - 1, t, g * G + hh, r, R, m_run[x], l_run[x], acc[x], lane * DPL, DPL,
+                    lane == 0);
     }
 }
 
@@ -440,13 +650,13 @@ __global__ __launch_bounds__(kThreads) void k_attn_merge(AttnArgs a) {
     for (int i = threadIdx.x; i < R * D4; i += kThreads) {
         const int r = i / D4, d4 = i - r * D4;
         float M = -INFINITY;
-        for (int s = 0; s < a.splits; ++s)
-            M = fmaxf(M, a.part_ml[(((int64_t)bg * a.splits + s) * R + r) * 2]);
+        for (int s = 0; s < a.nparts; ++s)
+            M = fmaxf(M, a.part_ml[(((int64_t)bg * a.nparts + s) * R + r) * 2]);
         float L = 0.f;
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
         if (M != -INFINITY) {
-            for (int s = 0; s < a.splits; ++s) {
-                const int64_t slot = ((int64_t)bg * a.splits + s) * R + r;
+            for (int s = 0; s < a.nparts; ++s) {
+                const int64_t slot = ((int64_t)bg * a.nparts + s) * R + r;
                 const float ms = a.part_ml[slot * 2];
                 if (ms == -INFINITY) continue;
                 const float f = exp2f(ms - M);
@@ -472,8 +682,8 @@ bool use_fast_path(dk_dtype dt, int D, int G, int T, int chunk, dk_strides ks, d
 
 }  // namespace
 
-AttnPlan plan_attn(int B, int Hkv, int T, int Hq, int dv, int N, int chunk) {
-    AttnPlan p{1, 0};
+AttnPlan plan_attn(int B, int Hkv, int T, int Hq, int dv, int N, int chunk, bool tail) {
+    AttnPlan p{1, 1, 0};
     const int64_t bg = (int64_t)B * Hkv;
     const int R = (Hq / Hkv) * T;
     const int64_t tiles = (int64_t)N * ((chunk + 31) / 32);
@@ -488,39 +698,82 @@ AttnPlan plan_attn(int B, int Hkv, int T, int Hq, int dv, int N, int chunk) {
     if (s > 64 && min_s <= 64) s = 64;
     if (s < 1) s = 1;
     p.splits = (int)s;
-    p.ws_bytes = s > 1 ? (size_t)(bg * s * R) * (size_t)(dv + 2) * 4 : 0;
+    p.nparts = (int)s + (tail ? 1 : 0);
+    p.ws_bytes = p.nparts > 1 ? (size_t)(bg * p.nparts * R) * (size_t)(dv + 2) * 4 : 0;
     return p;
+}
+
+// kernel selection by K/V type, head size and query rows per wave (R <= 16)
+struct GenericKernel {
+    template <typename KVT, int D, int XR>
+    static void launch(dim3 grid, hipStream_t st, const AttnArgs& a) {
+        hipLaunchKernelGGL((k_attn_generic<KVT, D, XR>), grid, dim3(kThreads), 0, st, a);
+    }
+};
+struct TailKernel {
+    template <typename KVT, int D, int XR>
+    static void launch(dim3 grid, hipStream_t st, const AttnArgs& a) {
+        hipLaunchKernelGGL((k_attn_tail<KVT, D, XR>), grid, dim3(kThreads), 0, st, a);
+    }
+};
+template <typename K, typename KVT, int D>
+void launch_xr(int R, dim3 grid, hipStream_t st, const AttnArgs& a) {
+    switch ((R + 3) / 4) {
+        case 1: K::template launch<KVT, D, 1>(grid, st, a); break;
+        case 2: K::template launch<KVT, D, 2>(grid, st, a); break;
+        case 3: K::template launch<KVT, D, 3>(grid, st, a); break;
+        default: K::template launch<KVT, D, 4>(grid, st, a); break;
+    }
+}
+template <typename K>
+void launch_rows(dk_dtype dt, int D, int R, dim3 grid, hipStream_t st, const AttnArgs& a) {
+    if (dt == DK_BF16) {
+        if (D == 128) launch_xr<K, uint16_t, 128>(R, grid, st, a);
+        else launch_xr<K, uint16_t, 64>(R, grid, st, a);
+    } else {
+        if (D == 128) launch_xr<K, float, 128>(R, grid, st, a);
+        else launch_xr<K, float, 64>(R, grid, st, a);
+    }
 }
 
 hipError_t launch_attention(const float* q, int B, int T, int Hq, int Hkv, const void* K,
                             const void* V, dk_dtype dt, dk_strides ks, dk_strides vs, int D,
                             int chunk, const int32_t* block_ids, const uint8_t* member,
                             const int32_t* count, int N, int pool_blocks, float scale, float* out,
-                            float* lse, void* ws, const AttnPlan& plan, hipStream_t st) {
-    AttnArgs a;
+                            float* lse, void* ws, const AttnPlan& plan, const AttnTail* tail,
+                            hipStream_t st) {
+    AttnArgs a{};
     a.q = q; a.Hq = Hq; a.Hkv = Hkv; a.T = T; a.G = Hq / Hkv;
     a.K = K; a.V = V; a.ks = ks; a.vs = vs; a.chunk = chunk;
     a.block_ids = block_ids; a.member = member; a.count = count;
     a.N = N; a.pool_blocks = pool_blocks;
     a.scale_log2 = scale * kLog2e;
     a.splits = plan.splits;
+    a.nparts = plan.nparts;
     a.out = out; a.lse = lse;
     const int64_t bg = (int64_t)B * Hkv;
     const int R = a.G * T;
-    a.part_acc = plan.splits > 1 ? (float*)ws : nullptr;
-    a.part_ml = plan.splits > 1 ? (float*)ws + bg * plan.splits * R * D : nullptr;
+    a.part_acc = plan.nparts > 1 ? (float*)ws : nullptr;
+    a.part_ml = plan.nparts > 1 ? (float*)ws + bg * plan.nparts * R * D : nullptr;
+    if (tail) {
+        a.Kt = tail->K_tail; a.Vt = tail->V_tail; a.kts = tail->kts; a.vts = tail->vts;
+        a.tail_len = tail->tail_len; a.tail_max = tail->tail_max;
+        a.Kn = tail->K_new; a.Vn = tail->V_new;
+    }
     const unsigned grid = (unsigned)(bg * plan.splits);
     if (use_fast_path(dt, D, a.G, T, chunk, ks, vs)) {
         hipLaunchKernelGGL(k_attn_bf16_d128_g4t2, dim3(grid), dim3(kThreads), 0, st, a);
-    } else if (dt == DK_BF16) {
-        if (D == 128) hipLaunchKernelGGL((k_attn_generic<uint16_t, 128>), dim3(grid), dim3(kThreads), 0, st, a);
-        else hipLaunchKernelGGL((k_attn_generic<uint16_t, 64>), dim3(grid), dim3(kThreads), 0, st, a);
     } else {
-        if (D == 128) hipLaunchKernelGGL((k_attn_generic<float, 128>), dim3(grid), dim3(kThreads), 0, st, a);
-        else hipLaunchKernelGGL((k_attn_generic<float, 64>), dim3(grid), dim3(kThreads), 0, st, a);
+        launch_rows<GenericKernel>(dt, D, R, dim3(grid), st, a);
     }
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || plan.splits == 1) return e;
+    if (e != hipSuccess) return e;
+    if (tail) {
+        launch_rows<TailKernel>(dt, D, R, dim3((unsigned)bg), st, a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (plan.nparts == 1) return hipSuccess;
     if (D == 128) hipLaunchKernelGGL(k_attn_merge<128>, dim3((unsigned)bg), dim3(kThreads), 0, st, a);
     else hipLaunchKernelGGL(k_attn_merge<64>, dim3((unsigned)bg), dim3(kThreads), 0, st, a);
     return hipGetLastError();

@@ -27,14 +27,14 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(lib, n), n
     assert {n for n, _, _ in b.EXPORTS} == set(names)
 
 
 def test_abi_version():
-    assert lib.dk_abi_version() == 4
+    assert lib.dk_abi_version() == 5
 
 
 def err():
@@ -195,6 +195,45 @@ def test_gather_host_kinds_need_pinned_host_memory(host):
     # or launch (with or without a GPU present).
     assert gather(host=host) == 1
     assert "pinned host memory" in err()
+
+
+def attn_tail(extra=None, **kw):
+    a = dict(q=FAKE, B=2, T=2, Hq=32, Hkv=8, K=FAKE, V=FAKE, dt=1, ks=b.dk_strides(1 << 22, 1 << 19, 128),
+             vs=b.dk_strides(1 << 22, 1 << 19, 128), dk=128, dv=128, chunk=32, ids=FAKE, mem=FAKE, cnt=FAKE,
+             N=128, pb=4096, scale=0.088, out=FAKE, lse=FAKE, ws=FAKE, wsb=16)
+    a.update(kw)
+    ex = ctypes.byref(extra) if extra is not None else None
+    return lib.dk_sparse_decode_attn_tail(a["q"], a["B"], a["T"], a["Hq"], a["Hkv"], a["K"], a["V"], a["dt"],
+                                          a["ks"], a["vs"], a["dk"], a["dv"], a["chunk"], a["ids"], a["mem"],
+                                          a["cnt"], a["N"], a["pb"], ex, a["scale"], a["out"], a["lse"], a["ws"],
+                                          a["wsb"], None)
+
+
+def extra(Kt=FAKE, Vt=FAKE, tmax=8, Kn=FAKE, Vn=FAKE, ts=b.dk_strides(8192, 1024, 128)):
+    return b.dk_attn_extra(Kt, Vt, ts, ts, 0, tmax, Kn, Vn)
+
+
+@pytest.mark.parametrize("kw,ex,status", [
+    (dict(), None, 1),                               # no extra
+    (dict(), extra(Vt=NULL), 1),                     # half a tail
+    (dict(), extra(Vn=NULL), 1),                     # half the new rows
+    (dict(), extra(tmax=-1), 1),
+    (dict(dk=96, dv=96), extra(), 2),
+    (dict(), extra(Kt=MIS), 2),
+    (dict(), extra(ts=b.dk_strides(8192, 1024, 100)), 2),
+    (dict(), extra(), 1),                            # the (16-byte) workspace is too small
+])
+def test_attention_tail_rejects(kw, ex, status):
+    # every case fails its checks, so nothing is launched
+    assert attn_tail(ex, **kw) == status, err()
+    assert err().startswith("dk_sparse_decode_attn_tail")
+
+
+def test_attention_tail_workspace_size():
+    # one more partial slot than the ranges: 3 ranges + the tail
+    assert lib.dk_attn_tail_workspace_size(64, 8, 2, 32, 128, 128, 32) == 64 * 8 * 4 * 8 * 130 * 4
+    # a single range still needs partials once a tail is attended
+    assert lib.dk_attn_tail_workspace_size(1, 1, 2, 4, 128, 4, 32) == 1 * 1 * 2 * 8 * 130 * 4
 
 
 def test_attention_workspace_sizes():

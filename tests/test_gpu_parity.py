@@ -392,6 +392,47 @@ def test_attention_workspace_reuse(dkb):
         assert max_abs(out.cpu().numpy(), ro_) <= tol and max_abs(lse.cpu().numpy(), rl_) <= tol, (i, w.name)
 
 
+@pytest.mark.parametrize("name,B,L,kw,tail_max,lens,fresh", [
+    ("llama8b_l32k", 3, 8192, {}, 40, [0, 17, 40], True),      # fast path + tail + fresh rows
+    ("llama8b_l32k", 2, 4096, {}, 33, None, False),            # tail only, every request full
+    ("llama8b_l32k", 2, 4096, {}, 0, None, True),              # the step's own rows only
+    ("llama8b_l32k", 2, 4096, dict(T=1), 9, [3, 9], True),     # one query: its own row
+    ("tiny", 2, None, {}, 70, [65, 0], True),                  # fp32 generic kernel, more rows than a wave
+])
+def test_attention_tail(dkb, name, B, L, kw, tail_max, lens, fresh):
+    w = workload(name, B, L, **kw)
+    q, K, V = make(w, 31)
+    gen = torch.Generator().manual_seed(31)
+    dt = synth.kv_torch_dtype(w)
+    Kt = Vt = Kn = Vn = tl = None
+    if tail_max:
+        Kt = torch.randn(w.B, w.Hkv, tail_max, w.d, generator=gen).to(dt)
+        Vt = torch.randn(w.B, w.Hkv, tail_max, w.d, generator=gen).to(dt)
+    if fresh:
+        Kn = torch.randn(w.B, w.T, w.Hkv, w.d, generator=gen).to(dt)
+        Vn = torch.randn(w.B, w.T, w.Hkv, w.d, generator=gen).to(dt)
+    if lens is not None:
+        tl = torch.tensor(lens, dtype=torch.int32)
+    qh = q.cpu().numpy().astype(np.float64)
+    Kh, Vh = synth.to_numpy_f64(K), synth.to_numpy_f64(V)
+    _, _, sel = oracle_selection(w, qh, Kh)
+    ru, rm, rc, _ = O.union_select(sel)
+    cuda = lambda x: None if x is None else x.cuda()
+    out, lse = dkb.sparse_decode_attn_tail(q, K, V, to_dev(ru), to_dev(rm, torch.uint8), to_dev(rc), w.chunk,
+                                           w.scale, K_tail=cuda(Kt), V_tail=cuda(Vt), tail_len=cuda(tl),
+                                           K_new=cuda(Kn), V_new=cuda(Vn))
+    torch.cuda.synchronize()
+    f64 = lambda x: None if x is None else synth.to_numpy_f64(x)
+    tl_ref = None if Kt is None else (np.array(lens) if lens is not None else np.full(w.B, tail_max))
+    ro_, rl_ = O.sparse_attention_tail(qh, Kh, Vh, sel, w.chunk, w.scale, f64(Kt), f64(Vt), tl_ref, f64(Kn),
+                                       f64(Vn))
+    tol = ATOL[w.kv_dtype]
+    e_out = max_abs(out.cpu().numpy(), ro_)
+    e_lse = max_abs(lse.cpu().numpy(), rl_)
+    print(f"max|out err| {e_out:.3e}  max|lse err| {e_lse:.3e}  (tol {tol})")
+    assert e_out <= tol and e_lse <= tol
+
+
 def test_attention_ragged_and_empty(dkb):
     def mutate(ru, rm, rc, lists, w):
         # (0, 0): empty; (0, 1): one chunk, real query only; (1, 2): out-of-range id skipped
