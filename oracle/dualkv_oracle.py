@@ -40,6 +40,18 @@ Readings where the pages are silent:
 * every query attends over the pool rows of its own chunk set only; there is no
   tail of fresh rows and L must be a multiple of the chunk size.
 
+Token-level selection over a latent KV head (Adaptive DHiSparse, Figure 2: an
+indexer reads its index state and emits the top-k token positions, and
+attention reads the selected rows; Table 3: 2,048 selections per selecting
+layer) is the same step with chunk = 1: the indexer keys are their own
+landmarks, and one latent head serves every query head.  Readings for it:
+* a token's index score is the mean over the indexer heads of the scaled dot
+  products of the indexer query with the token's indexer key (the same rule as
+  the chunk score);
+* attention uses the whole latent row (content part and position part) as the
+  key, the first dv columns of the same row as the value, and the scale the
+  caller passes (1/sqrt of the key width in the workloads).
+
 Parity of each function is pinned by the not-gpu tests (closed forms, brute
 force on tiny inputs, a library attention routine, hand-worked fixtures under
 tests/golden/).  The absolute prediction-accuracy level on synthetic data has
@@ -348,3 +360,42 @@ def decode_step(q, K, V, chunk: int, k: int, scale: float | None = None,
     out, lse = sparse_attention(q, K, V, sel, chunk, scale)
     return dict(lm=lm, scores=s, topk=sel, union_ids=union_ids, member=member, count=count,
                 overlap=overlap, accuracy=prediction_accuracy(overlap, k), out=out, lse=lse)
+
+
+# ----------------------------------------------------------------------------
+# token-level selection over one latent KV head
+# ----------------------------------------------------------------------------
+
+def indexer_topk(qi: np.ndarray, Kidx: np.ndarray, k: int, scale: float) -> np.ndarray:
+    """Top-k token positions of every query from the indexer.
+
+    Adaptive DHiSparse, Figure 2: the indexer turns the index state into the top-k
+    positions the step reads.  qi: [B, T, Hi, di] indexer queries; Kidx: [B, 1, L, di]
+    indexer keys, one per token.  A token's score is the mean over the Hi indexer
+    heads of scale * <qi[b, t, h], Kidx[b, 0, n]> (chunk_scores with the keys as
+    their own landmarks); the k best tokens, ties to the lower position, are
+    returned ascending.  Returns [B, 1, T, k].
+    """
+    return topk_chunks(chunk_scores(qi, Kidx, scale, "mean"), k)
+
+
+def mla_attention(q: np.ndarray, latent: np.ndarray, sel: np.ndarray, dv: int, scale: float):
+    """Attention of every query head over its own selected latent rows.
+
+    q: [B, T, Hq, dk] with dk the latent width (content + position parts);
+    latent: [B, 1, L, dk], one latent row per token shared by every query head;
+    sel: [B, 1, T, k] token positions of each query.  The key is the whole latent
+    row and the value its first dv columns; otherwise this is sparse_attention
+    with chunk = 1.  Returns out [B, T, Hq, dv] and lse [B, T, Hq].
+    """
+    latent = np.asarray(latent, dtype=np.float64)
+    return sparse_attention(q, latent, latent[..., :dv], sel, 1, scale)
+
+
+def mla_decode_step(qi, Kidx, q, latent, k: int, dv: int, index_scale: float, scale: float):
+    """Indexer top-k -> union -> latent attention for one layer of token-level selection."""
+    sel = indexer_topk(qi, Kidx, k, index_scale)
+    union_ids, member, count, overlap = union_select(sel)
+    out, lse = mla_attention(q, latent, sel, dv, scale)
+    return dict(topk=sel, union_ids=union_ids, member=member, count=count, overlap=overlap,
+                accuracy=prediction_accuracy(overlap, k), out=out, lse=lse)

@@ -17,6 +17,9 @@ Recipe (one layer):
   KV head's query group (layer 0, step 0) and alpha = 4 * sqrt(d), about four
   times the norm of an N(0, 1) key.
 * Host-pool query dynamics: q_real(step + 1) = q_spec(step) + 0.05 * N(0, 1).
+* Token-level latent workloads: indexer keys and latent rows ~ N(0, 1) in
+  bf16 (no heavy hitters); indexer queries and attention queries follow the
+  real / speculative rule above.
 
 Sub-streams are keyed by (seed, purpose, index) so that any slice can be
 regenerated on its own.  Values differ between devices (torch's CPU and GPU
@@ -29,7 +32,7 @@ import math
 
 import torch
 
-from .workloads import Workload
+from .workloads import MlaWorkload, Workload
 
 
 def sub_seed(base: int, *tags) -> int:
@@ -144,3 +147,36 @@ def to_numpy_f64(x: torch.Tensor):
         bits = x.view(torch.int16).numpy().view(np.uint16)
         return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     return x.numpy().astype(np.float64)
+
+
+def _real_spec(shape, seed: int, tag: str, layer: int, device, sigma: float) -> torch.Tensor:
+    """[B, 2, ...] fp32 holding bf16 values: t=0 real ~ N(0, 1), t=1 real + sigma * N(0, 1)."""
+    real = torch.randn(shape, generator=_gen(device, sub_seed(seed, tag + "_real", layer)), device=device)
+    noise = torch.randn(shape, generator=_gen(device, sub_seed(seed, tag + "_spec", layer)), device=device)
+    return torch.stack([round_bf16(real), round_bf16(real + sigma * noise)], dim=1)
+
+
+def make_mla_queries(w: MlaWorkload, seed: int, layer: int = 0, device="cpu"):
+    """Indexer queries qi [B, T, Hi, di] and attention queries q [B, T, Hq, dk], fp32 bf16 values."""
+    qi = _real_spec((w.B, w.Hi, w.di), seed, "qi", layer, device, w.sigma_spec)[:, : w.T]
+    q = _real_spec((w.B, w.Hq, w.dk), seed, "qa", layer, device, w.sigma_spec)[:, : w.T]
+    return qi.contiguous(), q.contiguous()
+
+
+def fill_mla_slice(w: MlaWorkload, seed: int, b: int, device):
+    """Indexer keys [L, di] and latent rows [L, dk] of request b, fp32 values before the bf16 cast."""
+    Kidx = torch.randn(w.L, w.di, generator=_gen(device, sub_seed(seed, "Kidx", b)), device=device)
+    lat = torch.randn(w.L, w.dk, generator=_gen(device, sub_seed(seed, "latent", b)), device=device)
+    return Kidx, lat
+
+
+def make_mla_pools(w: MlaWorkload, seed: int, device="cpu"):
+    """Indexer keys [B, 1, L, di] and latent cache [B, 1, L, dk], both bf16."""
+    Kidx = torch.empty((w.B, 1, w.L, w.di), dtype=torch.bfloat16, device=device)
+    lat = torch.empty((w.B, 1, w.L, w.dk), dtype=torch.bfloat16, device=device)
+    for b in range(w.B):
+        kb, lb = fill_mla_slice(w, seed, b, device)
+        Kidx[b, 0].copy_(kb.to(torch.bfloat16))
+        lat[b, 0].copy_(lb.to(torch.bfloat16))
+        del kb, lb
+    return Kidx, lat

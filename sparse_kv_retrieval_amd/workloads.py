@@ -99,6 +99,75 @@ WORKLOADS = {
 }
 
 
+@dataclass(frozen=True)
+class MlaWorkload:
+    """Token-level selection over one latent KV head (multi-head latent attention).
+
+    Adaptive DHiSparse, Figure 2 and Table 3: an indexer picks k token positions
+    per query (2,048 per selecting layer for the GLM model on the pages), and
+    attention reads those rows of a latent cache shared by every query head.
+    Each token has an indexer key of width di and a latent row of width
+    dk = d_c + d_r (content part, position part); the value is the first
+    dv = d_c columns of the latent row.  Hq attention heads and Hi indexer heads
+    per query token, T query tokens per request.
+    """
+    name: str
+    B: int
+    L: int
+    k: int
+    Hq: int = 128
+    d_c: int = 512
+    d_r: int = 64
+    Hi: int = 4
+    di: int = 128
+    T: int = 2
+    layers: int = 1
+    sigma_spec: float = 0.1
+    description: str = ""
+
+    @property
+    def dk(self) -> int:
+        return self.d_c + self.d_r
+
+    @property
+    def dv(self) -> int:
+        return self.d_c
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.dk)
+
+    @property
+    def index_scale(self) -> float:
+        return 1.0 / math.sqrt(self.di)
+
+    def index_key_bytes(self) -> int:
+        """bf16 indexer keys read by one scoring pass: B * L * di * 2."""
+        return self.B * self.L * self.di * 2
+
+    def latent_row_bytes(self) -> int:
+        return self.dk * 2
+
+    def with_(self, **kw) -> "MlaWorkload":
+        return replace(self, **kw)
+
+
+MLA_WORKLOADS = {
+    # The full shape: 32 requests at 128K context, 2,048 tokens per query.
+    "mla_b32_l128k": MlaWorkload(
+        name="mla_b32_l128k", B=32, L=131072, k=2048,
+        description="B=32 Hq=128 on one latent head (dk 576 = 512 + 64, dv 512), L=131072, "
+                    "indexer 4 heads x 128 (bf16 keys), token top-k=2048, T=2"),
+    # Test sizes with the same head layout.
+    "mla_b2_l16k": MlaWorkload(
+        name="mla_b2_l16k", B=2, L=16384, k=512,
+        description="B=2 Hq=128 latent dk 576 / dv 512, L=16384, indexer 4 x 128, top-k=512, T=2"),
+    "mla_b1_l2k": MlaWorkload(
+        name="mla_b1_l2k", B=1, L=2048, k=96,
+        description="B=1 Hq=128 latent dk 576 / dv 512, L=2048, indexer 4 x 128, top-k=96, T=2"),
+}
+
+
 def shrink(w: Workload, B: int | None = None, L: int | None = None,
            layers: int | None = None) -> Workload:
     """Same head layout and budget, fewer requests / shorter context (test sizes)."""

@@ -506,7 +506,119 @@ def _tail_ignores_tail_len(q, K, V, sel, chunk, scale, K_tail=None, V_tail=None,
     return O.sparse_attention_tail(q, K, V, sel, chunk, scale, K_tail, V_tail, full, K_new, V_new)
 
 
+# ----------------------------------------------------------------------------
+# token-level selection over one latent KV head (indexer top-k, latent attention)
+# ----------------------------------------------------------------------------
+
+def check_indexer(fn):
+    fx = golden("mla_token_hand.json")
+    sel = fn(np.array(fx["qi"], dtype=np.float64), np.array(fx["Kidx"], dtype=np.float64), fx["k"],
+             fx["index_scale"])
+    np.testing.assert_array_equal(sel, fx["expected_topk"])
+    ui, mb, ct, ov = O.union_select(sel)
+    np.testing.assert_array_equal(ui, fx["expected_union_ids"])
+    np.testing.assert_array_equal(mb, fx["expected_member"])
+    np.testing.assert_array_equal(ct, fx["expected_count"])
+    np.testing.assert_array_equal(ov, fx["expected_overlap"])
+
+    rng = np.random.default_rng(11)
+    B, T, Hi, di, L, k = 2, 2, 4, 8, 40, 6
+    qi = rng.standard_normal((B, T, Hi, di))
+    Kidx = rng.standard_normal((B, 1, L, di))
+    sel = fn(qi, Kidx, k, 0.3)
+    # linearity: the mean over heads of the scaled dots is the scaled dot with the
+    # mean query, so the selection is the top-k of that single product (distinct scores)
+    for b, t in itertools.product(range(B), range(T)):
+        sc = 0.3 * (Kidx[b, 0] @ qi[b, t].mean(axis=0))
+        assert len(set(np.round(sc, 9))) == L
+        np.testing.assert_array_equal(sel[b, 0, t], np.sort(np.argsort(-sc)[:k]))
+    # one-hot keys and one indexer head: the score of token n is scale * q[n % di], so the
+    # k best tokens are the positions of the k largest query components (lowest
+    # position first among the copies of a component)
+    qi1 = rng.standard_normal((1, 1, 1, di))
+    K1 = np.zeros((1, 1, 2 * di, di))
+    for n in range(2 * di):
+        K1[0, 0, n, n % di] = 1.0
+    sel = fn(qi1, K1, 3, 0.5)
+    top = np.argsort(-qi1[0, 0, 0])[:2]
+    expect = sorted([int(top[0]), int(top[0]) + di, int(top[1])])
+    np.testing.assert_array_equal(sel[0, 0, 0], expect)
+
+
+def test_indexer_pins():
+    check_indexer(O.indexer_topk)
+
+
+def check_mla(fn):
+    fx = golden("mla_token_hand.json")
+    out, lse = fn(np.array(fx["q"]), np.array(fx["latent"], dtype=np.float64),
+                  np.array(fx["expected_topk"]), fx["dv"], fx["scale"])
+    np.testing.assert_allclose(out, fx["expected_out"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, fx["expected_lse"], rtol=0, atol=1e-12)
+
+    rng = np.random.default_rng(12)
+    B, T, Hq, dk, dv, L = 2, 2, 5, 9, 6, 12
+    q = rng.standard_normal((B, T, Hq, dk))
+    lat = rng.standard_normal((B, 1, L, dk))
+    # every token selected: dense attention with the value aliasing the key's first dv
+    # columns (library routine, fp64)
+    sel_all = np.broadcast_to(np.arange(L), (B, 1, T, L))
+    out, lse = fn(q, lat, sel_all, dv, 0.25)
+    for b, t, h in itertools.product(range(B), range(T), range(Hq)):
+        Kb = lat[b, 0]
+        ref = sdpa_masked(q[b, t, h], Kb, np.ascontiguousarray(Kb[:, :dv]), np.ones(L, dtype=bool), 0.25)
+        np.testing.assert_allclose(out[b, t, h], ref, rtol=0, atol=1e-12)
+    # own token sets: masked library attention
+    sel = np.zeros((B, 1, T, 4), dtype=np.int64)
+    for b, t in itertools.product(range(B), range(T)):
+        sel[b, 0, t] = np.sort(rng.choice(L, 4, replace=False))
+    out, lse = fn(q, lat, sel, dv, 0.25)
+    for b, t, h in itertools.product(range(B), range(T), range(Hq)):
+        mask = np.zeros(L, dtype=bool)
+        mask[sel[b, 0, t]] = True
+        Kb = lat[b, 0]
+        ref = sdpa_masked(q[b, t, h], Kb, np.ascontiguousarray(Kb[:, :dv]), mask, 0.25)
+        np.testing.assert_allclose(out[b, t, h], ref, rtol=0, atol=1e-12)
+
+
+def test_mla_pins():
+    check_mla(O.mla_attention)
+
+
+def test_mla_decode_step_composes():
+    fx = golden("mla_token_hand.json")
+    r = O.mla_decode_step(np.array(fx["qi"], dtype=np.float64), np.array(fx["Kidx"], dtype=np.float64),
+                          np.array(fx["q"]), np.array(fx["latent"], dtype=np.float64), fx["k"], fx["dv"],
+                          fx["index_scale"], fx["scale"])
+    np.testing.assert_array_equal(r["topk"], fx["expected_topk"])
+    np.testing.assert_allclose(r["out"], fx["expected_out"], atol=1e-12)
+    assert r["accuracy"] == 0.5
+
+
+def _indexer_max_over_heads(qi, Kidx, k, scale):
+    return O.topk_chunks(O.chunk_scores(qi, Kidx, scale, "max"), k)
+
+
+def _indexer_first_head_only(qi, Kidx, k, scale):
+    return O.topk_chunks(O.chunk_scores(qi[:, :, :1], Kidx, scale, "mean"), k)
+
+
+def _mla_value_from_last_columns(q, latent, sel, dv, scale):
+    latent = np.asarray(latent, dtype=np.float64)
+    return O.sparse_attention(q, latent, latent[..., -dv:], sel, 1, scale)
+
+
+def _mla_key_content_only(q, latent, sel, dv, scale):
+    latent = np.asarray(latent, dtype=np.float64)
+    q = np.asarray(q, dtype=np.float64)
+    return O.sparse_attention(q[..., :dv], latent[..., :dv], latent[..., :dv], sel, 1, scale)
+
+
 @pytest.mark.parametrize("check,bad", [
+    (check_indexer, _indexer_max_over_heads),
+    (check_indexer, _indexer_first_head_only),
+    (check_mla, _mla_value_from_last_columns),
+    (check_mla, _mla_key_content_only),
     (check_attention_tail, _tail_no_causal_mask),
     (check_attention_tail, _tail_ignores_tail_len),
     (check_landmarks, _landmarks_off_by_one),

@@ -55,3 +55,22 @@ def test_bf16_to_f64_is_exact():
     x = torch.randn(1000).to(torch.bfloat16)
     a = synth.to_numpy_f64(x)
     assert (a == x.float().numpy().astype("float64")).all()
+
+
+def test_mla_inputs_shapes_values_and_slices():
+    from sparse_kv_retrieval_amd.workloads import MLA_WORKLOADS
+    w = MLA_WORKLOADS["mla_b1_l2k"].with_(B=2, L=256)
+    qi, q = synth.make_mla_queries(w, 3)
+    assert qi.shape == (2, 2, w.Hi, w.di) and q.shape == (2, 2, w.Hq, w.dk)
+    for x in (qi, q):
+        assert x.dtype == torch.float32
+        assert torch.equal(x, x.to(torch.bfloat16).to(torch.float32))      # bf16 values
+    # the speculative query is the real one plus a small perturbation
+    d = (q[:, 1] - q[:, 0]).std().item()
+    assert 0.05 < d < 0.2
+    Kidx, lat = synth.make_mla_pools(w, 3)
+    assert Kidx.shape == (2, 1, w.L, w.di) and lat.shape == (2, 1, w.L, w.dk)
+    assert Kidx.dtype == torch.bfloat16 and lat.dtype == torch.bfloat16
+    kb, lb = synth.fill_mla_slice(w, 3, 1, "cpu")
+    assert torch.equal(Kidx[1, 0], kb.to(torch.bfloat16)) and torch.equal(lat[1, 0], lb.to(torch.bfloat16))
+    assert abs(lat.float().std().item() - 1.0) < 0.05
