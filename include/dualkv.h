@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define DK_ABI_VERSION 5
+#define DK_ABI_VERSION 6
 
 typedef enum {
     DK_OK = 0,
@@ -136,23 +136,37 @@ dk_status dk_build_landmark_shadow(const float* lm, dk_strides ls, int B, int Hk
  *   topk_idx[b, g, t, :] = the k chunk ids with the largest s, ties to the lower
  *                          id, written in ascending id order.
  *
+ * Token-level selection (Adaptive DHiSparse, Figure 2: an indexer emits the
+ * top-k token positions of the step; Table 3: 2,048 per selecting layer) is
+ * the same call with lm_dtype = DK_BF16: lm then holds one bf16 indexer key
+ * per token, "chunk" means token (C = tokens), q holds the indexer queries
+ * (Hq indexer heads over Hkv key heads) and the scores are exact fp32 dot
+ * products with the keys.
+ *
  * q          : fp32 [B, T, Hq, d] contiguous; query head h belongs to KV head h / (Hq/Hkv).
- * lm         : landmarks, lm_dtype (v1: DK_F32), rows [B, Hkv, C] of d, strides ls.
+ * lm         : DK_F32 landmarks, or DK_BF16 per-token indexer keys; rows [B, Hkv, C]
+ *              of d, strides ls (elements).
  * reduce     : DK_REDUCE_MEAN (mean over the group's heads) or DK_REDUCE_MAX.
  * shadow     : the landmarks' shadow (see above) or NULL.  With a shadow the
  *              result is the same; the call reads about half the bytes.
  * topk_idx   : out, int32 [B, Hkv, T, k].
  * topk_score : out, fp32 [B, Hkv, T, k] (the selected scores, same order) or NULL.
  * ws         : workspace of dk_score_topk_workspace_size(B, Hkv, T, C, k,
- *              shadow != NULL) bytes (may be NULL when that size is 0).
- *              Contents on entry are ignored.
+ *              shadow != NULL) bytes for DK_F32 landmarks, of
+ *              dk_index_topk_workspace_size(B, Hkv, T, C) bytes for DK_BF16 keys
+ *              (may be NULL when that size is 0).  Contents on entry are ignored.
  * Errors     : DK_ERR_INVALID_ARG unless 1 <= T <= 2, Hq % Hkv == 0, 1 <= k <= C,
  *              pointers non-NULL and ws_bytes large enough; DK_ERR_UNSUPPORTED
- *              unless lm_dtype == DK_F32, d is 64 or 128, C <= 65536 (C <= 6144
- *              with a shadow), the number of query vectors (T for mean, G*T for
- *              max) is at most 16 and the 16-byte alignment rule holds.
+ *              unless d is 64 or 128 and the 16-byte alignment rule holds, and,
+ *              for DK_F32, C <= 65536 (C <= 6144 with a shadow) and the number
+ *              of query vectors (T for mean, G*T for max) is at most 16; for
+ *              DK_BF16, reduce is DK_REDUCE_MEAN, shadow is NULL, C % 4 == 0 and
+ *              C <= 2^28.
  */
 size_t dk_score_topk_workspace_size(int B, int Hkv, int T, int C, int k, int with_shadow);
+/* Workspace bytes of dk_score_topk / dk_score_topk_union with DK_BF16 indexer
+ * keys: the fp32 scores of every token (B*Hkv*T*C*4) plus per-block ranges. */
+size_t dk_index_topk_workspace_size(int B, int Hkv, int T, int C);
 dk_status dk_score_topk(const float* q, int B, int T, int Hq,
                         const void* lm, dk_dtype lm_dtype, dk_strides ls, int Hkv, int C, int d,
                         int k, float scale, dk_group_reduce reduce,
@@ -173,8 +187,8 @@ dk_status dk_score_topk(const float* q, int B, int T, int Hq,
  *
  * Arguments: as dk_score_topk, plus the union outputs of dk_union_select
  * (union_ids int32 [B, Hkv, T*k], member uint8 [B, Hkv, T*k], union_count
- * int32 [B, Hkv], overlap int32 [B, Hkv] or NULL).  ws: the same
- * dk_score_topk_workspace_size bytes; contents on entry are ignored.
+ * int32 [B, Hkv], overlap int32 [B, Hkv] or NULL).  ws: the same workspace as
+ * dk_score_topk; contents on entry are ignored.
  * Errors: those of dk_score_topk; DK_ERR_INVALID_ARG if a union output other
  * than overlap is NULL; DK_ERR_UNSUPPORTED beyond dk_union_select's limits.
  */

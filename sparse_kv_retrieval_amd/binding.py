@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libdualkv.so")
 DK_OK, DK_ERR_INVALID_ARG, DK_ERR_UNSUPPORTED, DK_ERR_HIP = 0, 1, 2, 3
 DK_F32, DK_BF16 = 0, 1
 DK_REDUCE_MEAN, DK_REDUCE_MAX = 0, 1
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 _STATUS = {0: "DK_OK", 1: "DK_ERR_INVALID_ARG", 2: "DK_ERR_UNSUPPORTED", 3: "DK_ERR_HIP"}
 
@@ -61,6 +61,7 @@ EXPORTS = [
     ("dk_build_landmarks", _I, [_P, _I, _S, _I, _I, _I, _I, _I, _P, _P]),
     ("dk_build_landmark_shadow", _I, [_P, _S, _I, _I, _I, _I, _P, _P, _P]),
     ("dk_score_topk_workspace_size", _Z, [_I, _I, _I, _I, _I, _I]),
+    ("dk_index_topk_workspace_size", _Z, [_I, _I, _I, _I]),
     ("dk_score_topk", _I, [_P, _I, _I, _I, _P, _I, _S, _I, _I, _I, _I, _F, _I,
                            ctypes.POINTER(dk_landmark_shadow), _P, _P, _P, _Z, _P]),
     ("dk_score_topk_union", _I, [_P, _I, _I, _I, _P, _I, _S, _I, _I, _I, _I, _F, _I,
@@ -169,6 +170,17 @@ def score_topk_workspace_size(B, Hkv, T, C, k, with_shadow=False) -> int:
     return int(lib.dk_score_topk_workspace_size(B, Hkv, T, C, k, int(bool(with_shadow))))
 
 
+def index_topk_workspace_size(B, Hkv, T, C) -> int:
+    """Workspace of score_topk / score_topk_union with bf16 per-token indexer keys."""
+    return int(lib.dk_index_topk_workspace_size(B, Hkv, T, C))
+
+
+def _topk_ws_bytes(lm, B, Hkv, T, C, k, shadow) -> int:
+    if lm.dtype == torch.bfloat16:
+        return index_topk_workspace_size(B, Hkv, T, C)
+    return score_topk_workspace_size(B, Hkv, T, C, k, shadow is not None)
+
+
 def score_topk(q: torch.Tensor, lm: torch.Tensor, k: int, scale: float, reduce: int = DK_REDUCE_MEAN,
                topk_idx=None, topk_score=None, ws=None, want_scores=True, shadow: Shadow | None = None,
                stream=None):
@@ -179,7 +191,7 @@ def score_topk(q: torch.Tensor, lm: torch.Tensor, k: int, scale: float, reduce: 
         topk_idx = torch.empty(B, Hkv, T, k, dtype=torch.int32, device=q.device)
     if topk_score is None and want_scores:
         topk_score = torch.empty(B, Hkv, T, k, dtype=torch.float32, device=q.device)
-    nbytes = score_topk_workspace_size(B, Hkv, T, C, k, shadow is not None)
+    nbytes = _topk_ws_bytes(lm, B, Hkv, T, C, k, shadow)
     if ws is None and nbytes:
         ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     csh = ctypes.byref(shadow.as_c()) if shadow is not None else None
@@ -212,7 +224,7 @@ def score_topk_union(q: torch.Tensor, lm: torch.Tensor, k: int, scale: float,
         count = torch.empty(B, Hkv, **i32)
     if overlap is None:
         overlap = torch.empty(B, Hkv, **i32)
-    nbytes = score_topk_workspace_size(B, Hkv, T, C, k, shadow is not None)
+    nbytes = _topk_ws_bytes(lm, B, Hkv, T, C, k, shadow)
     if ws is None and nbytes:
         ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     csh = ctypes.byref(shadow.as_c()) if shadow is not None else None

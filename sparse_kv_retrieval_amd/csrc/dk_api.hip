@@ -97,6 +97,11 @@ size_t dk_score_topk_workspace_size(int B, int Hkv, int T, int C, int k, int wit
     return dk::plan_topk(B, Hkv, T, C, k, with_shadow != 0).ws_bytes;
 }
 
+size_t dk_index_topk_workspace_size(int B, int Hkv, int T, int C) {
+    if (B < 1 || Hkv < 1 || T < 1 || T > 2 || C < 1) return 0;
+    return dk::plan_index_topk(B, Hkv, T, C).ws_bytes;
+}
+
 }  // extern "C"
 
 namespace {
@@ -138,6 +143,32 @@ dk_status check_score_topk(const char* fn, const float* q, int B, int T, int Hq,
     return DK_OK;
 }
 
+// Argument checks of the token-level path (DK_BF16 indexer keys).
+dk_status check_index_topk(const char* fn, const float* q, int B, int T, int Hq, const void* lm, dk_strides ls,
+                           int Hkv, int C, int d, int k, float scale, dk_group_reduce reduce,
+                           const dk_landmark_shadow* shadow, int32_t* topk_idx, void* ws, size_t ws_bytes,
+                           dk::IndexPlan* plan_out) {
+    DK_REQUIRE(q && lm && topk_idx, DK_ERR_INVALID_ARG, "%s: q, lm, topk_idx must be non-NULL", fn);
+    DK_REQUIRE(B >= 1 && Hq >= 1 && Hkv >= 1 && C >= 1 && d >= 1, DK_ERR_INVALID_ARG,
+               "%s: B, Hq, Hkv, C, d must be >= 1", fn);
+    DK_REQUIRE(T == 1 || T == 2, DK_ERR_INVALID_ARG, "%s: T must be 1 or 2 (got %d)", fn, T);
+    DK_REQUIRE(Hq % Hkv == 0, DK_ERR_INVALID_ARG, "%s: Hq (%d) %% Hkv (%d) != 0", fn, Hq, Hkv);
+    DK_REQUIRE(k >= 1 && k <= C, DK_ERR_INVALID_ARG, "%s: need 1 <= k (%d) <= C (%d)", fn, k, C);
+    DK_REQUIRE(std::isfinite(scale), DK_ERR_INVALID_ARG, "%s: scale must be finite", fn);
+    DK_REQUIRE(reduce == DK_REDUCE_MEAN, DK_ERR_UNSUPPORTED, "%s: bf16 indexer keys need DK_REDUCE_MEAN", fn);
+    DK_REQUIRE(!shadow, DK_ERR_UNSUPPORTED, "%s: bf16 indexer keys take no shadow", fn);
+    DK_REQUIRE(d == 64 || d == 128, DK_ERR_UNSUPPORTED, "%s: d must be 64 or 128 (got %d)", fn, d);
+    DK_REQUIRE(C % 4 == 0 && C <= (1 << 28), DK_ERR_UNSUPPORTED,
+               "%s: bf16 indexer keys need C %% 4 == 0 and C <= 2^28 (got %d)", fn, C);
+    DK_REQUIRE(aligned16(q) && aligned16(lm) && strides_ok(ls, 2), DK_ERR_UNSUPPORTED,
+               "%s: q, the keys and their strides must be 16-byte aligned", fn);
+    const dk::IndexPlan plan = dk::plan_index_topk(B, Hkv, T, C);
+    DK_REQUIRE(ws && ws_bytes >= plan.ws_bytes, DK_ERR_INVALID_ARG, "%s: workspace needs %zu bytes (got %zu)",
+               fn, plan.ws_bytes, ws_bytes);
+    *plan_out = plan;
+    return DK_OK;
+}
+
 // Limits of the union stage (one block per (b, g), everything in LDS).
 dk_status check_union(const char* fn, int T, int k, int slots, bool with_plan) {
     const int N = T * k;
@@ -156,6 +187,15 @@ dk_status dk_score_topk(const float* q, int B, int T, int Hq, const void* lm, dk
                         dk_group_reduce reduce, const dk_landmark_shadow* shadow, int32_t* topk_idx,
                         float* topk_score, void* ws, size_t ws_bytes, void* stream) {
     g_err.clear();
+    if (lm_dtype == DK_BF16) {
+        dk::IndexPlan ip{};
+        const dk_status s = check_index_topk("dk_score_topk", q, B, T, Hq, lm, ls, Hkv, C, d, k, scale, reduce,
+                                             shadow, topk_idx, ws, ws_bytes, &ip);
+        if (s != DK_OK) return s;
+        hipError_t e = dk::launch_index_topk(q, B, T, Hq, (const uint16_t*)lm, ls, Hkv, C, d, k, scale, topk_idx,
+                                             topk_score, ws, ip, nullptr, (hipStream_t)stream);
+        return e == hipSuccess ? DK_OK : hip_fail(e, "dk_score_topk");
+    }
     dk::TopkPlan plan{};
     const dk_status s = check_score_topk("dk_score_topk", q, B, T, Hq, lm, lm_dtype, ls, Hkv, C, d, k, scale,
                                          reduce, shadow, topk_idx, ws, ws_bytes, &plan);
@@ -173,6 +213,20 @@ dk_status dk_score_topk_union(const float* q, int B, int T, int Hq, const void* 
                               void* stream) {
     g_err.clear();
     const char* fn = "dk_score_topk_union";
+    if (lm_dtype == DK_BF16) {
+        dk::IndexPlan ip{};
+        dk_status s = check_index_topk(fn, q, B, T, Hq, lm, ls, Hkv, C, d, k, scale, reduce, shadow, topk_idx, ws,
+                                       ws_bytes, &ip);
+        if (s != DK_OK) return s;
+        DK_REQUIRE(union_ids && member && union_count, DK_ERR_INVALID_ARG,
+                   "%s: union_ids, member, union_count must be non-NULL", fn);
+        s = check_union(fn, T, k, 0, false);
+        if (s != DK_OK) return s;
+        const dk::UnionOut un{union_ids, member, union_count, overlap};
+        hipError_t e = dk::launch_index_topk(q, B, T, Hq, (const uint16_t*)lm, ls, Hkv, C, d, k, scale, topk_idx,
+                                             topk_score, ws, ip, &un, (hipStream_t)stream);
+        return e == hipSuccess ? DK_OK : hip_fail(e, fn);
+    }
     dk::TopkPlan plan{};
     dk_status s = check_score_topk(fn, q, B, T, Hq, lm, lm_dtype, ls, Hkv, C, d, k, scale, reduce, shadow,
                                    topk_idx, ws, ws_bytes, &plan);

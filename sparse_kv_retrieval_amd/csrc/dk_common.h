@@ -90,9 +90,35 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* to
 // ---------------------------------------------------------------------------
 // Cross-lane helpers.
 // ---------------------------------------------------------------------------
+// sum over the aligned group of LPR (8 or 16) lanes, every lane gets the total
+template <int LPR>
+__device__ __forceinline__ float dpp_group_sum(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+    if constexpr (LPR == 8) {
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+    } else {
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+    }
+    return v;
+}
+
 // value of lane i ^ 1 (DPP quad_perm [1,0,3,2]; a VALU op, no LDS round trip)
 __device__ __forceinline__ float dpp_xor1(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+
+// ---------------------------------------------------------------------------
+// Streamed once: non-temporal 16-byte loads.
+// ---------------------------------------------------------------------------
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4_t nt_load_u4(const void* p) {
+#ifdef DK_SCORE_PLAIN_LOADS
+    return *reinterpret_cast<const u32x4_t*>(p);
+#else
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+#endif
 }
 
 // ---------------------------------------------------------------------------
@@ -156,6 +182,18 @@ hipError_t launch_score_topk(const float* q, int B, int T, int Hq, const float* 
                              int Hkv, int C, int d, int k, float scale, dk_group_reduce reduce,
                              const dk_landmark_shadow* shadow, int32_t* topk_idx, float* topk_score,
                              void* ws, const TopkPlan& plan, const UnionOut* un, hipStream_t st);
+// Token-level indexer on bf16 keys (k_indexer.hip): fp32 scores of every token in
+// the workspace, then an exact threshold select per (b, g, t).
+struct IndexPlan {
+    int blocks_per_bg;   // scoring blocks per (b, g)
+    size_t off_min;      // byte offsets of the per-block score minima / maxima
+    size_t off_max;
+    size_t ws_bytes;
+};
+IndexPlan plan_index_topk(int B, int Hkv, int T, int C);
+hipError_t launch_index_topk(const float* q, int B, int T, int Hq, const uint16_t* keys, dk_strides ks, int Hkv,
+                             int C, int d, int k, float scale, int32_t* topk_idx, float* topk_score, void* ws,
+                             const IndexPlan& plan, const UnionOut* un, hipStream_t st);
 hipError_t launch_build_shadow(const float* lm, dk_strides ls, int B, int Hkv, int C, int d,
                                uint16_t* lm16, float* norm_max, hipStream_t st);
 

@@ -1,0 +1,482 @@
+// Token-level indexer: exact top-k token positions from bf16 indexer keys.
+//
+// Adaptive DHiSparse, Figure 2: an indexer turns its index state into the
+// top-k positions a decode step reads; Table 3: 2,048 positions per selecting
+// layer.  Every token of a (request, KV head) has one indexer key, so the keys
+// are their own landmarks (chunk = 1) and a token's score is the mean over the
+// query heads of the group of the scaled dot products, as for chunk scores.
+// The set is the k best tokens, ties to the lower position, in ascending order.
+//
+// Two kernels:
+//   k_idx_score  : streams the bf16 keys once (non-temporal 16-byte loads, D/8
+//                  lanes per row), writes fp32 scores of every token for each
+//                  query of the request to the workspace, and each block's
+//                  score range.
+//   k_idx_select : one block per (b, g, t).  Finds the threshold pair
+//                  (tau, id_tau), the k-th element in (score descending,
+//                  position ascending) order, then writes every position with
+//                  score > tau, or score == tau and position <= id_tau, in
+//                  ascending order.  The k-th element's bin comes from a
+//                  histogram over 2048 bins linear in the score between the
+//                  row's minimum and maximum (one row's scores cluster; linear
+//                  bins spread them, where the float's exponent bits would not).
+//                  That bin's elements are gathered into LDS and ranked exactly.
+//                  A bin too large to gather falls back to an 11/11/10-bit radix
+//                  select over order-preserving keys inside it, followed by a
+//                  count of the equal keys in position order.
+#include "dk_common.h"
+
+namespace dk {
+namespace {
+
+constexpr int kScoreThreads = 256;
+constexpr int kScoreRows = 1024;   // tokens per scoring block
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kBins = 2048;        // = 2 * kSelThreads
+constexpr int kCap = 2048;         // candidates ranked in LDS
+
+// ---------------------------------------------------------------------------
+// Scores: s[b, g, t, n] = scale * <mean over the group's heads of q[b, t, h], key[b, g, n]>
+// (the mean of the scaled per-head dots, up to fp32 rounding).
+// ---------------------------------------------------------------------------
+template <int D, int T>
+__global__ __launch_bounds__(kScoreThreads) void k_idx_score(const float* __restrict__ q, int Hq,
+                                                            const uint16_t* __restrict__ keys, dk_strides ks,
+                                                            int Hkv, int C, float scale, int blocks_per_bg,
+                                                            float* __restrict__ scores, float* __restrict__ bmin,
+                                                            float* __restrict__ bmax) {
+    constexpr int LPR = D / 8, RPW = kWave / LPR, U = 8, ROWS_PER_ITER = 4 * RPW * U;
+    __shared__ float sres[T][kScoreRows];
+    __shared__ __align__(16) float qs[T][D];
+    __shared__ float red[2][T][kScoreThreads / kWave];
+    const int blk = blockIdx.x % blocks_per_bg;
+    const int bg = blockIdx.x / blocks_per_bg;
+    const int b = bg / Hkv, g = bg - b * Hkv;
+    const int row0 = blk * kScoreRows;
+    const int nrows = min(kScoreRows, C - row0);
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int rp = lane / LPR, part = lane % LPR;
+    const int G = Hq / Hkv;
+
+    // the first rows are requested before the query staging
+    const uint16_t* base = keys + (int64_t)b * ks.b + (int64_t)g * ks.h + (int64_t)row0 * ks.t + part * 8;
+    u32x4_t x[U];
+    auto load_rows = [&](int it) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int r = it + (u * 4 + wave) * RPW + rp;
+            x[u] = r < nrows ? nt_load_u4(base + (int64_t)r * ks.t) : u32x4_t{0u, 0u, 0u, 0u};
+        }
+    };
+    load_rows(0);
+    for (int i = threadIdx.x; i < T * D; i += kScoreThreads) {
+        const int t = i / D, e = i - t * D;
+        float acc = 0.f;
+        for (int h = 0; h < G; ++h) acc += q[(((int64_t)b * T + t) * Hq + g * G + h) * D + e];
+        qs[t][e] = acc / (float)G;
+    }
+    __syncthreads();
+    float qr[T][8];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qr[t][e] = qs[t][part * 8 + e];
+
+    for (int it = 0; it < nrows; it += ROWS_PER_ITER) {
+        if (it) load_rows(it);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int r = it + (u * 4 + wave) * RPW + rp;
+            const uint32_t w[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+            float sc[T];
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                float a = 0.f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    a = fmaf(qr[t][2 * j], bf16_lo(w[j]), a);
+                    a = fmaf(qr[t][2 * j + 1], bf16_hi(w[j]), a);
+                }
+                sc[t] = scale * dpp_group_sum<LPR>(a);
+            }
+            if (part < T && r < nrows) sres[part][r] = part == 0 ? sc[0] : sc[T - 1];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        float* dst = scores + ((int64_t)bg * T + t) * C + row0;
+        float lo = INFINITY, hi = -INFINITY;
+        for (int i = threadIdx.x; i < nrows; i += kScoreThreads) {
+            const float v = sres[t][i];
+            dst[i] = v;
+            lo = fminf(lo, v);
+            hi = fmaxf(hi, v);
+        }
+        for (int off = 1; off < kWave; off <<= 1) {
+            lo = fminf(lo, __shfl_xor(lo, off, kWave));
+            hi = fmaxf(hi, __shfl_xor(hi, off, kWave));
+        }
+        if (lane == 0) {
+            red[0][t][wave] = lo;
+            red[1][t][wave] = hi;
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x < T) {
+        const int t = threadIdx.x;
+        float lo = red[0][t][0], hi = red[1][t][0];
+        for (int w2 = 1; w2 < kScoreThreads / kWave; ++w2) {
+            lo = fminf(lo, red[0][t][w2]);
+            hi = fmaxf(hi, red[1][t][w2]);
+        }
+        bmin[((int64_t)bg * T + t) * blocks_per_bg + blk] = lo;
+        bmax[((int64_t)bg * T + t) * blocks_per_bg + blk] = hi;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Selection
+// ---------------------------------------------------------------------------
+// linear bin of a score: non-decreasing in v, 0 for every v when inv == 0
+__device__ __forceinline__ int bin_of(float v, float lo, float inv) {
+    const float x = (v - lo) * inv;
+    if (!(x > 0.f)) return 0;
+    if (x >= (float)(kBins - 1)) return kBins - 1;
+    return (int)x;
+}
+
+// exclusive scan over the lanes of a wave; *total gets the wave's sum
+__device__ __forceinline__ int wave_excl_scan(int v, int* total) {
+    const int inc = wave_inclusive_scan(v);
+    *total = __shfl(inc, kWave - 1, kWave);
+    return inc - v;
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+    for (int off = 1; off < kWave; off <<= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+// Of the bins hist[0 .. nb) (nb <= 2 * blockDim.x), the one that holds the need-th
+// largest element, counting from the top bin.  Every thread gets the bin, the
+// elements in the bins above it (*above) and in it (*in).
+__device__ __forceinline__ int pick_bin(const int* hist, int nb, int need, int* scratch, int* ish,
+                                        int* above, int* in) {
+    const int tid = threadIdx.x;
+    const int b_hi = nb - 1 - 2 * tid, b_lo = b_hi - 1;
+    const int c_hi = b_hi >= 0 ? hist[b_hi] : 0, c_lo = b_lo >= 0 ? hist[b_lo] : 0;
+    int tot;
+    const int before = block_exclusive_scan(c_hi + c_lo, scratch, &tot);
+    if (before < need && need <= before + c_hi + c_lo) {
+        const bool top = before + c_hi >= need;
+        ish[0] = top ? b_hi : b_lo;
+        ish[1] = top ? before : before + c_hi;
+        ish[2] = top ? c_hi : c_lo;
+    }
+    __syncthreads();
+    *above = ish[1];
+    *in = ish[2];
+    const int r = ish[0];
+    __syncthreads();
+    return r;
+}
+
+__global__ __launch_bounds__(kSelThreads) void k_idx_select(const float* __restrict__ scores,
+                                                           const float* __restrict__ bmin,
+                                                           const float* __restrict__ bmax, int blocks_per_row,
+                                                           int C, int k, int32_t* __restrict__ topk_idx,
+                                                           float* __restrict__ topk_score) {
+    __shared__ int hist[kBins];
+    __shared__ float cval[kCap];
+    __shared__ int cid[kCap];
+    __shared__ int scratch[kSelWaves + 1];
+    __shared__ int wsel[kSelWaves];   // positions each wave's segment contributes
+    __shared__ int weq[kSelWaves];
+    __shared__ int ish[4];
+    __shared__ float fsh[2];
+    __shared__ uint32_t ush[1];
+
+    const int row = blockIdx.x;
+    const float* s = scores + (int64_t)row * C;
+    int32_t* out = topk_idx + (int64_t)row * k;
+    float* outs = topk_score ? topk_score + (int64_t)row * k : nullptr;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    // wave w owns positions [w * seg, (w + 1) * seg), read 256 at a time
+    const int seg = ((C + kSelWaves - 1) / kSelWaves + 255) & ~255;
+    const int s0 = wave * seg, s1 = min(C, s0 + seg);
+
+    if (k >= C) {
+        for (int i = tid; i < C; i += kSelThreads) {
+            out[i] = i;
+            if (outs) outs[i] = s[i];
+        }
+        return;
+    }
+
+    // the row's range, from the scoring blocks
+    if (tid < kWave) {
+        float lo = INFINITY, hi = -INFINITY;
+        for (int i = lane; i < blocks_per_row; i += kWave) {
+            lo = fminf(lo, bmin[(int64_t)row * blocks_per_row + i]);
+            hi = fmaxf(hi, bmax[(int64_t)row * blocks_per_row + i]);
+        }
+        for (int off = 1; off < kWave; off <<= 1) {
+            lo = fminf(lo, __shfl_xor(lo, off, kWave));
+            hi = fmaxf(hi, __shfl_xor(hi, off, kWave));
+        }
+        if (lane == 0) {
+            fsh[0] = lo;
+            fsh[1] = hi;
+        }
+    }
+    for (int i = tid; i < kBins; i += kSelThreads) hist[i] = 0;
+    __syncthreads();
+    const float lo = fsh[0];
+    const float span = fsh[1] - lo;
+    const float inv = span > 0.f ? (float)kBins / span : 0.f;
+
+    // ---- linear-bin histogram of the row
+    for (int c0 = s0; c0 < s1; c0 += 256) {
+        const int i0 = c0 + lane * 4;
+        if (i0 < s1) {
+            const float4 v4 = *reinterpret_cast<const float4*>(s + i0);
+            const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (i0 + j < s1) atomicAdd(&hist[bin_of(vv[j], lo, inv)], 1);
+        }
+    }
+    __syncthreads();
+    int above, inside;
+    const int p0 = pick_bin(hist, kBins, k, scratch, ish, &above, &inside);
+    int need = k - above;     // elements to take from inside bin p0 (1 <= need <= inside)
+
+    uint32_t tau_key;
+    int id_tau;
+    if (inside <= kCap) {
+        // ---- gather bin p0; count per wave the elements of higher bins
+        if (tid == 0) ish[3] = 0;
+        if (tid < kSelWaves) wsel[tid] = 0;
+        __syncthreads();
+        int n_above = 0;
+        for (int c0 = s0; c0 < s1; c0 += 256) {
+            const int i0 = c0 + lane * 4;
+            if (i0 < s1) {
+                const float4 v4 = *reinterpret_cast<const float4*>(s + i0);
+                const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (i0 + j >= s1) continue;
+                    const int bn = bin_of(vv[j], lo, inv);
+                    if (bn > p0) {
+                        ++n_above;
+                    } else if (bn == p0) {
+                        const int slot = atomicAdd(&ish[3], 1);
+                        cval[slot] = vv[j];
+                        cid[slot] = i0 + j;
+                    }
+                }
+            }
+        }
+        n_above = wave_sum(n_above);
+        if (lane == 0) atomicAdd(&wsel[wave], n_above);
+        __syncthreads();
+        // exact rank of each candidate in (score descending, position ascending) order
+        const int n = ish[3];
+        for (int i = tid; i < n; i += kSelThreads) {
+            const float v = cval[i];
+            const int id = cid[i];
+            int rank = 0;
+            for (int j = 0; j < n; ++j) {
+                const float u = cval[j];
+                rank += (u > v) || (u == v && cid[j] < id);
+            }
+            if (rank < need) atomicAdd(&wsel[id / seg], 1);
+            if (rank == need - 1) {
+                ush[0] = score_key(v);
+                ish[2] = id;
+            }
+        }
+        __syncthreads();
+        tau_key = ush[0];
+        id_tau = ish[2];
+    } else {
+        // ---- radix select over the keys inside bin p0: 11, 11 and 10 bits
+        uint32_t prefix = 0;
+        const int shifts[3] = {21, 10, 0}, widths[3] = {11, 11, 10};
+        for (int p = 0; p < 3; ++p) {
+            const int sh = shifts[p], nb = 1 << widths[p];
+            const uint32_t hmask = p == 0 ? 0u : ~((1u << (sh + widths[p])) - 1u);
+            for (int i = tid; i < kBins; i += kSelThreads) hist[i] = 0;
+            __syncthreads();
+            for (int c0 = s0; c0 < s1; c0 += 256) {
+                const int i0 = c0 + lane * 4;
+                if (i0 < s1) {
+                    const float4 v4 = *reinterpret_cast<const float4*>(s + i0);
+                    const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        if (i0 + j >= s1 || bin_of(vv[j], lo, inv) != p0) continue;
+                        const uint32_t kv = score_key(vv[j]);
+                        if ((kv & hmask) == prefix) atomicAdd(&hist[(kv >> sh) & (uint32_t)(nb - 1)], 1);
+                    }
+                }
+            }
+            __syncthreads();
+            int ab, in;
+            const int d = pick_bin(hist, nb, need, scratch, ish, &ab, &in);
+            need -= ab;
+            prefix |= (uint32_t)d << sh;
+        }
+        tau_key = prefix;
+        // need of the elements with key tau_key (all inside bin p0) are taken, the
+        // lowest positions first; per wave: elements above tau_key and equal to it
+        int n_gt = 0, n_eq = 0;
+        for (int c0 = s0; c0 < s1; c0 += 256) {
+            const int i0 = c0 + lane * 4;
+            if (i0 < s1) {
+                const float4 v4 = *reinterpret_cast<const float4*>(s + i0);
+                const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (i0 + j >= s1) continue;
+                    const uint32_t kv = score_key(vv[j]);
+                    n_gt += kv > tau_key;
+                    n_eq += kv == tau_key;
+                }
+            }
+        }
+        n_gt = wave_sum(n_gt);
+        n_eq = wave_sum(n_eq);
+        if (lane == 0) {
+            wsel[wave] = n_gt;
+            weq[wave] = n_eq;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            int run = 0;
+            for (int w2 = 0; w2 < kSelWaves; ++w2) {
+                const int e = weq[w2];
+                const int take = min(e, max(0, need - run));
+                wsel[w2] += take;
+                weq[w2] = run;          // equal keys before wave w2's segment
+                run += e;
+            }
+        }
+        __syncthreads();
+        // the wave whose segment holds the need-th equal key finds its position
+        const int before = weq[wave];
+        const int mine = (wave + 1 < kSelWaves ? weq[wave + 1] : 0x7fffffff) - before;
+        if (before < need && need - before <= mine) {
+            int run = before;
+            for (int c0 = s0; c0 < s1; c0 += 256) {
+                const int i0 = c0 + lane * 4;
+                int f[4] = {0, 0, 0, 0};
+                if (i0 < s1) {
+                    const float4 v4 = *reinterpret_cast<const float4*>(s + i0);
+                    const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) f[j] = i0 + j < s1 && score_key(vv[j]) == tau_key;
+                }
+                int tot;
+                const int ex = wave_excl_scan(f[0] + f[1] + f[2] + f[3], &tot);
+                int r = run + ex;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (f[j]) {
+                        if (r == need - 1) ish[2] = i0 + j;
+                        ++r;
+                    }
+                }
+                run += tot;
+                if (run >= need) break;
+            }
+        }
+        __syncthreads();
+        id_tau = ish[2];
+    }
+
+    // ---- per-wave output offsets, then the positions in ascending order
+    if (tid == 0) {
+        int run = 0;
+        for (int w2 = 0; w2 < kSelWaves; ++w2) {
+            const int c = wsel[w2];
+            wsel[w2] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    int run = wsel[wave];
+    for (int c0 = s0; c0 < s1; c0 += 256) {
+        const int i0 = c0 + lane * 4;
+        int f[4] = {0, 0, 0, 0};
+        float vv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (i0 < s1) {
+            const float4 v4 = *reinterpret_cast<const float4*>(s + i0);
+            vv[0] = v4.x;
+            vv[1] = v4.y;
+            vv[2] = v4.z;
+            vv[3] = v4.w;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t kv = score_key(vv[j]);
+                f[j] = i0 + j < s1 && (kv > tau_key || (kv == tau_key && i0 + j <= id_tau));
+            }
+        }
+        int tot;
+        int pos = run + wave_excl_scan(f[0] + f[1] + f[2] + f[3], &tot);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (f[j] && pos < k) {
+                out[pos] = i0 + j;
+                if (outs) outs[pos] = vv[j];
+            }
+            pos += f[j];
+        }
+        run += tot;
+    }
+}
+
+}  // namespace
+
+IndexPlan plan_index_topk(int B, int Hkv, int T, int C) {
+    IndexPlan p{};
+    const int64_t rows = (int64_t)B * Hkv * T;
+    p.blocks_per_bg = (C + kScoreRows - 1) / kScoreRows;
+    const size_t sbytes = (((size_t)rows * C * 4) + 255) & ~(size_t)255;
+    const size_t mbytes = (((size_t)rows * p.blocks_per_bg * 4) + 255) & ~(size_t)255;
+    p.off_min = sbytes;
+    p.off_max = sbytes + mbytes;
+    p.ws_bytes = sbytes + 2 * mbytes;
+    return p;
+}
+
+hipError_t launch_index_topk(const float* q, int B, int T, int Hq, const uint16_t* keys, dk_strides ks, int Hkv,
+                             int C, int d, int k, float scale, int32_t* topk_idx, float* topk_score, void* ws,
+                             const IndexPlan& plan, const UnionOut* un, hipStream_t st) {
+    float* scores = (float*)ws;
+    float* bmin = (float*)((char*)ws + plan.off_min);
+    float* bmax = (float*)((char*)ws + plan.off_max);
+    const int64_t bg = (int64_t)B * Hkv;
+    const dim3 sg((unsigned)(bg * plan.blocks_per_bg));
+#define DK_IDX_SCORE(D_, T_)                                                                               \
+    hipLaunchKernelGGL((k_idx_score<D_, T_>), sg, dim3(kScoreThreads), 0, st, q, Hq, keys, ks, Hkv, C, scale, \
+                       plan.blocks_per_bg, scores, bmin, bmax)
+    if (d == 128) {
+        if (T == 2) DK_IDX_SCORE(128, 2); else DK_IDX_SCORE(128, 1);
+    } else {
+        if (T == 2) DK_IDX_SCORE(64, 2); else DK_IDX_SCORE(64, 1);
+    }
+#undef DK_IDX_SCORE
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_idx_select, dim3((unsigned)(bg * T)), dim3(kSelThreads), 0, st, scores, bmin, bmax,
+                       plan.blocks_per_bg, C, k, topk_idx, topk_score);
+    e = hipGetLastError();
+    if (e != hipSuccess || !un) return e;
+    return launch_union(topk_idx, B, Hkv, T, k, C, un->ids, un->member, un->count, un->overlap, nullptr, st);
+}
+
+}  // namespace dk

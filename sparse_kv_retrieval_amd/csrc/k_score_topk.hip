@@ -33,20 +33,12 @@ constexpr int kMaxCand = 8192;       // candidates per (b, g, t) in the merge
 constexpr int kShadowMaxC = 6144;    // chunks per (b, g) with a shadow (pass-2 LDS <= 64 KiB)
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 // streamed once: non-temporal 16-byte loads
 __device__ __forceinline__ float4 nt_load_f4(const float* p) {
     const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
     return make_float4(v.x, v.y, v.z, v.w);
-}
-__device__ __forceinline__ u32x4_t nt_load_u4(const void* p) {
-#ifdef DK_SCORE_PLAIN_LOADS
-    return *reinterpret_cast<const u32x4_t*>(p);
-#else
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-#endif
 }
 __device__ __forceinline__ uint32_t f16_bits(float x) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
@@ -55,19 +47,6 @@ __device__ __forceinline__ uint32_t f16_bits(float x) {
 __device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c,
                                   false);
-}
-// sum over the aligned group of LPR (8 or 16) lanes, every lane gets the total
-template <int LPR>
-__device__ __forceinline__ float dpp_group_sum(float v) {
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
-    if constexpr (LPR == 8) {
-        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
-    } else {
-        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));
-        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
-    }
-    return v;
 }
 
 // The k-th largest of keys[0..n) (1 <= k <= n) by an 8-bit radix select; also

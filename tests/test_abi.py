@@ -27,14 +27,14 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(lib, n), n
     assert {n for n, _, _ in b.EXPORTS} == set(names)
 
 
 def test_abi_version():
-    assert lib.dk_abi_version() == 5
+    assert lib.dk_abi_version() == 6
 
 
 def err():
@@ -71,7 +71,11 @@ SH_MIS = b.dk_landmark_shadow(0x1008, 0x1000)
 @pytest.mark.parametrize("kw,status", [
     (dict(q=NULL), 1), (dict(idx=NULL), 1), (dict(T=3), 1), (dict(T=0), 1), (dict(Hq=30), 1),
     (dict(k=0), 1), (dict(k=1025), 1), (dict(reduce=5), 1), (dict(scale=float("nan")), 1),
-    (dict(lmdt=1), 2), (dict(d=96), 2), (dict(C=70000, k=64), 2), (dict(reduce=1, Hq=24), 2),
+    (dict(lmdt=7), 2), (dict(d=96), 2), (dict(C=70000, k=64), 2), (dict(reduce=1, Hq=24), 2),
+    # bf16 per-token indexer keys: mean only, no shadow, C % 4 == 0, their own workspace size
+    (dict(lmdt=1, reduce=1), 2), (dict(lmdt=1, shadow=ctypes.byref(SH_OK)), 2), (dict(lmdt=1, C=1022), 2),
+    (dict(lmdt=1, d=96), 2), (dict(lmdt=1, wsb=16), 1), (dict(lmdt=1, ws=NULL), 1), (dict(lmdt=1, k=1025), 1),
+    (dict(lmdt=1, ls=b.dk_strides(1 << 22, 1 << 19, 129)), 2),
     (dict(ws=NULL), 1), (dict(wsb=16), 1), (dict(lm=MIS), 2),
     (dict(shadow=ctypes.byref(SH_NULL)), 1), (dict(shadow=ctypes.byref(SH_MIS)), 2),
     (dict(shadow=ctypes.byref(SH_OK), C=8192), 2), (dict(shadow=ctypes.byref(SH_OK), wsb=1024), 1),
@@ -95,7 +99,7 @@ def score_union(uid=FAKE, mem=FAKE, cnt=FAKE, ov=NULL, **kw):
     (dict(uid=NULL), 1), (dict(mem=NULL), 1), (dict(cnt=NULL), 1), (dict(q=NULL), 1), (dict(T=3), 1),
     (dict(k=0), 1), (dict(wsb=16), 1), (dict(d=96), 2), (dict(lm=MIS), 2),
     (dict(shadow=ctypes.byref(SH_NULL)), 1), (dict(shadow=ctypes.byref(SH_OK), C=8192), 2),
-    (dict(C=65536, k=4097), 2),
+    (dict(C=65536, k=4097), 2), (dict(lmdt=1, C=131072, k=4097), 2), (dict(lmdt=1, uid=NULL), 1),
 ])
 def test_score_topk_union_rejects(kw, status):
     # every case fails its checks, so nothing is launched
@@ -111,6 +115,14 @@ def test_score_topk_workspace_sizes():
     assert lib.dk_score_topk_workspace_size(64, 8, 2, 4096, 64, 1) == 64 * 8 * 2 * 4096 * 4 + 64 * 8 * 4
     assert lib.dk_score_topk_workspace_size(1, 1, 2, 128, 8, 0) > 0
     assert lib.dk_score_topk_workspace_size(1, 1, 2, 128, 0, 0) == 0
+
+
+def test_index_topk_workspace_size():
+    # fp32 scores of every token of every (b, g, t), then the per-block score
+    # minima and maxima (1024 tokens per block), each region 256-byte aligned
+    assert lib.dk_index_topk_workspace_size(32, 1, 2, 131072) == 32 * 2 * 131072 * 4 + 2 * 32 * 2 * 128 * 4
+    assert lib.dk_index_topk_workspace_size(1, 1, 1, 2048) == 2048 * 4 + 2 * 256
+    assert lib.dk_index_topk_workspace_size(1, 1, 3, 2048) == 0
 
 
 @pytest.mark.parametrize("kw,status", [
