@@ -312,10 +312,20 @@ dk_status dk_gather_kv(const void* K_src, const void* V_src, dk_dtype dt, dk_str
  * count      : int32 [B, Hkv] valid entries (<= N), or NULL for N.
  * out, lse   : out fp32 [B, T, Hq, dv] and [B, T, Hq] (lse may be NULL).
  * ws         : workspace of dk_attn_workspace_size(...) bytes (NULL when 0).
+ *
+ * Latent rows (dk = 576, dv = 512, token-level selection; Adaptive DHiSparse
+ * Figure 2: attention reads the rows the indexer selected): K holds one bf16
+ * latent row per token (512 content + 64 position columns), V must be the same
+ * pointer with the same strides (the value is the first 512 columns of each
+ * row), chunk == 1, block_ids are token ids (pool_blocks = tokens), and every
+ * query head of a KV head reads the same rows.  The product runs on the matrix
+ * cores; Hq/Hkv must be a multiple of 64/T.  The workspace is
+ * dk_attn_workspace_size(B, Hkv, T, Hq, 512, N, 1).
+ *
  * Errors     : DK_ERR_INVALID_ARG unless sizes >= 1, Hq % Hkv == 0, 1 <= T <= 2,
  *              pointers non-NULL as stated and ws_bytes large enough;
- *              DK_ERR_UNSUPPORTED unless dk == dv in {64, 128}, G*T <= 16 and
- *              the 16-byte alignment rule holds.
+ *              DK_ERR_UNSUPPORTED unless dk == dv in {64, 128} with G*T <= 16, or
+ *              the latent form above holds, and the 16-byte alignment rule holds.
  */
 size_t dk_attn_workspace_size(int B, int Hkv, int T, int Hq, int dv, int N, int chunk);
 dk_status dk_sparse_decode_attn(const float* q, int B, int T, int Hq, int Hkv,

@@ -352,6 +352,15 @@ def sparse_decode_attn(q, K, V, block_ids, member, count, chunk: int, scale: flo
     return out, lse
 
 
+def mla_decode_attn(q, latent, token_ids, member, count, scale: float, dv: int = 512, out=None, lse=None,
+                    ws=None, want_lse=True, stream=None):
+    """Attention over latent rows [B, Hkv, L, dk]: the key is the whole row, the value
+    its first dv columns (the same buffer), token_ids index tokens (chunk = 1)."""
+    return sparse_decode_attn(q, latent, latent[..., :dv], token_ids, member, count, 1, scale,
+                              pool_blocks=latent.shape[2], out=out, lse=lse, ws=ws, want_lse=want_lse,
+                              stream=stream)
+
+
 # ----------------------------------------------------------------------------
 # one layer of the HBM-pool step with buffers allocated once
 # ----------------------------------------------------------------------------

@@ -361,6 +361,7 @@ dk_status dk_gather_kv(const void* K_src, const void* V_src, dk_dtype dt, dk_str
 size_t dk_attn_workspace_size(int B, int Hkv, int T, int Hq, int dv, int N, int chunk) {
     if (B < 1 || Hkv < 1 || T < 1 || T > 2 || Hq < 1 || Hq % Hkv || dv < 1 || N < 1 || chunk < 1)
         return 0;
+    if (dv == 512 && chunk == 1) return dk::plan_mla(B, Hkv, T, Hq, N).ws_bytes;
     return dk::plan_attn(B, Hkv, T, Hq, dv, N, chunk).ws_bytes;
 }
 
@@ -381,8 +382,29 @@ dk_status dk_sparse_decode_attn(const float* q, int B, int T, int Hq, int Hkv, c
     DK_REQUIRE(Hq % Hkv == 0, DK_ERR_INVALID_ARG, "dk_sparse_decode_attn: Hq (%d) %% Hkv (%d) != 0", Hq, Hkv);
     DK_REQUIRE(member || T == 1, DK_ERR_INVALID_ARG, "dk_sparse_decode_attn: member is required when T == 2");
     DK_REQUIRE(std::isfinite(scale), DK_ERR_INVALID_ARG, "dk_sparse_decode_attn: scale must be finite");
+    if (dk == 576 && dv == 512) {
+        // latent rows: the value is the first 512 columns of the key rows
+        const char* fn = "dk_sparse_decode_attn";
+        DK_REQUIRE(kv_dtype == DK_BF16 && chunk == 1, DK_ERR_UNSUPPORTED,
+                   "%s: latent attention (dk 576, dv 512) needs bf16 rows and chunk == 1", fn);
+        DK_REQUIRE(K == V && ks.b == vs.b && ks.h == vs.h && ks.t == vs.t, DK_ERR_UNSUPPORTED,
+                   "%s: latent attention reads the value from the key rows: V must equal K, vs must equal ks", fn);
+        DK_REQUIRE(ks.t >= 576 && ks.b >= 0 && ks.h >= 0, DK_ERR_INVALID_ARG,
+                   "%s: latent rows need a row stride >= 576", fn);
+        const int HB = 64 / T;
+        DK_REQUIRE((Hq / Hkv) % HB == 0, DK_ERR_UNSUPPORTED,
+                   "%s: latent attention needs Hq/Hkv a multiple of %d (got %d)", fn, HB, Hq / Hkv);
+        DK_REQUIRE(aligned16(q) && aligned16(out) && aligned16(K) && strides_ok(ks, 2), DK_ERR_UNSUPPORTED,
+                   "%s: q, out, the latent rows and their strides must be 16-byte aligned", fn);
+        const dk::MlaPlan mp = dk::plan_mla(B, Hkv, T, Hq, N);
+        DK_REQUIRE(ws_bytes >= mp.ws_bytes && (mp.ws_bytes == 0 || ws), DK_ERR_INVALID_ARG,
+                   "%s: workspace needs %zu bytes (got %zu)", fn, mp.ws_bytes, ws_bytes);
+        hipError_t e = dk::launch_mla_attention(q, B, T, Hq, Hkv, K, ks, block_ids, member, count, N, pool_blocks,
+                                                scale, out, lse, ws, mp, (hipStream_t)stream);
+        return e == hipSuccess ? DK_OK : hip_fail(e, fn);
+    }
     DK_REQUIRE(dk == dv && (dk == 64 || dk == 128), DK_ERR_UNSUPPORTED,
-               "dk_sparse_decode_attn: needs dk == dv in {64, 128} (got %d, %d)", dk, dv);
+               "dk_sparse_decode_attn: needs dk == dv in {64, 128}, or dk 576 / dv 512 (got %d, %d)", dk, dv);
     DK_REQUIRE((Hq / Hkv) * T <= 16, DK_ERR_UNSUPPORTED, "dk_sparse_decode_attn: G*T must be <= 16");
     DK_REQUIRE(aligned16(q) && aligned16(out) && aligned16(K) && aligned16(V) && strides_ok(ks, esz) &&
                    strides_ok(vs, esz),

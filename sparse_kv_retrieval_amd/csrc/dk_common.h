@@ -194,6 +194,18 @@ IndexPlan plan_index_topk(int B, int Hkv, int T, int C);
 hipError_t launch_index_topk(const float* q, int B, int T, int Hq, const uint16_t* keys, dk_strides ks, int Hkv,
                              int C, int d, int k, float scale, int32_t* topk_idx, float* topk_score, void* ws,
                              const IndexPlan& plan, const UnionOut* un, hipStream_t st);
+// Latent attention with token-level selection on the matrix cores (k_mla.hip):
+// dk = 576, dv = 512, bf16, value = the first 512 columns of the key rows.
+struct MlaPlan {
+    int splits;       // union ranges per (b, g)
+    int rgroups;      // 64-row query groups per (b, g)
+    size_t ws_bytes;  // range partials (0 when splits == 1)
+};
+MlaPlan plan_mla(int B, int Hkv, int T, int Hq, int N);
+hipError_t launch_mla_attention(const float* q, int B, int T, int Hq, int Hkv, const void* lat, dk_strides ks,
+                                const int32_t* ids, const uint8_t* member, const int32_t* count, int N, int L,
+                                float scale, float* out, float* lse, void* ws, const MlaPlan& plan,
+                                hipStream_t st);
 hipError_t launch_build_shadow(const float* lm, dk_strides ls, int B, int Hkv, int C, int d,
                                uint16_t* lm16, float* norm_max, hipStream_t st);
 

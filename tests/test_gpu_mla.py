@@ -136,3 +136,73 @@ def test_index_topk_full_size_sampled(dkb):
         np.testing.assert_array_equal(mem[b:b + 1].cpu().numpy(), rm)
         np.testing.assert_array_equal(cnt[b:b + 1].cpu().numpy(), rc)
     print(f"near-ties over 3 sampled requests: {near_total}", flush=True)
+
+
+# ----------------------------------------------------------------------------
+# latent attention (matrix cores) over each query's own tokens
+# ----------------------------------------------------------------------------
+
+def to_dev(a, dtype=torch.int32):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dtype).cuda()
+
+
+def check_mla_attention(dkb, w, q, lat, sel, label="", count_override=None):
+    """GPU latent attention on the oracle's union of `sel` against the oracle."""
+    ru, rm, rc, _ = O.union_select(sel)
+    if count_override is not None:
+        rc = count_override
+    member = None if w.T == 1 else to_dev(rm, torch.uint8)
+    out, lse = dkb.mla_decode_attn(q, lat, to_dev(ru), member, to_dev(rc), w.scale)
+    torch.cuda.synchronize()
+    qh = q.cpu().numpy().astype(np.float64)
+    lh = synth.to_numpy_f64(lat)
+    if count_override is None:
+        ro, rl = O.mla_attention(qh, lh, sel, w.dv, w.scale)
+    else:
+        ro, rl = np.zeros(out.shape), np.full(lse.shape, -np.inf)
+    from parity_utils import ATOL, max_abs
+    eo, el = max_abs(out.cpu().numpy(), ro), max_abs(lse.cpu().numpy(), rl)
+    print(f"{label}: max|out err| {eo:.3g}, max|lse err| {el:.3g}", flush=True)
+    assert eo <= ATOL["bf16"] and el <= ATOL["bf16"], (label, eo, el)
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("mla_b1_l2k", {}),                     # ranges merged, ragged last tile
+    ("mla_b1_l2k", dict(k=24)),             # one range: direct output
+    ("mla_b1_l2k", dict(T=1)),              # one query, no member bits
+    ("mla_b2_l16k", {}),
+    ("mla_b1_l2k", dict(Hq=64)),            # one 64-row group
+])
+def test_mla_attention(dkb, name, kw):
+    w = MLA_WORKLOADS[name].with_(**kw)
+    print(f"case {name} {kw}", flush=True)
+    qi, q, Kidx, lat = mla_inputs(w, 41)
+    sel = O.indexer_topk(qi.cpu().numpy().astype(np.float64), synth.to_numpy_f64(Kidx), w.k, w.index_scale)
+    check_mla_attention(dkb, w, q, lat, sel, label=f"{name} {kw}")
+
+
+def test_mla_attention_empty_selection(dkb):
+    w = MLA_WORKLOADS["mla_b1_l2k"].with_(B=2)
+    qi, q, Kidx, lat = mla_inputs(w, 42)
+    sel = O.indexer_topk(qi.cpu().numpy().astype(np.float64), synth.to_numpy_f64(Kidx), w.k, w.index_scale)
+    check_mla_attention(dkb, w, q, lat, sel, label="empty", count_override=np.zeros((2, 1), dtype=np.int64))
+
+
+def test_mla_step_full_size_sampled(dkb):
+    """Indexer + union + latent attention at the full shape (B=32, 131072 tokens,
+    top-2048, 128 heads), in the bench's launch configuration; oracle on sampled requests."""
+    w = MLA_WORKLOADS["mla_b32_l128k"]
+    qi, q, Kidx, lat = mla_inputs(w, 2)
+    idx, _, uid, mem, cnt, ov = dkb.score_topk_union(qi, Kidx, w.k, w.index_scale)
+    out, lse = dkb.mla_decode_attn(q, lat, uid, mem, cnt, w.scale)
+    torch.cuda.synchronize()
+    from parity_utils import ATOL, max_abs
+    for b in (0, 21, 31):
+        gi = idx[b:b + 1].cpu().numpy().astype(np.int64)
+        qh = q[b:b + 1].cpu().numpy().astype(np.float64)
+        lh = synth.to_numpy_f64(lat[b:b + 1])
+        ro, rl = O.mla_attention(qh, lh, gi, w.dv, w.scale)
+        eo = max_abs(out[b:b + 1].cpu().numpy(), ro)
+        el = max_abs(lse[b:b + 1].cpu().numpy(), rl)
+        print(f"request {b}: max|out err| {eo:.3g}, max|lse err| {el:.3g}", flush=True)
+        assert eo <= ATOL["bf16"] and el <= ATOL["bf16"], (b, eo, el)
