@@ -28,6 +28,8 @@ HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, 8 TB/s
 PCIE_PEAK_GBPS = 64.0    # PCIe 5.0 x16, one direction
 METRIC = "dual-query sparse decode steps/s + selected-KV GB/s (% HBM peak), B=64 L=128K"
 METRIC_HOST = "dual-query sparse decode steps/s, KV pool in pinned host memory, B=32 L=128K"
+METRIC_MLA = "token-level dual-query sparse decode steps/s (one layer, 128 heads on one latent head), B=32 L=128K"
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 
 
 def parse():
@@ -315,6 +317,159 @@ def bench_host_pool(args, w):
     print(json.dumps(out), flush=True)
 
 
+def bench_mla(args, w):
+    """Token-level selection over one latent KV head (one layer): the indexer call
+    (dk_score_topk_union on bf16 per-token keys) and latent attention on the matrix
+    cores (dk_sparse_decode_attn with dk 576 / dv 512)."""
+    import numpy as np
+    import torch
+    from sparse_kv_retrieval_amd import binding as dkb
+    from sparse_kv_retrieval_amd import synth
+
+    dev = "cuda"
+    t0 = time.time()
+    qi, q = synth.make_mla_queries(w, args.seed, device=dev)
+    Kidx, lat = synth.make_mla_pools(w, args.seed, device=dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    N = w.T * w.k
+    topk = torch.empty(w.B, 1, w.T, w.k, **i32)
+    uid = torch.empty(w.B, 1, N, **i32)
+    mem = torch.empty(w.B, 1, N, dtype=torch.uint8, device=dev)
+    cnt = torch.empty(w.B, 1, **i32)
+    ov = torch.empty(w.B, 1, **i32)
+    ws_i = torch.empty(dkb.index_topk_workspace_size(w.B, 1, w.T, w.L), dtype=torch.uint8, device=dev)
+    ws_a = torch.empty(max(1, dkb.attn_workspace_size(w.B, 1, w.T, w.Hq, w.dv, N, 1)), dtype=torch.uint8,
+                       device=dev)
+    out = torch.empty(w.B, w.T, w.Hq, w.dv, dtype=torch.float32, device=dev)
+    lse = torch.empty(w.B, w.T, w.Hq, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    print(f"[bench] inputs ready in {time.time() - t0:.1f} s: indexer keys {Kidx.nbytes / 1e9:.2f} GB, "
+          f"latent {lat.nbytes / 1e9:.2f} GB", file=sys.stderr, flush=True)
+
+    calls = ("index_topk_union", "mla_attention")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+
+    def step(record):
+        e = ev[record - 1] if record else None
+        if record:
+            e[0].record()
+        dkb.score_topk_union(qi, Kidx, w.k, w.index_scale, dkb.DK_REDUCE_MEAN, topk, None, uid, mem, cnt, ov,
+                             ws_i)
+        if record:
+            e[1].record()
+        dkb.mla_decode_attn(q, lat, uid, mem, cnt, w.scale, out=out, lse=lse, ws=ws_a)
+        if record:
+            e[2].record()
+
+    step(0)
+    torch.cuda.synchronize()
+    union_tokens = int(cnt.sum().item())
+    accuracy = float(ov.double().mean().item()) / w.k
+    for _ in range(args.warmup):
+        step(0)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for s_ in range(args.steps):
+        step(s_ + 1)
+    end.record()
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / args.steps
+    call_ms = {c: sum(ev[s_][i].elapsed_time(ev[s_][i + 1]) for s_ in range(args.steps)) / args.steps
+               for i, c in enumerate(calls)}
+    step_ms = [ev[s_][0].elapsed_time(ev[s_][2]) for s_ in range(args.steps)]
+
+    # algorithmic work: the indexer streams every key once (queries and the
+    # selected ids besides); attention reads each union row once and does
+    # 2 * (dk + dv) flops per (query row, own token)
+    idx_bytes = w.B * w.L * w.di * 2 + w.B * w.T * w.Hi * w.di * 4 + w.B * w.T * w.k * 4 * 3
+    attn_bytes = union_tokens * w.latent_row_bytes() + w.B * w.T * w.Hq * (w.dk * 4 + (w.dv + 1) * 4)
+    attn_flops = 2.0 * w.B * w.T * w.Hq * w.k * (w.dk + w.dv)
+    ki, ka = call_ms["index_topk_union"], call_ms["mla_attention"]
+    kernels = {
+        "index_topk_union": {"avg_us": round(ki * 1e3, 2), "bytes_per_launch": int(idx_bytes),
+                             "GBps": round(idx_bytes / (ki * 1e-3) / 1e9, 1),
+                             "frac_hbm_peak": round(idx_bytes / (ki * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
+        "mla_attention": {"avg_us": round(ka * 1e3, 2), "bytes_per_launch": int(attn_bytes),
+                          "flops_per_launch": attn_flops,
+                          "TFLOPs": round(attn_flops / (ka * 1e-3) / 1e12, 1),
+                          "frac_mfma_bf16_peak": round(attn_flops / (ka * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                          "GBps": round(attn_bytes / (ka * 1e-3) / 1e9, 1)},
+    }
+    dominant = max(kernels, key=lambda c: kernels[c]["avg_us"])
+    if dominant == "mla_attention":
+        kd = kernels[dominant]
+        roofline = {"bound": "mfma", "kernel": dominant, "achieved": kd["TFLOPs"],
+                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": kd["frac_mfma_bf16_peak"],
+                    "traffic": measured_traffic(w.name, dominant)}
+    else:
+        kd = kernels[dominant]
+        roofline = {"bound": "hbm", "kernel": dominant, "achieved": kd["GBps"], "peak": HBM_PEAK_GBPS,
+                    "unit": "GB/s", "frac": kd["frac_hbm_peak"], "traffic": measured_traffic(w.name, dominant)}
+    res = {
+        "metric": METRIC_MLA,
+        "value": round(1000.0 / ms_per_step, 3),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "L": w.L, "Hq": w.Hq, "dk": w.dk, "dv": w.dv, "Hi": w.Hi,
+                   "di": w.di, "k": w.k, "T": w.T, "seed": args.seed},
+        "ms_per_step_median": round(float(np.median(step_ms)), 4),
+        "ms_per_step_min": round(float(np.min(step_ms)), 4),
+        "mean_union_tokens": round(union_tokens / w.B, 1),
+        "prediction_accuracy": round(accuracy, 5),
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    if args.cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline_mla(w, qi, q, Kidx, lat, topk, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline_mla(w, qi, q, Kidx, lat, gpu_topk, budget_s):
+    """Time the fp64 CPU oracle (indexer top-k, union, latent attention) on whole
+    sampled requests, single thread; compare the sampled selections with the GPU's."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import dualkv_oracle as O
+    from sparse_kv_retrieval_amd import synth
+
+    spent, units = 0.0, 0
+    cmp = [0, 0, 0, 0]
+    with threadpool_limits(1):
+        b = 0
+        while spent < budget_s and b < w.B:
+            qih = qi[b:b + 1].cpu().numpy().astype(np.float64)
+            qh = q[b:b + 1].cpu().numpy().astype(np.float64)
+            kh = synth.to_numpy_f64(Kidx[b:b + 1])
+            lh = synth.to_numpy_f64(lat[b:b + 1])
+            t0 = time.perf_counter()
+            s = O.chunk_scores(qih, kh, w.index_scale, "mean")
+            sel = O.topk_chunks(s, w.k)
+            O.union_select(sel)
+            O.mla_attention(qh, lh, sel, w.dv, w.scale)
+            spent += time.perf_counter() - t0
+            units += 1
+            for i, x in enumerate(near_tie_report(gpu_topk[b:b + 1].cpu().numpy(), sel, s)):
+                cmp[i] += x
+            b += 1
+    per_unit = spent / units
+    return {"value": 1.0 / (per_unit * w.B), "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{units} whole requests of the {w.name} layer ({spent:.1f} s, {per_unit:.2f} s each), "
+                      f"scaled to {w.B} requests per step",
+            "selection_check": {"rows": cmp[0], "rows_differing": cmp[1], "near_tie_chunks": cmp[2],
+                                "mismatched_chunks": cmp[3]}}
+
+
 def calibrate_copy():
     """Three plain copies of 512 MiB K + 512 MiB V (1 GiB read, 1 GiB written each)."""
     import torch
@@ -346,11 +501,15 @@ def main():
 
     from sparse_kv_retrieval_amd import binding as dkb   # fails loudly without libdualkv.so
     from sparse_kv_retrieval_amd import synth
-    from sparse_kv_retrieval_amd.workloads import WORKLOADS
+    from sparse_kv_retrieval_amd.workloads import MLA_WORKLOADS, WORKLOADS
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.workload in MLA_WORKLOADS:
+        torch.cuda.set_device(0)
+        bench_mla(args, MLA_WORKLOADS[args.workload])
+        return
     w = WORKLOADS[args.workload]
     if args.layers:
         w = w.with_(layers=args.layers)
