@@ -110,6 +110,18 @@ __device__ __forceinline__ float dpp_xor1(float x) {
 }
 
 // ---------------------------------------------------------------------------
+// Agent-scope relaxed store / load: written through to, and read from, the
+// device-coherent level, so another block (on any XCD) that reads the value
+// after a device-scope atomic sees it without a whole-cache fence.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void store_agent(int32_t* p, int32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t load_agent(const int32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
 // Streamed once: non-temporal 16-byte loads.
 // ---------------------------------------------------------------------------
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -188,6 +200,7 @@ struct IndexPlan {
     int blocks_per_bg;   // scoring blocks per (b, g)
     size_t off_min;      // byte offsets of the per-block score minima / maxima
     size_t off_max;
+    size_t off_arrive;   // one arrival counter per (b, g) for the fused union
     size_t ws_bytes;
 };
 IndexPlan plan_index_topk(int B, int Hkv, int T, int C);

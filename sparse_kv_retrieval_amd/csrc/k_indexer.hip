@@ -23,8 +23,12 @@
 //                  That bin's elements are gathered into LDS and ranked exactly.
 //                  A bin too large to gather falls back to an 11/11/10-bit radix
 //                  select over order-preserving keys inside it, followed by a
-//                  count of the equal keys in position order.
+//                  count of the equal keys in position order.  Every pass keeps
+//                  eight 16-byte loads per lane in flight.  With union outputs,
+//                  the last of the T blocks of a (b, g) merges its T sets
+//                  (Adaptive DHiSparse, Figure 3 (2)).
 #include "dk_common.h"
+#include "dk_union_core.h"
 
 namespace dk {
 namespace {
@@ -45,7 +49,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_idx_score(const float* __rest
                                                             const uint16_t* __restrict__ keys, dk_strides ks,
                                                             int Hkv, int C, float scale, int blocks_per_bg,
                                                             float* __restrict__ scores, float* __restrict__ bmin,
-                                                            float* __restrict__ bmax) {
+                                                            float* __restrict__ bmax, uint32_t* __restrict__ arrivals) {
     constexpr int LPR = D / 8, RPW = kWave / LPR, U = 8, ROWS_PER_ITER = 4 * RPW * U;
     __shared__ float sres[T][kScoreRows];
     __shared__ __align__(16) float qs[T][D];
@@ -58,6 +62,8 @@ __global__ __launch_bounds__(kScoreThreads) void k_idx_score(const float* __rest
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int rp = lane / LPR, part = lane % LPR;
     const int G = Hq / Hkv;
+    // the selection kernel that follows counts its (b, g, t) blocks from zero
+    if (arrivals && blk == 0 && threadIdx.x == 0) arrivals[bg] = 0u;
 
     // the first rows are requested before the query staging
     const uint16_t* base = keys + (int64_t)b * ks.b + (int64_t)g * ks.h + (int64_t)row0 * ks.t + part * 8;
@@ -183,88 +189,105 @@ __device__ __forceinline__ int pick_bin(const int* hist, int nb, int need, int* 
     return r;
 }
 
+// Eight 256-position chunks of a wave's segment per step, every load issued
+// before the first is used; f(i0, v) gets each chunk's first position and values.
+template <typename F>
+__device__ __forceinline__ void for_segment(const float* s, int s0, int s1, F f) {
+    constexpr int U = 8;
+    const int lane = threadIdx.x & (kWave - 1);
+    for (int c0 = s0; c0 < s1; c0 += 256 * U) {
+        float4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i0 = c0 + 256 * u + 4 * lane;
+            v[u] = i0 < s1 ? *reinterpret_cast<const float4*>(s + i0) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i0 = c0 + 256 * u + 4 * lane;
+            if (c0 + 256 * u < s1) f(i0, v[u]);       // wave-uniform: the chunk is (partly) in range
+        }
+    }
+}
+
+constexpr int kSelPool = 3 * 4096 + 16;   // ints: hist + candidates, or the union merge (k <= 4096)
+
 __global__ __launch_bounds__(kSelThreads) void k_idx_select(const float* __restrict__ scores,
                                                            const float* __restrict__ bmin,
                                                            const float* __restrict__ bmax, int blocks_per_row,
-                                                           int C, int k, int32_t* __restrict__ topk_idx,
-                                                           float* __restrict__ topk_score) {
-    __shared__ int hist[kBins];
-    __shared__ float cval[kCap];
-    __shared__ int cid[kCap];
+                                                           int T, int C, int k, int32_t* __restrict__ topk_idx,
+                                                           float* __restrict__ topk_score, UnionOut un,
+                                                           uint32_t* __restrict__ arrivals) {
+    __shared__ int pool[kSelPool];
     __shared__ int scratch[kSelWaves + 1];
     __shared__ int wsel[kSelWaves];   // positions each wave's segment contributes
     __shared__ int weq[kSelWaves];
-    __shared__ int ish[4];
+    __shared__ int ish[8];
     __shared__ float fsh[2];
     __shared__ uint32_t ush[1];
+    int* hist = pool;                                   // [kBins]
+    float* cval = reinterpret_cast<float*>(pool + kBins);   // [kCap]
+    int* cid = pool + kBins + kCap;                     // [kCap]
 
     const int row = blockIdx.x;
+    const int bg = row / T;
     const float* s = scores + (int64_t)row * C;
     int32_t* out = topk_idx + (int64_t)row * k;
     float* outs = topk_score ? topk_score + (int64_t)row * k : nullptr;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    // wave w owns positions [w * seg, (w + 1) * seg), read 256 at a time
+    // wave w owns positions [w * seg, (w + 1) * seg)
     const int seg = ((C + kSelWaves - 1) / kSelWaves + 255) & ~255;
     const int s0 = wave * seg, s1 = min(C, s0 + seg);
 
     if (k >= C) {
         for (int i = tid; i < C; i += kSelThreads) {
-            out[i] = i;
+            store_agent(out + i, i);
             if (outs) outs[i] = s[i];
         }
-        return;
-    }
+    } else {
+        // the row's range, from the scoring blocks
+        if (tid < kWave) {
+            float lo = INFINITY, hi = -INFINITY;
+            for (int i = lane; i < blocks_per_row; i += kWave) {
+                lo = fminf(lo, bmin[(int64_t)row * blocks_per_row + i]);
+                hi = fmaxf(hi, bmax[(int64_t)row * blocks_per_row + i]);
+            }
+            for (int off = 1; off < kWave; off <<= 1) {
+                lo = fminf(lo, __shfl_xor(lo, off, kWave));
+                hi = fmaxf(hi, __shfl_xor(hi, off, kWave));
+            }
+            if (lane == 0) {
+                fsh[0] = lo;
+                fsh[1] = hi;
+            }
+        }
+        for (int i = tid; i < kBins; i += kSelThreads) hist[i] = 0;
+        __syncthreads();
+        const float lo = fsh[0];
+        const float span = fsh[1] - lo;
+        const float inv = span > 0.f ? (float)kBins / span : 0.f;
 
-    // the row's range, from the scoring blocks
-    if (tid < kWave) {
-        float lo = INFINITY, hi = -INFINITY;
-        for (int i = lane; i < blocks_per_row; i += kWave) {
-            lo = fminf(lo, bmin[(int64_t)row * blocks_per_row + i]);
-            hi = fmaxf(hi, bmax[(int64_t)row * blocks_per_row + i]);
-        }
-        for (int off = 1; off < kWave; off <<= 1) {
-            lo = fminf(lo, __shfl_xor(lo, off, kWave));
-            hi = fmaxf(hi, __shfl_xor(hi, off, kWave));
-        }
-        if (lane == 0) {
-            fsh[0] = lo;
-            fsh[1] = hi;
-        }
-    }
-    for (int i = tid; i < kBins; i += kSelThreads) hist[i] = 0;
-    __syncthreads();
-    const float lo = fsh[0];
-    const float span = fsh[1] - lo;
-    const float inv = span > 0.f ? (float)kBins / span : 0.f;
-
-    // ---- linear-bin histogram of the row
-    for (int c0 = s0; c0 < s1; c0 += 256) {
-        const int i0 = c0 + lane * 4;
-        if (i0 < s1) {
-            const float4 v4 = *reinterpret_cast<const float4*>(s + i0);
+        // ---- linear-bin histogram of the row
+        for_segment(s, s0, s1, [&](int i0, const float4& v4) {
             const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 if (i0 + j < s1) atomicAdd(&hist[bin_of(vv[j], lo, inv)], 1);
-        }
-    }
-    __syncthreads();
-    int above, inside;
-    const int p0 = pick_bin(hist, kBins, k, scratch, ish, &above, &inside);
-    int need = k - above;     // elements to take from inside bin p0 (1 <= need <= inside)
-
-    uint32_t tau_key;
-    int id_tau;
-    if (inside <= kCap) {
-        // ---- gather bin p0; count per wave the elements of higher bins
-        if (tid == 0) ish[3] = 0;
-        if (tid < kSelWaves) wsel[tid] = 0;
+        });
         __syncthreads();
-        int n_above = 0;
-        for (int c0 = s0; c0 < s1; c0 += 256) {
-            const int i0 = c0 + lane * 4;
-            if (i0 < s1) {
-                const float4 v4 = *reinterpret_cast<const float4*>(s + i0);
+        int above, inside;
+        const int p0 = pick_bin(hist, kBins, k, scratch, ish, &above, &inside);
+        int need = k - above;     // elements to take from inside bin p0 (1 <= need <= inside)
+
+        uint32_t tau_key;
+        int id_tau;
+        if (inside <= kCap) {
+            // ---- gather bin p0; count per wave the elements of higher bins
+            if (tid == 0) ish[3] = 0;
+            if (tid < kSelWaves) wsel[tid] = 0;
+            __syncthreads();
+            int n_above = 0;
+            for_segment(s, s0, s1, [&](int i0, const float4& v4) {
                 const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -278,43 +301,39 @@ __global__ __launch_bounds__(kSelThreads) void k_idx_select(const float* __restr
                         cid[slot] = i0 + j;
                     }
                 }
-            }
-        }
-        n_above = wave_sum(n_above);
-        if (lane == 0) atomicAdd(&wsel[wave], n_above);
-        __syncthreads();
-        // exact rank of each candidate in (score descending, position ascending) order
-        const int n = ish[3];
-        for (int i = tid; i < n; i += kSelThreads) {
-            const float v = cval[i];
-            const int id = cid[i];
-            int rank = 0;
-            for (int j = 0; j < n; ++j) {
-                const float u = cval[j];
-                rank += (u > v) || (u == v && cid[j] < id);
-            }
-            if (rank < need) atomicAdd(&wsel[id / seg], 1);
-            if (rank == need - 1) {
-                ush[0] = score_key(v);
-                ish[2] = id;
-            }
-        }
-        __syncthreads();
-        tau_key = ush[0];
-        id_tau = ish[2];
-    } else {
-        // ---- radix select over the keys inside bin p0: 11, 11 and 10 bits
-        uint32_t prefix = 0;
-        const int shifts[3] = {21, 10, 0}, widths[3] = {11, 11, 10};
-        for (int p = 0; p < 3; ++p) {
-            const int sh = shifts[p], nb = 1 << widths[p];
-            const uint32_t hmask = p == 0 ? 0u : ~((1u << (sh + widths[p])) - 1u);
-            for (int i = tid; i < kBins; i += kSelThreads) hist[i] = 0;
+            });
+            n_above = wave_sum(n_above);
+            if (lane == 0) atomicAdd(&wsel[wave], n_above);
             __syncthreads();
-            for (int c0 = s0; c0 < s1; c0 += 256) {
-                const int i0 = c0 + lane * 4;
-                if (i0 < s1) {
-                    const float4 v4 = *reinterpret_cast<const float4*>(s + i0);
+            // exact rank of each candidate in (score descending, position ascending) order
+            const int n = ish[3];
+            for (int i = tid; i < n; i += kSelThreads) {
+                const float v = cval[i];
+                const int id = cid[i];
+                int rank = 0;
+                for (int j = 0; j < n; ++j) {
+                    const float u = cval[j];
+                    rank += (u > v) || (u == v && cid[j] < id);
+                }
+                if (rank < need) atomicAdd(&wsel[id / seg], 1);
+                if (rank == need - 1) {
+                    ush[0] = score_key(v);
+                    ish[2] = id;
+                }
+            }
+            __syncthreads();
+            tau_key = ush[0];
+            id_tau = ish[2];
+        } else {
+            // ---- radix select over the keys inside bin p0: 11, 11 and 10 bits
+            uint32_t prefix = 0;
+            const int shifts[3] = {21, 10, 0}, widths[3] = {11, 11, 10};
+            for (int pz = 0; pz < 3; ++pz) {
+                const int sh = shifts[pz], nb = 1 << widths[pz];
+                const uint32_t hmask = pz == 0 ? 0u : ~((1u << (sh + widths[pz])) - 1u);
+                for (int i = tid; i < kBins; i += kSelThreads) hist[i] = 0;
+                __syncthreads();
+                for_segment(s, s0, s1, [&](int i0, const float4& v4) {
                     const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
@@ -322,22 +341,18 @@ __global__ __launch_bounds__(kSelThreads) void k_idx_select(const float* __restr
                         const uint32_t kv = score_key(vv[j]);
                         if ((kv & hmask) == prefix) atomicAdd(&hist[(kv >> sh) & (uint32_t)(nb - 1)], 1);
                     }
-                }
+                });
+                __syncthreads();
+                int ab, in;
+                const int d = pick_bin(hist, nb, need, scratch, ish, &ab, &in);
+                need -= ab;
+                prefix |= (uint32_t)d << sh;
             }
-            __syncthreads();
-            int ab, in;
-            const int d = pick_bin(hist, nb, need, scratch, ish, &ab, &in);
-            need -= ab;
-            prefix |= (uint32_t)d << sh;
-        }
-        tau_key = prefix;
-        // need of the elements with key tau_key (all inside bin p0) are taken, the
-        // lowest positions first; per wave: elements above tau_key and equal to it
-        int n_gt = 0, n_eq = 0;
-        for (int c0 = s0; c0 < s1; c0 += 256) {
-            const int i0 = c0 + lane * 4;
-            if (i0 < s1) {
-                const float4 v4 = *reinterpret_cast<const float4*>(s + i0);
+            tau_key = prefix;
+            // need of the elements with key tau_key (all inside bin p0) are taken, the
+            // lowest positions first; per wave: elements above tau_key and equal to it
+            int n_gt = 0, n_eq = 0;
+            for_segment(s, s0, s1, [&](int i0, const float4& v4) {
                 const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -346,96 +361,117 @@ __global__ __launch_bounds__(kSelThreads) void k_idx_select(const float* __restr
                     n_gt += kv > tau_key;
                     n_eq += kv == tau_key;
                 }
+            });
+            n_gt = wave_sum(n_gt);
+            n_eq = wave_sum(n_eq);
+            if (lane == 0) {
+                wsel[wave] = n_gt;
+                weq[wave] = n_eq;
             }
+            __syncthreads();
+            if (tid == 0) {
+                int run = 0;
+                for (int w2 = 0; w2 < kSelWaves; ++w2) {
+                    const int e = weq[w2];
+                    const int take = min(e, max(0, need - run));
+                    wsel[w2] += take;
+                    weq[w2] = run;          // equal keys before wave w2's segment
+                    run += e;
+                }
+            }
+            __syncthreads();
+            // the wave whose segment holds the need-th equal key finds its position
+            const int before = weq[wave];
+            const int mine = (wave + 1 < kSelWaves ? weq[wave + 1] : 0x7fffffff) - before;
+            if (before < need && need - before <= mine) {
+                int run = before;
+                for (int c0 = s0; c0 < s1 && run < need; c0 += 256) {
+                    const int i0 = c0 + lane * 4;
+                    int f[4] = {0, 0, 0, 0};
+                    if (i0 < s1) {
+                        const float4 v4 = *reinterpret_cast<const float4*>(s + i0);
+                        const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) f[j] = i0 + j < s1 && score_key(vv[j]) == tau_key;
+                    }
+                    int tot;
+                    const int ex = wave_excl_scan(f[0] + f[1] + f[2] + f[3], &tot);
+                    int r = run + ex;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        if (f[j]) {
+                            if (r == need - 1) ish[2] = i0 + j;
+                            ++r;
+                        }
+                    }
+                    run += tot;
+                }
+            }
+            __syncthreads();
+            id_tau = ish[2];
         }
-        n_gt = wave_sum(n_gt);
-        n_eq = wave_sum(n_eq);
-        if (lane == 0) {
-            wsel[wave] = n_gt;
-            weq[wave] = n_eq;
-        }
-        __syncthreads();
+
+        // ---- per-wave output offsets, then the positions in ascending order
         if (tid == 0) {
             int run = 0;
             for (int w2 = 0; w2 < kSelWaves; ++w2) {
-                const int e = weq[w2];
-                const int take = min(e, max(0, need - run));
-                wsel[w2] += take;
-                weq[w2] = run;          // equal keys before wave w2's segment
-                run += e;
+                const int c = wsel[w2];
+                wsel[w2] = run;
+                run += c;
             }
         }
         __syncthreads();
-        // the wave whose segment holds the need-th equal key finds its position
-        const int before = weq[wave];
-        const int mine = (wave + 1 < kSelWaves ? weq[wave + 1] : 0x7fffffff) - before;
-        if (before < need && need - before <= mine) {
-            int run = before;
-            for (int c0 = s0; c0 < s1; c0 += 256) {
-                const int i0 = c0 + lane * 4;
-                int f[4] = {0, 0, 0, 0};
-                if (i0 < s1) {
-                    const float4 v4 = *reinterpret_cast<const float4*>(s + i0);
-                    const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) f[j] = i0 + j < s1 && score_key(vv[j]) == tau_key;
-                }
-                int tot;
-                const int ex = wave_excl_scan(f[0] + f[1] + f[2] + f[3], &tot);
-                int r = run + ex;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    if (f[j]) {
-                        if (r == need - 1) ish[2] = i0 + j;
-                        ++r;
-                    }
-                }
-                run += tot;
-                if (run >= need) break;
-            }
-        }
-        __syncthreads();
-        id_tau = ish[2];
-    }
-
-    // ---- per-wave output offsets, then the positions in ascending order
-    if (tid == 0) {
-        int run = 0;
-        for (int w2 = 0; w2 < kSelWaves; ++w2) {
-            const int c = wsel[w2];
-            wsel[w2] = run;
-            run += c;
-        }
-    }
-    __syncthreads();
-    int run = wsel[wave];
-    for (int c0 = s0; c0 < s1; c0 += 256) {
-        const int i0 = c0 + lane * 4;
-        int f[4] = {0, 0, 0, 0};
-        float vv[4] = {0.f, 0.f, 0.f, 0.f};
-        if (i0 < s1) {
-            const float4 v4 = *reinterpret_cast<const float4*>(s + i0);
-            vv[0] = v4.x;
-            vv[1] = v4.y;
-            vv[2] = v4.z;
-            vv[3] = v4.w;
+        int run = wsel[wave];
+        for_segment(s, s0, s1, [&](int i0, const float4& v4) {
+            const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+            int f[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const uint32_t kv = score_key(vv[j]);
                 f[j] = i0 + j < s1 && (kv > tau_key || (kv == tau_key && i0 + j <= id_tau));
             }
-        }
-        int tot;
-        int pos = run + wave_excl_scan(f[0] + f[1] + f[2] + f[3], &tot);
+            int tot;
+            int pos = run + wave_excl_scan(f[0] + f[1] + f[2] + f[3], &tot);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (f[j] && pos < k) {
-                out[pos] = i0 + j;
-                if (outs) outs[pos] = vv[j];
+            for (int j = 0; j < 4; ++j) {
+                if (f[j] && pos < k) {
+                    store_agent(out + pos, i0 + j);
+                    if (outs) outs[pos] = vv[j];
+                }
+                pos += f[j];
             }
-            pos += f[j];
-        }
-        run += tot;
+            run += tot;
+        });
+    }
+    if (un.ids == nullptr) return;
+
+    // Union of the (b, g)'s T sets, by the last of its T blocks to finish.  The
+    // positions above were stored at agent scope; once every lane's stores have
+    // completed the block counts itself in, and the last block reads all T sets
+    // back at agent scope.  The scoring kernel of the same call zeroed the counter.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0)
+        ish[7] = __hip_atomic_fetch_add(&arrivals[bg], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                 (unsigned)(T - 1);
+    __syncthreads();
+    if (!ish[7]) return;
+    int32_t* u0s = pool;                 // the selection's LDS is free now
+    int32_t* u1s = u0s + k;
+    int32_t* dup_pre = u1s + k;
+    const int32_t* src = topk_idx + (int64_t)bg * T * k;
+    for (int i = tid; i < k; i += kSelThreads) {
+        u0s[i] = load_agent(src + i);
+        u1s[i] = T == 2 ? load_agent(src + k + i) : 0;
+    }
+    __syncthreads();
+    const int N = T * k;
+    int nshared;
+    const int count = block_union_two(u0s, u1s, T, k, un.ids + (int64_t)bg * N, un.member + (int64_t)bg * N,
+                                      dup_pre, scratch, nullptr, &nshared);
+    if (tid == 0) {
+        un.count[bg] = count;
+        if (un.overlap) un.overlap[bg] = nshared;
     }
 }
 
@@ -447,9 +483,11 @@ IndexPlan plan_index_topk(int B, int Hkv, int T, int C) {
     p.blocks_per_bg = (C + kScoreRows - 1) / kScoreRows;
     const size_t sbytes = (((size_t)rows * C * 4) + 255) & ~(size_t)255;
     const size_t mbytes = (((size_t)rows * p.blocks_per_bg * 4) + 255) & ~(size_t)255;
+    const size_t abytes = (((size_t)B * Hkv * 4) + 255) & ~(size_t)255;
     p.off_min = sbytes;
     p.off_max = sbytes + mbytes;
-    p.ws_bytes = sbytes + 2 * mbytes;
+    p.off_arrive = sbytes + 2 * mbytes;
+    p.ws_bytes = sbytes + 2 * mbytes + abytes;
     return p;
 }
 
@@ -459,11 +497,12 @@ hipError_t launch_index_topk(const float* q, int B, int T, int Hq, const uint16_
     float* scores = (float*)ws;
     float* bmin = (float*)((char*)ws + plan.off_min);
     float* bmax = (float*)((char*)ws + plan.off_max);
+    uint32_t* arrivals = un ? (uint32_t*)((char*)ws + plan.off_arrive) : nullptr;
     const int64_t bg = (int64_t)B * Hkv;
     const dim3 sg((unsigned)(bg * plan.blocks_per_bg));
 #define DK_IDX_SCORE(D_, T_)                                                                               \
     hipLaunchKernelGGL((k_idx_score<D_, T_>), sg, dim3(kScoreThreads), 0, st, q, Hq, keys, ks, Hkv, C, scale, \
-                       plan.blocks_per_bg, scores, bmin, bmax)
+                       plan.blocks_per_bg, scores, bmin, bmax, arrivals)
     if (d == 128) {
         if (T == 2) DK_IDX_SCORE(128, 2); else DK_IDX_SCORE(128, 1);
     } else {
@@ -472,11 +511,10 @@ hipError_t launch_index_topk(const float* q, int B, int T, int Hq, const uint16_
 #undef DK_IDX_SCORE
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    const UnionOut uo = un ? *un : UnionOut{nullptr, nullptr, nullptr, nullptr};
     hipLaunchKernelGGL(k_idx_select, dim3((unsigned)(bg * T)), dim3(kSelThreads), 0, st, scores, bmin, bmax,
-                       plan.blocks_per_bg, C, k, topk_idx, topk_score);
-    e = hipGetLastError();
-    if (e != hipSuccess || !un) return e;
-    return launch_union(topk_idx, B, Hkv, T, k, C, un->ids, un->member, un->count, un->overlap, nullptr, st);
+                       plan.blocks_per_bg, T, C, k, topk_idx, topk_score, uo, arrivals);
+    return hipGetLastError();
 }
 
 }  // namespace dk

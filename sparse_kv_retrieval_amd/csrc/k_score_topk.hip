@@ -562,16 +562,6 @@ __global__ __launch_bounds__(kThreads) void k_score_lo(const float* __restrict__
 // chunk, s the fp32 score this kernel computes), their fp32 re-scores, and the
 // exact top-k among them (ties to the lower id), written in ascending order.
 // ---------------------------------------------------------------------------
-// Agent-scope relaxed store / load: written through to, and read from, the
-// device-coherent level, so another block (on any XCD) that reads the value
-// after a device-scope atomic sees it without a whole-cache fence.
-__device__ __forceinline__ void store_agent(int32_t* p, int32_t v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int32_t load_agent(const int32_t* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 template <int D, bool MAXRED>
 __global__ __launch_bounds__(kThreads) void k_select_exact(
     const float* __restrict__ q, int T, int Hq, const float* __restrict__ lm, dk_strides ls,

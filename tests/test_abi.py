@@ -119,9 +119,10 @@ def test_score_topk_workspace_sizes():
 
 def test_index_topk_workspace_size():
     # fp32 scores of every token of every (b, g, t), then the per-block score
-    # minima and maxima (1024 tokens per block), each region 256-byte aligned
-    assert lib.dk_index_topk_workspace_size(32, 1, 2, 131072) == 32 * 2 * 131072 * 4 + 2 * 32 * 2 * 128 * 4
-    assert lib.dk_index_topk_workspace_size(1, 1, 1, 2048) == 2048 * 4 + 2 * 256
+    # minima and maxima (1024 tokens per block), then one union arrival counter
+    # per (b, g), each region 256-byte aligned
+    assert lib.dk_index_topk_workspace_size(32, 1, 2, 131072) == 32 * 2 * 131072 * 4 + 2 * 32 * 2 * 128 * 4 + 256
+    assert lib.dk_index_topk_workspace_size(1, 1, 1, 2048) == 2048 * 4 + 2 * 256 + 256
     assert lib.dk_index_topk_workspace_size(1, 1, 3, 2048) == 0
 
 
