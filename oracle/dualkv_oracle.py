@@ -399,3 +399,62 @@ def mla_decode_step(qi, Kidx, q, latent, k: int, dv: int, index_scale: float, sc
     out, lse = mla_attention(q, latent, sel, dv, scale)
     return dict(topk=sel, union_ids=union_ids, member=member, count=count, overlap=overlap,
                 accuracy=prediction_accuracy(overlap, k), out=out, lse=lse)
+
+
+# ----------------------------------------------------------------------------
+# selection variants: min/max chunk summaries (upper-bound scores)
+# ----------------------------------------------------------------------------
+
+def chunk_minmax(K: np.ndarray, chunk: int):
+    """Coordinate-wise minimum and maximum key of every chunk.
+
+    OasisKV summary, "Look-ahead Attention": the draft query scans compressed
+    key summaries, two vectors per block (coordinate-wise min and max).
+    K: [B, Hkv, L, d] with L a multiple of chunk.  Returns (kmin, kmax), each
+    [B, Hkv, C, d].
+    """
+    K = np.asarray(K, dtype=np.float64)
+    B, H, L, d = K.shape
+    if L % chunk != 0:
+        raise ValueError("L must be a multiple of chunk")
+    Kc = K.reshape(B, H, L // chunk, chunk, d)
+    return Kc.min(axis=3), Kc.max(axis=3)
+
+
+def minmax_scores(q: np.ndarray, kmin: np.ndarray, kmax: np.ndarray, scale: float,
+                  reduce: str = "mean") -> np.ndarray:
+    """Upper-bound chunk scores from min/max summaries.
+
+    For one query head h and chunk c the largest dot product any key inside the
+    box [kmin, kmax] can reach is sum_d max(q_d * kmin_d, q_d * kmax_d); the
+    score is scale times that bound, combined over the G heads of KV head g by
+    the chunk-score rule (mean by default, or max).  Returns [B, Hkv, T, C].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    kmin = np.asarray(kmin, dtype=np.float64)
+    kmax = np.asarray(kmax, dtype=np.float64)
+    B, T, Hq, d = q.shape
+    Hkv, C = kmin.shape[1], kmin.shape[2]
+    G = Hq // Hkv
+    s = np.zeros((B, Hkv, T, C), dtype=np.float64)
+    for b in range(B):
+        for g in range(Hkv):
+            for t in range(T):
+                per_head = np.zeros((G, C))
+                for i in range(G):
+                    qh = q[b, t, g * G + i]                      # [d]
+                    lo = kmin[b, g] * qh                         # [C, d]
+                    hi = kmax[b, g] * qh
+                    per_head[i] = scale * np.maximum(lo, hi).sum(axis=1)
+                if reduce == "mean":
+                    s[b, g, t] = per_head.mean(axis=0)
+                elif reduce == "max":
+                    s[b, g, t] = per_head.max(axis=0)
+                else:
+                    raise ValueError("reduce must be 'mean' or 'max'")
+    return s
+
+
+def minmax_topk(q, kmin, kmax, k: int, scale: float, reduce: str = "mean") -> np.ndarray:
+    """The k chunks with the largest upper-bound score (ties to the lower id), ascending."""
+    return topk_chunks(minmax_scores(q, kmin, kmax, scale, reduce), k)

@@ -614,7 +614,69 @@ def _mla_key_content_only(q, latent, sel, dv, scale):
     return O.sparse_attention(q[..., :dv], latent[..., :dv], latent[..., :dv], sel, 1, scale)
 
 
+# ----------------------------------------------------------------------------
+# min/max chunk summaries and their upper-bound scores
+# ----------------------------------------------------------------------------
+
+def check_minmax(fn):
+    """fn(q, kmin, kmax, scale, reduce) -> scores; pins the bound and its summaries."""
+    fx = golden("minmax_hand.json")
+    mn, mx = O.chunk_minmax(np.array(fx["K"], dtype=np.float64), fx["chunk"])
+    np.testing.assert_array_equal(mn, fx["expected_kmin"])
+    np.testing.assert_array_equal(mx, fx["expected_kmax"])
+    q = np.array(fx["q"], dtype=np.float64)
+    np.testing.assert_allclose(fn(q, mn, mx, fx["scale"], "mean"), fx["expected_scores_mean"], atol=1e-12)
+    np.testing.assert_allclose(fn(q, mn, mx, fx["scale"], "max"), fx["expected_scores_max"], atol=1e-12)
+    np.testing.assert_array_equal(O.topk_chunks(fn(q, mn, mx, fx["scale"], "mean"), fx["k"]),
+                                  fx["expected_topk_mean"])
+
+    rng = np.random.default_rng(21)
+    B, T, Hq, Hkv, d, chunk, C = 2, 2, 4, 2, 6, 4, 9
+    K = rng.standard_normal((B, Hkv, C * chunk, d))
+    q = rng.standard_normal((B, T, Hq, d))
+    mn, mx = O.chunk_minmax(K, chunk)
+    G = Hq // Hkv
+    # one head per KV head: the score bounds every key's dot product in the chunk, and
+    # is reached when the chunk holds the corner the query's signs pick
+    for h in range(Hq):
+        g = h // G
+        s1 = fn(q[:, :, h:h + 1], mn[:, g:g + 1], mx[:, g:g + 1], 0.7, "mean")
+        for b, t, c in itertools.product(range(B), range(T), range(C)):
+            dots = 0.7 * K[b, g, c * chunk:(c + 1) * chunk] @ q[b, t, h]
+            assert s1[b, 0, t, c] >= dots.max() - 1e-12
+    Kc = K.copy()
+    for b, g, c in itertools.product(range(B), range(Hkv), range(C)):
+        qs = q[b, 0, g * G]
+        lo, hi = mn[b, g, c], mx[b, g, c]
+        Kc[b, g, c * chunk] = np.where(qs >= 0, hi, lo)      # the corner is one of the keys
+    mnc, mxc = O.chunk_minmax(Kc, chunk)
+    s1 = fn(q[:, :1, ::G], mnc, mxc, 0.7, "mean")
+    for b, g, c in itertools.product(range(B), range(Hkv), range(C)):
+        dots = 0.7 * Kc[b, g, c * chunk:(c + 1) * chunk] @ q[b, 0, g * G]
+        assert abs(s1[b, g, 0, c] - dots.max()) < 1e-12
+    # chunk 1: the box is the key, the bound is the exact score
+    mn1, mx1 = O.chunk_minmax(K, 1)
+    np.testing.assert_allclose(fn(q, mn1, mx1, 0.3, "mean"), O.chunk_scores(q, K, 0.3, "mean"), atol=1e-12)
+    np.testing.assert_allclose(fn(q, mn1, mx1, 0.3, "max"), O.chunk_scores(q, K, 0.3, "max"), atol=1e-12)
+
+
+def test_minmax_pins():
+    check_minmax(O.minmax_scores)
+
+
+def _minmax_lower_bound(q, kmin, kmax, scale, reduce="mean"):
+    # the smallest dot product in the box instead of the largest
+    return -O.minmax_scores(-np.asarray(q), kmin, kmax, scale, reduce)
+
+
+def _minmax_no_sign_branch(q, kmin, kmax, scale, reduce="mean"):
+    return O.chunk_scores(q, np.asarray(kmax), scale, reduce)
+
+
+
 @pytest.mark.parametrize("check,bad", [
+    (check_minmax, _minmax_lower_bound),
+    (check_minmax, _minmax_no_sign_branch),
     (check_indexer, _indexer_max_over_heads),
     (check_indexer, _indexer_first_head_only),
     (check_mla, _mla_value_from_last_columns),
