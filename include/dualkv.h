@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define DK_ABI_VERSION 6
+#define DK_ABI_VERSION 7
 
 typedef enum {
     DK_OK = 0,
@@ -173,6 +173,45 @@ dk_status dk_score_topk(const float* q, int B, int T, int Hq,
                         const dk_landmark_shadow* shadow,
                         int32_t* topk_idx, float* topk_score,
                         void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * dk_build_minmax - coordinate-wise minimum and maximum key of every chunk.
+ *
+ * OasisKV summary, "Look-ahead Attention": a draft query ranks every block of a
+ * KV head from compressed key summaries, two vectors per block (coordinate-wise
+ * min and max), 1/16 of the key bytes for 32-row chunks.
+ *
+ * K          : keys (k_dtype, DK_BF16 or DK_F32) with strides ks, rows [B, Hkv, L] of d.
+ * kmin, kmax : out, k_dtype [B, Hkv, L/chunk, d] contiguous; the exact minima and
+ *              maxima of the chunk's keys.
+ * Errors     : DK_ERR_INVALID_ARG unless sizes >= 1, L % chunk == 0 and pointers
+ *              non-NULL; DK_ERR_UNSUPPORTED unless d is 64 or 128 and the 16-byte
+ *              alignment rule holds.
+ */
+dk_status dk_build_minmax(const void* K, dk_dtype k_dtype, dk_strides ks, int B, int Hkv, int L, int d,
+                          int chunk, void* kmin, void* kmax, void* stream);
+
+/*
+ * dk_score_topk_minmax - each query's k best chunks by upper-bound scores from
+ * min/max summaries, optionally with the union of the T sets.
+ *
+ * For query head h and chunk c the score bounds every key of the chunk:
+ *   U = scale * sum_d max(q[b,t,h,d] * kmin[b,g,c,d], q[b,t,h,d] * kmax[b,g,c,d]),
+ * combined over the group's heads by `reduce` (mean or max) like chunk scores;
+ * topk_idx as in dk_score_topk (ties to the lower id, ascending).  With
+ * union_ids non-NULL the union outputs of dk_union_select are written too.
+ *
+ * kmin, kmax : summaries (dtype) with strides ss, rows [B, Hkv, C] of d.
+ * ws         : dk_index_topk_workspace_size(B, Hkv, T, C) bytes; contents ignored.
+ * Errors     : those of dk_score_topk; DK_ERR_UNSUPPORTED unless d is 64 or 128,
+ *              C % 4 == 0, C <= 2^28, G*T is a power of two <= 8 for max, and the
+ *              16-byte alignment rule holds; union limits as dk_union_select.
+ */
+dk_status dk_score_topk_minmax(const float* q, int B, int T, int Hq, const void* kmin, const void* kmax,
+                               dk_dtype dtype, dk_strides ss, int Hkv, int C, int d, int k, float scale,
+                               dk_group_reduce reduce, int32_t* topk_idx, float* topk_score,
+                               int32_t* union_ids, uint8_t* member, int32_t* union_count, int32_t* overlap,
+                               void* ws, size_t ws_bytes, void* stream);
 
 /*
  * dk_score_topk_union - dk_score_topk and dk_union_select (without a cache

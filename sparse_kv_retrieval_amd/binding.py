@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libdualkv.so")
 DK_OK, DK_ERR_INVALID_ARG, DK_ERR_UNSUPPORTED, DK_ERR_HIP = 0, 1, 2, 3
 DK_F32, DK_BF16 = 0, 1
 DK_REDUCE_MEAN, DK_REDUCE_MAX = 0, 1
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 _STATUS = {0: "DK_OK", 1: "DK_ERR_INVALID_ARG", 2: "DK_ERR_UNSUPPORTED", 3: "DK_ERR_HIP"}
 
@@ -62,6 +62,9 @@ EXPORTS = [
     ("dk_build_landmark_shadow", _I, [_P, _S, _I, _I, _I, _I, _P, _P, _P]),
     ("dk_score_topk_workspace_size", _Z, [_I, _I, _I, _I, _I, _I]),
     ("dk_index_topk_workspace_size", _Z, [_I, _I, _I, _I]),
+    ("dk_build_minmax", _I, [_P, _I, _S, _I, _I, _I, _I, _I, _P, _P, _P]),
+    ("dk_score_topk_minmax", _I, [_P, _I, _I, _I, _P, _P, _I, _S, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P,
+                                  _P, _Z, _P]),
     ("dk_score_topk", _I, [_P, _I, _I, _I, _P, _I, _S, _I, _I, _I, _I, _F, _I,
                            ctypes.POINTER(dk_landmark_shadow), _P, _P, _P, _Z, _P]),
     ("dk_score_topk_union", _I, [_P, _I, _I, _I, _P, _I, _S, _I, _I, _I, _I, _F, _I,
@@ -199,6 +202,51 @@ def score_topk(q: torch.Tensor, lm: torch.Tensor, k: int, scale: float, reduce: 
                              float(scale), int(reduce), csh, _ptr(topk_idx), _ptr(topk_score),
                              _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
                              _stream(stream)))
+    return topk_idx, topk_score
+
+
+def build_minmax(K: torch.Tensor, chunk: int, kmin=None, kmax=None, stream=None):
+    """Coordinate-wise min and max key of every chunk, [B, Hkv, L/chunk, d] in K's dtype."""
+    B, Hkv, L, d = K.shape
+    C = L // chunk
+    if kmin is None:
+        kmin = torch.empty(B, Hkv, C, d, dtype=K.dtype, device=K.device)
+    if kmax is None:
+        kmax = torch.empty(B, Hkv, C, d, dtype=K.dtype, device=K.device)
+    _check(lib.dk_build_minmax(_ptr(K), _dtype(K), pool_strides(K), B, Hkv, L, d, chunk, _ptr(kmin), _ptr(kmax),
+                               _stream(stream)))
+    return kmin, kmax
+
+
+def score_topk_minmax(q: torch.Tensor, kmin: torch.Tensor, kmax: torch.Tensor, k: int, scale: float,
+                      reduce: int = DK_REDUCE_MEAN, topk_idx=None, topk_score=None, union=False, union_ids=None,
+                      member=None, count=None, overlap=None, ws=None, want_scores=True, stream=None):
+    """Top-k chunks by min/max upper-bound scores; with union=True also the union outputs."""
+    B, T, Hq, d = q.shape
+    _, Hkv, C, _ = kmin.shape
+    _need(q, torch.float32, (B, T, Hq, d), "q")
+    if kmin.stride() != kmax.stride() or kmin.dtype != kmax.dtype:
+        raise ValueError("kmin and kmax must share dtype and layout")
+    dev = q.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    if topk_idx is None:
+        topk_idx = torch.empty(B, Hkv, T, k, **i32)
+    if topk_score is None and want_scores:
+        topk_score = torch.empty(B, Hkv, T, k, dtype=torch.float32, device=dev)
+    if union:
+        union_ids = torch.empty(B, Hkv, T * k, **i32) if union_ids is None else union_ids
+        member = torch.empty(B, Hkv, T * k, dtype=torch.uint8, device=dev) if member is None else member
+        count = torch.empty(B, Hkv, **i32) if count is None else count
+        overlap = torch.empty(B, Hkv, **i32) if overlap is None else overlap
+    nbytes = index_topk_workspace_size(B, Hkv, T, C)
+    if ws is None:
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _check(lib.dk_score_topk_minmax(_ptr(q), B, T, Hq, _ptr(kmin), _ptr(kmax), _dtype(kmin), pool_strides(kmin),
+                                    Hkv, C, d, k, float(scale), int(reduce), _ptr(topk_idx), _ptr(topk_score),
+                                    _ptr(union_ids), _ptr(member), _ptr(count), _ptr(overlap), _ptr(ws),
+                                    ws.numel() * ws.element_size(), _stream(stream)))
+    if union:
+        return topk_idx, topk_score, union_ids, member, count, overlap
     return topk_idx, topk_score
 
 

@@ -78,6 +78,24 @@ dk_status dk_build_landmarks(const void* K, dk_dtype k_dtype, dk_strides ks, int
     return e == hipSuccess ? DK_OK : hip_fail(e, "dk_build_landmarks");
 }
 
+dk_status dk_build_minmax(const void* K, dk_dtype k_dtype, dk_strides ks, int B, int Hkv, int L, int d, int chunk,
+                          void* kmin, void* kmax, void* stream) {
+    g_err.clear();
+    const char* fn = "dk_build_minmax";
+    const int esz = dtype_size(k_dtype);
+    DK_REQUIRE(K && kmin && kmax, DK_ERR_INVALID_ARG, "%s: K, kmin and kmax must be non-NULL", fn);
+    DK_REQUIRE(esz != 0, DK_ERR_INVALID_ARG, "%s: unknown k_dtype %d", fn, (int)k_dtype);
+    DK_REQUIRE(B >= 1 && Hkv >= 1 && L >= 1 && d >= 1 && chunk >= 1, DK_ERR_INVALID_ARG,
+               "%s: B, Hkv, L, d, chunk must be >= 1", fn);
+    DK_REQUIRE(L % chunk == 0, DK_ERR_INVALID_ARG, "%s: L (%d) %% chunk (%d) != 0", fn, L, chunk);
+    DK_REQUIRE(d == 64 || d == 128, DK_ERR_UNSUPPORTED, "%s: d must be 64 or 128 (got %d)", fn, d);
+    DK_REQUIRE(aligned16(K) && aligned16(kmin) && aligned16(kmax) && strides_ok(ks, esz), DK_ERR_UNSUPPORTED,
+               "%s: K, kmin, kmax and K's strides must be 16-byte aligned", fn);
+    DK_REQUIRE((int64_t)B * Hkv * (L / chunk) < (int64_t)1 << 40, DK_ERR_INVALID_ARG, "%s: too many chunks", fn);
+    hipError_t e = dk::launch_build_minmax(K, k_dtype, ks, B, Hkv, L, d, chunk, kmin, kmax, (hipStream_t)stream);
+    return e == hipSuccess ? DK_OK : hip_fail(e, fn);
+}
+
 dk_status dk_build_landmark_shadow(const float* lm, dk_strides ls, int B, int Hkv, int C, int d,
                                    uint16_t* lm16, float* norm_max, void* stream) {
     g_err.clear();
@@ -238,6 +256,50 @@ dk_status dk_score_topk_union(const float* q, int B, int T, int Hq, const void* 
     const dk::UnionOut un{union_ids, member, union_count, overlap};
     hipError_t e = dk::launch_score_topk(q, B, T, Hq, (const float*)lm, ls, Hkv, C, d, k, scale, reduce,
                                          shadow, topk_idx, topk_score, ws, plan, &un, (hipStream_t)stream);
+    return e == hipSuccess ? DK_OK : hip_fail(e, fn);
+}
+
+dk_status dk_score_topk_minmax(const float* q, int B, int T, int Hq, const void* kmin, const void* kmax,
+                               dk_dtype dtype, dk_strides ss, int Hkv, int C, int d, int k, float scale,
+                               dk_group_reduce reduce, int32_t* topk_idx, float* topk_score, int32_t* union_ids,
+                               uint8_t* member, int32_t* union_count, int32_t* overlap, void* ws, size_t ws_bytes,
+                               void* stream) {
+    g_err.clear();
+    const char* fn = "dk_score_topk_minmax";
+    const int esz = dtype_size(dtype);
+    DK_REQUIRE(q && kmin && kmax && topk_idx, DK_ERR_INVALID_ARG, "%s: q, kmin, kmax, topk_idx must be non-NULL", fn);
+    DK_REQUIRE(esz != 0, DK_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
+    DK_REQUIRE(B >= 1 && Hq >= 1 && Hkv >= 1 && C >= 1 && d >= 1, DK_ERR_INVALID_ARG,
+               "%s: B, Hq, Hkv, C, d must be >= 1", fn);
+    DK_REQUIRE(T == 1 || T == 2, DK_ERR_INVALID_ARG, "%s: T must be 1 or 2 (got %d)", fn, T);
+    DK_REQUIRE(Hq % Hkv == 0, DK_ERR_INVALID_ARG, "%s: Hq (%d) %% Hkv (%d) != 0", fn, Hq, Hkv);
+    DK_REQUIRE(k >= 1 && k <= C, DK_ERR_INVALID_ARG, "%s: need 1 <= k (%d) <= C (%d)", fn, k, C);
+    DK_REQUIRE(reduce == DK_REDUCE_MEAN || reduce == DK_REDUCE_MAX, DK_ERR_INVALID_ARG, "%s: unknown reduce %d", fn,
+               (int)reduce);
+    DK_REQUIRE(std::isfinite(scale), DK_ERR_INVALID_ARG, "%s: scale must be finite", fn);
+    DK_REQUIRE(!union_ids || (member && union_count), DK_ERR_INVALID_ARG,
+               "%s: with union_ids, member and union_count must be non-NULL", fn);
+    DK_REQUIRE(d == 64 || d == 128, DK_ERR_UNSUPPORTED, "%s: d must be 64 or 128 (got %d)", fn, d);
+    DK_REQUIRE(C % 4 == 0 && C <= (1 << 28), DK_ERR_UNSUPPORTED, "%s: needs C %% 4 == 0 and C <= 2^28 (got %d)",
+               fn, C);
+    const int G = Hq / Hkv;
+    if (reduce == DK_REDUCE_MAX) {
+        const int nq = G * T;
+        DK_REQUIRE(nq <= 8 && (nq & (nq - 1)) == 0, DK_ERR_UNSUPPORTED,
+                   "%s: max reduction needs G*T a power of two <= 8 (got %d)", fn, nq);
+    }
+    DK_REQUIRE(aligned16(q) && aligned16(kmin) && aligned16(kmax) && strides_ok(ss, esz), DK_ERR_UNSUPPORTED,
+               "%s: q, kmin, kmax and the summaries' strides must be 16-byte aligned", fn);
+    const dk::IndexPlan plan = dk::plan_index_topk(B, Hkv, T, C);
+    DK_REQUIRE(ws && ws_bytes >= plan.ws_bytes, DK_ERR_INVALID_ARG, "%s: workspace needs %zu bytes (got %zu)", fn,
+               plan.ws_bytes, ws_bytes);
+    if (union_ids) {
+        const dk_status s = check_union(fn, T, k, 0, false);
+        if (s != DK_OK) return s;
+    }
+    const dk::UnionOut un{union_ids, member, union_count, overlap};
+    hipError_t e = dk::launch_minmax_topk(q, B, T, Hq, kmin, kmax, dtype, ss, Hkv, C, d, k, scale, reduce, topk_idx,
+                                          topk_score, ws, plan, union_ids ? &un : nullptr, (hipStream_t)stream);
     return e == hipSuccess ? DK_OK : hip_fail(e, fn);
 }
 

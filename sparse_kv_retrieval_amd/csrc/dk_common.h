@@ -197,6 +197,7 @@ hipError_t launch_score_topk(const float* q, int B, int T, int Hq, const float* 
 // Token-level indexer on bf16 keys (k_indexer.hip): fp32 scores of every token in
 // the workspace, then an exact threshold select per (b, g, t).
 struct IndexPlan {
+    int rows_per_block;  // score rows (tokens or chunks) per scoring block
     int blocks_per_bg;   // scoring blocks per (b, g)
     size_t off_min;      // byte offsets of the per-block score minima / maxima
     size_t off_max;
@@ -204,6 +205,18 @@ struct IndexPlan {
     size_t ws_bytes;
 };
 IndexPlan plan_index_topk(int B, int Hkv, int T, int C);
+// The exact selection over fp32 score rows [B*Hkv*T][C] with per-block ranges
+// (the plan's layout), optionally with the union of each (b, g)'s T sets.
+hipError_t launch_select_rows(const float* scores, const float* bmin, const float* bmax, int blocks_per_row, int B,
+                              int Hkv, int T, int C, int k, int32_t* topk_idx, float* topk_score, const UnionOut* un,
+                              uint32_t* arrivals, hipStream_t st);
+// Min/max chunk summaries and the top-k by their upper-bound scores (k_minmax.hip).
+hipError_t launch_build_minmax(const void* K, dk_dtype dt, dk_strides ks, int B, int Hkv, int L, int d, int chunk,
+                               void* kmin, void* kmax, hipStream_t st);
+hipError_t launch_minmax_topk(const float* q, int B, int T, int Hq, const void* kmin, const void* kmax, dk_dtype dt,
+                              dk_strides ss, int Hkv, int C, int d, int k, float scale, dk_group_reduce reduce,
+                              int32_t* topk_idx, float* topk_score, void* ws, const IndexPlan& plan,
+                              const UnionOut* un, hipStream_t st);
 hipError_t launch_index_topk(const float* q, int B, int T, int Hq, const uint16_t* keys, dk_strides ks, int Hkv,
                              int C, int d, int k, float scale, int32_t* topk_idx, float* topk_score, void* ws,
                              const IndexPlan& plan, const UnionOut* un, hipStream_t st);

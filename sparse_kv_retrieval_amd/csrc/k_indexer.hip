@@ -479,6 +479,7 @@ __global__ __launch_bounds__(kSelThreads) void k_idx_select(const float* __restr
 
 IndexPlan plan_index_topk(int B, int Hkv, int T, int C) {
     IndexPlan p{};
+    p.rows_per_block = kScoreRows;
     const int64_t rows = (int64_t)B * Hkv * T;
     p.blocks_per_bg = (C + kScoreRows - 1) / kScoreRows;
     const size_t sbytes = (((size_t)rows * C * 4) + 255) & ~(size_t)255;
@@ -511,9 +512,16 @@ hipError_t launch_index_topk(const float* q, int B, int T, int Hq, const uint16_
 #undef DK_IDX_SCORE
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    return launch_select_rows(scores, bmin, bmax, plan.blocks_per_bg, B, Hkv, T, C, k, topk_idx, topk_score, un,
+                              arrivals, st);
+}
+
+hipError_t launch_select_rows(const float* scores, const float* bmin, const float* bmax, int blocks_per_row, int B,
+                              int Hkv, int T, int C, int k, int32_t* topk_idx, float* topk_score, const UnionOut* un,
+                              uint32_t* arrivals, hipStream_t st) {
     const UnionOut uo = un ? *un : UnionOut{nullptr, nullptr, nullptr, nullptr};
-    hipLaunchKernelGGL(k_idx_select, dim3((unsigned)(bg * T)), dim3(kSelThreads), 0, st, scores, bmin, bmax,
-                       plan.blocks_per_bg, T, C, k, topk_idx, topk_score, uo, arrivals);
+    hipLaunchKernelGGL(k_idx_select, dim3((unsigned)((int64_t)B * Hkv * T)), dim3(kSelThreads), 0, st, scores, bmin,
+                       bmax, blocks_per_row, T, C, k, topk_idx, topk_score, uo, arrivals);
     return hipGetLastError();
 }
 

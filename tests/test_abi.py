@@ -27,14 +27,14 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(lib, n), n
     assert {n for n, _, _ in b.EXPORTS} == set(names)
 
 
 def test_abi_version():
-    assert lib.dk_abi_version() == 6
+    assert lib.dk_abi_version() == 7
 
 
 def err():
@@ -255,3 +255,34 @@ def test_attention_workspace_sizes():
     # a single (b, g) with few entries: one range, no workspace
     assert lib.dk_attn_workspace_size(1, 1, 2, 4, 128, 4, 32) == 0
     assert lib.dk_attn_workspace_size(64, 8, 2, 30, 128, 128, 32) == 0
+
+
+def minmax_topk(q=FAKE, B=2, T=2, Hq=32, mn=FAKE, mx=FAKE, dt=1, ss=b.dk_strides(1 << 19, 1 << 16, 128), Hkv=8,
+                C=1024, d=128, k=64, scale=0.088, reduce=0, idx=FAKE, sc=FAKE, uid=NULL, mem=NULL, cnt=NULL,
+                ov=NULL, ws=FAKE, wsb=1 << 30):
+    return lib.dk_score_topk_minmax(q, B, T, Hq, mn, mx, dt, ss, Hkv, C, d, k, scale, reduce, idx, sc, uid, mem,
+                                    cnt, ov, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=NULL), 1), (dict(mn=NULL), 1), (dict(idx=NULL), 1), (dict(T=3), 1), (dict(k=0), 1),
+    (dict(k=1025), 1), (dict(reduce=4), 1), (dict(scale=float("inf")), 1), (dict(dt=5), 1),
+    (dict(uid=FAKE), 1), (dict(d=96), 2), (dict(C=1022, k=8), 2), (dict(reduce=1, Hq=64), 2),
+    (dict(mx=MIS), 2),
+    (dict(wsb=16), 1), (dict(ws=NULL), 1), (dict(uid=FAKE, mem=FAKE, cnt=FAKE, k=4000, C=8192), 2),
+])
+def test_minmax_topk_rejects(kw, status):
+    assert minmax_topk(**kw) == status, err()
+    assert err().startswith("dk_score_topk_minmax")
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=NULL), 1), (dict(L=1000), 1), (dict(d=96), 2), (dict(mn=MIS), 2), (dict(dt=9), 1),
+])
+def test_build_minmax_rejects(kw, status):
+    a = dict(K=FAKE, dt=1, ks=b.dk_strides(1 << 22, 1 << 19, 128), B=2, Hkv=8, L=4096, d=128, chunk=32, mn=FAKE,
+             mx=FAKE)
+    a.update(kw)
+    assert lib.dk_build_minmax(a["K"], a["dt"], a["ks"], a["B"], a["Hkv"], a["L"], a["d"], a["chunk"], a["mn"],
+                               a["mx"], None) == status, err()
+    assert err().startswith("dk_build_minmax")
