@@ -52,6 +52,16 @@ landmarks, and one latent head serves every query head.  Readings for it:
   key, the first dv columns of the same row as the value, and the scale the
   caller passes (1/sqrt of the key width in the workloads).
 
+Selection variants replace the landmark score or the fixed budget k:
+* min/max chunk summaries (OasisKV, "Look-ahead Attention"): a chunk's score
+  is the largest scaled dot product any key in the box between its coordinate-
+  wise minimum and maximum can reach, combined over heads like chunk scores;
+* coverage budgets (MOIRA, abstract): a chunk's estimated attention mass is the
+  softmax of its chunk score over the row; the kept set is the shortest prefix
+  of the (score descending, id ascending) order whose mass reaches gamma, at
+  least one chunk and at most k_max (the caller's buffer); the union of the two
+  queries' sets is taken over their own counts.
+
 Parity of each function is pinned by the not-gpu tests (closed forms, brute
 force on tiny inputs, a library attention routine, hand-worked fixtures under
 tests/golden/).  The absolute prediction-accuracy level on synthetic data has
@@ -458,3 +468,69 @@ def minmax_scores(q: np.ndarray, kmin: np.ndarray, kmax: np.ndarray, scale: floa
 def minmax_topk(q, kmin, kmax, k: int, scale: float, reduce: str = "mean") -> np.ndarray:
     """The k chunks with the largest upper-bound score (ties to the lower id), ascending."""
     return topk_chunks(minmax_scores(q, kmin, kmax, scale, reduce), k)
+
+
+# ----------------------------------------------------------------------------
+# selection variants: coverage budgets (estimated attention mass)
+# ----------------------------------------------------------------------------
+
+def coverage_select(s: np.ndarray, gamma: float, k_max: int):
+    """Smallest set of chunks whose estimated attention mass reaches gamma.
+
+    MOIRA (abstract): per request, layer, KV head and step a coverage rule keeps
+    the smallest set of pages whose estimated attention mass reaches a fraction
+    gamma.  The estimate used here is the softmax of the chunk scores (the
+    chunk's landmark logit), and the set is the shortest prefix of the chunks in
+    (score descending, id ascending) order whose mass reaches gamma of the
+    total, at least 1 and at most k_max chunks (the output buffer).
+    s: [..., C].  Returns (idx [..., k_max] ascending ids, -1 padded;
+    count [...] chunks kept).
+    """
+    s = np.asarray(s, dtype=np.float64)
+    C = s.shape[-1]
+    if not 1 <= k_max <= C:
+        raise ValueError("need 1 <= k_max <= C")
+    if not 0.0 < gamma <= 1.0:
+        raise ValueError("need 0 < gamma <= 1")
+    flat = s.reshape(-1, C)
+    idx = np.full((flat.shape[0], k_max), -1, dtype=np.int64)
+    count = np.zeros(flat.shape[0], dtype=np.int64)
+    ids = np.arange(C)
+    for r in range(flat.shape[0]):
+        w = np.exp(flat[r] - flat[r].max())
+        mass = w / w.sum()
+        order = np.lexsort((ids, -flat[r]))
+        total = 0.0
+        n = 0
+        while n < C:
+            total += mass[order[n]]
+            n += 1
+            if total >= gamma:
+                break
+        n = max(1, min(n, k_max))
+        idx[r, :n] = np.sort(order[:n])
+        count[r] = n
+    return idx.reshape(s.shape[:-1] + (k_max,)), count.reshape(s.shape[:-1])
+
+
+def union_select_ragged(idx: np.ndarray, count: np.ndarray):
+    """union_select for sets of different sizes: row t of idx[b, g] holds count[b, g, t] ids.
+
+    Returns the same four arrays as union_select, with T * k_max union slots.
+    """
+    idx = np.asarray(idx)
+    B, H, T, k = idx.shape
+    union_ids = np.full((B, H, T * k), -1, dtype=np.int64)
+    member = np.zeros((B, H, T * k), dtype=np.uint8)
+    ucount = np.zeros((B, H), dtype=np.int64)
+    overlap = np.zeros((B, H), dtype=np.int64)
+    for b in range(B):
+        for g in range(H):
+            sets = [set(int(c) for c in idx[b, g, t, :int(count[b, g, t])]) for t in range(T)]
+            u = sorted(set().union(*sets))
+            ucount[b, g] = len(u)
+            for i, c in enumerate(u):
+                union_ids[b, g, i] = c
+                member[b, g, i] = sum(1 << t for t in range(T) if c in sets[t])
+            overlap[b, g] = len(sets[0] & sets[1]) if T == 2 else len(sets[0])
+    return union_ids, member, ucount, overlap

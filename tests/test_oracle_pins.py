@@ -674,7 +674,155 @@ def _minmax_no_sign_branch(q, kmin, kmax, scale, reduce="mean"):
 
 
 
+# ----------------------------------------------------------------------------
+# coverage budgets: smallest set of chunks reaching a fraction of the mass
+# ----------------------------------------------------------------------------
+
+def check_coverage(fn):
+    """fn(s, gamma, k_max) -> (idx, count); pins the coverage rule."""
+    fx = golden("coverage_hand.json")
+    s = np.array(fx["scores"], dtype=np.float64)
+    for case in fx["cases"]:
+        idx, n = fn(s, case["gamma"], case["k_max"])
+        np.testing.assert_array_equal(idx, case["idx"], err_msg=str(case))
+        np.testing.assert_array_equal(n, case["count"], err_msg=str(case))
+
+    # brute force over every subset: the count is the size of the smallest set whose
+    # softmax mass reaches gamma (at most k_max), and the kept set has the largest
+    # mass among the sets of that size
+    rng = np.random.default_rng(31)
+    checked = 0
+    for _ in range(300):
+        C = int(rng.integers(1, 8))
+        row = np.round(rng.standard_normal(C) * 2) / 2          # half-steps: ties occur
+        gamma = float(rng.uniform(0.05, 1.0))
+        k_max = int(rng.integers(1, C + 1))
+        m = np.exp(row - row.max())
+        m = m / m.sum()
+        sub = [(sum(m[list(S)]), S) for r in range(1, C + 1) for S in itertools.combinations(range(C), r)]
+        if min(abs(v - gamma) for v, _ in sub) < 1e-9:
+            continue                                           # a boundary the sum order decides
+        n_bf = min(len(S) for v, S in sub if v >= gamma)
+        n_bf = min(n_bf, k_max)
+        idx, n = fn(row[None], gamma, k_max)
+        assert int(n[0]) == n_bf, (row, gamma, k_max, n, n_bf)
+        kept = idx[0, :n_bf]
+        assert np.all(np.diff(kept) > 0) and np.all(idx[0, n_bf:] == -1)
+        best = max(v for v, S in sub if len(S) == n_bf)
+        assert sum(m[kept]) >= best - 1e-12
+        checked += 1
+    assert checked > 200
+
+    rows = rng.standard_normal((3, 5, 40)) * 3
+    # softmax masses: adding a constant to every score changes nothing
+    for gamma in (0.2, 0.6, 0.95):
+        a = fn(rows, gamma, 40)
+        b = fn(rows + 3.7, gamma, 40)
+        np.testing.assert_array_equal(a[0], b[0])
+        np.testing.assert_array_equal(a[1], b[1])
+    # a tiny gamma keeps the best chunk only; gamma = 1 keeps k_max chunks
+    idx, n = fn(rows, 1e-9, 7)
+    assert np.all(n == 1) and np.all(idx[..., 0] == rows.argmax(axis=-1))
+    idx, n = fn(rows, 1.0, 7)
+    assert np.all(n == 7)
+    np.testing.assert_array_equal(idx, O.topk_chunks(rows, 7))
+    # equal scores: masses 1/C, the first ceil(gamma C) ids
+    idx, n = fn(np.zeros((1, 16)), 3 / 8, 16)
+    assert n[0] == 6 and idx[0, :6].tolist() == list(range(6))
+    # one dominant chunk carries nearly all of the mass
+    row = np.zeros((1, 9))
+    row[0, 4] = 40.0
+    idx, n = fn(row, 0.99, 9)
+    assert n[0] == 1 and idx[0, 0] == 4
+
+
+def test_coverage_pins():
+    check_coverage(O.coverage_select)
+
+
+def test_coverage_rejects():
+    with pytest.raises(ValueError):
+        O.coverage_select(np.zeros((1, 4)), 0.0, 2)
+    with pytest.raises(ValueError):
+        O.coverage_select(np.zeros((1, 4)), 1.5, 2)
+    with pytest.raises(ValueError):
+        O.coverage_select(np.zeros((1, 4)), 0.5, 5)
+
+
+def check_union_ragged(fn):
+    """fn(idx, count) -> union_select's four arrays, for rows of different sizes."""
+    rng = np.random.default_rng(32)
+    C, k = 30, 8
+    idx = np.stack([np.sort(rng.choice(C, k, replace=False)) for _ in range(12)]).reshape(2, 3, 2, k)
+    # full rows: the same as the fixed-size union
+    full = fn(idx, np.full((2, 3, 2), k))
+    for a, b in zip(full, O.union_select(idx)):
+        np.testing.assert_array_equal(a[..., :b.shape[-1]], b)
+        assert np.all(a[..., b.shape[-1]:] <= 0)
+    # ragged rows: ids past a row's count are padding and take no part
+    count = rng.integers(1, k + 1, size=(2, 3, 2))
+    padded = idx.copy()
+    for b, g, t in itertools.product(range(2), range(3), range(2)):
+        padded[b, g, t, count[b, g, t]:] = -1
+    u, m, c, o = fn(padded, count)
+    for b, g in itertools.product(range(2), range(3)):
+        sets = [set(idx[b, g, t, :count[b, g, t]].tolist()) for t in range(2)]
+        n = c[b, g]
+        assert n == len(sets[0] | sets[1]) == count[b, g, 0] + count[b, g, 1] - o[b, g]
+        assert o[b, g] == len(sets[0] & sets[1])
+        ids = u[b, g, :n]
+        assert np.all(np.diff(ids) > 0) and np.all(u[b, g, n:] == -1) and np.all(m[b, g, n:] == 0)
+        for t in range(2):
+            assert set(ids[(m[b, g, :n] >> t) & 1 == 1].tolist()) == sets[t]
+
+
+def test_union_ragged_pins():
+    check_union_ragged(O.union_select_ragged)
+
+
+def _coverage_strict(s, gamma, k_max):
+    # stops only once the mass exceeds gamma
+    return O.coverage_select(s, min(1.0, gamma * (1 + 1e-12)), k_max)
+
+
+def _coverage_raw_scores(s, gamma, k_max):
+    # mass proportional to the shifted scores instead of their exponentials
+    s = np.asarray(s, dtype=np.float64)
+    lin = np.log(s - s.min(axis=-1, keepdims=True) + 1e-3)
+    return O.coverage_select(lin, gamma, k_max)
+
+
+def _coverage_ties_high_id(s, gamma, k_max):
+    s = np.asarray(s, dtype=np.float64)
+    idx, n = O.coverage_select(s[..., ::-1], gamma, k_max)
+    C = s.shape[-1]
+    out = np.where(idx >= 0, C - 1 - idx, -1)
+    out = np.sort(np.where(out >= 0, out, C + 1), axis=-1)
+    return np.where(out <= C, out, -1), n
+
+
+def _coverage_stop_before(s, gamma, k_max):
+    # keeps the chunks before the one that reaches gamma
+    s = np.asarray(s, dtype=np.float64)
+    idx, n = O.coverage_select(s, gamma, k_max)
+    n2 = np.maximum(n - 1, 1)
+    res = np.full(idx.shape, -1).reshape(-1, idx.shape[-1])
+    rows = s.reshape(-1, s.shape[-1])
+    for r, c in enumerate(n2.reshape(-1)):
+        res[r, :c] = np.sort(O.topk_chunks(rows[r:r + 1], int(c))[0])
+    return res.reshape(idx.shape), n2
+
+
+def _union_ragged_ignores_count(idx, count):
+    return O.union_select_ragged(idx, np.full(np.asarray(count).shape, np.asarray(idx).shape[-1]))
+
+
 @pytest.mark.parametrize("check,bad", [
+    (check_coverage, _coverage_strict),
+    (check_coverage, _coverage_raw_scores),
+    (check_coverage, _coverage_ties_high_id),
+    (check_coverage, _coverage_stop_before),
+    (check_union_ragged, _union_ragged_ignores_count),
     (check_minmax, _minmax_lower_bound),
     (check_minmax, _minmax_no_sign_branch),
     (check_indexer, _indexer_max_over_heads),
