@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define DK_ABI_VERSION 7
+#define DK_ABI_VERSION 8
 
 typedef enum {
     DK_OK = 0,
@@ -212,6 +212,48 @@ dk_status dk_score_topk_minmax(const float* q, int B, int T, int Hq, const void*
                                dk_group_reduce reduce, int32_t* topk_idx, float* topk_score,
                                int32_t* union_ids, uint8_t* member, int32_t* union_count, int32_t* overlap,
                                void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * dk_score_coverage - for each query, the smallest set of chunks whose estimated
+ * attention mass reaches a fraction gamma, optionally with the union of the T
+ * sets.
+ *
+ * MOIRA (abstract): per request, layer, KV head and step a coverage rule keeps
+ * the smallest set of pages whose estimated attention mass reaches gamma.  The
+ * estimate here is the softmax over the row of the chunk scores of
+ * dk_score_topk (landmark dot products combined over the group's heads by
+ * `reduce`, times scale); the set is the shortest prefix of the chunks in
+ * (score descending, id ascending) order whose mass reaches gamma * total, at
+ * least 1 and at most k_max chunks (gamma = 1: the k_max best).
+ *
+ * q          : fp32 [B, T, Hq, d] contiguous.
+ * lm         : landmarks (lm_dtype, DK_F32 or DK_BF16) with strides ls, rows
+ *              [B, Hkv, C] of d.
+ * sel_idx    : out, int32 [B, Hkv, T, k_max]: the kept chunk ids ascending, then -1.
+ * sel_count  : out, int32 [B, Hkv, T]: chunks kept (1..k_max).
+ * sel_score  : out or NULL, fp32 [B, Hkv, T, k_max]: the fp32 chunk scores of the
+ *              kept ids, then -inf.
+ * union_ids, member, union_count, overlap : NULL, or the outputs of
+ *              dk_union_select with T*k_max slots per (b, g): the union of the T
+ *              kept sets (ascending, then -1), member bits (bit t: in query t's
+ *              set; 0 on padding), its size, and the size of the intersection.
+ * ws         : dk_coverage_workspace_size(B, Hkv, T, C) bytes; contents ignored.
+ * Rounding   : masses and their sums are fp32; a set whose mass lands within
+ *              fp32 rounding of gamma * total may differ by one chunk from an
+ *              exact evaluation.  Equal inputs give equal outputs.
+ * Errors     : DK_ERR_INVALID_ARG unless sizes >= 1, T is 1 or 2, Hq % Hkv == 0,
+ *              1 <= k_max <= C, 0 < gamma <= 1, scale finite, q, lm, sel_idx,
+ *              sel_count non-NULL (and member, union_count with union_ids),
+ *              ws_bytes large enough; DK_ERR_UNSUPPORTED unless d is 64 or 128,
+ *              C <= 16384, G*T is a power of two <= 8 for max, and the 16-byte
+ *              alignment rule holds.  Scores must be finite (not checked).
+ */
+size_t dk_coverage_workspace_size(int B, int Hkv, int T, int C);
+dk_status dk_score_coverage(const float* q, int B, int T, int Hq, const void* lm, dk_dtype lm_dtype,
+                            dk_strides ls, int Hkv, int C, int d, float scale, dk_group_reduce reduce,
+                            float gamma, int k_max, int32_t* sel_idx, int32_t* sel_count, float* sel_score,
+                            int32_t* union_ids, uint8_t* member, int32_t* union_count, int32_t* overlap,
+                            void* ws, size_t ws_bytes, void* stream);
 
 /*
  * dk_score_topk_union - dk_score_topk and dk_union_select (without a cache

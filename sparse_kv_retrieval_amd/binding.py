@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libdualkv.so")
 DK_OK, DK_ERR_INVALID_ARG, DK_ERR_UNSUPPORTED, DK_ERR_HIP = 0, 1, 2, 3
 DK_F32, DK_BF16 = 0, 1
 DK_REDUCE_MEAN, DK_REDUCE_MAX = 0, 1
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 _STATUS = {0: "DK_OK", 1: "DK_ERR_INVALID_ARG", 2: "DK_ERR_UNSUPPORTED", 3: "DK_ERR_HIP"}
 
@@ -65,6 +65,9 @@ EXPORTS = [
     ("dk_build_minmax", _I, [_P, _I, _S, _I, _I, _I, _I, _I, _P, _P, _P]),
     ("dk_score_topk_minmax", _I, [_P, _I, _I, _I, _P, _P, _I, _S, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P,
                                   _P, _Z, _P]),
+    ("dk_coverage_workspace_size", _Z, [_I, _I, _I, _I]),
+    ("dk_score_coverage", _I, [_P, _I, _I, _I, _P, _I, _S, _I, _I, _I, _F, _I, _F, _I, _P, _P, _P, _P, _P, _P, _P,
+                               _P, _Z, _P]),
     ("dk_score_topk", _I, [_P, _I, _I, _I, _P, _I, _S, _I, _I, _I, _I, _F, _I,
                            ctypes.POINTER(dk_landmark_shadow), _P, _P, _P, _Z, _P]),
     ("dk_score_topk_union", _I, [_P, _I, _I, _I, _P, _I, _S, _I, _I, _I, _I, _F, _I,
@@ -248,6 +251,45 @@ def score_topk_minmax(q: torch.Tensor, kmin: torch.Tensor, kmax: torch.Tensor, k
     if union:
         return topk_idx, topk_score, union_ids, member, count, overlap
     return topk_idx, topk_score
+
+
+def coverage_workspace_size(B, Hkv, T, C) -> int:
+    return int(lib.dk_coverage_workspace_size(B, Hkv, T, C))
+
+
+def score_coverage(q: torch.Tensor, lm: torch.Tensor, gamma: float, k_max: int, scale: float,
+                   reduce: int = DK_REDUCE_MEAN, sel_idx=None, sel_count=None, sel_score=None, union=False,
+                   union_ids=None, member=None, count=None, overlap=None, ws=None, want_scores=True, stream=None):
+    """Smallest chunk sets reaching a fraction gamma of the softmax mass of the chunk scores.
+
+    Returns (sel_idx [B, Hkv, T, k_max] ascending then -1, sel_count [B, Hkv, T], sel_score or None),
+    followed by the union outputs (T * k_max slots) when union=True.
+    """
+    B, T, Hq, d = q.shape
+    _, Hkv, C, _ = lm.shape
+    _need(q, torch.float32, (B, T, Hq, d), "q")
+    dev = q.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    if sel_idx is None:
+        sel_idx = torch.empty(B, Hkv, T, k_max, **i32)
+    if sel_count is None:
+        sel_count = torch.empty(B, Hkv, T, **i32)
+    if sel_score is None and want_scores:
+        sel_score = torch.empty(B, Hkv, T, k_max, dtype=torch.float32, device=dev)
+    if union:
+        union_ids = torch.empty(B, Hkv, T * k_max, **i32) if union_ids is None else union_ids
+        member = torch.empty(B, Hkv, T * k_max, dtype=torch.uint8, device=dev) if member is None else member
+        count = torch.empty(B, Hkv, **i32) if count is None else count
+        overlap = torch.empty(B, Hkv, **i32) if overlap is None else overlap
+    if ws is None:
+        ws = torch.empty(max(coverage_workspace_size(B, Hkv, T, C), 1), dtype=torch.uint8, device=dev)
+    _check(lib.dk_score_coverage(_ptr(q), B, T, Hq, _ptr(lm), _dtype(lm), pool_strides(lm), Hkv, C, d, float(scale),
+                                 int(reduce), float(gamma), int(k_max), _ptr(sel_idx), _ptr(sel_count),
+                                 _ptr(sel_score), _ptr(union_ids), _ptr(member), _ptr(count), _ptr(overlap),
+                                 _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    if union:
+        return sel_idx, sel_count, sel_score, union_ids, member, count, overlap
+    return sel_idx, sel_count, sel_score
 
 
 def score_topk_union(q: torch.Tensor, lm: torch.Tensor, k: int, scale: float,

@@ -303,6 +303,53 @@ dk_status dk_score_topk_minmax(const float* q, int B, int T, int Hq, const void*
     return e == hipSuccess ? DK_OK : hip_fail(e, fn);
 }
 
+size_t dk_coverage_workspace_size(int B, int Hkv, int T, int C) {
+    if (B < 1 || Hkv < 1 || T < 1 || T > 2 || C < 1) return 0;
+    return dk::plan_index_topk(B, Hkv, T, C).ws_bytes;
+}
+
+dk_status dk_score_coverage(const float* q, int B, int T, int Hq, const void* lm, dk_dtype lm_dtype,
+                            dk_strides ls, int Hkv, int C, int d, float scale, dk_group_reduce reduce,
+                            float gamma, int k_max, int32_t* sel_idx, int32_t* sel_count, float* sel_score,
+                            int32_t* union_ids, uint8_t* member, int32_t* union_count, int32_t* overlap,
+                            void* ws, size_t ws_bytes, void* stream) {
+    g_err.clear();
+    const char* fn = "dk_score_coverage";
+    const int esz = dtype_size(lm_dtype);
+    DK_REQUIRE(q && lm && sel_idx && sel_count, DK_ERR_INVALID_ARG,
+               "%s: q, lm, sel_idx, sel_count must be non-NULL", fn);
+    DK_REQUIRE(esz != 0, DK_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)lm_dtype);
+    DK_REQUIRE(B >= 1 && Hq >= 1 && Hkv >= 1 && C >= 1 && d >= 1, DK_ERR_INVALID_ARG,
+               "%s: B, Hq, Hkv, C, d must be >= 1", fn);
+    DK_REQUIRE(T == 1 || T == 2, DK_ERR_INVALID_ARG, "%s: T must be 1 or 2 (got %d)", fn, T);
+    DK_REQUIRE(Hq % Hkv == 0, DK_ERR_INVALID_ARG, "%s: Hq (%d) %% Hkv (%d) != 0", fn, Hq, Hkv);
+    DK_REQUIRE(k_max >= 1 && k_max <= C, DK_ERR_INVALID_ARG, "%s: need 1 <= k_max (%d) <= C (%d)", fn, k_max, C);
+    DK_REQUIRE(gamma > 0.0f && gamma <= 1.0f, DK_ERR_INVALID_ARG, "%s: need 0 < gamma <= 1 (got %g)", fn,
+               (double)gamma);
+    DK_REQUIRE(reduce == DK_REDUCE_MEAN || reduce == DK_REDUCE_MAX, DK_ERR_INVALID_ARG, "%s: unknown reduce %d", fn,
+               (int)reduce);
+    DK_REQUIRE(std::isfinite(scale), DK_ERR_INVALID_ARG, "%s: scale must be finite", fn);
+    DK_REQUIRE(!union_ids || (member && union_count), DK_ERR_INVALID_ARG,
+               "%s: with union_ids, member and union_count must be non-NULL", fn);
+    DK_REQUIRE(d == 64 || d == 128, DK_ERR_UNSUPPORTED, "%s: d must be 64 or 128 (got %d)", fn, d);
+    DK_REQUIRE(C <= dk::kCoverageMaxC, DK_ERR_UNSUPPORTED, "%s: C must be <= %d (got %d)", fn, dk::kCoverageMaxC,
+               C);
+    if (reduce == DK_REDUCE_MAX) {
+        const int nq = (Hq / Hkv) * T;
+        DK_REQUIRE(nq <= 8 && (nq & (nq - 1)) == 0, DK_ERR_UNSUPPORTED,
+                   "%s: max reduction needs G*T a power of two <= 8 (got %d)", fn, nq);
+    }
+    DK_REQUIRE(aligned16(q) && aligned16(lm) && strides_ok(ls, esz), DK_ERR_UNSUPPORTED,
+               "%s: q, lm and lm's strides must be 16-byte aligned", fn);
+    const dk::IndexPlan plan = dk::plan_index_topk(B, Hkv, T, C);
+    DK_REQUIRE(ws && ws_bytes >= plan.ws_bytes, DK_ERR_INVALID_ARG, "%s: workspace needs %zu bytes (got %zu)", fn,
+               plan.ws_bytes, ws_bytes);
+    const dk::UnionOut un{union_ids, member, union_count, overlap};
+    hipError_t e = dk::launch_coverage(q, B, T, Hq, lm, lm_dtype, ls, Hkv, C, d, scale, reduce, gamma, k_max, sel_idx,
+                                       sel_count, sel_score, union_ids ? &un : nullptr, ws, plan, (hipStream_t)stream);
+    return e == hipSuccess ? DK_OK : hip_fail(e, fn);
+}
+
 dk_status dk_union_select(const int32_t* topk_idx, int B, int Hkv, int T, int k, int C,
                           int32_t* union_ids, uint8_t* member, int32_t* union_count,
                           int32_t* overlap, const dk_cache_plan* plan, void* stream) {

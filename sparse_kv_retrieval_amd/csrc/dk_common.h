@@ -217,6 +217,16 @@ hipError_t launch_minmax_topk(const float* q, int B, int T, int Hq, const void* 
                               dk_strides ss, int Hkv, int C, int d, int k, float scale, dk_group_reduce reduce,
                               int32_t* topk_idx, float* topk_score, void* ws, const IndexPlan& plan,
                               const UnionOut* un, hipStream_t st);
+// Plain (box == null) or upper-bound (kmin = a, kmax = b) chunk score rows and their
+// block ranges into the IndexPlan workspace.
+hipError_t launch_score_rows(const float* q, int B, int T, int Hq, const void* a, const void* b, dk_dtype dt,
+                             dk_strides ss, int Hkv, int C, int d, float scale, dk_group_reduce reduce, void* ws,
+                             const IndexPlan& plan, uint32_t* arrivals, hipStream_t st);
+constexpr int kCoverageMaxC = 16384;   // chunks per row of the coverage selection (registers of one block)
+hipError_t launch_coverage(const float* q, int B, int T, int Hq, const void* lm, dk_dtype dt, dk_strides ls, int Hkv,
+                           int C, int d, float scale, dk_group_reduce reduce, float gamma, int k_max,
+                           int32_t* sel_idx, int32_t* sel_count, float* sel_score, const UnionOut* un, void* ws,
+                           const IndexPlan& plan, hipStream_t st);
 hipError_t launch_index_topk(const float* q, int B, int T, int Hq, const uint16_t* keys, dk_strides ks, int Hkv,
                              int C, int d, int k, float scale, int32_t* topk_idx, float* topk_score, void* ws,
                              const IndexPlan& plan, const UnionOut* un, hipStream_t st);

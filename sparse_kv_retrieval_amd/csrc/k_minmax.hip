@@ -12,10 +12,12 @@
 // mean |query|, so the bound costs two FMAs per dimension.
 //
 // k_build_minmax writes the summaries (exact: minima and maxima of the keys,
-// in the keys' dtype).  k_minmax_score streams them and writes fp32 score rows
+// in the keys' dtype).  k_row_score streams them and writes fp32 score rows
 // and block ranges in the format of the exact selection kernel, which then
 // returns the k best chunks (ties to the lower id, ascending) and, optionally,
-// the union of the T sets.
+// the union of the T sets.  Without the box (BOX = false) the same kernel
+// streams one landmark per chunk and writes the plain chunk scores, the rows the
+// coverage selection reads.
 #include "dk_common.h"
 
 namespace dk {
@@ -100,11 +102,12 @@ __global__ __launch_bounds__(kMmThreads) void k_build_minmax(const T* __restrict
     st16(kmax + cid * d + part * EPT, MmElems<T>::pack(hi));
 }
 
-// Upper-bound scores of one block of chunk rows for the T queries of (b, g):
-// D/8 lanes per row, 8 dimensions per lane, row sums in DPP.  NQ query vectors:
-// T (mean: the heads folded) or G*T (max: one per head).
-template <typename ET, int D, int NQ, int T, bool MAXRED>
-__global__ __launch_bounds__(kMmThreads) void k_minmax_score(const float* __restrict__ q, int Hq,
+// Scores of one block of chunk rows for the T queries of (b, g): D/8 lanes per
+// row, 8 dimensions per lane, row sums in DPP.  NQ query vectors: T (mean: the
+// heads folded) or G*T (max: one per head).  BOX: upper bounds over [kmin, kmax];
+// otherwise plain scores of the landmarks in kmin (kmax unused).
+template <typename ET, int D, int NQ, int T, bool MAXRED, bool BOX>
+__global__ __launch_bounds__(kMmThreads) void k_row_score(const float* __restrict__ q, int Hq,
                                                             const ET* __restrict__ kmin, const ET* __restrict__ kmax,
                                                             dk_strides ss, int Hkv, int C, float scale,
                                                             int rows_per_block, int blocks_per_bg,
@@ -112,7 +115,7 @@ __global__ __launch_bounds__(kMmThreads) void k_minmax_score(const float* __rest
                                                             float* __restrict__ bmax, uint32_t* __restrict__ arrivals) {
     constexpr int LPR = D / 8, RPW = kWave / LPR, EPT = MmElems<ET>::kPer16B, NV = 8 / EPT;
     constexpr int G = MAXRED ? NQ / T : 1;
-    extern __shared__ float sm_mm[];   // [T][rows_per_block], then [2][NQ][D] query vectors
+    extern __shared__ float sm_mm[];   // [T][rows_per_block], then [BOX ? 2 : 1][NQ][D] query vectors
     const int blk = blockIdx.x % blocks_per_bg;
     const int bg = blockIdx.x / blocks_per_bg;
     const int b = bg / Hkv, g = bg - b * Hkv;
@@ -130,7 +133,7 @@ __global__ __launch_bounds__(kMmThreads) void k_minmax_score(const float* __rest
         if constexpr (MAXRED) {
             const float x = q[(((int64_t)b * T + v / G) * Hq + g * Gq + v % G) * D + e];
             qv[i] = x;
-            qv[NQ * D + i] = fabsf(x);
+            if constexpr (BOX) qv[NQ * D + i] = fabsf(x);
         } else {
             float s = 0.f, a = 0.f;
             for (int h = 0; h < Gq; ++h) {
@@ -139,7 +142,7 @@ __global__ __launch_bounds__(kMmThreads) void k_minmax_score(const float* __rest
                 a += fabsf(x);
             }
             qv[i] = s / (float)Gq;
-            qv[NQ * D + i] = a / (float)Gq;
+            if constexpr (BOX) qv[NQ * D + i] = a / (float)Gq;
         }
     }
     __syncthreads();
@@ -149,11 +152,11 @@ __global__ __launch_bounds__(kMmThreads) void k_minmax_score(const float* __rest
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             qm[v][e] = qv[v * D + part * 8 + e];
-            qa[v][e] = qv[NQ * D + v * D + part * 8 + e];
+            qa[v][e] = BOX ? qv[NQ * D + v * D + part * 8 + e] : 0.f;
         }
 
     const ET* lb = kmin + (int64_t)b * ss.b + (int64_t)g * ss.h + (int64_t)row0 * ss.t + part * 8;
-    const ET* hb = kmax + (int64_t)b * ss.b + (int64_t)g * ss.h + (int64_t)row0 * ss.t + part * 8;
+    const ET* hb = BOX ? kmax + (int64_t)b * ss.b + (int64_t)g * ss.h + (int64_t)row0 * ss.t + part * 8 : nullptr;
     constexpr int U = 4;
     for (int it = 0; it < nrows; it += 4 * RPW * U) {
         uint4 xl[U][NV], xh[U][NV];
@@ -163,7 +166,8 @@ __global__ __launch_bounds__(kMmThreads) void k_minmax_score(const float* __rest
 #pragma unroll
             for (int x = 0; x < NV; ++x) {
                 xl[u][x] = r < nrows ? ld16(lb + (int64_t)r * ss.t + x * EPT) : make_uint4(0, 0, 0, 0);
-                xh[u][x] = r < nrows ? ld16(hb + (int64_t)r * ss.t + x * EPT) : make_uint4(0, 0, 0, 0);
+                if constexpr (BOX)
+                    xh[u][x] = r < nrows ? ld16(hb + (int64_t)r * ss.t + x * EPT) : make_uint4(0, 0, 0, 0);
             }
         }
 #pragma unroll
@@ -174,11 +178,16 @@ __global__ __launch_bounds__(kMmThreads) void k_minmax_score(const float* __rest
             for (int x = 0; x < NV; ++x) {
                 float fl[EPT], fh[EPT];
                 MmElems<ET>::unpack(xl[u][x], fl);
-                MmElems<ET>::unpack(xh[u][x], fh);
+                if constexpr (BOX) {
+                    MmElems<ET>::unpack(xh[u][x], fh);
 #pragma unroll
-                for (int e = 0; e < EPT; ++e) {
-                    mid[x * EPT + e] = 0.5f * (fl[e] + fh[e]);
-                    rad[x * EPT + e] = 0.5f * (fh[e] - fl[e]);
+                    for (int e = 0; e < EPT; ++e) {
+                        mid[x * EPT + e] = 0.5f * (fl[e] + fh[e]);
+                        rad[x * EPT + e] = 0.5f * (fh[e] - fl[e]);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < EPT; ++e) mid[x * EPT + e] = fl[e];
                 }
             }
             float sc[T];
@@ -188,7 +197,10 @@ __global__ __launch_bounds__(kMmThreads) void k_minmax_score(const float* __rest
             for (int v = 0; v < NQ; ++v) {
                 float a = 0.f;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) a = fmaf(qa[v][e], rad[e], fmaf(qm[v][e], mid[e], a));
+                for (int e = 0; e < 8; ++e) {
+                    if constexpr (BOX) a = fmaf(qa[v][e], rad[e], fmaf(qm[v][e], mid[e], a));
+                    else a = fmaf(qm[v][e], mid[e], a);
+                }
                 const float sv = scale * dpp_group_sum<LPR>(a);
                 const int t = MAXRED ? v / G : v;
                 sc[t] = MAXRED ? fmaxf(sc[t], sv) : sv;
@@ -230,21 +242,21 @@ __global__ __launch_bounds__(kMmThreads) void k_minmax_score(const float* __rest
     }
 }
 
-template <typename ET, int D, int NQ, int T, bool MAXRED>
-void launch_mm_score(dim3 grid, size_t lds, hipStream_t st, const float* q, int Hq, const void* kmin,
-                     const void* kmax, dk_strides ss, int Hkv, int C, float scale, const IndexPlan& p,
-                     float* scores, float* bmin, float* bmax, uint32_t* arrivals) {
-    hipLaunchKernelGGL((k_minmax_score<ET, D, NQ, T, MAXRED>), grid, dim3(kMmThreads), lds, st, q, Hq,
+template <typename ET, int D, int NQ, int T, bool MAXRED, bool BOX>
+void launch_row_score(dim3 grid, size_t lds, hipStream_t st, const float* q, int Hq, const void* kmin,
+                      const void* kmax, dk_strides ss, int Hkv, int C, float scale, const IndexPlan& p,
+                      float* scores, float* bmin, float* bmax, uint32_t* arrivals) {
+    hipLaunchKernelGGL((k_row_score<ET, D, NQ, T, MAXRED, BOX>), grid, dim3(kMmThreads), lds, st, q, Hq,
                        (const ET*)kmin, (const ET*)kmax, ss, Hkv, C, scale, p.rows_per_block, p.blocks_per_bg,
                        scores, bmin, bmax, arrivals);
 }
 
-template <typename ET, int D>
-hipError_t dispatch_mm(int nq, int T, bool maxred, dim3 grid, size_t lds, hipStream_t st, const float* q, int Hq,
+template <typename ET, int D, bool BOX>
+hipError_t dispatch_rows(int nq, int T, bool maxred, dim3 grid, size_t lds, hipStream_t st, const float* q, int Hq,
                        const void* kmin, const void* kmax, dk_strides ss, int Hkv, int C, float scale,
                        const IndexPlan& p, float* scores, float* bmin, float* bmax, uint32_t* arrivals) {
 #define DK_MM(NQ_, T_, MX_) \
-    launch_mm_score<ET, D, NQ_, T_, MX_>(grid, lds, st, q, Hq, kmin, kmax, ss, Hkv, C, scale, p, scores, bmin, bmax, arrivals)
+    launch_row_score<ET, D, NQ_, T_, MX_, BOX>(grid, lds, st, q, Hq, kmin, kmax, ss, Hkv, C, scale, p, scores, bmin, bmax, arrivals)
     if (!maxred) {
         if (T == 2) DK_MM(2, 2, false); else DK_MM(1, 1, false);
     } else if (T == 2) {
@@ -276,33 +288,41 @@ hipError_t launch_build_minmax(const void* K, dk_dtype dt, dk_strides ks, int B,
     return hipGetLastError();
 }
 
-hipError_t launch_minmax_topk(const float* q, int B, int T, int Hq, const void* kmin, const void* kmax, dk_dtype dt,
-                              dk_strides ss, int Hkv, int C, int d, int k, float scale, dk_group_reduce reduce,
-                              int32_t* topk_idx, float* topk_score, void* ws, const IndexPlan& plan,
-                              const UnionOut* un, hipStream_t st) {
+hipError_t launch_score_rows(const float* q, int B, int T, int Hq, const void* a, const void* b, dk_dtype dt,
+                             dk_strides ss, int Hkv, int C, int d, float scale, dk_group_reduce reduce, void* ws,
+                             const IndexPlan& plan, uint32_t* arrivals, hipStream_t st) {
     float* scores = (float*)ws;
     float* bmin = (float*)((char*)ws + plan.off_min);
     float* bmax = (float*)((char*)ws + plan.off_max);
-    uint32_t* arrivals = un ? (uint32_t*)((char*)ws + plan.off_arrive) : nullptr;
     const int G = Hq / Hkv;
     const bool maxred = reduce == DK_REDUCE_MAX;
     const int nq = maxred ? G * T : T;
     const dim3 grid((unsigned)((int64_t)B * Hkv * plan.blocks_per_bg));
-    const size_t lds = ((size_t)T * plan.rows_per_block + 2 * (size_t)nq * d) * 4;
-    hipError_t e;
-    if (dt == DK_BF16)
-        e = d == 128 ? dispatch_mm<uint16_t, 128>(nq, T, maxred, grid, lds, st, q, Hq, kmin, kmax, ss, Hkv, C, scale,
-                                                  plan, scores, bmin, bmax, arrivals)
-                     : dispatch_mm<uint16_t, 64>(nq, T, maxred, grid, lds, st, q, Hq, kmin, kmax, ss, Hkv, C, scale,
-                                                 plan, scores, bmin, bmax, arrivals);
-    else
-        e = d == 128 ? dispatch_mm<float, 128>(nq, T, maxred, grid, lds, st, q, Hq, kmin, kmax, ss, Hkv, C, scale,
-                                               plan, scores, bmin, bmax, arrivals)
-                     : dispatch_mm<float, 64>(nq, T, maxred, grid, lds, st, q, Hq, kmin, kmax, ss, Hkv, C, scale,
-                                              plan, scores, bmin, bmax, arrivals);
+    const size_t lds = ((size_t)T * plan.rows_per_block + (b ? 2 : 1) * (size_t)nq * d) * 4;
+#define DK_ROWS(ET_, D_, BOX_)                                                                                  \
+    return dispatch_rows<ET_, D_, BOX_>(nq, T, maxred, grid, lds, st, q, Hq, a, b, ss, Hkv, C, scale, plan,    \
+                                        scores, bmin, bmax, arrivals)
+    if (dt == DK_BF16) {
+        if (d == 128) { if (b) DK_ROWS(uint16_t, 128, true); else DK_ROWS(uint16_t, 128, false); }
+        else { if (b) DK_ROWS(uint16_t, 64, true); else DK_ROWS(uint16_t, 64, false); }
+    } else {
+        if (d == 128) { if (b) DK_ROWS(float, 128, true); else DK_ROWS(float, 128, false); }
+        else { if (b) DK_ROWS(float, 64, true); else DK_ROWS(float, 64, false); }
+    }
+#undef DK_ROWS
+}
+
+hipError_t launch_minmax_topk(const float* q, int B, int T, int Hq, const void* kmin, const void* kmax, dk_dtype dt,
+                              dk_strides ss, int Hkv, int C, int d, int k, float scale, dk_group_reduce reduce,
+                              int32_t* topk_idx, float* topk_score, void* ws, const IndexPlan& plan,
+                              const UnionOut* un, hipStream_t st) {
+    uint32_t* arrivals = un ? (uint32_t*)((char*)ws + plan.off_arrive) : nullptr;
+    hipError_t e = launch_score_rows(q, B, T, Hq, kmin, kmax, dt, ss, Hkv, C, d, scale, reduce, ws, plan, arrivals,
+                                     st);
     if (e != hipSuccess) return e;
-    return launch_select_rows(scores, bmin, bmax, plan.blocks_per_bg, B, Hkv, T, C, k, topk_idx, topk_score, un,
-                              arrivals, st);
+    return launch_select_rows((const float*)ws, (const float*)((char*)ws + plan.off_min),
+                              (const float*)((char*)ws + plan.off_max), plan.blocks_per_bg, B, Hkv, T, C, k, topk_idx,
+                              topk_score, un, arrivals, st);
 }
 
 }  // namespace dk

@@ -27,14 +27,14 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(lib, n), n
     assert {n for n, _, _ in b.EXPORTS} == set(names)
 
 
 def test_abi_version():
-    assert lib.dk_abi_version() == 7
+    assert lib.dk_abi_version() == 8
 
 
 def err():
@@ -286,3 +286,33 @@ def test_build_minmax_rejects(kw, status):
     assert lib.dk_build_minmax(a["K"], a["dt"], a["ks"], a["B"], a["Hkv"], a["L"], a["d"], a["chunk"], a["mn"],
                                a["mx"], None) == status, err()
     assert err().startswith("dk_build_minmax")
+
+
+def coverage(q=FAKE, B=2, T=2, Hq=32, lm=FAKE, dt=0, ls=b.dk_strides(1 << 22, 1 << 19, 128), Hkv=8, C=1024,
+             d=128, scale=0.088, reduce=0, gamma=0.9, k_max=64, idx=FAKE, cnt=FAKE, sc=NULL, uid=NULL, mem=NULL,
+             ucnt=NULL, ov=NULL, ws=FAKE, wsb=1 << 30):
+    return lib.dk_score_coverage(q, B, T, Hq, lm, dt, ls, Hkv, C, d, scale, reduce, gamma, k_max, idx, cnt, sc, uid,
+                                 mem, ucnt, ov, ws, wsb, None)
+
+
+# every case breaks exactly one rule, so no call reaches a launch
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=NULL), 1), (dict(lm=NULL), 1), (dict(idx=NULL), 1), (dict(cnt=NULL), 1), (dict(T=3), 1),
+    (dict(k_max=0), 1), (dict(k_max=1025), 1), (dict(gamma=0.0), 1), (dict(gamma=1.5), 1),
+    (dict(gamma=float("nan")), 1), (dict(reduce=4), 1), (dict(scale=float("inf")), 1), (dict(dt=5), 1),
+    (dict(uid=FAKE), 1), (dict(Hq=30), 1), (dict(d=96), 2), (dict(C=16385, k_max=8), 2),
+    (dict(reduce=1, Hq=64), 2), (dict(lm=MIS), 2), (dict(ls=b.dk_strides(1 << 22, 1 << 19, 129)), 2),
+    (dict(wsb=16), 1), (dict(ws=NULL), 1),
+])
+def test_coverage_rejects(kw, status):
+    assert coverage(**kw) == status, err()
+    assert err().startswith("dk_score_coverage")
+
+
+def test_coverage_workspace_size():
+    # fp32 score rows [B*Hkv*T, C], per-block minima and maxima, one counter per (b, g); 256-byte aligned
+    assert lib.dk_coverage_workspace_size(64, 8, 2, 4096) == 1024 * 4096 * 4 + 2 * 16384 + 2048
+    assert lib.dk_coverage_workspace_size(1, 1, 1, 100) == 512 + 2 * 256 + 256
+    assert lib.dk_coverage_workspace_size(1, 1, 3, 100) == 0
+    assert lib.dk_coverage_workspace_size(0, 1, 1, 100) == 0
+
