@@ -60,7 +60,10 @@ Selection variants replace the landmark score or the fixed budget k:
   softmax of its chunk score over the row; the kept set is the shortest prefix
   of the (score descending, id ascending) order whose mass reaches gamma, at
   least one chunk and at most k_max (the caller's buffer); the union of the two
-  queries' sets is taken over their own counts.
+  queries' sets is taken over their own counts;
+* capped eviction (OasisKV, "Delta Selection and Capped Eviction"): see
+  capped_plan for the readings of the order of admissions, eviction targets
+  and their pairing.
 
 Parity of each function is pinned by the not-gpu tests (closed forms, brute
 force on tiny inputs, a library attention routine, hand-worked fixtures under
@@ -534,3 +537,73 @@ def union_select_ragged(idx: np.ndarray, count: np.ndarray):
                 member[b, g, i] = sum(1 << t for t in range(T) if c in sets[t])
             overlap[b, g] = len(sets[0] & sets[1]) if T == 2 else len(sets[0])
     return union_ids, member, ucount, overlap
+
+
+# ----------------------------------------------------------------------------
+# selection variants: delta selection with capped LRU eviction
+# ----------------------------------------------------------------------------
+
+def capped_plan(sel_ids, sel_score, sel_count, resident, stamp, cap: int, step: int):
+    """One step of a bounded per-(request, KV head) working set under capped eviction.
+
+    OasisKV, "Delta Selection and Capped Eviction": resident blocks of the
+    predicted set cost no traffic; resident blocks outside it are ranked by the
+    step at which they were last selected; each admitted non-resident block is
+    paired with one eviction target, least recently selected first; at most
+    `cap` pairs are admitted per step and KV head.
+
+    Readings: the predicted set P of (b, g) is sel_ids[b, g, :sel_count[b, g]]
+    (ascending chunk ids) with priorities sel_score (None: all equal).  Hits keep
+    their slot and their stamp becomes `step`.  Eviction targets are the slots
+    whose chunk is not in P, empty slots first, then the oldest stamp, then the
+    lower slot.  The admitted misses are the min(cap, #misses, #targets) best by
+    (score descending, id ascending); they are paired in ascending chunk order
+    with the chosen targets in ascending slot order, and stamped `step`.  Misses
+    not admitted stay out of the working set for this step (slot -1).
+
+    resident, stamp: [B, Hkv, S] (chunk per slot or -1; last-selected step).
+    Returns a dict: resident, stamp (new arrays), sel_slot [B, Hkv, N] (slot of
+    each entry after the step, -1 when dropped or padding), admit_chunk,
+    admit_slot [B, Hkv, cap] (-1 padded), admit_count, hit_count [B, Hkv].
+    """
+    sel_ids = np.asarray(sel_ids)
+    B, H, N = sel_ids.shape
+    resident = np.array(resident, dtype=np.int64, copy=True)
+    stamp = np.array(stamp, dtype=np.int64, copy=True)
+    S = resident.shape[2]
+    score = np.zeros(sel_ids.shape) if sel_score is None else np.asarray(sel_score, dtype=np.float64)
+    count = np.full((B, H), N) if sel_count is None else np.asarray(sel_count)
+    sel_slot = np.full((B, H, N), -1, dtype=np.int64)
+    admit_chunk = np.full((B, H, cap), -1, dtype=np.int64)
+    admit_slot = np.full((B, H, cap), -1, dtype=np.int64)
+    admit_count = np.zeros((B, H), dtype=np.int64)
+    hit_count = np.zeros((B, H), dtype=np.int64)
+    for b in range(B):
+        for g in range(H):
+            n = int(count[b, g])
+            P = [int(c) for c in sel_ids[b, g, :n]]
+            res, st = resident[b, g], stamp[b, g]
+            where = {int(c): s for s, c in enumerate(res) if c >= 0}
+            in_p = set(P)
+            misses = []
+            for i, c in enumerate(P):
+                if c in where:
+                    sel_slot[b, g, i] = where[c]
+                    st[where[c]] = step
+                    hit_count[b, g] += 1
+                else:
+                    misses.append(i)
+            targets = [s for s in range(S) if res[s] < 0 or int(res[s]) not in in_p]
+            targets.sort(key=lambda s: (res[s] >= 0, st[s] if res[s] >= 0 else 0, s))
+            misses.sort(key=lambda i: (-score[b, g, i], P[i]))
+            a = min(cap, len(misses), len(targets))
+            admitted = sorted(misses[:a], key=lambda i: P[i])
+            for r, (i, s) in enumerate(zip(admitted, sorted(targets[:a]))):
+                res[s] = P[i]
+                st[s] = step
+                sel_slot[b, g, i] = s
+                admit_chunk[b, g, r] = P[i]
+                admit_slot[b, g, r] = s
+            admit_count[b, g] = a
+    return dict(resident=resident, stamp=stamp, sel_slot=sel_slot, admit_chunk=admit_chunk,
+                admit_slot=admit_slot, admit_count=admit_count, hit_count=hit_count)

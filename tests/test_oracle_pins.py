@@ -817,7 +817,144 @@ def _union_ragged_ignores_count(idx, count):
     return O.union_select_ragged(idx, np.full(np.asarray(count).shape, np.asarray(idx).shape[-1]))
 
 
+# ----------------------------------------------------------------------------
+# delta selection with capped LRU eviction
+# ----------------------------------------------------------------------------
+
+def lru_reference(seq, S):
+    """Textbook LRU cache of S entries over an access sequence: (hit, evicted) per access."""
+    from collections import OrderedDict
+    cache, out = OrderedDict(), []
+    for x in seq:
+        if x in cache:
+            cache.move_to_end(x)
+            out.append((True, None))
+            continue
+        ev = None
+        if len(cache) == S:
+            ev, _ = cache.popitem(last=False)
+        cache[x] = True
+        out.append((False, ev))
+    return out, set(cache)
+
+
+def check_capped(fn):
+    """fn(sel_ids, sel_score, sel_count, resident, stamp, cap, step) -> dict; pins the capped plan."""
+    fx = golden("capped_plan_hand.json")
+    for case in fx["cases"]:
+        r = fn(np.array(fx["sel_ids"])[None, None], np.array(fx["sel_score"])[None, None] if case["scores"] else None,
+               None, np.array(fx["resident"])[None, None], np.array(fx["stamp"])[None, None], case["cap"], fx["step"])
+        for key in ("resident", "stamp", "sel_slot", "admit_chunk", "admit_slot"):
+            np.testing.assert_array_equal(r[key][0, 0], case[key], err_msg=f"{key} {case['cap']}")
+        assert r["admit_count"][0, 0] == case["admit_count"] and r["hit_count"][0, 0] == case["hit_count"]
+
+    # one block per step and one admission per step: a textbook LRU cache
+    rng = np.random.default_rng(41)
+    S, seq = 5, rng.integers(0, 12, size=300).tolist()
+    ref, final = lru_reference(seq, S)
+    res, st = np.full((1, 1, S), -1), np.full((1, 1, S), -1)
+    for step, (x, (hit, ev)) in enumerate(zip(seq, ref)):
+        before = set(res[0, 0].tolist())
+        r = fn(np.array([[[x]]]), None, None, res, st, 1, step)
+        res, st = r["resident"], r["stamp"]
+        assert (r["hit_count"][0, 0] == 1) == hit, step
+        after = set(res[0, 0].tolist())
+        if ev is not None:
+            assert before - after == {ev}, (step, before, after, ev)
+        assert x in after
+    assert set(res[0, 0].tolist()) == final
+
+    # from an empty cache with room for every miss: the uncapped cache plan
+    B, H, S, N = 2, 3, 40, 12
+    ids = np.stack([np.sort(rng.choice(100, N, replace=False)) for _ in range(B * H)]).reshape(B, H, N)
+    cnt = rng.integers(1, N + 1, size=(B, H))
+    sc = rng.standard_normal((B, H, N))
+    empty = np.full((B, H, S), -1)
+    r = fn(ids, sc, cnt, empty, empty, N, 3)
+    u = np.where(np.arange(N) < cnt[..., None], ids, -1)
+    cp = O.cache_plan(empty, u, cnt)
+    np.testing.assert_array_equal(r["sel_slot"], cp["slot_of_union"])
+    np.testing.assert_array_equal(r["resident"], cp["new_resident"])
+
+    # invariants over random multi-step traces
+    res = np.full((B, H, S), -1)
+    st = np.full((B, H, S), -1)
+    for step in range(12):
+        ids = np.stack([np.sort(rng.choice(60, N, replace=False)) for _ in range(B * H)]).reshape(B, H, N)
+        cnt = rng.integers(1, N + 1, size=(B, H))
+        sc = np.round(rng.standard_normal((B, H, N)), 1)
+        cap = int(rng.integers(0, 6))
+        r = fn(ids, sc, cnt, res, st, cap, step)
+        for b, g in itertools.product(range(B), range(H)):
+            n = cnt[b, g]
+            P = ids[b, g, :n].tolist()
+            old, new = res[b, g], r["resident"][b, g]
+            a = int(r["admit_count"][b, g])
+            assert a <= cap
+            occ = new[new >= 0]
+            assert len(set(occ.tolist())) == len(occ)                          # distinct chunks
+            changed = np.nonzero(old != new)[0]
+            assert len(changed) == a and set(changed.tolist()) == set(r["admit_slot"][b, g, :a].tolist())
+            for s in changed:
+                assert old[s] < 0 or old[s] not in P                           # hits are never evicted
+            # least recently selected first: no surviving candidate is older than an evicted one
+            surv = [s for s in range(S) if s not in changed and (old[s] < 0 or old[s] not in P)]
+            for s in changed:
+                for t in surv:
+                    ks = (old[s] >= 0, st[b, g, s] if old[s] >= 0 else 0, s)
+                    kt = (old[t] >= 0, st[b, g, t] if old[t] >= 0 else 0, t)
+                    assert ks < kt, (step, b, g, s, t)
+            # the best misses are admitted
+            miss = [i for i in range(n) if P[i] not in old.tolist()]
+            adm = [i for i in miss if r["sel_slot"][b, g, i] >= 0]
+            drop = [i for i in miss if r["sel_slot"][b, g, i] < 0]
+            assert len(adm) == a and len(drop) == len(miss) - a
+            for i in adm:
+                for j in drop:
+                    assert (-sc[b, g, i], P[i]) < (-sc[b, g, j], P[j])
+            for i in range(n):
+                s = r["sel_slot"][b, g, i]
+                assert s < 0 or new[s] == P[i]
+                if s >= 0:
+                    assert r["stamp"][b, g, s] == step
+        res, st = r["resident"], r["stamp"]
+
+
+def test_capped_pins():
+    check_capped(O.capped_plan)
+
+
+def _capped_mru(sel_ids, sel_score, sel_count, resident, stamp, cap, step):
+    # evicts the most recently selected block first
+    r = O.capped_plan(sel_ids, sel_score, sel_count, resident, -np.asarray(stamp), cap, step)
+    r["stamp"] = np.where(r["stamp"] == step, step, np.asarray(stamp))
+    return r
+
+
+def _capped_ignores_cap(sel_ids, sel_score, sel_count, resident, stamp, cap, step):
+    r = O.capped_plan(sel_ids, sel_score, sel_count, resident, stamp, 10 ** 6, step)
+    r["admit_chunk"] = r["admit_chunk"][..., :cap]
+    r["admit_slot"] = r["admit_slot"][..., :cap]
+    return r
+
+
+def _capped_low_score_first(sel_ids, sel_score, sel_count, resident, stamp, cap, step):
+    neg = None if sel_score is None else -np.asarray(sel_score)
+    return O.capped_plan(sel_ids, neg, sel_count, resident, stamp, cap, step)
+
+
+def _capped_hits_not_restamped(sel_ids, sel_score, sel_count, resident, stamp, cap, step):
+    r = O.capped_plan(sel_ids, sel_score, sel_count, resident, stamp, cap, step)
+    kept = np.asarray(resident) == r["resident"]
+    r["stamp"] = np.where(kept, np.asarray(stamp), r["stamp"])
+    return r
+
+
 @pytest.mark.parametrize("check,bad", [
+    (check_capped, _capped_mru),
+    (check_capped, _capped_ignores_cap),
+    (check_capped, _capped_low_score_first),
+    (check_capped, _capped_hits_not_restamped),
     (check_coverage, _coverage_strict),
     (check_coverage, _coverage_raw_scores),
     (check_coverage, _coverage_ties_high_id),
