@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define DK_ABI_VERSION 8
+#define DK_ABI_VERSION 9
 
 typedef enum {
     DK_OK = 0,
@@ -303,6 +303,48 @@ typedef struct {
     int32_t* miss_count;     /* out [B, Hkv]                                                */
     int32_t* hit_count;      /* out [B, Hkv]                                                */
 } dk_cache_plan;
+
+/*
+ * dk_capped_plan - one step of a bounded per-(request, KV head) working set
+ * under delta selection with capped eviction.
+ *
+ * OasisKV, "Delta Selection and Capped Eviction": predicted blocks already
+ * resident cost no traffic; resident blocks outside the predicted set are ranked
+ * by the step of their last selection; each admitted non-resident block is
+ * paired with one eviction target, least recently selected first; at most `cap`
+ * pairs are admitted per step and KV head.
+ *
+ * Rule: hits keep their slot and their stamp becomes `step`.  Targets are the
+ * slots whose chunk is not predicted: empty slots first, then the oldest stamp,
+ * then the lower slot.  The admitted misses are the best min(cap, misses,
+ * targets) by (score descending, id ascending; all tied when sel_score is NULL),
+ * paired in ascending chunk order with the targets in ascending slot order; the
+ * target takes the chunk and the stamp `step`.  Other misses get no slot.
+ *
+ * sel_ids      : int32, row (b, g) at sel_ids + (b*Hkv + g) * sel_stride: N entries,
+ *                the first sel_count of them strictly ascending chunk ids >= 0
+ *                (e.g. one query's row of dk_score_topk output: offset t*k, stride T*k).
+ * sel_score    : fp32 priorities in the same layout, or NULL.
+ * sel_count    : int32 at sel_count + (b*Hkv + g) * count_stride (clamped to [0, N]), or NULL (N).
+ * resident     : in/out int32 [B, Hkv, slots]: chunk per slot, -1 empty; distinct chunks.
+ * stamp        : in/out int32 [B, Hkv, slots]: step of the slot's last selection.
+ * sel_slot     : out int32 [B, Hkv, N]: slot of each entry after the step, -1 when
+ *                not admitted or past the count.
+ * admit_chunk, admit_slot : out int32 [B, Hkv, cap]: the transfers (chunk -> slot)
+ *                in ascending chunk order, -1 padded (may be NULL when cap == 0);
+ *                dk_gather_kv(src_chunk = admit_chunk, dst_slot = admit_slot,
+ *                count = admit_count) performs them.
+ * admit_count  : out int32 [B, Hkv].   hit_count : out int32 [B, Hkv] or NULL.
+ * Errors       : DK_ERR_INVALID_ARG unless B, Hkv, N, slots >= 1, sel_stride >= N,
+ *                count_stride >= 1 with sel_count, 0 <= cap <= 2^20 and the required
+ *                pointers are non-NULL; DK_ERR_UNSUPPORTED if N or slots > 4096.
+ *                Row contents are not checked: ids that are not ascending or
+ *                resident chunks that repeat give an unspecified (in-bounds) plan.
+ */
+dk_status dk_capped_plan(const int32_t* sel_ids, const float* sel_score, const int32_t* sel_count, int B, int Hkv,
+                         int N, int sel_stride, int count_stride, int32_t* resident, int32_t* stamp, int slots,
+                         int cap, int32_t step, int32_t* sel_slot, int32_t* admit_chunk, int32_t* admit_slot,
+                         int32_t* admit_count, int32_t* hit_count, void* stream);
 
 /*
  * dk_union_select - the distinct chunks of the T selections of every (b, g).

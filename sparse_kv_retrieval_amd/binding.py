@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libdualkv.so")
 DK_OK, DK_ERR_INVALID_ARG, DK_ERR_UNSUPPORTED, DK_ERR_HIP = 0, 1, 2, 3
 DK_F32, DK_BF16 = 0, 1
 DK_REDUCE_MEAN, DK_REDUCE_MAX = 0, 1
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 _STATUS = {0: "DK_OK", 1: "DK_ERR_INVALID_ARG", 2: "DK_ERR_UNSUPPORTED", 3: "DK_ERR_HIP"}
 
@@ -72,6 +72,7 @@ EXPORTS = [
                            ctypes.POINTER(dk_landmark_shadow), _P, _P, _P, _Z, _P]),
     ("dk_score_topk_union", _I, [_P, _I, _I, _I, _P, _I, _S, _I, _I, _I, _I, _F, _I,
                                  ctypes.POINTER(dk_landmark_shadow), _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    ("dk_capped_plan", _I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
     ("dk_union_select", _I, [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, ctypes.POINTER(dk_cache_plan), _P]),
     ("dk_gather_kv", _I, [_P, _P, _I, _S, _I, _I, _I, _I, _P, _P, _P, _I, _I, _P, _P, _S, _I, _I, _P]),
     ("dk_attn_workspace_size", _Z, [_I, _I, _I, _I, _I, _I, _I]),
@@ -290,6 +291,43 @@ def score_coverage(q: torch.Tensor, lm: torch.Tensor, gamma: float, k_max: int, 
     if union:
         return sel_idx, sel_count, sel_score, union_ids, member, count, overlap
     return sel_idx, sel_count, sel_score
+
+
+def capped_plan(sel_ids: torch.Tensor, resident: torch.Tensor, stamp: torch.Tensor, cap: int, step: int,
+                sel_score: torch.Tensor | None = None, sel_count: torch.Tensor | None = None, sel_slot=None,
+                admit_chunk=None, admit_slot=None, admit_count=None, hit_count=None, stream=None):
+    """One step of capped eviction: updates resident/stamp [B, Hkv, S] in place.
+
+    sel_ids: [B, Hkv, N] (or a strided view of one query's rows, e.g. topk_idx[:, :, t]) with ascending ids;
+    sel_score: the same layout or None; sel_count: [B, Hkv] (or a view with one stride) or None.
+    Returns (sel_slot [B, Hkv, N], admit_chunk [B, Hkv, cap], admit_slot, admit_count [B, Hkv], hit_count).
+    """
+    B, Hkv, N = sel_ids.shape
+    S = resident.shape[2]
+    for name, t in (("resident", resident), ("stamp", stamp)):
+        _need(t, torch.int32, (B, Hkv, S), name)
+    if sel_ids.dtype != torch.int32 or sel_ids.stride(2) != 1 or sel_ids.stride(0) != Hkv * sel_ids.stride(1):
+        raise ValueError("sel_ids must be int32 rows of unit stride, (b, g) rows at one stride")
+    stride = sel_ids.stride(1)
+    if sel_score is not None and (sel_score.dtype != torch.float32 or sel_score.shape != sel_ids.shape
+                                  or sel_score.stride() != sel_ids.stride()):
+        raise ValueError("sel_score must be float32 in the layout of sel_ids")
+    cstride = 1
+    if sel_count is not None:
+        if sel_count.dtype != torch.int32 or sel_count.shape != (B, Hkv) or sel_count.stride(0) != Hkv * sel_count.stride(1):
+            raise ValueError("sel_count must be int32 [B, Hkv] with one stride")
+        cstride = sel_count.stride(1)
+    dev = sel_ids.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    sel_slot = torch.empty(B, Hkv, N, **i32) if sel_slot is None else sel_slot
+    admit_chunk = torch.empty(B, Hkv, max(cap, 1), **i32) if admit_chunk is None else admit_chunk
+    admit_slot = torch.empty(B, Hkv, max(cap, 1), **i32) if admit_slot is None else admit_slot
+    admit_count = torch.empty(B, Hkv, **i32) if admit_count is None else admit_count
+    hit_count = torch.empty(B, Hkv, **i32) if hit_count is None else hit_count
+    _check(lib.dk_capped_plan(_ptr(sel_ids), _ptr(sel_score), _ptr(sel_count), B, Hkv, N, stride, cstride,
+                              _ptr(resident), _ptr(stamp), S, int(cap), int(step), _ptr(sel_slot), _ptr(admit_chunk),
+                              _ptr(admit_slot), _ptr(admit_count), _ptr(hit_count), _stream(stream)))
+    return sel_slot, admit_chunk[..., :cap], admit_slot[..., :cap], admit_count, hit_count
 
 
 def score_topk_union(q: torch.Tensor, lm: torch.Tensor, k: int, scale: float,

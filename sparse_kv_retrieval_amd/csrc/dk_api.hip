@@ -350,6 +350,29 @@ dk_status dk_score_coverage(const float* q, int B, int T, int Hq, const void* lm
     return e == hipSuccess ? DK_OK : hip_fail(e, fn);
 }
 
+dk_status dk_capped_plan(const int32_t* sel_ids, const float* sel_score, const int32_t* sel_count, int B, int Hkv,
+                         int N, int sel_stride, int count_stride, int32_t* resident, int32_t* stamp, int slots,
+                         int cap, int32_t step, int32_t* sel_slot, int32_t* admit_chunk, int32_t* admit_slot,
+                         int32_t* admit_count, int32_t* hit_count, void* stream) {
+    g_err.clear();
+    const char* fn = "dk_capped_plan";
+    DK_REQUIRE(sel_ids && resident && stamp && sel_slot && admit_count, DK_ERR_INVALID_ARG,
+               "%s: sel_ids, resident, stamp, sel_slot, admit_count must be non-NULL", fn);
+    DK_REQUIRE(B >= 1 && Hkv >= 1 && N >= 1 && slots >= 1, DK_ERR_INVALID_ARG, "%s: B, Hkv, N, slots must be >= 1",
+               fn);
+    DK_REQUIRE(sel_stride >= N, DK_ERR_INVALID_ARG, "%s: sel_stride (%d) must be >= N (%d)", fn, sel_stride, N);
+    DK_REQUIRE(!sel_count || count_stride >= 1, DK_ERR_INVALID_ARG, "%s: count_stride must be >= 1", fn);
+    DK_REQUIRE(cap >= 0 && cap <= (1 << 20), DK_ERR_INVALID_ARG, "%s: need 0 <= cap <= 2^20 (got %d)", fn, cap);
+    DK_REQUIRE(cap == 0 || (admit_chunk && admit_slot), DK_ERR_INVALID_ARG,
+               "%s: admit_chunk and admit_slot must be non-NULL when cap > 0", fn);
+    DK_REQUIRE(N <= dk::kCappedMaxN && slots <= dk::kCappedMaxN, DK_ERR_UNSUPPORTED,
+               "%s: N and slots must be <= %d (got %d, %d)", fn, dk::kCappedMaxN, N, slots);
+    hipError_t e = dk::launch_capped_plan(sel_ids, sel_score, sel_count, B, Hkv, N, sel_stride, count_stride, resident,
+                                          stamp, slots, cap, step, sel_slot, admit_chunk, admit_slot, admit_count,
+                                          hit_count, (hipStream_t)stream);
+    return e == hipSuccess ? DK_OK : hip_fail(e, fn);
+}
+
 dk_status dk_union_select(const int32_t* topk_idx, int B, int Hkv, int T, int k, int C,
                           int32_t* union_ids, uint8_t* member, int32_t* union_count,
                           int32_t* overlap, const dk_cache_plan* plan, void* stream) {

@@ -227,6 +227,11 @@ hipError_t launch_coverage(const float* q, int B, int T, int Hq, const void* lm,
                            int C, int d, float scale, dk_group_reduce reduce, float gamma, int k_max,
                            int32_t* sel_idx, int32_t* sel_count, float* sel_score, const UnionOut* un, void* ws,
                            const IndexPlan& plan, hipStream_t st);
+constexpr int kCappedMaxN = 4096;   // predicted entries and slots per (b, g) of the capped plan (LDS <= 48 KB)
+hipError_t launch_capped_plan(const int32_t* sel_ids, const float* sel_score, const int32_t* sel_count, int B,
+                              int Hkv, int N, int64_t sel_stride, int64_t count_stride, int32_t* resident,
+                              int32_t* stamp, int S, int cap, int32_t step, int32_t* sel_slot, int32_t* admit_chunk,
+                              int32_t* admit_slot, int32_t* admit_count, int32_t* hit_count, hipStream_t st);
 hipError_t launch_index_topk(const float* q, int B, int T, int Hq, const uint16_t* keys, dk_strides ks, int Hkv,
                              int C, int d, int k, float scale, int32_t* topk_idx, float* topk_score, void* ws,
                              const IndexPlan& plan, const UnionOut* un, hipStream_t st);

@@ -21,119 +21,14 @@
 // k_max is replaced by the top k_max, found by a second bisection on counts.
 // Tie ranks and output positions come from ballots and one wave's scan of the
 // per-wave counts.
-#include "dk_common.h"
+#include "dk_block.h"
 
 namespace dk {
 namespace {
 
-constexpr int kCovThreads = 1024;
-constexpr int kCovWaves = kCovThreads / kWave;
-
-__device__ __forceinline__ float wave_sum_f(float v) {
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) v += __shfl_xor(v, off, kWave);
-    return v;
-}
-__device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) v += __shfl_xor(v, off, kWave);
-    return v;
-}
-__device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, kWave));
-    return v;
-}
-
-// Block sums of N values; every thread gets the same results (fixed order).
-// buf: [N][kCovWaves]; the caller alternates two buffers between calls, so one
-// barrier per call suffices.
-template <int N>
-__device__ __forceinline__ void block_sums_f(float (&v)[N], float (*buf)[kCovWaves]) {
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-#pragma unroll
-    for (int i = 0; i < N; ++i) v[i] = wave_sum_f(v[i]);
-    if (lane == 0) {
-#pragma unroll
-        for (int i = 0; i < N; ++i) buf[i][wave] = v[i];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-        float s = 0.f;
-#pragma unroll
-        for (int w = 0; w < kCovWaves; ++w) s += buf[i][w];
-        v[i] = s;
-    }
-}
-template <int N>
-__device__ __forceinline__ void block_sums_i(int (&v)[N], int (*buf)[kCovWaves]) {
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-#pragma unroll
-    for (int i = 0; i < N; ++i) v[i] = wave_sum_i(v[i]);
-    if (lane == 0) {
-#pragma unroll
-        for (int i = 0; i < N; ++i) buf[i][wave] = v[i];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-        int s = 0;
-#pragma unroll
-        for (int w = 0; w < kCovWaves; ++w) s += buf[i][w];
-        v[i] = s;
-    }
-}
-
-// Exclusive ranks, in chunk-id order, of the flagged elements of R rows, and
-// each row's total.  cnt: [R][EPT * kCovWaves] ints, tot: [R].
-template <int R, int EPT>
-__device__ __forceinline__ void block_ranks(const bool (&flag)[R][EPT], int (&rank)[R][EPT], int (&total)[R],
-                                            int* cnt, int* tot) {
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    const uint64_t below = (1ull << lane) - 1ull;
-    uint64_t bal[R][EPT];
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-            bal[r][e] = __ballot(flag[r][e]);
-            if (lane == 0) cnt[(r * EPT + e) * kCovWaves + wave] = __popcll(bal[r][e]);
-        }
-    __syncthreads();
-    if (wave < R) {
-        // the counts of row `wave` in id order (e, then wave), scanned by one wave
-        constexpr int N = EPT * kCovWaves;
-        constexpr int P = (N + kWave - 1) / kWave;
-        int* c = cnt + wave * N;
-        int loc[P];
-        int s = 0;
-#pragma unroll
-        for (int p = 0; p < P; ++p) {
-            const int i = lane * P + p;
-            loc[p] = i < N ? c[i] : 0;
-            s += loc[p];
-        }
-        const int inc = wave_inclusive_scan(s);
-        int run = inc - s;
-#pragma unroll
-        for (int p = 0; p < P; ++p) {
-            const int i = lane * P + p;
-            if (i < N) c[i] = run;
-            run += loc[p];
-        }
-        if (lane == kWave - 1) tot[wave] = inc;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-#pragma unroll
-        for (int e = 0; e < EPT; ++e)
-            rank[r][e] = cnt[(r * EPT + e) * kCovWaves + wave] + __popcll(bal[r][e] & below);
-        total[r] = tot[r];
-    }
-    __syncthreads();   // cnt and tot are free again
-}
+using namespace blk;
+constexpr int kCovThreads = kBlkThreads;
+constexpr int kCovWaves = kBlkWaves;
 
 template <int EPT, int T>
 __global__ __launch_bounds__(kCovThreads) void k_cov_select(const float* __restrict__ scores, int C, float gamma,

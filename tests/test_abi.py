@@ -27,14 +27,14 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(lib, n), n
     assert {n for n, _, _ in b.EXPORTS} == set(names)
 
 
 def test_abi_version():
-    assert lib.dk_abi_version() == 8
+    assert lib.dk_abi_version() == 9
 
 
 def err():
@@ -315,4 +315,21 @@ def test_coverage_workspace_size():
     assert lib.dk_coverage_workspace_size(1, 1, 1, 100) == 512 + 2 * 256 + 256
     assert lib.dk_coverage_workspace_size(1, 1, 3, 100) == 0
     assert lib.dk_coverage_workspace_size(0, 1, 1, 100) == 0
+
+
+def capped(ids=FAKE, sc=NULL, cnt=NULL, B=2, Hkv=8, N=64, stride=64, cstride=1, res=FAKE, st=FAKE, S=128, cap=8,
+           step=3, slot=FAKE, ac=FAKE, asl=FAKE, acnt=FAKE, hc=NULL):
+    return lib.dk_capped_plan(ids, sc, cnt, B, Hkv, N, stride, cstride, res, st, S, cap, step, slot, ac, asl, acnt,
+                              hc, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ids=NULL), 1), (dict(res=NULL), 1), (dict(st=NULL), 1), (dict(slot=NULL), 1), (dict(acnt=NULL), 1),
+    (dict(B=0), 1), (dict(N=0), 1), (dict(S=0), 1), (dict(stride=63), 1), (dict(cnt=FAKE, cstride=0), 1),
+    (dict(cap=-1), 1), (dict(cap=(1 << 20) + 1), 1), (dict(ac=NULL), 1), (dict(asl=NULL), 1),
+    (dict(N=4097, stride=4097), 2), (dict(S=4097), 2),
+])
+def test_capped_plan_rejects(kw, status):
+    assert capped(**kw) == status, err()
+    assert err().startswith("dk_capped_plan")
 

@@ -10,6 +10,10 @@ cumulative masses allow within a derived fp32 bound (equal to the oracle's count
 away from that band), the kept ids are the oracle's best `count` chunks except at
 counted score near-ties, and the union of the ragged sets is exact against the
 oracle's union of the GPU's own sets.
+
+Capped eviction (dk_capped_plan) is integer work on given fp32 priorities: the
+new resident table, stamps, slots and transfers equal the oracle's capped_plan
+exactly, step after step of multi-step traces.
 """
 import numpy as np
 import pytest
@@ -272,4 +276,91 @@ def test_coverage_full_128k_sampled(dkb):
         assert torch.equal(u2[0, 0], uid[b, g]) and torch.equal(uc2[0], ucnt[b:b + 1, g])
         check_coverage(dkb, qh.contiguous(), lmh.contiguous(), 0.9, 1024, 1.0, "mean", True,
                        label=f"b64_l128k ({b}, {g})")
+
+
+# ----------------------------------------------------------------------------
+# delta selection with capped eviction
+# ----------------------------------------------------------------------------
+
+def run_capped_both(dkb, ids, score, count, res, st, cap, step, label=""):
+    """One plan step on the GPU (in place on res/st) and in the oracle; asserts equality."""
+    ref = O.capped_plan(ids.cpu().numpy(), None if score is None else score.cpu().numpy(),
+                        None if count is None else count.cpu().numpy(), res.cpu().numpy(), st.cpu().numpy(), cap,
+                        step)
+    slot, ac, asl, acnt, hc = dkb.capped_plan(ids, res, st, cap, step, sel_score=score, sel_count=count)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(res.cpu().numpy(), ref["resident"], err_msg=label)
+    np.testing.assert_array_equal(st.cpu().numpy(), ref["stamp"], err_msg=label)
+    np.testing.assert_array_equal(slot.cpu().numpy(), ref["sel_slot"], err_msg=label)
+    np.testing.assert_array_equal(ac.cpu().numpy(), ref["admit_chunk"], err_msg=label)
+    np.testing.assert_array_equal(asl.cpu().numpy(), ref["admit_slot"], err_msg=label)
+    np.testing.assert_array_equal(acnt.cpu().numpy(), ref["admit_count"], err_msg=label)
+    np.testing.assert_array_equal(hc.cpu().numpy(), ref["hit_count"], err_msg=label)
+    return ref
+
+
+def test_capped_plan_hand_fixture(dkb):
+    import json, os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "capped_plan_hand.json")) as f:
+        fx = json.load(f)
+    dev = dict(device="cuda")
+    for case in fx["cases"]:
+        ids = torch.tensor([[fx["sel_ids"]]], dtype=torch.int32, **dev)
+        sc = torch.tensor([[fx["sel_score"]]], dtype=torch.float32, **dev) if case["scores"] else None
+        res = torch.tensor([[fx["resident"]]], dtype=torch.int32, **dev)
+        st = torch.tensor([[fx["stamp"]]], dtype=torch.int32, **dev)
+        slot, ac, asl, acnt, hc = dkb.capped_plan(ids, res, st, case["cap"], fx["step"], sel_score=sc)
+        torch.cuda.synchronize()
+        assert res[0, 0].tolist() == case["resident"] and st[0, 0].tolist() == case["stamp"], case
+        assert slot[0, 0].tolist() == case["sel_slot"], case
+        assert ac[0, 0].tolist() == case["admit_chunk"] and asl[0, 0].tolist() == case["admit_slot"], case
+        assert int(acnt[0, 0]) == case["admit_count"] and int(hc[0, 0]) == case["hit_count"], case
+
+
+@pytest.mark.parametrize("B,H,N,S,C,scores", [
+    (2, 4, 12, 20, 40, True),       # small: many empties early, evictions later
+    (4, 8, 64, 96, 512, True),      # chunk-level working set, one query's k = 64
+    (2, 2, 64, 96, 300, False),     # no priorities: lower ids first
+    (1, 2, 3000, 4096, 6000, True), # four entries per thread
+])
+def test_capped_plan_trace(dkb, B, H, N, S, C, scores):
+    """A drifting predicted set over 10 steps, caps from 0 to unbounded, ragged counts and tied scores."""
+    rng = np.random.default_rng(50 + N)
+    dev = dict(device="cuda")
+    res = torch.full((B, H, S), -1, dtype=torch.int32, **dev)
+    st = torch.full((B, H, S), -1, dtype=torch.int32, **dev)
+    prev = [rng.choice(C, N, replace=False) for _ in range(B * H)]
+    for step in range(10):
+        rows = []
+        for r in range(B * H):
+            keep = prev[r][rng.random(N) < 0.7]                  # most of the set survives a step
+            fresh = rng.choice(np.setdiff1d(np.arange(C), keep), N - len(keep), replace=False)
+            prev[r] = np.concatenate([keep, fresh])
+            rows.append(np.sort(prev[r]))
+        ids = torch.from_numpy(np.stack(rows).reshape(B, H, N).astype(np.int32)).to(**dev)
+        sc = torch.from_numpy(np.round(rng.standard_normal((B, H, N)), 1).astype(np.float32)).to(**dev) \
+            if scores else None
+        cnt = torch.from_numpy(rng.integers(N // 2, N + 1, size=(B, H)).astype(np.int32)).to(**dev)
+        cap = [0, 1, 4, N // 3, 10 ** 5][step % 5]
+        print(f"trace B={B} H={H} N={N} S={S} step {step} cap {cap}", flush=True)
+        run_capped_both(dkb, ids, sc, cnt, res, st, cap, step, label=f"step {step}")
+
+
+def test_capped_plan_from_selection(dkb):
+    """The speculative query's top-k row (a strided view) and its fp32 scores drive the plan;
+    then a coverage row with ragged counts (count stride T)."""
+    w = workload("llama8b_l32k", 4, 8192)
+    q = synth.make_queries(w, 17, device="cuda")
+    K, _ = synth.make_kv_pool(w, 17, device="cuda", q0=q)
+    lm = dkb.build_landmarks(K, w.chunk)
+    idx, sc = dkb.score_topk(q, lm, w.k, w.scale)
+    S = 96
+    res = torch.full((w.B, w.Hkv, S), -1, dtype=torch.int32, device="cuda")
+    st = torch.full((w.B, w.Hkv, S), -1, dtype=torch.int32, device="cuda")
+    run_capped_both(dkb, idx[:, :, 1], sc[:, :, 1], None, res, st, 16, 0, label="spec row")
+    run_capped_both(dkb, idx[:, :, 0], sc[:, :, 0], None, res, st, 16, 1, label="real row")
+    ci, cc, cs = dkb.score_coverage(q, lm, 0.5, 128, 1.0)
+    torch.cuda.synchronize()
+    run_capped_both(dkb, ci[:, :, 0], cs[:, :, 0], cc[:, :, 0], res, st, 8, 2,   # -inf padding is never read
+                    label="coverage row")
 
