@@ -55,6 +55,16 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB + 1 GiB device copy (dk_gather_kv over consecutive "
                          "chunks) three times: the known-size reference for HBM byte counters")
+    ap.add_argument("--selection", choices=("landmark", "minmax", "coverage", "capped"), default="landmark",
+                    help="chunk selection of the step: landmark top-k (default), top-k by min/max summary "
+                         "bounds, coverage budgets, or landmark top-k plus a capped-eviction working-set plan")
+    ap.add_argument("--gamma", type=float, default=0.9, help="coverage: fraction of the estimated mass")
+    ap.add_argument("--k-max", type=int, default=None, help="coverage: most chunks per query (default 2k)")
+    ap.add_argument("--cov-scale", type=float, default=0.5,
+                    help="coverage: logit scale of the mass estimate (the synthetic keys' logits are flat at "
+                         "1/sqrt(d))")
+    ap.add_argument("--cap", type=int, default=8, help="capped: admissions per step and KV head")
+    ap.add_argument("--slots", type=int, default=None, help="capped: working-set slots per (b, g) (default 4k)")
     ap.add_argument("--lookahead", type=int, default=2,
                     help="host-pool workloads: layers between a selection/transfer and its attention")
     return ap.parse_args()
@@ -435,6 +445,262 @@ def bench_mla(args, w):
     print(json.dumps(res), flush=True)
 
 
+METRIC_VARIANT = {
+    "minmax": "dual-query sparse decode steps/s, chunks ranked by min/max summary bounds, B=64 L=128K",
+    "coverage": "dual-query sparse decode steps/s, coverage budgets (smallest chunk sets reaching gamma of the "
+                "estimated mass), B=64 L=128K",
+    "capped": "dual-query sparse decode steps/s with a capped-eviction working-set plan per layer, B=64 L=128K",
+}
+
+
+def bench_variant(args, w):
+    """The HBM-pool step with a selection variant: per layer, the variant's selection
+    and union (plus, for `capped`, the working-set plan of the speculative query's
+    top-k), then attention of both queries over their own chunks."""
+    import numpy as np
+    import torch
+
+    from sparse_kv_retrieval_amd import binding as dkb
+    from sparse_kv_retrieval_amd import synth
+
+    dev, sel = "cuda", args.selection
+    B, T, Hq, Hkv, d, C, k = w.B, w.T, w.Hq, w.Hkv, w.d, w.C, w.k
+    i32 = dict(dtype=torch.int32, device=dev)
+    t0 = time.time()
+    # layer l's queries drift l steps from the planted layer-0 queries, so every layer
+    # meets the pool's heavy hitters (independent queries see flat chunk masses)
+    qs = synth.make_query_sequence(w, args.seed, w.layers, device=dev)
+    K, V = synth.make_kv_pool(w, args.seed, device=dev, q0=qs[0])
+    k_max = args.k_max or 2 * k
+    N = T * (k_max if sel == "coverage" else k)
+    union_ids = torch.empty(B, Hkv, N, **i32)
+    member = torch.empty(B, Hkv, N, dtype=torch.uint8, device=dev)
+    count = torch.empty(B, Hkv, **i32)
+    overlap = torch.empty(B, Hkv, **i32)
+    ws_attn = torch.empty(max(dkb.attn_workspace_size(B, Hkv, T, Hq, d, N, w.chunk), 1), dtype=torch.uint8,
+                          device=dev)
+    out = torch.empty(B, T, Hq, d, dtype=torch.float32, device=dev)
+    lse = torch.empty(B, T, Hq, dtype=torch.float32, device=dev)
+    summary_bytes = 0
+    if sel == "minmax":
+        kmin, kmax = dkb.build_minmax(K, w.chunk)
+        summary_bytes = kmin.nbytes + kmax.nbytes
+        topk_idx = torch.empty(B, Hkv, T, k, **i32)
+        ws_sel = torch.empty(dkb.index_topk_workspace_size(B, Hkv, T, C), dtype=torch.uint8, device=dev)
+    else:
+        lm = dkb.build_landmarks(K, w.chunk)
+        summary_bytes = lm.nbytes
+    if sel == "coverage":
+        cov_idx = torch.empty(B, Hkv, T, k_max, **i32)
+        cov_cnt = torch.empty(B, Hkv, T, **i32)
+        ws_sel = torch.empty(dkb.coverage_workspace_size(B, Hkv, T, C), dtype=torch.uint8, device=dev)
+    if sel == "capped":
+        shadow = dkb.build_landmark_shadow(lm)
+        topk_idx = torch.empty(B, Hkv, T, k, **i32)
+        topk_score = torch.empty(B, Hkv, T, k, dtype=torch.float32, device=dev)
+        ws_sel = torch.empty(max(dkb.score_topk_workspace_size(B, Hkv, T, C, k, True), 1), dtype=torch.uint8,
+                             device=dev)
+        S = args.slots or 4 * k
+        resident = torch.full((w.layers, B, Hkv, S), -1, **i32)
+        stamp = torch.full((w.layers, B, Hkv, S), -1, **i32)
+        sel_slot = torch.empty(B, Hkv, k, **i32)
+        admit_chunk = torch.empty(B, Hkv, max(args.cap, 1), **i32)
+        admit_slot = torch.empty(B, Hkv, max(args.cap, 1), **i32)
+        admit_count = torch.empty(w.layers, B, Hkv, **i32)
+        hit_count = torch.empty(w.layers, B, Hkv, **i32)
+    torch.cuda.synchronize()
+    print(f"[bench] {sel} inputs ready in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+
+    plan_step = [0]
+
+    def select(l):
+        q = qs[l]
+        if sel == "minmax":
+            dkb.score_topk_minmax(q, kmin, kmax, k, w.scale, topk_idx=topk_idx, union=True, union_ids=union_ids,
+                                  member=member, count=count, overlap=overlap, ws=ws_sel, want_scores=False)
+        elif sel == "coverage":
+            dkb.score_coverage(q, lm, args.gamma, k_max, args.cov_scale, sel_idx=cov_idx, sel_count=cov_cnt,
+                               union=True, union_ids=union_ids, member=member, count=count, overlap=overlap,
+                               ws=ws_sel, want_scores=False)
+        else:
+            dkb.score_topk_union(q, lm, k, w.scale, dkb.DK_REDUCE_MEAN, topk_idx, topk_score, union_ids, member,
+                                 count, overlap, ws_sel, shadow=shadow)
+
+    def plan(l):
+        dkb.capped_plan(topk_idx[:, :, 1], resident[l], stamp[l], args.cap, plan_step[0],
+                        sel_score=topk_score[:, :, 1], sel_slot=sel_slot, admit_chunk=admit_chunk,
+                        admit_slot=admit_slot, admit_count=admit_count[l], hit_count=hit_count[l])
+
+    def attend(l):
+        dkb.sparse_decode_attn(qs[l], K, V, union_ids, member, count, w.chunk, w.scale, out=out, lse=lse,
+                               ws=ws_attn)
+
+    calls = ("select", "plan", "attn") if sel == "capped" else ("select", "attn")
+    fns = {"select": select, "plan": plan, "attn": attend}
+
+    # per-layer union sizes (deterministic for the stateless selections)
+    sel_chunks, ov = [], []
+    for l in range(w.layers):
+        select(l)
+        sel_chunks.append(int(count.sum().item()))
+        ov.append(overlap.double().mean().item())
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(w.layers)]
+          for _ in range(args.steps)]
+
+    def step(record):
+        for l in range(w.layers):
+            e = ev[record - 1][l] if record else None
+            if record:
+                e[0].record()
+            for i, c in enumerate(calls):
+                fns[c](l)
+                if record:
+                    e[i + 1].record()
+        plan_step[0] += 1
+
+    for _ in range(args.warmup):
+        step(0)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for s_ in range(args.steps):
+        step(s_ + 1)
+    end.record()
+    torch.cuda.synchronize()
+    call_ms = {c: 0.0 for c in calls}
+    step_ms = []
+    for s_ in range(args.steps):
+        for l in range(w.layers):
+            for i, c in enumerate(calls):
+                call_ms[c] += ev[s_][l][i].elapsed_time(ev[s_][l][i + 1])
+        step_ms.append(ev[s_][0][0].elapsed_time(ev[s_][w.layers - 1][len(calls)]))
+    ms_per_step = start.elapsed_time(end) / args.steps
+
+    chunk_bytes = w.chunk_kv_bytes()
+    sel_bytes_step = sum(sel_chunks) * chunk_bytes
+    q_bytes = B * T * Hq * d * 4
+    rows_bytes = 2 * B * Hkv * T * C * 4            # fp32 score rows written, then read
+    if sel == "capped":
+        score_bytes = (w.landmark_bytes() // 2 + rows_bytes + B * Hkv * T * k * d * 4 + q_bytes
+                       + B * Hkv * T * k * 4 * 4)
+    else:
+        score_bytes = summary_bytes + rows_bytes + q_bytes + B * Hkv * N * 5
+    S_ = args.slots or 4 * k
+    per_call_bytes = {
+        "select": score_bytes,
+        "plan": B * Hkv * (k * 8 + S_ * 16 + k * 4 + 2 * args.cap * 4),
+        "attn": sel_bytes_step / w.layers,
+    }
+    n_launch = args.steps * w.layers
+    kernels = {}
+    for c in calls:
+        avg_ms = call_ms[c] / n_launch
+        gbps = per_call_bytes[c] / (avg_ms * 1e-3) / 1e9
+        kernels[c] = {"avg_us": round(avg_ms * 1e3, 2), "bytes_per_launch": int(per_call_bytes[c]),
+                      "GBps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+    dominant = max(kernels, key=lambda c: kernels[c]["avg_us"])
+    kd = kernels[dominant]
+    roofline = {"bound": "hbm", "kernel": dominant, "achieved": kd["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(kd["GBps"] / HBM_PEAK_GBPS, 4), "traffic": None}
+    attn_gbps = sel_bytes_step / (call_ms["attn"] / args.steps * 1e-3) / 1e9
+    cfg = {"workload": w.name, "B": B, "L": w.L, "Hq": Hq, "Hkv": Hkv, "d": d, "chunk": w.chunk, "k": k, "T": T,
+           "layers": w.layers, "seed": args.seed, "selection": sel, "queries": "drifting sequence over layers"}
+    if sel == "coverage":
+        cfg.update(gamma=args.gamma, k_max=k_max, estimate_scale=args.cov_scale)
+    if sel == "capped":
+        cfg.update(cap=args.cap, slots=S_)
+    res = {
+        "metric": METRIC_VARIANT[sel],
+        "value": round(1000.0 / ms_per_step, 3),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": cfg,
+        "ms_per_step_median": round(float(np.median(step_ms)), 4),
+        "selected_kv_GBps": round(attn_gbps, 1),
+        "selected_kv_frac_hbm_peak": round(attn_gbps / HBM_PEAK_GBPS, 4),
+        "mean_union_chunks": round(sum(sel_chunks) / (w.layers * B * Hkv), 2),
+        "mean_overlap_chunks": round(float(np.mean(ov)), 2),
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    if sel == "coverage":
+        res["mean_kept_chunks_per_query"] = round(float(cov_cnt.double().mean().item()), 2)
+    if sel == "capped":
+        res["mean_admits_per_head_step"] = round(float(admit_count.double().mean().item()), 2)
+        res["mean_hits_per_head_step"] = round(float(hit_count.double().mean().item()), 2)
+    res["cpu_baseline"] = cpu_baseline_variant(w, sel, qs, K, V, args) if args.cpu_seconds > 0 else None
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline_variant(w, sel, qs, K, V, args):
+    """Time the fp64 CPU oracle of the variant step (selection, union, and for
+    `capped` the plan from an empty working set, then attention) on sampled
+    (request, KV head, layer) units, single thread."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import dualkv_oracle as O
+    from sparse_kv_retrieval_amd import synth
+
+    rng = np.random.default_rng(args.seed)
+    pairs = [(int(rng.integers(w.B)), int(rng.integers(w.Hkv))) for _ in range(4)]
+    per_pair = args.cpu_seconds / len(pairs)
+    k_max = args.k_max or 2 * w.k
+    S = args.slots or 4 * w.k
+    units, spent = 0, 0.0
+    with threadpool_limits(1):
+        for b, g in pairs:
+            Kh = synth.to_numpy_f64(K[b:b + 1, g:g + 1])
+            Vh = synth.to_numpy_f64(V[b:b + 1, g:g + 1])
+            if sel == "minmax":
+                mn, mx = O.chunk_minmax(Kh, w.chunk)        # summaries: built once, not timed
+            else:
+                lm = O.chunk_landmarks(Kh, w.chunk)
+            res, st = np.full((1, 1, S), -1), np.full((1, 1, S), -1)
+            pair_spent, layer = 0.0, 0
+            while pair_spent < per_pair:
+                qh = qs[layer % len(qs)][b:b + 1, :, g * w.G:(g + 1) * w.G].cpu().numpy().astype(np.float64)
+                t0 = time.perf_counter()
+                if sel == "minmax":
+                    chosen = O.minmax_topk(qh, mn, mx, w.k, w.scale)
+                    O.union_select(chosen)
+                elif sel == "coverage":
+                    s = O.chunk_scores(qh, lm, args.cov_scale, "mean")
+                    idx, n = O.coverage_select(s, args.gamma, k_max)
+                    O.union_select_ragged(idx, n)
+                    chosen = [[[idx[0, 0, t, :n[0, 0, t]] for t in range(w.T)]]]
+                else:
+                    s = O.chunk_scores(qh, lm, w.scale, "mean")
+                    chosen = O.topk_chunks(s, w.k)
+                    O.union_select(chosen)
+                    sc = np.take_along_axis(s, chosen, axis=-1)
+                    r = O.capped_plan(chosen[:, :, 1], sc[:, :, 1], None, res, st, args.cap, layer)
+                    res, st = r["resident"], r["stamp"]
+                if sel == "coverage":
+                    for t in range(w.T):
+                        sel_t = np.asarray(chosen[0][0][t])[None, None, None]
+                        O.sparse_attention(qh[:, t:t + 1], Kh, Vh, sel_t, w.chunk, w.scale)
+                else:
+                    O.sparse_attention(qh, Kh, Vh, chosen, w.chunk, w.scale)
+                pair_spent += time.perf_counter() - t0
+                units += 1
+                layer += 1
+            spent += pair_spent
+    per_unit = spent / units
+    per_step = per_unit * w.B * w.Hkv * w.layers
+    return {"value": 1.0 / per_step, "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{units} (request, KV head, layer) units of the {w.name} {sel} step ({spent:.1f} s, "
+                      f"{per_unit * 1e3:.1f} ms each), scaled to {w.B * w.Hkv * w.layers} units per step; "
+                      f"summaries precomputed"}
+
+
 def cpu_baseline_mla(w, qi, q, Kidx, lat, gpu_topk, budget_s):
     """Time the fp64 CPU oracle (indexer top-k, union, latent attention) on whole
     sampled requests, single thread; compare the sampled selections with the GPU's."""
@@ -520,6 +786,9 @@ def main():
         return
     if w.host_pool:
         bench_host_pool(args, w)
+        return
+    if args.selection != "landmark":
+        bench_variant(args, w)
         return
 
     t0 = time.time()

@@ -152,4 +152,56 @@ __device__ __forceinline__ void block_best(const uint32_t (&key)[EPT], const boo
 }
 
 }  // namespace blk
+
+// Wave-level versions: one wave owns a whole row (element j = lane + 64 e), so no
+// barrier is needed.  Sums are a fixed tree (lane-serial, DPP sums of 16-lane
+// rows, then the four rows read from lanes 0, 16, 32, 48 and added in order):
+// deterministic, identical in every lane, and monotone in every term.
+namespace wv {
+
+__device__ __forceinline__ float sum_f(float v) {
+    v = dpp_group_sum<16>(v);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+// integer sums below 2^24 are exact in fp32
+__device__ __forceinline__ int sum_i(int v) { return (int)sum_f((float)v); }
+__device__ __forceinline__ uint32_t max_u(uint32_t v) {
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, kWave));
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+}
+__device__ __forceinline__ uint64_t lanes_below() { return (1ull << (threadIdx.x & (kWave - 1))) - 1ull; }
+
+// The best n (1 <= n <= flagged count) of the flagged elements by key (larger
+// first), ties to the lower element index (lane + 64 e).
+template <int EPL>
+__device__ __forceinline__ void best(const uint32_t (&key)[EPL], const bool (&flag)[EPL], int n, bool (&take)[EPL]) {
+    uint32_t v = 0u;   // the largest v with at least n flagged keys >= v
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = v | (1u << bit);
+        int part = 0;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) part += flag[e] && key[e] >= cand ? 1 : 0;
+        if (sum_i(part) >= n) v = cand;
+    }
+    int gt = 0;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) gt += flag[e] && key[e] > v ? 1 : 0;
+    const int room = n - sum_i(gt);
+    const uint64_t below = lanes_below();
+    int pre = 0;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+        const bool tie = flag[e] && key[e] == v;
+        const uint64_t tb = __ballot(tie);
+        take[e] = flag[e] && (key[e] > v || (tie && pre + __popcll(tb & below) < room));
+        pre += __popcll(tb);
+    }
+}
+
+}  // namespace wv
 }  // namespace dk

@@ -22,7 +22,8 @@
 // key (score; inverted stamp) with ties to the lower index, by count bisection;
 // both are then ranked in index order by ballots and paired rank to rank.
 // resident and stamp are read whole before any of them is written, so the plan
-// updates them in place.
+// updates them in place.  Up to 512 entries and slots one wave does the same work
+// alone (index = lane + 64 e), with wave reductions instead of block barriers.
 #include "dk_block.h"
 
 namespace dk {
@@ -185,6 +186,156 @@ __global__ __launch_bounds__(kBlkThreads) void k_capped_plan(
     }
 }
 
+template <int EPL>
+__global__ __launch_bounds__(kWave) void k_capped_wave(
+    const int32_t* __restrict__ sel_ids, const float* __restrict__ sel_score, const int32_t* __restrict__ sel_count,
+    int N, int64_t sel_stride, int64_t count_stride, int32_t* __restrict__ resident, int32_t* __restrict__ stamp,
+    int S, int cap, int32_t step, int32_t* __restrict__ sel_slot, int32_t* __restrict__ admit_chunk,
+    int32_t* __restrict__ admit_slot, int32_t* __restrict__ admit_count, int32_t* __restrict__ hit_count) {
+    extern __shared__ int sm_cw[];
+    int* pid = sm_cw;          // [N] predicted ids (INT_MAX past the count)
+    int* hitslot = pid + N;    // [N] slot holding each predicted id, or -1
+    int* tslot = hitslot + N;  // [min(N, S)] the chosen targets in slot order
+    const int64_t bg = blockIdx.x;
+    const int lane = threadIdx.x;
+    const uint64_t below = wv::lanes_below();
+    const int32_t* ids = sel_ids + bg * sel_stride;
+    const float* scr = sel_score ? sel_score + bg * sel_stride : nullptr;
+    const int n = sel_count ? min(max(sel_count[bg * count_stride], 0), N) : N;
+    int32_t* res = resident + bg * S;
+    int32_t* st = stamp + bg * S;
+
+    int my_id[EPL], my_res[EPL], my_st[EPL];
+    uint32_t my_key[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+        const int i = lane + e * kWave;
+        my_id[e] = i < n ? ids[i] : -1;
+        my_key[e] = i < n && scr ? score_key(scr[i]) : 1u;   // no scores: all tied, lower id first
+        if (i < N) {
+            pid[i] = i < n ? my_id[e] : INT32_MAX;
+            hitslot[i] = -1;
+        }
+        my_res[e] = i < S ? res[i] : -1;
+        my_st[e] = i < S ? st[i] : 0;
+    }
+    __syncthreads();
+    bool hit[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+        const int s = lane + e * kWave;
+        hit[e] = false;
+        if (s < S && my_res[e] >= 0) {
+            int lo = 0, hi = n;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (pid[mid] < my_res[e]) lo = mid + 1;
+                else hi = mid;
+            }
+            if (lo < n && pid[lo] == my_res[e]) {
+                hitslot[lo] = s;
+                hit[e] = true;
+            }
+        }
+    }
+    __syncthreads();
+    bool miss[EPL], emp[EPL], occ[EPL];
+    int hs[EPL];
+    int c0 = 0, c1 = 0, c2 = 0;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+        const int i = lane + e * kWave;
+        hs[e] = i < n ? hitslot[i] : -1;
+        miss[e] = i < n && hs[e] < 0;
+        emp[e] = i < S && my_res[e] < 0;
+        occ[e] = i < S && my_res[e] >= 0 && !hit[e];
+        c0 += miss[e] ? 1 : 0;
+        c1 += emp[e] ? 1 : 0;
+        c2 += occ[e] ? 1 : 0;
+    }
+    const int n_miss = wv::sum_i(c0), n_empty = wv::sum_i(c1), n_occ = wv::sum_i(c2);
+    const int a = min(min(cap, n_miss), n_empty + n_occ);
+
+    bool adm[EPL], tgt[EPL];
+    if (a == n_miss) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) adm[e] = miss[e];
+    } else if (a == 0) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) adm[e] = false;
+    } else {
+        wv::best<EPL>(my_key, miss, a, adm);
+    }
+    if (a == 0) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) tgt[e] = false;
+    } else if (a <= n_empty) {
+        int pre = 0;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            const uint64_t b = __ballot(emp[e]);
+            tgt[e] = emp[e] && pre + __popcll(b & below) < a;
+            pre += __popcll(b);
+        }
+    } else if (a - n_empty == n_occ) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) tgt[e] = emp[e] || occ[e];
+    } else {
+        uint32_t old[EPL];   // larger = selected longer ago
+        bool take[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) old[e] = ~((uint32_t)my_st[e] ^ 0x80000000u);
+        wv::best<EPL>(old, occ, a - n_empty, take);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) tgt[e] = emp[e] || take[e];
+    }
+
+    // pair the admitted misses (id order) with the targets (slot order)
+    int ra[EPL];
+    int tpre = 0, apre = 0;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+        const uint64_t tb = __ballot(tgt[e]);
+        const int rt = tpre + __popcll(tb & below);
+        if (tgt[e] && rt < a) tslot[rt] = lane + e * kWave;
+        tpre += __popcll(tb);
+        const uint64_t ab = __ballot(adm[e]);
+        ra[e] = apre + __popcll(ab & below);
+        apre += __popcll(ab);
+    }
+    __syncthreads();
+
+    int32_t* oslot = sel_slot + bg * N;
+    int32_t* ac = admit_chunk ? admit_chunk + bg * cap : nullptr;
+    int32_t* as = admit_slot ? admit_slot + bg * cap : nullptr;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+        const int i = lane + e * kWave;
+        if (i < S && hit[e]) st[i] = step;
+        if (i < N) {
+            int slot = -1;
+            if (hs[e] >= 0) {
+                slot = hs[e];
+            } else if (adm[e] && ra[e] < a) {
+                slot = tslot[ra[e]];
+                res[slot] = my_id[e];
+                st[slot] = step;
+                ac[ra[e]] = my_id[e];
+                as[ra[e]] = slot;
+            }
+            oslot[i] = slot;
+        }
+    }
+    for (int r = a + lane; r < cap; r += kWave) {
+        ac[r] = -1;
+        as[r] = -1;
+    }
+    if (lane == 0) {
+        admit_count[bg] = a;
+        if (hit_count) hit_count[bg] = n - n_miss;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_capped_plan(const int32_t* sel_ids, const float* sel_score, const int32_t* sel_count, int B,
@@ -198,12 +349,20 @@ hipError_t launch_capped_plan(const int32_t* sel_ids, const float* sel_score, co
     hipLaunchKernelGGL(k_capped_plan<E_>, grid, dim3(kBlkThreads), lds, st, sel_ids, sel_score, sel_count, N,    \
                        sel_stride, count_stride, resident, stamp, S, cap, step, sel_slot, admit_chunk, admit_slot, \
                        admit_count, hit_count)
+#define DK_CW(E_)                                                                                                   \
+    hipLaunchKernelGGL(k_capped_wave<E_>, grid, dim3(kWave), lds, st, sel_ids, sel_score, sel_count, N, sel_stride, \
+                       count_stride, resident, stamp, S, cap, step, sel_slot, admit_chunk, admit_slot, admit_count,  \
+                       hit_count)
     static_assert(kCappedMaxN <= 4 * kBlkThreads, "four entries per thread at most");
-    if (m <= kBlkThreads) DK_CP(1);
+    if (m <= 2 * kWave) DK_CW(2);
+    else if (m <= 4 * kWave) DK_CW(4);
+    else if (m <= 8 * kWave) DK_CW(8);
+    else if (m <= kBlkThreads) DK_CP(1);
     else if (m <= 2 * kBlkThreads) DK_CP(2);
     else if (m <= kCappedMaxN) DK_CP(4);
     else return hipErrorInvalidValue;
 #undef DK_CP
+#undef DK_CW
     return hipGetLastError();
 }
 

@@ -21,6 +21,12 @@
 // k_max is replaced by the top k_max, found by a second bisection on counts.
 // Tie ranks and output positions come from ballots and one wave's scan of the
 // per-wave counts.
+//
+// Rows of up to 4096 chunks take the wave form instead: one wave per row with
+// its 64 * EPL scores and masses in registers (chunk id = lane + 64 e), every
+// sum a wave reduction (DPP row sums, then four lanes in order), so the
+// bisections need no barrier; the T waves of a (b, g) exchange their 64-bit
+// selection masks through LDS once for the union.
 #include "dk_block.h"
 
 namespace dk {
@@ -242,6 +248,157 @@ __global__ __launch_bounds__(kCovThreads) void k_cov_select(const float* __restr
     }
 }
 
+template <int EPL, int T>
+__global__ __launch_bounds__(kWave * T) void k_cov_wave(const float* __restrict__ scores, int C, float gamma,
+                                                       int k_max, int32_t* __restrict__ sel_idx,
+                                                       int32_t* __restrict__ sel_count, float* __restrict__ sel_score,
+                                                       UnionOut un) {
+    __shared__ uint64_t s_mask[T][EPL];
+    __shared__ int s_n[T];
+    const int64_t bg = blockIdx.x;
+    const int t = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const uint64_t below = wv::lanes_below();
+    const float* row = scores + (bg * T + t) * C;
+    uint32_t key[EPL];
+    float w[EPL];
+    uint32_t m = 0u;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+        const int j = lane + e * kWave;
+        key[e] = j < C ? score_key(row[j]) : 0u;   // a real (non-NaN) score's key is > 0
+        m = max(m, key[e]);
+    }
+    const float smax = key_score(wv::max_u(m));
+    float z = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+        w[e] = key[e] ? expf(key_score(key[e]) - smax) : 0.f;   // tied chunks: recomputed below alike
+        z += w[e];
+    }
+    const float target = gamma * wv::sum_f(z);
+
+    uint32_t v = 0u;   // threshold key
+    int n = 0, rtie = 0;
+    bool over = gamma >= 1.0f;   // every chunk, so the top k_max
+    if (!over) {
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = v | (1u << bit);
+            float part = 0.f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) part += key[e] >= cand ? w[e] : 0.f;
+            if (wv::sum_f(part) >= target) v = cand;
+        }
+        float above = 0.f;
+        int gt = 0, eq = 0;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            above += key[e] > v ? w[e] : 0.f;
+            gt += key[e] > v ? 1 : 0;
+            eq += key[e] == v ? 1 : 0;
+        }
+        above = wv::sum_f(above);
+        gt = wv::sum_i(gt);
+        eq = wv::sum_i(eq);
+        const float wt = expf(key_score(v) - smax);
+        const float need = (target - above) / wt;   // > 0: the mass above v is below the target
+        int r = eq;
+        if (wt > 0.f && need < (float)r) r = max(1, (int)ceilf(need));
+        rtie = r;
+        n = gt + r;
+        over = n > k_max;
+    }
+    if (over) {
+        uint32_t vc = 0u;   // the largest key with at least k_max chunks at or above it
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = vc | (1u << bit);
+            int part = 0;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) part += key[e] >= cand ? 1 : 0;
+            if (wv::sum_i(part) >= k_max) vc = cand;
+        }
+        int gt = 0;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) gt += key[e] > vc ? 1 : 0;
+        v = vc;
+        rtie = k_max - wv::sum_i(gt);
+        n = k_max;
+    }
+
+    // kept: above v, or tied at v with one of the rtie lowest ids; written in id order
+    int32_t* oi = sel_idx + (bg * T + t) * k_max;
+    float* os = sel_score ? sel_score + (bg * T + t) * k_max : nullptr;
+    int tpre = 0, spre = 0;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+        const bool tie = key[e] == v;
+        const uint64_t tb = __ballot(tie);
+        const bool sel = key[e] > v || (tie && tpre + __popcll(tb & below) < rtie);
+        tpre += __popcll(tb);
+        const uint64_t sb = __ballot(sel);
+        const int pos = spre + __popcll(sb & below);
+        spre += __popcll(sb);
+        if (sel && pos < k_max) {   // at most k_max are kept: the guard never fires
+            oi[pos] = lane + e * kWave;
+            if (os) os[pos] = key_score(key[e]);
+        }
+        if (lane == 0) s_mask[t][e] = sb;
+    }
+    for (int i = n + lane; i < k_max; i += kWave) {
+        oi[i] = -1;
+        if (os) os[i] = -INFINITY;
+    }
+    if (lane == 0) {
+        sel_count[bg * T + t] = n;
+        s_n[t] = n;
+    }
+    if (!un.ids) return;
+    __syncthreads();
+    if (t != 0) return;
+    // lane e merges mask word e: chunks 64 e + bit, in ascending order
+    const int slots = T * k_max;
+    uint64_t m0 = 0ull, m1 = 0ull;
+    if (lane < EPL) {
+        m0 = s_mask[0][lane];
+        m1 = s_mask[T - 1][lane];
+    }
+    uint64_t um = m0 | m1;
+    const int c = __popcll(um);
+    const int inc = wave_inclusive_scan(c);
+    int pos = inc - c;
+    const int total = __builtin_amdgcn_readlane(inc, kWave - 1);
+    int32_t* ui = un.ids + bg * slots;
+    uint8_t* mb = un.member + bg * slots;
+    while (um) {
+        const int bit = __builtin_ctzll(um);
+        um &= um - 1ull;
+        if (pos < slots) {
+            ui[pos] = lane * kWave + bit;
+            mb[pos] = (uint8_t)(((m0 >> bit) & 1ull) | (T == 2 ? ((m1 >> bit) & 1ull) << 1 : 0ull));
+        }
+        ++pos;
+    }
+    for (int i = total + lane; i < slots; i += kWave) {
+        ui[i] = -1;
+        mb[i] = 0;
+    }
+    if (lane == 0) {
+        un.count[bg] = total;
+        if (un.overlap) un.overlap[bg] = T == 2 ? s_n[0] + s_n[1] - total : s_n[0];
+    }
+}
+
+template <int EPL>
+hipError_t launch_cov_wave(int T, unsigned grid, hipStream_t st, const float* scores, int C, float gamma, int k_max,
+                           int32_t* sel_idx, int32_t* sel_count, float* sel_score, const UnionOut& un) {
+    if (T == 2)
+        hipLaunchKernelGGL((k_cov_wave<EPL, 2>), dim3(grid), dim3(2 * kWave), 0, st, scores, C, gamma, k_max, sel_idx,
+                           sel_count, sel_score, un);
+    else
+        hipLaunchKernelGGL((k_cov_wave<EPL, 1>), dim3(grid), dim3(kWave), 0, st, scores, C, gamma, k_max, sel_idx,
+                           sel_count, sel_score, un);
+    return hipGetLastError();
+}
+
 template <int EPT>
 hipError_t launch_cov(int T, unsigned grid, hipStream_t st, const float* scores, int C, float gamma, int k_max,
                       int32_t* sel_idx, int32_t* sel_count, float* sel_score, const UnionOut& un) {
@@ -267,9 +424,9 @@ hipError_t launch_coverage(const float* q, int B, int T, int Hq, const void* lm,
     const UnionOut none{nullptr, nullptr, nullptr, nullptr};
     const UnionOut& u = un ? *un : none;
     const float* scores = (const float*)ws;
-    if (C <= 1 * kCovThreads) return launch_cov<1>(T, grid, st, scores, C, gamma, k_max, sel_idx, sel_count, sel_score, u);
-    if (C <= 2 * kCovThreads) return launch_cov<2>(T, grid, st, scores, C, gamma, k_max, sel_idx, sel_count, sel_score, u);
-    if (C <= 4 * kCovThreads) return launch_cov<4>(T, grid, st, scores, C, gamma, k_max, sel_idx, sel_count, sel_score, u);
+    if (C <= 4 * kWave) return launch_cov_wave<4>(T, grid, st, scores, C, gamma, k_max, sel_idx, sel_count, sel_score, u);
+    if (C <= 16 * kWave) return launch_cov_wave<16>(T, grid, st, scores, C, gamma, k_max, sel_idx, sel_count, sel_score, u);
+    if (C <= 64 * kWave) return launch_cov_wave<64>(T, grid, st, scores, C, gamma, k_max, sel_idx, sel_count, sel_score, u);
     if (C <= 8 * kCovThreads) return launch_cov<8>(T, grid, st, scores, C, gamma, k_max, sel_idx, sel_count, sel_score, u);
     if (C <= kCoverageMaxC) return launch_cov<16>(T, grid, st, scores, C, gamma, k_max, sel_idx, sel_count, sel_score, u);
     return hipErrorInvalidValue;

@@ -221,6 +221,8 @@ def pool_landmarks(dkb, w, seed):
     ("llama8b_l32k", 2, 4096, 0.7, 128, 1.0, "mean", "bf16", False),
     ("llama8b_l32k", 3, 40000, 0.8, 600, 1.0, "mean", "f32", True),   # C = 1250: a ragged second slab
     ("llama8b_l32k", 1, 32768, 1.0, 300, None, "mean", "f32", True),  # gamma 1: the top k_max
+    ("llama8b_l32k", 1, 160000, 0.6, 400, 1.0, "mean", "f32", True),  # C = 5000: the block form
+    ("llama8b_l32k", 2, 22400, 0.6, 200, 0.5, "max", "f32", True),    # C = 700: 16 per lane
 ])
 def test_coverage(dkb, name, B, L, gamma, k_max, scale, reduce, dtype, union):
     w = workload(name, B, L)
@@ -321,7 +323,11 @@ def test_capped_plan_hand_fixture(dkb):
     (2, 4, 12, 20, 40, True),       # small: many empties early, evictions later
     (4, 8, 64, 96, 512, True),      # chunk-level working set, one query's k = 64
     (2, 2, 64, 96, 300, False),     # no priorities: lower ids first
-    (1, 2, 3000, 4096, 6000, True), # four entries per thread
+    (1, 2, 3000, 4096, 6000, True), # four entries per thread of a block
+    (2, 4, 64, 256, 1024, True),    # one wave, four entries per lane
+    (1, 4, 300, 500, 2000, True),   # one wave, eight entries per lane
+    (1, 2, 600, 1000, 3000, True),  # a block, one entry per thread
+    (1, 2, 1500, 2000, 5000, True), # a block, two entries per thread
 ])
 def test_capped_plan_trace(dkb, B, H, N, S, C, scores):
     """A drifting predicted set over 10 steps, caps from 0 to unbounded, ragged counts and tied scores."""
