@@ -6,7 +6,7 @@ A step is one pass of the whole hot path over every layer of the workload: per
 layer, chunk scores, top-k of both queries and their union in one call
 (dk_score_topk_union), and attention of both queries over their own chunks,
 read once per union chunk straight from the HBM pool (dk_sparse_decode_attn).
-Landmarks (and their fp16 shadow) are built once before timing: they are fixed
+Landmarks (and their 8-bit shadow) are built once before timing: they are fixed
 for the whole decode.
 Inputs are seeded synthetic tensors resident in HBM before the timed region.
 
@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--no-events", action="store_true",
                     help="time only whole steps (no per-call events inside the step)")
     ap.add_argument("--no-shadow", action="store_true",
-                    help="score from the fp32 landmarks only (no fp16 landmark shadow)")
+                    help="score from the fp32 landmarks only (no 8-bit landmark shadow)")
     ap.add_argument("--host-copy", choices=("mapped", "copy"), default="mapped",
                     help="host-pool workloads: gather kernel over the mapped pool, or hipMemcpyAsync")
     ap.add_argument("--tail", type=int, default=0,
@@ -581,7 +581,7 @@ def bench_variant(args, w):
     q_bytes = B * T * Hq * d * 4
     rows_bytes = 2 * B * Hkv * T * C * 4            # fp32 score rows written, then read
     if sel == "capped":
-        score_bytes = (w.landmark_bytes() // 2 + rows_bytes + B * Hkv * T * k * d * 4 + q_bytes
+        score_bytes = (w.landmark_bytes() // 4 + B * Hkv * C * 4 + rows_bytes + B * Hkv * T * k * d * 4 + q_bytes
                        + B * Hkv * T * k * 4 * 4)
     else:
         score_bytes = summary_bytes + rows_bytes + q_bytes + B * Hkv * N * 5
@@ -883,9 +883,9 @@ def main():
     if shadow is None:
         score_bytes = lm_bytes_layer + q_bytes
     else:
-        # fp16 landmarks + the fp32 scores written and read back + at least k fp32
-        # landmark rows re-scored per (b, g, t)
-        score_bytes = (lm_bytes_layer // 2 + 2 * w.B * w.Hkv * w.T * w.C * 4
+        # 8-bit codes and one fp32 scale per chunk + the fp32 scores written and read
+        # back + at least k fp32 landmark rows re-scored per (b, g, t)
+        score_bytes = (lm_bytes_layer // 4 + w.B * w.Hkv * w.C * 4 + 2 * w.B * w.Hkv * w.T * w.C * 4
                        + w.B * w.Hkv * w.T * w.k * w.d * 4 + q_bytes)
     per_call_bytes = {
         # scores and selection, then the union: both sets read back, ids + bits written

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define DK_ABI_VERSION 9
+#define DK_ABI_VERSION 10
 
 typedef enum {
     DK_OK = 0,
@@ -97,32 +97,36 @@ dk_status dk_build_landmarks(const void* K, dk_dtype k_dtype, dk_strides ks,
                              float* lm, void* stream);
 
 /*
- * Landmark shadow: an fp16 copy of the landmarks plus, per (b, g), an upper
- * bound of the largest landmark norm.  It lets dk_score_topk stream half the
- * landmark bytes and still return exactly the k chunks that scoring with the
- * fp32 landmarks returns: every chunk whose shadow score is within a proven
- * error bound of the k-th shadow score is re-scored from the fp32 landmarks
- * before the final selection.  Made once per pool by dk_build_landmark_shadow.
+ * Landmark shadow: 8-bit codes of the landmarks with one scale per chunk.  It
+ * lets dk_score_topk stream a quarter of the fp32 landmark bytes and still
+ * return exactly the k chunks that scoring with the fp32 landmarks returns:
+ * every chunk whose shadow score is within a proven error bound of the k-th
+ * score is re-scored from the fp32 landmarks before the final selection.  For
+ * chunk c, s_c = max_i |lm[c, i]| / 127, and byte i is rint(lm[c, i] / s_c) + 128
+ * (|code - 128| <= 127), so |lm[c, i] - s_c (byte - 128)| <= s_c (1/2 + 127 u).
+ * Made once per pool by dk_build_landmark_shadow.
  */
 typedef struct {
-    const uint16_t* lm16;     /* fp16 landmarks [B, Hkv, C, d], contiguous   */
-    const float*    norm_max; /* [B, Hkv]: >= max_c ||lm[b, g, c, :]||_2, or +inf */
+    const uint8_t* lm8;         /* codes [B, Hkv, C, d], contiguous                        */
+    const float*   chunk_scale; /* [B, Hkv, C]: s_c                                        */
+    const float*   scale_max;   /* [B, Hkv]: max_c s_c, or +inf when a landmark is not finite */
 } dk_landmark_shadow;
 
 /*
- * dk_build_landmark_shadow - fp16 copy and norm bound of fp32 landmarks.
+ * dk_build_landmark_shadow - 8-bit codes and per-chunk scales of fp32 landmarks.
  *
- * lm       : fp32 landmarks, rows [B, Hkv, C] of d, strides ls (as written by
- *            dk_build_landmarks).
- * lm16     : out, fp16 [B, Hkv, C, d] contiguous, round-to-nearest-even.
- * norm_max : out, fp32 [B, Hkv]; +inf when a landmark does not fit fp16 (the
- *            scoring then re-scores every chunk of that (b, g) exactly).
- * Errors   : DK_ERR_INVALID_ARG unless sizes >= 1 and pointers non-NULL;
- *            DK_ERR_UNSUPPORTED unless d is 64 or 128 and the 16-byte alignment
- *            rule holds.
+ * lm          : fp32 landmarks, rows [B, Hkv, C] of d, strides ls (as written by
+ *               dk_build_landmarks).
+ * lm8         : out, uint8 [B, Hkv, C, d] contiguous (the codes above).
+ * chunk_scale : out, fp32 [B, Hkv, C] contiguous.
+ * scale_max   : out, fp32 [B, Hkv]; +inf when a landmark of (b, g) is inf or NaN
+ *               (the scoring then re-scores every chunk of that (b, g) exactly).
+ * Errors      : DK_ERR_INVALID_ARG unless sizes >= 1 and pointers non-NULL;
+ *               DK_ERR_UNSUPPORTED unless d is 64 or 128 and the 16-byte alignment
+ *               rule holds.
  */
 dk_status dk_build_landmark_shadow(const float* lm, dk_strides ls, int B, int Hkv, int C, int d,
-                                   uint16_t* lm16, float* norm_max, void* stream);
+                                   uint8_t* lm8, float* chunk_scale, float* scale_max, void* stream);
 
 /*
  * dk_score_topk - chunk scores of both queries and each query's k best chunks.
@@ -148,7 +152,7 @@ dk_status dk_build_landmark_shadow(const float* lm, dk_strides ls, int B, int Hk
  *              of d, strides ls (elements).
  * reduce     : DK_REDUCE_MEAN (mean over the group's heads) or DK_REDUCE_MAX.
  * shadow     : the landmarks' shadow (see above) or NULL.  With a shadow the
- *              result is the same; the call reads about half the bytes.
+ *              result is the same; the call reads about a quarter of the bytes.
  * topk_idx   : out, int32 [B, Hkv, T, k].
  * topk_score : out, fp32 [B, Hkv, T, k] (the selected scores, same order) or NULL.
  * ws         : workspace of dk_score_topk_workspace_size(B, Hkv, T, C, k,

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libdualkv.so")
 DK_OK, DK_ERR_INVALID_ARG, DK_ERR_UNSUPPORTED, DK_ERR_HIP = 0, 1, 2, 3
 DK_F32, DK_BF16 = 0, 1
 DK_REDUCE_MEAN, DK_REDUCE_MAX = 0, 1
-ABI_VERSION = 9
+ABI_VERSION = 10
 
 _STATUS = {0: "DK_OK", 1: "DK_ERR_INVALID_ARG", 2: "DK_ERR_UNSUPPORTED", 3: "DK_ERR_HIP"}
 
@@ -37,7 +37,7 @@ class dk_strides(ctypes.Structure):
 
 
 class dk_landmark_shadow(ctypes.Structure):
-    _fields_ = [("lm16", ctypes.c_void_p), ("norm_max", ctypes.c_void_p)]
+    _fields_ = [("lm8", ctypes.c_void_p), ("chunk_scale", ctypes.c_void_p), ("scale_max", ctypes.c_void_p)]
 
 
 class dk_cache_plan(ctypes.Structure):
@@ -59,7 +59,7 @@ EXPORTS = [
     ("dk_abi_version", ctypes.c_int, []),
     ("dk_last_error", ctypes.c_char_p, []),
     ("dk_build_landmarks", _I, [_P, _I, _S, _I, _I, _I, _I, _I, _P, _P]),
-    ("dk_build_landmark_shadow", _I, [_P, _S, _I, _I, _I, _I, _P, _P, _P]),
+    ("dk_build_landmark_shadow", _I, [_P, _S, _I, _I, _I, _I, _P, _P, _P, _P]),
     ("dk_score_topk_workspace_size", _Z, [_I, _I, _I, _I, _I, _I]),
     ("dk_index_topk_workspace_size", _Z, [_I, _I, _I, _I]),
     ("dk_build_minmax", _I, [_P, _I, _S, _I, _I, _I, _I, _I, _P, _P, _P]),
@@ -156,20 +156,23 @@ def build_landmarks(K: torch.Tensor, chunk: int, lm: torch.Tensor | None = None,
 
 @dataclass
 class Shadow:
-    """fp16 copy of the landmarks and the per-(b, g) norm bound (dk_landmark_shadow)."""
-    lm16: torch.Tensor       # [B, Hkv, C, d] float16
-    norm_max: torch.Tensor   # [B, Hkv] float32
+    """8-bit landmark codes, per-chunk scales and the per-(b, g) largest scale (dk_landmark_shadow)."""
+    lm8: torch.Tensor          # [B, Hkv, C, d] uint8: rint(lm / scale) + 128
+    chunk_scale: torch.Tensor  # [B, Hkv, C] float32: max |lm| / 127 per chunk
+    scale_max: torch.Tensor    # [B, Hkv] float32: largest chunk scale, +inf if a landmark is not finite
 
     def as_c(self) -> dk_landmark_shadow:
-        return dk_landmark_shadow(self.lm16.data_ptr(), self.norm_max.data_ptr())
+        return dk_landmark_shadow(self.lm8.data_ptr(), self.chunk_scale.data_ptr(), self.scale_max.data_ptr())
 
 
 def build_landmark_shadow(lm: torch.Tensor, stream=None) -> Shadow:
     B, H, C, d = lm.shape
-    sh = Shadow(torch.empty(B, H, C, d, dtype=torch.float16, device=lm.device),
-                torch.empty(B, H, dtype=torch.float32, device=lm.device))
-    _check(lib.dk_build_landmark_shadow(_ptr(lm), pool_strides(lm), B, H, C, d, _ptr(sh.lm16),
-                                        _ptr(sh.norm_max), _stream(stream)))
+    dev = lm.device
+    sh = Shadow(torch.empty(B, H, C, d, dtype=torch.uint8, device=dev),
+                torch.empty(B, H, C, dtype=torch.float32, device=dev),
+                torch.empty(B, H, dtype=torch.float32, device=dev))
+    _check(lib.dk_build_landmark_shadow(_ptr(lm), pool_strides(lm), B, H, C, d, _ptr(sh.lm8), _ptr(sh.chunk_scale),
+                                        _ptr(sh.scale_max), _stream(stream)))
     return sh
 
 

@@ -96,17 +96,17 @@ dk_status dk_build_minmax(const void* K, dk_dtype k_dtype, dk_strides ks, int B,
     return e == hipSuccess ? DK_OK : hip_fail(e, fn);
 }
 
-dk_status dk_build_landmark_shadow(const float* lm, dk_strides ls, int B, int Hkv, int C, int d,
-                                   uint16_t* lm16, float* norm_max, void* stream) {
+dk_status dk_build_landmark_shadow(const float* lm, dk_strides ls, int B, int Hkv, int C, int d, uint8_t* lm8,
+                                   float* chunk_scale, float* scale_max, void* stream) {
     g_err.clear();
-    DK_REQUIRE(lm && lm16 && norm_max, DK_ERR_INVALID_ARG,
-               "dk_build_landmark_shadow: lm, lm16, norm_max must be non-NULL");
+    DK_REQUIRE(lm && lm8 && chunk_scale && scale_max, DK_ERR_INVALID_ARG,
+               "dk_build_landmark_shadow: lm, lm8, chunk_scale, scale_max must be non-NULL");
     DK_REQUIRE(B >= 1 && Hkv >= 1 && C >= 1 && d >= 1, DK_ERR_INVALID_ARG,
                "dk_build_landmark_shadow: B, Hkv, C, d must be >= 1");
     DK_REQUIRE(d == 64 || d == 128, DK_ERR_UNSUPPORTED, "dk_build_landmark_shadow: d must be 64 or 128");
-    DK_REQUIRE(aligned16(lm) && aligned16(lm16) && strides_ok(ls, 4), DK_ERR_UNSUPPORTED,
-               "dk_build_landmark_shadow: lm, lm16 and lm's strides must be 16-byte aligned");
-    hipError_t e = dk::launch_build_shadow(lm, ls, B, Hkv, C, d, lm16, norm_max, (hipStream_t)stream);
+    DK_REQUIRE(aligned16(lm) && aligned16(lm8) && strides_ok(ls, 4), DK_ERR_UNSUPPORTED,
+               "dk_build_landmark_shadow: lm, lm8 and lm's strides must be 16-byte aligned");
+    hipError_t e = dk::launch_build_shadow(lm, ls, B, Hkv, C, d, lm8, chunk_scale, scale_max, (hipStream_t)stream);
     return e == hipSuccess ? DK_OK : hip_fail(e, "dk_build_landmark_shadow");
 }
 
@@ -139,8 +139,8 @@ dk_status check_score_topk(const char* fn, const float* q, int B, int T, int Hq,
     DK_REQUIRE(reduce == DK_REDUCE_MEAN || reduce == DK_REDUCE_MAX, DK_ERR_INVALID_ARG,
                "%s: unknown reduce %d", fn, (int)reduce);
     DK_REQUIRE(std::isfinite(scale), DK_ERR_INVALID_ARG, "%s: scale must be finite", fn);
-    DK_REQUIRE(!shadow || (shadow->lm16 && shadow->norm_max), DK_ERR_INVALID_ARG,
-               "%s: shadow->lm16 and shadow->norm_max must be non-NULL", fn);
+    DK_REQUIRE(!shadow || (shadow->lm8 && shadow->chunk_scale && shadow->scale_max), DK_ERR_INVALID_ARG,
+               "%s: shadow->lm8, chunk_scale and scale_max must be non-NULL", fn);
     DK_REQUIRE(lm_dtype == DK_F32, DK_ERR_UNSUPPORTED, "%s: landmarks must be DK_F32", fn);
     DK_REQUIRE(d == 64 || d == 128, DK_ERR_UNSUPPORTED, "%s: d must be 64 or 128 (got %d)", fn, d);
     DK_REQUIRE(C <= 65536, DK_ERR_UNSUPPORTED, "%s: C must be <= 65536 (got %d)", fn, C);
@@ -150,8 +150,8 @@ dk_status check_score_topk(const char* fn, const float* q, int B, int T, int Hq,
         DK_REQUIRE(nq <= 16 && (nq & (nq - 1)) == 0, DK_ERR_UNSUPPORTED,
                    "%s: max reduction needs G*T a power of two <= 16 (got %d)", fn, nq);
     }
-    DK_REQUIRE(aligned16(q) && aligned16(lm) && strides_ok(ls, 4) && (!shadow || aligned16(shadow->lm16)),
-               DK_ERR_UNSUPPORTED, "%s: q, lm, lm's strides and lm16 must be 16-byte aligned", fn);
+    DK_REQUIRE(aligned16(q) && aligned16(lm) && strides_ok(ls, 4) && (!shadow || (aligned16(shadow->lm8) && aligned16(shadow->chunk_scale))),
+               DK_ERR_UNSUPPORTED, "%s: q, lm, lm's strides, lm8 and chunk_scale must be 16-byte aligned", fn);
     const dk::TopkPlan plan = dk::plan_topk(B, Hkv, T, C, k, shadow != nullptr);
     DK_REQUIRE(plan.splits > 0, DK_ERR_UNSUPPORTED, "%s: no plan for C=%d k=%d%s", fn, C, k,
                shadow ? " with a shadow (C <= 6144)" : "");

@@ -90,12 +90,15 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* to
 // ---------------------------------------------------------------------------
 // Cross-lane helpers.
 // ---------------------------------------------------------------------------
-// sum over the aligned group of LPR (8 or 16) lanes, every lane gets the total
+// sum over the aligned group of LPR (4, 8 or 16) lanes, every lane gets the total
 template <int LPR>
 __device__ __forceinline__ float dpp_group_sum(float v) {
+    static_assert(LPR == 4 || LPR == 8 || LPR == 16, "groups of 4, 8 or 16 lanes");
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
-    if constexpr (LPR == 8) {
+    if constexpr (LPR == 4) {
+        return v;
+    } else if constexpr (LPR == 8) {
         v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
     } else {
         v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));
@@ -248,7 +251,7 @@ hipError_t launch_mla_attention(const float* q, int B, int T, int Hq, int Hkv, c
                                 float scale, float* out, float* lse, void* ws, const MlaPlan& plan,
                                 hipStream_t st);
 hipError_t launch_build_shadow(const float* lm, dk_strides ls, int B, int Hkv, int C, int d,
-                               uint16_t* lm16, float* norm_max, hipStream_t st);
+                               uint8_t* lm8, float* chunk_scale, float* scale_max, hipStream_t st);
 
 hipError_t launch_union(const int32_t* topk_idx, int B, int Hkv, int T, int k, int C,
                         int32_t* union_ids, uint8_t* member, int32_t* union_count, int32_t* overlap,

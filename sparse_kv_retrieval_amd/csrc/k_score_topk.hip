@@ -398,71 +398,90 @@ __global__ __launch_bounds__(kThreads) void k_topk_merge(const uint32_t* __restr
 }
 
 // ---------------------------------------------------------------------------
-// Landmark shadow: fp16 copy (round to nearest even) and a per-(b, g) upper
-// bound of the largest landmark norm.  One block per (b, g).
+// Landmark shadow: 8-bit codes with one scale per chunk.  For row c,
+//   s_c = max_i |lm[c, i]| / 127,  m_i = rint(lm[c, i] / s_c)  (|m_i| <= 127),
+// stored as the byte m_i + 128, so |lm[c, i] - s_c m_i| <= s_c (1/2 + 127 u).
+// scale_max[b, g] = max_c s_c, or +inf when a landmark of (b, g) is not finite
+// (the selection then re-scores every chunk of that (b, g) exactly).  One
+// block per (b, g); TPR threads per row, four dimensions each.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_build_shadow(const float* __restrict__ lm, dk_strides ls,
-                                                          int Hkv, int C, uint16_t* __restrict__ lm16,
-                                                          float* __restrict__ norm_max) {
+                                                          int Hkv, int C, uint8_t* __restrict__ lm8,
+                                                          float* __restrict__ chunk_scale,
+                                                          float* __restrict__ scale_max) {
     constexpr int TPR = D / 4;                 // threads per row, one float4 each
     constexpr int RPB = kThreads / TPR;        // rows per block pass
     __shared__ float smax[kThreads / kWave];
-    __shared__ int sinf;
+    __shared__ int sbad;
     const int bg = blockIdx.x;
     const int b = bg / Hkv, g = bg - b * Hkv;
     const int tr = threadIdx.x / TPR, part = threadIdx.x % TPR;
-    if (threadIdx.x == 0) sinf = 0;
+    if (threadIdx.x == 0) sbad = 0;
     __syncthreads();
     float vmax = 0.f;
-    bool overflow = false;
+    bool bad = false;
     const float* base = lm + (int64_t)b * ls.b + (int64_t)g * ls.h + part * 4;
-    uint16_t* obase = lm16 + (int64_t)bg * C * D + part * 4;
+    uint8_t* obase = lm8 + (int64_t)bg * C * D + part * 4;
     for (int r0 = 0; r0 < C; r0 += RPB) {
         const int r = r0 + tr;
-        float ss = 0.f;
+        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (r < C) x = *reinterpret_cast<const float4*>(base + (int64_t)r * ls.t);
+        // largest magnitude of the row: its TPR threads are an aligned lane group
+        // inf or NaN anywhere (fmaxf would drop a NaN)
+        bad |= !(fabsf(x.x) <= 3.0e38f && fabsf(x.y) <= 3.0e38f && fabsf(x.z) <= 3.0e38f &&
+                 fabsf(x.w) <= 3.0e38f);
+        float a = fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w)));
+        for (int off = 1; off < TPR; off <<= 1) a = fmaxf(a, __shfl_xor(a, off, kWave));
         if (r < C) {
-            const float4 x = *reinterpret_cast<const float4*>(base + (int64_t)r * ls.t);
-            const uint32_t h0 = f16_bits(x.x), h1 = f16_bits(x.y), h2 = f16_bits(x.z), h3 = f16_bits(x.w);
-            // an fp16 infinity (or NaN) means the shadow cannot bound this (b, g)
-            overflow |= (h0 & 0x7c00u) == 0x7c00u || (h1 & 0x7c00u) == 0x7c00u ||
-                        (h2 & 0x7c00u) == 0x7c00u || (h3 & 0x7c00u) == 0x7c00u;
-            *reinterpret_cast<uint2*>(obase + (int64_t)r * D) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
-            ss = x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
+            const float sc = __fdiv_rn(a, 127.0f);
+            auto code = [sc](float v) -> uint32_t {
+                const float m = sc > 0.f ? rintf(__fdiv_rn(v, sc)) : 0.f;
+                return (uint32_t)((int)fminf(fmaxf(m, -127.f), 127.f) + 128);
+            };
+            *reinterpret_cast<uint32_t*>(obase + (int64_t)r * D) =
+                code(x.x) | (code(x.y) << 8) | (code(x.z) << 16) | (code(x.w) << 24);
+            if (part == 0) chunk_scale[(int64_t)bg * C + r] = sc;
+            vmax = fmaxf(vmax, sc);
         }
-        // squared norm of the row: sum over its TPR threads (aligned lane groups)
-        for (int off = 1; off < TPR; off <<= 1) ss += __shfl_xor(ss, off, kWave);
-        vmax = fmaxf(vmax, ss);
     }
-    if (overflow) sinf = 1;
+    if (bad) sbad = 1;
     for (int off = 1; off < kWave; off <<= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, off, kWave));
     if ((threadIdx.x & (kWave - 1)) == 0) smax[threadIdx.x / kWave] = vmax;
     __syncthreads();
     if (threadIdx.x == 0) {
         float m = 0.f;
         for (int w = 0; w < kThreads / kWave; ++w) m = fmaxf(m, smax[w]);
-        // sum of D squares and a square root in fp32: relative error below (D + 4) u
-        const float bound = sqrtf(m) * (1.0f + (float)(D + 8) * 5.9604645e-8f);
-        norm_max[bg] = sinf ? INFINITY : bound;
+        scale_max[bg] = sbad ? INFINITY : m;
     }
 }
 
 // ---------------------------------------------------------------------------
-// Shadow pass 1: fp16 scores of every chunk, streamed with non-temporal 16-byte
-// loads; LPR = D / 8 lanes per row, 8 fp16 dims per lane; the row sums use DPP
-// only.  Scores of one block's rows are staged in LDS and stored coalesced to
-// s_lo [B * Hkv, T, C] (fp32).
+// Shadow pass 1: scores of every chunk from the 8-bit codes, streamed with
+// non-temporal 16-byte loads; LPR = D / 16 lanes per row, 16 codes per lane.
+// A byte pair becomes two exact fp16 values with one v_perm against the fp16
+// exponent byte 0x64 (0x64XX is 1024 + XX) and one packed subtraction of 1152,
+// then v_dot2_f32_f16 against the fp16 query; the row sums use DPP only and the
+// chunk's scale multiplies the sum.  Scores of one block's rows are staged in
+// LDS and stored coalesced to s_lo [B * Hkv, T, C] (fp32).
 // ---------------------------------------------------------------------------
 #ifndef DK_SCORE_LO_UNROLL
-#define DK_SCORE_LO_UNROLL 8   // 16-byte landmark loads in flight per lane
+#define DK_SCORE_LO_UNROLL 8   // 16-byte code loads in flight per lane
 #endif
+
+// bytes 0, 1 (sel 0x04010400) or 2, 3 (sel 0x04030402) of w as two fp16 values byte - 128
+__device__ __forceinline__ uint32_t code_pair(uint32_t w, uint32_t sel) {
+    const f16x2_t h = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, w, sel));
+    return __builtin_bit_cast(uint32_t, h - f16x2_t{(_Float16)1152.0f, (_Float16)1152.0f});
+}
 
 template <int D, int NQ, int T, bool MAXRED>
 __global__ __launch_bounds__(kThreads) void k_score_lo(const float* __restrict__ q, int Hq,
-                                                      const uint16_t* __restrict__ lm16, int Hkv, int C,
+                                                      const uint8_t* __restrict__ lm8,
+                                                      const float* __restrict__ chunk_scale, int Hkv, int C,
                                                       float scale, int rows_per_block, int blocks_per_bg,
                                                       float* __restrict__ s_lo, uint32_t* __restrict__ arrivals) {
-    constexpr int LPR = D / 8, RPW = kWave / LPR, U = DK_SCORE_LO_UNROLL;
+    constexpr int LPR = D / 16, RPW = kWave / LPR, U = DK_SCORE_LO_UNROLL;
     constexpr int G = MAXRED ? NQ / T : 0;
     extern __shared__ float sres[];    // [T][rows_per_block], then [NQ][D] query vectors
     const int blk = blockIdx.x % blocks_per_bg;
@@ -478,14 +497,18 @@ __global__ __launch_bounds__(kThreads) void k_score_lo(const float* __restrict__
 
     // The first rows are requested before anything else: their loads overlap
     // the query staging below.
-    const uint16_t* base = lm16 + ((int64_t)bg * C + row0) * D + part * 8;
+    const uint8_t* base = lm8 + ((int64_t)bg * C + row0) * D + part * 16;
+    const float* sbase = chunk_scale + (int64_t)bg * C + row0;
     constexpr int ROWS_PER_ITER = 4 * RPW * U;
     u32x4_t x[U];
+    float rs[U];
     auto load_rows = [&](int it) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int r = it + (u * 4 + wave) * RPW + rp;
-            x[u] = r < nrows ? nt_load_u4(base + (int64_t)r * D) : u32x4_t{0u, 0u, 0u, 0u};
+            x[u] = r < nrows ? nt_load_u4(base + (int64_t)r * D) : u32x4_t{0x80808080u, 0x80808080u, 0x80808080u,
+                                                                           0x80808080u};
+            rs[u] = part < T && r < nrows ? sbase[r] : 0.f;
         }
     };
     load_rows(0);
@@ -506,16 +529,12 @@ __global__ __launch_bounds__(kThreads) void k_score_lo(const float* __restrict__
         qs[i] = xq;
     }
     __syncthreads();
-    uint32_t qh[NQ][4];
+    uint32_t qh[NQ][8];
 #pragma unroll
-    for (int v = 0; v < NQ; ++v) {
-        const float4 x0 = *reinterpret_cast<const float4*>(qs + v * D + part * 8);
-        const float4 x1 = *reinterpret_cast<const float4*>(qs + v * D + part * 8 + 4);
-        qh[v][0] = f16_bits(x0.x) | (f16_bits(x0.y) << 16);
-        qh[v][1] = f16_bits(x0.z) | (f16_bits(x0.w) << 16);
-        qh[v][2] = f16_bits(x1.x) | (f16_bits(x1.y) << 16);
-        qh[v][3] = f16_bits(x1.z) | (f16_bits(x1.w) << 16);
-    }
+    for (int v = 0; v < NQ; ++v)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            qh[v][j] = f16_bits(qs[v * D + part * 16 + 2 * j]) | (f16_bits(qs[v * D + part * 16 + 2 * j + 1]) << 16);
 
     for (int it = 0; it < nrows; it += ROWS_PER_ITER) {
         if (it) load_rows(it);
@@ -524,25 +543,30 @@ __global__ __launch_bounds__(kThreads) void k_score_lo(const float* __restrict__
         for (int u = 0; u < U; ++u) rr[u] = it + (u * 4 + wave) * RPW + rp;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+            uint32_t h[8];
+            h[0] = code_pair(x[u].x, 0x04010400u); h[1] = code_pair(x[u].x, 0x04030402u);
+            h[2] = code_pair(x[u].y, 0x04010400u); h[3] = code_pair(x[u].y, 0x04030402u);
+            h[4] = code_pair(x[u].z, 0x04010400u); h[5] = code_pair(x[u].z, 0x04030402u);
+            h[6] = code_pair(x[u].w, 0x04010400u); h[7] = code_pair(x[u].w, 0x04030402u);
             float dot[NQ];
 #pragma unroll
             for (int v = 0; v < NQ; ++v) {
-                float a = dot2_f16(qh[v][0], x[u].x, 0.f);
-                a = dot2_f16(qh[v][1], x[u].y, a);
-                a = dot2_f16(qh[v][2], x[u].z, a);
-                a = dot2_f16(qh[v][3], x[u].w, a);
+                float a = 0.f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) a = dot2_f16(qh[v][j], h[j], a);
                 dot[v] = dpp_group_sum<LPR>(a);
             }
             // per-query scores with compile-time register indices
+            const float sc = scale * rs[u];
             float sct[T];
 #pragma unroll
             for (int t = 0; t < T; ++t) {
                 if constexpr (MAXRED) {
-                    sct[t] = scale * dot[t * G];
+                    sct[t] = sc * dot[t * G];
 #pragma unroll
-                    for (int h = 1; h < G; ++h) sct[t] = fmaxf(sct[t], scale * dot[t * G + h]);
+                    for (int hh = 1; hh < G; ++hh) sct[t] = fmaxf(sct[t], sc * dot[t * G + hh]);
                 } else {
-                    sct[t] = scale * dot[t];
+                    sct[t] = sc * dot[t];
                 }
             }
             if (part < T && rr[u] < nrows)
@@ -557,15 +581,19 @@ __global__ __launch_bounds__(kThreads) void k_score_lo(const float* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// Shadow pass 2, one block per (b, g, t): the k-th largest fp16 score tau, the
-// candidates {c : s_lo[c] >= tau - 2 delta} (delta bounds |s_lo - s| for every
-// chunk, s the fp32 score this kernel computes), their fp32 re-scores, and the
-// exact top-k among them (ties to the lower id), written in ascending order.
+// Shadow pass 2, one block per (b, g, t).  Every chunk's fp32 score s (as this
+// kernel computes it) lies in [s_lo - d_c, s_lo + d_c] with d_c = K * s_c, K
+// from the query's 1-norm (the derivation is at the bound below).  L = the k-th
+// largest per-thread maximum of s_lo - d_c is a lower bound of the k-th largest
+// s; the candidates {c : s_lo[c] + d_c >= L} hold every chunk of the top k,
+// ties included.  Their fp32 re-scores give the exact top-k (ties to the lower
+// id), written in ascending order.
 // ---------------------------------------------------------------------------
 template <int D, bool MAXRED>
 __global__ __launch_bounds__(kThreads) void k_select_exact(
     const float* __restrict__ q, int T, int Hq, const float* __restrict__ lm, dk_strides ls,
-    const float* __restrict__ norm_max, const float* __restrict__ s_lo, int Hkv, int C, int k,
+    const float* __restrict__ chunk_scale, const float* __restrict__ scale_max, const float* __restrict__ s_lo,
+    int Hkv, int C, int k,
     float scale, int32_t* __restrict__ topk_idx, float* __restrict__ topk_score, UnionOut un,
     uint32_t* __restrict__ arrivals) {
     constexpr int LPR = D / 8;                 // lanes per fp32 row, 8 floats each
@@ -583,7 +611,7 @@ __global__ __launch_bounds__(kThreads) void k_select_exact(
     uint32_t* hist = (uint32_t*)(qv + nvec * D);     // [256]
     int* scratch = (int*)(hist + 256);               // [8]
     int* bc = scratch + 8;                           // [2]
-    float* sf = (float*)(bc + 2);                    // [2] norm, threshold
+    float* sf = (float*)(bc + 2);                    // [2] query 1-norm, largest |q|
 
     const int t = blockIdx.x % T;
     const int bg = blockIdx.x / T;
@@ -591,31 +619,34 @@ __global__ __launch_bounds__(kThreads) void k_select_exact(
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
 
     // Every independent global load first: this thread's contiguous range of
-    // fp16-pass scores (kept in registers), the norm bound, the query rows.
+    // shadow scores and chunk scales (kept in registers), the query rows.
     constexpr int KPT = kShadowMaxC / kThreads;      // scores per thread, at most
     const int per = (C + kThreads - 1) / kThreads;
     const int lo = min(C, tid * per), hi = min(C, lo + per);
     const float* sl = s_lo + ((int64_t)bg * T + t) * C;
-    // straight into registers: 16-byte loads when the ranges are 4-aligned
-    uint32_t kr[KPT];
+    const float* cs = chunk_scale + (int64_t)bg * C;
+    float sv[KPT], sc[KPT];
     if ((per & 3) == 0 && (C & 3) == 0) {
 #pragma unroll
         for (int i = 0; i < KPT / 4; ++i) {
             if (lo + 4 * i < hi) {
                 const float4 x = *reinterpret_cast<const float4*>(sl + lo + 4 * i);
-                kr[4 * i] = score_key(x.x);
-                kr[4 * i + 1] = score_key(x.y);
-                kr[4 * i + 2] = score_key(x.z);
-                kr[4 * i + 3] = score_key(x.w);
+                const float4 y = *reinterpret_cast<const float4*>(cs + lo + 4 * i);
+                sv[4 * i] = x.x; sv[4 * i + 1] = x.y; sv[4 * i + 2] = x.z; sv[4 * i + 3] = x.w;
+                sc[4 * i] = y.x; sc[4 * i + 1] = y.y; sc[4 * i + 2] = y.z; sc[4 * i + 3] = y.w;
             } else {
-                kr[4 * i] = kr[4 * i + 1] = kr[4 * i + 2] = kr[4 * i + 3] = 0u;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sv[4 * i + j] = sc[4 * i + j] = 0.f;
             }
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) kr[i] = lo + i < hi ? score_key(sl[lo + i]) : 0u;
+        for (int i = 0; i < KPT; ++i) {
+            sv[i] = lo + i < hi ? sl[lo + i] : 0.f;
+            sc[i] = lo + i < hi ? cs[lo + i] : 0.f;
+        }
     }
-    const float M = norm_max[bg];
+    const float SM = scale_max[bg];
     for (int i = tid; i < nvec * D; i += kThreads) {
         const int v = i / D, e = i - v * D;
         float x;
@@ -629,24 +660,55 @@ __global__ __launch_bounds__(kThreads) void k_select_exact(
         qv[i] = x;
     }
     __syncthreads();
+    if (wave == 0) {
+        // largest 1-norm of the query vectors (rounded up) and largest |q|
+        float l1max = 0.f, amax = 0.f;
+        for (int v = 0; v < nvec; ++v) {
+            float s1 = 0.f;
+            for (int e = lane; e < D; e += kWave) {
+                s1 += fabsf(qv[v * D + e]);
+                amax = fmaxf(amax, fabsf(qv[v * D + e]));
+            }
+            for (int off = 1; off < kWave; off <<= 1) s1 += __shfl_xor(s1, off, kWave);
+            l1max = fmaxf(l1max, s1);
+        }
+        for (int off = 1; off < kWave; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+        if (lane == 0) {
+            sf[0] = l1max * (1.0f + (float)(D + 8) * 5.9604645e-8f);
+            sf[1] = amax;
+        }
+    }
+    __syncthreads();
+    // The bound.  With m_i the codes, s_c the scale, q^ = fp16(q) and u16 = 2^-11:
+    //   |sum q_i l_i - s_c sum q^_i m_i| <= s_c (1/2 + 127 u32) |q|_1   (the codes)
+    //                                     + s_c 127 (u16 |q|_1 + D 2^-25)  (q in fp16, incl. subnormals),
+    // the fp32 sums on both sides add at most (D + 40) roundings of terms up to
+    // 127 s_c |q_i|, and the scale products a few relative roundings more.
+    const float u16 = 4.8828125e-4f, u32 = 5.9604645e-8f;
+    const float L1 = sf[0];
+    const float Kq = fabsf(scale) *
+                     (L1 * (0.5f + 127.f * u32 + 127.f * u16 + (float)(D + 40) * 127.f * u32) +
+                      127.f * (float)D * 2.9802322e-8f) * 1.01f;
+    // a landmark or query value that the codes or fp16 cannot hold voids the bound:
+    // every chunk is then a candidate
+    const bool valid = SM <= 3.0e38f && sf[1] <= 65000.f && Kq <= 3.0e38f;
+    uint32_t kr[KPT];
     uint32_t tmax = 0u;
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) tmax = max(tmax, kr[i]);
+    for (int i = 0; i < KPT; ++i) {
+        const float d = Kq * sc[i];
+        const float slo = sv[i] - d, shi = sv[i] + d;
+        const float pad = (fabsf(sv[i]) + d) * 2.4e-7f + 1e-37f;   // round the bounds outwards
+        const bool in = lo + i < hi;
+        tmax = max(tmax, in ? score_key(slo - pad) : 0u);
+        kr[i] = in ? score_key(shi + pad) : 0u;
+    }
     uint32_t* tmaxs = cand_u;                     // [256] scratch (cand[] is not used yet)
     tmaxs[tid] = tmax;
     __syncthreads();
     if (wave == 0) {
-        // largest query-vector norm, rounded up
-        float nmax = 0.f;
-        for (int v = 0; v < nvec; ++v) {
-            float ss = 0.f;
-            for (int e = lane; e < D; e += kWave) ss += qv[v * D + e] * qv[v * D + e];
-            for (int off = 1; off < kWave; off <<= 1) ss += __shfl_xor(ss, off, kWave);
-            nmax = fmaxf(nmax, ss);
-        }
-        // A lower bound of the k-th largest fp16 score: the k-th largest of the
-        // per-thread maxima (at least k scores reach it).  For k > 256 the
-        // bound is 0, i.e. every chunk is a candidate.
+        // the k-th largest of the per-thread maxima: at least k chunks score at
+        // least this much.  For k > 256 the bound is 0, i.e. every chunk is a candidate.
         uint32_t kb = 0u;
         if (k <= kThreads) {
             uint32_t x[4];
@@ -655,26 +717,10 @@ __global__ __launch_bounds__(kThreads) void k_select_exact(
             int nd;
             kb = wave_kth_key_bisect(x, k, &nd);
         }
-        if (lane == 0) {
-            sf[0] = sqrtf(nmax) * (1.0f + (float)(D + 8) * 5.9604645e-8f);
-            bc[0] = (int)kb;
-        }
+        if (lane == 0) bc[0] = (int)kb;
     }
     __syncthreads();
-    const uint32_t kth = (uint32_t)bc[0];
-    const float nq = sf[0];
-    const float u16 = 4.8828125e-4f, u32 = 5.9604645e-8f;
-    const float A = nq * M;   // >= sum_i |q_i lm_ci| for every chunk (Cauchy-Schwarz)
-    const float sqd = sqrtf((float)D);
-    const float e1 = (2.f * u16 + u16 * u16 + (D + 2) * u32 * 1.01f) * A +
-                     2.9802322e-8f * 1.01f * sqd * (M + nq) + (float)D * 8.9e-16f;
-    const float e2 = (D + 2) * u32 * 1.01f * A;
-    const float delta = fabsf(scale) * (e1 + e2) * 1.01f;
-    const float tau = key_score(kth);
-    float thr = tau - 2.f * delta;
-    thr -= (fabsf(tau) + 2.f * delta) * 2.4e-7f;     // round the bound down
-    const uint32_t thr_key =
-        (M != M || M == INFINITY || thr != thr || kth == 0u) ? 0u : score_key(thr);
+    const uint32_t thr_key = valid ? (uint32_t)bc[0] : 0u;
 
     // candidates in ascending chunk order
     int mine = 0;
@@ -841,22 +887,24 @@ hipError_t dispatch_split(int nq, int T, bool maxred, const float* q, int B, int
 }
 
 template <int D, int NQ, int T, bool MAXRED>
-hipError_t launch_lo(const float* q, int B, int Hq, const uint16_t* lm16, int Hkv, int C, float scale,
+hipError_t launch_lo(const float* q, int B, int Hq, const uint8_t* lm8, const float* cscale, int Hkv, int C,
+                     float scale,
                      const TopkPlan& p, float* s_lo, uint32_t* arrivals, hipStream_t st) {
     const size_t lds = (((size_t)T * p.rows + 3) & ~(size_t)3) * 4 + (size_t)NQ * D * 4;
     const unsigned grid = (unsigned)((int64_t)B * Hkv * p.splits);
-    hipLaunchKernelGGL((k_score_lo<D, NQ, T, MAXRED>), dim3(grid), dim3(kThreads), lds, st, q, Hq, lm16,
+    hipLaunchKernelGGL((k_score_lo<D, NQ, T, MAXRED>), dim3(grid), dim3(kThreads), lds, st, q, Hq, lm8, cscale,
                        Hkv, C, scale, p.rows, p.splits, s_lo, arrivals);
     return hipGetLastError();
 }
 
 template <int D>
-hipError_t dispatch_lo(int nq, int T, bool maxred, const float* q, int B, int Hq, const uint16_t* lm16,
+hipError_t dispatch_lo(int nq, int T, bool maxred, const float* q, int B, int Hq, const uint8_t* lm8,
+                       const float* cscale,
                        int Hkv, int C, float scale, const TopkPlan& p, float* s_lo, uint32_t* arrivals,
                        hipStream_t st) {
 #define DK_LO(NQ_, T_, MX_) \
     if (nq == NQ_ && T == T_ && maxred == MX_) \
-        return launch_lo<D, NQ_, T_, MX_>(q, B, Hq, lm16, Hkv, C, scale, p, s_lo, arrivals, st);
+        return launch_lo<D, NQ_, T_, MX_>(q, B, Hq, lm8, cscale, Hkv, C, scale, p, s_lo, arrivals, st);
     DK_LO(1, 1, false)
     DK_LO(2, 2, false)
     DK_LO(1, 1, true)
@@ -935,12 +983,14 @@ size_t select_lds_bytes(int C, int D, int nvec) {
 }
 
 hipError_t launch_build_shadow(const float* lm, dk_strides ls, int B, int Hkv, int C, int d,
-                               uint16_t* lm16, float* norm_max, hipStream_t st) {
+                               uint8_t* lm8, float* chunk_scale, float* scale_max, hipStream_t st) {
     const unsigned grid = (unsigned)((int64_t)B * Hkv);
     if (d == 128)
-        hipLaunchKernelGGL(k_build_shadow<128>, dim3(grid), dim3(kThreads), 0, st, lm, ls, Hkv, C, lm16, norm_max);
+        hipLaunchKernelGGL(k_build_shadow<128>, dim3(grid), dim3(kThreads), 0, st, lm, ls, Hkv, C, lm8, chunk_scale,
+                           scale_max);
     else
-        hipLaunchKernelGGL(k_build_shadow<64>, dim3(grid), dim3(kThreads), 0, st, lm, ls, Hkv, C, lm16, norm_max);
+        hipLaunchKernelGGL(k_build_shadow<64>, dim3(grid), dim3(kThreads), 0, st, lm, ls, Hkv, C, lm8, chunk_scale,
+                           scale_max);
     return hipGetLastError();
 }
 
@@ -961,8 +1011,10 @@ hipError_t launch_score_topk(const float* q, int B, int T, int Hq, const float* 
         uint32_t* arrivals =
             fuse ? (uint32_t*)((char*)ws + (((size_t)bg * T * C * 4 + 15) & ~(size_t)15)) : nullptr;
         hipError_t e = d == 128
-            ? dispatch_lo<128>(nq, T, maxred, q, B, Hq, shadow->lm16, Hkv, C, scale, p, s_lo, arrivals, st)
-            : dispatch_lo<64>(nq, T, maxred, q, B, Hq, shadow->lm16, Hkv, C, scale, p, s_lo, arrivals, st);
+            ? dispatch_lo<128>(nq, T, maxred, q, B, Hq, shadow->lm8, shadow->chunk_scale, Hkv, C, scale, p, s_lo,
+                               arrivals, st)
+            : dispatch_lo<64>(nq, T, maxred, q, B, Hq, shadow->lm8, shadow->chunk_scale, Hkv, C, scale, p, s_lo,
+                              arrivals, st);
         if (e != hipSuccess) return e;
         const unsigned grid = (unsigned)(bg * T);
         const size_t lds = select_lds_bytes(C, d, maxred ? G : 1);
@@ -970,7 +1022,8 @@ hipError_t launch_score_topk(const float* q, int B, int T, int Hq, const float* 
         const UnionOut uo = fuse ? *un : none;
 #define DK_SEL(D_, MX_)                                                                            \
     hipLaunchKernelGGL((k_select_exact<D_, MX_>), dim3(grid), dim3(kThreads), lds, st, q, T, Hq, lm, ls, \
-                       shadow->norm_max, s_lo, Hkv, C, k, scale, topk_idx, topk_score, uo, arrivals)
+                       shadow->chunk_scale, shadow->scale_max, s_lo, Hkv, C, k, scale, topk_idx, topk_score, uo, \
+                       arrivals)
         if (d == 128) { if (maxred) DK_SEL(128, true); else DK_SEL(128, false); }
         else { if (maxred) DK_SEL(64, true); else DK_SEL(64, false); }
 #undef DK_SEL

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version():
-    assert lib.dk_abi_version() == 9
+    assert lib.dk_abi_version() == 10
 
 
 def err():
@@ -63,9 +63,9 @@ def score(q=FAKE, B=2, T=2, Hq=32, lm=FAKE, lmdt=0, ls=b.dk_strides(1 << 22, 1 <
                              ws, wsb, None)
 
 
-SH_OK = b.dk_landmark_shadow(0x1000, 0x1000)
-SH_NULL = b.dk_landmark_shadow(0x1000, 0)
-SH_MIS = b.dk_landmark_shadow(0x1008, 0x1000)
+SH_OK = b.dk_landmark_shadow(0x1000, 0x1000, 0x1000)
+SH_NULL = b.dk_landmark_shadow(0x1000, 0x1000, 0)
+SH_MIS = b.dk_landmark_shadow(0x1008, 0x1000, 0x1000)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -127,13 +127,14 @@ def test_index_topk_workspace_size():
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(lm=NULL), 1), (dict(C=0), 1), (dict(d=96), 2), (dict(lm16=MIS), 2),
+    (dict(lm=NULL), 1), (dict(C=0), 1), (dict(d=96), 2), (dict(lm8=MIS), 2), (dict(cs=NULL), 1), (dict(sm=NULL), 1),
 ])
 def test_shadow_rejects(kw, status):
-    a = dict(lm=FAKE, ls=b.dk_strides(1 << 22, 1 << 19, 128), B=2, H=8, C=1024, d=128, lm16=FAKE, nm=FAKE)
+    a = dict(lm=FAKE, ls=b.dk_strides(1 << 22, 1 << 19, 128), B=2, H=8, C=1024, d=128, lm8=FAKE, cs=FAKE,
+             sm=FAKE)
     a.update(kw)
-    assert lib.dk_build_landmark_shadow(a["lm"], a["ls"], a["B"], a["H"], a["C"], a["d"], a["lm16"],
-                                        a["nm"], None) == status
+    assert lib.dk_build_landmark_shadow(a["lm"], a["ls"], a["B"], a["H"], a["C"], a["d"], a["lm8"], a["cs"],
+                                        a["sm"], None) == status
     assert err().startswith("dk_build_landmark_shadow")
 
 

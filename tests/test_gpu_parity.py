@@ -97,7 +97,7 @@ def test_landmarks_strided_pool(dkb):
 def check_score_topk(dkb, qh, lm32, k, scale, reduce, G, shadow=False):
     """GPU scores/top-k on fp32 landmarks lm32 against the oracle on the same values.
 
-    With shadow=True the call streams the fp16 shadow and re-scores candidates;
+    With shadow=True the call streams the 8-bit shadow and re-scores candidates;
     the bar is the same (the selected set and the reported scores)."""
     q = torch.from_numpy(qh.astype(np.float32)).cuda()
     lm = torch.from_numpy(lm32).cuda()
@@ -171,15 +171,28 @@ def test_score_topk_exact_ties_and_k_equals_c(dkb, shadow):
 def test_landmark_shadow_builder(dkb):
     g = torch.Generator().manual_seed(6)
     lm = torch.randn(3, 2, 200, 128, generator=g) * torch.rand(3, 2, 200, 1, generator=g) * 3
-    lm[1, 1, 17] *= 1e5                      # beyond fp16: that (b, g) gets an infinite bound
+    lm[0, 1, 5] = 0.0                          # an all-zero chunk: scale 0, codes 128
+    lm[2, 0, 9, 3] = 1e-39                     # a subnormal landmark value
+    lm[1, 1, 17, 40] = float("inf")            # not finite: that (b, g) gets an infinite bound
+    lm[2, 1, 30, 7] = float("nan")
     sh = dkb.build_landmark_shadow(lm.cuda())
     torch.cuda.synchronize()
-    assert torch.equal(sh.lm16.cpu(), lm.half())          # round to nearest even, per element
-    nm = sh.norm_max.cpu().numpy()
-    true = np.linalg.norm(lm.numpy().astype(np.float64), axis=-1).max(axis=-1)
-    assert np.isinf(nm[1, 1])
-    fin = np.isfinite(nm)
-    assert np.all(nm[fin] >= true[fin]) and np.all(nm[fin] <= true[fin] * (1 + 1e-5))
+    codes = sh.lm8.cpu().to(torch.int32) - 128
+    cs = sh.chunk_scale.cpu()
+    sm = sh.scale_max.cpu().numpy()
+    assert torch.all(codes.abs() <= 127)
+    fin = torch.isfinite(lm).all(dim=-1)        # [B, H, C]
+    # the scale is max |lm| / 127, correctly rounded
+    expect = lm.abs().amax(dim=-1) / 127                   # fp32 division, correctly rounded
+    assert torch.equal(cs[fin], expect[fin])
+    # each value within half a step (plus the division's rounding) of scale * code
+    err = (lm.double() - cs.double()[..., None] * codes.double()).abs()
+    bound = cs.double()[..., None] * (0.5 + 127 * 2.0 ** -23) + 1e-45
+    assert torch.all(err[fin] <= bound[fin])
+    assert np.all(codes[0, 1, 5].numpy() == 0) and cs[0, 1, 5] == 0
+    assert np.isinf(sm[1, 1]) and np.isinf(sm[2, 1])
+    ok = np.isfinite(sm)
+    assert np.all(sm[ok] == cs.amax(dim=-1).numpy()[ok])
 
 
 def test_score_topk_shadow_degenerate(dkb):
@@ -189,13 +202,13 @@ def test_score_topk_shadow_degenerate(dkb):
     lm_eq = np.broadcast_to(torch.randn(128, generator=g).numpy(), (1, 1, 300, 128)).astype(np.float32).copy()
     rows_diff, near = check_score_topk(dkb, qh, lm_eq, 37, 0.09, "mean", 4, True)
     assert rows_diff == 0
-    # near-ties finer than fp16 can see: a base row plus perturbations of 1e-5
+    # near-ties finer than the codes can see: a base row plus perturbations of 1e-5
     base = torch.randn(128, generator=g)
     pert = torch.randn(1, 1, 600, 128, generator=g) * 1e-5
     lm_nt = (base + pert).numpy().astype(np.float32)
     rows_diff, near = check_score_topk(dkb, qh, lm_nt, 50, 0.09, "mean", 4, True)
     print(f"near-tie stress: rows differing {rows_diff}, near-tie chunks {near}")
-    # a landmark beyond fp16 range: the (b, g) is re-scored exactly
+    # one landmark far larger than the rest: its chunk's scale is huge, the others' are not
     lm_big = torch.randn(1, 1, 256, 128, generator=g).numpy().astype(np.float32)
     lm_big[0, 0, 100] = 7e4
     rows_diff, near = check_score_topk(dkb, qh, lm_big, 9, 0.09, "mean", 4, True)
