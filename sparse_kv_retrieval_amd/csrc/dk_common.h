@@ -107,6 +107,22 @@ __device__ __forceinline__ float dpp_group_sum(float v) {
     return v;
 }
 
+// Workgroups go to the 8 XCDs (each with its own L2) round-robin by block id.
+// Block id -> (unit, sub) with `per` blocks per unit and n_units units: when
+// n_units is a multiple of 8 every block of a unit runs on XCD unit % 8, so the
+// kernels of one step that map their blocks this way find a (b, g)'s
+// intermediate rows in the L2 that wrote them; otherwise the plain order.
+__device__ __forceinline__ void xcd_unit(int bid, int per, int n_units, int& unit, int& sub) {
+    if ((n_units & 7) == 0) {
+        const int slot = bid >> 3;
+        sub = slot % per;
+        unit = (slot / per) * 8 + (bid & 7);
+    } else {
+        sub = bid % per;
+        unit = bid / per;
+    }
+}
+
 // value of lane i ^ 1 (DPP quad_perm [1,0,3,2]; a VALU op, no LDS round trip)
 __device__ __forceinline__ float dpp_xor1(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));

@@ -112,8 +112,8 @@ __global__ __launch_bounds__(kThreads) void k_attn_bf16_d128_g4t2(AttnArgs a) {
     __shared__ FastSmem sm;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int split = blockIdx.x % a.splits;
-    const int bg = blockIdx.x / a.splits;
+    int bg, split;
+    xcd_unit(blockIdx.x, a.splits, gridDim.x / a.splits, bg, split);
     const int b = bg / a.Hkv, g = bg - b * a.Hkv;
     int u0, u1;
     entry_range(a, bg, split, u0, u1);
@@ -516,8 +516,8 @@ __global__ __launch_bounds__(kThreads) void k_attn_generic(AttnArgs a) {
     __shared__ __align__(16) float zs[RMAX][TR];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int split = blockIdx.x % a.splits;
-    const int bg = blockIdx.x / a.splits;
+    int bg, split;
+    xcd_unit(blockIdx.x, a.splits, gridDim.x / a.splits, bg, split);
     const int b = bg / a.Hkv, g = bg - b * a.Hkv;
     const int G = a.G, T = a.T, R = G * T;
     int u0, u1;

@@ -480,12 +480,13 @@ __global__ __launch_bounds__(kThreads) void k_score_lo(const float* __restrict__
                                                       const uint8_t* __restrict__ lm8,
                                                       const float* __restrict__ chunk_scale, int Hkv, int C,
                                                       float scale, int rows_per_block, int blocks_per_bg,
-                                                      float* __restrict__ s_lo, uint32_t* __restrict__ arrivals) {
+                                                      float* __restrict__ s_lo, uint32_t* __restrict__ arrivals,
+                                                      float* __restrict__ kq) {
     constexpr int LPR = D / 16, RPW = kWave / LPR, U = DK_SCORE_LO_UNROLL;
     constexpr int G = MAXRED ? NQ / T : 0;
     extern __shared__ float sres[];    // [T][rows_per_block], then [NQ][D] query vectors
-    const int blk = blockIdx.x % blocks_per_bg;
-    const int bg = blockIdx.x / blocks_per_bg;
+    int bg, blk;
+    xcd_unit(blockIdx.x, blocks_per_bg, gridDim.x / blocks_per_bg, bg, blk);
     const int b = bg / Hkv, g = bg - b * Hkv;
     const int row0 = blk * rows_per_block;
     const int nrows = min(rows_per_block, C - row0);
@@ -529,6 +530,50 @@ __global__ __launch_bounds__(kThreads) void k_score_lo(const float* __restrict__
         qs[i] = xq;
     }
     __syncthreads();
+    if (blk == 0) {
+        // The error bound's query factor for the selection pass.  With m_i the
+        // codes, s_c the chunk scale, q^ = fp16(q) and u16 = 2^-11:
+        //   |sum q_i l_i - s_c sum q^_i m_i| <= s_c (1/2 + 127 u32) |q|_1            (the codes)
+        //                                     + s_c 127 (u16 |q|_1 + D 2^-25)   (q in fp16, subnormals too),
+        // the fp32 sums here and of the fp32 re-score add at most (D + 40)
+        // roundings of terms up to 127 s_c |q_i|, and the scale products a few
+        // relative roundings: |s - s_lo| <= kq * s_c.  A query value beyond fp16
+        // voids the bound (kq = inf: every chunk becomes a candidate).
+        float* part = sres;   // the score rows are not written yet
+        const int w = threadIdx.x / kWave;
+        for (int v = w; v < NQ; v += kThreads / kWave) {
+            float a1 = 0.f, am = 0.f;
+            for (int e = lane; e < D; e += kWave) {
+                a1 += fabsf(qs[v * D + e]);
+                am = fmaxf(am, fabsf(qs[v * D + e]));
+            }
+            for (int off = 1; off < kWave; off <<= 1) {
+                a1 += __shfl_xor(a1, off, kWave);
+                am = fmaxf(am, __shfl_xor(am, off, kWave));
+            }
+            if (lane == 0) {
+                part[2 * v] = a1;
+                part[2 * v + 1] = am;
+            }
+        }
+        __syncthreads();
+        if (threadIdx.x < T) {
+            const int t = threadIdx.x;
+            float l1 = 0.f, amax = 0.f;
+            for (int v = (MAXRED ? t * G : t); v < (MAXRED ? (t + 1) * G : t + 1); ++v) {
+                l1 = fmaxf(l1, part[2 * v]);
+                amax = fmaxf(amax, part[2 * v + 1]);
+            }
+            l1 *= 1.0f + (float)(D + 8) * 5.9604645e-8f;   // round the sum up
+            const float u16 = 4.8828125e-4f, u32 = 5.9604645e-8f;
+            float k_ = fabsf(scale) *
+                       (l1 * (0.5f + 127.f * u32 + 127.f * u16 + (float)(D + 40) * 127.f * u32) +
+                        127.f * (float)D * 2.9802322e-8f) * 1.01f;
+            if (!(amax <= 65000.f) || !(k_ <= 3.0e38f)) k_ = INFINITY;
+            kq[(int64_t)bg * T + t] = k_;
+        }
+        __syncthreads();
+    }
     uint32_t qh[NQ][8];
 #pragma unroll
     for (int v = 0; v < NQ; ++v)
@@ -595,7 +640,7 @@ __global__ __launch_bounds__(kThreads) void k_select_exact(
     const float* __restrict__ chunk_scale, const float* __restrict__ scale_max, const float* __restrict__ s_lo,
     int Hkv, int C, int k,
     float scale, int32_t* __restrict__ topk_idx, float* __restrict__ topk_score, UnionOut un,
-    uint32_t* __restrict__ arrivals) {
+    uint32_t* __restrict__ arrivals, const float* __restrict__ kq) {
     constexpr int LPR = D / 8;                 // lanes per fp32 row, 8 floats each
     constexpr int RPW = kWave / LPR;
     extern __shared__ uint32_t smem2[];
@@ -611,10 +656,10 @@ __global__ __launch_bounds__(kThreads) void k_select_exact(
     uint32_t* hist = (uint32_t*)(qv + nvec * D);     // [256]
     int* scratch = (int*)(hist + 256);               // [8]
     int* bc = scratch + 8;                           // [2]
-    float* sf = (float*)(bc + 2);                    // [2] query 1-norm, largest |q|
+    float* sf = (float*)(bc + 2);                    // [2] spare
 
-    const int t = blockIdx.x % T;
-    const int bg = blockIdx.x / T;
+    int bg, t;
+    xcd_unit(blockIdx.x, T, gridDim.x / T, bg, t);
     const int b = bg / Hkv, g = bg - b * Hkv;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
 
@@ -647,6 +692,7 @@ __global__ __launch_bounds__(kThreads) void k_select_exact(
         }
     }
     const float SM = scale_max[bg];
+    const float Kq = kq[(int64_t)bg * T + t];
     for (int i = tid; i < nvec * D; i += kThreads) {
         const int v = i / D, e = i - v * D;
         float x;
@@ -659,39 +705,9 @@ __global__ __launch_bounds__(kThreads) void k_select_exact(
         }
         qv[i] = x;
     }
-    __syncthreads();
-    if (wave == 0) {
-        // largest 1-norm of the query vectors (rounded up) and largest |q|
-        float l1max = 0.f, amax = 0.f;
-        for (int v = 0; v < nvec; ++v) {
-            float s1 = 0.f;
-            for (int e = lane; e < D; e += kWave) {
-                s1 += fabsf(qv[v * D + e]);
-                amax = fmaxf(amax, fabsf(qv[v * D + e]));
-            }
-            for (int off = 1; off < kWave; off <<= 1) s1 += __shfl_xor(s1, off, kWave);
-            l1max = fmaxf(l1max, s1);
-        }
-        for (int off = 1; off < kWave; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
-        if (lane == 0) {
-            sf[0] = l1max * (1.0f + (float)(D + 8) * 5.9604645e-8f);
-            sf[1] = amax;
-        }
-    }
-    __syncthreads();
-    // The bound.  With m_i the codes, s_c the scale, q^ = fp16(q) and u16 = 2^-11:
-    //   |sum q_i l_i - s_c sum q^_i m_i| <= s_c (1/2 + 127 u32) |q|_1   (the codes)
-    //                                     + s_c 127 (u16 |q|_1 + D 2^-25)  (q in fp16, incl. subnormals),
-    // the fp32 sums on both sides add at most (D + 40) roundings of terms up to
-    // 127 s_c |q_i|, and the scale products a few relative roundings more.
-    const float u16 = 4.8828125e-4f, u32 = 5.9604645e-8f;
-    const float L1 = sf[0];
-    const float Kq = fabsf(scale) *
-                     (L1 * (0.5f + 127.f * u32 + 127.f * u16 + (float)(D + 40) * 127.f * u32) +
-                      127.f * (float)D * 2.9802322e-8f) * 1.01f;
-    // a landmark or query value that the codes or fp16 cannot hold voids the bound:
-    // every chunk is then a candidate
-    const bool valid = SM <= 3.0e38f && sf[1] <= 65000.f && Kq <= 3.0e38f;
+    // the bound |s - s_lo| <= Kq * s_c (Kq from the score pass); a landmark the
+    // codes cannot hold, or Kq = inf, voids it: every chunk is then a candidate
+    const bool valid = SM <= 3.0e38f && Kq <= 3.0e38f;
     uint32_t kr[KPT];
     uint32_t tmax = 0u;
 #pragma unroll
@@ -889,22 +905,22 @@ hipError_t dispatch_split(int nq, int T, bool maxred, const float* q, int B, int
 template <int D, int NQ, int T, bool MAXRED>
 hipError_t launch_lo(const float* q, int B, int Hq, const uint8_t* lm8, const float* cscale, int Hkv, int C,
                      float scale,
-                     const TopkPlan& p, float* s_lo, uint32_t* arrivals, hipStream_t st) {
+                     const TopkPlan& p, float* s_lo, uint32_t* arrivals, float* kq, hipStream_t st) {
     const size_t lds = (((size_t)T * p.rows + 3) & ~(size_t)3) * 4 + (size_t)NQ * D * 4;
     const unsigned grid = (unsigned)((int64_t)B * Hkv * p.splits);
     hipLaunchKernelGGL((k_score_lo<D, NQ, T, MAXRED>), dim3(grid), dim3(kThreads), lds, st, q, Hq, lm8, cscale,
-                       Hkv, C, scale, p.rows, p.splits, s_lo, arrivals);
+                       Hkv, C, scale, p.rows, p.splits, s_lo, arrivals, kq);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t dispatch_lo(int nq, int T, bool maxred, const float* q, int B, int Hq, const uint8_t* lm8,
                        const float* cscale,
-                       int Hkv, int C, float scale, const TopkPlan& p, float* s_lo, uint32_t* arrivals,
+                       int Hkv, int C, float scale, const TopkPlan& p, float* s_lo, uint32_t* arrivals, float* kq,
                        hipStream_t st) {
 #define DK_LO(NQ_, T_, MX_) \
     if (nq == NQ_ && T == T_ && maxred == MX_) \
-        return launch_lo<D, NQ_, T_, MX_>(q, B, Hq, lm8, cscale, Hkv, C, scale, p, s_lo, arrivals, st);
+        return launch_lo<D, NQ_, T_, MX_>(q, B, Hq, lm8, cscale, Hkv, C, scale, p, s_lo, arrivals, kq, st);
     DK_LO(1, 1, false)
     DK_LO(2, 2, false)
     DK_LO(1, 1, true)
@@ -949,8 +965,9 @@ TopkPlan plan_topk(int B, int Hkv, int T, int C, int k, bool shadow) {
             p.splits -= 1;
             p.rows = (C + p.splits - 1) / p.splits;
         }
-        // fp16-pass scores, then one arrival counter per (b, g) for the fused union
-        p.ws_bytes = (((size_t)bg * T * C * 4 + 15) & ~(size_t)15) + (size_t)bg * 4;
+        // shadow-pass scores, one arrival counter per (b, g) for the fused union, the
+        // bound factor per (b, g, t)
+        p.ws_bytes = (((size_t)bg * T * C * 4 + 15) & ~(size_t)15) + (size_t)bg * 4 + (size_t)bg * T * 4;
         return p;
     }
     int64_t want = (2048 + bg - 1) / bg;
@@ -1008,13 +1025,15 @@ hipError_t launch_score_topk(const float* q, int B, int T, int Hq, const float* 
         // prefix (3k + 1 ints) fit where its keys and candidates were
         const int Cp = (C + 3) & ~3;
         const bool fuse = un && 3 * (int64_t)k + 1 <= (int64_t)Cp + (Cp > kThreads ? Cp : kThreads);
-        uint32_t* arrivals =
-            fuse ? (uint32_t*)((char*)ws + (((size_t)bg * T * C * 4 + 15) & ~(size_t)15)) : nullptr;
+        // workspace: scores [bg, T, C] | one arrival counter per (b, g) | the bound factor per (b, g, t)
+        const size_t sbytes = ((size_t)bg * T * C * 4 + 15) & ~(size_t)15;
+        uint32_t* arrivals = fuse ? (uint32_t*)((char*)ws + sbytes) : nullptr;
+        float* kq = (float*)((char*)ws + sbytes + (size_t)bg * 4);
         hipError_t e = d == 128
             ? dispatch_lo<128>(nq, T, maxred, q, B, Hq, shadow->lm8, shadow->chunk_scale, Hkv, C, scale, p, s_lo,
-                               arrivals, st)
+                               arrivals, kq, st)
             : dispatch_lo<64>(nq, T, maxred, q, B, Hq, shadow->lm8, shadow->chunk_scale, Hkv, C, scale, p, s_lo,
-                              arrivals, st);
+                              arrivals, kq, st);
         if (e != hipSuccess) return e;
         const unsigned grid = (unsigned)(bg * T);
         const size_t lds = select_lds_bytes(C, d, maxred ? G : 1);
@@ -1023,7 +1042,7 @@ hipError_t launch_score_topk(const float* q, int B, int T, int Hq, const float* 
 #define DK_SEL(D_, MX_)                                                                            \
     hipLaunchKernelGGL((k_select_exact<D_, MX_>), dim3(grid), dim3(kThreads), lds, st, q, T, Hq, lm, ls, \
                        shadow->chunk_scale, shadow->scale_max, s_lo, Hkv, C, k, scale, topk_idx, topk_score, uo, \
-                       arrivals)
+                       arrivals, kq)
         if (d == 128) { if (maxred) DK_SEL(128, true); else DK_SEL(128, false); }
         else { if (maxred) DK_SEL(64, true); else DK_SEL(64, false); }
 #undef DK_SEL

@@ -112,7 +112,8 @@ def test_score_topk_workspace_sizes():
     assert lib.dk_score_topk_workspace_size(64, 8, 2, 4096, 64, 0) == 64 * 8 * 2 * 4 * 64 * 8
     # with a shadow: every fp16 score of every (b, g, t), then one arrival
     # counter per (b, g) for the fused union
-    assert lib.dk_score_topk_workspace_size(64, 8, 2, 4096, 64, 1) == 64 * 8 * 2 * 4096 * 4 + 64 * 8 * 4
+    # shadow scores [B, Hkv, T, C], one arrival counter per (b, g), one bound factor per (b, g, t)
+    assert lib.dk_score_topk_workspace_size(64, 8, 2, 4096, 64, 1) == 64 * 8 * 2 * 4096 * 4 + 64 * 8 * 4 + 64 * 8 * 2 * 4
     assert lib.dk_score_topk_workspace_size(1, 1, 2, 128, 8, 0) > 0
     assert lib.dk_score_topk_workspace_size(1, 1, 2, 128, 0, 0) == 0
 
