@@ -460,19 +460,20 @@ __global__ __launch_bounds__(kThreads) void k_build_shadow(const float* __restri
 // Shadow pass 1: scores of every chunk from the 8-bit codes, streamed with
 // non-temporal 16-byte loads; LPR = D / 16 lanes per row, 16 codes per lane.
 // A byte pair becomes two exact fp16 values with one v_perm against the fp16
-// exponent byte 0x64 (0x64XX is 1024 + XX) and one packed subtraction of 1152,
-// then v_dot2_f32_f16 against the fp16 query; the row sums use DPP only and the
-// chunk's scale multiplies the sum.  Scores of one block's rows are staged in
+// exponent byte 0x64 (0x64XX is 1024 + XX = code + 1152), multiplied into the
+// fp16 query with v_dot2_f32_f16; each lane then takes 1152 times its share of
+// the query sum off once, the row sums use DPP only, and the chunk's scale
+// multiplies the sum.  Two load batches alternate, so one is in flight while
+// the other is decoded.  Scores of one block's rows are staged in
 // LDS and stored coalesced to s_lo [B * Hkv, T, C] (fp32).
 // ---------------------------------------------------------------------------
 #ifndef DK_SCORE_LO_UNROLL
-#define DK_SCORE_LO_UNROLL 8   // 16-byte code loads in flight per lane
+#define DK_SCORE_LO_UNROLL 2   // 16-byte code loads per lane per batch
 #endif
 
-// bytes 0, 1 (sel 0x04010400) or 2, 3 (sel 0x04030402) of w as two fp16 values byte - 128
+// bytes 0, 1 (sel 0x04010400) or 2, 3 (sel 0x04030402) of w as two fp16 values byte + 1024
 __device__ __forceinline__ uint32_t code_pair(uint32_t w, uint32_t sel) {
-    const f16x2_t h = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, w, sel));
-    return __builtin_bit_cast(uint32_t, h - f16x2_t{(_Float16)1152.0f, (_Float16)1152.0f});
+    return __builtin_amdgcn_perm(0x64646464u, w, sel);
 }
 
 template <int D, int NQ, int T, bool MAXRED>
@@ -501,18 +502,18 @@ __global__ __launch_bounds__(kThreads) void k_score_lo(const float* __restrict__
     const uint8_t* base = lm8 + ((int64_t)bg * C + row0) * D + part * 16;
     const float* sbase = chunk_scale + (int64_t)bg * C + row0;
     constexpr int ROWS_PER_ITER = 4 * RPW * U;
-    u32x4_t x[U];
-    float rs[U];
-    auto load_rows = [&](int it) {
+    u32x4_t xa[U], xb[U];
+    float ra[U], rb[U];
+    auto load_rows = [&](int it, u32x4_t (&xx)[U], float (&rr)[U]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int r = it + (u * 4 + wave) * RPW + rp;
-            x[u] = r < nrows ? nt_load_u4(base + (int64_t)r * D) : u32x4_t{0x80808080u, 0x80808080u, 0x80808080u,
-                                                                           0x80808080u};
-            rs[u] = part < T && r < nrows ? sbase[r] : 0.f;
+            xx[u] = r < nrows ? nt_load_u4(base + (int64_t)r * D) : u32x4_t{0x80808080u, 0x80808080u, 0x80808080u,
+                                                                            0x80808080u};
+            rr[u] = part < T && r < nrows ? sbase[r] : 0.f;
         }
     };
-    load_rows(0);
+    load_rows(0, xa, ra);
 
     // The query vectors of this (b, g) go through LDS once per block (one 16-byte
     // global load per lane would otherwise be repeated by every row-lane group).
@@ -536,8 +537,9 @@ __global__ __launch_bounds__(kThreads) void k_score_lo(const float* __restrict__
         //   |sum q_i l_i - s_c sum q^_i m_i| <= s_c (1/2 + 127 u32) |q|_1            (the codes)
         //                                     + s_c 127 (u16 |q|_1 + D 2^-25)   (q in fp16, subnormals too),
         // the fp32 sums here and of the fp32 re-score add at most (D + 40)
-        // roundings of terms up to 127 s_c |q_i|, and the scale products a few
-        // relative roundings: |s - s_lo| <= kq * s_c.  A query value beyond fp16
+        // roundings of terms up to 127 s_c |q_i|; the lanes sum q^_i (code_i + 1152)
+        // and take off 1152 times their fp32 sum of q^: at most 48000 u32 s_c |q|_1
+        // more; the scale products add a few relative roundings: |s - s_lo| <= kq * s_c.  A query value beyond fp16
         // voids the bound (kq = inf: every chunk becomes a candidate).
         float* part = sres;   // the score rows are not written yet
         const int w = threadIdx.x / kWave;
@@ -567,7 +569,7 @@ __global__ __launch_bounds__(kThreads) void k_score_lo(const float* __restrict__
             l1 *= 1.0f + (float)(D + 8) * 5.9604645e-8f;   // round the sum up
             const float u16 = 4.8828125e-4f, u32 = 5.9604645e-8f;
             float k_ = fabsf(scale) *
-                       (l1 * (0.5f + 127.f * u32 + 127.f * u16 + (float)(D + 40) * 127.f * u32) +
+                       (l1 * (0.5f + 127.f * u32 + 127.f * u16 + ((float)(D + 40) * 127.f + 48000.f) * u32) +
                         127.f * (float)D * 2.9802322e-8f) * 1.01f;
             if (!(amax <= 65000.f) || !(k_ <= 3.0e38f)) k_ = INFINITY;
             kq[(int64_t)bg * T + t] = k_;
@@ -575,19 +577,24 @@ __global__ __launch_bounds__(kThreads) void k_score_lo(const float* __restrict__
         __syncthreads();
     }
     uint32_t qh[NQ][8];
+    float qbias[NQ];   // 1152 times this lane's share of the fp16 query sum
 #pragma unroll
-    for (int v = 0; v < NQ; ++v)
+    for (int v = 0; v < NQ; ++v) {
+        float sq = 0.f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            qh[v][j] = f16_bits(qs[v * D + part * 16 + 2 * j]) | (f16_bits(qs[v * D + part * 16 + 2 * j + 1]) << 16);
+        for (int j = 0; j < 8; ++j) {
+            const _Float16 h0 = (_Float16)qs[v * D + part * 16 + 2 * j];
+            const _Float16 h1 = (_Float16)qs[v * D + part * 16 + 2 * j + 1];
+            qh[v][j] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+            sq += (float)h0 + (float)h1;
+        }
+        qbias[v] = 1152.f * sq;
+    }
 
-    for (int it = 0; it < nrows; it += ROWS_PER_ITER) {
-        if (it) load_rows(it);
-        int rr[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) rr[u] = it + (u * 4 + wave) * RPW + rp;
+    auto process = [&](int it, const u32x4_t (&x)[U], const float (&rs)[U]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+            const int rr = it + (u * 4 + wave) * RPW + rp;
             uint32_t h[8];
             h[0] = code_pair(x[u].x, 0x04010400u); h[1] = code_pair(x[u].x, 0x04030402u);
             h[2] = code_pair(x[u].y, 0x04010400u); h[3] = code_pair(x[u].y, 0x04030402u);
@@ -596,10 +603,10 @@ __global__ __launch_bounds__(kThreads) void k_score_lo(const float* __restrict__
             float dot[NQ];
 #pragma unroll
             for (int v = 0; v < NQ; ++v) {
-                float a = 0.f;
+                float a = dot2_f16(qh[v][0], h[0], 0.f);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) a = dot2_f16(qh[v][j], h[j], a);
-                dot[v] = dpp_group_sum<LPR>(a);
+                for (int jj = 1; jj < 8; ++jj) a = dot2_f16(qh[v][jj], h[jj], a);
+                dot[v] = dpp_group_sum<LPR>(a - qbias[v]);
             }
             // per-query scores with compile-time register indices
             const float sc = scale * rs[u];
@@ -614,9 +621,15 @@ __global__ __launch_bounds__(kThreads) void k_score_lo(const float* __restrict__
                     sct[t] = sc * dot[t];
                 }
             }
-            if (part < T && rr[u] < nrows)
-                sres[part * rows_per_block + rr[u]] = (part == 0) ? sct[0] : sct[T - 1];
+            if (part < T && rr < nrows) sres[part * rows_per_block + rr] = (part == 0) ? sct[0] : sct[T - 1];
         }
+    };
+    for (int it = 0; it < nrows; it += 2 * ROWS_PER_ITER) {
+        if (it + ROWS_PER_ITER < nrows) load_rows(it + ROWS_PER_ITER, xb, rb);
+        process(it, xa, ra);
+        if (it + ROWS_PER_ITER >= nrows) break;
+        if (it + 2 * ROWS_PER_ITER < nrows) load_rows(it + 2 * ROWS_PER_ITER, xa, ra);
+        process(it + ROWS_PER_ITER, xb, rb);
     }
     __syncthreads();
     for (int t = 0; t < T; ++t) {
