@@ -221,6 +221,10 @@ struct IndexPlan {
     size_t off_min;      // byte offsets of the per-block score minima / maxima
     size_t off_max;
     size_t off_arrive;   // one arrival counter per (b, g) for the fused union
+    // split selection of long rows (slices == 0: one block per row)
+    int slices;          // blocks per row
+    int slice_len;       // positions per slice (a multiple of 4096)
+    size_t off_hist, off_aid, off_aval, off_cid, off_cval, off_cnt, off_flag;
     size_t ws_bytes;
 };
 IndexPlan plan_index_topk(int B, int Hkv, int T, int C);
@@ -228,7 +232,7 @@ IndexPlan plan_index_topk(int B, int Hkv, int T, int C);
 // (the plan's layout), optionally with the union of each (b, g)'s T sets.
 hipError_t launch_select_rows(const float* scores, const float* bmin, const float* bmax, int blocks_per_row, int B,
                               int Hkv, int T, int C, int k, int32_t* topk_idx, float* topk_score, const UnionOut* un,
-                              uint32_t* arrivals, hipStream_t st);
+                              uint32_t* arrivals, const IndexPlan& plan, void* ws, hipStream_t st);
 // Min/max chunk summaries and the top-k by their upper-bound scores (k_minmax.hip).
 hipError_t launch_build_minmax(const void* K, dk_dtype dt, dk_strides ks, int B, int Hkv, int L, int d, int chunk,
                                void* kmin, void* kmax, hipStream_t st);

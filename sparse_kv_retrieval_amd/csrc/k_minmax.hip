@@ -322,7 +322,7 @@ hipError_t launch_minmax_topk(const float* q, int B, int T, int Hq, const void* 
     if (e != hipSuccess) return e;
     return launch_select_rows((const float*)ws, (const float*)((char*)ws + plan.off_min),
                               (const float*)((char*)ws + plan.off_max), plan.blocks_per_bg, B, Hkv, T, C, k, topk_idx,
-                              topk_score, un, arrivals, st);
+                              topk_score, un, arrivals, plan, ws, st);
 }
 
 }  // namespace dk

@@ -122,7 +122,12 @@ def test_index_topk_workspace_size():
     # fp32 scores of every token of every (b, g, t), then the per-block score
     # minima and maxima (1024 tokens per block), then one union arrival counter
     # per (b, g), each region 256-byte aligned
-    assert lib.dk_index_topk_workspace_size(32, 1, 2, 131072) == 32 * 2 * 131072 * 4 + 2 * 32 * 2 * 128 * 4 + 256
+    # scores, per-block minima and maxima, arrival counters; rows of >= 32768 positions also
+    # get the split selection's regions (8 slices: histograms, ordered lists, candidates,
+    # counts, flags; each 256-byte aligned)
+    rows, P = 32 * 2, 8
+    split = rows * P * (2048 * 4 + 2 * 4096 * 4 + 2 * 2048 * 4 + 2 * 4) + 256
+    assert lib.dk_index_topk_workspace_size(32, 1, 2, 131072) == 32 * 2 * 131072 * 4 + 2 * 32 * 2 * 128 * 4 + 256 + split
     assert lib.dk_index_topk_workspace_size(1, 1, 1, 2048) == 2048 * 4 + 2 * 256 + 256
     assert lib.dk_index_topk_workspace_size(1, 1, 3, 2048) == 0
 

@@ -77,6 +77,8 @@ def mla_inputs(w, seed):
     ("mla_b1_l2k", dict(T=1)),
     ("mla_b1_l2k", dict(k=2048)),          # every token
     ("mla_b1_l2k", dict(L=3076, k=700)),   # tokens not a multiple of the scoring block
+    ("mla_b1_l2k", dict(L=50004, k=700)),  # split selection: three slices, the last one short
+    ("mla_b2_l16k", dict(L=65536, k=2048)),  # split selection: four slices per row
 ])
 def test_index_topk(dkb, name, kw):
     w = MLA_WORKLOADS[name].with_(**kw)
@@ -99,17 +101,18 @@ def test_index_topk_grouped_heads_d64(dkb):
     check_index(dkb, qi, keys, 333, 0.125, union=True)
 
 
-@pytest.mark.parametrize("kind", ["zeros", "quantised"])
-def test_index_topk_ties(dkb, kind):
-    # equal scores over whole bins: the radix fallback and the position rule
+@pytest.mark.parametrize("kind,C", [("zeros", 8192), ("quantised", 8192), ("zeros", 40000), ("quantised", 40000)])
+def test_index_topk_ties(dkb, kind, C):
+    # equal scores over whole bins: the radix fallback and the position rule; at
+    # C = 40000 the split selection flags the rows and falls back to one block per row
     g = torch.Generator(device="cuda").manual_seed(10)
     qi = synth.round_bf16(torch.randn(2, 2, 4, 128, generator=g, device="cuda"))
     if kind == "zeros":
-        keys = torch.zeros(2, 1, 8192, 128, dtype=torch.bfloat16, device="cuda")
+        keys = torch.zeros(2, 1, C, 128, dtype=torch.bfloat16, device="cuda")
     else:
         # keys in {-1, 0, 1} on 2 dims: a handful of distinct scores, thousands each
-        keys = torch.zeros(2, 1, 8192, 128, device="cuda")
-        keys[..., :2] = torch.randint(-1, 2, (2, 1, 8192, 2), generator=g, device="cuda").float()
+        keys = torch.zeros(2, 1, C, 128, device="cuda")
+        keys[..., :2] = torch.randint(-1, 2, (2, 1, C, 2), generator=g, device="cuda").float()
         keys = bf16_keys(keys)
     near = check_index(dkb, qi, keys, 3000, 0.1, union=True, label=kind)
     assert near == 0
