@@ -657,7 +657,7 @@ __global__ __launch_bounds__(kThreads) void k_select_exact(
     constexpr int LPR = D / 8;                 // lanes per fp32 row, 8 floats each
     constexpr int RPW = kWave / LPR;
     extern __shared__ uint32_t smem2[];
-    // LDS: keys [Cp] | cand [max(Cp, 256)] | qv [nvec][D] | hist [256] | scratch | bc | sf,
+    // LDS: keys [Cp] | cand [max(Cp, 256)] | qv [nvec][D] | hist [256] | scratch [8] | bc [2],
     // Cp = C rounded up to 4 so that every array starts on 16 bytes
     const int Cp = (C + 3) & ~3;
     uint32_t* keys = smem2;
@@ -669,7 +669,6 @@ __global__ __launch_bounds__(kThreads) void k_select_exact(
     uint32_t* hist = (uint32_t*)(qv + nvec * D);     // [256]
     int* scratch = (int*)(hist + 256);               // [8]
     int* bc = scratch + 8;                           // [2]
-    float* sf = (float*)(bc + 2);                    // [2] spare
 
     int bg, t;
     xcd_unit(blockIdx.x, T, gridDim.x / T, bg, t);
