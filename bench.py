@@ -67,6 +67,9 @@ def parse():
     ap.add_argument("--slots", type=int, default=None, help="capped: working-set slots per (b, g) (default 4k)")
     ap.add_argument("--lookahead", type=int, default=2,
                     help="host-pool workloads: layers between a selection/transfer and its attention")
+    ap.add_argument("--host-buffers", choices=("per-layer", "ping-pong"), default="per-layer",
+                    help="host-pool workloads: a hot cache per layer (residency kept across steps) or "
+                         "max(2, lookahead) buffers shared by the layers (every union chunk copied every step)")
     return ap.parse_args()
 
 
@@ -234,7 +237,7 @@ def bench_host_pool(args, w):
     del K, V
     torch.cuda.empty_cache()
     dec = HostPoolDecoder(Kh, Vh, lm, shadow, T=w.T, Hq=w.Hq, k=w.k, scale=w.scale, layers=w.layers,
-                          mode=args.host_copy, lookahead=args.lookahead)
+                          mode=args.host_copy, lookahead=args.lookahead, buffers=args.host_buffers)
     link_gbps = h2d_peak_gbps(torch)
     torch.cuda.synchronize()
     print(f"[bench] inputs ready in {time.time() - t0:.1f} s: host pool {2 * Kh.nbytes / 1e9:.2f} GB pinned, "
@@ -287,7 +290,8 @@ def bench_host_pool(args, w):
         "config": {"workload": w.name, "B": w.B, "L": w.L, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d,
                    "chunk": w.chunk, "k": w.k, "T": w.T, "layers": w.layers, "seed": args.seed,
                    "landmark_shadow": shadow is not None, "host_copy": args.host_copy,
-                   "hot_cache_slots": dec.slots, "drift": 0.05, "lookahead": dec.lookahead},
+                   "hot_cache_slots": dec.slots, "drift": 0.05, "lookahead": dec.lookahead,
+                   "host_buffers": dec.buffers, "hot_cache_GB": round(2 * dec.Kc.nbytes / 1e9, 2)},
         "hit_rate": round(hits / max(unions, 1), 5),
         "misses_per_bg_layer": round(misses / max(n_units, 1), 3),
         "miss_bytes_per_step": int(miss_bytes_step),

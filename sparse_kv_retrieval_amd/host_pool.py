@@ -7,7 +7,12 @@ Figure 2: a per-head hot cache in HBM, a resolver that copies only the missed
 rows from host DRAM, and attention that reads the hot cache afterwards.
 
 Per layer the hot cache holds exactly the previous step's union of the two
-queries' chunk sets (T*k slots per (b, g)).  One step, per layer l:
+queries' chunk sets (T*k slots per (b, g)).  With buffers="ping-pong" the
+layers share max(2, lookahead) such buffers instead (layer l uses buffer
+l mod that count; DualDecoder "5.3", the two-layer buffer of Figure 9(a)):
+HBM holds two layers' selected KV instead of every layer's, and since a buffer
+last held another layer's chunks, every chunk of a layer's union is copied at
+every step.  One step, per layer l:
 
   compute stream : dk_score_topk(l), dk_union_select(l, plan)  -> misses of l
   copy stream    : dk_gather_kv(l)  host pool -> free slots of l's hot cache
@@ -38,9 +43,11 @@ from . import binding as dkb
 
 class HostPoolDecoder:
     def __init__(self, K_host, V_host, lm, shadow, *, T, Hq, k, scale, layers, mode="mapped",
-                 device="cuda", reduce=dkb.DK_REDUCE_MEAN, lookahead=2):
+                 device="cuda", reduce=dkb.DK_REDUCE_MEAN, lookahead=2, buffers="per-layer"):
         if mode not in ("mapped", "copy"):
             raise ValueError("mode must be 'mapped' or 'copy'")
+        if buffers not in ("per-layer", "ping-pong"):
+            raise ValueError("buffers must be 'per-layer' or 'ping-pong'")
         if K_host.is_cuda or not (K_host.is_pinned() and V_host.is_pinned()):
             raise ValueError("the KV pool must be in pinned host memory")
         B, Hkv, L, d = K_host.shape
@@ -54,8 +61,15 @@ class HostPoolDecoder:
         self.K_host, self.V_host, self.lm, self.shadow = K_host, V_host, lm, shadow
         self.slots = T * k
         n = T * k
+        # Buffer of each layer.  A ping-pong buffer is refilled for layer l + nbuf
+        # only after layer l's attention: in both schedules that selection (and so
+        # the copy that waits for it) is queued on the compute stream behind it.
+        self.buffers = buffers
+        self.nbuf = layers if buffers == "per-layer" else min(layers, max(2, lookahead))
+        self.buf = [l % self.nbuf for l in range(layers)]
+        self.shared = self.nbuf < layers           # a buffer changes layers: no residency
         i32 = dict(dtype=torch.int32, device=device)
-        cache_shape = (layers, B, Hkv, self.slots * chunk, d)
+        cache_shape = (self.nbuf, B, Hkv, self.slots * chunk, d)
         self.Kc = torch.zeros(cache_shape, dtype=K_host.dtype, device=device)
         self.Vc = torch.zeros(cache_shape, dtype=V_host.dtype, device=device)
         self.plans = [dkb.CachePlan.empty(B, Hkv, T, k, self.slots, device) for _ in range(layers)]
@@ -89,6 +103,8 @@ class HostPoolDecoder:
         cs = torch.cuda.current_stream()
         if timer:
             timer.begin("select", l, cs)
+        if self.shared:
+            self.plans[l].resident.fill_(-1)       # the buffer holds another layer's chunks
         dkb.score_topk(q, self.lm, self.k, self.scale, self.reduce, self.topk_idx[l], None, self.ws_topk,
                        shadow=self.shadow)
         dkb.union_select(self.topk_idx[l], self.C, self.union_ids[l], self.member[l], self.count[l],
@@ -111,11 +127,11 @@ class HostPoolDecoder:
         if timer:
             timer.begin("gather", l, cps)
         if self.mode == "mapped":
-            dkb.gather_kv(self.K_host, self.V_host, p.miss_chunk, p.miss_count, self.chunk, self.Kc[l],
-                          self.Vc[l], dst_slot=p.miss_slot, stream=cps)
+            dkb.gather_kv(self.K_host, self.V_host, p.miss_chunk, p.miss_count, self.chunk, self.Kc[self.buf[l]],
+                          self.Vc[self.buf[l]], dst_slot=p.miss_slot, stream=cps)
         else:
             dkb.gather_kv(self.K_host, self.V_host, self.h_miss_chunk[l], self.h_miss_count[l], self.chunk,
-                          self.Kc[l], self.Vc[l], dst_slot=self.h_miss_slot[l], stream=cps)
+                          self.Kc[self.buf[l]], self.Vc[self.buf[l]], dst_slot=self.h_miss_slot[l], stream=cps)
         if timer:
             timer.end("gather", l, cps)
         self.ev_gather[l].record(cps)
@@ -125,7 +141,8 @@ class HostPoolDecoder:
         cs.wait_event(self.ev_gather[l])
         if timer:
             timer.begin("attn", l, cs)
-        dkb.sparse_decode_attn(q, self.Kc[l], self.Vc[l], self.plans[l].slot_of_union, self.member[l],
+        dkb.sparse_decode_attn(q, self.Kc[self.buf[l]], self.Vc[self.buf[l]], self.plans[l].slot_of_union,
+                               self.member[l],
                                self.count[l], self.chunk, self.scale, pool_blocks=self.slots,
                                out=self.out[l], lse=self.lse[l], ws=self.ws_attn)
         if timer:

@@ -607,10 +607,12 @@ def test_step_full_size_sampled(dkb, name, samples):
 # host-resident pool: hot cache, misses copied from pinned host memory
 # ----------------------------------------------------------------------------
 
-def run_host_pool_steps(dkb, w, steps, mode, seed, check_pairs=None):
+def run_host_pool_steps(dkb, w, steps, mode, seed, check_pairs=None, buffers="per-layer"):
     """Run `steps` decode steps of the host-pool path and check every layer of every
     step against the oracle: selection (near-ties counted), the hot-cache plan
-    (oracle state machine over the GPU's sets), the cache contents, attention."""
+    (oracle state machine over the GPU's sets; with shared ping-pong buffers every
+    layer starts each step empty), the cache contents (layers that still own their
+    buffer when the step ends), attention."""
     from sparse_kv_retrieval_amd.host_pool import HostPoolDecoder
 
     qseq = [synth.make_query_sequence(w, seed, steps, layer=l, device="cuda") for l in range(w.layers)]
@@ -619,7 +621,7 @@ def run_host_pool_steps(dkb, w, steps, mode, seed, check_pairs=None):
     sh = dkb.build_landmark_shadow(lm)
     Kh_pin, Vh_pin = K.cpu().pin_memory(), V.cpu().pin_memory()
     dec = HostPoolDecoder(Kh_pin, Vh_pin, lm, sh, T=w.T, Hq=w.Hq, k=w.k, scale=w.scale, layers=w.layers,
-                          mode=mode)
+                          mode=mode, buffers=buffers)
     pairs = check_pairs or [(b, g) for b in range(w.B) for g in range(w.Hkv)]
     Kf = {bg: synth.to_numpy_f64(K[bg[0]:bg[0] + 1, bg[1]:bg[1] + 1]) for bg in pairs}
     Vf = {bg: synth.to_numpy_f64(V[bg[0]:bg[0] + 1, bg[1]:bg[1] + 1]) for bg in pairs}
@@ -634,6 +636,8 @@ def run_host_pool_steps(dkb, w, steps, mode, seed, check_pairs=None):
             plan = dec.plans[l]
             # the plan, bit-exact, from the oracle's state machine on the GPU's sets
             ru, rm, rc, ro = O.union_select(idx)
+            if dec.shared:
+                res[l] = np.full_like(res[l], -1)
             ref = O.cache_plan(res[l], ru, rc)
             np.testing.assert_array_equal(dec.union_ids[l].cpu().numpy(), ru)
             np.testing.assert_array_equal(dec.member[l].cpu().numpy(), rm)
@@ -644,15 +648,18 @@ def run_host_pool_steps(dkb, w, steps, mode, seed, check_pairs=None):
             if s:
                 hits += int(ref["hit_count"].sum())
                 unions += int(rc.sum())
-            # the hot cache holds exactly the union's chunks in their slots
+            # the hot cache holds exactly the union's chunks in their slots (a shared
+            # buffer only for the last layer that used it)
             sl = torch.from_numpy(ref["slot_of_union"]).cuda()
             uid = torch.from_numpy(ru).cuda()
-            for b, g in pairs:
+            owns = l >= w.layers - dec.nbuf
+            for b, g in (pairs if owns else []):
                 n = int(rc[b, g])
                 rows_c = (sl[b, g, :n, None] * w.chunk + torch.arange(w.chunk, device="cuda")).reshape(-1)
                 rows_p = (uid[b, g, :n, None] * w.chunk + torch.arange(w.chunk, device="cuda")).reshape(-1)
-                assert torch.equal(dec.Kc[l, b, g, rows_c], K[b, g, rows_p]), (s, l, b, g)
-                assert torch.equal(dec.Vc[l, b, g, rows_c], V[b, g, rows_p]), (s, l, b, g)
+                bi = dec.buf[l]
+                assert torch.equal(dec.Kc[bi, b, g, rows_c], K[b, g, rows_p]), (s, l, b, g)
+                assert torch.equal(dec.Vc[bi, b, g, rows_c], V[b, g, rows_p]), (s, l, b, g)
             # selection and attention against the oracle
             q = qseq[l][s]
             qh_all = q.cpu().numpy().astype(np.float64)
@@ -680,6 +687,16 @@ def test_host_pool_steps(dkb, mode):
     near, hit_rate = run_host_pool_steps(dkb, w, steps=4, mode=mode, seed=3)
     print(f"host pool ({mode}): near-tie chunks {near}, steady-state hit rate {hit_rate:.3f}")
     assert 0.0 < hit_rate < 1.0
+
+
+@pytest.mark.parametrize("mode", ["mapped", "copy"])
+def test_host_pool_steps_ping_pong(dkb, mode):
+    """Four layers over two shared buffers: every union chunk is copied at every
+    step, attention reads the buffer its layer was given."""
+    w = shrink(WORKLOADS["host_b32_l128k"], B=2, L=8192, layers=4)
+    near, hit_rate = run_host_pool_steps(dkb, w, steps=3, mode=mode, seed=5, buffers="ping-pong")
+    print(f"host pool ping-pong ({mode}): near-tie chunks {near}, hit rate {hit_rate:.3f}")
+    assert hit_rate == 0.0
 
 
 def test_host_pool_full_size_sampled(dkb):
