@@ -41,13 +41,28 @@ import torch
 from . import binding as dkb
 
 
+def buffer_layout(layers, lookahead, buffers):
+    """(buffer count, buffer of each layer, whether buffers change layers).
+
+    "per-layer": one buffer per layer, so residency carries over to the next step.
+    "ping-pong": max(2, lookahead) buffers (at most one per layer), layer l in
+    buffer l mod count.  The refill for layer l + count is queued behind layer l's
+    attention in both schedules of HostPoolDecoder.step, so it never overwrites
+    rows still being read; two buffers are the least the "copy" schedule needs,
+    since it queues layer l + 1's selection before layer l's attention."""
+    if buffers not in ("per-layer", "ping-pong"):
+        raise ValueError("buffers must be 'per-layer' or 'ping-pong'")
+    if layers < 1 or lookahead < 1:
+        raise ValueError("layers and lookahead must be >= 1")
+    nbuf = layers if buffers == "per-layer" else min(layers, max(2, lookahead))
+    return nbuf, [l % nbuf for l in range(layers)], nbuf < layers
+
+
 class HostPoolDecoder:
     def __init__(self, K_host, V_host, lm, shadow, *, T, Hq, k, scale, layers, mode="mapped",
                  device="cuda", reduce=dkb.DK_REDUCE_MEAN, lookahead=2, buffers="per-layer"):
         if mode not in ("mapped", "copy"):
             raise ValueError("mode must be 'mapped' or 'copy'")
-        if buffers not in ("per-layer", "ping-pong"):
-            raise ValueError("buffers must be 'per-layer' or 'ping-pong'")
         if K_host.is_cuda or not (K_host.is_pinned() and V_host.is_pinned()):
             raise ValueError("the KV pool must be in pinned host memory")
         B, Hkv, L, d = K_host.shape
@@ -61,13 +76,8 @@ class HostPoolDecoder:
         self.K_host, self.V_host, self.lm, self.shadow = K_host, V_host, lm, shadow
         self.slots = T * k
         n = T * k
-        # Buffer of each layer.  A ping-pong buffer is refilled for layer l + nbuf
-        # only after layer l's attention: in both schedules that selection (and so
-        # the copy that waits for it) is queued on the compute stream behind it.
         self.buffers = buffers
-        self.nbuf = layers if buffers == "per-layer" else min(layers, max(2, lookahead))
-        self.buf = [l % self.nbuf for l in range(layers)]
-        self.shared = self.nbuf < layers           # a buffer changes layers: no residency
+        self.nbuf, self.buf, self.shared = buffer_layout(layers, lookahead, buffers)
         i32 = dict(dtype=torch.int32, device=device)
         cache_shape = (self.nbuf, B, Hkv, self.slots * chunk, d)
         self.Kc = torch.zeros(cache_shape, dtype=K_host.dtype, device=device)
