@@ -607,7 +607,7 @@ def test_step_full_size_sampled(dkb, name, samples):
 # host-resident pool: hot cache, misses copied from pinned host memory
 # ----------------------------------------------------------------------------
 
-def run_host_pool_steps(dkb, w, steps, mode, seed, check_pairs=None, buffers="per-layer"):
+def run_host_pool_steps(dkb, w, steps, mode, seed, check_pairs=None, buffers="per-layer", lookahead=2):
     """Run `steps` decode steps of the host-pool path and check every layer of every
     step against the oracle: selection (near-ties counted), the hot-cache plan
     (oracle state machine over the GPU's sets; with shared ping-pong buffers every
@@ -621,7 +621,7 @@ def run_host_pool_steps(dkb, w, steps, mode, seed, check_pairs=None, buffers="pe
     sh = dkb.build_landmark_shadow(lm)
     Kh_pin, Vh_pin = K.cpu().pin_memory(), V.cpu().pin_memory()
     dec = HostPoolDecoder(Kh_pin, Vh_pin, lm, sh, T=w.T, Hq=w.Hq, k=w.k, scale=w.scale, layers=w.layers,
-                          mode=mode, buffers=buffers)
+                          mode=mode, buffers=buffers, lookahead=lookahead)
     pairs = check_pairs or [(b, g) for b in range(w.B) for g in range(w.Hkv)]
     Kf = {bg: synth.to_numpy_f64(K[bg[0]:bg[0] + 1, bg[1]:bg[1] + 1]) for bg in pairs}
     Vf = {bg: synth.to_numpy_f64(V[bg[0]:bg[0] + 1, bg[1]:bg[1] + 1]) for bg in pairs}
@@ -689,13 +689,15 @@ def test_host_pool_steps(dkb, mode):
     assert 0.0 < hit_rate < 1.0
 
 
-@pytest.mark.parametrize("mode", ["mapped", "copy"])
-def test_host_pool_steps_ping_pong(dkb, mode):
-    """Four layers over two shared buffers: every union chunk is copied at every
-    step, attention reads the buffer its layer was given."""
+@pytest.mark.parametrize("mode,lookahead", [("mapped", 2), ("copy", 2), ("mapped", 3)])
+def test_host_pool_steps_ping_pong(dkb, mode, lookahead):
+    """Four layers over max(2, lookahead) shared buffers: every union chunk is
+    copied at every step, attention reads the buffer its layer was given (with
+    lookahead 3, layer 3 reuses layer 0's buffer three layers ahead)."""
     w = shrink(WORKLOADS["host_b32_l128k"], B=2, L=8192, layers=4)
-    near, hit_rate = run_host_pool_steps(dkb, w, steps=3, mode=mode, seed=5, buffers="ping-pong")
-    print(f"host pool ping-pong ({mode}): near-tie chunks {near}, hit rate {hit_rate:.3f}")
+    near, hit_rate = run_host_pool_steps(dkb, w, steps=3, mode=mode, seed=5, buffers="ping-pong",
+                                         lookahead=lookahead)
+    print(f"host pool ping-pong ({mode}, lookahead {lookahead}): near-tie chunks {near}, hit rate {hit_rate:.3f}")
     assert hit_rate == 0.0
 
 
