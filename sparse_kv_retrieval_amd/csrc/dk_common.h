@@ -217,7 +217,10 @@ hipError_t launch_score_topk(const float* q, int B, int T, int Hq, const float* 
 // the workspace, then an exact threshold select per (b, g, t).
 struct IndexPlan {
     int rows_per_block;  // score rows (tokens or chunks) per scoring block
-    int blocks_per_bg;   // scoring blocks per (b, g)
+    int blocks_per_bg;   // scoring blocks per (b, g); the per-block ranges are sized for these
+    // the token-level bf16 scoring kernel's own blocks (longer for long rows with
+    // many (b, g)); its per-block ranges use score_blocks_per_bg <= blocks_per_bg
+    int score_rows, score_blocks_per_bg;
     size_t off_min;      // byte offsets of the per-block score minima / maxima
     size_t off_max;
     size_t off_arrive;   // one arrival counter per (b, g) for the fused union

@@ -34,7 +34,14 @@ namespace dk {
 namespace {
 
 constexpr int kScoreThreads = 256;
-constexpr int kScoreRows = 1024;   // tokens per scoring block
+constexpr int kScoreRows = 1024;   // tokens per scoring block (the workspace's per-block ranges)
+// Long rows with many (b, g) take 8192 tokens per block instead, when that still
+// gives at least two blocks per CU (kScoreMinBlocks): fewer block starts and
+// epilogues.  Measured on 32 rows of 131072 tokens (512 blocks of 8192): the
+// scoring call 230-231 us against 251-252 us with 1024-token blocks; 16384
+// tokens (one block per CU) took 280 us.
+constexpr int kScoreRowsLong = 8192;
+constexpr int kScoreMinBlocks = 512;
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / kWave;
 constexpr int kBins = 2048;        // = 2 * kSelThreads
@@ -44,21 +51,21 @@ constexpr int kCap = 2048;         // candidates ranked in LDS
 // Scores: s[b, g, t, n] = scale * <mean over the group's heads of q[b, t, h], key[b, g, n]>
 // (the mean of the scaled per-head dots, up to fp32 rounding).
 // ---------------------------------------------------------------------------
-template <int D, int T>
+template <int D, int T, int RPB>
 __global__ __launch_bounds__(kScoreThreads) void k_idx_score(const float* __restrict__ q, int Hq,
                                                             const uint16_t* __restrict__ keys, dk_strides ks,
                                                             int Hkv, int C, float scale, int blocks_per_bg,
                                                             float* __restrict__ scores, float* __restrict__ bmin,
                                                             float* __restrict__ bmax, uint32_t* __restrict__ arrivals) {
     constexpr int LPR = D / 8, RPW = kWave / LPR, U = 8, ROWS_PER_ITER = 4 * RPW * U;
-    __shared__ float sres[T][kScoreRows];
+    __shared__ float sres[T][RPB];
     __shared__ __align__(16) float qs[T][D];
     __shared__ float red[2][T][kScoreThreads / kWave];
     const int blk = blockIdx.x % blocks_per_bg;
     const int bg = blockIdx.x / blocks_per_bg;
     const int b = bg / Hkv, g = bg - b * Hkv;
-    const int row0 = blk * kScoreRows;
-    const int nrows = min(kScoreRows, C - row0);
+    const int row0 = blk * RPB;
+    const int nrows = min(RPB, C - row0);
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int rp = lane / LPR, part = lane % LPR;
     const int G = Hq / Hkv;
@@ -818,6 +825,9 @@ IndexPlan plan_index_topk(int B, int Hkv, int T, int C) {
     p.rows_per_block = kScoreRows;
     const int64_t rows = (int64_t)B * Hkv * T;
     p.blocks_per_bg = (C + kScoreRows - 1) / kScoreRows;
+    const int64_t long_blocks = (int64_t)B * Hkv * ((C + kScoreRowsLong - 1) / kScoreRowsLong);
+    p.score_rows = (C >= kSplitMinC && long_blocks >= kScoreMinBlocks) ? kScoreRowsLong : kScoreRows;
+    p.score_blocks_per_bg = (C + p.score_rows - 1) / p.score_rows;
     const size_t sbytes = (((size_t)rows * C * 4) + 255) & ~(size_t)255;
     const size_t mbytes = (((size_t)rows * p.blocks_per_bg * 4) + 255) & ~(size_t)255;
     const size_t abytes = (((size_t)B * Hkv * 4) + 255) & ~(size_t)255;
@@ -859,10 +869,18 @@ hipError_t launch_index_topk(const float* q, int B, int T, int Hq, const uint16_
     float* bmax = (float*)((char*)ws + plan.off_max);
     uint32_t* arrivals = un ? (uint32_t*)((char*)ws + plan.off_arrive) : nullptr;
     const int64_t bg = (int64_t)B * Hkv;
-    const dim3 sg((unsigned)(bg * plan.blocks_per_bg));
-#define DK_IDX_SCORE(D_, T_)                                                                               \
-    hipLaunchKernelGGL((k_idx_score<D_, T_>), sg, dim3(kScoreThreads), 0, st, q, Hq, keys, ks, Hkv, C, scale, \
-                       plan.blocks_per_bg, scores, bmin, bmax, arrivals)
+    // the scoring kernel's own blocks; its per-block ranges fit the workspace's,
+    // which is sized for the shorter blocks
+    const dim3 sg((unsigned)(bg * plan.score_blocks_per_bg));
+#define DK_IDX_SCORE(D_, T_)                                                                                   \
+    do {                                                                                                       \
+        if (plan.score_rows == kScoreRowsLong)                                                                 \
+            hipLaunchKernelGGL((k_idx_score<D_, T_, kScoreRowsLong>), sg, dim3(kScoreThreads), 0, st, q, Hq, keys, \
+                               ks, Hkv, C, scale, plan.score_blocks_per_bg, scores, bmin, bmax, arrivals);     \
+        else                                                                                                   \
+            hipLaunchKernelGGL((k_idx_score<D_, T_, kScoreRows>), sg, dim3(kScoreThreads), 0, st, q, Hq, keys,   \
+                               ks, Hkv, C, scale, plan.score_blocks_per_bg, scores, bmin, bmax, arrivals);     \
+    } while (0)
     if (d == 128) {
         if (T == 2) DK_IDX_SCORE(128, 2); else DK_IDX_SCORE(128, 1);
     } else {
@@ -871,8 +889,8 @@ hipError_t launch_index_topk(const float* q, int B, int T, int Hq, const uint16_
 #undef DK_IDX_SCORE
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_select_rows(scores, bmin, bmax, plan.blocks_per_bg, B, Hkv, T, C, k, topk_idx, topk_score, un,
-                              arrivals, plan, ws, st);
+    return launch_select_rows(scores, bmin, bmax, plan.score_blocks_per_bg, B, Hkv, T, C, k, topk_idx, topk_score,
+                              un, arrivals, plan, ws, st);
 }
 
 hipError_t launch_select_rows(const float* scores, const float* bmin, const float* bmax, int blocks_per_row, int B,
