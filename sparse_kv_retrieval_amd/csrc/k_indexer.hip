@@ -35,11 +35,11 @@ namespace {
 
 constexpr int kScoreThreads = 256;
 constexpr int kScoreRows = 1024;   // tokens per scoring block (the workspace's per-block ranges)
-// Long rows with many (b, g) take 8192 tokens per block instead, when that still
-// gives at least two blocks per CU (kScoreMinBlocks): fewer block starts and
-// epilogues.  Measured on 32 rows of 131072 tokens (512 blocks of 8192): the
-// scoring call 230-231 us against 251-252 us with 1024-token blocks; 16384
-// tokens (one block per CU) took 280 us.
+// Scoring blocks are made longer (doubling up to 8192 rows, at most the row
+// rounded up) as long as at least kScoreMinBlocks blocks remain, two per CU:
+// fewer block starts and epilogues, one resident round.  Measured on 32 rows of
+// 131072 tokens (512 blocks of 8192): the scoring call 230-231 us against
+// 251-252 us with 1024-row blocks; 16384 rows (one block per CU) took 280 us.
 constexpr int kScoreRowsLong = 8192;
 constexpr int kScoreMinBlocks = 512;
 constexpr int kSelThreads = 1024;
@@ -825,8 +825,12 @@ IndexPlan plan_index_topk(int B, int Hkv, int T, int C) {
     p.rows_per_block = kScoreRows;
     const int64_t rows = (int64_t)B * Hkv * T;
     p.blocks_per_bg = (C + kScoreRows - 1) / kScoreRows;
-    const int64_t long_blocks = (int64_t)B * Hkv * ((C + kScoreRowsLong - 1) / kScoreRowsLong);
-    p.score_rows = (C >= kSplitMinC && long_blocks >= kScoreMinBlocks) ? kScoreRowsLong : kScoreRows;
+    int cap = kScoreRows;
+    while (cap < kScoreRowsLong && cap < C) cap *= 2;
+    p.score_rows = kScoreRows;
+    while (p.score_rows < cap &&
+           (int64_t)B * Hkv * ((C + 2 * p.score_rows - 1) / (2 * p.score_rows)) >= kScoreMinBlocks)
+        p.score_rows *= 2;
     p.score_blocks_per_bg = (C + p.score_rows - 1) / p.score_rows;
     const size_t sbytes = (((size_t)rows * C * 4) + 255) & ~(size_t)255;
     const size_t mbytes = (((size_t)rows * p.blocks_per_bg * 4) + 255) & ~(size_t)255;
@@ -872,14 +876,15 @@ hipError_t launch_index_topk(const float* q, int B, int T, int Hq, const uint16_
     // the scoring kernel's own blocks; its per-block ranges fit the workspace's,
     // which is sized for the shorter blocks
     const dim3 sg((unsigned)(bg * plan.score_blocks_per_bg));
-#define DK_IDX_SCORE(D_, T_)                                                                                   \
-    do {                                                                                                       \
-        if (plan.score_rows == kScoreRowsLong)                                                                 \
-            hipLaunchKernelGGL((k_idx_score<D_, T_, kScoreRowsLong>), sg, dim3(kScoreThreads), 0, st, q, Hq, keys, \
-                               ks, Hkv, C, scale, plan.score_blocks_per_bg, scores, bmin, bmax, arrivals);     \
-        else                                                                                                   \
-            hipLaunchKernelGGL((k_idx_score<D_, T_, kScoreRows>), sg, dim3(kScoreThreads), 0, st, q, Hq, keys,   \
-                               ks, Hkv, C, scale, plan.score_blocks_per_bg, scores, bmin, bmax, arrivals);     \
+#define DK_IDX_SCORE_R(D_, T_, R_)                                                                           \
+    hipLaunchKernelGGL((k_idx_score<D_, T_, R_>), sg, dim3(kScoreThreads), 0, st, q, Hq, keys, ks, Hkv, C, scale, \
+                       plan.score_blocks_per_bg, scores, bmin, bmax, arrivals)
+#define DK_IDX_SCORE(D_, T_)                                                   \
+    do {                                                                       \
+        if (plan.score_rows == 8192) DK_IDX_SCORE_R(D_, T_, 8192);             \
+        else if (plan.score_rows == 4096) DK_IDX_SCORE_R(D_, T_, 4096);        \
+        else if (plan.score_rows == 2048) DK_IDX_SCORE_R(D_, T_, 2048);        \
+        else DK_IDX_SCORE_R(D_, T_, 1024);                                     \
     } while (0)
     if (d == 128) {
         if (T == 2) DK_IDX_SCORE(128, 2); else DK_IDX_SCORE(128, 1);
@@ -887,6 +892,7 @@ hipError_t launch_index_topk(const float* q, int B, int T, int Hq, const uint16_
         if (T == 2) DK_IDX_SCORE(64, 2); else DK_IDX_SCORE(64, 1);
     }
 #undef DK_IDX_SCORE
+#undef DK_IDX_SCORE_R
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_select_rows(scores, bmin, bmax, plan.score_blocks_per_bg, B, Hkv, T, C, k, topk_idx, topk_score,

@@ -242,12 +242,23 @@ __global__ __launch_bounds__(kMmThreads) void k_row_score(const float* __restric
     }
 }
 
+// Rows per block of k_row_score: the plan's scoring-block length, at most 4096
+// so that its dynamic LDS (T rows of scores plus the query vectors) stays within
+// 64 KiB; the per-block ranges it writes fit the workspace, sized for 1024.
+struct RowBlocks {
+    int rows, per_bg;
+};
+inline RowBlocks row_blocks(const IndexPlan& p, int C) {
+    const int rows = p.score_rows < 4096 ? p.score_rows : 4096;
+    return {rows, (C + rows - 1) / rows};
+}
+
 template <typename ET, int D, int NQ, int T, bool MAXRED, bool BOX>
 void launch_row_score(dim3 grid, size_t lds, hipStream_t st, const float* q, int Hq, const void* kmin,
                       const void* kmax, dk_strides ss, int Hkv, int C, float scale, const IndexPlan& p,
                       float* scores, float* bmin, float* bmax, uint32_t* arrivals) {
     hipLaunchKernelGGL((k_row_score<ET, D, NQ, T, MAXRED, BOX>), grid, dim3(kMmThreads), lds, st, q, Hq,
-                       (const ET*)kmin, (const ET*)kmax, ss, Hkv, C, scale, p.rows_per_block, p.blocks_per_bg,
+                       (const ET*)kmin, (const ET*)kmax, ss, Hkv, C, scale, row_blocks(p, C).rows, row_blocks(p, C).per_bg,
                        scores, bmin, bmax, arrivals);
 }
 
@@ -297,8 +308,9 @@ hipError_t launch_score_rows(const float* q, int B, int T, int Hq, const void* a
     const int G = Hq / Hkv;
     const bool maxred = reduce == DK_REDUCE_MAX;
     const int nq = maxred ? G * T : T;
-    const dim3 grid((unsigned)((int64_t)B * Hkv * plan.blocks_per_bg));
-    const size_t lds = ((size_t)T * plan.rows_per_block + (b ? 2 : 1) * (size_t)nq * d) * 4;
+    const RowBlocks rb = row_blocks(plan, C);
+    const dim3 grid((unsigned)((int64_t)B * Hkv * rb.per_bg));
+    const size_t lds = ((size_t)T * rb.rows + (b ? 2 : 1) * (size_t)nq * d) * 4;
 #define DK_ROWS(ET_, D_, BOX_)                                                                                  \
     return dispatch_rows<ET_, D_, BOX_>(nq, T, maxred, grid, lds, st, q, Hq, a, b, ss, Hkv, C, scale, plan,    \
                                         scores, bmin, bmax, arrivals)
@@ -321,7 +333,7 @@ hipError_t launch_minmax_topk(const float* q, int B, int T, int Hq, const void* 
                                      st);
     if (e != hipSuccess) return e;
     return launch_select_rows((const float*)ws, (const float*)((char*)ws + plan.off_min),
-                              (const float*)((char*)ws + plan.off_max), plan.blocks_per_bg, B, Hkv, T, C, k, topk_idx,
+                              (const float*)((char*)ws + plan.off_max), row_blocks(plan, C).per_bg, B, Hkv, T, C, k, topk_idx,
                               topk_score, un, arrivals, plan, ws, st);
 }
 
