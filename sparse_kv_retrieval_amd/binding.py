@@ -10,6 +10,7 @@ built (``python -m sparse_kv_retrieval_amd.build``).
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 from dataclasses import dataclass
 
@@ -110,6 +111,21 @@ def _ptr(t: torch.Tensor | None):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _on_stream(fn):
+    """Run a wrapper with its `stream` argument (when given) as torch's current
+    stream, so that every buffer the wrapper allocates (outputs, workspaces)
+    belongs to the stream its library call is enqueued on: the caching allocator
+    then never hands that memory out again while the call may still use it."""
+    @functools.wraps(fn)
+    def run(*args, stream=None, **kw):
+        if stream is None:
+            return fn(*args, **kw)
+        s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(int(stream))
+        with torch.cuda.stream(s):
+            return fn(*args, stream=s, **kw)
+    return run
+
+
 def _stream(stream=None):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -143,6 +159,7 @@ def _need(t: torch.Tensor, dtype, shape, name, device=True):
 # one wrapper per C entry point
 # ----------------------------------------------------------------------------
 
+@_on_stream
 def build_landmarks(K: torch.Tensor, chunk: int, lm: torch.Tensor | None = None, stream=None):
     B, H, L, d = K.shape
     C = L // chunk if chunk > 0 else 0
@@ -165,6 +182,7 @@ class Shadow:
         return dk_landmark_shadow(self.lm8.data_ptr(), self.chunk_scale.data_ptr(), self.scale_max.data_ptr())
 
 
+@_on_stream
 def build_landmark_shadow(lm: torch.Tensor, stream=None) -> Shadow:
     B, H, C, d = lm.shape
     dev = lm.device
@@ -191,6 +209,7 @@ def _topk_ws_bytes(lm, B, Hkv, T, C, k, shadow) -> int:
     return score_topk_workspace_size(B, Hkv, T, C, k, shadow is not None)
 
 
+@_on_stream
 def score_topk(q: torch.Tensor, lm: torch.Tensor, k: int, scale: float, reduce: int = DK_REDUCE_MEAN,
                topk_idx=None, topk_score=None, ws=None, want_scores=True, shadow: Shadow | None = None,
                stream=None):
@@ -212,6 +231,7 @@ def score_topk(q: torch.Tensor, lm: torch.Tensor, k: int, scale: float, reduce: 
     return topk_idx, topk_score
 
 
+@_on_stream
 def build_minmax(K: torch.Tensor, chunk: int, kmin=None, kmax=None, stream=None):
     """Coordinate-wise min and max key of every chunk, [B, Hkv, L/chunk, d] in K's dtype."""
     B, Hkv, L, d = K.shape
@@ -225,6 +245,7 @@ def build_minmax(K: torch.Tensor, chunk: int, kmin=None, kmax=None, stream=None)
     return kmin, kmax
 
 
+@_on_stream
 def score_topk_minmax(q: torch.Tensor, kmin: torch.Tensor, kmax: torch.Tensor, k: int, scale: float,
                       reduce: int = DK_REDUCE_MEAN, topk_idx=None, topk_score=None, union=False, union_ids=None,
                       member=None, count=None, overlap=None, ws=None, want_scores=True, stream=None):
@@ -261,6 +282,7 @@ def coverage_workspace_size(B, Hkv, T, C) -> int:
     return int(lib.dk_coverage_workspace_size(B, Hkv, T, C))
 
 
+@_on_stream
 def score_coverage(q: torch.Tensor, lm: torch.Tensor, gamma: float, k_max: int, scale: float,
                    reduce: int = DK_REDUCE_MEAN, sel_idx=None, sel_count=None, sel_score=None, union=False,
                    union_ids=None, member=None, count=None, overlap=None, ws=None, want_scores=True, stream=None):
@@ -296,6 +318,7 @@ def score_coverage(q: torch.Tensor, lm: torch.Tensor, gamma: float, k_max: int, 
     return sel_idx, sel_count, sel_score
 
 
+@_on_stream
 def capped_plan(sel_ids: torch.Tensor, resident: torch.Tensor, stamp: torch.Tensor, cap: int, step: int,
                 sel_score: torch.Tensor | None = None, sel_count: torch.Tensor | None = None, sel_slot=None,
                 admit_chunk=None, admit_slot=None, admit_count=None, hit_count=None, stream=None):
@@ -333,6 +356,7 @@ def capped_plan(sel_ids: torch.Tensor, resident: torch.Tensor, stamp: torch.Tens
     return sel_slot, admit_chunk[..., :cap], admit_slot[..., :cap], admit_count, hit_count
 
 
+@_on_stream
 def score_topk_union(q: torch.Tensor, lm: torch.Tensor, k: int, scale: float,
                      reduce: int = DK_REDUCE_MEAN, topk_idx=None, topk_score=None, union_ids=None,
                      member=None, count=None, overlap=None, ws=None, want_scores=False,
@@ -390,6 +414,7 @@ class CachePlan:
                              self.hit_count.data_ptr())
 
 
+@_on_stream
 def union_select(topk_idx: torch.Tensor, C: int, union_ids=None, member=None, count=None,
                  overlap=None, plan: CachePlan | None = None, stream=None):
     B, Hkv, T, k = topk_idx.shape
@@ -412,6 +437,7 @@ def union_select(topk_idx: torch.Tensor, C: int, union_ids=None, member=None, co
 DK_SRC_DEVICE, DK_SRC_HOST_COPY, DK_SRC_HOST_MAPPED = 0, 1, 2
 
 
+@_on_stream
 def gather_kv(K_src, V_src, src_chunk, count, chunk, K_dst, V_dst, dst_slot=None,
               src_blocks=None, dst_blocks=None, stream=None):
     """Copy chunks src_chunk[b, g, j] (j < count[b, g]) into slots of K_dst / V_dst.
@@ -450,6 +476,7 @@ def attn_workspace_size(B, Hkv, T, Hq, dv, N, chunk) -> int:
     return int(lib.dk_attn_workspace_size(B, Hkv, T, Hq, dv, N, chunk))
 
 
+@_on_stream
 def sparse_decode_attn(q, K, V, block_ids, member, count, chunk: int, scale: float,
                        pool_blocks: int | None = None, out=None, lse=None, ws=None, want_lse=True,
                        stream=None):
@@ -483,6 +510,7 @@ def sparse_decode_attn(q, K, V, block_ids, member, count, chunk: int, scale: flo
     return out, lse
 
 
+@_on_stream
 def mla_decode_attn(q, latent, token_ids, member, count, scale: float, dv: int = 512, out=None, lse=None,
                     ws=None, want_lse=True, stream=None):
     """Attention over latent rows [B, Hkv, L, dk]: the key is the whole row, the value
@@ -500,6 +528,7 @@ def attn_tail_workspace_size(B, Hkv, T, Hq, dv, N, chunk) -> int:
     return int(lib.dk_attn_tail_workspace_size(B, Hkv, T, Hq, dv, N, chunk))
 
 
+@_on_stream
 def sparse_decode_attn_tail(q, K, V, block_ids, member, count, chunk: int, scale: float, K_tail=None,
                             V_tail=None, tail_len=None, K_new=None, V_new=None, pool_blocks: int | None = None,
                             out=None, lse=None, ws=None, stream=None):
