@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define DK_ABI_VERSION 10
+#define DK_ABI_VERSION 11
 
 typedef enum {
     DK_OK = 0,
@@ -461,6 +461,38 @@ dk_status dk_sparse_decode_attn(const float* q, int B, int T, int Hq, int Hkv,
                                 const int32_t* block_ids, const uint8_t* member,
                                 const int32_t* count, int N, int pool_blocks, float scale,
                                 float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * dk_sparse_decode_attn_noalloc - dk_sparse_decode_attn without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, serving loops that forbid allocation, harnesses without
+ * hipMalloc).
+ *
+ * The result is the one dk_sparse_decode_attn writes: the same kernels run on
+ * the same plan.  The split partials go to a fixed 64 MiB device array inside
+ * the library instead of a caller workspace; each device the library runs on
+ * holds its own copy from the first call on it until the process ends.  The
+ * call allocates nothing (no hipMalloc, no hipFree); its first call on a device
+ * looks the array's device address up once.  Nothing in the array needs to
+ * start at zero: every partial is written before it is read.
+ *
+ * Concurrency: every call on one device shares that device's array.  Calls
+ * whose execution overlaps on one device (different streams, or host threads
+ * with no ordering between their streams) race on it and give undefined
+ * results; calls ordered on one stream are safe.
+ *
+ * Arguments: as dk_sparse_decode_attn, without ws and ws_bytes.
+ * Errors: those of dk_sparse_decode_attn; DK_ERR_UNSUPPORTED when the shape
+ * needs more scratch than the array holds (dk_attn_workspace_size(...) of the
+ * same arguments above 64 MiB); DK_ERR_HIP when the device address cannot be
+ * looked up.
+ */
+dk_status dk_sparse_decode_attn_noalloc(const float* q, int B, int T, int Hq, int Hkv,
+                                        const void* K, const void* V, dk_dtype kv_dtype,
+                                        dk_strides ks, dk_strides vs, int dk, int dv, int chunk,
+                                        const int32_t* block_ids, const uint8_t* member,
+                                        const int32_t* count, int N, int pool_blocks, float scale,
+                                        float* out, float* lse, void* stream);
 
 /*
  * dk_sparse_decode_attn_tail - dk_sparse_decode_attn plus the rows every query

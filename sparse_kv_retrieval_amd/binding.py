@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_PKG, "libdualkv.so")
 DK_OK, DK_ERR_INVALID_ARG, DK_ERR_UNSUPPORTED, DK_ERR_HIP = 0, 1, 2, 3
 DK_F32, DK_BF16 = 0, 1
 DK_REDUCE_MEAN, DK_REDUCE_MAX = 0, 1
-ABI_VERSION = 10
+ABI_VERSION = 11
 
 _STATUS = {0: "DK_OK", 1: "DK_ERR_INVALID_ARG", 2: "DK_ERR_UNSUPPORTED", 3: "DK_ERR_HIP"}
 
@@ -79,6 +79,8 @@ EXPORTS = [
     ("dk_attn_workspace_size", _Z, [_I, _I, _I, _I, _I, _I, _I]),
     ("dk_sparse_decode_attn", _I, [_P, _I, _I, _I, _I, _P, _P, _I, _S, _S, _I, _I, _I, _P, _P, _P,
                                    _I, _I, _F, _P, _P, _P, _Z, _P]),
+    ("dk_sparse_decode_attn_noalloc", _I, [_P, _I, _I, _I, _I, _P, _P, _I, _S, _S, _I, _I, _I, _P, _P, _P,
+                                           _I, _I, _F, _P, _P, _P]),
     ("dk_attn_tail_workspace_size", _Z, [_I, _I, _I, _I, _I, _I, _I]),
     ("dk_sparse_decode_attn_tail", _I, [_P, _I, _I, _I, _I, _P, _P, _I, _S, _S, _I, _I, _I, _P, _P, _P,
                                         _I, _I, ctypes.POINTER(dk_attn_extra), _F, _P, _P, _P, _Z, _P]),
@@ -507,6 +509,37 @@ def sparse_decode_attn(q, K, V, block_ids, member, count, chunk: int, scale: flo
                                      float(scale), _ptr(out), _ptr(lse), _ptr(ws),
                                      0 if ws is None else ws.numel() * ws.element_size(),
                                      _stream(stream)))
+    return out, lse
+
+
+@_on_stream
+def sparse_decode_attn_noalloc(q, K, V, block_ids, member, count, chunk: int, scale: float,
+                               pool_blocks: int | None = None, out=None, lse=None, want_lse=True, stream=None):
+    """sparse_decode_attn with the library's fixed device scratch instead of a workspace
+    (dk_sparse_decode_attn_noalloc): the C call allocates nothing.  Calls that overlap
+    on one device share that scratch and race."""
+    B, T, Hq, dk = q.shape
+    Hkv = K.shape[1]
+    dv = V.shape[3]
+    N = block_ids.shape[2]
+    _need(q, torch.float32, (B, T, Hq, dk), "q")
+    _need(block_ids, torch.int32, (B, Hkv, N), "block_ids")
+    if member is not None:
+        _need(member, torch.uint8, (B, Hkv, N), "member")
+    if count is not None:
+        _need(count, torch.int32, (B, Hkv), "count")
+    if K.dtype != V.dtype:
+        raise ValueError("K and V must share a dtype")
+    if out is None:
+        out = torch.empty(B, T, Hq, dv, dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty(B, T, Hq, dtype=torch.float32, device=q.device)
+    if pool_blocks is None:
+        pool_blocks = K.shape[2] // chunk
+    _check(lib.dk_sparse_decode_attn_noalloc(_ptr(q), B, T, Hq, Hkv, _ptr(K), _ptr(V), _dtype(K),
+                                             pool_strides(K), pool_strides(V), dk, dv, chunk,
+                                             _ptr(block_ids), _ptr(member), _ptr(count), N, pool_blocks,
+                                             float(scale), _ptr(out), _ptr(lse), _stream(stream)))
     return out, lse
 
 

@@ -3,6 +3,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "dk_common.h"
@@ -194,6 +195,113 @@ dk_status check_union(const char* fn, int T, int k, int slots, bool with_plan) {
     const int64_t lds = (int64_t)(3 * k + 1 + N + 8 + (with_plan ? 2 * slots + N : 0)) * 4;
     DK_REQUIRE(lds <= 65536, DK_ERR_UNSUPPORTED, "%s: k and slots too large for one block", fn);
     return DK_OK;
+}
+
+// Attention call shared by dk_sparse_decode_attn and dk_sparse_decode_attn_noalloc:
+// the kernel family that runs and the scratch bytes it needs.
+struct AttnCall {
+    bool latent;          // dk 576 / dv 512 rows on the matrix cores
+    dk::AttnPlan plan;
+    dk::MlaPlan mla;
+    size_t ws_bytes;
+};
+
+dk_status check_attn(const char* fn, const float* q, int B, int T, int Hq, int Hkv, const void* K, const void* V,
+                     dk_dtype kv_dtype, dk_strides ks, dk_strides vs, int dk, int dv, int chunk,
+                     const int32_t* block_ids, const uint8_t* member, const float* out, int pool_blocks, int N,
+                     float scale, AttnCall* c) {
+    const int esz = dtype_size(kv_dtype);
+    DK_REQUIRE(q && K && V && block_ids && out, DK_ERR_INVALID_ARG, "%s: q, K, V, block_ids, out must be non-NULL",
+               fn);
+    DK_REQUIRE(esz != 0, DK_ERR_INVALID_ARG, "%s: unknown kv_dtype %d", fn, (int)kv_dtype);
+    DK_REQUIRE(B >= 1 && Hq >= 1 && Hkv >= 1 && dk >= 1 && dv >= 1 && chunk >= 1 && N >= 1 && pool_blocks >= 0,
+               DK_ERR_INVALID_ARG, "%s: sizes out of range", fn);
+    DK_REQUIRE(T == 1 || T == 2, DK_ERR_INVALID_ARG, "%s: T must be 1 or 2 (got %d)", fn, T);
+    DK_REQUIRE(Hq % Hkv == 0, DK_ERR_INVALID_ARG, "%s: Hq (%d) %% Hkv (%d) != 0", fn, Hq, Hkv);
+    DK_REQUIRE(member || T == 1, DK_ERR_INVALID_ARG, "%s: member is required when T == 2", fn);
+    DK_REQUIRE(std::isfinite(scale), DK_ERR_INVALID_ARG, "%s: scale must be finite", fn);
+    if (dk == 576 && dv == 512) {
+        // latent rows: the value is the first 512 columns of the key rows
+        DK_REQUIRE(kv_dtype == DK_BF16 && chunk == 1, DK_ERR_UNSUPPORTED,
+                   "%s: latent attention (dk 576, dv 512) needs bf16 rows and chunk == 1", fn);
+        DK_REQUIRE(K == V && ks.b == vs.b && ks.h == vs.h && ks.t == vs.t, DK_ERR_UNSUPPORTED,
+                   "%s: latent attention reads the value from the key rows: V must equal K, vs must equal ks", fn);
+        DK_REQUIRE(ks.t >= 576 && ks.b >= 0 && ks.h >= 0, DK_ERR_INVALID_ARG,
+                   "%s: latent rows need a row stride >= 576", fn);
+        const int HB = 64 / T;
+        DK_REQUIRE((Hq / Hkv) % HB == 0, DK_ERR_UNSUPPORTED,
+                   "%s: latent attention needs Hq/Hkv a multiple of %d (got %d)", fn, HB, Hq / Hkv);
+        DK_REQUIRE(aligned16(q) && aligned16(out) && aligned16(K) && strides_ok(ks, 2), DK_ERR_UNSUPPORTED,
+                   "%s: q, out, the latent rows and their strides must be 16-byte aligned", fn);
+        c->latent = true;
+        c->mla = dk::plan_mla(B, Hkv, T, Hq, N);
+        c->ws_bytes = c->mla.ws_bytes;
+        return DK_OK;
+    }
+    DK_REQUIRE(dk == dv && (dk == 64 || dk == 128), DK_ERR_UNSUPPORTED,
+               "%s: needs dk == dv in {64, 128}, or dk 576 / dv 512 (got %d, %d)", fn, dk, dv);
+    DK_REQUIRE((Hq / Hkv) * T <= 16, DK_ERR_UNSUPPORTED, "%s: G*T must be <= 16", fn);
+    DK_REQUIRE(aligned16(q) && aligned16(out) && aligned16(K) && aligned16(V) && strides_ok(ks, esz) &&
+                   strides_ok(vs, esz),
+               DK_ERR_UNSUPPORTED, "%s: q, out, K, V and strides must be 16-byte aligned", fn);
+    c->latent = false;
+    c->plan = dk::plan_attn(B, Hkv, T, Hq, dv, N, chunk);
+    c->ws_bytes = c->plan.ws_bytes;
+    return DK_OK;
+}
+
+hipError_t run_attn(const AttnCall& c, const float* q, int B, int T, int Hq, int Hkv, const void* K, const void* V,
+                    dk_dtype kv_dtype, dk_strides ks, dk_strides vs, int dk, int chunk, const int32_t* block_ids,
+                    const uint8_t* member, const int32_t* count, int N, int pool_blocks, float scale, float* out,
+                    float* lse, void* ws, hipStream_t st) {
+    if (c.latent)
+        return dk::launch_mla_attention(q, B, T, Hq, Hkv, K, ks, block_ids, member, count, N, pool_blocks, scale, out,
+                                        lse, ws, c.mla, st);
+    return dk::launch_attention(q, B, T, Hq, Hkv, K, V, kv_dtype, ks, vs, dk, chunk, block_ids, member, count, N,
+                                pool_blocks, scale, out, lse, ws, c.plan, nullptr, st);
+}
+
+}  // namespace
+
+// Scratch of dk_sparse_decode_attn_noalloc, for callers that cannot allocate:
+// the attention partials live in this fixed device array instead of a caller
+// workspace.  Each device the library runs on holds its own copy until the
+// process ends.  In host code `scratch` is only a handle, not a device address:
+// the address comes from hipGetSymbolAddress, once per device (static_scratch).
+static __device__ __align__(256) unsigned char scratch[64u << 20];
+
+namespace {
+
+constexpr size_t kStaticScratchBytes = sizeof(scratch);
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the device that `st` belongs to (the current
+// device for the null stream), looked up with that device current on the first
+// call for the device and kept.
+hipError_t static_scratch(hipStream_t st, void** out) {
+    int dev = -1;
+    hipError_t e = st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = -1;
+        e = hipGetDevice(&cur);
+        if (e != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 }  // namespace
@@ -503,51 +611,41 @@ dk_status dk_sparse_decode_attn(const float* q, int B, int T, int Hq, int Hkv, c
                                 const int32_t* count, int N, int pool_blocks, float scale, float* out,
                                 float* lse, void* ws, size_t ws_bytes, void* stream) {
     g_err.clear();
-    const int esz = dtype_size(kv_dtype);
-    DK_REQUIRE(q && K && V && block_ids && out, DK_ERR_INVALID_ARG,
-               "dk_sparse_decode_attn: q, K, V, block_ids, out must be non-NULL");
-    DK_REQUIRE(esz != 0, DK_ERR_INVALID_ARG, "dk_sparse_decode_attn: unknown kv_dtype %d", (int)kv_dtype);
-    DK_REQUIRE(B >= 1 && Hq >= 1 && Hkv >= 1 && dk >= 1 && dv >= 1 && chunk >= 1 && N >= 1 &&
-                   pool_blocks >= 0,
-               DK_ERR_INVALID_ARG, "dk_sparse_decode_attn: sizes out of range");
-    DK_REQUIRE(T == 1 || T == 2, DK_ERR_INVALID_ARG, "dk_sparse_decode_attn: T must be 1 or 2 (got %d)", T);
-    DK_REQUIRE(Hq % Hkv == 0, DK_ERR_INVALID_ARG, "dk_sparse_decode_attn: Hq (%d) %% Hkv (%d) != 0", Hq, Hkv);
-    DK_REQUIRE(member || T == 1, DK_ERR_INVALID_ARG, "dk_sparse_decode_attn: member is required when T == 2");
-    DK_REQUIRE(std::isfinite(scale), DK_ERR_INVALID_ARG, "dk_sparse_decode_attn: scale must be finite");
-    if (dk == 576 && dv == 512) {
-        // latent rows: the value is the first 512 columns of the key rows
-        const char* fn = "dk_sparse_decode_attn";
-        DK_REQUIRE(kv_dtype == DK_BF16 && chunk == 1, DK_ERR_UNSUPPORTED,
-                   "%s: latent attention (dk 576, dv 512) needs bf16 rows and chunk == 1", fn);
-        DK_REQUIRE(K == V && ks.b == vs.b && ks.h == vs.h && ks.t == vs.t, DK_ERR_UNSUPPORTED,
-                   "%s: latent attention reads the value from the key rows: V must equal K, vs must equal ks", fn);
-        DK_REQUIRE(ks.t >= 576 && ks.b >= 0 && ks.h >= 0, DK_ERR_INVALID_ARG,
-                   "%s: latent rows need a row stride >= 576", fn);
-        const int HB = 64 / T;
-        DK_REQUIRE((Hq / Hkv) % HB == 0, DK_ERR_UNSUPPORTED,
-                   "%s: latent attention needs Hq/Hkv a multiple of %d (got %d)", fn, HB, Hq / Hkv);
-        DK_REQUIRE(aligned16(q) && aligned16(out) && aligned16(K) && strides_ok(ks, 2), DK_ERR_UNSUPPORTED,
-                   "%s: q, out, the latent rows and their strides must be 16-byte aligned", fn);
-        const dk::MlaPlan mp = dk::plan_mla(B, Hkv, T, Hq, N);
-        DK_REQUIRE(ws_bytes >= mp.ws_bytes && (mp.ws_bytes == 0 || ws), DK_ERR_INVALID_ARG,
-                   "%s: workspace needs %zu bytes (got %zu)", fn, mp.ws_bytes, ws_bytes);
-        hipError_t e = dk::launch_mla_attention(q, B, T, Hq, Hkv, K, ks, block_ids, member, count, N, pool_blocks,
-                                                scale, out, lse, ws, mp, (hipStream_t)stream);
-        return e == hipSuccess ? DK_OK : hip_fail(e, fn);
+    const char* fn = "dk_sparse_decode_attn";
+    AttnCall c{};
+    dk_status s = check_attn(fn, q, B, T, Hq, Hkv, K, V, kv_dtype, ks, vs, dk, dv, chunk, block_ids, member,
+                             out, pool_blocks, N, scale, &c);
+    if (s != DK_OK) return s;
+    DK_REQUIRE(ws_bytes >= c.ws_bytes && (c.ws_bytes == 0 || ws), DK_ERR_INVALID_ARG,
+               "%s: workspace needs %zu bytes (got %zu)", fn, c.ws_bytes, ws_bytes);
+    hipError_t e = run_attn(c, q, B, T, Hq, Hkv, K, V, kv_dtype, ks, vs, dk, chunk, block_ids, member, count, N,
+                            pool_blocks, scale, out, lse, ws, (hipStream_t)stream);
+    return e == hipSuccess ? DK_OK : hip_fail(e, fn);
+}
+
+dk_status dk_sparse_decode_attn_noalloc(const float* q, int B, int T, int Hq, int Hkv, const void* K,
+                                        const void* V, dk_dtype kv_dtype, dk_strides ks, dk_strides vs, int dk,
+                                        int dv, int chunk, const int32_t* block_ids, const uint8_t* member,
+                                        const int32_t* count, int N, int pool_blocks, float scale, float* out,
+                                        float* lse, void* stream) {
+    g_err.clear();
+    const char* fn = "dk_sparse_decode_attn_noalloc";
+    AttnCall c{};
+    dk_status s = check_attn(fn, q, B, T, Hq, Hkv, K, V, kv_dtype, ks, vs, dk, dv, chunk, block_ids, member,
+                             out, pool_blocks, N, scale, &c);
+    if (s != DK_OK) return s;
+    DK_REQUIRE(c.ws_bytes <= kStaticScratchBytes, DK_ERR_UNSUPPORTED,
+               "%s: this shape needs %zu bytes of scratch, more than the library's fixed %zu; use "
+               "dk_sparse_decode_attn with a workspace", fn, c.ws_bytes, kStaticScratchBytes);
+    void* ws = nullptr;
+    hipError_t e = hipSuccess;
+    if (c.ws_bytes > 0) {
+        e = static_scratch((hipStream_t)stream, &ws);
+        if (e != hipSuccess) return hip_fail(e, fn);
     }
-    DK_REQUIRE(dk == dv && (dk == 64 || dk == 128), DK_ERR_UNSUPPORTED,
-               "dk_sparse_decode_attn: needs dk == dv in {64, 128}, or dk 576 / dv 512 (got %d, %d)", dk, dv);
-    DK_REQUIRE((Hq / Hkv) * T <= 16, DK_ERR_UNSUPPORTED, "dk_sparse_decode_attn: G*T must be <= 16");
-    DK_REQUIRE(aligned16(q) && aligned16(out) && aligned16(K) && aligned16(V) && strides_ok(ks, esz) &&
-                   strides_ok(vs, esz),
-               DK_ERR_UNSUPPORTED, "dk_sparse_decode_attn: q, out, K, V and strides must be 16-byte aligned");
-    const dk::AttnPlan plan = dk::plan_attn(B, Hkv, T, Hq, dv, N, chunk);
-    DK_REQUIRE(ws_bytes >= plan.ws_bytes && (plan.ws_bytes == 0 || ws), DK_ERR_INVALID_ARG,
-               "dk_sparse_decode_attn: workspace needs %zu bytes (got %zu)", plan.ws_bytes, ws_bytes);
-    hipError_t e = dk::launch_attention(q, B, T, Hq, Hkv, K, V, kv_dtype, ks, vs, dk, chunk, block_ids,
-                                        member, count, N, pool_blocks, scale, out, lse, ws, plan, nullptr,
-                                        (hipStream_t)stream);
-    return e == hipSuccess ? DK_OK : hip_fail(e, "dk_sparse_decode_attn");
+    e = run_attn(c, q, B, T, Hq, Hkv, K, V, kv_dtype, ks, vs, dk, chunk, block_ids, member, count, N, pool_blocks,
+                 scale, out, lse, ws, (hipStream_t)stream);
+    return e == hipSuccess ? DK_OK : hip_fail(e, fn);
 }
 
 size_t dk_attn_tail_workspace_size(int B, int Hkv, int T, int Hq, int dv, int N, int chunk) {
