@@ -467,6 +467,81 @@ def test_attention_k_equals_c_is_dense(dkb):
     run_attention(dkb, w, 43)
 
 
+def random_unions(rng, B, Hkv, N, C, counts):
+    """Union lists with the given sizes: distinct ascending chunk ids, member bits in
+    {1, 2, 3}, -1 / 0 padding; also each query's own list for the oracle."""
+    ids = np.full((B, Hkv, N), -1, dtype=np.int32)
+    mem = np.zeros((B, Hkv, N), dtype=np.uint8)
+    lists = [[[[], []] for _ in range(Hkv)] for _ in range(B)]
+    for b in range(B):
+        for g in range(Hkv):
+            n = int(counts[b, g])
+            chosen = np.sort(rng.choice(C, n, replace=False))
+            bits = rng.integers(1, 4, n)
+            ids[b, g, :n] = chosen
+            mem[b, g, :n] = bits
+            for t in range(2):
+                lists[b][g][t] = [int(c) for c, bit in zip(chosen, bits) if (bit >> t) & 1]
+    return ids, mem, counts.astype(np.int32), lists
+
+
+@pytest.mark.parametrize("case", ["short", "few", "empty", "chunk64", "full"])
+def test_attention_ragged_unions(dkb, case):
+    """The fast shape over many (b, g) with ragged unions: 0-3 chunks each, a few
+    non-empty (b, g) among many empty ones, none at all, two tiles per chunk, and
+    every union full."""
+    rng = np.random.default_rng(7)
+    kw = dict(chunk=64, k=8) if case == "chunk64" else dict(k=8)
+    w = workload("llama8b_l32k", 24, 4096 if case == "chunk64" else 2048, **kw)
+    N = w.T * w.k
+    if case == "short" or case == "chunk64":
+        counts = rng.integers(0, 4, (w.B, w.Hkv))
+    elif case == "few":
+        counts = np.zeros((w.B, w.Hkv), dtype=np.int64)
+        counts[rng.integers(0, w.B, 5), rng.integers(0, w.Hkv, 5)] = rng.integers(1, N + 1, 5)
+    elif case == "empty":
+        counts = np.zeros((w.B, w.Hkv), dtype=np.int64)
+    else:
+        counts = np.full((w.B, w.Hkv), N)
+    q, K, V = make(w, 71)
+    ids, mem, cnt, lists = random_unions(rng, w.B, w.Hkv, N, w.C, counts)
+    out, lse = dkb.sparse_decode_attn(q, K, V, to_dev(ids), to_dev(mem, torch.uint8), to_dev(cnt), w.chunk,
+                                      w.scale)
+    torch.cuda.synchronize()
+    qh = q.cpu().numpy().astype(np.float64)
+    ro_, rl_ = oracle_attention_lists(qh, synth.to_numpy_f64(K), synth.to_numpy_f64(V), lists, w.chunk, w.scale,
+                                      w.G)
+    tol = ATOL[w.kv_dtype]
+    e_out, e_lse = max_abs(out.cpu().numpy(), ro_), max_abs(lse.cpu().numpy(), rl_)
+    print(f"{case}: {int(counts.sum())} entries, max|out err| {e_out:.3e}  max|lse err| {e_lse:.3e}")
+    assert e_out <= tol and e_lse <= tol
+
+
+def test_attention_fast_shape_many_heads(dkb):
+    """The fast shape over 8200 (b, g) pairs with unions of 0-2 chunks; the oracle
+    checks sampled (b, g)."""
+    w = workload("llama8b_l32k", 1025, 64, k=2)
+    assert w.B * w.Hkv > 8192
+    q, K, V = make(w, 73)
+    rng = np.random.default_rng(73)
+    counts = rng.integers(0, 3, (w.B, w.Hkv))
+    ids, mem, cnt, lists = random_unions(rng, w.B, w.Hkv, w.T * w.k, w.C, counts)
+    out, lse = dkb.sparse_decode_attn(q, K, V, to_dev(ids), to_dev(mem, torch.uint8), to_dev(cnt), w.chunk,
+                                      w.scale)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    qh = q.cpu().numpy().astype(np.float64)
+    tol = ATOL[w.kv_dtype]
+    for b in [0, 1, 511, 1024]:
+        for g in [0, 3, 7]:
+            Kh = synth.to_numpy_f64(K[b:b + 1, g:g + 1])
+            Vh = synth.to_numpy_f64(V[b:b + 1, g:g + 1])
+            ro_, rl_ = oracle_attention_lists(qh[b:b + 1, :, g * w.G:(g + 1) * w.G], Kh, Vh, [[lists[b][g]]],
+                                              w.chunk, w.scale, w.G)
+            assert max_abs(out[b:b + 1, :, g * w.G:(g + 1) * w.G], ro_) <= tol, (b, g)
+            assert max_abs(lse[b:b + 1, :, g * w.G:(g + 1) * w.G], rl_) <= tol, (b, g)
+
+
 # ----------------------------------------------------------------------------
 # gather
 # ----------------------------------------------------------------------------
@@ -562,6 +637,33 @@ def check_step_sampled(dkb, w, q, K, V, st, samples):
     return total_near
 
 
+def check_attention_every_pair(w, q, K, V, st):
+    """Attention of every (b, g) against the oracle over the GPU's own sets.  The
+    union's chunks of a (b, g) are copied (plain indexing) into a compact pool, and
+    the sets are renumbered to positions in it, so the oracle reads exactly the
+    rows the kernel should."""
+    u, c, idx = st.union_ids.cpu().numpy(), st.count.cpu().numpy(), st.topk_idx.cpu().numpy()
+    out, lse = st.out.cpu().numpy(), st.lse.cpu().numpy()
+    qh_all = q.cpu().numpy().astype(np.float64)
+    tol = ATOL[w.kv_dtype]
+    off = torch.arange(w.chunk, device=K.device)
+    worst = 0.0
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            ids = u[b, g, :c[b, g]]
+            rows = (torch.from_numpy(ids.astype(np.int64)).to(K.device)[:, None] * w.chunk + off).reshape(-1)
+            Kc = synth.to_numpy_f64(K[b, g].index_select(0, rows)[None, None])
+            Vc = synth.to_numpy_f64(V[b, g].index_select(0, rows)[None, None])
+            pos = {int(x): i for i, x in enumerate(ids)}
+            sel = np.array([[[[pos[int(x)] for x in idx[b, g, t]] for t in range(w.T)]]])
+            ro, rl = O.sparse_attention(qh_all[b:b + 1, :, g * w.G:(g + 1) * w.G], Kc, Vc, sel, w.chunk, w.scale)
+            e = max(max_abs(out[b:b + 1, :, g * w.G:(g + 1) * w.G], ro),
+                    max_abs(lse[b:b + 1, :, g * w.G:(g + 1) * w.G], rl))
+            assert e <= tol, (b, g, e)
+            worst = max(worst, e)
+    return worst
+
+
 @pytest.mark.parametrize("shadow", [False, True])
 def test_step_tiny_full(dkb, shadow):
     w = WORKLOADS["tiny"]
@@ -599,6 +701,8 @@ def test_step_full_size_sampled(dkb, name, samples):
     np.testing.assert_array_equal(st.member.cpu().numpy(), rm)
     np.testing.assert_array_equal(c, rc)
     np.testing.assert_array_equal(ov, ro)
+    worst = check_attention_every_pair(w, q, K, V, st)
+    print(f"{name}: attention of all {w.B * w.Hkv} (b, g) within {worst:.3e}")
     del K, V, lm
     torch.cuda.empty_cache()
 
