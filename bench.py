@@ -10,10 +10,12 @@ Landmarks (and their 8-bit shadow) are built once before timing: they are fixed
 for the whole decode.
 Inputs are seeded synthetic tensors resident in HBM before the timed region.
 
-Prints one JSON line.  `roofline` covers the kernel family that takes the most
-time per step; `kernels` lists every call's measured duration and algorithmic
-bytes; `cpu_baseline` times the CPU oracle on a bounded sample of the same
-workload (single thread).
+Prints one JSON line.  `value` comes from steps timed with nothing between the
+library calls; a second pass of the same steps, with events around every call,
+gives `kernels` (every call's measured duration and algorithmic bytes) and
+`roofline` (the call that takes the most time per step).  `cpu_baseline` times
+the CPU oracle on a bounded sample of the same workload, one worker process per
+host core.
 """
 from __future__ import annotations
 
@@ -43,7 +45,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU oracle sample budget (0 disables the CPU baseline)")
     ap.add_argument("--no-events", action="store_true",
-                    help="time only whole steps (no per-call events inside the step)")
+                    help="skip the second pass that times every call with events")
     ap.add_argument("--no-shadow", action="store_true",
                     help="score from the fp32 landmarks only (no 8-bit landmark shadow)")
     ap.add_argument("--host-copy", choices=("mapped", "copy"), default="mapped",
@@ -125,55 +127,145 @@ def near_tie_report(gpu_sel, ref_sel, scores):
     return rows, diff_rows, near, hard
 
 
-def cpu_baseline(w, qs_host, K, V, budget_s, seed, gpu_topk=None):
-    """Time the fp64 CPU oracle on sampled (request, KV head, layer) units; with the
-    GPU's top-k of every layer, also compare the sampled selections."""
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle, unchanged, on every host core.  A pool of
+# worker processes (one BLAS thread each) is forked before anything touches the
+# GPU; each worker times the oracle on units of one sampled (request, KV head)
+# of the same workload for the whole budget, so the workers run side by side
+# and their rates add up.  Inputs reach the workers as raw bf16 bit patterns
+# (or fp32) and are widened there, untimed.
+# ---------------------------------------------------------------------------
+MAX_CPU_WORKERS = 16      # the host share of one GPU on the boxes this runs on
+_POOL = None
+
+
+def cpu_pool_size():
+    aff = len(os.sched_getaffinity(0))
+    return max(1, min(aff, MAX_CPU_WORKERS)), aff
+
+
+def start_cpu_pool():
+    """Fork the oracle workers (call before the GPU is initialised)."""
+    import multiprocessing as mp
+    global _POOL
+    n, _ = cpu_pool_size()
+    _POOL = mp.get_context("fork").Pool(n)
+
+
+def stop_cpu_pool():
+    global _POOL
+    if _POOL is not None:
+        _POOL.close()
+        _POOL.join()
+        _POOL = None
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def raw_host(t):
+    """A torch tensor as numpy: uint16 bit patterns for bf16, the values otherwise."""
+    import numpy as np
+    import torch
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def _widen(a):
+    import numpy as np
+    from oracle import dualkv_oracle as O
+    return O.bf16_bits_to_f64(a) if a.dtype == np.uint16 else np.asarray(a, dtype=np.float64)
+
+
+def run_cpu_pool(worker, tasks):
+    """Run one task per worker; returns the results and the summed rate in units/s."""
+    if _POOL is None:
+        raise RuntimeError("the CPU worker pool was not started")
+    res = _POOL.map(worker, tasks, chunksize=1)
+    rate = sum(r["units"] / r["spent"] for r in res if r["spent"] > 0)
+    return res, rate
+
+
+def cpu_record(rate, units_per_step, res, what, slice_="(request, KV head)"):
+    n, aff = cpu_pool_size()
+    units = sum(r["units"] for r in res)
+    spent = sum(r["spent"] for r in res)
+    per_unit = spent / max(units, 1)
+    return {"value": rate / units_per_step, "unit": "steps/s", "cores": len(res), "kind": "oracle",
+            "cpu_model": cpu_model(), "affinity_cores": aff,
+            "sample": f"{units} {what} on {len(res)} worker processes (one per core, one BLAS thread each; "
+                      f"{spent:.1f} s of CPU time, {per_unit * 1e3:.1f} ms per unit), each worker on one sampled "
+                      f"{slice_} for the whole budget; the summed rate scaled to {units_per_step} units per step"}
+
+
+def _chunk_step_worker(task):
+    """The oracle's chunk step (scores, top-k, union, attention) on one (b, g),
+    layer after layer, for `budget` seconds; with the GPU's sets, the sampled
+    selections are compared too."""
     import numpy as np
     from threadpoolctl import threadpool_limits
     from oracle import dualkv_oracle as O
-    from sparse_kv_retrieval_amd import synth
-
-    rng = np.random.default_rng(seed)
-    pairs = [(int(rng.integers(w.B)), int(rng.integers(w.Hkv))) for _ in range(4)]
-    per_pair = budget_s / len(pairs)
-    units, spent = 0, 0.0
+    Kr, Vr, qs, gsel, chunk, k, scale, budget = task
+    units, spent, layer = 0, 0.0, 0
     cmp = [0, 0, 0, 0]
-    overlap_gpu = overlap_ref = 0
+    ov = [0, 0]
     with threadpool_limits(1):
-        for b, g in pairs:
-            Kh = synth.to_numpy_f64(K[b:b + 1, g:g + 1])
-            Vh = synth.to_numpy_f64(V[b:b + 1, g:g + 1])
-            lm = O.chunk_landmarks(Kh, w.chunk)            # built once per prefill: not timed
-            pair_spent, layer = 0.0, 0
-            while pair_spent < per_pair:
-                li = layer % len(qs_host)
-                qh = qs_host[li][b:b + 1, :, g * w.G:(g + 1) * w.G]
-                t0 = time.perf_counter()
-                s = O.chunk_scores(qh, lm, w.scale, "mean")
-                sel = O.topk_chunks(s, w.k)
-                O.union_select(sel)
-                O.sparse_attention(qh, Kh, Vh, sel, w.chunk, w.scale)
-                pair_spent += time.perf_counter() - t0
-                units += 1
-                if gpu_topk is not None and layer < len(qs_host):
-                    gsel = gpu_topk[li][b:b + 1, g:g + 1]
-                    for i, x in enumerate(near_tie_report(gsel, sel, s)):
-                        cmp[i] += x
-                    if w.T == 2:
-                        overlap_gpu += len(set(gsel[0, 0, 0].tolist()) & set(gsel[0, 0, 1].tolist()))
-                        overlap_ref += len(set(sel[0, 0, 0].tolist()) & set(sel[0, 0, 1].tolist()))
-                layer += 1
-            spent += pair_spent
-    per_unit = spent / units
-    per_step = per_unit * w.B * w.Hkv * len(qs_host)
-    out = {"value": 1.0 / per_step, "unit": "steps/s", "cores": 1, "kind": "oracle",
-           "sample": f"{units} (request, KV head, layer) units of the {w.name} step "
-                     f"({spent:.1f} s, {per_unit * 1e3:.1f} ms each), scaled to "
-                     f"{w.B * w.Hkv * len(qs_host)} units per step; landmarks precomputed"}
+        Kh, Vh = _widen(Kr)[None, None], _widen(Vr)[None, None]
+        lm = O.chunk_landmarks(Kh, chunk)            # built once per prefill: not timed
+        while spent < budget:
+            li = layer % len(qs)
+            qh = qs[li]
+            t0 = time.perf_counter()
+            s = O.chunk_scores(qh, lm, scale, "mean")
+            sel = O.topk_chunks(s, k)
+            O.union_select(sel)
+            O.sparse_attention(qh, Kh, Vh, sel, chunk, scale)
+            spent += time.perf_counter() - t0
+            units += 1
+            if gsel is not None and layer < len(qs):
+                for i, x in enumerate(near_tie_report(gsel[li], sel, s)):
+                    cmp[i] += x
+                if sel.shape[2] == 2:
+                    g_ = gsel[li]
+                    ov[0] += len(set(g_[0, 0, 0].tolist()) & set(g_[0, 0, 1].tolist()))
+                    ov[1] += len(set(sel[0, 0, 0].tolist()) & set(sel[0, 0, 1].tolist()))
+            layer += 1
+    return {"units": units, "spent": spent, "cmp": cmp, "ov": ov}
+
+
+def cpu_baseline(w, qs_host, K, V, budget_s, seed, gpu_topk=None):
+    """Time the fp64 CPU oracle on sampled (request, KV head, layer) units on every
+    host core; with the GPU's top-k of every layer, also compare the sampled
+    selections."""
+    import numpy as np
+    n, _ = cpu_pool_size()
+    rng = np.random.default_rng(seed)
+    flat = rng.choice(w.B * w.Hkv, size=min(n, w.B * w.Hkv), replace=False)
+    tasks = []
+    for f in flat:
+        b, g = divmod(int(f), w.Hkv)
+        qs = [q[b:b + 1, :, g * w.G:(g + 1) * w.G] for q in qs_host]
+        gsel = None if gpu_topk is None else [t[b:b + 1, g:g + 1] for t in gpu_topk]
+        tasks.append((raw_host(K[b, g]), raw_host(V[b, g]), qs, gsel, w.chunk, w.k, w.scale, budget_s))
+    res, rate = run_cpu_pool(_chunk_step_worker, tasks)
+    out = cpu_record(rate, w.B * w.Hkv * len(qs_host), res,
+                     f"(request, KV head, layer) units of the {w.name} step (landmarks precomputed)")
     if gpu_topk is not None:
+        cmp = [sum(r["cmp"][i] for r in res) for i in range(4)]
         out["selection_check"] = {"rows": cmp[0], "rows_differing": cmp[1], "near_tie_chunks": cmp[2],
-                                  "mismatched_chunks": cmp[3], "overlap_gpu": overlap_gpu,
-                                  "overlap_oracle": overlap_ref}
+                                  "mismatched_chunks": cmp[3], "overlap_gpu": sum(r["ov"][0] for r in res),
+                                  "overlap_oracle": sum(r["ov"][1] for r in res)}
     return out
 
 
@@ -224,7 +316,10 @@ def bench_host_pool(args, w):
     from sparse_kv_retrieval_amd.host_pool import HostPoolDecoder, StageTimer
 
     dev = "cuda"
-    total = 1 + args.warmup + args.steps           # one cold step, warm-up, timed steps
+    # one cold step, warm-up, the timed steps, then (with events) the same number of
+    # steps again with events around every stage
+    timed0 = 1 + args.warmup
+    total = timed0 + args.steps * (1 if args.no_events else 2)
     t0 = time.time()
     qseq = [synth.make_query_sequence(w, args.seed, total, layer=l, device=dev) for l in range(w.layers)]
     K, V = synth.make_kv_pool(w, args.seed, device=dev, q0=qseq[0][0])
@@ -247,29 +342,42 @@ def bench_host_pool(args, w):
     def qs_at(s):
         return [qseq[l][s] for l in range(w.layers)]
 
-    for s in range(1 + args.warmup):
+    for s in range(timed0):
         dec.step(qs_at(s))
     torch.cuda.synchronize()
-    timer = None if args.no_events else StageTimer()
+    # headline: event-free steps
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
-    for s in range(1 + args.warmup, total):
-        dec.step(qs_at(s), timer)
+    for s in range(timed0, timed0 + args.steps):
+        dec.step(qs_at(s))
     end.record()
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
+    # stage durations: the following steps with events around every stage
+    timer = None if args.no_events else StageTimer()
+    if timer:
+        t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t_start.record()
+        for s in range(timed0 + args.steps, total):
+            dec.step(qs_at(s), timer)
+        t_end.record()
+        torch.cuda.synchronize()
+        timer_ms_per_step = t_start.elapsed_time(t_end) / args.steps
 
     # Statistics from a deterministic replay of the same steps (untimed).
     dec.reset()
     prev_spec = [None] * w.layers
     hits = unions = misses = overlap_sum = temporal_hits = 0
+    misses_timer = 0      # misses of the stage-timed steps (their copies give the PCIe rate)
     n_units = 0
     for s in range(total):
         dec.step(qs_at(s))
         torch.cuda.synchronize()
         for l in range(w.layers):
             idx = dec.topk_idx[l]
-            if s >= 1 + args.warmup:
+            if s >= timed0 + args.steps:
+                misses_timer += int(dec.plans[l].miss_count.sum())
+            if timed0 <= s < timed0 + args.steps:
                 p = dec.plans[l]
                 hits += int(p.hit_count.sum())
                 misses += int(p.miss_count.sum())
@@ -303,8 +411,8 @@ def bench_host_pool(args, w):
         g_ms = timer.total_ms("gather") / args.steps
         sel_ms = timer.total_ms("select") / args.steps
         att_ms = timer.total_ms("attn") / args.steps
-        pcie = miss_bytes_step / (g_ms * 1e-3) / 1e9
-        hidden = (g_ms + sel_ms + att_ms - ms_per_step) / g_ms if g_ms > 0 else 0.0
+        pcie = misses_timer * chunk_bytes / args.steps / (g_ms * 1e-3) / 1e9
+        hidden = (g_ms + sel_ms + att_ms - timer_ms_per_step) / g_ms if g_ms > 0 else 0.0
         out["pcie_GBps"] = round(pcie, 2)
         out["pcie_frac_of_contiguous"] = round(pcie / link_gbps, 4)
         out["copy_ms_per_step"] = round(g_ms, 3)
@@ -317,7 +425,7 @@ def bench_host_pool(args, w):
         out["kernels"] = {
             "select (score_topk + union_select)": {"avg_us": round(sel_ms * 1e3 / w.layers, 2)},
             "gather_kv": {"avg_us": round(g_ms * 1e3 / w.layers, 2),
-                          "bytes_per_launch": int(miss_bytes_step / w.layers)},
+                          "bytes_per_launch": int(misses_timer * chunk_bytes / args.steps / w.layers)},
             "sparse_decode_attn": {"avg_us": round(att_ms * 1e3 / w.layers, 2),
                                    "bytes_per_launch": int(union_bytes_step / w.layers)},
         }
@@ -382,16 +490,21 @@ def bench_mla(args, w):
     for _ in range(args.warmup):
         step(0)
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
+    # headline: event-free steps, one event per step boundary
+    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    bounds[0].record()
+    for s_ in range(args.steps):
+        step(0)
+        bounds[s_ + 1].record()
+    torch.cuda.synchronize()
+    ms_per_step = bounds[0].elapsed_time(bounds[-1]) / args.steps
+    step_ms = [bounds[s_].elapsed_time(bounds[s_ + 1]) for s_ in range(args.steps)]
+    # call durations: the same steps again with events around every call
     for s_ in range(args.steps):
         step(s_ + 1)
-    end.record()
     torch.cuda.synchronize()
-    ms_per_step = start.elapsed_time(end) / args.steps
     call_ms = {c: sum(ev[s_][i].elapsed_time(ev[s_][i + 1]) for s_ in range(args.steps)) / args.steps
                for i, c in enumerate(calls)}
-    step_ms = [ev[s_][0].elapsed_time(ev[s_][2]) for s_ in range(args.steps)]
 
     # algorithmic work: the indexer streams every key once (queries and the
     # selected ids besides); attention reads each union row once and does
@@ -437,6 +550,7 @@ def bench_mla(args, w):
                    "di": w.di, "k": w.k, "T": w.T, "seed": args.seed},
         "ms_per_step_median": round(float(np.median(step_ms)), 4),
         "ms_per_step_min": round(float(np.min(step_ms)), 4),
+        "timing": "value: event-free steps; kernels and roofline: a second pass with events around every call",
         "mean_union_tokens": round(union_tokens / w.B, 1),
         "prediction_accuracy": round(accuracy, 5),
         "roofline": roofline,
@@ -565,20 +679,24 @@ def bench_variant(args, w):
     for _ in range(args.warmup):
         step(0)
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
+    # headline: event-free steps, one event per step boundary
+    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    bounds[0].record()
+    for s_ in range(args.steps):
+        step(0)
+        bounds[s_ + 1].record()
+    torch.cuda.synchronize()
+    ms_per_step = bounds[0].elapsed_time(bounds[-1]) / args.steps
+    step_ms = [bounds[s_].elapsed_time(bounds[s_ + 1]) for s_ in range(args.steps)]
+    # call durations: the same steps again with events around every call
     for s_ in range(args.steps):
         step(s_ + 1)
-    end.record()
     torch.cuda.synchronize()
     call_ms = {c: 0.0 for c in calls}
-    step_ms = []
     for s_ in range(args.steps):
         for l in range(w.layers):
             for i, c in enumerate(calls):
                 call_ms[c] += ev[s_][l][i].elapsed_time(ev[s_][l][i + 1])
-        step_ms.append(ev[s_][0][0].elapsed_time(ev[s_][w.layers - 1][len(calls)]))
-    ms_per_step = start.elapsed_time(end) / args.steps
 
     chunk_bytes = w.chunk_kv_bytes()
     sel_bytes_step = sum(sel_chunks) * chunk_bytes
@@ -628,6 +746,7 @@ def bench_variant(args, w):
         "data": "synthetic",
         "config": cfg,
         "ms_per_step_median": round(float(np.median(step_ms)), 4),
+        "timing": "value: event-free steps; kernels and roofline: a second pass with events around every call",
         "selected_kv_GBps": round(attn_gbps, 1),
         "selected_kv_frac_hbm_peak": round(attn_gbps / HBM_PEAK_GBPS, 4),
         "mean_union_chunks": round(sum(sel_chunks) / (w.layers * B * Hkv), 2),
@@ -644,100 +763,110 @@ def bench_variant(args, w):
     print(json.dumps(res), flush=True)
 
 
-def cpu_baseline_variant(w, sel, qs, K, V, args):
-    """Time the fp64 CPU oracle of the variant step (selection, union, and for
-    `capped` the plan from an empty working set, then attention) on sampled
-    (request, KV head, layer) units, single thread."""
+def _variant_worker(task):
+    """The oracle's variant step (selection, union, for `capped` the plan from an
+    empty working set, then attention) on one (b, g), layer after layer."""
     import numpy as np
     from threadpoolctl import threadpool_limits
     from oracle import dualkv_oracle as O
-    from sparse_kv_retrieval_amd import synth
-
-    rng = np.random.default_rng(args.seed)
-    pairs = [(int(rng.integers(w.B)), int(rng.integers(w.Hkv))) for _ in range(4)]
-    per_pair = args.cpu_seconds / len(pairs)
-    k_max = args.k_max or 2 * w.k
-    S = args.slots or 4 * w.k
-    units, spent = 0, 0.0
+    Kr, Vr, qs, sel, chunk, k, scale, T, k_max, S, cap, gamma, cov_scale, budget = task
+    units, spent, layer = 0, 0.0, 0
     with threadpool_limits(1):
-        for b, g in pairs:
-            Kh = synth.to_numpy_f64(K[b:b + 1, g:g + 1])
-            Vh = synth.to_numpy_f64(V[b:b + 1, g:g + 1])
+        Kh, Vh = _widen(Kr)[None, None], _widen(Vr)[None, None]
+        if sel == "minmax":
+            mn, mx = O.chunk_minmax(Kh, chunk)        # summaries: built once, not timed
+        else:
+            lm = O.chunk_landmarks(Kh, chunk)
+        res, st = np.full((1, 1, S), -1), np.full((1, 1, S), -1)
+        while spent < budget:
+            qh = qs[layer % len(qs)]
+            t0 = time.perf_counter()
             if sel == "minmax":
-                mn, mx = O.chunk_minmax(Kh, w.chunk)        # summaries: built once, not timed
+                chosen = O.minmax_topk(qh, mn, mx, k, scale)
+                O.union_select(chosen)
+            elif sel == "coverage":
+                s = O.chunk_scores(qh, lm, cov_scale, "mean")
+                idx, n = O.coverage_select(s, gamma, k_max)
+                O.union_select_ragged(idx, n)
+                chosen = [[[idx[0, 0, t, :n[0, 0, t]] for t in range(T)]]]
             else:
-                lm = O.chunk_landmarks(Kh, w.chunk)
-            res, st = np.full((1, 1, S), -1), np.full((1, 1, S), -1)
-            pair_spent, layer = 0.0, 0
-            while pair_spent < per_pair:
-                qh = qs[layer % len(qs)][b:b + 1, :, g * w.G:(g + 1) * w.G].cpu().numpy().astype(np.float64)
-                t0 = time.perf_counter()
-                if sel == "minmax":
-                    chosen = O.minmax_topk(qh, mn, mx, w.k, w.scale)
-                    O.union_select(chosen)
-                elif sel == "coverage":
-                    s = O.chunk_scores(qh, lm, args.cov_scale, "mean")
-                    idx, n = O.coverage_select(s, args.gamma, k_max)
-                    O.union_select_ragged(idx, n)
-                    chosen = [[[idx[0, 0, t, :n[0, 0, t]] for t in range(w.T)]]]
-                else:
-                    s = O.chunk_scores(qh, lm, w.scale, "mean")
-                    chosen = O.topk_chunks(s, w.k)
-                    O.union_select(chosen)
-                    sc = np.take_along_axis(s, chosen, axis=-1)
-                    r = O.capped_plan(chosen[:, :, 1], sc[:, :, 1], None, res, st, args.cap, layer)
-                    res, st = r["resident"], r["stamp"]
-                if sel == "coverage":
-                    for t in range(w.T):
-                        sel_t = np.asarray(chosen[0][0][t])[None, None, None]
-                        O.sparse_attention(qh[:, t:t + 1], Kh, Vh, sel_t, w.chunk, w.scale)
-                else:
-                    O.sparse_attention(qh, Kh, Vh, chosen, w.chunk, w.scale)
-                pair_spent += time.perf_counter() - t0
-                units += 1
-                layer += 1
-            spent += pair_spent
-    per_unit = spent / units
-    per_step = per_unit * w.B * w.Hkv * w.layers
-    return {"value": 1.0 / per_step, "unit": "steps/s", "cores": 1, "kind": "oracle",
-            "sample": f"{units} (request, KV head, layer) units of the {w.name} {sel} step ({spent:.1f} s, "
-                      f"{per_unit * 1e3:.1f} ms each), scaled to {w.B * w.Hkv * w.layers} units per step; "
-                      f"summaries precomputed"}
+                s = O.chunk_scores(qh, lm, scale, "mean")
+                chosen = O.topk_chunks(s, k)
+                O.union_select(chosen)
+                sc = np.take_along_axis(s, chosen, axis=-1)
+                r = O.capped_plan(chosen[:, :, 1], sc[:, :, 1], None, res, st, cap, layer)
+                res, st = r["resident"], r["stamp"]
+            if sel == "coverage":
+                for t in range(T):
+                    sel_t = np.asarray(chosen[0][0][t])[None, None, None]
+                    O.sparse_attention(qh[:, t:t + 1], Kh, Vh, sel_t, chunk, scale)
+            else:
+                O.sparse_attention(qh, Kh, Vh, chosen, chunk, scale)
+            spent += time.perf_counter() - t0
+            units += 1
+            layer += 1
+    return {"units": units, "spent": spent}
+
+
+def cpu_baseline_variant(w, sel, qs, K, V, args):
+    """Time the fp64 CPU oracle of the variant step on sampled (request, KV head,
+    layer) units on every host core."""
+    import numpy as np
+    n, _ = cpu_pool_size()
+    rng = np.random.default_rng(args.seed)
+    flat = rng.choice(w.B * w.Hkv, size=min(n, w.B * w.Hkv), replace=False)
+    qs_h = [q.cpu().numpy().astype(np.float64) for q in qs]
+    tasks = []
+    for f in flat:
+        b, g = divmod(int(f), w.Hkv)
+        tasks.append((raw_host(K[b, g]), raw_host(V[b, g]), [q[b:b + 1, :, g * w.G:(g + 1) * w.G] for q in qs_h],
+                      sel, w.chunk, w.k, w.scale, w.T, args.k_max or 2 * w.k, args.slots or 4 * w.k, args.cap,
+                      args.gamma, args.cov_scale, args.cpu_seconds))
+    res, rate = run_cpu_pool(_variant_worker, tasks)
+    return cpu_record(rate, w.B * w.Hkv * w.layers, res,
+                      f"(request, KV head, layer) units of the {w.name} {sel} step (summaries precomputed)")
+
+
+def _mla_worker(task):
+    """The oracle's token-level step (indexer top-k, union, latent attention) on
+    one request, repeated for `budget` seconds; the GPU's sets are compared."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import dualkv_oracle as O
+    qih, qh, Kr, Lr, gsel, k, index_scale, dv, scale, budget = task
+    units, spent = 0, 0.0
+    cmp = [0, 0, 0, 0]
+    with threadpool_limits(1):
+        kh, lh = _widen(Kr)[None, None], _widen(Lr)[None, None]
+        while spent < budget:
+            t0 = time.perf_counter()
+            s = O.chunk_scores(qih, kh, index_scale, "mean")
+            sel = O.topk_chunks(s, k)
+            O.union_select(sel)
+            O.mla_attention(qh, lh, sel, dv, scale)
+            spent += time.perf_counter() - t0
+            if units == 0:
+                cmp = list(near_tie_report(gsel, sel, s))
+            units += 1
+    return {"units": units, "spent": spent, "cmp": cmp}
 
 
 def cpu_baseline_mla(w, qi, q, Kidx, lat, gpu_topk, budget_s):
-    """Time the fp64 CPU oracle (indexer top-k, union, latent attention) on whole
-    sampled requests, single thread; compare the sampled selections with the GPU's."""
+    """Time the fp64 CPU oracle (indexer top-k, union, latent attention) on sampled
+    whole requests on every host core; compare the sampled selections with the
+    GPU's."""
     import numpy as np
-    from threadpoolctl import threadpool_limits
-    from oracle import dualkv_oracle as O
-    from sparse_kv_retrieval_amd import synth
-
-    spent, units = 0.0, 0
-    cmp = [0, 0, 0, 0]
-    with threadpool_limits(1):
-        b = 0
-        while spent < budget_s and b < w.B:
-            qih = qi[b:b + 1].cpu().numpy().astype(np.float64)
-            qh = q[b:b + 1].cpu().numpy().astype(np.float64)
-            kh = synth.to_numpy_f64(Kidx[b:b + 1])
-            lh = synth.to_numpy_f64(lat[b:b + 1])
-            t0 = time.perf_counter()
-            s = O.chunk_scores(qih, kh, w.index_scale, "mean")
-            sel = O.topk_chunks(s, w.k)
-            O.union_select(sel)
-            O.mla_attention(qh, lh, sel, w.dv, w.scale)
-            spent += time.perf_counter() - t0
-            units += 1
-            for i, x in enumerate(near_tie_report(gpu_topk[b:b + 1].cpu().numpy(), sel, s)):
-                cmp[i] += x
-            b += 1
-    per_unit = spent / units
-    return {"value": 1.0 / (per_unit * w.B), "unit": "steps/s", "cores": 1, "kind": "oracle",
-            "sample": f"{units} whole requests of the {w.name} layer ({spent:.1f} s, {per_unit:.2f} s each), "
-                      f"scaled to {w.B} requests per step",
-            "selection_check": {"rows": cmp[0], "rows_differing": cmp[1], "near_tie_chunks": cmp[2],
-                                "mismatched_chunks": cmp[3]}}
+    n, _ = cpu_pool_size()
+    reqs = list(range(min(n, w.B)))
+    qih, qh, gt = (x.cpu().numpy() for x in (qi, q, gpu_topk))
+    tasks = [(qih[b:b + 1].astype(np.float64), qh[b:b + 1].astype(np.float64), raw_host(Kidx[b, 0]),
+              raw_host(lat[b, 0]), gt[b:b + 1], w.k, w.index_scale, w.dv, w.scale, budget_s) for b in reqs]
+    res, rate = run_cpu_pool(_mla_worker, tasks)
+    out = cpu_record(rate, w.B, res, f"whole requests of the {w.name} layer", "request")
+    cmp = [sum(r["cmp"][i] for r in res) for i in range(4)]
+    out["selection_check"] = {"rows": cmp[0], "rows_differing": cmp[1], "near_tie_chunks": cmp[2],
+                              "mismatched_chunks": cmp[3]}
+    return out
 
 
 def calibrate_copy():
@@ -766,6 +895,15 @@ def main():
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the decode step has no "
               "cross-GPU exchange and this benchmark measures a single MI355X.", file=sys.stderr)
         sys.exit(2)
+    if args.cpu_seconds > 0 and not args.calibrate_copy:
+        start_cpu_pool()          # forked before anything touches the GPU
+    try:
+        run(args)
+    finally:
+        stop_cpu_pool()
+
+
+def run(args):
     import numpy as np
     import torch
 
@@ -836,20 +974,18 @@ def main():
                               dtype=torch.uint8, device=dev)
         tail_rows = int(tail_len.sum().item())
     use_events = not args.no_events
-    # one set of events per (step, layer), read only after the timed region
-    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(w.layers)]
-          for _ in range(args.steps)] if use_events else None
     call_ms = {c: 0.0 for c in calls}
 
-    def step(record):
+    def step(ev_step=None):
+        """One decode step over every layer; with ev_step, events around every call."""
         for l in range(w.layers):
             q = qs[l]
-            e = ev[record - 1][l] if record else None
-            if record:
+            e = ev_step[l] if ev_step else None
+            if e:
                 e[0].record()
             dkb.score_topk_union(q, lm, w.k, w.scale, dkb.DK_REDUCE_MEAN, st.topk_idx, None, st.union_ids,
                                  st.member, st.count, st.overlap, st.ws_topk, shadow=shadow)
-            if record:
+            if e:
                 e[1].record()
             if args.tail:
                 dkb.sparse_decode_attn_tail(q, K, V, st.union_ids, st.member, st.count, w.chunk, w.scale,
@@ -858,27 +994,37 @@ def main():
             else:
                 dkb.sparse_decode_attn(q, K, V, st.union_ids, st.member, st.count, w.chunk, w.scale,
                                        out=st.out, lse=st.lse, ws=st.ws_attn)
-            if record:
+            if e:
                 e[2].record()
 
     for _ in range(args.warmup):
-        step(0)
+        step()
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
+    # The headline: K steps with nothing between the calls but one event at each
+    # step boundary.
+    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    bounds[0].record()
     for s in range(args.steps):
-        step(s + 1 if use_events else 0)
-    end.record()
+        step()
+        bounds[s + 1].record()
     torch.cuda.synchronize()
-    step_ms = []
+    step_ms = [bounds[s].elapsed_time(bounds[s + 1]) for s in range(args.steps)]
+    total_ms = bounds[0].elapsed_time(bounds[-1])
+    ms_per_step = total_ms / args.steps
+    # Call durations: the same K steps again, with events around every call (on the
+    # launch stream), read only afterwards.
+    call_pass_ms = None
     if use_events:
+        ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(w.layers)]
+              for _ in range(args.steps)]
+        for s in range(args.steps):
+            step(ev[s])
+        torch.cuda.synchronize()
         for s in range(args.steps):
             for l in range(w.layers):
                 for i, c in enumerate(calls):
                     call_ms[c] += ev[s][l][i].elapsed_time(ev[s][l][i + 1])
-            step_ms.append(ev[s][0][0].elapsed_time(ev[s][w.layers - 1][len(calls)]))
-    total_ms = start.elapsed_time(end)
-    ms_per_step = total_ms / args.steps
+        call_pass_ms = ev[0][0][0].elapsed_time(ev[args.steps - 1][w.layers - 1][len(calls)]) / args.steps
     steps_per_s = 1000.0 / ms_per_step
 
     kernels = {}
@@ -937,8 +1083,11 @@ def main():
         "config": {"workload": w.name, "B": w.B, "L": w.L, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d,
                    "chunk": w.chunk, "k": w.k, "T": w.T, "layers": w.layers, "seed": args.seed,
                    "landmark_shadow": shadow is not None, "tail_max": args.tail},
-        "ms_per_step_median": round(float(np.median(step_ms)), 4) if step_ms else None,
-        "ms_per_step_min": round(float(np.min(step_ms)), 4) if step_ms else None,
+        "ms_per_step_median": round(float(np.median(step_ms)), 4),
+        "ms_per_step_min": round(float(np.min(step_ms)), 4),
+        "timing": "value and ms_per_step: event-free steps (one event per step boundary); kernels and "
+                  "roofline: a second pass of the same steps with events around every call",
+        "ms_per_step_call_pass": None if call_pass_ms is None else round(call_pass_ms, 4),
         "selected_kv_GBps": round(sel_gbps, 1),
         "selected_kv_frac_hbm_peak": round(sel_gbps / HBM_PEAK_GBPS, 4),
         "hbm_copy_GBps": round(copy_gbps, 1),

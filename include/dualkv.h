@@ -23,7 +23,10 @@
  * - Arguments are checked before anything is enqueued.  A call that returns
  *   anything other than DK_OK has enqueued nothing and written nothing; the
  *   reason is in dk_last_error().  HIP failures return DK_ERR_HIP with the HIP
- *   error string.
+ *   error string.  One exception: dk_gather_kv with DK_SRC_HOST_COPY issues one
+ *   copy per run of chunks, and when the HIP runtime fails partway (DK_ERR_HIP)
+ *   the copies issued before the failure stay enqueued; the destination slots
+ *   are then undefined.
  * - Tensors are dense in their last dimension.  KV pools are described by a
  *   base pointer and dk_strides {b, h, t}: the element offset of row n of
  *   (request b, head g) is b*s.b + g*s.h + n*s.t.  Pool and landmark rows must
@@ -397,7 +400,9 @@ dk_status dk_union_select(const int32_t* topk_idx, int B, int Hkv, int T, int k,
  *                                 hipMemcpyAsync (2-D when rows are strided) per run of
  *                                 consecutive chunks on `stream` and returns after
  *                                 issuing.  Every copy costs a few microseconds of host
- *                                 time, so scattered misses are API-bound.
+ *                                 time, so scattered misses are API-bound.  A HIP
+ *                                 failure partway returns DK_ERR_HIP with the earlier
+ *                                 copies still enqueued (destination slots undefined).
  * src_kind = DK_SRC_HOST_MAPPED : K_src/V_src are pinned host memory, the lists are
  *                                 device memory; one kernel on `stream` reads the pool
  *                                 through its device mapping over PCIe.  Fully

@@ -87,6 +87,18 @@ def test_index_topk(dkb, name, kw):
     check_index(dkb, qi, Kidx, w.k, w.index_scale, label=name)
 
 
+@pytest.mark.parametrize("B,rows_per_block", [(128, 2048), (200, 4096)])
+def test_index_topk_long_scoring_blocks(dkb, B, rows_per_block):
+    """Many rows of 10000 tokens: the scoring kernel takes 2048- or 4096-token blocks
+    (the longest that keep 512 blocks), and the last block of every row is short
+    (10000 - 8192 = 1808 tokens)."""
+    g = torch.Generator(device="cuda").manual_seed(12)
+    qi = synth.round_bf16(torch.randn(B, 2, 4, 128, generator=g, device="cuda"))
+    keys = bf16_keys(torch.randn(B, 1, 10000, 128, generator=g, device="cuda"))
+    print(f"B={B}: {rows_per_block}-token scoring blocks", flush=True)
+    check_index(dkb, qi, keys, 700, 1.0 / 128 ** 0.5, union=True, label=f"B={B}")
+
+
 def test_index_topk_union(dkb):
     w = MLA_WORKLOADS["mla_b2_l16k"]
     qi, _, Kidx, _ = mla_inputs(w, 32)

@@ -813,3 +813,113 @@ def test_host_pool_full_size_sampled(dkb):
                                          check_pairs=[(0, 0), (17, 4), (31, 7)])
     print(f"host_b32_l128k: near-tie chunks {near}, steady-state hit rate {hit_rate:.3f}")
     torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------------------
+# host-pool stream ordering, and the host path against the HBM path
+# ----------------------------------------------------------------------------
+
+DELAY_CYCLES = 2_000_000     # torch.cuda._sleep: a bounded spin kernel, no flag waits
+
+
+def host_pool_setup(dkb, w, steps, seed):
+    qseq = [synth.make_query_sequence(w, seed, steps, layer=l, device="cuda") for l in range(w.layers)]
+    K, V = synth.make_kv_pool(w, seed, device="cuda", q0=qseq[0][0])
+    lm = dkb.build_landmarks(K, w.chunk)
+    sh = dkb.build_landmark_shadow(lm)
+    return qseq, K, V, lm, sh
+
+
+def host_pool_outputs(dec, qseq, steps):
+    """out and lse of every (step, layer), from an empty hot cache."""
+    dec.reset()
+    outs = []
+    for s in range(steps):
+        dec.step([q[s] for q in qseq])
+        torch.cuda.synchronize()
+        outs.append((dec.out.clone(), dec.lse.clone()))
+    return outs
+
+
+@pytest.mark.parametrize("delay", ["copy", "compute"])
+@pytest.mark.parametrize("mode,buffers", [("mapped", "per-layer"), ("copy", "per-layer"),
+                                          ("mapped", "ping-pong"), ("copy", "ping-pong")])
+def test_host_pool_stream_order_under_delays(dkb, monkeypatch, mode, buffers, delay):
+    """DualDecoder 5.4: events order the transfers against the compute without a
+    global synchronisation.  A bounded spin kernel queued on the copy stream before
+    every gather (a late copy: attention must still wait for it), or on the compute
+    stream before every attention (a late reader: a shared ping-pong buffer must not
+    be refilled under it), must leave every output bit-identical."""
+    from sparse_kv_retrieval_amd.host_pool import HostPoolDecoder
+    w = shrink(WORKLOADS["host_b32_l128k"], B=2, L=8192, layers=4)
+    steps = 3
+    qseq, K, V, lm, sh = host_pool_setup(dkb, w, steps, seed=9)
+    dec = HostPoolDecoder(K.cpu().pin_memory(), V.cpu().pin_memory(), lm, sh, T=w.T, Hq=w.Hq, k=w.k,
+                          scale=w.scale, layers=w.layers, mode=mode, buffers=buffers)
+    ref = host_pool_outputs(dec, qseq, steps)
+    name = "gather_kv" if delay == "copy" else "sparse_decode_attn"
+    orig = getattr(dkb, name)
+    spins = [0]
+
+    def late(*a, stream=None, **kw):
+        s = stream if stream is not None else torch.cuda.current_stream()
+        with torch.cuda.stream(s):
+            torch.cuda._sleep(DELAY_CYCLES)
+        spins[0] += 1
+        return orig(*a, stream=stream, **kw)
+
+    monkeypatch.setattr(dkb, name, late)
+    got = host_pool_outputs(dec, qseq, steps)
+    assert spins[0] == steps * w.layers
+    for s in range(steps):
+        assert torch.equal(got[s][0], ref[s][0]), (s, "out")
+        assert torch.equal(got[s][1], ref[s][1]), (s, "lse")
+
+
+@pytest.mark.parametrize("mode", ["mapped", "copy"])
+def test_host_pool_matches_hbm_pool(dkb, mode):
+    """The host-pool path and the HBM-pool path run the same union in the same
+    order with the same splits; only the addresses differ (hot-cache slots against
+    pool chunks), so out and lse must be bit-identical at every step and layer."""
+    from sparse_kv_retrieval_amd.host_pool import HostPoolDecoder
+    w = shrink(WORKLOADS["host_b32_l128k"], B=2, L=8192, layers=2)
+    steps = 3
+    qseq, K, V, lm, sh = host_pool_setup(dkb, w, steps, seed=11)
+    dec = HostPoolDecoder(K.cpu().pin_memory(), V.cpu().pin_memory(), lm, sh, T=w.T, Hq=w.Hq, k=w.k,
+                          scale=w.scale, layers=w.layers, mode=mode)
+    host = host_pool_outputs(dec, qseq, steps)
+    for s in range(steps):
+        for l in range(w.layers):
+            q = qseq[l][s]
+            _, _, uid, mem, cnt, _ = dkb.score_topk_union(q, lm, w.k, w.scale, shadow=sh)
+            out, lse = dkb.sparse_decode_attn(q, K, V, uid, mem, cnt, w.chunk, w.scale)
+            torch.cuda.synchronize()
+            assert torch.equal(out, host[s][0][l]), (s, l, "out")
+            assert torch.equal(lse, host[s][1][l]), (s, l, "lse")
+
+
+@pytest.mark.parametrize("name,B,L,kw", [
+    ("llama8b_l32k", 2, 8192, {}),          # bf16, d 128, G 4: the fast kernel for T = 2
+    ("tiny", 2, None, {}),                  # fp32 generic kernel
+])
+def test_queries_are_independent(dkb, name, B, L, kw):
+    """Each query attends over its own chunks only (DHiSparse Fig. 3 (2)): the
+    two-query step must give each query the result of a one-query step on its own
+    (selection bit-exact, attention within the bar)."""
+    w = workload(name, B, L, **kw)
+    q, K, V = make(w, 81)
+    lm = dkb.build_landmarks(K, w.chunk)
+    sh = dkb.build_landmark_shadow(lm)
+    idx2, _, uid, mem, cnt, _ = dkb.score_topk_union(q, lm, w.k, w.scale, shadow=sh)
+    out2, lse2 = dkb.sparse_decode_attn(q, K, V, uid, mem, cnt, w.chunk, w.scale)
+    tol = ATOL[w.kv_dtype]
+    for t in range(2):
+        qt = q[:, t:t + 1].contiguous()
+        idx1, _, uid1, mem1, cnt1, _ = dkb.score_topk_union(qt, lm, w.k, w.scale, shadow=sh)
+        out1, lse1 = dkb.sparse_decode_attn(qt, K, V, uid1, mem1, cnt1, w.chunk, w.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(idx1[:, :, 0], idx2[:, :, t]), t
+        e1 = max_abs(out1[:, 0].cpu().numpy(), out2[:, t].cpu().numpy())
+        e2 = max_abs(lse1[:, 0].cpu().numpy(), lse2[:, t].cpu().numpy())
+        print(f"query {t}: max|out diff| {e1:.3e}  max|lse diff| {e2:.3e}")
+        assert e1 <= tol and e2 <= tol, (t, e1, e2)

@@ -61,6 +61,10 @@ def test_build_minmax(dkb, name, B, L, strided):
 
 def check_minmax_topk(dkb, w, q, K, reduce, union=False):
     mn, mx = dkb.build_minmax(K, w.chunk)
+    return check_minmax_summaries(dkb, w, q, mn, mx, reduce, union)
+
+
+def check_minmax_summaries(dkb, w, q, mn, mx, reduce, union=False):
     red = dkb.DK_REDUCE_MAX if reduce == "max" else dkb.DK_REDUCE_MEAN
     res = dkb.score_topk_minmax(q, mn, mx, w.k, w.scale, red, union=union)
     torch.cuda.synchronize()
@@ -107,6 +111,20 @@ def test_minmax_topk(dkb, name, B, L, reduce, union):
     q = synth.make_queries(w, 7, device="cuda")
     K, _ = synth.make_kv_pool(w, 7, device="cuda", q0=q)
     check_minmax_topk(dkb, w, q, K, reduce, union)
+
+
+def test_minmax_topk_long_scoring_blocks(dkb):
+    """512 (b, g) rows of 5000 chunks: the row-score kernel takes 4096-chunk blocks
+    and the second block of every row is short (904 chunks).  The summaries are
+    drawn directly (kmin <= kmax), no pool behind them."""
+    w = workload("llama8b_l32k", 64, 32 * 5000)
+    g = torch.Generator(device="cuda").manual_seed(13)
+    mn = torch.randn(w.B, w.Hkv, 5000, w.d, generator=g, device="cuda")
+    mx = (mn + torch.randn(w.B, w.Hkv, 5000, w.d, generator=g, device="cuda").abs()).to(torch.bfloat16)
+    mn = mn.to(torch.bfloat16)
+    mx = torch.maximum(mx, mn)
+    q = synth.make_queries(w, 13, device="cuda")
+    check_minmax_summaries(dkb, w, q, mn, mx, "mean", union=True)
 
 
 def test_minmax_topk_one_query(dkb):
