@@ -44,6 +44,10 @@ def parse():
     ap.add_argument("--layers", type=int, default=None, help="override the layer count")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU oracle sample budget (0 disables the CPU baseline)")
+    ap.add_argument("--flush-mb", type=int, default=None,
+                    help="write this many MiB between timed steps, outside the timed intervals, so the "
+                         "256 MB Infinity Cache does not serve a step's bytes from the step before "
+                         "(default: 1024 for one-layer workloads, whose working set fits that cache; 0 otherwise)")
     ap.add_argument("--no-events", action="store_true",
                     help="skip the second pass that times every call with events")
     ap.add_argument("--no-shadow", action="store_true",
@@ -54,6 +58,9 @@ def parse():
                     help="attend, besides the chunks, a per-request tail of up to this many rows "
                          "(lengths drawn in [tail/2, tail]) and the step's two fresh rows "
                          "(dk_sparse_decode_attn_tail)")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="only measure the card's read ceilings (register loads and the attention's LDS-DMA ring, "
+                         "contiguous and as random 8 KiB K/V chunk pairs) and the host-pool transfer paths")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB + 1 GiB device copy (dk_gather_kv over consecutive "
                          "chunks) three times: the known-size reference for HBM byte counters")
@@ -869,6 +876,86 @@ def cpu_baseline_mla(w, qi, q, Kidx, lat, gpu_topk, budget_s):
     return out
 
 
+def bench_ceiling(args):
+    """Read ceilings of the card in the attention's geometry (1536 blocks of 256
+    threads, 24 tiles of 16 KiB each: 604 MB), with the probe library, and the
+    rate of three ways to move scattered 8 KiB chunks from pinned host memory."""
+    import ctypes
+    import numpy as np
+    import torch
+    from sparse_kv_retrieval_amd import binding as dkb
+
+    path = os.path.join(ROOT, "sparse_kv_retrieval_amd", "libdkprobe.so")
+    if not os.path.exists(path):
+        raise SystemExit("libdkprobe.so is not built (python -m sparse_kv_retrieval_amd.build)")
+    probe = ctypes.CDLL(path)
+    probe.dkp_read_pass.restype = ctypes.c_int
+    probe.dkp_read_pass.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                    ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    nch = 1 << 19                                      # 8 KiB chunks per array: 4 GiB each
+    K = torch.ones(nch * 4096, dtype=torch.bfloat16, device="cuda")
+    V = torch.ones(nch * 4096, dtype=torch.bfloat16, device="cuda")
+    blocks, tpb = 1536, 24
+    ntile = blocks * tpb
+    g = torch.Generator(device="cuda")
+    g.manual_seed(args.seed)
+    ids = torch.randint(0, nch, (ntile,), generator=g, device="cuda", dtype=torch.int64)
+    sink = torch.zeros(blocks, dtype=torch.int32, device="cuda")
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    res = {}
+    for mode, mname in ((0, "register_loads"), (1, "lds_dma_ring")):
+        for gather in (False, True):
+            best = float("inf")
+            for r in range(7):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                rc = probe.dkp_read_pass(mode, ctypes.c_void_p(K.data_ptr()), ctypes.c_void_p(V.data_ptr()),
+                                         ctypes.c_void_p(ids.data_ptr()) if gather else None, blocks, tpb,
+                                         ctypes.c_void_p(sink.data_ptr()), st)
+                b.record()
+                b.synchronize()
+                if rc != 0:
+                    raise SystemExit(f"dkp_read_pass failed: {rc}")
+                if r:
+                    best = min(best, a.elapsed_time(b))
+            res[f"{mname}_{'gather_8KiB' if gather else 'contiguous'}"] = {
+                "us": round(best * 1e3, 1), "GBps": round(ntile * 16384 / (best * 1e-3) / 1e9, 1)}
+    del K, V
+    torch.cuda.empty_cache()
+    # scattered 8 KiB chunks of a pinned host pool into an HBM cache: 64 (b, g) of
+    # 1024 chunks each, 78 missed chunks per (b, g) (4992 in all)
+    B_, H_, per, chunk, d = 8, 8, 78, 32, 128
+    Ch = 1024
+    Kh = torch.ones(B_, H_, Ch * chunk, d, dtype=torch.bfloat16, pin_memory=True)
+    Vh = torch.ones(B_, H_, Ch * chunk, d, dtype=torch.bfloat16, pin_memory=True)
+    Kd = torch.empty(B_, H_, per * chunk, d, dtype=torch.bfloat16, device="cuda")
+    Vd = torch.empty_like(Kd)
+    rng = np.random.default_rng(args.seed)
+    src = torch.from_numpy(np.stack([np.sort(rng.choice(Ch, per, replace=False)) for _ in range(B_ * H_)])
+                           .astype(np.int32)).reshape(B_, H_, per)
+    host_src = src.pin_memory()
+    dev_src = src.cuda()
+    n = B_ * H_ * per
+    nbytes = 2 * n * chunk * d * 2
+    host = {}
+    for name, fn in (("hipMemcpyAsync_per_chunk", lambda: dkb.gather_kv(Kh, Vh, host_src, None, chunk, Kd, Vd)),
+                     ("mapped_gather_kernel", lambda: dkb.gather_kv(Kh, Vh, dev_src, None, chunk, Kd, Vd)),
+                     ("one_contiguous_copy", lambda: (Kd.view(-1).copy_(Kh.view(-1)[:Kd.numel()], non_blocking=True),
+                                                      Vd.view(-1).copy_(Vh.view(-1)[:Vd.numel()], non_blocking=True)))):
+        best = float("inf")
+        for r in range(4):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            if r:
+                best = min(best, time.perf_counter() - t0)
+        host[name] = {"ms": round(best * 1e3, 3), "GBps": round(nbytes / best / 1e9, 2)}
+    print(json.dumps({"ceiling": "read", "geometry": f"{blocks} blocks x {tpb} tiles of 16 KiB ({ntile * 16384} B)",
+                      "device_read": res,
+                      "host_pool_scattered_chunks": {"chunks": n, "bytes": nbytes, **host}}), flush=True)
+
+
 def calibrate_copy():
     """Three plain copies of 512 MiB K + 512 MiB V (1 GiB read, 1 GiB written each)."""
     import torch
@@ -895,7 +982,7 @@ def main():
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the decode step has no "
               "cross-GPU exchange and this benchmark measures a single MI355X.", file=sys.stderr)
         sys.exit(2)
-    if args.cpu_seconds > 0 and not args.calibrate_copy:
+    if args.cpu_seconds > 0 and not args.calibrate_copy and not args.ceiling:
         start_cpu_pool()          # forked before anything touches the GPU
     try:
         run(args)
@@ -925,6 +1012,9 @@ def run(args):
     torch.cuda.set_device(0)
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.ceiling:
+        bench_ceiling(args)
         return
     if w.host_pool:
         bench_host_pool(args, w)
@@ -997,19 +1087,39 @@ def run(args):
             if e:
                 e[2].record()
 
+    flush_mb = args.flush_mb if args.flush_mb is not None else (1024 if w.layers == 1 else 0)
+    flush_buf = torch.empty(flush_mb << 20, dtype=torch.uint8, device=dev) if flush_mb else None
+
+    def flush():
+        if flush_buf is not None:
+            flush_buf.fill_(1)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     # The headline: K steps with nothing between the calls but one event at each
-    # step boundary.
-    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    bounds[0].record()
-    for s in range(args.steps):
-        step()
-        bounds[s + 1].record()
-    torch.cuda.synchronize()
-    step_ms = [bounds[s].elapsed_time(bounds[s + 1]) for s in range(args.steps)]
-    total_ms = bounds[0].elapsed_time(bounds[-1])
+    # step boundary (with a cache flush, each step between its own pair of events,
+    # the flush outside them).
+    if flush_buf is None:
+        bounds = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        bounds[0].record()
+        for s in range(args.steps):
+            step()
+            bounds[s + 1].record()
+        torch.cuda.synchronize()
+        step_ms = [bounds[s].elapsed_time(bounds[s + 1]) for s in range(args.steps)]
+        total_ms = bounds[0].elapsed_time(bounds[-1])
+    else:
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(args.steps)]
+        for s in range(args.steps):
+            flush()
+            pairs[s][0].record()
+            step()
+            pairs[s][1].record()
+        torch.cuda.synchronize()
+        step_ms = [a.elapsed_time(b) for a, b in pairs]
+        total_ms = sum(step_ms)
     ms_per_step = total_ms / args.steps
     # Call durations: the same K steps again, with events around every call (on the
     # launch stream), read only afterwards.
@@ -1018,13 +1128,15 @@ def run(args):
         ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(w.layers)]
               for _ in range(args.steps)]
         for s in range(args.steps):
+            flush()
             step(ev[s])
         torch.cuda.synchronize()
         for s in range(args.steps):
             for l in range(w.layers):
                 for i, c in enumerate(calls):
                     call_ms[c] += ev[s][l][i].elapsed_time(ev[s][l][i + 1])
-        call_pass_ms = ev[0][0][0].elapsed_time(ev[args.steps - 1][w.layers - 1][len(calls)]) / args.steps
+        call_pass_ms = sum(ev[s][0][0].elapsed_time(ev[s][w.layers - 1][len(calls)])
+                           for s in range(args.steps)) / args.steps
     steps_per_s = 1000.0 / ms_per_step
 
     kernels = {}
@@ -1068,7 +1180,8 @@ def run(args):
                     "traffic": None if traffic is None else int(traffic)}
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC if w.name == "b64_l128k" else
+        f"dual-query sparse decode steps/s + selected-KV GB/s (% HBM peak), B={w.B} L={w.L}, {w.layers} layer(s)",
         "value": round(steps_per_s, 3),
         "unit": "steps/s",
         "n_gpus": 1,
@@ -1078,11 +1191,12 @@ def run(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if w.kv_dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "L": w.L, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d,
                    "chunk": w.chunk, "k": w.k, "T": w.T, "layers": w.layers, "seed": args.seed,
-                   "landmark_shadow": shadow is not None, "tail_max": args.tail},
+                   "landmark_shadow": shadow is not None, "tail_max": args.tail,
+                   "cache_flush_MiB_between_steps": flush_mb},
         "ms_per_step_median": round(float(np.median(step_ms)), 4),
         "ms_per_step_min": round(float(np.min(step_ms)), 4),
         "timing": "value and ms_per_step: event-free steps (one event per step boundary); kernels and "

@@ -72,12 +72,25 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     return LIB
 
 
+PROBE_SRC = os.path.join(PKG, "probe", "read_ceiling.hip")
+PROBE_LIB = os.path.join(PKG, "libdkprobe.so")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """The read-ceiling probe library bench.py --ceiling loads (not part of libdualkv)."""
+    tmp_lib = PROBE_LIB + ".tmp"
+    _run([hipcc(), *HIP_FLAGS, "-shared", PROBE_SRC, "-o", tmp_lib], verbose)
+    os.replace(tmp_lib, PROBE_LIB)
+    return PROBE_LIB
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--jobs", type=int, default=None)
     ap.add_argument("--verbose", action="store_true")
     a = ap.parse_args(argv)
     print(build(a.jobs, a.verbose))
+    print(build_probe(a.verbose))
 
 
 if __name__ == "__main__":

@@ -643,26 +643,44 @@ __global__ __launch_bounds__(kThreads) void k_attn_tail(AttnArgs a) {
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_attn_merge(AttnArgs a) {
+    constexpr int P = 8;   // partials read per batch: their loads are in flight together
     const int bg = blockIdx.x;
     const int b = bg / a.Hkv, g = bg - b * a.Hkv;
     const int R = a.G * a.T;
     constexpr int D4 = D / 4;
     for (int i = threadIdx.x; i < R * D4; i += kThreads) {
         const int r = i / D4, d4 = i - r * D4;
+        const int64_t slot0 = (int64_t)bg * a.nparts * R + r;   // partial s of row r: slot0 + s * R
         float M = -INFINITY;
-        for (int s = 0; s < a.nparts; ++s)
-            M = fmaxf(M, a.part_ml[(((int64_t)bg * a.nparts + s) * R + r) * 2]);
+        for (int s0 = 0; s0 < a.nparts; s0 += P) {
+            float m[P];
+#pragma unroll
+            for (int j = 0; j < P; ++j)
+                m[j] = s0 + j < a.nparts ? a.part_ml[(slot0 + (int64_t)(s0 + j) * R) * 2] : -INFINITY;
+#pragma unroll
+            for (int j = 0; j < P; ++j) M = fmaxf(M, m[j]);
+        }
         float L = 0.f;
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
         if (M != -INFINITY) {
-            for (int s = 0; s < a.nparts; ++s) {
-                const int64_t slot = ((int64_t)bg * a.nparts + s) * R + r;
-                const float ms = a.part_ml[slot * 2];
-                if (ms == -INFINITY) continue;
-                const float f = exp2f(ms - M);
-                L += a.part_ml[slot * 2 + 1] * f;
-                const float4 x = *reinterpret_cast<const float4*>(a.part_acc + slot * D + d4 * 4);
-                acc.x += x.x * f; acc.y += x.y * f; acc.z += x.z * f; acc.w += x.w * f;
+            for (int s0 = 0; s0 < a.nparts; s0 += P) {
+                float2 ml[P];
+                float4 x[P];
+#pragma unroll
+                for (int j = 0; j < P; ++j) {
+                    const int64_t slot = slot0 + (int64_t)(s0 + j) * R;
+                    const bool in = s0 + j < a.nparts;
+                    ml[j] = in ? *reinterpret_cast<const float2*>(a.part_ml + slot * 2) : make_float2(-INFINITY, 0.f);
+                    x[j] = in ? *reinterpret_cast<const float4*>(a.part_acc + slot * D + d4 * 4)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+#pragma unroll
+                for (int j = 0; j < P; ++j) {
+                    if (ml[j].x == -INFINITY) continue;
+                    const float f = exp2f(ml[j].x - M);
+                    L += ml[j].y * f;
+                    acc.x += x[j].x * f; acc.y += x[j].y * f; acc.z += x[j].z * f; acc.w += x[j].w * f;
+                }
             }
         }
         const int t = r / a.G, hh = r - t * a.G;
@@ -687,10 +705,13 @@ AttnPlan plan_attn(int B, int Hkv, int T, int Hq, int dv, int N, int chunk, bool
     const int64_t bg = (int64_t)B * Hkv;
     const int R = (Hq / Hkv) * T;
     const int64_t tiles = (int64_t)N * ((chunk + 31) / 32);
-    // about two rounds of three resident blocks per CU, at least ~6 tiles per
-    // range, and never more entries per range than the fast path stages in LDS
+    // about two rounds of three resident blocks per CU; for long unions at least
+    // ~20 tiles of a full union per range (about 11 at the usual half-full union:
+    // shorter ranges spend more on their prologue and on the merge than they gain
+    // in parallelism), for short ones (latency-bound) at least ~6; never more
+    // entries per range than the fast path stages in LDS
     int64_t want = (1536 + bg - 1) / bg;
-    int64_t by_work = tiles / 6;
+    int64_t by_work = tiles >= 120 ? tiles / 20 : tiles / 6;
     if (by_work < 1) by_work = 1;
     int64_t s = want < by_work ? want : by_work;
     const int64_t min_s = (N + kFastMaxEntries - 1) / kFastMaxEntries;

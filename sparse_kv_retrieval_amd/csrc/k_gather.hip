@@ -51,14 +51,20 @@ __global__ __launch_bounds__(256) void k_gather(const char* __restrict__ Ks,
     }
 }
 
-// One wave per block, one block per CU: the link needs only a few hundred KB in
-// flight, and every lane that waits on PCIe also holds part of its CU's memory
-// pipeline, which concurrently running HBM kernels on that CU then wait behind.
-// Thin (one wave, four 16-byte loads per lane) slows a concurrent HBM stream by
-// about a quarter; 128 blocks of four waves with eight loads per lane, by half.
-constexpr int kStreamThreads = 64;
-constexpr int kStreamBlocks = 256;
-constexpr int kStreamUnroll = 2;     // K and V loads in flight per lane: 2 x kStreamUnroll
+// Few blocks, many loads in flight: 32 blocks of 256 threads (one per CU on 32
+// of the 256 CUs), four K and four V 16-byte loads in flight per lane (1 MiB in
+// all; the link needs a few hundred KB).  Every lane that waits on PCIe holds
+// part of its CU's memory pipeline, and HBM kernels running on that CU at the
+// same time wait behind it, so the gather is kept off most CUs.  Measured on
+// the host-pool step (per-layer hot caches, B=32, L=128K, 32 layers): one
+// wave on every CU gave 16.4 ms per step (hot-cache attention about 480 us per
+// layer under the gather, the gather at 49.9 GB/s); this form 15.4 ms
+// (attention about 210-235 us, the gather at 53.7 GB/s).  16, 24 and 48 blocks,
+// two or eight loads per lane, 128 or 512 threads, 8 blocks of 1024 threads
+// were all between 15.4 and 16.0 ms.
+constexpr int kStreamThreads = 256;
+constexpr int kStreamBlocks = 32;
+constexpr int kStreamUnroll = 4;     // K and V loads in flight per lane: 2 x kStreamUnroll
 
 __global__ __launch_bounds__(kStreamThreads) void k_gather_stream(
     const char* __restrict__ Ks, const char* __restrict__ Vs, dk_strides ss, int Hkv, int chunk,
