@@ -13,25 +13,27 @@
 // latent row: the product is a dense GEMM (about 480 flop per byte of latent
 // row), so it runs on v_mfma_f32_16x16x32_bf16.
 //
-// Block (512 threads, 8 waves): 64 query rows = HB heads x T tokens (HB = 64/T)
-// of one (b, g), over one contiguous range of its union entries, 32 tokens per
-// tile.
-//   * the range's union entries are staged in LDS first, then tiles of 32
-//     latent rows (36 KiB) go global -> LDS by DMA into a three-stage ring (two
-//     tiles in flight while one is used); each LDS row is padded by 16 bytes
-//     (1168-byte stride: eight consecutive rows start on distinct bank groups)
-//     and its 16-byte pieces are XOR-permuted by 2 * ((row / 8) mod 4), so the
-//     key reads (16 bytes per lane, eight consecutive rows) and the value reads
-//     (2 bytes per lane, four groups of rows eight apart) hit distinct banks, and
-//     every read is a per-lane base plus immediate offsets;
-//   * S = Q K^T: wave w owns row tile w % 4 (16 rows of one query token) and
-//     token half w / 4, Q in registers as bf16 A operands, K pieces from LDS as
-//     B operands, 18 k-steps;
-//   * online softmax in log2 units per row (mask: the token is in the row's own
-//     set), the row maximum shared between the two token halves through LDS,
-//     weights rounded to bf16 into LDS;
-//   * O += P V: wave w owns value columns 64w..64w+63 for all 64 rows, P rows
-//     from LDS as A operands, value columns gathered from the same LDS tile.
+// Block (512 threads, 8 waves, two per SIMD): 64 query rows = HB heads x T
+// tokens (HB = 64/T) of one (b, g), over one contiguous range of its union
+// entries, 32 tokens per tile.  Each SIMD runs one wave of each role, so one
+// wave's LDS and DMA waits are covered by the other's matrix work:
+//   * S waves (0..3), 16 query rows of one token each: S^T = K Q^T for all 32
+//     tokens of the tile (K pieces from LDS as A operands, Q in registers as B
+//     operands, 18 k-steps, two token tiles), then the online softmax per row
+//     in log2 units inside the wave (a row's 32 weights sit in its 4 lanes) with
+//     a lazy running maximum; the weights, rounded to bf16, already have the
+//     layout of the B operand of the value product and go to LDS with the
+//     per-row rescale factor;
+//   * O waves (4..7), value columns 128(w-4) .. +127 of all 64 rows:
+//     O^T += V^T P^T with V^T operands from ds_read_b64_tr_b16 (4 tokens x 1
+//     column per lane and read, in the weights' token order); they also issue
+//     the tile DMAs and the ids DMA.
+//   * S of tile i + 1 and O of tile i run in one barrier interval.
+// Tiles of 32 latent rows go global -> LDS by DMA into a four-stage ring; an LDS
+// row is 1184 bytes (72 pieces + 2 pad), which keeps the key reads (16 lanes =
+// 16 rows, one piece) at the full ds_read_b128 rate.  The tile's token ids
+// arrive by a dword DMA a tile ahead of its rows, so the only vector-memory
+// operations in the loop are DMAs and the wait counts are exact.
 // Ranges of one (b, g) are combined by k_mla_merge.  The four row groups of a
 // (b, g, range) share an XCD (block id mod 8) so that the other three find the
 // tiles in L2.
@@ -41,34 +43,40 @@ namespace dk {
 namespace {
 
 constexpr int kMlaThreads = 512;
-constexpr int kMlaWaves = kMlaThreads / 64;
-constexpr int kMlaRows = 64;              // query rows per block
+constexpr int kMlaRows = 64;              // query rows per block: 16 per S wave
 constexpr int kMlaDk = 576, kMlaDv = 512;
 constexpr int kMlaTok = 32;               // tokens per tile
 constexpr int kMlaPieces = kMlaDk / 8;    // 16-byte pieces per latent row (72)
-constexpr int kMlaRowPieces = kMlaPieces + 1;   // LDS row: 72 pieces + one pad (1168 bytes)
-constexpr int kMlaRowBytes = kMlaRowPieces * 16;
-constexpr int kMlaDmaTotal = (kMlaTok * kMlaRowPieces + 63) / 64;       // 37 per tile
-constexpr int kMlaTilePieces = kMlaDmaTotal * 64;                       // ring stage, DMA overrun included
-constexpr int kMlaDmaMax = (kMlaDmaTotal + kMlaWaves - 1) / kMlaWaves;   // 5 (waves 0-4), else 4
-constexpr int kMlaStages = 3;             // LDS ring: two tiles in flight while one is used
-constexpr int kMlaMaxRange = 2048;        // union entries per block (ids staged in LDS)
-constexpr int kPRow = 40;                 // bf16 per row of the P tile (80 bytes)
+constexpr int kMlaRowPieces = kMlaPieces + 2;                            // LDS row with its pad (74)
+constexpr int kMlaRowBytes = 16 * kMlaRowPieces;                         // 1184
+constexpr int kMlaTileBytes = kMlaTok * kMlaRowBytes;                    // 37,888
+constexpr int kMlaDmaTotal = kMlaTok * kMlaRowPieces / 64;               // 37 per tile
+constexpr int kMlaDmaMax = (kMlaDmaTotal + 3) / 4;                       // O wave 0: 10, others 9
+constexpr int kMlaStages = 4;             // tile i in O, i + 1 in S, i + 2 and i + 3 in flight
+constexpr int kMlaMaxRange = 2048;        // union entries per block (member bits staged in LDS)
+constexpr int kMlaColTiles = kMlaDv / 16 / 4;                            // 8 value column tiles per O wave
 constexpr float kMlaSlack = 8.f;          // log2 headroom of the lazy running maximum
 
+static_assert(kMlaDmaTotal * 64 == kMlaTok * kMlaRowPieces, "a tile is a whole number of DMAs");
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
 struct __align__(16) MlaSmem {
-    uint4 tile[kMlaStages][kMlaTilePieces];   // latent rows, 73 pieces each (the last a pad)
-    int32_t ids[kMlaMaxRange];             // the range's token ids (0 when invalid)
-    uint8_t mem[kMlaMaxRange];             // and their member bits (0 when invalid)
-    uint16_t p[kMlaRows * kPRow];          // bf16 weights [row][token]
-    float alpha[kMlaRows];                 // per-row rescale of this tile
-    float hmax[2][kMlaRows];               // tile maximum of each token half
-    float row_m[kMlaRows];
-    float row_l[2][kMlaRows];
-    int flag[kMlaWaves];
+    uint4 tile[kMlaStages][kMlaTileBytes / 16];
+    uint4 p[2][4][4][16];                  // [buffer][row tile][lane group][row]: 8 bf16 weights
+    float alpha[2][kMlaRows];              // per-row rescale of the tile's weights
+    int flag[2][4];                        // some row of the row tile rescaled
+    union {
+        int32_t idr[kMlaStages][64];       // token ids of a tile (lanes 32..63 repeat them)
+        struct {
+            float row_m[kMlaRows];         // after the loop: row statistics
+            float row_l[kMlaRows];
+        } st;
+    } u;
+    uint8_t mem[kMlaMaxRange];             // member bits of the range (0: invalid entry)
 };
 
 // LDS DMA that keeps the lines in L2 (the other row groups read the same tile)
@@ -76,8 +84,10 @@ __device__ __forceinline__ void lds_dma16_keep(const void* g, uint32_t lds_base)
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  :: "v"(g), "s"(lds_base) : "memory", "m0");
 }
-// piece permutation of LDS row j: global piece p sits at position p ^ mla_swz(j)
-__device__ __forceinline__ int mla_swz(int j) { return 2 * ((j >> 3) & 3); }
+__device__ __forceinline__ void lds_dma4_keep(const void* g, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                 :: "v"(g), "s"(lds_base) : "memory", "m0");
+}
 
 template <int N>
 __device__ __forceinline__ void vm_wait() {
@@ -88,17 +98,26 @@ __device__ __forceinline__ void lds_barrier() {
     raw_barrier();
 }
 
-__device__ __forceinline__ float dpp_group_max16(float v) {
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false)));
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false)));
-    return v;
+// max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (v_permlane16/32_swap:
+// with both operands equal, the two results hold the values of the lane pair)
+__device__ __forceinline__ float group4_max(float v) {
+    auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
-
+__device__ __forceinline__ float group4_sum(float v) {
+    auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
 __device__ __forceinline__ f32x4_t mfma16(const uint4& a, const uint4& b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ uint2 lds_read_tr(const char* p) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p)));
 }
 
 struct MlaArgs {
@@ -120,9 +139,9 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_attn(MlaArgs a) {
     __shared__ MlaSmem sm;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // S phase: wave w owns row tile mw (rows 16mw .. 16mw+15) and token half nw;
-    // O phase: value columns 64w .. 64w+63 of all 64 rows
-    const int mw = w & 3, nw = w >> 2;
+    const bool s_wave = w < 4;
+    const int wr = w & 3;                     // row tile (S wave) or column quarter (O wave)
+    const int lr = lane & 15, lg = lane >> 4;
     // block -> (work item f, row group rg); the row groups of f share blockIdx mod 8
     const int blk = blockIdx.x;
     const int f = (blk / (8 * a.rgroups)) * 8 + (blk % 8);
@@ -132,283 +151,295 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_attn(MlaArgs a) {
     const int bg = f / a.splits;
     const int b = bg / a.Hkv, g = bg - b * a.Hkv;
     const int T = a.T, HB = kMlaRows / T, G = a.Hq / a.Hkv;
-    const int t_w = (16 * mw) / HB;                           // query token of row tile mw
-    const int h_lane = g * G + rg * HB + (16 * mw) % HB + (lane & 15);   // head of row lane%16
 
     // entries of this range
-    const int cnt = max(0, min(a.count[bg], a.N));
+    const int cnt = __builtin_amdgcn_readfirstlane(max(0, min(a.count[bg], a.N)));
     const int per = (cnt + a.splits - 1) / a.splits;
     const int u0 = min(cnt, split * per);
     const int u1 = min(min(cnt, u0 + per), u0 + kMlaMaxRange);   // the plan keeps per <= kMlaMaxRange
-    const int ntiles = (u1 - u0 + kMlaTok - 1) / kMlaTok;
-    const int32_t* ids = a.ids + (int64_t)bg * a.N;
-    const uint8_t* mem = a.member ? a.member + (int64_t)bg * a.N : nullptr;
+    const int n_ent = u1 - u0;
+    const int ntiles = (n_ent + kMlaTok - 1) / kMlaTok;
+    const int32_t* ids = a.ids + (int64_t)bg * a.N + u0;
+    const uint8_t* mem = a.member ? a.member + (int64_t)bg * a.N + u0 : nullptr;
     const char* lat_bg = (const char*)(a.lat + (int64_t)b * a.ks.b + (int64_t)g * a.ks.h);
     const int64_t row_bytes = a.ks.t * 2;
+    const int L = a.L;
 
-    // the tile's 37 DMA instructions: wave w issues i = w, w + 8, ... (< 37); the
-    // (row, global piece) of each of this lane's slots is the same for every tile
-    const int n_ent = u1 - u0;
-    int slot[kMlaDmaMax];                            // row << 16 | byte offset in the row, or -1
+    // ---- O waves: tile DMAs.  DMA i of a tile lands LDS pieces 64i .. 64i + 63:
+    // row pos / 74, piece pos % 74 (72, 73: the pad, loaded from the row start);
+    // O wave wr issues i = wr, wr + 4, ...
+    int dsel[kMlaDmaMax];                     // row << 16 | byte offset in the row
 #pragma unroll
     for (int c = 0; c < kMlaDmaMax; ++c) {
-        const int pos = 64 * (w + kMlaWaves * c) + lane;
+        const int pos = 64 * (wr + 4 * c) + lane;
         const int j = pos / kMlaRowPieces, qp = pos - j * kMlaRowPieces;
-        slot[c] = (qp < kMlaPieces && j < kMlaTok) ? (j << 16) | (16 * (qp ^ mla_swz(j))) : -1;
+        dsel[c] = (min(j, kMlaTok - 1) << 16) | (qp < kMlaPieces ? 16 * qp : 0);
     }
-    // source of slot c of a tile (pad slot, past the tile or past the range: row 0)
-    auto dma_src = [&](int tile, int c) {
-        int id = 0, off = 0;
-        if (slot[c] >= 0) {
-            const int e = tile * kMlaTok + (slot[c] >> 16);
-            if (e < n_ent) {
-                id = sm.ids[e];
-                off = slot[c] & 0xffff;
-            }
-        }
-        return lat_bg + (int64_t)id * row_bytes + off;
+    // the token ids of tile x into u.idr[x % 4] (O wave 0; entries past the range
+    // repeat the last one, and the rows' member bits mask them out)
+    auto issue_ids = [&](int x) {
+        if (w == 4)
+            lds_dma4_keep(ids + min(x * kMlaTok + (lane & (kMlaTok - 1)), n_ent - 1),
+                          lds_addr(&sm.u.idr[x % kMlaStages][0]));
     };
-    auto issue_slot = [&](int tile, int stage, int c) {
-        const int i = w + kMlaWaves * c;             // DMA instruction (wave-uniform)
-        if (i < kMlaDmaTotal) lds_dma16_keep(dma_src(tile, c), lds_addr(&sm.tile[stage][0]) + 1024u * (uint32_t)i);
+    // rows of tile x: ids from LDS (invalid ids read row 0, masked out by their bits)
+    auto issue_tile = [&](int x, int stage) {
+        int id[kMlaDmaMax];
+#pragma unroll
+        for (int c = 0; c < kMlaDmaMax; ++c) id[c] = sm.u.idr[x % kMlaStages][dsel[c] >> 16];
+#pragma unroll
+        for (int c = 0; c < kMlaDmaMax; ++c) {
+            const int i = wr + 4 * c;
+            if (i < kMlaDmaTotal) {
+                const int v = (id[c] < 0 || id[c] >= L) ? 0 : id[c];
+                lds_dma16_keep(lat_bg + (int64_t)v * row_bytes + (dsel[c] & 0xffff),
+                               lds_addr(&sm.tile[stage][0]) + 1024u * (uint32_t)i);
+            }
+        }
     };
-    auto issue_tile = [&](int tile, int stage) {
+    // ---- prologue: ids of tiles 0..3, member bits and the queries in flight
+    // together, then tiles 0..2
+    if (!s_wave) {
 #pragma unroll
-        for (int c = 0; c < kMlaDmaMax; ++c) issue_slot(tile, stage, c);
-    };
-    // DMAs per tile of this wave (the wait counts below)
-    const bool dma5 = w < kMlaDmaTotal - kMlaWaves * (kMlaDmaMax - 1);
-
-    // ---- prologue: the range's entries into LDS, the queries, tiles 0 and 1
-    for (int x = tid; x < n_ent; x += kMlaThreads) {
-        int v = ids[u0 + x];
-        int m = mem ? (int)mem[u0 + x] : 0xff;
-        if (v < 0 || v >= a.L) {
-            v = 0;
-            m = 0;
-        }
-        sm.ids[x] = v;
-        sm.mem[x] = (uint8_t)m;
+        for (int x = 0; x < 4; ++x)
+            if (x < ntiles) issue_ids(x);
     }
-    uint4 qa[18];
-    {
-        const float* qrow = a.q + (((int64_t)b * T + t_w) * a.Hq + h_lane) * kMlaDk + 8 * (lane >> 4);
+    constexpr int kStage = kMlaMaxRange / kMlaThreads;   // entries per thread
+    int sv[kStage], sb[kStage];
 #pragma unroll
-        for (int s = 0; s < 18; ++s) {
-            const float4 x0 = *reinterpret_cast<const float4*>(qrow + 32 * s);
-            const float4 x1 = *reinterpret_cast<const float4*>(qrow + 32 * s + 4);
-            qa[s] = make_uint4(pack_bf16x2(x0.x, x0.y), pack_bf16x2(x0.z, x0.w), pack_bf16x2(x1.x, x1.y),
-                               pack_bf16x2(x1.z, x1.w));
-        }
-    }
-    __syncthreads();                                  // entries staged, every earlier load complete
-    if (ntiles > 0) issue_tile(0, 0);
-    if (ntiles > 1) issue_tile(1, 1);
-
-    float m_run[4], l_half[4];
-    f32x4_t acc[4][4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        m_run[e] = -INFINITY;
-        l_half[e] = 0.f;
+    for (int i = 0; i < kStage; ++i) {
+        const int x = min(tid + kMlaThreads * i, max(n_ent - 1, 0));
+        sv[i] = n_ent > 0 ? ids[x] : 0;
+        sb[i] = mem && n_ent > 0 ? (int)mem[x] : 0xff;
     }
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int n = 0; n < 4; ++n) acc[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const int jt = 16 * nw + (lane & 15);        // this lane's token in the S phase
-
-    // The loop issues no vector-memory operation but the tile DMAs, so the wait
-    // counts are exact: at the top of iteration it the DMAs of tiles it and it + 1
-    // may be outstanding, and tile it is complete once only tile it + 1's remain.
-    // Tile it + 2 is issued during this iteration's S phase into the stage tile
-    // it - 1 used; the barrier below is the last point any wave read it, and it
-    // also orders this tile's P, flags and maxima after the previous tile's reads.
-    for (int it = 0; it < ntiles; ++it) {
-        const int stage = it % kMlaStages;
-        if (it + 1 < ntiles) {
-            if (dma5) vm_wait<kMlaDmaMax>();
-            else vm_wait<kMlaDmaMax - 1>();
-        } else {
-            vm_wait<0>();
-        }
-        lds_barrier();
-        const bool prefetch = it + 2 < ntiles;
-        const int nstage = (it + 2) % kMlaStages;
-        const uint4* tl = sm.tile[stage];
-
-        // ---- S = Q K^T for row tile mw and the 16 tokens of half nw
-        f32x4_t sacc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-        // key operands in groups of three k-steps, the next group loaded before
-        // the current one's products (at most six operands live)
-        // global piece 4s + lane/16 of row jt sits at (4s + lane/16) ^ x, x = mla_swz(jt):
-        // 4 (s ^ x/4) + (lane/16 ^ x%4), i.e. +4 pieces for even s and -4 for odd s when x >= 4
-        const int xs = mla_swz(jt);
-        const uint4* krow = tl + jt * kMlaRowPieces + ((lane >> 4) ^ (xs & 3));
-        const uint4* kev = krow + 4 * (xs >> 2);
-        const uint4* kod = krow - 4 * (xs >> 2);
-        uint4 kb[2][3];
-#pragma unroll
-        for (int u = 0; u < 3; ++u) kb[0][u] = ((u & 1) ? kod : kev)[4 * u];
-#pragma unroll
-        for (int gi = 0; gi < 6; ++gi) {
-            if (gi + 1 < 6) {
-#pragma unroll
-                for (int u = 0; u < 3; ++u) {
-                    const int st = 3 * (gi + 1) + u;
-                    kb[(gi + 1) & 1][u] = ((st & 1) ? kod : kev)[4 * st];
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int u = 0; u < 3; ++u) {
-                const int st = 3 * gi + u;
-                sacc[st & 3] = mfma16(qa[st], kb[gi & 1][u], sacc[st & 3]);
-            }
-            // one DMA of tile it + 2 per group, under the products
-            if (gi < kMlaDmaMax && prefetch) issue_slot(it + 2, nstage, gi);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // ---- mask and online softmax (log2 units) with a lazy running maximum:
-        // the weights use m_run as long as no logit of the row exceeds it by more
-        // than kMlaSlack (the result does not depend on the reference, and the
-        // weights stay below 2^kMlaSlack); otherwise the exact maximum over both
-        // token halves is exchanged and the row rescaled.  Each lane keeps its own
-        // token's share of the row sum, summed over the lanes once at the end.
-        const int et = it * kMlaTok + jt;
-        const bool valid = et < n_ent && ((sm.mem[et] >> t_w) & 1);
-        float z[4];
-        bool over = false;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            z[e] = valid ? ((sacc[0][e] + sacc[1][e]) + (sacc[2][e] + sacc[3][e])) * a.scale_log2 : -INFINITY;
-            over |= z[e] > m_run[e] + kMlaSlack;     // also any finite z while m_run is -inf
-        }
-        float l_prev[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = 16 * mw + 4 * (lane >> 4) + e;
-            l_prev[e] = l_half[e];
-            const float p = m_run[e] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[e] - m_run[e]);
-            const __bf16 pb = (__bf16)p;
-            l_half[e] += (float)pb;
-            sm.p[r * kPRow + jt] = __builtin_bit_cast(uint16_t, pb);
-        }
-        const uint64_t anyover = __ballot(over);
-        if (lane == 0) sm.flag[w] = anyover != 0;
-        lds_barrier();
-        bool rescale = false;
-#pragma unroll
-        for (int x = 0; x < kMlaWaves; ++x) rescale |= sm.flag[x] != 0;
-        if (rescale) {
-            // exact maximum of each row over both halves, then the weights again
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float hm = dpp_group_max16(z[e]);
-                if ((lane & 15) == 0) sm.hmax[nw][16 * mw + 4 * (lane >> 4) + e] = hm;
-            }
-            lds_barrier();
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * mw + 4 * (lane >> 4) + e;
-                const float mx = fmaxf(sm.hmax[0][r], sm.hmax[1][r]);
-                const float mn = fmaxf(m_run[e], mx);
-                float alpha = 1.f, p = 0.f;
-                if (mn != -INFINITY) {
-                    alpha = __builtin_amdgcn_exp2f(m_run[e] - mn);
-                    p = __builtin_amdgcn_exp2f(z[e] - mn);
-                }
-                const __bf16 pb = (__bf16)p;
-                l_half[e] = l_prev[e] * alpha + (float)pb;
-                m_run[e] = mn;
-                sm.p[r * kPRow + jt] = __builtin_bit_cast(uint16_t, pb);
-                if (nw == 0 && (lane & 15) == 0) sm.alpha[r] = alpha;
-            }
-            lds_barrier();
-        }
-
-        // ---- O += P V for value columns 64w .. 64w+63 of all 64 rows
-        if (rescale) {
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const float4 al = *reinterpret_cast<const float4*>(&sm.alpha[16 * m + 4 * (lane >> 4)]);
-#pragma unroll
-                for (int n = 0; n < 4; ++n) {
-                    acc[m][n][0] *= al.x;
-                    acc[m][n][1] *= al.y;
-                    acc[m][n][2] *= al.z;
-                    acc[m][n][3] *= al.w;
-                }
-            }
-        }
-        uint4 pa[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-            pa[m] = *reinterpret_cast<const uint4*>(&sm.p[(16 * m + (lane & 15)) * kPRow + 8 * (lane >> 4)]);
-        // value column c = 64w + 16n + lane%16 of token j = 8g + e (g = lane/16) sits in
-        // piece (c / 8) ^ 2g = 8w + 2 (n ^ g) + (lane%16) / 8 of LDS row j
-        const int gq = lane >> 4;
-        const uint16_t* vcol = reinterpret_cast<const uint16_t*>(tl) + 8 * gq * (kMlaRowBytes / 2) +
-                               8 * (8 * w + ((lane & 15) >> 3)) + (lane & 7);
-#pragma unroll
-        for (int n = 0; n < 4; ++n) {
-            const uint16_t* vn = vcol + 16 * (n ^ gq);
-            uint16_t v[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = vn[e * (kMlaRowBytes / 2)];
-            const uint4 vb = make_uint4(v[0] | ((uint32_t)v[1] << 16), v[2] | ((uint32_t)v[3] << 16),
-                                        v[4] | ((uint32_t)v[5] << 16), v[6] | ((uint32_t)v[7] << 16));
-#pragma unroll
-            for (int m = 0; m < 4; ++m) acc[m][n] = mfma16(pa[m], vb, acc[m][n]);
-        }
+    for (int i = 0; i < kStage; ++i) {
+        const int x = tid + kMlaThreads * i;
+        if (x < n_ent) sm.mem[x] = (uint8_t)((sv[i] < 0 || sv[i] >= L) ? 0 : sb[i]);
     }
-
-    // ---- row statistics to every wave, then this wave's columns of all rows
-#pragma unroll
-    for (int e = 0; e < 4; ++e) l_half[e] = dpp_group_sum<16>(l_half[e]);
-    if ((lane & 15) == 0) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = 16 * mw + 4 * (lane >> 4) + e;
-            if (nw == 0) sm.row_m[r] = m_run[e];
-            sm.row_l[nw][r] = l_half[e];
-        }
-    }
-    lds_barrier();
     constexpr float kLn2 = 0.69314718055994531f;
-    if (a.splits == 1) {
+
+    // The two roles run separate loops with the same sequence of barriers:
+    // (1) bits and the first ids staged, (2) tile 0 landed, one per iteration,
+    // (3) row statistics published.
+    if (s_wave) {
+        // ---- S wave: rows 16wr .. 16wr + 15 (one query token)
+        const int t_w = (16 * wr) / HB;
+        const int h_lane = g * G + rg * HB + (16 * wr) % HB + lr;   // head of row lane%16
+        uint4 qa[18];
+        {
+            const float* qrow = a.q + (((int64_t)b * T + t_w) * a.Hq + h_lane) * kMlaDk + 8 * lg;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * m + 4 * (lane >> 4) + e;
-                const int t = r / HB, h = g * G + rg * HB + r % HB;
-                const float l = sm.row_l[0][r] + sm.row_l[1][r];
-                const float inv = l > 0.f ? 1.f / l : 0.f;
-                float* orow = a.out + (((int64_t)b * T + t) * a.Hq + h) * kMlaDv + 64 * w + (lane & 15);
-#pragma unroll
-                for (int n = 0; n < 4; ++n) orow[16 * n] = acc[m][n][e] * inv;
-                if (a.lse && w == 0 && (lane & 15) == 0)
-                    a.lse[((int64_t)b * T + t) * a.Hq + h] = l > 0.f ? sm.row_m[r] * kLn2 + logf(l) : -INFINITY;
+            for (int s = 0; s < 18; ++s) {
+                const float4 x0 = *reinterpret_cast<const float4*>(qrow + 32 * s);
+                const float4 x1 = *reinterpret_cast<const float4*>(qrow + 32 * s + 4);
+                qa[s] = make_uint4(pack_bf16x2(x0.x, x0.y), pack_bf16x2(x0.z, x0.w), pack_bf16x2(x1.x, x1.y),
+                                   pack_bf16x2(x1.z, x1.w));
             }
         }
+        // key piece 4s + lg of row 16tt + lr
+        const int koff = lr * kMlaRowBytes + 16 * lg;
+        float m_run = -INFINITY, l_part = 0.f;
+        // S^T of tile x, mask, lazy-maximum softmax, weights to LDS
+        auto s_tile = [&](int x) {
+            const char* st = reinterpret_cast<const char*>(&sm.tile[x % kMlaStages][0]) + koff;
+            uint32_t mb[2];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+                mb[tt] = *reinterpret_cast<const uint32_t*>(&sm.mem[x * kMlaTok + 16 * tt + 4 * lg]);
+            f32x4_t sacc[2][2] = {{{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}},
+                                  {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}};
+            // groups of two k-steps x two token tiles; operands two groups ahead
+            uint4 kb[3][4];
+#pragma unroll
+            for (int gq = 0; gq < 2; ++gq)
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    kb[gq][u] = *reinterpret_cast<const uint4*>(st + 64 * (2 * gq + (u >> 1)) +
+                                                                (u & 1) * 16 * kMlaRowBytes);
+#pragma unroll
+            for (int gq = 0; gq < 9; ++gq) {
+                if (gq + 2 < 9) {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        kb[(gq + 2) % 3][u] = *reinterpret_cast<const uint4*>(
+                            st + 64 * (2 * (gq + 2) + (u >> 1)) + (u & 1) * 16 * kMlaRowBytes);
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int s = 2 * gq + (u >> 1), tt = u & 1;
+                    sacc[tt][s & 1] = mfma16(kb[gq % 3][u], qa[s], sacc[tt][s & 1]);
+                }
+            }
+            const int buf = x & 1;
+            float z[2][4];
+            float hm = -INFINITY;
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                const int e0 = x * kMlaTok + 16 * tt + 4 * lg;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t valid = (uint32_t)(e0 + e < n_ent) & (mb[tt] >> (8 * e + t_w));
+                    const float zs = (sacc[tt][0][e] + sacc[tt][1][e]) * a.scale_log2;
+                    z[tt][e] = (valid & 1u) ? zs : -INFINITY;
+                    hm = fmaxf(hm, z[tt][e]);
+                }
+            }
+            hm = group4_max(hm);
+            // the reference moves only when a logit exceeds it by more than the
+            // slack (the result does not depend on it; weights stay below 2^slack)
+            const bool over = hm > m_run + kMlaSlack;     // also any finite logit while m_run is -inf
+            float alpha = 1.f;
+            if (over) {
+                alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - hm);
+                m_run = hm;
+            }
+            float pf[2][4], ls = 0.f;
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float p = z[tt][e] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[tt][e] - m_run);
+                    pf[tt][e] = __uint_as_float(f32_to_bf16_rne(p) << 16);
+                    ls += pf[tt][e];
+                }
+            l_part = l_part * alpha + ls;
+            sm.p[buf][wr][lg][lr] = make_uint4(pack_bf16x2(pf[0][0], pf[0][1]), pack_bf16x2(pf[0][2], pf[0][3]),
+                                               pack_bf16x2(pf[1][0], pf[1][1]), pack_bf16x2(pf[1][2], pf[1][3]));
+            if (lg == 0) sm.alpha[buf][16 * wr + lr] = alpha;
+            const uint64_t anyover = __ballot(over);
+            if (lane == 0) sm.flag[buf][wr] = anyover != 0;
+        };
+
+        vm_wait<0>();                                 // queries and bits complete
+        lds_barrier();                                // (1)
+        if (ntiles > 0) {
+            lds_barrier();                            // (2)
+            s_tile(0);
+        }
+        for (int it = 0; it < ntiles; ++it) {
+            lds_barrier();
+            if (it + 1 < ntiles) s_tile(it + 1);
+        }
+        const float l_row = group4_sum(l_part);
+        if (lg == 0) {
+            const int r = 16 * wr + lr;
+            sm.u.st.row_m[r] = m_run;
+            sm.u.st.row_l[r] = l_row;
+            const int t = r / HB, h = g * G + rg * HB + r % HB;
+            if (a.splits == 1) {
+                if (a.lse)
+                    a.lse[((int64_t)b * T + t) * a.Hq + h] = l_row > 0.f ? m_run * kLn2 + logf(l_row) : -INFINITY;
+            } else {
+                float* pml = a.part_ml + ((int64_t)f * a.rgroups + rg) * kMlaRows * 2;
+                pml[2 * r] = m_run;
+                pml[2 * r + 1] = l_row;
+            }
+        }
+        lds_barrier();                                // (3)
     } else {
-        const int64_t slot = (int64_t)f * a.rgroups + rg;
-        float* po = a.part_o + slot * kMlaRows * kMlaDv;
+        // ---- O wave: value columns 128wr .. 128wr + 127 of all 64 rows
+        // transposed value reads: lane i of group lg addresses row 4lg + i/4 (and
+        // 16 more), columns 128wr + 16ct + 4(i%4) .. +3
+        const int voff = (4 * lg + (lr >> 2)) * kMlaRowBytes + 256 * wr + 8 * (lr & 3);
+        const bool dma10 = wr == 0;           // O wave 0 issues 10 DMAs per tile, the others 9
+        f32x4_t acc[4][kMlaColTiles];         // rows 16rt + lr, columns 128wr + 16ct + 4lg + e
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
+        for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * m + 4 * (lane >> 4) + e;
-                float* prow = po + (int64_t)r * kMlaDv + 64 * w + (lane & 15);
+            for (int ct = 0; ct < kMlaColTiles; ++ct) acc[rt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        auto o_tile = [&](int y) {
+            const int buf = y & 1;
+            const char* st = reinterpret_cast<const char*>(&sm.tile[y % kMlaStages][0]) + voff;
+            const int4 fl = *reinterpret_cast<const int4*>(&sm.flag[buf][0]);
+            uint4 pb[4];
 #pragma unroll
-                for (int n = 0; n < 4; ++n) prow[16 * n] = acc[m][n][e];
+            for (int rt = 0; rt < 4; ++rt) pb[rt] = sm.p[buf][rt][lg][lr];
+            uint2 vb[3][2];
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                vb[ct][0] = lds_read_tr(st + 32 * ct);
+                vb[ct][1] = lds_read_tr(st + 32 * ct + 16 * kMlaRowBytes);
             }
+            if ((fl.x | fl.y | fl.z | fl.w) != 0) {
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) {
+                    const float al = sm.alpha[buf][16 * rt + lr];
+#pragma unroll
+                    for (int ct = 0; ct < kMlaColTiles; ++ct) acc[rt][ct] *= al;
+                }
+            }
+#pragma unroll
+            for (int ct = 0; ct < kMlaColTiles; ++ct) {
+                if (ct + 2 < kMlaColTiles) {
+                    vb[(ct + 2) % 3][0] = lds_read_tr(st + 32 * (ct + 2));
+                    vb[(ct + 2) % 3][1] = lds_read_tr(st + 32 * (ct + 2) + 16 * kMlaRowBytes);
+                }
+                const uint4 va = make_uint4(vb[ct % 3][0].x, vb[ct % 3][0].y, vb[ct % 3][1].x, vb[ct % 3][1].y);
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) acc[rt][ct] = mfma16(va, pb[rt], acc[rt][ct]);
+            }
+        };
+
+        vm_wait<0>();                                 // ids of tiles 0..3 landed
+        lds_barrier();                                // (1)
+#pragma unroll
+        for (int x = 0; x < 3; ++x)
+            if (x < ntiles) issue_tile(x, x);
+        if (ntiles > 0) {
+            if (ntiles > 2) {
+                if (dma10) vm_wait<2 * kMlaDmaMax>(); else vm_wait<2 * (kMlaDmaMax - 1)>();
+            } else if (ntiles > 1) {
+                if (dma10) vm_wait<kMlaDmaMax>(); else vm_wait<kMlaDmaMax - 1>();
+            } else {
+                vm_wait<0>();
+            }
+            lds_barrier();                            // (2)
         }
-        if (w == 0) {
-            float* pml = a.part_ml + slot * kMlaRows * 2;
-            pml[2 * lane] = sm.row_m[lane];
-            pml[2 * lane + 1] = sm.row_l[0][lane] + sm.row_l[1][lane];
+        // O of tile it runs beside S of tile it + 1.  At the top of iteration it
+        // the DMAs of tiles it + 1 and it + 2 may be outstanding (and, issued
+        // before tile it + 2's rows, tile it + 3's ids); tile it + 1 and those ids
+        // are complete once only tile it + 2's rows remain.  The barrier also
+        // publishes tile it's weights and frees the stage and id slot of tile
+        // it - 1, which receive tile it + 3 and tile it + 4's ids.
+        for (int it = 0; it < ntiles; ++it) {
+            if (it + 2 < ntiles) {
+                if (dma10) vm_wait<kMlaDmaMax>(); else vm_wait<kMlaDmaMax - 1>();
+            } else {
+                vm_wait<0>();
+            }
+            lds_barrier();
+            if (it + 3 < ntiles) {
+                if (it + 4 < ntiles) issue_ids(it + 4);
+                issue_tile(it + 3, (it + 3) % kMlaStages);
+            }
+            o_tile(it);
+        }
+        lds_barrier();                                // (3)
+        if (a.splits == 1) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                const int r = 16 * rt + lr;
+                const int t = r / HB, h = g * G + rg * HB + r % HB;
+                const float l = sm.u.st.row_l[r];
+                const float inv = l > 0.f ? 1.f / l : 0.f;
+                float* orow = a.out + (((int64_t)b * T + t) * a.Hq + h) * kMlaDv + 128 * wr + 4 * lg;
+#pragma unroll
+                for (int ct = 0; ct < kMlaColTiles; ++ct)
+                    *reinterpret_cast<float4*>(orow + 16 * ct) =
+                        make_float4(acc[rt][ct][0] * inv, acc[rt][ct][1] * inv, acc[rt][ct][2] * inv,
+                                    acc[rt][ct][3] * inv);
+            }
+        } else {
+            float* po = a.part_o + ((int64_t)f * a.rgroups + rg) * kMlaRows * kMlaDv;
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                float* prow = po + (int64_t)(16 * rt + lr) * kMlaDv + 128 * wr + 4 * lg;
+#pragma unroll
+                for (int ct = 0; ct < kMlaColTiles; ++ct)
+                    *reinterpret_cast<float4*>(prow + 16 * ct) =
+                        make_float4(acc[rt][ct][0], acc[rt][ct][1], acc[rt][ct][2], acc[rt][ct][3]);
+            }
         }
     }
 }
@@ -460,8 +491,7 @@ MlaPlan plan_mla(int B, int Hkv, int T, int Hq, int N) {
     const int HB = kMlaRows / T;
     p.rgroups = (Hq / Hkv) / HB;
     const int64_t bg = (int64_t)B * Hkv;
-    // one block per CU (the accumulators and the bf16 queries take the register
-    // file), at least two tiles per range
+    // one block per CU (the LDS ring takes the CU's LDS), at least two tiles per range
     int64_t s = (256 + bg * p.rgroups - 1) / (bg * p.rgroups);
     const int64_t max_s = (N + 2 * kMlaTok - 1) / (2 * kMlaTok);
     if (s > max_s) s = max_s;
