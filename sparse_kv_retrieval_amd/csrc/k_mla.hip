@@ -54,6 +54,7 @@ constexpr int kMlaDmaTotal = kMlaTok * kMlaRowPieces / 64;               // 37 p
 constexpr int kMlaDmaMax = (kMlaDmaTotal + 3) / 4;                       // O wave 0: 10, others 9
 constexpr int kMlaStages = 4;             // tile i in O, i + 1 in S, i + 2 and i + 3 in flight
 constexpr int kMlaMaxRange = 2048;        // union entries per block (member bits staged in LDS)
+constexpr int kMlaIdSlots = 8;            // ring of tile ids (a tile's ids land 5 tiles before its rows)
 constexpr int kMlaColTiles = kMlaDv / 16 / 4;                            // 8 value column tiles per O wave
 constexpr float kMlaSlack = 8.f;          // log2 headroom of the lazy running maximum
 
@@ -70,7 +71,7 @@ struct __align__(16) MlaSmem {
     float alpha[2][kMlaRows];              // per-row rescale of the tile's weights
     int flag[2][4];                        // some row of the row tile rescaled
     union {
-        int32_t idr[kMlaStages][64];       // token ids of a tile (lanes 32..63 repeat them)
+        int32_t idr[kMlaIdSlots][kMlaTok]; // token ids of a tile, five tiles ahead of its rows
         struct {
             float row_m[kMlaRows];         // after the loop: row statistics
             float row_l[kMlaRows];
@@ -83,6 +84,11 @@ struct __align__(16) MlaSmem {
 __device__ __forceinline__ void lds_dma16_keep(const void* g, uint32_t lds_base) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  :: "v"(g), "s"(lds_base) : "memory", "m0");
+}
+// the same from a scalar base plus a 32-bit per-lane offset
+__device__ __forceinline__ void lds_dma16_keep_off(const void* base, uint32_t off, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(off), "s"(base), "s"(lds_base) : "memory", "m0");
 }
 __device__ __forceinline__ void lds_dma4_keep(const void* g, uint32_t lds_base) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
@@ -135,6 +141,8 @@ struct MlaArgs {
     float* part_ml;            // [work][rgroups][64][2]
 };
 
+// kWide: the latent rows of one (b, g) span 4 GiB or more (64-bit row addresses)
+template <bool kWide>
 __global__ __launch_bounds__(kMlaThreads) void k_mla_attn(MlaArgs a) {
     __shared__ MlaSmem sm;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -142,13 +150,16 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_attn(MlaArgs a) {
     const bool s_wave = w < 4;
     const int wr = w & 3;                     // row tile (S wave) or column quarter (O wave)
     const int lr = lane & 15, lg = lane >> 4;
-    // block -> (work item f, row group rg); the row groups of f share blockIdx mod 8
+    // block -> (b, g), range, row group: every block of one (b, g) has the same
+    // blockIdx mod 8, i.e. the same XCD, so the row groups find the tiles and the
+    // ranges find the queries in that XCD's L2
     const int blk = blockIdx.x;
-    const int f = (blk / (8 * a.rgroups)) * 8 + (blk % 8);
-    const int rg = (blk / 8) % a.rgroups;
-    if (f >= a.work) return;
-    const int split = f % a.splits;
-    const int bg = f / a.splits;
+    const int n_per = a.splits * a.rgroups;
+    const int bg = (blk / (8 * n_per)) * 8 + (blk % 8);
+    const int kq = (blk / 8) % n_per;
+    const int split = kq / a.rgroups, rg = kq - split * a.rgroups;
+    if (bg >= a.B * a.Hkv) return;
+    const int f = bg * a.splits + split;
     const int b = bg / a.Hkv, g = bg - b * a.Hkv;
     const int T = a.T, HB = kMlaRows / T, G = a.Hq / a.Hkv;
 
@@ -175,53 +186,67 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_attn(MlaArgs a) {
         const int j = pos / kMlaRowPieces, qp = pos - j * kMlaRowPieces;
         dsel[c] = (min(j, kMlaTok - 1) << 16) | (qp < kMlaPieces ? 16 * qp : 0);
     }
-    // the token ids of tile x into u.idr[x % 4] (O wave 0; entries past the range
-    // repeat the last one, and the rows' member bits mask them out)
+    // the token ids of tile x into u.idr[x % 8] (lanes 0..31 of one O wave;
+    // entries past the range repeat the last one, and the rows' member bits
+    // mask them out)
     auto issue_ids = [&](int x) {
-        if (w == 4)
-            lds_dma4_keep(ids + min(x * kMlaTok + (lane & (kMlaTok - 1)), n_ent - 1),
-                          lds_addr(&sm.u.idr[x % kMlaStages][0]));
+        if (lane < kMlaTok)
+            lds_dma4_keep(ids + min(x * kMlaTok + lane, n_ent - 1), lds_addr(&sm.u.idr[x % kMlaIdSlots][0]));
     };
-    // rows of tile x: ids from LDS (invalid ids read row 0, masked out by their bits)
-    auto issue_tile = [&](int x, int stage) {
-        int id[kMlaDmaMax];
+    // rows of a tile: the ids of this lane's rows from LDS, then DMA c (invalid
+    // ids read row 0, masked out by their bits)
+    auto read_ids = [&](int x, int (&id)[kMlaDmaMax]) {
 #pragma unroll
-        for (int c = 0; c < kMlaDmaMax; ++c) id[c] = sm.u.idr[x % kMlaStages][dsel[c] >> 16];
-#pragma unroll
-        for (int c = 0; c < kMlaDmaMax; ++c) {
-            const int i = wr + 4 * c;
-            if (i < kMlaDmaTotal) {
-                const int v = (id[c] < 0 || id[c] >= L) ? 0 : id[c];
-                lds_dma16_keep(lat_bg + (int64_t)v * row_bytes + (dsel[c] & 0xffff),
-                               lds_addr(&sm.tile[stage][0]) + 1024u * (uint32_t)i);
-            }
+        for (int c = 0; c < kMlaDmaMax; ++c) id[c] = sm.u.idr[x % kMlaIdSlots][dsel[c] >> 16];
+    };
+    const uint32_t row_bytes32 = (uint32_t)row_bytes;
+    auto issue_one = [&](int c, int stage, const int (&id)[kMlaDmaMax]) {
+        const int i = wr + 4 * c;
+        if (i < kMlaDmaTotal) {
+            const int v = (id[c] < 0 || id[c] >= L) ? 0 : id[c];
+            const uint32_t lds = lds_addr(&sm.tile[stage][0]) + 1024u * (uint32_t)i;
+            if (kWide)
+                lds_dma16_keep(lat_bg + (int64_t)v * row_bytes + (dsel[c] & 0xffff), lds);
+            else
+                lds_dma16_keep_off(lat_bg, __umul24((uint32_t)v, row_bytes32) + (uint32_t)(dsel[c] & 0xffff), lds);
         }
     };
-    // ---- prologue: ids of tiles 0..3, member bits and the queries in flight
-    // together, then tiles 0..2
+    auto issue_tile = [&](int x, int stage) {
+        int id[kMlaDmaMax];
+        read_ids(x, id);
+#pragma unroll
+        for (int c = 0; c < kMlaDmaMax; ++c) issue_one(c, stage, id);
+    };
+    // ---- prologue.  O waves: each fetches the ids of tiles 0..4 itself (the
+    // four write the same values) and issues tiles 0..2 as soon as its own have
+    // landed.  S waves: the member bits and the queries meanwhile.
     if (!s_wave) {
 #pragma unroll
-        for (int x = 0; x < 4; ++x)
+        for (int x = 0; x < 5; ++x)
             if (x < ntiles) issue_ids(x);
     }
-    constexpr int kStage = kMlaMaxRange / kMlaThreads;   // entries per thread
+    constexpr int kStage = kMlaMaxRange / (kMlaThreads / 2);   // entries per S-wave thread
     int sv[kStage], sb[kStage];
+    if (s_wave) {
 #pragma unroll
-    for (int i = 0; i < kStage; ++i) {
-        const int x = min(tid + kMlaThreads * i, max(n_ent - 1, 0));
-        sv[i] = n_ent > 0 ? ids[x] : 0;
-        sb[i] = mem && n_ent > 0 ? (int)mem[x] : 0xff;
+        for (int i = 0; i < kStage; ++i) {
+            const int x = min(tid + (kMlaThreads / 2) * i, max(n_ent - 1, 0));
+            sv[i] = n_ent > 0 ? ids[x] : 0;
+            sb[i] = mem && n_ent > 0 ? (int)mem[x] : 0xff;
+        }
     }
+    if (s_wave) {
 #pragma unroll
-    for (int i = 0; i < kStage; ++i) {
-        const int x = tid + kMlaThreads * i;
-        if (x < n_ent) sm.mem[x] = (uint8_t)((sv[i] < 0 || sv[i] >= L) ? 0 : sb[i]);
+        for (int i = 0; i < kStage; ++i) {
+            const int x = tid + (kMlaThreads / 2) * i;
+            if (x < n_ent) sm.mem[x] = (uint8_t)((sv[i] < 0 || sv[i] >= L) ? 0 : sb[i]);
+        }
     }
     constexpr float kLn2 = 0.69314718055994531f;
 
     // The two roles run separate loops with the same sequence of barriers:
-    // (1) bits and the first ids staged, (2) tile 0 landed, one per iteration,
-    // (3) row statistics published.
+    // (1) bits staged, (2) tile 0 landed, one per iteration, (3) row statistics
+    // published.
     if (s_wave) {
         // ---- S wave: rows 16wr .. 16wr + 15 (one query token)
         const int t_w = (16 * wr) / HB;
@@ -249,27 +274,31 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_attn(MlaArgs a) {
                 mb[tt] = *reinterpret_cast<const uint32_t*>(&sm.mem[x * kMlaTok + 16 * tt + 4 * lg]);
             f32x4_t sacc[2][2] = {{{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}},
                                   {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}};
-            // groups of two k-steps x two token tiles; operands two groups ahead
-            uint4 kb[3][4];
+            // groups of two k-steps x two token tiles; operands read kAhead groups
+            // ahead (the schedule barriers keep the compiler from sinking them)
+            constexpr int kAhead = 3;
+            uint4 kb[kAhead + 1][4];
 #pragma unroll
-            for (int gq = 0; gq < 2; ++gq)
+            for (int gq = 0; gq < kAhead; ++gq)
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
                     kb[gq][u] = *reinterpret_cast<const uint4*>(st + 64 * (2 * gq + (u >> 1)) +
                                                                 (u & 1) * 16 * kMlaRowBytes);
 #pragma unroll
             for (int gq = 0; gq < 9; ++gq) {
-                if (gq + 2 < 9) {
+                if (gq + kAhead < 9) {
 #pragma unroll
                     for (int u = 0; u < 4; ++u)
-                        kb[(gq + 2) % 3][u] = *reinterpret_cast<const uint4*>(
-                            st + 64 * (2 * (gq + 2) + (u >> 1)) + (u & 1) * 16 * kMlaRowBytes);
+                        kb[(gq + kAhead) % (kAhead + 1)][u] = *reinterpret_cast<const uint4*>(
+                            st + 64 * (2 * (gq + kAhead) + (u >> 1)) + (u & 1) * 16 * kMlaRowBytes);
                 }
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int s = 2 * gq + (u >> 1), tt = u & 1;
-                    sacc[tt][s & 1] = mfma16(kb[gq % 3][u], qa[s], sacc[tt][s & 1]);
+                    sacc[tt][s & 1] = mfma16(kb[gq % (kAhead + 1)][u], qa[s], sacc[tt][s & 1]);
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
             const int buf = x & 1;
             float z[2][4];
@@ -348,7 +377,11 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_attn(MlaArgs a) {
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
             for (int ct = 0; ct < kMlaColTiles; ++ct) acc[rt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        auto o_tile = [&](int y) {
+        // O^T of tile y; with dma, tile y + 3's rows are issued first: the DMA
+        // queue drains while the S wave of this SIMD holds the matrix core, and
+        // the products here then run beside that wave's softmax
+        auto o_tile = [&](int y, bool dma, const int (&id)[kMlaDmaMax]) {
+            const int dstage = (y + 3) % kMlaStages;
             const int buf = y & 1;
             const char* st = reinterpret_cast<const char*>(&sm.tile[y % kMlaStages][0]) + voff;
             const int4 fl = *reinterpret_cast<const int4*>(&sm.flag[buf][0]);
@@ -360,6 +393,10 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_attn(MlaArgs a) {
             for (int ct = 0; ct < 2; ++ct) {
                 vb[ct][0] = lds_read_tr(st + 32 * ct);
                 vb[ct][1] = lds_read_tr(st + 32 * ct + 16 * kMlaRowBytes);
+            }
+            if (dma) {
+#pragma unroll
+                for (int c = 0; c < kMlaDmaMax; ++c) issue_one(c, dstage, id);
             }
             if ((fl.x | fl.y | fl.z | fl.w) != 0) {
 #pragma unroll
@@ -381,11 +418,13 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_attn(MlaArgs a) {
             }
         };
 
-        vm_wait<0>();                                 // ids of tiles 0..3 landed
-        lds_barrier();                                // (1)
+        vm_wait<0>();                                 // this wave's ids of tiles 0..4 landed
 #pragma unroll
         for (int x = 0; x < 3; ++x)
             if (x < ntiles) issue_tile(x, x);
+        int id[kMlaDmaMax];                           // ids of the rows of tile it + 3
+        if (3 < ntiles) read_ids(3, id);
+        lds_barrier();                                // (1)
         if (ntiles > 0) {
             if (ntiles > 2) {
                 if (dma10) vm_wait<2 * kMlaDmaMax>(); else vm_wait<2 * (kMlaDmaMax - 1)>();
@@ -398,10 +437,11 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_attn(MlaArgs a) {
         }
         // O of tile it runs beside S of tile it + 1.  At the top of iteration it
         // the DMAs of tiles it + 1 and it + 2 may be outstanding (and, issued
-        // before tile it + 2's rows, tile it + 3's ids); tile it + 1 and those ids
+        // before tile it + 2's rows, tile it + 4's ids); tile it + 1 and those ids
         // are complete once only tile it + 2's rows remain.  The barrier also
-        // publishes tile it's weights and frees the stage and id slot of tile
-        // it - 1, which receive tile it + 3 and tile it + 4's ids.
+        // publishes tile it's weights and frees the stage of tile it - 1, which
+        // receives tile it + 3; tile it + 5's ids go to the slot of tile it - 3.
+        // Tile it + 4's ids are read at the end of the iteration, for the next.
         for (int it = 0; it < ntiles; ++it) {
             if (it + 2 < ntiles) {
                 if (dma10) vm_wait<kMlaDmaMax>(); else vm_wait<kMlaDmaMax - 1>();
@@ -409,11 +449,9 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_attn(MlaArgs a) {
                 vm_wait<0>();
             }
             lds_barrier();
-            if (it + 3 < ntiles) {
-                if (it + 4 < ntiles) issue_ids(it + 4);
-                issue_tile(it + 3, (it + 3) % kMlaStages);
-            }
-            o_tile(it);
+            if (it + 5 < ntiles && wr == 0) issue_ids(it + 5);
+            o_tile(it, it + 3 < ntiles, id);
+            if (it + 4 < ntiles) read_ids(it + 4, id);
         }
         lds_barrier();                                // (3)
         if (a.splits == 1) {
@@ -530,8 +568,13 @@ hipError_t launch_mla_attention(const float* q, int B, int T, int Hq, int Hkv, c
         a.part_o = (float*)ws;
         a.part_ml = (float*)ws + slots * kMlaRows * kMlaDv;
     }
-    const unsigned grid = (unsigned)(((a.work + 7) / 8) * 8 * plan.rgroups);
-    hipLaunchKernelGGL(k_mla_attn, dim3(grid), dim3(kMlaThreads), 0, st, a);
+    const unsigned grid = (unsigned)(((B * Hkv + 7) / 8) * 8 * plan.splits * plan.rgroups);
+    // row offsets fit 32 bits unless one (b, g)'s rows span 4 GiB
+    const bool wide = (int64_t)L * ks.t * 2 >= (int64_t(1) << 32);
+    if (wide)
+        hipLaunchKernelGGL(k_mla_attn<true>, dim3(grid), dim3(kMlaThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL(k_mla_attn<false>, dim3(grid), dim3(kMlaThreads), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.splits == 1) return e;
     const int rows = B * Hkv * plan.rgroups * kMlaRows;
