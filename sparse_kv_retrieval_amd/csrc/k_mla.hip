@@ -235,22 +235,18 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_attn(MlaArgs a) {
             sb[i] = mem && n_ent > 0 ? (int)mem[x] : 0xff;
         }
     }
-    if (s_wave) {
-#pragma unroll
-        for (int i = 0; i < kStage; ++i) {
-            const int x = tid + (kMlaThreads / 2) * i;
-            if (x < n_ent) sm.mem[x] = (uint8_t)((sv[i] < 0 || sv[i] >= L) ? 0 : sb[i]);
-        }
-    }
     constexpr float kLn2 = 0.69314718055994531f;
 
     // The two roles run separate loops with the same sequence of barriers:
-    // (1) bits staged, (2) tile 0 landed, one per iteration, (3) row statistics
+    // (1) bits staged and tile 0 landed, one per iteration, (2) row statistics
     // published.
     if (s_wave) {
         // ---- S wave: rows 16wr .. 16wr + 15 (one query token)
         const int t_w = (16 * wr) / HB;
         const int h_lane = g * G + rg * HB + (16 * wr) % HB + lr;   // head of row lane%16
+        // the queries: issued after the bits, converted as the first tile's
+        // k-steps need them (S waves issue no DMAs, so the compiler's own wait
+        // counts are exact here)
         uint4 qa[18];
         {
             const float* qrow = a.q + (((int64_t)b * T + t_w) * a.Hq + h_lane) * kMlaDk + 8 * lg;
@@ -261,6 +257,11 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_attn(MlaArgs a) {
                 qa[s] = make_uint4(pack_bf16x2(x0.x, x0.y), pack_bf16x2(x0.z, x0.w), pack_bf16x2(x1.x, x1.y),
                                    pack_bf16x2(x1.z, x1.w));
             }
+        }
+#pragma unroll
+        for (int i = 0; i < kStage; ++i) {
+            const int x = tid + (kMlaThreads / 2) * i;
+            if (x < n_ent) sm.mem[x] = (uint8_t)((sv[i] < 0 || sv[i] >= L) ? 0 : sb[i]);
         }
         // key piece 4s + lg of row 16tt + lr
         const int koff = lr * kMlaRowBytes + 16 * lg;
@@ -275,7 +276,8 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_attn(MlaArgs a) {
             f32x4_t sacc[2][2] = {{{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}},
                                   {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}};
             // groups of two k-steps x two token tiles; operands read kAhead groups
-            // ahead (the schedule barriers keep the compiler from sinking them)
+            // ahead (the schedule barriers keep the compiler from sinking them).
+
             constexpr int kAhead = 3;
             uint4 kb[kAhead + 1][4];
 #pragma unroll
@@ -323,29 +325,28 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_attn(MlaArgs a) {
                 alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - hm);
                 m_run = hm;
             }
-            float pf[2][4], ls = 0.f;
+            // weights rounded to bf16 (v_cvt_pk_bf16_f32, to nearest even); the row
+            // sum adds the rounded values the value product uses
+            uint32_t pk[4];
+            float ls = 0.f;
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float p = z[tt][e] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[tt][e] - m_run);
-                    pf[tt][e] = __uint_as_float(f32_to_bf16_rne(p) << 16);
-                    ls += pf[tt][e];
-                }
+            for (int h = 0; h < 4; ++h) {
+                const float z0 = z[h >> 1][2 * (h & 1)], z1 = z[h >> 1][2 * (h & 1) + 1];
+                const float p0 = z0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z0 - m_run);
+                const float p1 = z1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z1 - m_run);
+                const bf16x2_t v = {(__bf16)p0, (__bf16)p1};
+                pk[h] = __builtin_bit_cast(uint32_t, v);
+                ls += __uint_as_float(pk[h] << 16) + __uint_as_float(pk[h] & 0xffff0000u);
+            }
             l_part = l_part * alpha + ls;
-            sm.p[buf][wr][lg][lr] = make_uint4(pack_bf16x2(pf[0][0], pf[0][1]), pack_bf16x2(pf[0][2], pf[0][3]),
-                                               pack_bf16x2(pf[1][0], pf[1][1]), pack_bf16x2(pf[1][2], pf[1][3]));
+            sm.p[buf][wr][lg][lr] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
             if (lg == 0) sm.alpha[buf][16 * wr + lr] = alpha;
             const uint64_t anyover = __ballot(over);
             if (lane == 0) sm.flag[buf][wr] = anyover != 0;
         };
 
-        vm_wait<0>();                                 // queries and bits complete
         lds_barrier();                                // (1)
-        if (ntiles > 0) {
-            lds_barrier();                            // (2)
-            s_tile(0);
-        }
+        if (ntiles > 0) s_tile(0);
         for (int it = 0; it < ntiles; ++it) {
             lds_barrier();
             if (it + 1 < ntiles) s_tile(it + 1);
@@ -365,7 +366,7 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_attn(MlaArgs a) {
                 pml[2 * r + 1] = l_row;
             }
         }
-        lds_barrier();                                // (3)
+        lds_barrier();                                // (2)
     } else {
         // ---- O wave: value columns 128wr .. 128wr + 127 of all 64 rows
         // transposed value reads: lane i of group lg addresses row 4lg + i/4 (and
@@ -424,17 +425,14 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_attn(MlaArgs a) {
             if (x < ntiles) issue_tile(x, x);
         int id[kMlaDmaMax];                           // ids of the rows of tile it + 3
         if (3 < ntiles) read_ids(3, id);
-        lds_barrier();                                // (1)
-        if (ntiles > 0) {
-            if (ntiles > 2) {
-                if (dma10) vm_wait<2 * kMlaDmaMax>(); else vm_wait<2 * (kMlaDmaMax - 1)>();
-            } else if (ntiles > 1) {
-                if (dma10) vm_wait<kMlaDmaMax>(); else vm_wait<kMlaDmaMax - 1>();
-            } else {
-                vm_wait<0>();
-            }
-            lds_barrier();                            // (2)
+        if (ntiles > 2) {
+            if (dma10) vm_wait<2 * kMlaDmaMax>(); else vm_wait<2 * (kMlaDmaMax - 1)>();
+        } else if (ntiles > 1) {
+            if (dma10) vm_wait<kMlaDmaMax>(); else vm_wait<kMlaDmaMax - 1>();
+        } else {
+            vm_wait<0>();
         }
+        lds_barrier();                                // (1)
         // O of tile it runs beside S of tile it + 1.  At the top of iteration it
         // the DMAs of tiles it + 1 and it + 2 may be outstanding (and, issued
         // before tile it + 2's rows, tile it + 4's ids); tile it + 1 and those ids
@@ -453,7 +451,7 @@ __global__ __launch_bounds__(kMlaThreads) void k_mla_attn(MlaArgs a) {
             o_tile(it, it + 3 < ntiles, id);
             if (it + 4 < ntiles) read_ids(it + 4, id);
         }
-        lds_barrier();                                // (3)
+        lds_barrier();                                // (2)
         if (a.splits == 1) {
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
