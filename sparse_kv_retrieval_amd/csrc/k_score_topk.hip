@@ -136,9 +136,13 @@ __device__ __forceinline__ int wave_prefix_sum(int v) {
 // unused slots hold 0, below every real key) by a bitwise search over the key
 // space with wave-wide ballot counts; also how many keys equal to it are among
 // the k largest.  No LDS, no barriers.
+// With LOW_BIT > 0 only the key bits above it are settled: r is then the
+// largest key with those low bits zero that still has k keys at or above it, a
+// lower bound of the k-th largest (need_out is then not meaningful).
+template <int LOW_BIT = 0>
 __device__ uint32_t wave_kth_key_bisect(const uint32_t (&x)[4], int k, int* need_out) {
     uint32_t r = 0;
-    for (int bit = 31; bit >= 0; --bit) {
+    for (int bit = 31; bit >= LOW_BIT; --bit) {
         const uint32_t c = r | (1u << bit);
         int cnt = 0;
 #pragma unroll
@@ -641,10 +645,10 @@ __global__ __launch_bounds__(kThreads) void k_score_lo(const float* __restrict__
 // ---------------------------------------------------------------------------
 // Shadow pass 2, one block per (b, g, t).  Every chunk's fp32 score s (as this
 // kernel computes it) lies in [s_lo - d_c, s_lo + d_c] with d_c = K * s_c, K
-// from the query's 1-norm (the derivation is at the bound below).  L = the k-th
-// largest per-thread maximum of s_lo - d_c is a lower bound of the k-th largest
-// s; the candidates {c : s_lo[c] + d_c >= L} hold every chunk of the top k,
-// ties included.  Their fp32 re-scores give the exact top-k (ties to the lower
+// from the query's 1-norm (the derivation is at the bound below).  L, at most
+// the k-th largest per-thread maximum of s_lo - d_c, is a lower bound of the
+// k-th largest s; the candidates {c : s_lo[c] + d_c >= L} hold every chunk of
+// the top k, ties included.  Their fp32 re-scores give the exact top-k (ties to the lower
 // id), written in ascending order.
 // ---------------------------------------------------------------------------
 template <int D, bool MAXRED>
@@ -735,15 +739,17 @@ __global__ __launch_bounds__(kThreads) void k_select_exact(
     tmaxs[tid] = tmax;
     __syncthreads();
     if (wave == 0) {
-        // the k-th largest of the per-thread maxima: at least k chunks score at
-        // least this much.  For k > 256 the bound is 0, i.e. every chunk is a candidate.
+        // a lower bound of the k-th largest of the per-thread maxima (its top 20
+        // key bits, a relative 2^-11 of the score below it at most): at least k
+        // chunks score at least this much.  For k > 256 the bound is 0, i.e.
+        // every chunk is a candidate.
         uint32_t kb = 0u;
         if (k <= kThreads) {
             uint32_t x[4];
 #pragma unroll
             for (int v = 0; v < 4; ++v) x[v] = tmaxs[lane + 64 * v];
             int nd;
-            kb = wave_kth_key_bisect(x, k, &nd);
+            kb = wave_kth_key_bisect<12>(x, k, &nd);
         }
         if (lane == 0) bc[0] = (int)kb;
     }
