@@ -181,6 +181,41 @@ __device__ __forceinline__ void raw_barrier() {
 }
 
 // ---------------------------------------------------------------------------
+// Matrix-core operands (v_mfma_f32_16x16x32_bf16: A is 16 x 32, B is 32 x 16;
+// lane l holds A[l % 16][8 (l / 16) .. + 7] and B[8 (l / 16) .. + 7][l % 16];
+// the fp32 result has D[4 (l / 16) + i][l % 16] in element i of lane l).
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+
+// max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (v_permlane16/32_swap:
+// with both operands equal, the two results hold the values of the lane pair)
+__device__ __forceinline__ float group4_max(float v) {
+    auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float group4_sum(float v) {
+    auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ f32x4_t mfma16(const uint4& a, const uint4& b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+// ds_read_b64_tr_b16: within each 16-lane group, lane i addresses 8 bytes (row
+// i / 4, columns 4 (i % 4) .. + 3 of a 4 x 16 bf16 block); lane j receives
+// column j of that block, its four rows in ascending order.
+__device__ __forceinline__ uint2 lds_read_tr(const char* p) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p)));
+}
+
+// ---------------------------------------------------------------------------
 // 16-byte global loads/stores.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }

@@ -14,19 +14,21 @@
 // the online-softmax rule.  Logits are kept in log2 units (scale * log2 e).
 //
 // Fast path (bf16 K/V, d = 128, G = 4, T = 2, chunk a multiple of 32): four
-// waves, wave w owning query head g*4 + w for both tokens.  32-row tiles of K
-// and V (16 KiB) stream from HBM straight into a three-stage LDS ring with
-// global_load_lds_dwordx4 (non-temporal; no register staging), so two tiles are
-// in flight while one is computed, and each tile is read from HBM once for all
-// eight query rows.  Q.K: two lanes per key, each holding its 64-dim half of
-// both queries as packed bf16 in registers (v_dot2c_f32_bf16); one DPP lane swap
-// leaves lane (key, t) with its logit.  K pieces are XOR-swizzled by row in LDS
-// and odd lanes walk their half in rotated order, so the lanes served per LDS
-// cycle hit distinct banks.  The running max only moves when a logit exceeds it
-// (a ballot), so most tiles need no cross-lane reduction.  P.V: the weights
-// are rounded to bf16 and keys j, j + 4 are paired along v_dot2c_f32_bf16
-// (V words re-paired with v_perm_b32); the row sums use the same rounded
-// weights, so each output stays an exact convex combination of its values.
+// waves over 32-row tiles of K and V (16 KiB) that stream from HBM straight
+// into a three-stage LDS ring with global_load_lds_dwordx4 (non-temporal; no
+// register staging), so two tiles are in flight while one is computed, and each
+// tile is read from HBM once for all eight query rows.  Both products run on
+// the matrix cores (v_mfma_f32_16x16x32_bf16) with the keys along M:
+// S^T = K Q^T gives every lane one query row's logits of eight keys; after the
+// online-softmax step those weights, rounded to bf16, are already the B operand
+// of O^T = V^T P^T, whose A operand comes from transposed LDS reads of V
+// (ds_read_b64_tr_b16).  Every wave computes S for all eight rows (the same
+// values in each wave, so the running max and sums agree) and owns 32 of the
+// 128 value dims.  K and V pieces are XOR-swizzled by row in LDS so that the
+// operand reads hit distinct banks.  The running max moves only when a logit
+// exceeds it by a slack, so most tiles need no rescale; the row sums use the
+// rounded weights, so each output stays an exact convex combination of its
+// values.
 #include "dk_common.h"
 
 namespace dk {
@@ -99,19 +101,21 @@ __device__ __forceinline__ void emit_row(const AttnArgs& a, int b, int bg, int s
 // ---------------------------------------------------------------------------
 constexpr int kFastStages = 3;     // LDS ring: one tile computed, two in flight
 constexpr int kFastMaxEntries = 256;
+constexpr float kFastSlack = 8.f;  // log2 headroom of the lazy running maximum
 
 struct __align__(16) FastSmem {
     uint4 kv[kFastStages][2][32 * 16];     // [stage][K|V][row * 16 + 16-byte piece]
     int32_t erow[kFastMaxEntries];         // first pool row of each entry's chunk
     uint32_t ebits[kFastMaxEntries];       // membership bits (0: skip the entry)
-    uint32_t p16[4][16][2];                // [wave][key pair][t]: bf16 weights of keys j, j + 4
 };
 
 __global__ __launch_bounds__(kThreads) void k_attn_bf16_d128_g4t2(AttnArgs a) {
     constexpr int D = 128, G = 4, T = 2, R = G * T, KT = 32, NS = kFastStages;
+    constexpr int kRowBytes = D * 2, kHalfTile = 16 * kRowBytes;   // 16 keys of K or V
     __shared__ FastSmem sm;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int lr = lane & 15, lg = lane >> 4;   // matrix-core lane coordinates
     int bg, split;
     xcd_unit(blockIdx.x, a.splits, gridDim.x / a.splits, bg, split);
     const int b = bg / a.Hkv, g = bg - b * a.Hkv;
@@ -119,19 +123,20 @@ __global__ __launch_bounds__(kThreads) void k_attn_bf16_d128_g4t2(AttnArgs a) {
     entry_range(a, bg, split, u0, u1);
     const int tpc = a.chunk / KT;
     const int ntiles = a.pool_blocks > 0 ? (u1 - u0) * tpc : 0;
-    const int h = g * G + w;
 
-    // The block's eight query rows (row t * G + w) go through LDS once: one
-    // 16-byte load per thread, instead of every key lane fetching its own copy.
-    // They borrow the last ring stage, which the first DMA into it (issued after
-    // the first barrier of the tile loop) overwrites only once every wave has
-    // taken its rows into registers.
-    float* qs = reinterpret_cast<float*>(&sm.kv[NS - 1][0][0]);   // [R][D]
+    // Query operand of S^T = K Q^T (B of the 16x16x32 product): lane (lr, lg)
+    // holds query row lr (token lr / 4, head g * 4 + lr % 4) at dims
+    // 32 ks + 8 lg .. + 7; columns 8..15 stay zero.
+    const bool qrow = lr < R;
+    float4 qf[4][2];
     {
-        const int r = tid >> 5, c4 = tid & 31;   // 256 threads: 8 rows x 32 float4
-        const int t = r / G, hh = r - t * G;
-        *reinterpret_cast<float4*>(qs + r * D + c4 * 4) =
-            *reinterpret_cast<const float4*>(a.q + (((int64_t)b * T + t) * a.Hq + g * G + hh) * D + c4 * 4);
+        const int r = qrow ? lr : 0;
+        const float* qp = a.q + (((int64_t)b * T + r / G) * a.Hq + g * G + r % G) * D + 8 * lg;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            qf[ks][0] = qrow ? *reinterpret_cast<const float4*>(qp + 32 * ks) : make_float4(0.f, 0.f, 0.f, 0.f);
+            qf[ks][1] = qrow ? *reinterpret_cast<const float4*>(qp + 32 * ks + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
     }
     // This block's entries go to LDS, so the tile loop issues no vector loads of
     // its own besides the DMA (keeps the explicit vmcnt accounting exact).
@@ -146,31 +151,17 @@ __global__ __launch_bounds__(kThreads) void k_attn_bf16_d128_g4t2(AttnArgs a) {
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    uint4 qb[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+        qb[ks] = make_uint4(pack_bf16x2(qf[ks][0].x, qf[ks][0].y), pack_bf16x2(qf[ks][0].z, qf[ks][0].w),
+                            pack_bf16x2(qf[ks][1].x, qf[ks][1].y), pack_bf16x2(qf[ks][1].z, qf[ks][1].w));
 
-    // Q in registers: lane (key j, half hd) holds its 64-dim half of both queries
-    // as bf16 pairs, in the rotated order in which it reads its K half.
-    const int j = lane >> 1, hd = lane & 1;
-    uint4 qr[T][8];
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-        const float* qp = qs + (t * G + w) * D;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int ls = 8 * hd + ((i + 4 * hd) & 7);
-            const float4 x0 = *reinterpret_cast<const float4*>(qp + ls * 8);
-            const float4 x1 = *reinterpret_cast<const float4*>(qp + ls * 8 + 4);
-            qr[t][i] = make_uint4(pack_bf16x2(x0.x, x0.y), pack_bf16x2(x0.z, x0.w),
-                                  pack_bf16x2(x1.x, x1.y), pack_bf16x2(x1.z, x1.w));
-        }
-    }
-#pragma unroll
-    for (int t = 0; t < T; ++t)
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            asm volatile("" : "+v"(qr[t][i].x), "+v"(qr[t][i].y), "+v"(qr[t][i].z), "+v"(qr[t][i].w));
-
-    // DMA geometry: wave w fills rows 8w..8w+7 of the K tile (pieces XOR-swizzled
-    // by row) and of the V tile (plain), two 1 KiB wave-loads each.
+    // DMA geometry: wave w fills rows 8w..8w+7 of the K and of the V tile, two
+    // 1 KiB wave-loads each.  Row r's 16-byte pieces are XOR-swizzled, K by
+    // r & 15 and V by 2 (r & 7), so that the matrix-core operand reads below
+    // (16 key rows at one K piece; 8 key rows at two adjacent V pieces) hit
+    // distinct LDS banks.
     const uint16_t* Kb = (const uint16_t*)a.K + (int64_t)b * a.ks.b + (int64_t)g * a.ks.h;
     const uint16_t* Vb = (const uint16_t*)a.V + (int64_t)b * a.vs.b + (int64_t)g * a.vs.h;
     int koff[2], voff[2];
@@ -178,8 +169,8 @@ __global__ __launch_bounds__(kThreads) void k_attn_bf16_d128_g4t2(AttnArgs a) {
     for (int jj = 0; jj < 2; ++jj) {
         const int p = (2 * w + jj) * 64 + lane;
         const int row = p >> 4, phys = p & 15;
-        koff[jj] = row * (int)a.ks.t + (phys ^ (row & 7)) * 8;
-        voff[jj] = row * (int)a.vs.t + phys * 8;
+        koff[jj] = row * (int)a.ks.t + (phys ^ (row & 15)) * 8;
+        voff[jj] = row * (int)a.vs.t + (phys ^ (2 * (row & 7))) * 8;
     }
     // the wave index as a scalar: the DMA's LDS bases (M0) are then plain SALU math
     const int wu = __builtin_amdgcn_readfirstlane(w);
@@ -197,16 +188,28 @@ __global__ __launch_bounds__(kThreads) void k_attn_bf16_d128_g4t2(AttnArgs a) {
         for (int jj = 0; jj < 2; ++jj) lds_dma16(vp + voff[jj], lds_addr(&sm.kv[s][1][(2 * wu + jj) * 64]));
     };
 
-    // Running max in log2 units.  It starts at a finite floor far below every
-    // logit, so exp2 of (masked logit = -inf) - max is 0 without a guard, and a
-    // range with no valid key ends with l = 0 (reported as out 0, lse -inf).
-    float m_run = kNoLogit, l_run = 0.f;     // this lane's query t = hd
-    float acc[T][8];
+    // Operand reads within a tile (bytes).  K (A of S^T): key 16 mt + lr, logical
+    // piece lg + 4 ks.  V (A of O^T = V^T P^T, transposed reads): value dims
+    // 32 w + 16 j + lr, keys 4 lg .. + 3 and 16 + 4 lg .. + 3, so that the k-th
+    // element of the operand is the key whose weight S^T leaves in element k
+    // of the same lane.
+    int kro[4], vro[2];
 #pragma unroll
-    for (int t = 0; t < T; ++t)
+    for (int ks = 0; ks < 4; ++ks) kro[ks] = lr * kRowBytes + ((lg + 4 * ks) ^ lr) * 16;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[t][e] = 0.f;
-    const int ps = lane & 15, kg = lane >> 4;
+    for (int j = 0; j < 2; ++j) {
+        const int key = 4 * lg + (lr >> 2);
+        const int lp = 4 * w + 2 * j + ((lr & 3) >> 1);
+        vro[j] = key * kRowBytes + (lp ^ (2 * (key & 7))) * 16 + 8 * (lr & 1);
+    }
+
+    // Running max in log2 units, moved only when a logit exceeds it by more than
+    // the slack (weights stay below 2^slack).  It starts at a finite floor far
+    // below every logit, so exp2 of (masked logit = -inf) - max is 0 without a
+    // guard, and a range with no valid key ends with l = 0 (reported as out 0,
+    // lse -inf).  Every wave computes the same S, so m and l agree across waves.
+    float m_run = kNoLogit, l_part = 0.f;     // l_part: this lane's share of row lr's sum
+    f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s)
@@ -226,96 +229,79 @@ __global__ __launch_bounds__(kThreads) void k_attn_bf16_d128_g4t2(AttnArgs a) {
         row_next = it + NS < ntiles ? tile_row(it + NS) : 0;
         bits_next = it + 1 < ntiles ? sm.ebits[(it + 1) / tpc] : 0u;
         if (m_cur == 0) continue;
-        const uint4* kb = sm.kv[it % NS][0];
-        const uint4* vb = sm.kv[it % NS][1];
+        const char* kb = reinterpret_cast<const char*>(sm.kv[it % NS][0]);
+        const char* vb = reinterpret_cast<const char*>(sm.kv[it % NS][1]);
 
-        // ---- logits of both queries ----
-        float a0 = 0.f, a1 = 0.f;
+        uint4 kr[2][4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) kr[mt][ks] = *reinterpret_cast<const uint4*>(kb + kro[ks] + mt * kHalfTile);
+        uint2 vr[2][2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh) vr[j][kh] = lds_read_tr(vb + vro[j] + kh * kHalfTile);
+
+        // ---- S^T for all eight query rows: element i of s[mt] is key 16 mt + 4 lg + i ----
+        f32x4_t s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) s[mt] = mfma16(kr[mt][ks], qb[ks], s[mt]);
+
+        // ---- online softmax of row lr ----
+        const bool on = qrow && ((m_cur >> (lr >> 2)) & 1u);
+        float z[8];
+        float hm = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int ls = 8 * hd + ((i + 4 * hd) & 7);
-            const uint4 kv = kb[j * 16 + (ls ^ (j & 7))];
-            a0 = dot2_bf16(qr[0][i].x, kv.x, a0);
-            a0 = dot2_bf16(qr[0][i].y, kv.y, a0);
-            a0 = dot2_bf16(qr[0][i].z, kv.z, a0);
-            a0 = dot2_bf16(qr[0][i].w, kv.w, a0);
-            a1 = dot2_bf16(qr[1][i].x, kv.x, a1);
-            a1 = dot2_bf16(qr[1][i].y, kv.y, a1);
-            a1 = dot2_bf16(qr[1][i].z, kv.z, a1);
-            a1 = dot2_bf16(qr[1][i].w, kv.w, a1);
+            z[i] = on ? s[i >> 2][i & 3] * a.scale_log2 : -INFINITY;
+            hm = fmaxf(hm, z[i]);
         }
-        const float send = hd ? a0 : a1;
-        const float keep = hd ? a1 : a0;
-        float z = (keep + dpp_xor1(send)) * a.scale_log2;
-        if (!((m_cur >> hd) & 1u)) z = -INFINITY;
+        hm = group4_max(hm);
+        const bool over = hm > m_run + kFastSlack;
+        float alpha = 1.f;
+        if (over) {
+            alpha = __builtin_amdgcn_exp2f(m_run - hm);
+            m_run = hm;
+        }
+        // weights rounded to bf16 (to nearest even); the row sum adds the rounded
+        // values the value product uses, so each output stays an exact convex
+        // combination of its values
+        uint32_t pk[4];
+        float ls = 0.f;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            const bf16x2_t v = {(__bf16)__builtin_amdgcn_exp2f(z[2 * h] - m_run),
+                                (__bf16)__builtin_amdgcn_exp2f(z[2 * h + 1] - m_run)};
+            pk[h] = __builtin_bit_cast(uint32_t, v);
+            ls += bf16_lo(pk[h]) + bf16_hi(pk[h]);
+        }
+        l_part = l_part * alpha + ls;
+        if (__builtin_amdgcn_ballot_w64(over) != 0ull) {
+            acc[0] *= alpha;
+            acc[1] *= alpha;
+        }
 
-        // ---- online softmax; the running max moves only when a logit exceeds it,
-        // and then the accumulators are rescaled in place ----
-        if (__builtin_amdgcn_ballot_w64(z > m_run) != 0ull) {
-            float cm = z;
+        // ---- O^T += V^T P^T for this wave's 32 value dims ----
+        const uint4 pb = make_uint4(pk[0], pk[1], pk[2], pk[3]);
 #pragma unroll
-            for (int off = 2; off < kWave; off <<= 1) cm = fmaxf(cm, __shfl_xor(cm, off, kWave));
-            const float mn = fmaxf(m_run, cm);
-            const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
-            l_run *= alpha;
-            m_run = mn;
-            const float al0 = __shfl(alpha, 0, kWave);
-            const float al1 = __shfl(alpha, 1, kWave);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                acc[0][e] *= al0;
-                acc[1][e] *= al1;
-            }
-        }
-        const float p = __builtin_amdgcn_exp2f(z - m_run);
-        // weights go to P.V as bf16; the row sum uses the same rounded weights
-        const uint32_t pb = f32_to_bf16_rne(p);
-        l_run += __uint_as_float(pb << 16);
-        reinterpret_cast<uint16_t*>(&sm.p16[w][(j >> 3) * 4 + (j & 3)][hd])[(j >> 2) & 1] = (uint16_t)pb;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-        // ---- P.V: keys j1 = 8i + kg and j2 = j1 + 4 paired along the bf16 dot ----
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int j1 = 8 * i + kg, j2 = j1 + 4;
-            const uint4 va = vb[j1 * 16 + ps];
-            const uint4 vc = vb[j2 * 16 + ps];
-            const uint2 pp = *reinterpret_cast<const uint2*>(&sm.p16[w][i * 4 + kg][0]);
-            const uint32_t av[4] = {va.x, va.y, va.z, va.w};
-            const uint32_t cv[4] = {vc.x, vc.y, vc.z, vc.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                // (V[j1][d], V[j2][d]) for the even and the odd dim of this word
-                const uint32_t lo = __builtin_amdgcn_perm(cv[e], av[e], 0x05040100u);
-                const uint32_t hi = __builtin_amdgcn_perm(cv[e], av[e], 0x07060302u);
-                acc[0][2 * e] = dot2_bf16(pp.x, lo, acc[0][2 * e]);
-                acc[0][2 * e + 1] = dot2_bf16(pp.x, hi, acc[0][2 * e + 1]);
-                acc[1][2 * e] = dot2_bf16(pp.y, lo, acc[1][2 * e]);
-                acc[1][2 * e + 1] = dot2_bf16(pp.y, hi, acc[1][2 * e + 1]);
-            }
-        }
-        // p16 is rewritten next tile only after every lane has read it
-        __builtin_amdgcn_wave_barrier();
+        for (int j = 0; j < 2; ++j)
+            acc[j] = mfma16(make_uint4(vr[j][0].x, vr[j][0].y, vr[j][1].x, vr[j][1].y), pb, acc[j]);
     }
     lds_dma_wait<0>();
 
-    // ---- combine lanes ----
+    // ---- row results: every wave holds m and l of all rows, and 32 dims ----
+    const float l_row = group4_sum(l_part);
+    if (qrow) {
+        const int t = lr / G, h = g * G + lr % G;
 #pragma unroll
-    for (int off = 2; off < kWave; off <<= 1) l_run += __shfl_xor(l_run, off, kWave);
-#pragma unroll
-    for (int t = 0; t < T; ++t)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            acc[t][e] += __shfl_xor(acc[t][e], 16, kWave);
-            acc[t][e] += __shfl_xor(acc[t][e], 32, kWave);
+        for (int j = 0; j < 2; ++j) {
+            const float o[4] = {acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
+            emit_row<D>(a, b, bg, split, t, h, lr, R, m_run, l_row, o, 32 * w + 16 * j + 4 * lg, 4,
+                        w == 0 && lg == 0 && j == 0);
         }
-    const float m0 = __shfl(m_run, 0, kWave), m1 = __shfl(m_run, 1, kWave);
-    const float l0 = __shfl(l_run, 0, kWave), l1 = __shfl(l_run, 1, kWave);
-    if (kg == 0) {
-        emit_row<D>(a, b, bg, split, 0, h, 0 * G + w, R, m0, l0, acc[0], ps * 8, 8, ps == 0);
-        emit_row<D>(a, b, bg, split, 1, h, 1 * G + w, R, m1, l1, acc[1], ps * 8, 8, ps == 0);
     }
 }
 

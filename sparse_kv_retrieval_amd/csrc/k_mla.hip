@@ -60,11 +60,6 @@ constexpr float kMlaSlack = 8.f;          // log2 headroom of the lazy running m
 
 static_assert(kMlaDmaTotal * 64 == kMlaTok * kMlaRowPieces, "a tile is a whole number of DMAs");
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
-
 struct __align__(16) MlaSmem {
     uint4 tile[kMlaStages][kMlaTileBytes / 16];
     uint4 p[2][4][4][16];                  // [buffer][row tile][lane group][row]: 8 bf16 weights
@@ -102,28 +97,6 @@ __device__ __forceinline__ void vm_wait() {
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     raw_barrier();
-}
-
-// max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (v_permlane16/32_swap:
-// with both operands equal, the two results hold the values of the lane pair)
-__device__ __forceinline__ float group4_max(float v) {
-    auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
-    p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
-}
-__device__ __forceinline__ float group4_sum(float v) {
-    auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
-    p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
-}
-__device__ __forceinline__ f32x4_t mfma16(const uint4& a, const uint4& b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
-__device__ __forceinline__ uint2 lds_read_tr(const char* p) {
-    return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p)));
 }
 
 struct MlaArgs {

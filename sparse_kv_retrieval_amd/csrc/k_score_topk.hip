@@ -32,7 +32,6 @@ constexpr int kMaxRows = 4096;       // landmark rows per range (LDS: T * 16 KiB
 constexpr int kMaxCand = 8192;       // candidates per (b, g, t) in the merge
 constexpr int kShadowMaxC = 6144;    // chunks per (b, g) with a shadow (pass-2 LDS <= 64 KiB)
 
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 // streamed once: non-temporal 16-byte loads
