@@ -293,15 +293,39 @@ __global__ __launch_bounds__(kThreads) void k_attn_bf16_d128_g4t2(AttnArgs a) {
     lds_dma_wait<0>();
 
     // ---- row results: every wave holds m and l of all rows, and 32 dims ----
+    // The eight rows go through LDS (the first ring stage, free once every wave
+    // is past its last tile) so that the block writes them as whole lines: one
+    // 16-byte store per thread.  Scattered 4-byte stores of partial lines cost
+    // several microseconds per launch at full size.
     const float l_row = group4_sum(l_part);
+    const bool single = a.nparts == 1;
+    const float inv = single ? (l_row > 0.f ? 1.f / l_row : 0.f) : 1.f;
+    __syncthreads();
+    float* ostage = reinterpret_cast<float*>(&sm.kv[0][0][0]);   // [R][D]
     if (qrow) {
-        const int t = lr / G, h = g * G + lr % G;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const float o[4] = {acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
-            emit_row<D>(a, b, bg, split, t, h, lr, R, m_run, l_row, o, 32 * w + 16 * j + 4 * lg, 4,
-                        w == 0 && lg == 0 && j == 0);
+        for (int j = 0; j < 2; ++j)
+            *reinterpret_cast<float4*>(ostage + lr * D + 32 * w + 16 * j + 4 * lg) =
+                make_float4(acc[j][0] * inv, acc[j][1] * inv, acc[j][2] * inv, acc[j][3] * inv);
+        if (w == 0 && lg == 0) {
+            const int t = lr / G, h = g * G + lr % G;
+            if (single) {
+                if (a.lse)
+                    a.lse[((int64_t)b * T + t) * a.Hq + h] = l_row > 0.f ? (m_run + log2f(l_row)) * kLn2 : -INFINITY;
+            } else {
+                const int64_t slot = ((int64_t)bg * a.nparts + split) * R + lr;
+                a.part_ml[slot * 2] = m_run;
+                a.part_ml[slot * 2 + 1] = l_row;
+            }
         }
+    }
+    __syncthreads();
+    {
+        const int r = tid >> 5, c4 = tid & 31;    // 256 threads: 8 rows x 32 float4
+        const float4 v = *reinterpret_cast<const float4*>(ostage + r * D + 4 * c4);
+        float* dst = single ? a.out + (((int64_t)b * T + r / G) * a.Hq + g * G + r % G) * D
+                            : a.part_acc + (((int64_t)bg * a.nparts + split) * R + r) * D;
+        *reinterpret_cast<float4*>(dst + 4 * c4) = v;
     }
 }
 
@@ -691,12 +715,14 @@ AttnPlan plan_attn(int B, int Hkv, int T, int Hq, int dv, int N, int chunk, bool
     const int64_t bg = (int64_t)B * Hkv;
     const int R = (Hq / Hkv) * T;
     const int64_t tiles = (int64_t)N * ((chunk + 31) / 32);
-    // about two rounds of three resident blocks per CU; for long unions at least
-    // ~20 tiles of a full union per range (about 11 at the usual half-full union:
-    // shorter ranges spend more on their prologue and on the merge than they gain
-    // in parallelism), for short ones (latency-bound) at least ~6; never more
-    // entries per range than the fast path stages in LDS
-    int64_t want = (1536 + bg - 1) / bg;
+    // about 512 blocks: two resident per CU, one round.  Fewer, longer ranges
+    // write fewer partials (at B * Hkv >= 512 none at all, and no merge), and the
+    // partial writes cost far more than their bytes suggest while the ranges'
+    // gathers stream.  For long unions at least ~20 tiles of a full union per
+    // range (about 11 at the usual half-full union), for short ones
+    // (latency-bound) at least ~6; never more entries per range than the fast
+    // path stages in LDS
+    int64_t want = (512 + bg - 1) / bg;
     int64_t by_work = tiles >= 120 ? tiles / 20 : tiles / 6;
     if (by_work < 1) by_work = 1;
     int64_t s = want < by_work ? want : by_work;

@@ -542,6 +542,34 @@ def test_attention_fast_shape_many_heads(dkb):
             assert max_abs(lse[b:b + 1, :, g * w.G:(g + 1) * w.G], rl_) <= tol, (b, g)
 
 
+def test_attention_one_range_per_head(dkb):
+    """512 (b, g) with full 128-chunk unions: one range per (b, g), so the fast
+    path writes the normalised rows itself (no partials, no merge); the oracle
+    checks sampled (b, g)."""
+    w = workload("llama8b_l32k", 64, 4096, k=64)
+    N = w.T * w.k
+    assert w.B * w.Hkv == 512 and N == w.C
+    assert dkb.attn_workspace_size(w.B, w.Hkv, w.T, w.Hq, w.d, N, w.chunk) == 0
+    q, K, V = make(w, 75)
+    rng = np.random.default_rng(75)
+    counts = np.full((w.B, w.Hkv), N)
+    ids, mem, cnt, lists = random_unions(rng, w.B, w.Hkv, N, w.C, counts)
+    out, lse = dkb.sparse_decode_attn(q, K, V, to_dev(ids), to_dev(mem, torch.uint8), to_dev(cnt), w.chunk,
+                                      w.scale)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    qh = q.cpu().numpy().astype(np.float64)
+    tol = ATOL[w.kv_dtype]
+    for b in [0, 13, 37, 63]:
+        for g in [0, 5, 7]:
+            Kh = synth.to_numpy_f64(K[b:b + 1, g:g + 1])
+            Vh = synth.to_numpy_f64(V[b:b + 1, g:g + 1])
+            ro_, rl_ = oracle_attention_lists(qh[b:b + 1, :, g * w.G:(g + 1) * w.G], Kh, Vh, [[lists[b][g]]],
+                                              w.chunk, w.scale, w.G)
+            assert max_abs(out[b:b + 1, :, g * w.G:(g + 1) * w.G], ro_) <= tol, (b, g)
+            assert max_abs(lse[b:b + 1, :, g * w.G:(g + 1) * w.G], rl_) <= tol, (b, g)
+
+
 # ----------------------------------------------------------------------------
 # gather
 # ----------------------------------------------------------------------------
