@@ -268,9 +268,9 @@ dk_status dk_score_coverage(const float* q, int B, int T, int Hq, const void* lm
  *
  * DualDecoder "4.1": the index comes from the queries and the landmarks;
  * Adaptive DHiSparse, Figure 3 (2): the queries' selections are resolved
- * together.  With a landmark shadow the last of the T selection blocks of each
- * (b, g) merges the union itself, so the step needs no separate union launch;
- * otherwise the union runs as dk_union_select would.  Every output equals what
+ * together.  With a landmark shadow one selection block per (b, g) selects for
+ * both tokens and merges the union from its LDS, so the step needs no separate
+ * union launch; otherwise the union runs as dk_union_select would.  Every output equals what
  * dk_score_topk followed by dk_union_select(plan = NULL) writes.
  *
  * Arguments: as dk_score_topk, plus the union outputs of dk_union_select

@@ -48,12 +48,35 @@ __device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
                                   false);
 }
 
+// Exclusive prefix sum within a group of kThreads threads (group g holds
+// threads g * kThreads .. + kThreads - 1 of the block; a kThreads block is one
+// group).  scratch: 4 ints of the group's own LDS.  Every thread of the block
+// must call it: it holds two block barriers.
+__device__ __forceinline__ int group_exclusive_scan(int v, int* scratch, int* total) {
+    const int lane = threadIdx.x & (kWave - 1), gw = (threadIdx.x / kWave) & 3;
+    const int inc = wave_inclusive_scan(v);
+    if (lane == kWave - 1) scratch[gw] = inc;
+    __syncthreads();
+    int pre = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const int c = scratch[w];
+        pre += w < gw ? c : 0;
+        tot += c;
+    }
+    *total = tot;
+    __syncthreads();   // scratch is rewritten by the next call
+    return pre + inc - v;
+}
+
 // The k-th largest of keys[0..n) (1 <= k <= n) by an 8-bit radix select; also
 // returns how many of the keys equal to it belong to the k largest (*need).
-// Uses `hist` (256 uint) and `bc` (2 int) of LDS.  Every thread must call it.
+// Uses `hist` (256 uint) and `bc` (2 int) of LDS.  Works within a group of
+// kThreads threads (its keys and LDS its own); every thread of the block must
+// call it, the same number of times.
 __device__ uint32_t block_kth_key(const uint32_t* keys, int n, int k, uint32_t* hist, int* bc,
                                   int* need_out) {
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x & (kThreads - 1);
     uint32_t prefix = 0, pmask = 0;
     int need = k;
     for (int shift = 24; shift >= 0; shift -= 8) {
@@ -201,12 +224,13 @@ __device__ uint32_t wave_kth_key(const uint32_t (&x)[4], int k, uint32_t* hist, 
 
 // Select the k largest keys of keys[0..n) (k <= n), ties to the lower position,
 // and call emit(j, position, key) for j = 0..k-1 in ascending position order.
-// Uses `hist` (256 uint), `scratch` (>= 5 int) and `bc` (2 int) of LDS.  Every
-// thread of the block must call it.
+// Uses `hist` (256 uint), `scratch` (>= 4 int) and `bc` (2 int) of LDS.  Works
+// within a group of kThreads threads, like block_kth_key; every thread of the
+// block must call it.
 template <typename Emit>
 __device__ void block_topk(const uint32_t* keys, int n, int k, uint32_t* hist, int* scratch,
                            int* bc, Emit emit) {
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x & (kThreads - 1);
     int need;
     const uint32_t thr = block_kth_key(keys, n, k, hist, bc, &need);
     // keys > thr are all taken; of the keys == thr, the `need` lowest positions.
@@ -215,7 +239,7 @@ __device__ void block_topk(const uint32_t* keys, int n, int k, uint32_t* hist, i
     int eq = 0;
     for (int i = lo; i < hi; ++i) eq += keys[i] == thr;
     int tot;
-    const int eq_before = block_exclusive_scan(eq, scratch, &tot);
+    const int eq_before = group_exclusive_scan(eq, scratch, &tot);
     int sel = 0, er = eq_before;
     for (int i = lo; i < hi; ++i) {
         const uint32_t key = keys[i];
@@ -223,7 +247,7 @@ __device__ void block_topk(const uint32_t* keys, int n, int k, uint32_t* hist, i
         er += key == thr;
         sel += take;
     }
-    int pos = block_exclusive_scan(sel, scratch, &tot);
+    int pos = group_exclusive_scan(sel, scratch, &tot);
     er = eq_before;
     for (int i = lo; i < hi; ++i) {
         const uint32_t key = keys[i];
@@ -484,8 +508,7 @@ __global__ __launch_bounds__(kThreads) void k_score_lo(const float* __restrict__
                                                       const uint8_t* __restrict__ lm8,
                                                       const float* __restrict__ chunk_scale, int Hkv, int C,
                                                       float scale, int rows_per_block, int blocks_per_bg,
-                                                      float* __restrict__ s_lo, uint32_t* __restrict__ arrivals,
-                                                      float* __restrict__ kq) {
+                                                      float* __restrict__ s_lo, float* __restrict__ kq) {
     constexpr int LPR = D / 16, RPW = kWave / LPR, U = DK_SCORE_LO_UNROLL;
     constexpr int G = MAXRED ? NQ / T : 0;
     extern __shared__ float sres[];    // [T][rows_per_block], then [NQ][D] query vectors
@@ -497,8 +520,6 @@ __global__ __launch_bounds__(kThreads) void k_score_lo(const float* __restrict__
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int rp = lane / LPR, part = lane % LPR;
     const int Gq = Hq / Hkv;
-    // the selection kernel that follows counts its (b, g, t) blocks from zero
-    if (arrivals && blk == 0 && threadIdx.x == 0) arrivals[bg] = 0u;
 
     // The first rows are requested before anything else: their loads overlap
     // the query staging below.
@@ -642,41 +663,52 @@ __global__ __launch_bounds__(kThreads) void k_score_lo(const float* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// Shadow pass 2, one block per (b, g, t).  Every chunk's fp32 score s (as this
-// kernel computes it) lies in [s_lo - d_c, s_lo + d_c] with d_c = K * s_c, K
-// from the query's 1-norm (the derivation is at the bound below).  L, at most
-// the k-th largest per-thread maximum of s_lo - d_c, is a lower bound of the
-// k-th largest s; the candidates {c : s_lo[c] + d_c >= L} hold every chunk of
-// the top k, ties included.  Their fp32 re-scores give the exact top-k (ties to the lower
-// id), written in ascending order.
+// Shadow pass 2, one block per (b, g) and one group of kThreads threads per
+// query token t.  Every chunk's fp32 score s (as this kernel computes it) lies
+// in [s_lo - d_c, s_lo + d_c] with d_c = K * s_c, K from the query's 1-norm
+// (the derivation is at the bound below).  L, at most the k-th largest
+// per-thread maximum of s_lo - d_c, is a lower bound of the k-th largest s; the
+// candidates {c : s_lo[c] + d_c >= L} hold every chunk of the top k, ties
+// included.  Their fp32 re-scores give the exact top-k (ties to the lower id),
+// written in ascending order.  With a union output the block then merges the T
+// lists, which it still holds in LDS.
 // ---------------------------------------------------------------------------
+// 32-bit words of one group's LDS: keys [Cp] | cand [max(Cp, 256)] | qv [nvec][D]
+// | hist [256] | scratch [8] | bc [2] | ncand [2], Cp = C rounded up to 4 so that
+// every array starts on 16 bytes
+__host__ __device__ inline size_t select_group_words(int C, int D, int nvec) {
+    const int Cp = (C + 3) & ~3;
+    return (size_t)Cp + (size_t)(Cp > 256 ? Cp : 256) + (size_t)nvec * D + 256 + 12;
+}
+
 template <int D, bool MAXRED>
-__global__ __launch_bounds__(kThreads) void k_select_exact(
+__global__ __launch_bounds__(2 * kThreads) void k_select_exact(
     const float* __restrict__ q, int T, int Hq, const float* __restrict__ lm, dk_strides ls,
     const float* __restrict__ chunk_scale, const float* __restrict__ scale_max, const float* __restrict__ s_lo,
     int Hkv, int C, int k,
     float scale, int32_t* __restrict__ topk_idx, float* __restrict__ topk_score, UnionOut un,
-    uint32_t* __restrict__ arrivals, const float* __restrict__ kq) {
+    const float* __restrict__ kq) {
     constexpr int LPR = D / 8;                 // lanes per fp32 row, 8 floats each
     constexpr int RPW = kWave / LPR;
     extern __shared__ uint32_t smem2[];
-    // LDS: keys [Cp] | cand [max(Cp, 256)] | qv [nvec][D] | hist [256] | scratch [8] | bc [2],
-    // Cp = C rounded up to 4 so that every array starts on 16 bytes
     const int Cp = (C + 3) & ~3;
-    uint32_t* keys = smem2;
+    const int Gq = Hq / Hkv;
+    const int nvec = MAXRED ? Gq : 1;
+    const int t = threadIdx.x / kThreads;                     // this group's query token
+    uint32_t* gbase = smem2 + (size_t)t * select_group_words(C, D, nvec);
+    uint32_t* keys = gbase;
     int32_t* cand = (int32_t*)(keys + Cp);
     uint32_t* cand_u = (uint32_t*)cand;
     float* qv = (float*)(cand + (Cp > kThreads ? Cp : kThreads));
-    const int Gq = Hq / Hkv;
-    const int nvec = MAXRED ? Gq : 1;
     uint32_t* hist = (uint32_t*)(qv + nvec * D);     // [256]
     int* scratch = (int*)(hist + 256);               // [8]
     int* bc = scratch + 8;                           // [2]
+    int* ncand_all = (int*)(smem2 + select_group_words(C, D, nvec)) - 2;   // group 0's last 2 words
 
-    int bg, t;
-    xcd_unit(blockIdx.x, T, gridDim.x / T, bg, t);
+    int bg, unused;
+    xcd_unit(blockIdx.x, 1, gridDim.x, bg, unused);
     const int b = bg / Hkv, g = bg - b * Hkv;
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int tid = threadIdx.x & (kThreads - 1), lane = tid & (kWave - 1), wave = tid / kWave;
 
     // Every independent global load first: this thread's contiguous range of
     // shadow scores and chunk scales (kept in registers), the query rows.
@@ -760,11 +792,16 @@ __global__ __launch_bounds__(kThreads) void k_select_exact(
 #pragma unroll
     for (int i = 0; i < KPT; ++i) mine += (lo + i < hi) && kr[i] >= thr_key;
     int ncand;
-    int pos = block_exclusive_scan(mine, scratch, &ncand);
+    int pos = group_exclusive_scan(mine, scratch, &ncand);
 #pragma unroll
     for (int i = 0; i < KPT; ++i)
         if ((lo + i < hi) && kr[i] >= thr_key) cand[pos++] = lo + i;
+    if (tid == 0) ncand_all[t] = ncand;
     __syncthreads();
+    // the wave selection below needs at most 256 candidates in every group (a
+    // block-uniform choice: the block selection holds block barriers)
+    bool wide = false;
+    for (int u = 0; u < T; ++u) wide = wide || ncand_all[u] > kThreads;
 
     // exact fp32 scores of the candidates (keys[] is reused for them); UG rows
     // per lane group are loaded before any is used, so the gathers overlap
@@ -815,12 +852,20 @@ __global__ __launch_bounds__(kThreads) void k_select_exact(
     __syncthreads();
     int32_t* oi = topk_idx + ((int64_t)bg * T + t) * k;
     float* os = topk_score ? topk_score + ((int64_t)bg * T + t) * k : nullptr;
-    if (ncand <= kThreads) {
+    // the group's k ids in ascending order also go to sel[] (over keys[], once
+    // the selection has read them) for the union below
+    int32_t* sel = (int32_t*)keys;
+    if (!wide) {
         // one wave: exact k-th key, then the winners in ascending position order
         if (wave == 0) {
             uint32_t x[4];
+            int32_t cid[4];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) x[v] = lane + 64 * v < ncand ? keys[lane + 64 * v] : 0u;
+            for (int v = 0; v < 4; ++v) {
+                const bool in = lane + 64 * v < ncand;
+                x[v] = in ? keys[lane + 64 * v] : 0u;
+                cid[v] = in ? cand[lane + 64 * v] : 0;
+            }
             int need;
             const uint32_t thr2 = wave_kth_key_bisect(x, k, &need);
             const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -835,7 +880,8 @@ __global__ __launch_bounds__(kThreads) void k_select_exact(
                 if (take) {
                     const int jpos = base + __builtin_popcountll(tm & below);
                     if (jpos < k) {
-                        store_agent(oi + jpos, cand[lane + 64 * v]);
+                        oi[jpos] = cid[v];
+                        sel[jpos] = cid[v];
                         if (os) os[jpos] = key_score(x[v]);
                     }
                 }
@@ -844,42 +890,30 @@ __global__ __launch_bounds__(kThreads) void k_select_exact(
             }
         }
     } else {
+        // the ids also go to sel[] through global memory, as emit runs while
+        // the selection still reads keys[]
         block_topk(keys, ncand, k, hist, scratch, bc, [&](int jpos, int i, uint32_t key) {
-            store_agent(oi + jpos, cand[i]);
+            oi[jpos] = cand[i];
             if (os) os[jpos] = key_score(key);
         });
+        __syncthreads();
+        for (int i = tid; i < k; i += kThreads) sel[i] = oi[i];
     }
     if (un.ids == nullptr) return;
 
-    // Union of the (b, g)'s T sets, by the last of its T blocks to finish.  The
-    // ids above were stored at agent scope; once every lane's stores have
-    // completed the block counts itself in, and the last block reads all T sets
-    // back at agent scope.  The score pass of the same call zeroed the counter;
-    // the last block rezeroes it.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // Union of the (b, g)'s T sets (block-wide; sel[] of group 1 is s1).
     __syncthreads();
-    if (tid == 0)
-        scratch[7] = __hip_atomic_fetch_add(&arrivals[bg], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                     (unsigned)(T - 1);
-    __syncthreads();
-    if (!scratch[7]) return;
-    int32_t* s0 = (int32_t*)keys;        // keys[] and cand[] are free now
-    int32_t* s1 = s0 + k;
-    int32_t* dup_pre = s1 + k;
-    const int32_t* src = topk_idx + (int64_t)bg * T * k;
-    for (int i = tid; i < k; i += kThreads) {
-        s0[i] = load_agent(src + i);
-        s1[i] = T == 2 ? load_agent(src + k + i) : 0;
-    }
-    __syncthreads();
+    int32_t* s0 = (int32_t*)smem2;
+    int32_t* s1 = (int32_t*)(smem2 + select_group_words(C, D, nvec));
+    int32_t* dup_pre = (int32_t*)smem2 + Cp;              // group 0's cand[] (k + 1 ints)
+    int* uscratch = (int*)(smem2 + (size_t)Cp + (Cp > kThreads ? Cp : kThreads) + nvec * D);   // group 0's hist[]
     const int N = T * k;
     int nshared;
     const int count = block_union_two(s0, s1, T, k, un.ids + (int64_t)bg * N, un.member + (int64_t)bg * N,
-                                      dup_pre, scratch, nullptr, &nshared);
-    if (tid == 0) {
+                                      dup_pre, uscratch, nullptr, &nshared);
+    if (threadIdx.x == 0) {
         un.count[bg] = count;
         if (un.overlap) un.overlap[bg] = nshared;
-        arrivals[bg] = 0u;
     }
 }
 
@@ -922,22 +956,22 @@ hipError_t dispatch_split(int nq, int T, bool maxred, const float* q, int B, int
 template <int D, int NQ, int T, bool MAXRED>
 hipError_t launch_lo(const float* q, int B, int Hq, const uint8_t* lm8, const float* cscale, int Hkv, int C,
                      float scale,
-                     const TopkPlan& p, float* s_lo, uint32_t* arrivals, float* kq, hipStream_t st) {
+                     const TopkPlan& p, float* s_lo, float* kq, hipStream_t st) {
     const size_t lds = (((size_t)T * p.rows + 3) & ~(size_t)3) * 4 + (size_t)NQ * D * 4;
     const unsigned grid = (unsigned)((int64_t)B * Hkv * p.splits);
     hipLaunchKernelGGL((k_score_lo<D, NQ, T, MAXRED>), dim3(grid), dim3(kThreads), lds, st, q, Hq, lm8, cscale,
-                       Hkv, C, scale, p.rows, p.splits, s_lo, arrivals, kq);
+                       Hkv, C, scale, p.rows, p.splits, s_lo, kq);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t dispatch_lo(int nq, int T, bool maxred, const float* q, int B, int Hq, const uint8_t* lm8,
                        const float* cscale,
-                       int Hkv, int C, float scale, const TopkPlan& p, float* s_lo, uint32_t* arrivals, float* kq,
+                       int Hkv, int C, float scale, const TopkPlan& p, float* s_lo, float* kq,
                        hipStream_t st) {
 #define DK_LO(NQ_, T_, MX_) \
     if (nq == NQ_ && T == T_ && maxred == MX_) \
-        return launch_lo<D, NQ_, T_, MX_>(q, B, Hq, lm8, cscale, Hkv, C, scale, p, s_lo, arrivals, kq, st);
+        return launch_lo<D, NQ_, T_, MX_>(q, B, Hq, lm8, cscale, Hkv, C, scale, p, s_lo, kq, st);
     DK_LO(1, 1, false)
     DK_LO(2, 2, false)
     DK_LO(1, 1, true)
@@ -985,9 +1019,8 @@ TopkPlan plan_topk(int B, int Hkv, int T, int C, int k, bool shadow) {
             p.splits -= 1;
             p.rows = (C + p.splits - 1) / p.splits;
         }
-        // shadow-pass scores, one arrival counter per (b, g) for the fused union, the
-        // bound factor per (b, g, t)
-        p.ws_bytes = (((size_t)bg * T * C * 4 + 15) & ~(size_t)15) + (size_t)bg * 4 + (size_t)bg * T * 4;
+        // shadow-pass scores, the bound factor per (b, g, t)
+        p.ws_bytes = (((size_t)bg * T * C * 4 + 15) & ~(size_t)15) + (size_t)bg * T * 4;
         return p;
     }
     int64_t want = (2048 + bg - 1) / bg;
@@ -1014,11 +1047,6 @@ TopkPlan plan_topk(int B, int Hkv, int T, int C, int k, bool shadow) {
     return p;
 }
 
-size_t select_lds_bytes(int C, int D, int nvec) {
-    const int Cp = (C + 3) & ~3;
-    return (size_t)(Cp + (Cp > 256 ? Cp : 256) + nvec * D + 256 + 12) * 4;
-}
-
 hipError_t launch_build_shadow(const float* lm, dk_strides ls, int B, int Hkv, int C, int d,
                                uint8_t* lm8, float* chunk_scale, float* scale_max, hipStream_t st) {
     const unsigned grid = (unsigned)((int64_t)B * Hkv);
@@ -1041,28 +1069,27 @@ hipError_t launch_score_topk(const float* q, int B, int T, int Hq, const float* 
     const int64_t bg = (int64_t)B * Hkv;
     if (shadow) {
         float* s_lo = (float*)ws;
-        // the selection kernel merges the union itself when s0, s1 and the scan
-        // prefix (3k + 1 ints) fit where its keys and candidates were
+        // the selection kernel merges the union itself when the merge's scan
+        // prefix (k + 1 ints) fits where its first group's candidates were
         const int Cp = (C + 3) & ~3;
-        const bool fuse = un && 3 * (int64_t)k + 1 <= (int64_t)Cp + (Cp > kThreads ? Cp : kThreads);
-        // workspace: scores [bg, T, C] | one arrival counter per (b, g) | the bound factor per (b, g, t)
+        const bool fuse = un && (int64_t)k + 1 <= (int64_t)(Cp > kThreads ? Cp : kThreads);
+        // workspace: scores [bg, T, C] | the bound factor per (b, g, t)
         const size_t sbytes = ((size_t)bg * T * C * 4 + 15) & ~(size_t)15;
-        uint32_t* arrivals = fuse ? (uint32_t*)((char*)ws + sbytes) : nullptr;
-        float* kq = (float*)((char*)ws + sbytes + (size_t)bg * 4);
+        float* kq = (float*)((char*)ws + sbytes);
         hipError_t e = d == 128
             ? dispatch_lo<128>(nq, T, maxred, q, B, Hq, shadow->lm8, shadow->chunk_scale, Hkv, C, scale, p, s_lo,
-                               arrivals, kq, st)
+                               kq, st)
             : dispatch_lo<64>(nq, T, maxred, q, B, Hq, shadow->lm8, shadow->chunk_scale, Hkv, C, scale, p, s_lo,
-                              arrivals, kq, st);
+                              kq, st);
         if (e != hipSuccess) return e;
-        const unsigned grid = (unsigned)(bg * T);
-        const size_t lds = select_lds_bytes(C, d, maxred ? G : 1);
+        // one block per (b, g), one group of kThreads threads per query token
+        const unsigned grid = (unsigned)bg;
+        const size_t lds = (size_t)T * select_group_words(C, d, maxred ? G : 1) * 4;
         const UnionOut none{nullptr, nullptr, nullptr, nullptr};
         const UnionOut uo = fuse ? *un : none;
 #define DK_SEL(D_, MX_)                                                                            \
-    hipLaunchKernelGGL((k_select_exact<D_, MX_>), dim3(grid), dim3(kThreads), lds, st, q, T, Hq, lm, ls, \
-                       shadow->chunk_scale, shadow->scale_max, s_lo, Hkv, C, k, scale, topk_idx, topk_score, uo, \
-                       arrivals, kq)
+    hipLaunchKernelGGL((k_select_exact<D_, MX_>), dim3(grid), dim3(kThreads * T), lds, st, q, T, Hq, lm, ls, \
+                       shadow->chunk_scale, shadow->scale_max, s_lo, Hkv, C, k, scale, topk_idx, topk_score, uo, kq)
         if (d == 128) { if (maxred) DK_SEL(128, true); else DK_SEL(128, false); }
         else { if (maxred) DK_SEL(64, true); else DK_SEL(64, false); }
 #undef DK_SEL

@@ -110,10 +110,9 @@ def test_score_topk_union_rejects(kw, status):
 def test_score_topk_workspace_sizes():
     # 64 x 8 (b, g) rows over 4096 chunks: 4 ranges of 1024, 64 candidates each
     assert lib.dk_score_topk_workspace_size(64, 8, 2, 4096, 64, 0) == 64 * 8 * 2 * 4 * 64 * 8
-    # with a shadow: every fp16 score of every (b, g, t), then one arrival
-    # counter per (b, g) for the fused union
-    # shadow scores [B, Hkv, T, C], one arrival counter per (b, g), one bound factor per (b, g, t)
-    assert lib.dk_score_topk_workspace_size(64, 8, 2, 4096, 64, 1) == 64 * 8 * 2 * 4096 * 4 + 64 * 8 * 4 + 64 * 8 * 2 * 4
+    # with a shadow: the shadow score of every chunk of every (b, g, t) in fp32,
+    # then one bound factor per (b, g, t)
+    assert lib.dk_score_topk_workspace_size(64, 8, 2, 4096, 64, 1) == 64 * 8 * 2 * 4096 * 4 + 64 * 8 * 2 * 4
     assert lib.dk_score_topk_workspace_size(1, 1, 2, 128, 8, 0) > 0
     assert lib.dk_score_topk_workspace_size(1, 1, 2, 128, 0, 0) == 0
 
