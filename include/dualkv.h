@@ -159,7 +159,8 @@ dk_status dk_build_landmark_shadow(const float* lm, dk_strides ls, int B, int Hk
  * topk_idx   : out, int32 [B, Hkv, T, k].
  * topk_score : out, fp32 [B, Hkv, T, k] (the selected scores, same order) or NULL.
  * ws         : workspace of dk_score_topk_workspace_size(B, Hkv, T, C, k,
- *              shadow != NULL) bytes for DK_F32 landmarks, of
+ *              shadow != NULL) bytes for DK_F32 landmarks (0 with a shadow: one
+ *              block per (b, g) then scores and selects in LDS), of
  *              dk_index_topk_workspace_size(B, Hkv, T, C) bytes for DK_BF16 keys
  *              (may be NULL when that size is 0).  Contents on entry are ignored.
  * Errors     : DK_ERR_INVALID_ARG unless 1 <= T <= 2, Hq % Hkv == 0, 1 <= k <= C,

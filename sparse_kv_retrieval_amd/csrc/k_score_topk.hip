@@ -484,15 +484,26 @@ __global__ __launch_bounds__(kThreads) void k_build_shadow(const float* __restri
 }
 
 // ---------------------------------------------------------------------------
-// Shadow pass 1: scores of every chunk from the 8-bit codes, streamed with
-// non-temporal 16-byte loads; LPR = D / 16 lanes per row, 16 codes per lane.
-// A byte pair becomes two exact fp16 values with one v_perm against the fp16
-// exponent byte 0x64 (0x64XX is 1024 + XX = code + 1152), multiplied into the
-// fp16 query with v_dot2_f32_f16; each lane then takes 1152 times its share of
-// the query sum off once, the row sums use DPP only, and the chunk's scale
-// multiplies the sum.  Two load batches alternate, so one is in flight while
-// the other is decoded.  Scores of one block's rows are staged in
-// LDS and stored coalesced to s_lo [B * Hkv, T, C] (fp32).
+// Shadow scoring and exact selection in one kernel: one block per (b, g) with
+// T groups of kThreads threads; the scores never leave LDS.
+//
+// Pass 1 (every wave): the shadow score of every chunk from the 8-bit codes,
+// streamed with non-temporal 16-byte loads; LPR = D / 16 lanes per row, 16
+// codes per lane.  A byte pair becomes two exact fp16 values with one v_perm
+// against the fp16 exponent byte 0x64 (0x64XX is 1024 + XX = code + 1152),
+// multiplied into the fp16 query with v_dot2_f32_f16; each lane then takes 1152
+// times its share of the query sum off once, the row sums use DPP only, and
+// the chunk's scale multiplies the sum.  Two load batches alternate, so one is
+// in flight while the other is decoded.
+//
+// Pass 2 (group t selects for query t).  Every chunk's fp32 score s (as this
+// kernel computes it) lies in [s_lo - d_c, s_lo + d_c] with d_c = K * s_c, K
+// from the query's 1-norm (the derivation is at the bound below).  L, at most
+// the k-th largest per-thread maximum of s_lo - d_c, is a lower bound of the
+// k-th largest s; the candidates {c : s_lo[c] + d_c >= L} hold every chunk of
+// the top k, ties included.  Their fp32 re-scores give the exact top-k (ties
+// to the lower id), written in ascending order.  With a union output the block
+// then merges the T lists, which it still holds in LDS.
 // ---------------------------------------------------------------------------
 #ifndef DK_SCORE_LO_UNROLL
 #define DK_SCORE_LO_UNROLL 2   // 16-byte code loads per lane per batch
@@ -503,219 +514,200 @@ __device__ __forceinline__ uint32_t code_pair(uint32_t w, uint32_t sel) {
     return __builtin_amdgcn_perm(0x64646464u, w, sel);
 }
 
-template <int D, int NQ, int T, bool MAXRED>
-__global__ __launch_bounds__(kThreads) void k_score_lo(const float* __restrict__ q, int Hq,
-                                                      const uint8_t* __restrict__ lm8,
-                                                      const float* __restrict__ chunk_scale, int Hkv, int C,
-                                                      float scale, int rows_per_block, int blocks_per_bg,
-                                                      float* __restrict__ s_lo, float* __restrict__ kq) {
-    constexpr int LPR = D / 16, RPW = kWave / LPR, U = DK_SCORE_LO_UNROLL;
-    constexpr int G = MAXRED ? NQ / T : 0;
-    extern __shared__ float sres[];    // [T][rows_per_block], then [NQ][D] query vectors
-    int bg, blk;
-    xcd_unit(blockIdx.x, blocks_per_bg, gridDim.x / blocks_per_bg, bg, blk);
-    const int b = bg / Hkv, g = bg - b * Hkv;
-    const int row0 = blk * rows_per_block;
-    const int nrows = min(rows_per_block, C - row0);
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    const int rp = lane / LPR, part = lane % LPR;
-    const int Gq = Hq / Hkv;
-
-    // The first rows are requested before anything else: their loads overlap
-    // the query staging below.
-    const uint8_t* base = lm8 + ((int64_t)bg * C + row0) * D + part * 16;
-    const float* sbase = chunk_scale + (int64_t)bg * C + row0;
-    constexpr int ROWS_PER_ITER = 4 * RPW * U;
-    u32x4_t xa[U], xb[U];
-    float ra[U], rb[U];
-    auto load_rows = [&](int it, u32x4_t (&xx)[U], float (&rr)[U]) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int r = it + (u * 4 + wave) * RPW + rp;
-            xx[u] = r < nrows ? nt_load_u4(base + (int64_t)r * D) : u32x4_t{0x80808080u, 0x80808080u, 0x80808080u,
-                                                                            0x80808080u};
-            rr[u] = part < T && r < nrows ? sbase[r] : 0.f;
-        }
-    };
-    load_rows(0, xa, ra);
-
-    // The query vectors of this (b, g) go through LDS once per block (one 16-byte
-    // global load per lane would otherwise be repeated by every row-lane group).
-    float* qs = sres + ((T * rows_per_block + 3) & ~3);   // [NQ][D], 16-byte aligned
-    for (int i = threadIdx.x; i < NQ * D; i += kThreads) {
-        const int v = i / D, e = i - v * D;
-        float xq;
-        if constexpr (MAXRED) {
-            xq = q[(((int64_t)b * T + v / G) * Hq + g * Gq + v % G) * D + e];
-        } else {
-            xq = 0.f;
-            for (int h = 0; h < Gq; ++h) xq += q[(((int64_t)b * T + v) * Hq + g * Gq + h) * D + e];
-            xq = xq / (float)Gq;
-        }
-        qs[i] = xq;
-    }
-    __syncthreads();
-    if (blk == 0) {
-        // The error bound's query factor for the selection pass.  With m_i the
-        // codes, s_c the chunk scale, q^ = fp16(q) and u16 = 2^-11:
-        //   |sum q_i l_i - s_c sum q^_i m_i| <= s_c (1/2 + 127 u32) |q|_1            (the codes)
-        //                                     + s_c 127 (u16 |q|_1 + D 2^-25)   (q in fp16, subnormals too),
-        // the fp32 sums here and of the fp32 re-score add at most (D + 40)
-        // roundings of terms up to 127 s_c |q_i|; the lanes sum q^_i (code_i + 1152)
-        // and take off 1152 times their fp32 sum of q^: at most 48000 u32 s_c |q|_1
-        // more; the scale products add a few relative roundings: |s - s_lo| <= kq * s_c.  A query value beyond fp16
-        // voids the bound (kq = inf: every chunk becomes a candidate).
-        float* part = sres;   // the score rows are not written yet
-        const int w = threadIdx.x / kWave;
-        for (int v = w; v < NQ; v += kThreads / kWave) {
-            float a1 = 0.f, am = 0.f;
-            for (int e = lane; e < D; e += kWave) {
-                a1 += fabsf(qs[v * D + e]);
-                am = fmaxf(am, fabsf(qs[v * D + e]));
-            }
-            for (int off = 1; off < kWave; off <<= 1) {
-                a1 += __shfl_xor(a1, off, kWave);
-                am = fmaxf(am, __shfl_xor(am, off, kWave));
-            }
-            if (lane == 0) {
-                part[2 * v] = a1;
-                part[2 * v + 1] = am;
-            }
-        }
-        __syncthreads();
-        if (threadIdx.x < T) {
-            const int t = threadIdx.x;
-            float l1 = 0.f, amax = 0.f;
-            for (int v = (MAXRED ? t * G : t); v < (MAXRED ? (t + 1) * G : t + 1); ++v) {
-                l1 = fmaxf(l1, part[2 * v]);
-                amax = fmaxf(amax, part[2 * v + 1]);
-            }
-            l1 *= 1.0f + (float)(D + 8) * 5.9604645e-8f;   // round the sum up
-            const float u16 = 4.8828125e-4f, u32 = 5.9604645e-8f;
-            float k_ = fabsf(scale) *
-                       (l1 * (0.5f + 127.f * u32 + 127.f * u16 + ((float)(D + 40) * 127.f + 48000.f) * u32) +
-                        127.f * (float)D * 2.9802322e-8f) * 1.01f;
-            if (!(amax <= 65000.f) || !(k_ <= 3.0e38f)) k_ = INFINITY;
-            kq[(int64_t)bg * T + t] = k_;
-        }
-        __syncthreads();
-    }
-    uint32_t qh[NQ][8];
-    float qbias[NQ];   // 1152 times this lane's share of the fp16 query sum
-#pragma unroll
-    for (int v = 0; v < NQ; ++v) {
-        float sq = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const _Float16 h0 = (_Float16)qs[v * D + part * 16 + 2 * j];
-            const _Float16 h1 = (_Float16)qs[v * D + part * 16 + 2 * j + 1];
-            qh[v][j] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-            sq += (float)h0 + (float)h1;
-        }
-        qbias[v] = 1152.f * sq;
-    }
-
-    auto process = [&](int it, const u32x4_t (&x)[U], const float (&rs)[U]) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int rr = it + (u * 4 + wave) * RPW + rp;
-            uint32_t h[8];
-            h[0] = code_pair(x[u].x, 0x04010400u); h[1] = code_pair(x[u].x, 0x04030402u);
-            h[2] = code_pair(x[u].y, 0x04010400u); h[3] = code_pair(x[u].y, 0x04030402u);
-            h[4] = code_pair(x[u].z, 0x04010400u); h[5] = code_pair(x[u].z, 0x04030402u);
-            h[6] = code_pair(x[u].w, 0x04010400u); h[7] = code_pair(x[u].w, 0x04030402u);
-            float dot[NQ];
-#pragma unroll
-            for (int v = 0; v < NQ; ++v) {
-                float a = dot2_f16(qh[v][0], h[0], 0.f);
-#pragma unroll
-                for (int jj = 1; jj < 8; ++jj) a = dot2_f16(qh[v][jj], h[jj], a);
-                dot[v] = dpp_group_sum<LPR>(a - qbias[v]);
-            }
-            // per-query scores with compile-time register indices
-            const float sc = scale * rs[u];
-            float sct[T];
-#pragma unroll
-            for (int t = 0; t < T; ++t) {
-                if constexpr (MAXRED) {
-                    sct[t] = sc * dot[t * G];
-#pragma unroll
-                    for (int hh = 1; hh < G; ++hh) sct[t] = fmaxf(sct[t], sc * dot[t * G + hh]);
-                } else {
-                    sct[t] = sc * dot[t];
-                }
-            }
-            if (part < T && rr < nrows) sres[part * rows_per_block + rr] = (part == 0) ? sct[0] : sct[T - 1];
-        }
-    };
-    for (int it = 0; it < nrows; it += 2 * ROWS_PER_ITER) {
-        if (it + ROWS_PER_ITER < nrows) load_rows(it + ROWS_PER_ITER, xb, rb);
-        process(it, xa, ra);
-        if (it + ROWS_PER_ITER >= nrows) break;
-        if (it + 2 * ROWS_PER_ITER < nrows) load_rows(it + 2 * ROWS_PER_ITER, xa, ra);
-        process(it + ROWS_PER_ITER, xb, rb);
-    }
-    __syncthreads();
-    for (int t = 0; t < T; ++t) {
-        float* dst = s_lo + ((int64_t)bg * T + t) * C + row0;
-        for (int i = threadIdx.x; i < nrows; i += kThreads) dst[i] = sres[t * rows_per_block + i];
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Shadow pass 2, one block per (b, g) and one group of kThreads threads per
-// query token t.  Every chunk's fp32 score s (as this kernel computes it) lies
-// in [s_lo - d_c, s_lo + d_c] with d_c = K * s_c, K from the query's 1-norm
-// (the derivation is at the bound below).  L, at most the k-th largest
-// per-thread maximum of s_lo - d_c, is a lower bound of the k-th largest s; the
-// candidates {c : s_lo[c] + d_c >= L} hold every chunk of the top k, ties
-// included.  Their fp32 re-scores give the exact top-k (ties to the lower id),
-// written in ascending order.  With a union output the block then merges the T
-// lists, which it still holds in LDS.
-// ---------------------------------------------------------------------------
 // 32-bit words of one group's LDS: keys [Cp] | cand [max(Cp, 256)] | qv [nvec][D]
-// | hist [256] | scratch [8] | bc [2] | ncand [2], Cp = C rounded up to 4 so that
-// every array starts on 16 bytes
+// | hist [256] | scratch [8] | bc [2] | misc [6], Cp = C rounded up to 4 so that
+// every array starts on 16 bytes.  Pass 1 keeps its scores [T][C] over group
+// 0's keys and cand.
 __host__ __device__ inline size_t select_group_words(int C, int D, int nvec) {
     const int Cp = (C + 3) & ~3;
-    return (size_t)Cp + (size_t)(Cp > 256 ? Cp : 256) + (size_t)nvec * D + 256 + 12;
+    return (size_t)Cp + (size_t)(Cp > 256 ? Cp : 256) + (size_t)nvec * D + 256 + 16;
 }
 
-template <int D, bool MAXRED>
-__global__ __launch_bounds__(2 * kThreads) void k_select_exact(
-    const float* __restrict__ q, int T, int Hq, const float* __restrict__ lm, dk_strides ls,
-    const float* __restrict__ chunk_scale, const float* __restrict__ scale_max, const float* __restrict__ s_lo,
-    int Hkv, int C, int k,
-    float scale, int32_t* __restrict__ topk_idx, float* __restrict__ topk_score, UnionOut un,
-    const float* __restrict__ kq) {
-    constexpr int LPR = D / 8;                 // lanes per fp32 row, 8 floats each
-    constexpr int RPW = kWave / LPR;
+template <int D, int NQ, int T, bool MAXRED>
+__global__ __launch_bounds__(T * kThreads) void k_score_select(
+    const float* __restrict__ q, int Hq, const uint8_t* __restrict__ lm8, const float* __restrict__ chunk_scale,
+    const float* __restrict__ scale_max, const float* __restrict__ lm, dk_strides ls, int Hkv, int C, int k,
+    float scale, int32_t* __restrict__ topk_idx, float* __restrict__ topk_score, UnionOut un) {
+    constexpr int NVEC = MAXRED ? NQ / T : 1;          // query vectors per group
+    constexpr int NW = T * kThreads / kWave;           // waves of the block
     extern __shared__ uint32_t smem2[];
     const int Cp = (C + 3) & ~3;
-    const int Gq = Hq / Hkv;
-    const int nvec = MAXRED ? Gq : 1;
-    const int t = threadIdx.x / kThreads;                     // this group's query token
-    uint32_t* gbase = smem2 + (size_t)t * select_group_words(C, D, nvec);
-    uint32_t* keys = gbase;
-    int32_t* cand = (int32_t*)(keys + Cp);
-    uint32_t* cand_u = (uint32_t*)cand;
-    float* qv = (float*)(cand + (Cp > kThreads ? Cp : kThreads));
-    uint32_t* hist = (uint32_t*)(qv + nvec * D);     // [256]
-    int* scratch = (int*)(hist + 256);               // [8]
-    int* bc = scratch + 8;                           // [2]
-    int* ncand_all = (int*)(smem2 + select_group_words(C, D, nvec)) - 2;   // group 0's last 2 words
+    const int cand_words = Cp > kThreads ? Cp : kThreads;
+    const size_t gw = select_group_words(C, D, NVEC);
+    auto qv_of = [&](int u) { return (float*)(smem2 + (size_t)u * gw + Cp + cand_words); };
+    auto misc_of = [&](int u) { return (int*)(smem2 + (size_t)u * gw + gw - 6); };
 
     int bg, unused;
     xcd_unit(blockIdx.x, 1, gridDim.x, bg, unused);
     const int b = bg / Hkv, g = bg - b * Hkv;
+    const int Gq = Hq / Hkv;
+
+    // ================= pass 1: shadow scores of every chunk =================
+    {
+        constexpr int LPR = D / 16, RPW = kWave / LPR, U = DK_SCORE_LO_UNROLL;
+        constexpr int G = MAXRED ? NQ / T : 0;
+        constexpr int ROWS_PER_ITER = NW * RPW * U;
+        float* sres = (float*)smem2;                   // [T][C]
+        const int lane = threadIdx.x & (kWave - 1), bw = threadIdx.x / kWave;
+        const int rp = lane / LPR, part = lane % LPR;
+
+        // The first rows are requested before anything else: their loads
+        // overlap the query staging below.
+        const uint8_t* base = lm8 + (int64_t)bg * C * D + part * 16;
+        const float* sbase = chunk_scale + (int64_t)bg * C;
+        u32x4_t xa[U], xb[U];
+        float ra[U], rb[U];
+        auto load_rows = [&](int it, u32x4_t (&xx)[U], float (&rr)[U]) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int r = it + (u * NW + bw) * RPW + rp;
+                xx[u] = r < C ? nt_load_u4(base + (int64_t)r * D)
+                              : u32x4_t{0x80808080u, 0x80808080u, 0x80808080u, 0x80808080u};
+                rr[u] = part < T && r < C ? sbase[r] : 0.f;
+            }
+        };
+        load_rows(0, xa, ra);
+
+        // The query vectors go through LDS once per block, into the groups'
+        // qv[] (vector v is vector v % NVEC of group v / NVEC), which pass 2
+        // re-scores with.
+        for (int i = threadIdx.x; i < NQ * D; i += NW * kWave) {
+            const int v = i / D, e = i - v * D;
+            float xq;
+            if constexpr (MAXRED) {
+                xq = q[(((int64_t)b * T + v / G) * Hq + g * Gq + v % G) * D + e];
+            } else {
+                xq = 0.f;
+                for (int h = 0; h < Gq; ++h) xq += q[(((int64_t)b * T + v) * Hq + g * Gq + h) * D + e];
+                xq = xq / (float)Gq;
+            }
+            qv_of(v / NVEC)[(v % NVEC) * D + e] = xq;
+        }
+        __syncthreads();
+        {
+            // The error bound's query factor for pass 2.  With m_i the codes,
+            // s_c the chunk scale, q^ = fp16(q) and u16 = 2^-11:
+            //   |sum q_i l_i - s_c sum q^_i m_i| <= s_c (1/2 + 127 u32) |q|_1            (the codes)
+            //                                     + s_c 127 (u16 |q|_1 + D 2^-25)   (q in fp16, subnormals too),
+            // the fp32 sums here and of the fp32 re-score add at most (D + 40)
+            // roundings of terms up to 127 s_c |q_i|; the lanes sum q^_i (code_i + 1152)
+            // and take off 1152 times their fp32 sum of q^: at most 48000 u32 s_c |q|_1
+            // more; the scale products add a few relative roundings: |s - s_lo| <= kq * s_c.  A query value beyond fp16
+            // voids the bound (kq = inf: every chunk becomes a candidate).
+            float* pq = qv_of(0) + NVEC * D;   // group 0's hist[]: free until pass 2
+            for (int v = bw; v < NQ; v += NW) {
+                const float* qp = qv_of(v / NVEC) + (v % NVEC) * D;
+                float a1 = 0.f, am = 0.f;
+                for (int e = lane; e < D; e += kWave) {
+                    a1 += fabsf(qp[e]);
+                    am = fmaxf(am, fabsf(qp[e]));
+                }
+                for (int off = 1; off < kWave; off <<= 1) {
+                    a1 += __shfl_xor(a1, off, kWave);
+                    am = fmaxf(am, __shfl_xor(am, off, kWave));
+                }
+                if (lane == 0) {
+                    pq[2 * v] = a1;
+                    pq[2 * v + 1] = am;
+                }
+            }
+            __syncthreads();
+            if (threadIdx.x < T) {
+                const int t = threadIdx.x;
+                float l1 = 0.f, amax = 0.f;
+                for (int v = (MAXRED ? t * G : t); v < (MAXRED ? (t + 1) * G : t + 1); ++v) {
+                    l1 = fmaxf(l1, pq[2 * v]);
+                    amax = fmaxf(amax, pq[2 * v + 1]);
+                }
+                l1 *= 1.0f + (float)(D + 8) * 5.9604645e-8f;   // round the sum up
+                const float u16 = 4.8828125e-4f, u32 = 5.9604645e-8f;
+                float k_ = fabsf(scale) *
+                           (l1 * (0.5f + 127.f * u32 + 127.f * u16 + ((float)(D + 40) * 127.f + 48000.f) * u32) +
+                            127.f * (float)D * 2.9802322e-8f) * 1.01f;
+                if (!(amax <= 65000.f) || !(k_ <= 3.0e38f)) k_ = INFINITY;
+                misc_of(t)[1] = __float_as_int(k_);
+            }
+        }
+        uint32_t qh[NQ][8];
+        float qbias[NQ];   // 1152 times this lane's share of the fp16 query sum
+#pragma unroll
+        for (int v = 0; v < NQ; ++v) {
+            const float* qp = qv_of(v / NVEC) + (v % NVEC) * D;
+            float sq = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const _Float16 h0 = (_Float16)qp[part * 16 + 2 * j];
+                const _Float16 h1 = (_Float16)qp[part * 16 + 2 * j + 1];
+                qh[v][j] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+                           ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+                sq += (float)h0 + (float)h1;
+            }
+            qbias[v] = 1152.f * sq;
+        }
+
+        auto process = [&](int it, const u32x4_t (&x)[U], const float (&rs)[U]) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int rr = it + (u * NW + bw) * RPW + rp;
+                uint32_t h[8];
+                h[0] = code_pair(x[u].x, 0x04010400u); h[1] = code_pair(x[u].x, 0x04030402u);
+                h[2] = code_pair(x[u].y, 0x04010400u); h[3] = code_pair(x[u].y, 0x04030402u);
+                h[4] = code_pair(x[u].z, 0x04010400u); h[5] = code_pair(x[u].z, 0x04030402u);
+                h[6] = code_pair(x[u].w, 0x04010400u); h[7] = code_pair(x[u].w, 0x04030402u);
+                float dot[NQ];
+#pragma unroll
+                for (int v = 0; v < NQ; ++v) {
+                    float a = dot2_f16(qh[v][0], h[0], 0.f);
+#pragma unroll
+                    for (int jj = 1; jj < 8; ++jj) a = dot2_f16(qh[v][jj], h[jj], a);
+                    dot[v] = dpp_group_sum<LPR>(a - qbias[v]);
+                }
+                // per-query scores with compile-time register indices
+                const float sc = scale * rs[u];
+                float sct[T];
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    if constexpr (MAXRED) {
+                        sct[t] = sc * dot[t * G];
+#pragma unroll
+                        for (int hh = 1; hh < G; ++hh) sct[t] = fmaxf(sct[t], sc * dot[t * G + hh]);
+                    } else {
+                        sct[t] = sc * dot[t];
+                    }
+                }
+                if (part < T && rr < C) sres[part * C + rr] = (part == 0) ? sct[0] : sct[T - 1];
+            }
+        };
+        for (int it = 0; it < C; it += 2 * ROWS_PER_ITER) {
+            if (it + ROWS_PER_ITER < C) load_rows(it + ROWS_PER_ITER, xb, rb);
+            process(it, xa, ra);
+            if (it + ROWS_PER_ITER >= C) break;
+            if (it + 2 * ROWS_PER_ITER < C) load_rows(it + 2 * ROWS_PER_ITER, xa, ra);
+            process(it + ROWS_PER_ITER, xb, rb);
+        }
+        __syncthreads();
+    }
+
+    // ================= pass 2: exact top-k of group t's query ================
+    constexpr int LPR = D / 8;                 // lanes per fp32 row, 8 floats each
+    constexpr int RPW = kWave / LPR;
+    const int t = threadIdx.x / kThreads;
+    uint32_t* keys = smem2 + (size_t)t * gw;
+    int32_t* cand = (int32_t*)(keys + Cp);
+    uint32_t* cand_u = (uint32_t*)cand;
+    float* qv = qv_of(t);
+    uint32_t* hist = (uint32_t*)(qv + NVEC * D);     // [256]
+    int* scratch = (int*)(hist + 256);               // [8]
+    int* bc = scratch + 8;                           // [2]
+    int* misc = misc_of(t);                          // [0] candidates, [1] bound factor (bits)
     const int tid = threadIdx.x & (kThreads - 1), lane = tid & (kWave - 1), wave = tid / kWave;
 
-    // Every independent global load first: this thread's contiguous range of
-    // shadow scores and chunk scales (kept in registers), the query rows.
+    // this thread's contiguous range of shadow scores (LDS) and chunk scales
+    // (global: pass 1 just read them), kept in registers
     constexpr int KPT = kShadowMaxC / kThreads;      // scores per thread, at most
     const int per = (C + kThreads - 1) / kThreads;
     const int lo = min(C, tid * per), hi = min(C, lo + per);
-    const float* sl = s_lo + ((int64_t)bg * T + t) * C;
+    const float* sl = (const float*)smem2 + t * C;
     const float* cs = chunk_scale + (int64_t)bg * C;
     float sv[KPT], sc[KPT];
     if ((per & 3) == 0 && (C & 3) == 0) {
@@ -739,21 +731,11 @@ __global__ __launch_bounds__(2 * kThreads) void k_select_exact(
         }
     }
     const float SM = scale_max[bg];
-    const float Kq = kq[(int64_t)bg * T + t];
-    for (int i = tid; i < nvec * D; i += kThreads) {
-        const int v = i / D, e = i - v * D;
-        float x;
-        if (MAXRED) {
-            x = q[(((int64_t)b * T + t) * Hq + g * Gq + v) * D + e];
-        } else {
-            x = 0.f;
-            for (int h = 0; h < Gq; ++h) x += q[(((int64_t)b * T + t) * Hq + g * Gq + h) * D + e];
-            x = x / (float)Gq;
-        }
-        qv[i] = x;
-    }
-    // the bound |s - s_lo| <= Kq * s_c (Kq from the score pass); a landmark the
-    // codes cannot hold, or Kq = inf, voids it: every chunk is then a candidate
+    const float Kq = __int_as_float(misc[1]);
+    __syncthreads();   // every score is in registers: the scores' LDS is reused from here on
+
+    // the bound |s - s_lo| <= Kq * s_c (Kq from pass 1); a landmark the codes
+    // cannot hold, or Kq = inf, voids it: every chunk is then a candidate
     const bool valid = SM <= 3.0e38f && Kq <= 3.0e38f;
     uint32_t kr[KPT];
     uint32_t tmax = 0u;
@@ -796,12 +778,12 @@ __global__ __launch_bounds__(2 * kThreads) void k_select_exact(
 #pragma unroll
     for (int i = 0; i < KPT; ++i)
         if ((lo + i < hi) && kr[i] >= thr_key) cand[pos++] = lo + i;
-    if (tid == 0) ncand_all[t] = ncand;
+    if (tid == 0) misc[0] = ncand;
     __syncthreads();
     // the wave selection below needs at most 256 candidates in every group (a
     // block-uniform choice: the block selection holds block barriers)
     bool wide = false;
-    for (int u = 0; u < T; ++u) wide = wide || ncand_all[u] > kThreads;
+    for (int u = 0; u < T; ++u) wide = wide || misc_of(u)[0] > kThreads;
 
     // exact fp32 scores of the candidates (keys[] is reused for them); UG rows
     // per lane group are loaded before any is used, so the gathers overlap
@@ -833,7 +815,7 @@ __global__ __launch_bounds__(2 * kThreads) void k_select_exact(
             float best;
             if (MAXRED) {
                 best = -INFINITY;
-                for (int v = 0; v < nvec; ++v) {
+                for (int v = 0; v < NVEC; ++v) {
                     float a = 0.f;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) a = fmaf(qv[v * D + part * 8 + e], x[u][e], a);
@@ -904,9 +886,9 @@ __global__ __launch_bounds__(2 * kThreads) void k_select_exact(
     // Union of the (b, g)'s T sets (block-wide; sel[] of group 1 is s1).
     __syncthreads();
     int32_t* s0 = (int32_t*)smem2;
-    int32_t* s1 = (int32_t*)(smem2 + select_group_words(C, D, nvec));
+    int32_t* s1 = (int32_t*)(smem2 + gw);
     int32_t* dup_pre = (int32_t*)smem2 + Cp;              // group 0's cand[] (k + 1 ints)
-    int* uscratch = (int*)(smem2 + (size_t)Cp + (Cp > kThreads ? Cp : kThreads) + nvec * D);   // group 0's hist[]
+    int* uscratch = (int*)(qv_of(0) + NVEC * D);          // group 0's hist[]
     const int N = T * k;
     int nshared;
     const int count = block_union_two(s0, s1, T, k, un.ids + (int64_t)bg * N, un.member + (int64_t)bg * N,
@@ -916,6 +898,7 @@ __global__ __launch_bounds__(2 * kThreads) void k_select_exact(
         if (un.overlap) un.overlap[bg] = nshared;
     }
 }
+
 
 template <int D, int NQ, int T, bool MAXRED>
 hipError_t launch_split(const float* q, int B, int Hq, const float* lm, dk_strides ls, int Hkv,
@@ -954,73 +937,51 @@ hipError_t dispatch_split(int nq, int T, bool maxred, const float* q, int B, int
 }
 
 template <int D, int NQ, int T, bool MAXRED>
-hipError_t launch_lo(const float* q, int B, int Hq, const uint8_t* lm8, const float* cscale, int Hkv, int C,
-                     float scale,
-                     const TopkPlan& p, float* s_lo, float* kq, hipStream_t st) {
-    const size_t lds = (((size_t)T * p.rows + 3) & ~(size_t)3) * 4 + (size_t)NQ * D * 4;
-    const unsigned grid = (unsigned)((int64_t)B * Hkv * p.splits);
-    hipLaunchKernelGGL((k_score_lo<D, NQ, T, MAXRED>), dim3(grid), dim3(kThreads), lds, st, q, Hq, lm8, cscale,
-                       Hkv, C, scale, p.rows, p.splits, s_lo, kq);
+hipError_t launch_score_select(const float* q, int B, int Hq, const dk_landmark_shadow* sh, const float* lm,
+                               dk_strides ls, int Hkv, int C, int k, float scale, int32_t* topk_idx,
+                               float* topk_score, const UnionOut& un, hipStream_t st) {
+    constexpr int NVEC = MAXRED ? NQ / T : 1;
+    const size_t lds = (size_t)T * select_group_words(C, D, NVEC) * 4;
+    hipLaunchKernelGGL((k_score_select<D, NQ, T, MAXRED>), dim3((unsigned)((int64_t)B * Hkv)), dim3(T * kThreads),
+                       lds, st, q, Hq, sh->lm8, sh->chunk_scale, sh->scale_max, lm, ls, Hkv, C, k, scale, topk_idx,
+                       topk_score, un);
     return hipGetLastError();
 }
 
 template <int D>
-hipError_t dispatch_lo(int nq, int T, bool maxred, const float* q, int B, int Hq, const uint8_t* lm8,
-                       const float* cscale,
-                       int Hkv, int C, float scale, const TopkPlan& p, float* s_lo, float* kq,
-                       hipStream_t st) {
-#define DK_LO(NQ_, T_, MX_) \
+hipError_t dispatch_score_select(int nq, int T, bool maxred, const float* q, int B, int Hq,
+                                 const dk_landmark_shadow* sh, const float* lm, dk_strides ls, int Hkv, int C,
+                                 int k, float scale, int32_t* topk_idx, float* topk_score, const UnionOut& un,
+                                 hipStream_t st) {
+#define DK_SS(NQ_, T_, MX_) \
     if (nq == NQ_ && T == T_ && maxred == MX_) \
-        return launch_lo<D, NQ_, T_, MX_>(q, B, Hq, lm8, cscale, Hkv, C, scale, p, s_lo, kq, st);
-    DK_LO(1, 1, false)
-    DK_LO(2, 2, false)
-    DK_LO(1, 1, true)
-    DK_LO(2, 1, true)
-    DK_LO(4, 1, true)
-    DK_LO(8, 1, true)
-    DK_LO(16, 1, true)
-    DK_LO(2, 2, true)
-    DK_LO(4, 2, true)
-    DK_LO(8, 2, true)
-    DK_LO(16, 2, true)
-#undef DK_LO
+        return launch_score_select<D, NQ_, T_, MX_>(q, B, Hq, sh, lm, ls, Hkv, C, k, scale, topk_idx, topk_score, \
+                                                    un, st);
+    DK_SS(1, 1, false)
+    DK_SS(2, 2, false)
+    DK_SS(1, 1, true)
+    DK_SS(2, 1, true)
+    DK_SS(4, 1, true)
+    DK_SS(8, 1, true)
+    DK_SS(16, 1, true)
+    DK_SS(2, 2, true)
+    DK_SS(4, 2, true)
+    DK_SS(8, 2, true)
+    DK_SS(16, 2, true)
+#undef DK_SS
     return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-// About 1024 shadow-pass blocks: at B = 64, Hkv = 8 two ranges of 2048 rows per
-// (b, g).  Measured against 2048 and 4096 blocks on the 128K-token step: about
-// 1.2 us less per call than 2048 (longer blocks, fewer starts), 4096 the slowest.
-#ifndef DK_SCORE_LO_BLOCKS
-#define DK_SCORE_LO_BLOCKS 1024
-#endif
-#ifndef DK_SCORE_LO_MIN_ROWS
-#define DK_SCORE_LO_MIN_ROWS 256
-#endif
-
 TopkPlan plan_topk(int B, int Hkv, int T, int C, int k, bool shadow) {
     TopkPlan p{0, 0, 0};
     const int64_t bg = (int64_t)B * Hkv;
     if (shadow) {
-        // pass 1: ranges of rows for about DK_SCORE_LO_BLOCKS blocks, at least
-        // DK_SCORE_LO_MIN_ROWS rows each, at most kMaxRows (LDS staging); pass 2
-        // keeps every score of a (b, g) in LDS.
+        // one block per (b, g) scores and selects; everything stays in LDS
         if (C > kShadowMaxC) return p;
-        int64_t s = (DK_SCORE_LO_BLOCKS + bg - 1) / bg;
-        int64_t by_rows = C / DK_SCORE_LO_MIN_ROWS;
-        if (by_rows < 1) by_rows = 1;
-        if (s > by_rows) s = by_rows;
-        const int64_t min_s = (C + kMaxRows - 1) / kMaxRows;
-        if (s < min_s) s = min_s;
-        p.splits = (int)s;
-        p.rows = (int)((C + s - 1) / s);
-        while (p.splits > 1 && (int64_t)(p.splits - 1) * p.rows >= C) {
-            p.splits -= 1;
-            p.rows = (C + p.splits - 1) / p.splits;
-        }
-        // shadow-pass scores, the bound factor per (b, g, t)
-        p.ws_bytes = (((size_t)bg * T * C * 4 + 15) & ~(size_t)15) + (size_t)bg * T * 4;
+        p.splits = 1;
+        p.rows = C;
         return p;
     }
     int64_t want = (2048 + bg - 1) / bg;
@@ -1068,32 +1029,17 @@ hipError_t launch_score_topk(const float* q, int B, int T, int Hq, const float* 
     const int nq = maxred ? G * T : T;
     const int64_t bg = (int64_t)B * Hkv;
     if (shadow) {
-        float* s_lo = (float*)ws;
-        // the selection kernel merges the union itself when the merge's scan
-        // prefix (k + 1 ints) fits where its first group's candidates were
+        // the kernel merges the union itself when the merge's scan prefix
+        // (k + 1 ints) fits where its first group's candidates were
         const int Cp = (C + 3) & ~3;
         const bool fuse = un && (int64_t)k + 1 <= (int64_t)(Cp > kThreads ? Cp : kThreads);
-        // workspace: scores [bg, T, C] | the bound factor per (b, g, t)
-        const size_t sbytes = ((size_t)bg * T * C * 4 + 15) & ~(size_t)15;
-        float* kq = (float*)((char*)ws + sbytes);
-        hipError_t e = d == 128
-            ? dispatch_lo<128>(nq, T, maxred, q, B, Hq, shadow->lm8, shadow->chunk_scale, Hkv, C, scale, p, s_lo,
-                               kq, st)
-            : dispatch_lo<64>(nq, T, maxred, q, B, Hq, shadow->lm8, shadow->chunk_scale, Hkv, C, scale, p, s_lo,
-                              kq, st);
-        if (e != hipSuccess) return e;
-        // one block per (b, g), one group of kThreads threads per query token
-        const unsigned grid = (unsigned)bg;
-        const size_t lds = (size_t)T * select_group_words(C, d, maxred ? G : 1) * 4;
         const UnionOut none{nullptr, nullptr, nullptr, nullptr};
         const UnionOut uo = fuse ? *un : none;
-#define DK_SEL(D_, MX_)                                                                            \
-    hipLaunchKernelGGL((k_select_exact<D_, MX_>), dim3(grid), dim3(kThreads * T), lds, st, q, T, Hq, lm, ls, \
-                       shadow->chunk_scale, shadow->scale_max, s_lo, Hkv, C, k, scale, topk_idx, topk_score, uo, kq)
-        if (d == 128) { if (maxred) DK_SEL(128, true); else DK_SEL(128, false); }
-        else { if (maxred) DK_SEL(64, true); else DK_SEL(64, false); }
-#undef DK_SEL
-        e = hipGetLastError();
+        hipError_t e = d == 128
+            ? dispatch_score_select<128>(nq, T, maxred, q, B, Hq, shadow, lm, ls, Hkv, C, k, scale, topk_idx,
+                                         topk_score, uo, st)
+            : dispatch_score_select<64>(nq, T, maxred, q, B, Hq, shadow, lm, ls, Hkv, C, k, scale, topk_idx,
+                                        topk_score, uo, st);
         if (e != hipSuccess || !un || fuse) return e;
         return launch_union(topk_idx, B, Hkv, T, k, C, un->ids, un->member, un->count, un->overlap,
                             nullptr, st);

@@ -78,7 +78,7 @@ SH_MIS = b.dk_landmark_shadow(0x1008, 0x1000, 0x1000)
     (dict(lmdt=1, ls=b.dk_strides(1 << 22, 1 << 19, 129)), 2),
     (dict(ws=NULL), 1), (dict(wsb=16), 1), (dict(lm=MIS), 2),
     (dict(shadow=ctypes.byref(SH_NULL)), 1), (dict(shadow=ctypes.byref(SH_MIS)), 2),
-    (dict(shadow=ctypes.byref(SH_OK), C=8192), 2), (dict(shadow=ctypes.byref(SH_OK), wsb=1024), 1),
+    (dict(shadow=ctypes.byref(SH_OK), C=8192), 2), (dict(shadow=ctypes.byref(SH_OK), C=6145), 2),
 ])
 def test_score_topk_rejects(kw, status):
     assert score(**kw) == status, err()
@@ -110,9 +110,8 @@ def test_score_topk_union_rejects(kw, status):
 def test_score_topk_workspace_sizes():
     # 64 x 8 (b, g) rows over 4096 chunks: 4 ranges of 1024, 64 candidates each
     assert lib.dk_score_topk_workspace_size(64, 8, 2, 4096, 64, 0) == 64 * 8 * 2 * 4 * 64 * 8
-    # with a shadow: the shadow score of every chunk of every (b, g, t) in fp32,
-    # then one bound factor per (b, g, t)
-    assert lib.dk_score_topk_workspace_size(64, 8, 2, 4096, 64, 1) == 64 * 8 * 2 * 4096 * 4 + 64 * 8 * 2 * 4
+    # with a shadow one block per (b, g) scores and selects in LDS: no workspace
+    assert lib.dk_score_topk_workspace_size(64, 8, 2, 4096, 64, 1) == 0
     assert lib.dk_score_topk_workspace_size(1, 1, 2, 128, 8, 0) > 0
     assert lib.dk_score_topk_workspace_size(1, 1, 2, 128, 0, 0) == 0
 
