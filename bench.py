@@ -710,7 +710,8 @@ def bench_variant(args, w):
     q_bytes = B * T * Hq * d * 4
     rows_bytes = 2 * B * Hkv * T * C * 4            # fp32 score rows written, then read
     if sel == "capped":
-        score_bytes = (w.landmark_bytes() // 4 + B * Hkv * C * 4 + rows_bytes + B * Hkv * T * k * d * 4 + q_bytes
+        # the shadow selection keeps its score rows in LDS
+        score_bytes = (w.landmark_bytes() // 4 + B * Hkv * C * 4 + B * Hkv * T * k * d * 4 + q_bytes
                        + B * Hkv * T * k * 4 * 4)
     else:
         score_bytes = summary_bytes + rows_bytes + q_bytes + B * Hkv * N * 5
@@ -1145,9 +1146,9 @@ def run(args):
     if shadow is None:
         score_bytes = lm_bytes_layer + q_bytes
     else:
-        # 8-bit codes and one fp32 scale per chunk + the fp32 scores written and read
-        # back + at least k fp32 landmark rows re-scored per (b, g, t)
-        score_bytes = (lm_bytes_layer // 4 + w.B * w.Hkv * w.C * 4 + 2 * w.B * w.Hkv * w.T * w.C * 4
+        # 8-bit codes and one fp32 scale per chunk + at least k fp32 landmark rows
+        # re-scored per (b, g, t) (the shadow scores stay in LDS)
+        score_bytes = (lm_bytes_layer // 4 + w.B * w.Hkv * w.C * 4
                        + w.B * w.Hkv * w.T * w.k * w.d * 4 + q_bytes)
     per_call_bytes = {
         # scores and selection, then the union: both sets read back, ids + bits written

@@ -15,6 +15,16 @@
 
 namespace dk {
 
+// |{a[i] < x}| for an ascending a of n <= 64 entries: fixed steps, no branches
+// on the data, so two searches of one lane interleave their LDS reads.
+__device__ __forceinline__ int lower_bound_64(const int32_t* a, int n, int32_t x) {
+    int lo = 0;
+#pragma unroll
+    for (int s = 64; s >= 1; s >>= 1)
+        if (lo + s <= n && a[lo + s - 1] < x) lo += s;
+    return lo;
+}
+
 __device__ __forceinline__ int lower_bound_i32(const int32_t* a, int n, int32_t x) {
     int lo = 0, hi = n;
     while (lo < hi) {
@@ -45,6 +55,40 @@ __device__ __forceinline__ int block_union_two(const int32_t* s0, const int32_t*
         }
         count = k;
         *nshared = k;
+    } else if (k <= kWave) {
+        // One wave: lane l searches S0[l] in S1 and S1[l] in S0; the shared
+        // chunks below a position come from one ballot, not a block scan.
+        if (tid < kWave) {
+            const bool h = tid < k;
+            const int32_t x = h ? s0[tid] : 0, y = h ? s1[tid] : 0;
+            const int j = h ? lower_bound_64(s1, k, x) : k;
+            const int i = h ? lower_bound_64(s0, k, y) : k;
+            const bool both = h && j < k && s1[j] == x;
+            const bool iny = h && i < k && s0[i] == y;
+            const uint64_t dm = __builtin_amdgcn_ballot_w64(both);
+            const auto below = [](int n) { return n <= 0 ? 0ull : (n >= 64 ? ~0ull : (~0ull >> (64 - n))); };
+            if (h) {
+                const int pos = tid + j - __builtin_popcountll(dm & below(tid));
+                if (pos >= 0 && pos < N) {
+                    uo[pos] = x;
+                    mo[pos] = both ? 3 : 1;
+                    if (u_ids) u_ids[pos] = x;
+                }
+            }
+            if (h && !iny) {
+                const int pos = i + tid - __builtin_popcountll(dm & below(i));
+                if (pos >= 0 && pos < N) {
+                    uo[pos] = y;
+                    mo[pos] = 2;
+                    if (u_ids) u_ids[pos] = y;
+                }
+            }
+            if (tid == 0) scratch[0] = __builtin_popcountll(dm);
+        }
+        __syncthreads();
+        const int total = scratch[0];
+        *nshared = total;
+        count = 2 * k - total;
     } else {
         // flags of S0 entries that S1 also holds, scanned in S0 order
         const int per = (k + nthr - 1) / nthr;

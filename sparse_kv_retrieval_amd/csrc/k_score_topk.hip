@@ -541,6 +541,7 @@ __global__ __launch_bounds__(T * kThreads) void k_score_select(
     xcd_unit(blockIdx.x, 1, gridDim.x, bg, unused);
     const int b = bg / Hkv, g = bg - b * Hkv;
     const int Gq = Hq / Hkv;
+    const float SM = scale_max[bg];   // for pass 2, loaded early
 
     // ================= pass 1: shadow scores of every chunk =================
     {
@@ -551,8 +552,6 @@ __global__ __launch_bounds__(T * kThreads) void k_score_select(
         const int lane = threadIdx.x & (kWave - 1), bw = threadIdx.x / kWave;
         const int rp = lane / LPR, part = lane % LPR;
 
-        // The first rows are requested before anything else: their loads
-        // overlap the query staging below.
         const uint8_t* base = lm8 + (int64_t)bg * C * D + part * 16;
         const float* sbase = chunk_scale + (int64_t)bg * C;
         u32x4_t xa[U], xb[U];
@@ -566,68 +565,51 @@ __global__ __launch_bounds__(T * kThreads) void k_score_select(
                 rr[u] = part < T && r < C ? sbase[r] : 0.f;
             }
         };
+        // the first two batches of rows are requested before anything else
         load_rows(0, xa, ra);
+        if (ROWS_PER_ITER < C) load_rows(ROWS_PER_ITER, xb, rb);
+        // The query elements this thread stages: their loads go out right
+        // after the first two batches of rows, so both arrive within about one
+        // memory latency (a wait for the queries is also a wait for the rows
+        // issued before them).
+        constexpr int QI = (NQ * D + NW * kWave - 1) / (NW * kWave);   // query elements per thread
+        float xqv[QI];
+#pragma unroll
+        for (int j = 0; j < QI; ++j) {
+            const int i = threadIdx.x + j * NW * kWave;
+            const int v = i / D, e = i - v * D;
+            float xq = 0.f;
+            if (i < NQ * D) {
+                if constexpr (MAXRED) {
+                    xq = q[(((int64_t)b * T + v / G) * Hq + g * Gq + v % G) * D + e];
+                } else {
+                    // heads four at a time, their loads issued together
+                    const float* qh0 = q + (((int64_t)b * T + v) * Hq + g * Gq) * D + e;
+                    for (int h0 = 0; h0 < Gq; h0 += 4) {
+                        float x4[4];
+#pragma unroll
+                        for (int hh = 0; hh < 4; ++hh) x4[hh] = h0 + hh < Gq ? qh0[(int64_t)(h0 + hh) * D] : 0.f;
+#pragma unroll
+                        for (int hh = 0; hh < 4; ++hh) xq += x4[hh];
+                    }
+                    xq = xq / (float)Gq;
+                }
+            }
+            xqv[j] = xq;
+        }
+        // the chunk scales also go to LDS for pass 2: over group 1's keys (group
+        // 0's cand with T = 1), which pass 2 writes only after reading them
+        float* scl = (float*)smem2 + (T == 2 ? gw : (size_t)C);
 
         // The query vectors go through LDS once per block, into the groups'
         // qv[] (vector v is vector v % NVEC of group v / NVEC), which pass 2
         // re-scores with.
-        for (int i = threadIdx.x; i < NQ * D; i += NW * kWave) {
-            const int v = i / D, e = i - v * D;
-            float xq;
-            if constexpr (MAXRED) {
-                xq = q[(((int64_t)b * T + v / G) * Hq + g * Gq + v % G) * D + e];
-            } else {
-                xq = 0.f;
-                for (int h = 0; h < Gq; ++h) xq += q[(((int64_t)b * T + v) * Hq + g * Gq + h) * D + e];
-                xq = xq / (float)Gq;
-            }
-            qv_of(v / NVEC)[(v % NVEC) * D + e] = xq;
+#pragma unroll
+        for (int j = 0; j < QI; ++j) {
+            const int i = threadIdx.x + j * NW * kWave;
+            if (i < NQ * D) qv_of(i / D / NVEC)[(i / D % NVEC) * D + i % D] = xqv[j];
         }
         __syncthreads();
-        {
-            // The error bound's query factor for pass 2.  With m_i the codes,
-            // s_c the chunk scale, q^ = fp16(q) and u16 = 2^-11:
-            //   |sum q_i l_i - s_c sum q^_i m_i| <= s_c (1/2 + 127 u32) |q|_1            (the codes)
-            //                                     + s_c 127 (u16 |q|_1 + D 2^-25)   (q in fp16, subnormals too),
-            // the fp32 sums here and of the fp32 re-score add at most (D + 40)
-            // roundings of terms up to 127 s_c |q_i|; the lanes sum q^_i (code_i + 1152)
-            // and take off 1152 times their fp32 sum of q^: at most 48000 u32 s_c |q|_1
-            // more; the scale products add a few relative roundings: |s - s_lo| <= kq * s_c.  A query value beyond fp16
-            // voids the bound (kq = inf: every chunk becomes a candidate).
-            float* pq = qv_of(0) + NVEC * D;   // group 0's hist[]: free until pass 2
-            for (int v = bw; v < NQ; v += NW) {
-                const float* qp = qv_of(v / NVEC) + (v % NVEC) * D;
-                float a1 = 0.f, am = 0.f;
-                for (int e = lane; e < D; e += kWave) {
-                    a1 += fabsf(qp[e]);
-                    am = fmaxf(am, fabsf(qp[e]));
-                }
-                for (int off = 1; off < kWave; off <<= 1) {
-                    a1 += __shfl_xor(a1, off, kWave);
-                    am = fmaxf(am, __shfl_xor(am, off, kWave));
-                }
-                if (lane == 0) {
-                    pq[2 * v] = a1;
-                    pq[2 * v + 1] = am;
-                }
-            }
-            __syncthreads();
-            if (threadIdx.x < T) {
-                const int t = threadIdx.x;
-                float l1 = 0.f, amax = 0.f;
-                for (int v = (MAXRED ? t * G : t); v < (MAXRED ? (t + 1) * G : t + 1); ++v) {
-                    l1 = fmaxf(l1, pq[2 * v]);
-                    amax = fmaxf(amax, pq[2 * v + 1]);
-                }
-                l1 *= 1.0f + (float)(D + 8) * 5.9604645e-8f;   // round the sum up
-                const float u16 = 4.8828125e-4f, u32 = 5.9604645e-8f;
-                float k_ = fabsf(scale) *
-                           (l1 * (0.5f + 127.f * u32 + 127.f * u16 + ((float)(D + 40) * 127.f + 48000.f) * u32) +
-                            127.f * (float)D * 2.9802322e-8f) * 1.01f;
-                if (!(amax <= 65000.f) || !(k_ <= 3.0e38f)) k_ = INFINITY;
-                misc_of(t)[1] = __float_as_int(k_);
-            }
-        }
         uint32_t qh[NQ][8];
         float qbias[NQ];   // 1152 times this lane's share of the fp16 query sum
 #pragma unroll
@@ -676,16 +658,61 @@ __global__ __launch_bounds__(T * kThreads) void k_score_select(
                     }
                 }
                 if (part < T && rr < C) sres[part * C + rr] = (part == 0) ? sct[0] : sct[T - 1];
+                if (part == 0 && rr < C) scl[rr] = rs[u];
             }
         };
+        // two batches in flight: a batch's registers are refilled once it is scored
         for (int it = 0; it < C; it += 2 * ROWS_PER_ITER) {
-            if (it + ROWS_PER_ITER < C) load_rows(it + ROWS_PER_ITER, xb, rb);
             process(it, xa, ra);
-            if (it + ROWS_PER_ITER >= C) break;
             if (it + 2 * ROWS_PER_ITER < C) load_rows(it + 2 * ROWS_PER_ITER, xa, ra);
+            if (it + ROWS_PER_ITER >= C) break;
             process(it + ROWS_PER_ITER, xb, rb);
+            if (it + 3 * ROWS_PER_ITER < C) load_rows(it + 3 * ROWS_PER_ITER, xb, rb);
         }
-        __syncthreads();
+        {
+            // The error bound's query factor for pass 2.  With m_i the codes,
+            // s_c the chunk scale, q^ = fp16(q) and u16 = 2^-11:
+            //   |sum q_i l_i - s_c sum q^_i m_i| <= s_c (1/2 + 127 u32) |q|_1            (the codes)
+            //                                     + s_c 127 (u16 |q|_1 + D 2^-25)   (q in fp16, subnormals too),
+            // the fp32 sums here and of the fp32 re-score add at most (D + 40)
+            // roundings of terms up to 127 s_c |q_i|; the lanes sum q^_i (code_i + 1152)
+            // and take off 1152 times their fp32 sum of q^: at most 48000 u32 s_c |q|_1
+            // more; the scale products add a few relative roundings: |s - s_lo| <= kq * s_c.  A query value beyond fp16
+            // voids the bound (kq = inf: every chunk becomes a candidate).
+            float* pq = qv_of(0) + NVEC * D;   // group 0's hist[]: free until pass 2
+            for (int v = bw; v < NQ; v += NW) {
+                const float* qp = qv_of(v / NVEC) + (v % NVEC) * D;
+                float a1 = 0.f, am = 0.f;
+                for (int e = lane; e < D; e += kWave) {
+                    a1 += fabsf(qp[e]);
+                    am = fmaxf(am, fabsf(qp[e]));
+                }
+                for (int off = 1; off < kWave; off <<= 1) {
+                    a1 += __shfl_xor(a1, off, kWave);
+                    am = fmaxf(am, __shfl_xor(am, off, kWave));
+                }
+                if (lane == 0) {
+                    pq[2 * v] = a1;
+                    pq[2 * v + 1] = am;
+                }
+            }
+            __syncthreads();   // (the end of pass 1)
+            if (threadIdx.x < T) {
+                const int t = threadIdx.x;
+                float l1 = 0.f, amax = 0.f;
+                for (int v = (MAXRED ? t * G : t); v < (MAXRED ? (t + 1) * G : t + 1); ++v) {
+                    l1 = fmaxf(l1, pq[2 * v]);
+                    amax = fmaxf(amax, pq[2 * v + 1]);
+                }
+                l1 *= 1.0f + (float)(D + 8) * 5.9604645e-8f;   // round the sum up
+                const float u16 = 4.8828125e-4f, u32 = 5.9604645e-8f;
+                float k_ = fabsf(scale) *
+                           (l1 * (0.5f + 127.f * u32 + 127.f * u16 + ((float)(D + 40) * 127.f + 48000.f) * u32) +
+                            127.f * (float)D * 2.9802322e-8f) * 1.01f;
+                if (!(amax <= 65000.f) || !(k_ <= 3.0e38f)) k_ = INFINITY;
+                misc_of(t)[1] = __float_as_int(k_);
+            }
+        }
     }
 
     // ================= pass 2: exact top-k of group t's query ================
@@ -702,13 +729,13 @@ __global__ __launch_bounds__(T * kThreads) void k_score_select(
     int* misc = misc_of(t);                          // [0] candidates, [1] bound factor (bits)
     const int tid = threadIdx.x & (kThreads - 1), lane = tid & (kWave - 1), wave = tid / kWave;
 
-    // this thread's contiguous range of shadow scores (LDS) and chunk scales
-    // (global: pass 1 just read them), kept in registers
+    // this thread's contiguous range of shadow scores and chunk scales (both
+    // in LDS), kept in registers
     constexpr int KPT = kShadowMaxC / kThreads;      // scores per thread, at most
     const int per = (C + kThreads - 1) / kThreads;
     const int lo = min(C, tid * per), hi = min(C, lo + per);
     const float* sl = (const float*)smem2 + t * C;
-    const float* cs = chunk_scale + (int64_t)bg * C;
+    const float* cs = (const float*)smem2 + (T == 2 ? gw : (size_t)C);
     float sv[KPT], sc[KPT];
     if ((per & 3) == 0 && (C & 3) == 0) {
 #pragma unroll
@@ -730,9 +757,8 @@ __global__ __launch_bounds__(T * kThreads) void k_score_select(
             sc[i] = lo + i < hi ? cs[lo + i] : 0.f;
         }
     }
-    const float SM = scale_max[bg];
-    const float Kq = __int_as_float(misc[1]);
     __syncthreads();   // every score is in registers: the scores' LDS is reused from here on
+    const float Kq = __int_as_float(misc[1]);
 
     // the bound |s - s_lo| <= Kq * s_c (Kq from pass 1); a landmark the codes
     // cannot hold, or Kq = inf, voids it: every chunk is then a candidate
