@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define DK_ABI_VERSION 11
+#define DK_ABI_VERSION 12
 
 typedef enum {
     DK_OK = 0,

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version():
-    assert lib.dk_abi_version() == 11
+    assert lib.dk_abi_version() == 12
 
 
 def err():
