@@ -763,19 +763,19 @@ __global__ __launch_bounds__(T * kThreads) void k_score_select(
     // the bound |s - s_lo| <= Kq * s_c (Kq from pass 1); a landmark the codes
     // cannot hold, or Kq = inf, voids it: every chunk is then a candidate
     const bool valid = SM <= 3.0e38f && Kq <= 3.0e38f;
+    // the key order is the float order: the maximum of the lower bounds takes one key
     uint32_t kr[KPT];
-    uint32_t tmax = 0u;
+    float flo = -INFINITY;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
         const float d = Kq * sc[i];
         const float slo = sv[i] - d, shi = sv[i] + d;
         const float pad = (fabsf(sv[i]) + d) * 2.4e-7f + 1e-37f;   // round the bounds outwards
-        const bool in = lo + i < hi;
-        tmax = max(tmax, in ? score_key(slo - pad) : 0u);
-        kr[i] = in ? score_key(shi + pad) : 0u;
+        kr[i] = lo + i < hi ? score_key(shi + pad) : 0u;
+        if (lo + i < hi) flo = fmaxf(flo, slo - pad);
     }
     uint32_t* tmaxs = cand_u;                     // [256] scratch (cand[] is not used yet)
-    tmaxs[tid] = tmax;
+    tmaxs[tid] = hi > lo ? score_key(flo) : 0u;
     __syncthreads();
     if (wave == 0) {
         // a lower bound of the k-th largest of the per-thread maxima (its top 20
