@@ -523,13 +523,13 @@ __host__ __device__ inline size_t select_group_words(int C, int D, int nvec) {
     return (size_t)Cp + (size_t)(Cp > 256 ? Cp : 256) + (size_t)nvec * D + 256 + 16;
 }
 
-template <int D, int NQ, int T, bool MAXRED>
-__global__ __launch_bounds__(T * kThreads) void k_score_select(
+template <int D, int NQ, int T, bool MAXRED, int F>
+__global__ __launch_bounds__(T * kThreads * F) void k_score_select(
     const float* __restrict__ q, int Hq, const uint8_t* __restrict__ lm8, const float* __restrict__ chunk_scale,
     const float* __restrict__ scale_max, const float* __restrict__ lm, dk_strides ls, int Hkv, int C, int k,
     float scale, int32_t* __restrict__ topk_idx, float* __restrict__ topk_score, UnionOut un) {
     constexpr int NVEC = MAXRED ? NQ / T : 1;          // query vectors per group
-    constexpr int NW = T * kThreads / kWave;           // waves of the block
+    constexpr int NW = T * F * kThreads / kWave;       // waves of the block (pass 1 uses all)
     extern __shared__ uint32_t smem2[];
     const int Cp = (C + 3) & ~3;
     const int cand_words = Cp > kThreads ? Cp : kThreads;
@@ -714,6 +714,9 @@ __global__ __launch_bounds__(T * kThreads) void k_score_select(
             }
         }
     }
+    // Pass 2 runs T groups of kThreads threads; the waves beyond them (F = 2)
+    // end here, and the block barriers below wait only for the waves left.
+    if (threadIdx.x >= T * kThreads) return;
 
     // ================= pass 2: exact top-k of group t's query ================
     constexpr int LPR = D / 8;                 // lanes per fp32 row, 8 floats each
@@ -968,9 +971,19 @@ hipError_t launch_score_select(const float* q, int B, int Hq, const dk_landmark_
                                float* topk_score, const UnionOut& un, hipStream_t st) {
     constexpr int NVEC = MAXRED ? NQ / T : 1;
     const size_t lds = (size_t)T * select_group_words(C, D, NVEC) * 4;
-    hipLaunchKernelGGL((k_score_select<D, NQ, T, MAXRED>), dim3((unsigned)((int64_t)B * Hkv)), dim3(T * kThreads),
-                       lds, st, q, Hq, sh->lm8, sh->chunk_scale, sh->scale_max, lm, ls, Hkv, C, k, scale, topk_idx,
-                       topk_score, un);
+    const int64_t bg = (int64_t)B * Hkv;
+    // With at most one block per CU (256 CUs) the score pass streams with twice
+    // the waves (rows enough to stream: C >= 512; a short row is latency-bound
+    // and pays for the extra waves); with more blocks two resident blocks per
+    // CU give the same.
+    if (bg <= 256 && C >= 512)
+        hipLaunchKernelGGL((k_score_select<D, NQ, T, MAXRED, 2>), dim3((unsigned)bg), dim3(2 * T * kThreads), lds, st,
+                           q, Hq, sh->lm8, sh->chunk_scale, sh->scale_max, lm, ls, Hkv, C, k, scale, topk_idx,
+                           topk_score, un);
+    else
+        hipLaunchKernelGGL((k_score_select<D, NQ, T, MAXRED, 1>), dim3((unsigned)bg), dim3(T * kThreads), lds, st,
+                           q, Hq, sh->lm8, sh->chunk_scale, sh->scale_max, lm, ls, Hkv, C, k, scale, topk_idx,
+                           topk_score, un);
     return hipGetLastError();
 }
 
