@@ -135,6 +135,10 @@ def check_score_topk(dkb, qh, lm32, k, scale, reduce, G, shadow=False):
     ("llama8b_l32k", 2, 8192, 2, "max"),
     ("llama8b_l32k", 2, 8192, 1, "max"),
     ("llama8b_l32k", None, None, 2, "mean"),
+    # C = 1024 chunks at few (b, g): the shadow kernel's wider pass-1 block
+    ("llama8b_l32k", 2, 32768, 1, "mean"),
+    ("llama8b_l32k", 2, 32768, 2, "max"),
+    ("llama8b_l32k", 2, 32768, 1, "max"),
 ])
 def test_score_topk(dkb, name, B, L, T, reduce, shadow):
     w = workload(name, B, L, T=T)
