@@ -726,6 +726,10 @@ AttnPlan plan_attn(int B, int Hkv, int T, int Hq, int dv, int N, int chunk, bool
     int64_t by_work = tiles >= 120 ? tiles / 20 : tiles / 6;
     if (by_work < 1) by_work = 1;
     int64_t s = want < by_work ? want : by_work;
+    // and at most ~128 tiles of a full union per range: with ragged unions (a
+    // coverage budget's sets) the longest (b, g) then spreads over ranges
+    const int64_t cap_s = (tiles + 127) / 128;
+    if (s < cap_s) s = cap_s;
     const int64_t min_s = (N + kFastMaxEntries - 1) / kFastMaxEntries;
     if (s < min_s) s = min_s;
     if (s > 64 && min_s <= 64) s = 64;
