@@ -547,7 +547,6 @@ __global__ __launch_bounds__(T * kThreads * F) void k_score_select(
     {
         constexpr int LPR = D / 16, RPW = kWave / LPR, U = DK_SCORE_LO_UNROLL;
         constexpr int G = MAXRED ? NQ / T : 0;
-        constexpr int ROWS_PER_ITER = NW * RPW * U;
         float* sres = (float*)smem2;                   // [T][C]
         const int lane = threadIdx.x & (kWave - 1), bw = threadIdx.x / kWave;
         const int rp = lane / LPR, part = lane % LPR;
@@ -556,18 +555,32 @@ __global__ __launch_bounds__(T * kThreads * F) void k_score_select(
         const float* sbase = chunk_scale + (int64_t)bg * C;
         u32x4_t xa[U], xb[U];
         float ra[U], rb[U];
-        auto load_rows = [&](int it, u32x4_t (&xx)[U], float (&rr)[U]) {
+        // Rows go in batches of BR consecutive rows, one wave per batch: each
+        // wave takes its first two batches statically and every later one from
+        // a counter in LDS, so waves that meet slower memory take fewer batches
+        // and the waves end pass 1 together.
+        constexpr int BR = RPW * U;
+        const int nbatch = (C + BR - 1) / BR;
+        int* batch_ctr = misc_of(0) + 2;
+        auto grab = [&]() {
+            int j = 0;
+            if (lane == 0) j = atomicAdd(batch_ctr, 1);
+            return __builtin_amdgcn_readfirstlane(j);
+        };
+        auto load_rows = [&](int jb, u32x4_t (&xx)[U], float (&rr)[U]) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int r = it + (u * NW + bw) * RPW + rp;
+                const int r = jb * BR + u * RPW + rp;
                 xx[u] = r < C ? nt_load_u4(base + (int64_t)r * D)
                               : u32x4_t{0x80808080u, 0x80808080u, 0x80808080u, 0x80808080u};
                 rr[u] = part < T && r < C ? sbase[r] : 0.f;
             }
         };
         // the first two batches of rows are requested before anything else
-        load_rows(0, xa, ra);
-        if (ROWS_PER_ITER < C) load_rows(ROWS_PER_ITER, xb, rb);
+        int ja = bw, jb = NW + bw;
+        if (ja < nbatch) load_rows(ja, xa, ra);
+        if (jb < nbatch) load_rows(jb, xb, rb);
+        if (threadIdx.x == 0) *batch_ctr = 2 * NW;   // read only after the staging barrier below
         // The query elements this thread stages: their loads go out right
         // after the first two batches of rows, so both arrive within about one
         // memory latency (a wait for the queries is also a wait for the rows
@@ -627,10 +640,10 @@ __global__ __launch_bounds__(T * kThreads * F) void k_score_select(
             qbias[v] = 1152.f * sq;
         }
 
-        auto process = [&](int it, const u32x4_t (&x)[U], const float (&rs)[U]) {
+        auto process = [&](int jbt, const u32x4_t (&x)[U], const float (&rs)[U]) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int rr = it + (u * NW + bw) * RPW + rp;
+                const int rr = jbt * BR + u * RPW + rp;
                 uint32_t h[8];
                 h[0] = code_pair(x[u].x, 0x04010400u); h[1] = code_pair(x[u].x, 0x04030402u);
                 h[2] = code_pair(x[u].y, 0x04010400u); h[3] = code_pair(x[u].y, 0x04030402u);
@@ -661,13 +674,18 @@ __global__ __launch_bounds__(T * kThreads * F) void k_score_select(
                 if (part == 0 && rr < C) scl[rr] = rs[u];
             }
         };
-        // two batches in flight: a batch's registers are refilled once it is scored
-        for (int it = 0; it < C; it += 2 * ROWS_PER_ITER) {
-            process(it, xa, ra);
-            if (it + 2 * ROWS_PER_ITER < C) load_rows(it + 2 * ROWS_PER_ITER, xa, ra);
-            if (it + ROWS_PER_ITER >= C) break;
-            process(it + ROWS_PER_ITER, xb, rb);
-            if (it + 3 * ROWS_PER_ITER < C) load_rows(it + 3 * ROWS_PER_ITER, xb, rb);
+        // two batches in flight: a batch's registers are refilled once it is
+        // scored.  Batches come from the counter in increasing order, so once jb
+        // is past the end the batch taken into ja is too.
+        for (;;) {
+            if (ja >= nbatch) break;
+            process(ja, xa, ra);
+            ja = grab();
+            if (ja < nbatch) load_rows(ja, xa, ra);
+            if (jb >= nbatch) break;
+            process(jb, xb, rb);
+            jb = grab();
+            if (jb < nbatch) load_rows(jb, xb, rb);
         }
         {
             // The error bound's query factor for pass 2.  With m_i the codes,
