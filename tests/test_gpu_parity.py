@@ -262,7 +262,8 @@ def test_union(dkb, T, k, C, mode):
 @pytest.mark.parametrize("name,B,L,kw,shadow", [
     ("llama8b_l32k", 4, 8192, {}, True),            # fused into the selection kernel
     ("llama8b_l32k", 4, 8192, {}, False),           # fp32 path: separate union kernel
-    ("llama8b_l32k", 2, 16384, dict(k=400), True),  # 3k + 1 beyond the selection LDS: separate kernel
+    ("llama8b_l32k", 2, 16384, dict(k=400), True),  # k > 64: the block-wide merge inside the kernel
+    ("llama8b_l32k", 2, 16384, dict(k=512), True),  # k = C: the merge's prefix does not fit; separate kernel
     ("tiny", None, None, dict(T=1), True),          # one query: the union is S_0
     ("tiny", None, None, {}, True),
 ])
