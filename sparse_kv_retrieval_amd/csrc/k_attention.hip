@@ -14,21 +14,21 @@
 // the online-softmax rule.  Logits are kept in log2 units (scale * log2 e).
 //
 // Fast path (bf16 K/V, d = 128, G = 4, T = 2, chunk a multiple of 32): four
-// waves over 32-row tiles of K and V (16 KiB) that stream from HBM straight
-// into a three-stage LDS ring with global_load_lds_dwordx4 (non-temporal; no
-// register staging), so two tiles are in flight while one is computed, and each
-// tile is read from HBM once for all eight query rows.  Both products run on
-// the matrix cores (v_mfma_f32_16x16x32_bf16) with the keys along M:
-// S^T = K Q^T gives every lane one query row's logits of eight keys; after the
-// online-softmax step those weights, rounded to bf16, are already the B operand
-// of O^T = V^T P^T, whose A operand comes from transposed LDS reads of V
-// (ds_read_b64_tr_b16).  Every wave computes S for all eight rows (the same
-// values in each wave, so the running max and sums agree) and owns 32 of the
-// 128 value dims.  K and V pieces are XOR-swizzled by row in LDS so that the
-// operand reads hit distinct banks.  The running max moves only when a logit
-// exceeds it by a slack, so most tiles need no rescale; the row sums use the
-// rounded weights, so each output stays an exact convex combination of its
-// values.
+// independent waves per block, each over its own 16-row tiles of K and V
+// (every fourth tile of the block's range) that stream from HBM straight into a
+// private two-stage LDS ring with global_load_lds_dwordx4 (non-temporal; no
+// register staging), so no block barrier sits in the tile loop and each tile is
+// read from HBM once for all eight query rows.  Both products run on the matrix
+// cores with the keys along M: S^T = K Q^T (v_mfma_f32_16x16x32_bf16) gives
+// every lane one query row's logits of four keys; after the online-softmax step
+// those weights, rounded to bf16, are already the B operand of O^T = V^T P^T
+// (v_mfma_f32_16x16x16_bf16), whose A operand comes from transposed LDS reads of
+// V (ds_read_b64_tr_b16).  Each wave keeps its own running max, sums and all 128
+// value dims; the four partial results are merged through LDS at the end.  K
+// and V pieces are XOR-swizzled by row in LDS so that the operand reads hit
+// distinct banks.  The running max moves only when a logit exceeds it by a
+// slack, so most tiles need no rescale; the row sums use the rounded weights,
+// so each output stays an exact convex combination of its values.
 #include "dk_common.h"
 
 namespace dk {
@@ -98,20 +98,37 @@ __device__ __forceinline__ void emit_row(const AttnArgs& a, int b, int bg, int s
 
 // ---------------------------------------------------------------------------
 // Fast path: bf16, D = 128, G = 4, T = 2, chunk % 32 == 0.
+//
+// Each of the block's four waves streams its own 16-key tiles (tiles w, w + 4,
+// ... of the block's range) through a private two-stage LDS ring filled by
+// direct global-to-LDS loads, so no block barrier sits inside the tile loop and
+// a wave waits only for its own loads.  Per tile a wave computes S^T = K Q^T for
+// all eight query rows (four 16x16x32 products) and O^T += V^T P^T over all 128
+// value dims (eight 16x16x16 products), keeping its own running maximum, row sum
+// and output; the four partial results are merged through LDS at the end.
 // ---------------------------------------------------------------------------
-constexpr int kFastStages = 3;     // LDS ring: one tile computed, two in flight
+constexpr int kFastWaves = 4;
+constexpr int kFastThreads = kFastWaves * 64;
+constexpr int kFastStages = 2;     // per-wave LDS ring: one tile computed, one in flight
 constexpr int kFastMaxEntries = 256;
 constexpr float kFastSlack = 8.f;  // log2 headroom of the lazy running maximum
 
 struct __align__(16) FastSmem {
-    uint4 kv[kFastStages][2][32 * 16];     // [stage][K|V][row * 16 + 16-byte piece]
-    int32_t erow[kFastMaxEntries];         // first pool row of each entry's chunk
-    uint32_t ebits[kFastMaxEntries];       // membership bits (0: skip the entry)
+    uint4 kv[kFastWaves][kFastStages][2][16 * 16];  // [wave][stage][K|V][row * 16 + 16-byte piece]
+    int32_t erow[kFastMaxEntries];                  // first pool row of each entry's chunk
+    uint32_t ebits[kFastMaxEntries];                // membership bits (0: skip the entry)
 };
 
-__global__ __launch_bounds__(kThreads) void k_attn_bf16_d128_g4t2(AttnArgs a) {
-    constexpr int D = 128, G = 4, T = 2, R = G * T, KT = 32, NS = kFastStages;
-    constexpr int kRowBytes = D * 2, kHalfTile = 16 * kRowBytes;   // 16 keys of K or V
+typedef __bf16 bf16x4k_t __attribute__((ext_vector_type(4)));
+// D (16x16 fp32) += A (16x16) B (16x16), bf16 operands of four elements per lane
+__device__ __forceinline__ f32x4_t mfma16k16(uint2 a, uint2 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4k_t, a), __builtin_bit_cast(bf16x4k_t, b),
+                                                     c, 0, 0, 0);
+}
+
+__global__ __launch_bounds__(kFastThreads) void k_attn_bf16_d128_g4t2(AttnArgs a) {
+    constexpr int D = 128, G = 4, T = 2, R = G * T, KT = 16, NS = kFastStages;
+    constexpr int kRowBytes = D * 2;
     __shared__ FastSmem sm;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -138,11 +155,11 @@ __global__ __launch_bounds__(kThreads) void k_attn_bf16_d128_g4t2(AttnArgs a) {
             qf[ks][1] = qrow ? *reinterpret_cast<const float4*>(qp + 32 * ks + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
         }
     }
-    // This block's entries go to LDS, so the tile loop issues no vector loads of
-    // its own besides the DMA (keeps the explicit vmcnt accounting exact).
     const int32_t* ids = a.block_ids + (int64_t)bg * a.N;
     const uint8_t* mem = a.member + (int64_t)bg * a.N;
-    for (int e = tid; e < u1 - u0; e += kThreads) {
+    // This block's entries go to LDS, so the tile loop issues no vector loads of
+    // its own besides the DMA (keeps the explicit vmcnt accounting exact).
+    for (int e = tid; e < u1 - u0; e += kFastThreads) {
         const int c = ids[u0 + e];
         uint32_t m = mem[u0 + e];
         if (c < 0 || c >= a.pool_blocks) m = 0;
@@ -157,106 +174,90 @@ __global__ __launch_bounds__(kThreads) void k_attn_bf16_d128_g4t2(AttnArgs a) {
         qb[ks] = make_uint4(pack_bf16x2(qf[ks][0].x, qf[ks][0].y), pack_bf16x2(qf[ks][0].z, qf[ks][0].w),
                             pack_bf16x2(qf[ks][1].x, qf[ks][1].y), pack_bf16x2(qf[ks][1].z, qf[ks][1].w));
 
-    // DMA geometry: wave w fills rows 8w..8w+7 of the K and of the V tile, two
-    // 1 KiB wave-loads each.  Row r's 16-byte pieces are XOR-swizzled, K by
-    // r & 15 and V by 2 (r & 7), so that the matrix-core operand reads below
-    // (16 key rows at one K piece; 8 key rows at two adjacent V pieces) hit
-    // distinct LDS banks.
+    // DMA geometry: a wave fills its 16-row K and V tiles with four 1 KiB
+    // wave-loads each.  Row r's 16-byte pieces are XOR-swizzled, K by r & 15 and
+    // V by 2 (r & 7), so that the matrix-core operand reads below (16 key rows at
+    // one K piece; 4 key rows at two adjacent V pieces) hit distinct LDS banks.
     const uint16_t* Kb = (const uint16_t*)a.K + (int64_t)b * a.ks.b + (int64_t)g * a.ks.h;
     const uint16_t* Vb = (const uint16_t*)a.V + (int64_t)b * a.vs.b + (int64_t)g * a.vs.h;
-    int koff[2], voff[2];
+    int koff[4], voff[4];
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-        const int p = (2 * w + jj) * 64 + lane;
+    for (int jj = 0; jj < 4; ++jj) {
+        const int p = jj * 64 + lane;
         const int row = p >> 4, phys = p & 15;
         koff[jj] = row * (int)a.ks.t + (phys ^ (row & 15)) * 8;
         voff[jj] = row * (int)a.vs.t + (phys ^ (2 * (row & 7))) * 8;
     }
     // the wave index as a scalar: the DMA's LDS bases (M0) are then plain SALU math
     const int wu = __builtin_amdgcn_readfirstlane(w);
-    auto tile_row = [&](int it) {
+    auto issue = [&](int it, int slot) {
         const int e = it / tpc;
-        return sm.erow[e] + (it - e * tpc) * KT;
-    };
-    auto issue = [&](int it, int row0) {
-        const int s = it % NS;
+        const int row0 = sm.erow[e] + (it - e * tpc) * KT;
         const uint16_t* kp = Kb + (int64_t)row0 * a.ks.t;
         const uint16_t* vp = Vb + (int64_t)row0 * a.vs.t;
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) lds_dma16(kp + koff[jj], lds_addr(&sm.kv[s][0][(2 * wu + jj) * 64]));
+        for (int jj = 0; jj < 4; ++jj) lds_dma16(kp + koff[jj], lds_addr(&sm.kv[wu][slot][0][jj * 64]));
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) lds_dma16(vp + voff[jj], lds_addr(&sm.kv[s][1][(2 * wu + jj) * 64]));
+        for (int jj = 0; jj < 4; ++jj) lds_dma16(vp + voff[jj], lds_addr(&sm.kv[wu][slot][1][jj * 64]));
     };
-
-    // Operand reads within a tile (bytes).  K (A of S^T): key 16 mt + lr, logical
-    // piece lg + 4 ks.  V (A of O^T = V^T P^T, transposed reads): value dims
-    // 32 w + 16 j + lr, keys 4 lg .. + 3 and 16 + 4 lg .. + 3, so that the k-th
-    // element of the operand is the key whose weight S^T leaves in element k
-    // of the same lane.
-    int kro[4], vro[2];
+    // Operand reads within a tile (bytes).  K (A of S^T): key lr, logical piece
+    // lg + 4 ks.  V (A of O^T = V^T P^T, transposed reads): value dims 16 j + lr,
+    // keys 4 lg .. + 3, so that the k-th element of the operand is the key whose
+    // weight S^T leaves in element k of the same lane.
+    int kro[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) kro[ks] = lr * kRowBytes + ((lg + 4 * ks) ^ lr) * 16;
+    int vro[8];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < 8; ++j) {
         const int key = 4 * lg + (lr >> 2);
-        const int lp = 4 * w + 2 * j + ((lr & 3) >> 1);
+        const int lp = 2 * j + ((lr & 3) >> 1);
         vro[j] = key * kRowBytes + (lp ^ (2 * (key & 7))) * 16 + 8 * (lr & 1);
     }
 
     // Running max in log2 units, moved only when a logit exceeds it by more than
     // the slack (weights stay below 2^slack).  It starts at a finite floor far
     // below every logit, so exp2 of (masked logit = -inf) - max is 0 without a
-    // guard, and a range with no valid key ends with l = 0 (reported as out 0,
-    // lse -inf).  Every wave computes the same S, so m and l agree across waves.
+    // guard, and a wave (or range) with no valid key ends with l = 0 (a range
+    // reports out 0, lse -inf).
     float m_run = kNoLogit, l_part = 0.f;     // l_part: this lane's share of row lr's sum
-    f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-
+    f32x4_t acc[8];                           // O^T: value dims 16 j + 4 lg + i of row lr
 #pragma unroll
-    for (int s = 0; s < NS - 1; ++s)
-        if (s < ntiles) issue(s, tile_row(s));
-    // per-tile metadata is read one iteration ahead, off the critical path
-    int row_next = NS - 1 < ntiles ? tile_row(NS - 1) : 0;
-    uint32_t bits_next = ntiles > 0 ? sm.ebits[0] : 0u;
+    for (int j = 0; j < 8; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    for (int it = 0; it < ntiles; ++it) {
-        // tile `it` has landed when at most the 4 loads of tile it + 1 are pending
-        if (it + 1 < ntiles) lds_dma_wait<4>();
+    static_assert(NS == 2, "the waits below count one tile (8 loads) in flight");
+    if (w < ntiles) issue(w, 0);
+    for (int it = w, slot = 0; it < ntiles; it += kFastWaves, slot ^= 1) {
+        // the other slot was computed in the previous iteration: its reads have
+        // returned, so the next tile may overwrite it
+        const bool more = it + kFastWaves < ntiles;
+        if (more) issue(it + kFastWaves, slot ^ 1);
+        // tile `it` has landed when at most the 8 loads of the next one are pending
+        if (more) lds_dma_wait<8>();
         else lds_dma_wait<0>();
-        raw_barrier();
-        // the stage computed in the previous iteration is free for tile it + 2
-        if (it + NS - 1 < ntiles) issue(it + NS - 1, row_next);
-        const uint32_t m_cur = bits_next;
-        row_next = it + NS < ntiles ? tile_row(it + NS) : 0;
-        bits_next = it + 1 < ntiles ? sm.ebits[(it + 1) / tpc] : 0u;
+        const uint32_t m_cur = sm.ebits[it / tpc];
         if (m_cur == 0) continue;
-        const char* kb = reinterpret_cast<const char*>(sm.kv[it % NS][0]);
-        const char* vb = reinterpret_cast<const char*>(sm.kv[it % NS][1]);
+        const char* kb = reinterpret_cast<const char*>(sm.kv[wu][slot][0]);
+        const char* vb = reinterpret_cast<const char*>(sm.kv[wu][slot][1]);
+        uint4 kr[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) kr[ks] = *reinterpret_cast<const uint4*>(kb + kro[ks]);
+        uint2 vr[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) vr[j] = lds_read_tr(vb + vro[j]);
 
-        uint4 kr[2][4];
+        // ---- S^T for all eight query rows: element i of s is key 4 lg + i ----
+        f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) kr[mt][ks] = *reinterpret_cast<const uint4*>(kb + kro[ks] + mt * kHalfTile);
-        uint2 vr[2][2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh) vr[j][kh] = lds_read_tr(vb + vro[j] + kh * kHalfTile);
-
-        // ---- S^T for all eight query rows: element i of s[mt] is key 16 mt + 4 lg + i ----
-        f32x4_t s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) s[mt] = mfma16(kr[mt][ks], qb[ks], s[mt]);
+        for (int ks = 0; ks < 4; ++ks) s = mfma16(kr[ks], qb[ks], s);
 
         // ---- online softmax of row lr ----
         const bool on = qrow && ((m_cur >> (lr >> 2)) & 1u);
-        float z[8];
+        float z[4];
         float hm = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            z[i] = on ? s[i >> 2][i & 3] * a.scale_log2 : -INFINITY;
+        for (int i = 0; i < 4; ++i) {
+            z[i] = on ? s[i] * a.scale_log2 : -INFINITY;
             hm = fmaxf(hm, z[i]);
         }
         hm = group4_max(hm);
@@ -269,10 +270,10 @@ __global__ __launch_bounds__(kThreads) void k_attn_bf16_d128_g4t2(AttnArgs a) {
         // weights rounded to bf16 (to nearest even); the row sum adds the rounded
         // values the value product uses, so each output stays an exact convex
         // combination of its values
-        uint32_t pk[4];
+        uint32_t pk[2];
         float ls = 0.f;
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
+        for (int h = 0; h < 2; ++h) {
             const bf16x2_t v = {(__bf16)__builtin_amdgcn_exp2f(z[2 * h] - m_run),
                                 (__bf16)__builtin_amdgcn_exp2f(z[2 * h + 1] - m_run)};
             pk[h] = __builtin_bit_cast(uint32_t, v);
@@ -280,52 +281,66 @@ __global__ __launch_bounds__(kThreads) void k_attn_bf16_d128_g4t2(AttnArgs a) {
         }
         l_part = l_part * alpha + ls;
         if (__builtin_amdgcn_ballot_w64(over) != 0ull) {
-            acc[0] *= alpha;
-            acc[1] *= alpha;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[j] *= alpha;
         }
 
-        // ---- O^T += V^T P^T for this wave's 32 value dims ----
-        const uint4 pb = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        // ---- O^T += V^T P^T over all 128 value dims ----
+        const uint2 pb = make_uint2(pk[0], pk[1]);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            acc[j] = mfma16(make_uint4(vr[j][0].x, vr[j][0].y, vr[j][1].x, vr[j][1].y), pb, acc[j]);
+        for (int j = 0; j < 8; ++j) acc[j] = mfma16k16(vr[j], pb, acc[j]);
     }
     lds_dma_wait<0>();
 
-    // ---- row results: every wave holds m and l of all rows, and 32 dims ----
-    // The eight rows go through LDS (the first ring stage, free once every wave
-    // is past its last tile) so that the block writes them as whole lines: one
+    // ---- merge the four waves' (m, l, O) through LDS (the rings, free once
+    // every wave is past its last tile); the rows then leave as whole lines, one
     // 16-byte store per thread.  Scattered 4-byte stores of partial lines cost
     // several microseconds per launch at full size.
     const float l_row = group4_sum(l_part);
-    const bool single = a.nparts == 1;
-    const float inv = single ? (l_row > 0.f ? 1.f / l_row : 0.f) : 1.f;
     __syncthreads();
-    float* ostage = reinterpret_cast<float*>(&sm.kv[0][0][0]);   // [R][D]
+    float* os = reinterpret_cast<float*>(&sm.kv[0][0][0][0]);   // [wave][R][D]
+    float* ml = os + kFastWaves * R * D;                         // [wave][R][2]
     if (qrow) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            *reinterpret_cast<float4*>(ostage + lr * D + 32 * w + 16 * j + 4 * lg) =
-                make_float4(acc[j][0] * inv, acc[j][1] * inv, acc[j][2] * inv, acc[j][3] * inv);
-        if (w == 0 && lg == 0) {
-            const int t = lr / G, h = g * G + lr % G;
-            if (single) {
-                if (a.lse)
-                    a.lse[((int64_t)b * T + t) * a.Hq + h] = l_row > 0.f ? (m_run + log2f(l_row)) * kLn2 : -INFINITY;
-            } else {
-                const int64_t slot = ((int64_t)bg * a.nparts + split) * R + lr;
-                a.part_ml[slot * 2] = m_run;
-                a.part_ml[slot * 2 + 1] = l_row;
-            }
+        for (int j = 0; j < 8; ++j)
+            *reinterpret_cast<float4*>(os + (w * R + lr) * D + 16 * j + 4 * lg) =
+                make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+        if (lg == 0) {
+            ml[(w * R + lr) * 2] = m_run;
+            ml[(w * R + lr) * 2 + 1] = l_row;
         }
     }
     __syncthreads();
-    {
-        const int r = tid >> 5, c4 = tid & 31;    // 256 threads: 8 rows x 32 float4
-        const float4 v = *reinterpret_cast<const float4*>(ostage + r * D + 4 * c4);
-        float* dst = single ? a.out + (((int64_t)b * T + r / G) * a.Hq + g * G + r % G) * D
-                            : a.part_acc + (((int64_t)bg * a.nparts + split) * R + r) * D;
-        *reinterpret_cast<float4*>(dst + 4 * c4) = v;
+    for (int q4 = tid; q4 < R * 32; q4 += kFastThreads) {
+        const bool single = a.nparts == 1;
+        const int r = q4 >> 5, c4 = q4 & 31;      // 8 rows x 32 float4 (one pass at 256 threads)
+        float M = kNoLogit;
+#pragma unroll
+        for (int ww = 0; ww < kFastWaves; ++ww) M = fmaxf(M, ml[(ww * R + r) * 2]);
+        float L = 0.f;
+        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int ww = 0; ww < kFastWaves; ++ww) {
+            const float f = __builtin_amdgcn_exp2f(ml[(ww * R + r) * 2] - M);
+            L += ml[(ww * R + r) * 2 + 1] * f;
+            const float4 x = *reinterpret_cast<const float4*>(os + (ww * R + r) * D + 4 * c4);
+            o.x += x.x * f; o.y += x.y * f; o.z += x.z * f; o.w += x.w * f;
+        }
+        const int t = r / G, h = g * G + r % G;
+        if (single) {
+            const float inv = L > 0.f ? 1.f / L : 0.f;
+            o.x *= inv; o.y *= inv; o.z *= inv; o.w *= inv;
+            *reinterpret_cast<float4*>(a.out + (((int64_t)b * T + t) * a.Hq + h) * D + 4 * c4) = o;
+            if (c4 == 0 && a.lse)
+                a.lse[((int64_t)b * T + t) * a.Hq + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+        } else {
+            const int64_t slot = ((int64_t)bg * a.nparts + split) * R + r;
+            *reinterpret_cast<float4*>(a.part_acc + slot * D + 4 * c4) = o;
+            if (c4 == 0) {
+                a.part_ml[slot * 2] = M;
+                a.part_ml[slot * 2 + 1] = L;
+            }
+        }
     }
 }
 
@@ -799,7 +814,7 @@ hipError_t launch_attention(const float* q, int B, int T, int Hq, int Hkv, const
     }
     const unsigned grid = (unsigned)(bg * plan.splits);
     if (use_fast_path(dt, D, a.G, T, chunk, ks, vs)) {
-        hipLaunchKernelGGL(k_attn_bf16_d128_g4t2, dim3(grid), dim3(kThreads), 0, st, a);
+        hipLaunchKernelGGL(k_attn_bf16_d128_g4t2, dim3(grid), dim3(kFastThreads), 0, st, a);
     } else {
         launch_rows<GenericKernel>(dt, D, R, dim3(grid), st, a);
     }
