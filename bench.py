@@ -1036,10 +1036,11 @@ def run(args):
           f"landmarks {lm.nbytes / 1e9:.3f} GB", file=sys.stderr, flush=True)
 
     # Per-layer union sizes (deterministic): the selected-KV bytes of each layer.
-    sel_chunks, overlap, gpu_topk = [], [], []
+    sel_chunks, overlap, gpu_topk, max_chunks = [], [], [], 0
     for l in range(w.layers):
         st.run(qs[l], lm, K, V)
         sel_chunks.append(int(st.count.sum().item()))
+        max_chunks = max(max_chunks, int(st.count.max().item()))
         overlap.append(st.overlap.double().mean().item())
         gpu_topk.append(st.topk_idx.cpu().numpy())
     torch.cuda.synchronize()
@@ -1211,6 +1212,7 @@ def run(args):
         "full_step_frac_hbm_peak": round(full_bytes_step / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "selected_kv_bytes_per_step": int(sel_bytes_step),
         "mean_union_chunks": round(sum(sel_chunks) / (w.layers * w.B * w.Hkv), 2),
+        "max_union_chunks": max_chunks,
         "prediction_accuracy": round(accuracy, 5),
         "roofline": roofline,
         "kernels": kernels,
