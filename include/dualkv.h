@@ -521,8 +521,10 @@ dk_status dk_sparse_decode_attn_noalloc(const float* q, int B, int T, int Hq, in
  * extra->K_new, V_new   : [B, T, Hkv, dk] contiguous (kv_dtype): the step's own
  *                         tokens' keys and values, or both NULL.
  * ws                    : dk_attn_tail_workspace_size(...) bytes; contents on
- *                         entry are ignored.  The tail goes to a partial result of
- *                         its own that is merged with the chunks' partials.
+ *                         entry are ignored.  The size allows the tail a partial
+ *                         result of its own; on the bf16 d = 128, G = 4, T = 2 path
+ *                         the last chunk range attends the tail rows itself and
+ *                         the workspace is used as for dk_sparse_decode_attn.
  * Other arguments and errors: as dk_sparse_decode_attn; DK_ERR_INVALID_ARG also
  * for a NULL extra, a half-given K/V pair or negative tail sizes.
  */

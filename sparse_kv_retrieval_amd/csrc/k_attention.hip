@@ -29,6 +29,12 @@
 // distinct banks.  The running max moves only when a logit exceeds it by a
 // slack, so most tiles need no rescale; the row sums use the rounded weights,
 // so each output stays an exact convex combination of its values.
+//
+// Rows besides the chunks (dk_sparse_decode_attn_tail: a request's tail rows
+// and the step's own rows, causally masked): on the fast path the last range of
+// each (b, g) streams them as extra tiles of the same loop, masked per key row,
+// so they need no partial of their own; elsewhere k_attn_tail writes them as
+// one more partial for the merge.
 #include "dk_common.h"
 
 namespace dk {
@@ -126,6 +132,9 @@ __device__ __forceinline__ f32x4_t mfma16k16(uint2 a, uint2 b, f32x4_t c) {
                                                      c, 0, 0, 0);
 }
 
+// kTail: the (b, g)'s last range also attends the request's tail rows and the
+// step's own rows (masked per key row)
+template <bool kTail>
 __global__ __launch_bounds__(kFastThreads) void k_attn_bf16_d128_g4t2(AttnArgs a) {
     constexpr int D = 128, G = 4, T = 2, R = G * T, KT = 16, NS = kFastStages;
     constexpr int kRowBytes = D * 2;
@@ -140,6 +149,17 @@ __global__ __launch_bounds__(kFastThreads) void k_attn_bf16_d128_g4t2(AttnArgs a
     entry_range(a, bg, split, u0, u1);
     const int tpc = a.chunk / KT;
     const int ntiles = a.pool_blocks > 0 ? (u1 - u0) * tpc : 0;
+    // Rows besides the chunks, attended by the (b, g)'s last range: nt rows of
+    // the request's tail, then the step's T own rows
+    int nt = 0, nx = 0;
+    if (kTail && split == a.splits - 1) {
+        if (a.Kt) {
+            nt = a.tail_len ? a.tail_len[b] : a.tail_max;
+            nt = nt < 0 ? 0 : (nt > a.tail_max ? a.tail_max : nt);
+        }
+        nx = nt + (a.Kn ? T : 0);
+    }
+    const int ttot = ntiles + (nx + KT - 1) / KT;
 
     // Query operand of S^T = K Q^T (B of the 16x16x32 product): lane (lr, lg)
     // holds query row lr (token lr / 4, head g * 4 + lr % 4) at dims
@@ -190,15 +210,47 @@ __global__ __launch_bounds__(kFastThreads) void k_attn_bf16_d128_g4t2(AttnArgs a
     }
     // the wave index as a scalar: the DMA's LDS bases (M0) are then plain SALU math
     const int wu = __builtin_amdgcn_readfirstlane(w);
+    const uint16_t* Ktb = (const uint16_t*)a.Kt + (int64_t)b * a.kts.b + (int64_t)g * a.kts.h;
+    const uint16_t* Vtb = (const uint16_t*)a.Vt + (int64_t)b * a.vts.b + (int64_t)g * a.vts.h;
     auto issue = [&](int it, int slot) {
-        const int e = it / tpc;
-        const int row0 = sm.erow[e] + (it - e * tpc) * KT;
-        const uint16_t* kp = Kb + (int64_t)row0 * a.ks.t;
-        const uint16_t* vp = Vb + (int64_t)row0 * a.vs.t;
+        if (!kTail || it < ntiles) {
+            const int e = it / tpc;
+            const int row0 = sm.erow[e] + (it - e * tpc) * KT;
+            const uint16_t* kp = Kb + (int64_t)row0 * a.ks.t;
+            const uint16_t* vp = Vb + (int64_t)row0 * a.vs.t;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) lds_dma16(kp + koff[jj], lds_addr(&sm.kv[wu][slot][0][jj * 64]));
+            for (int jj = 0; jj < 4; ++jj) lds_dma16(kp + koff[jj], lds_addr(&sm.kv[wu][slot][0][jj * 64]));
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) lds_dma16(vp + voff[jj], lds_addr(&sm.kv[wu][slot][1][jj * 64]));
+            for (int jj = 0; jj < 4; ++jj) lds_dma16(vp + voff[jj], lds_addr(&sm.kv[wu][slot][1][jj * 64]));
+        } else {
+            // tail / own rows: each lane addresses its row; rows past nx read
+            // row 0 (masked below)
+            const int r0 = (it - ntiles) * KT;
+            const uint16_t* kp[4];
+            const uint16_t* vp[4];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int p = jj * 64 + lane;
+                const int row = p >> 4, phys = p & 15;
+                const int xr = r0 + row < nx ? r0 + row : 0;
+                const uint16_t* krow;
+                const uint16_t* vrow;
+                if (xr < nt) {
+                    krow = Ktb + (int64_t)xr * a.kts.t;
+                    vrow = Vtb + (int64_t)xr * a.vts.t;
+                } else {
+                    const int64_t off = (((int64_t)b * T + (xr - nt)) * a.Hkv + g) * D;
+                    krow = (const uint16_t*)a.Kn + off;
+                    vrow = (const uint16_t*)a.Vn + off;
+                }
+                kp[jj] = krow + (phys ^ (row & 15)) * 8;
+                vp[jj] = vrow + (phys ^ (2 * (row & 7))) * 8;
+            }
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) lds_dma16(kp[jj], lds_addr(&sm.kv[wu][slot][0][jj * 64]));
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) lds_dma16(vp[jj], lds_addr(&sm.kv[wu][slot][1][jj * 64]));
+        }
     };
     // Operand reads within a tile (bytes).  K (A of S^T): key lr, logical piece
     // lg + 4 ks.  V (A of O^T = V^T P^T, transposed reads): value dims 16 j + lr,
@@ -226,16 +278,17 @@ __global__ __launch_bounds__(kFastThreads) void k_attn_bf16_d128_g4t2(AttnArgs a
     for (int j = 0; j < 8; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     static_assert(NS == 2, "the waits below count one tile (8 loads) in flight");
-    if (w < ntiles) issue(w, 0);
-    for (int it = w, slot = 0; it < ntiles; it += kFastWaves, slot ^= 1) {
+    if (w < ttot) issue(w, 0);
+    for (int it = w, slot = 0; it < ttot; it += kFastWaves, slot ^= 1) {
         // the other slot was computed in the previous iteration: its reads have
         // returned, so the next tile may overwrite it
-        const bool more = it + kFastWaves < ntiles;
+        const bool more = it + kFastWaves < ttot;
         if (more) issue(it + kFastWaves, slot ^ 1);
         // tile `it` has landed when at most the 8 loads of the next one are pending
         if (more) lds_dma_wait<8>();
         else lds_dma_wait<0>();
-        const uint32_t m_cur = sm.ebits[it / tpc];
+        const bool xtile = kTail && it >= ntiles; // tail / own rows: every query, masked by row
+        const uint32_t m_cur = xtile ? 3u : sm.ebits[it / tpc];
         if (m_cur == 0) continue;
         const char* kb = reinterpret_cast<const char*>(sm.kv[wu][slot][0]);
         const char* vb = reinterpret_cast<const char*>(sm.kv[wu][slot][1]);
@@ -257,7 +310,14 @@ __global__ __launch_bounds__(kFastThreads) void k_attn_bf16_d128_g4t2(AttnArgs a
         float hm = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            z[i] = on ? s[i] * a.scale_log2 : -INFINITY;
+            bool key = true;
+            if (xtile) {
+                // a tail row is seen by every query, the own row of token t' by
+                // the queries of tokens t >= t' (row lr is token lr / 4)
+                const int xr = (it - ntiles) * KT + 4 * lg + i;
+                key = xr < nt || (xr < nx && xr - nt <= (lr >> 2));
+            }
+            z[i] = on && key ? s[i] * a.scale_log2 : -INFINITY;
             hm = fmaxf(hm, z[i]);
         }
         hm = group4_max(hm);
@@ -592,8 +652,8 @@ __global__ __launch_bounds__(kThreads) void k_attn_generic(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Tail rows and the step's own rows, one block per (b, g), written as the last
-// partial of the (b, g) (DualDecoder "5.2": the real token is masked from the
+// Tail rows and the step's own rows off the fast path, one block per (b, g),
+// written as the last partial of the (b, g) (DualDecoder "5.2": the real token is masked from the
 // speculative token's row, the speculative token sees the real one; Adaptive
 // DHiSparse Figure 2: the request's tail rows are resolved for every lookup).
 // Rows 0 .. nt-1 are the tail, rows nt .. nt+T-1 the step's tokens; 64-row
@@ -813,19 +873,27 @@ hipError_t launch_attention(const float* q, int B, int T, int Hq, int Hkv, const
         a.Kn = tail->K_new; a.Vn = tail->V_new;
     }
     const unsigned grid = (unsigned)(bg * plan.splits);
-    if (use_fast_path(dt, D, a.G, T, chunk, ks, vs)) {
-        hipLaunchKernelGGL(k_attn_bf16_d128_g4t2, dim3(grid), dim3(kFastThreads), 0, st, a);
+    const bool fast = use_fast_path(dt, D, a.G, T, chunk, ks, vs);
+    if (fast) {
+        // the fast kernel's last range of each (b, g) attends the tail and own
+        // rows itself: no tail partial, and with one range no merge either
+        if (tail) {
+            a.nparts = plan.splits;
+            hipLaunchKernelGGL(k_attn_bf16_d128_g4t2<true>, dim3(grid), dim3(kFastThreads), 0, st, a);
+        } else {
+            hipLaunchKernelGGL(k_attn_bf16_d128_g4t2<false>, dim3(grid), dim3(kFastThreads), 0, st, a);
+        }
     } else {
         launch_rows<GenericKernel>(dt, D, R, dim3(grid), st, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (tail) {
+    if (tail && !fast) {
         launch_rows<TailKernel>(dt, D, R, dim3((unsigned)bg), st, a);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (plan.nparts == 1) return hipSuccess;
+    if (a.nparts == 1) return hipSuccess;
     if (D == 128) hipLaunchKernelGGL(k_attn_merge<128>, dim3((unsigned)bg), dim3(kThreads), 0, st, a);
     else hipLaunchKernelGGL(k_attn_merge<64>, dim3((unsigned)bg), dim3(kThreads), 0, st, a);
     return hipGetLastError();

@@ -575,6 +575,50 @@ def test_attention_one_range_per_head(dkb):
             assert max_abs(lse[b:b + 1, :, g * w.G:(g + 1) * w.G], rl_) <= tol, (b, g)
 
 
+def test_attention_tail_one_range(dkb):
+    """512 (b, g): one range per (b, g), so the fast kernel attends each request's
+    tail rows and the step's own rows itself and writes the final rows (no
+    partials, no merge).  Ragged unions (some empty), tail lengths 0..40, fresh
+    rows; the oracle checks sampled (b, g), the empty ones included."""
+    w = workload("llama8b_l32k", 64, 2048, k=16)
+    N = w.T * w.k
+    assert w.B * w.Hkv == 512
+    q, K, V = make(w, 79)
+    rng = np.random.default_rng(79)
+    counts = rng.choice([0, 1, 3, N // 2, N], (w.B, w.Hkv))
+    ids, mem, cnt, lists = random_unions(rng, w.B, w.Hkv, N, w.C, counts)
+    gen = torch.Generator().manual_seed(79)
+    tmax = 40
+    Kt = torch.randn(w.B, w.Hkv, tmax, w.d, generator=gen).to(torch.bfloat16)
+    Vt = torch.randn(w.B, w.Hkv, tmax, w.d, generator=gen).to(torch.bfloat16)
+    Kn = torch.randn(w.B, w.T, w.Hkv, w.d, generator=gen).to(torch.bfloat16)
+    Vn = torch.randn(w.B, w.T, w.Hkv, w.d, generator=gen).to(torch.bfloat16)
+    lens = rng.integers(0, tmax + 1, w.B)
+    lens[:3] = [0, tmax, 15]
+    out, lse = dkb.sparse_decode_attn_tail(q, K, V, to_dev(ids), to_dev(mem, torch.uint8), to_dev(cnt), w.chunk,
+                                           w.scale, K_tail=Kt.cuda(), V_tail=Vt.cuda(),
+                                           tail_len=torch.tensor(lens, dtype=torch.int32).cuda(), K_new=Kn.cuda(),
+                                           V_new=Vn.cuda())
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    qh = q.cpu().numpy().astype(np.float64)
+    Kth, Vth, Knh, Vnh = (synth.to_numpy_f64(x) for x in (Kt, Vt, Kn, Vn))
+    empty = [(int(b), int(g)) for b, g in zip(*np.nonzero(counts == 0))][:4]
+    pairs = [(0, 0), (1, 3), (2, 7), (13, 7), (37, 2), (63, 5)] + empty
+    tol = ATOL[w.kv_dtype]
+    for b, g in pairs:
+        sel = np.empty((1, 1, w.T), dtype=object)     # each query's own (ragged) chunk list
+        for t in range(w.T):
+            sel[0, 0, t] = lists[b][g][t]
+        hs = slice(g * w.G, (g + 1) * w.G)
+        ro_, rl_ = O.sparse_attention_tail(qh[b:b + 1, :, hs], synth.to_numpy_f64(K[b:b + 1, g:g + 1]),
+                                           synth.to_numpy_f64(V[b:b + 1, g:g + 1]), sel, w.chunk, w.scale,
+                                           Kth[b:b + 1, g:g + 1], Vth[b:b + 1, g:g + 1], lens[b:b + 1],
+                                           Knh[b:b + 1, :, g:g + 1], Vnh[b:b + 1, :, g:g + 1])
+        assert max_abs(out[b:b + 1, :, hs], ro_) <= tol, (b, g, int(counts[b, g]), int(lens[b]))
+        assert max_abs(lse[b:b + 1, :, hs], rl_) <= tol, (b, g, int(counts[b, g]), int(lens[b]))
+
+
 # ----------------------------------------------------------------------------
 # gather
 # ----------------------------------------------------------------------------
