@@ -21,6 +21,8 @@
 // With the mean reduction the G query heads are averaged first (mean of dot
 // products = dot product with the mean query), so each landmark row costs
 // T dot products; the max reduction keeps all G*T vectors.
+#include <type_traits>
+
 #include "dk_common.h"
 #include "dk_union_core.h"
 
@@ -523,7 +525,8 @@ __host__ __device__ inline size_t select_group_words(int C, int D, int nvec) {
     return (size_t)Cp + (size_t)(Cp > 256 ? Cp : 256) + (size_t)nvec * D + 256 + 16;
 }
 
-template <int D, int NQ, int T, bool MAXRED, int F>
+// KPT: shadow scores each pass-2 thread holds in registers (at least C / 256)
+template <int D, int NQ, int T, bool MAXRED, int F, int KPT>
 __global__ __launch_bounds__(T * kThreads * F) void k_score_select(
     const float* __restrict__ q, int Hq, const uint8_t* __restrict__ lm8, const float* __restrict__ chunk_scale,
     const float* __restrict__ scale_max, const float* __restrict__ lm, dk_strides ls, int Hkv, int C, int k,
@@ -752,7 +755,7 @@ __global__ __launch_bounds__(T * kThreads * F) void k_score_select(
 
     // this thread's contiguous range of shadow scores and chunk scales (both
     // in LDS), kept in registers
-    constexpr int KPT = kShadowMaxC / kThreads;      // scores per thread, at most
+    static_assert(KPT % 4 == 0 && KPT <= kShadowMaxC / kThreads, "KPT: a multiple of 4, at most 24");
     const int per = (C + kThreads - 1) / kThreads;
     const int lo = min(C, tid * per), hi = min(C, lo + per);
     const float* sl = (const float*)smem2 + t * C;
@@ -994,14 +997,32 @@ hipError_t launch_score_select(const float* q, int B, int Hq, const dk_landmark_
     // the waves (rows enough to stream: C >= 512; a short row is latency-bound
     // and pays for the extra waves); with more blocks two resident blocks per
     // CU give the same.
-    if (bg <= 256 && C >= 512)
-        hipLaunchKernelGGL((k_score_select<D, NQ, T, MAXRED, 2>), dim3((unsigned)bg), dim3(2 * T * kThreads), lds, st,
-                           q, Hq, sh->lm8, sh->chunk_scale, sh->scale_max, lm, ls, Hkv, C, k, scale, topk_idx,
-                           topk_score, un);
-    else
-        hipLaunchKernelGGL((k_score_select<D, NQ, T, MAXRED, 1>), dim3((unsigned)bg), dim3(T * kThreads), lds, st,
-                           q, Hq, sh->lm8, sh->chunk_scale, sh->scale_max, lm, ls, Hkv, C, k, scale, topk_idx,
-                           topk_score, un);
+    auto go = [&](auto kpt) {
+        constexpr int KPT = decltype(kpt)::value;
+        if (bg <= 256 && C >= 512)
+            hipLaunchKernelGGL((k_score_select<D, NQ, T, MAXRED, 2, KPT>), dim3((unsigned)bg), dim3(2 * T * kThreads),
+                               lds, st, q, Hq, sh->lm8, sh->chunk_scale, sh->scale_max, lm, ls, Hkv, C, k, scale,
+                               topk_idx, topk_score, un);
+        else
+            hipLaunchKernelGGL((k_score_select<D, NQ, T, MAXRED, 1, KPT>), dim3((unsigned)bg), dim3(T * kThreads),
+                               lds, st, q, Hq, sh->lm8, sh->chunk_scale, sh->scale_max, lm, ls, Hkv, C, k, scale,
+                               topk_idx, topk_score, un);
+    };
+    // pass 2 keeps ceil(C / 256) scores per thread in registers: the mean-reduced
+    // selections (the decode step's) get a register count fitted to C, so no
+    // masked slots run; the others keep the largest
+    constexpr int kMax = kShadowMaxC / kThreads;
+    const int per = (C + kThreads - 1) / kThreads;
+    if constexpr (!MAXRED) {
+        if (per <= 4)
+            go(std::integral_constant<int, 4>{});
+        else if (per <= 16)
+            go(std::integral_constant<int, 16>{});
+        else
+            go(std::integral_constant<int, kMax>{});
+    } else {
+        go(std::integral_constant<int, kMax>{});
+    }
     return hipGetLastError();
 }
 
