@@ -790,14 +790,14 @@ AttnPlan plan_attn(int B, int Hkv, int T, int Hq, int dv, int N, int chunk, bool
     const int64_t bg = (int64_t)B * Hkv;
     const int R = (Hq / Hkv) * T;
     const int64_t tiles = (int64_t)N * ((chunk + 31) / 32);
-    // about 512 blocks: two resident per CU, one round.  Fewer, longer ranges
-    // write fewer partials (at B * Hkv >= 512 none at all, and no merge), and the
-    // partial writes cost far more than their bytes suggest while the ranges'
-    // gathers stream.  For long unions at least ~20 tiles of a full union per
-    // range (about 11 at the usual half-full union), for short ones
-    // (latency-bound) at least ~6; never more entries per range than the fast
-    // path stages in LDS
-    int64_t want = (512 + bg - 1) / bg;
+    // at least about 256 blocks, one per CU: fewer, longer ranges write fewer
+    // partials (at B * Hkv >= 256 none at all, and no merge), and the partial
+    // writes cost far more than their bytes suggest while the ranges' gathers
+    // stream (measured: at B * Hkv = 128 two ranges beat four, at 256 one range
+    // beats two).  For long unions at least ~20 tiles of a full union per range
+    // (about 11 at the usual half-full union), for short ones (latency-bound) at
+    // least ~6; never more entries per range than the fast path stages in LDS
+    int64_t want = (256 + bg - 1) / bg;
     int64_t by_work = tiles >= 120 ? tiles / 20 : tiles / 6;
     if (by_work < 1) by_work = 1;
     int64_t s = want < by_work ? want : by_work;

@@ -250,17 +250,18 @@ def test_attention_tail_rejects(kw, ex, status):
 def test_attention_tail_workspace_size():
     # one more partial slot than the ranges: 1 range per (b, g) at 512 of them + the tail
     assert lib.dk_attn_tail_workspace_size(64, 8, 2, 32, 128, 128, 32) == 64 * 8 * 2 * 8 * 130 * 4
-    # 16 x 8 (b, g): 4 ranges (about 512 blocks) + the tail
-    assert lib.dk_attn_tail_workspace_size(16, 8, 2, 32, 128, 128, 32) == 16 * 8 * 5 * 8 * 130 * 4
+    # 16 x 8 (b, g): 2 ranges (about 256 blocks) + the tail
+    assert lib.dk_attn_tail_workspace_size(16, 8, 2, 32, 128, 128, 32) == 16 * 8 * 3 * 8 * 130 * 4
     # a single range still needs partials once a tail is attended
     assert lib.dk_attn_tail_workspace_size(1, 1, 2, 4, 128, 4, 32) == 1 * 1 * 2 * 8 * 130 * 4
 
 
 def test_attention_workspace_sizes():
-    # 16 x 8 (b, g) rows, 4 ranges each (about 512 blocks), 8 query rows of 128
+    # 16 x 8 (b, g) rows, 2 ranges each (about 256 blocks), 8 query rows of 128
     # values plus (m, l)
-    assert lib.dk_attn_workspace_size(16, 8, 2, 32, 128, 128, 32) == 16 * 8 * 4 * 8 * 130 * 4
-    # 512 (b, g): one range each, no merge, no workspace
+    assert lib.dk_attn_workspace_size(16, 8, 2, 32, 128, 128, 32) == 16 * 8 * 2 * 8 * 130 * 4
+    # 256 or 512 (b, g): one range each, no merge, no workspace
+    assert lib.dk_attn_workspace_size(32, 8, 2, 32, 128, 128, 32) == 0
     assert lib.dk_attn_workspace_size(64, 8, 2, 32, 128, 128, 32) == 0
     # a single (b, g) with few entries: one range, no workspace
     assert lib.dk_attn_workspace_size(1, 1, 2, 4, 128, 4, 32) == 0
