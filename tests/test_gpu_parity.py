@@ -160,6 +160,19 @@ def test_score_topk_full_128k_shape(dkb, shadow):
     print(f"rows differing only by near-ties: {rows_diff}, near-tie chunks: {near}")
 
 
+@pytest.mark.parametrize("C,T", [(1500, 2), (2500, 1), (5000, 2), (6144, 1)])
+def test_score_topk_shadow_register_counts(dkb, C, T):
+    # the fused shadow kernel keeps ceil(C / 256) scores per thread in arrays of
+    # 4, 16 or 24 slots: chunk counts that leave masked slots in the 16- and
+    # 24-slot forms, at two (b, g) per request and both query counts
+    g = torch.Generator().manual_seed(C + T)
+    B, Hkv, G, d = 2, 8, 4, 128
+    lm32 = (torch.randn(B, Hkv, C, d, generator=g) / math.sqrt(32)).numpy()
+    qh = synth.round_bf16(torch.randn(B, T, Hkv * G, d, generator=g)).numpy().astype(np.float64)
+    rows_diff, near = check_score_topk(dkb, qh, lm32, 64, 1.0 / math.sqrt(d), "mean", G, True)
+    print(f"C={C} T={T}: rows differing only by near-ties: {rows_diff}, near-tie chunks: {near}", flush=True)
+
+
 @pytest.mark.parametrize("shadow", [False, True])
 def test_score_topk_exact_ties_and_k_equals_c(dkb, shadow):
     # duplicated landmark rows give bit-identical scores: the lower id must win
