@@ -50,6 +50,8 @@ def parse():
                          "(default: 1024 for one-layer workloads, whose working set fits that cache; 0 otherwise)")
     ap.add_argument("--no-events", action="store_true",
                     help="skip the second pass that times every call with events")
+    ap.add_argument("--two-calls", action="store_true",
+                    help="time the step as score_topk_union + sparse_decode_attn instead of one dk_decode_step")
     ap.add_argument("--no-shadow", action="store_true",
                     help="score from the fp32 landmarks only (no 8-bit landmark shadow)")
     ap.add_argument("--host-copy", choices=("mapped", "copy"), default="mapped",
@@ -1050,7 +1052,11 @@ def run(args):
     accuracy = float(np.mean(overlap)) / w.k
 
     attn_call = "sparse_decode_attn_tail" if args.tail else "sparse_decode_attn"
-    calls = ("score_topk_union", attn_call)
+    # the step as one dk_decode_step call (one fused kernel at this shape) unless the
+    # tail rows or --two-calls ask for the separate calls
+    fused = not args.tail and not args.two_calls
+    split_calls = ("score_topk_union", attn_call)
+    calls = ("decode_step",) if fused else split_calls
     if args.tail:
         # one tail and one pair of fresh rows, shared by the layers like the pool
         gt = torch.Generator(device=dev)
@@ -1066,15 +1072,21 @@ def run(args):
                               dtype=torch.uint8, device=dev)
         tail_rows = int(tail_len.sum().item())
     use_events = not args.no_events
-    call_ms = {c: 0.0 for c in calls}
+    call_ms = {c: 0.0 for c in calls + (split_calls if fused else ())}
 
-    def step(ev_step=None):
+    def step(ev_step=None, one_call=fused):
         """One decode step over every layer; with ev_step, events around every call."""
         for l in range(w.layers):
             q = qs[l]
             e = ev_step[l] if ev_step else None
             if e:
                 e[0].record()
+            if one_call:
+                dkb.decode_step(q, lm, K, V, w.chunk, w.k, w.scale, dkb.DK_REDUCE_MEAN, shadow, st.topk_idx, None,
+                                st.union_ids, st.member, st.count, st.overlap, st.out, st.lse, st.ws_step)
+                if e:
+                    e[1].record()
+                continue
             dkb.score_topk_union(q, lm, w.k, w.scale, dkb.DK_REDUCE_MEAN, st.topk_idx, None, st.union_ids,
                                  st.member, st.count, st.overlap, st.ws_topk, shadow=shadow)
             if e:
@@ -1139,6 +1151,18 @@ def run(args):
                     call_ms[c] += ev[s][l][i].elapsed_time(ev[s][l][i + 1])
         call_pass_ms = sum(ev[s][0][0].elapsed_time(ev[s][w.layers - 1][len(calls)])
                            for s in range(args.steps)) / args.steps
+        if fused:
+            # the same steps once more as the two separate calls, for their own durations
+            ev2 = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(w.layers)]
+                   for _ in range(args.steps)]
+            for s in range(args.steps):
+                flush()
+                step(ev2[s], one_call=False)
+            torch.cuda.synchronize()
+            for s in range(args.steps):
+                for l in range(w.layers):
+                    for i, c in enumerate(split_calls):
+                        call_ms[c] += ev2[s][l][i].elapsed_time(ev2[s][l][i + 1])
     steps_per_s = 1000.0 / ms_per_step
 
     kernels = {}
@@ -1157,7 +1181,9 @@ def run(args):
         attn_call: sel_bytes_step / w.layers
         + (w.Hkv * (tail_rows + w.B * w.T) * w.d * 2 * K.element_size() if args.tail else 0),
     }
-    for c in calls:
+    # the fused call: the selection's bytes (its union stays in the block) and the selected KV
+    per_call_bytes["decode_step"] = score_bytes + w.B * w.Hkv * w.T * w.k * 4 * 3 + sel_bytes_step / w.layers
+    for c in calls + (split_calls if fused else ()):
         if not use_events:
             break
         avg_ms = call_ms[c] / n_launch
@@ -1173,6 +1199,8 @@ def run(args):
     copy_gbps = hbm_copy_gbps(torch, dkb)
 
     dominant = max(kernels, key=lambda c: kernels[c]["avg_us"]) if kernels else None
+    if fused and kernels:
+        dominant = "decode_step"      # the one call of the timed step
     roofline = None
     if dominant:
         kd = kernels[dominant]
@@ -1202,7 +1230,12 @@ def run(args):
         "ms_per_step_median": round(float(np.median(step_ms)), 4),
         "ms_per_step_min": round(float(np.min(step_ms)), 4),
         "timing": "value and ms_per_step: event-free steps (one event per step boundary); kernels and "
-                  "roofline: a second pass of the same steps with events around every call",
+                  "roofline: a second pass of the same steps with events around every call"
+                  + ("; the step is one dk_decode_step call per layer (one fused kernel), and a third pass "
+                     "times the same work as its two separate calls (score_topk_union, sparse_decode_attn: "
+                     "selected_kv_GBps is the selected KV over the separate attention call's time)"
+                     if fused else ""),
+        "step_call": "dk_decode_step" if fused else "dk_score_topk_union + " + ("dk_sparse_decode_attn_tail" if args.tail else "dk_sparse_decode_attn"),
         "ms_per_step_call_pass": None if call_pass_ms is None else round(call_pass_ms, 4),
         "selected_kv_GBps": round(sel_gbps, 1),
         "selected_kv_frac_hbm_peak": round(sel_gbps / HBM_PEAK_GBPS, 4),

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_PKG, "libdualkv.so")
 DK_OK, DK_ERR_INVALID_ARG, DK_ERR_UNSUPPORTED, DK_ERR_HIP = 0, 1, 2, 3
 DK_F32, DK_BF16 = 0, 1
 DK_REDUCE_MEAN, DK_REDUCE_MAX = 0, 1
-ABI_VERSION = 12
+ABI_VERSION = 13
 
 _STATUS = {0: "DK_OK", 1: "DK_ERR_INVALID_ARG", 2: "DK_ERR_UNSUPPORTED", 3: "DK_ERR_HIP"}
 
@@ -73,6 +73,9 @@ EXPORTS = [
                            ctypes.POINTER(dk_landmark_shadow), _P, _P, _P, _Z, _P]),
     ("dk_score_topk_union", _I, [_P, _I, _I, _I, _P, _I, _S, _I, _I, _I, _I, _F, _I,
                                  ctypes.POINTER(dk_landmark_shadow), _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    ("dk_decode_step_workspace_size", _Z, [_I, _I, _I, _I, _I, _I, _I, _I, _I]),
+    ("dk_decode_step", _I, [_P, _I, _I, _I, _I, _P, _I, _S, _I, _I, _I, _F, _I, ctypes.POINTER(dk_landmark_shadow),
+                            _P, _P, _I, _S, _S, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     ("dk_capped_plan", _I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
     ("dk_union_select", _I, [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, ctypes.POINTER(dk_cache_plan), _P]),
     ("dk_gather_kv", _I, [_P, _P, _I, _S, _I, _I, _I, _I, _P, _P, _P, _I, _I, _P, _P, _S, _I, _I, _P]),
@@ -512,6 +515,46 @@ def sparse_decode_attn(q, K, V, block_ids, member, count, chunk: int, scale: flo
     return out, lse
 
 
+def decode_step_workspace_size(B, Hkv, T, Hq, C, d, k, chunk, with_shadow) -> int:
+    return int(lib.dk_decode_step_workspace_size(B, Hkv, T, Hq, C, d, k, chunk, int(bool(with_shadow))))
+
+
+@_on_stream
+def decode_step(q, lm, K, V, chunk: int, k: int, scale: float, reduce: int = DK_REDUCE_MEAN,
+                shadow: Shadow | None = None, topk_idx=None, topk_score=None, union_ids=None, member=None,
+                count=None, overlap=None, out=None, lse=None, ws=None, want_scores=False, want_lse=True,
+                stream=None):
+    """score_topk_union then sparse_decode_attn over its union, as one library call
+    (dk_decode_step: one fused kernel where the shapes allow it)."""
+    B, T, Hq, d = q.shape
+    _, Hkv, C, _ = lm.shape
+    _need(q, torch.float32, (B, T, Hq, d), "q")
+    if K.dtype != V.dtype:
+        raise ValueError("K and V must share a dtype")
+    dev = q.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    topk_idx = torch.empty(B, Hkv, T, k, **i32) if topk_idx is None else topk_idx
+    if topk_score is None and want_scores:
+        topk_score = torch.empty(B, Hkv, T, k, dtype=torch.float32, device=dev)
+    union_ids = torch.empty(B, Hkv, T * k, **i32) if union_ids is None else union_ids
+    member = torch.empty(B, Hkv, T * k, dtype=torch.uint8, device=dev) if member is None else member
+    count = torch.empty(B, Hkv, **i32) if count is None else count
+    overlap = torch.empty(B, Hkv, **i32) if overlap is None else overlap
+    out = torch.empty(B, T, Hq, d, dtype=torch.float32, device=dev) if out is None else out
+    if lse is None and want_lse:
+        lse = torch.empty(B, T, Hq, dtype=torch.float32, device=dev)
+    nbytes = decode_step_workspace_size(B, Hkv, T, Hq, C, d, k, chunk, shadow is not None)
+    if ws is None and nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    csh = ctypes.byref(shadow.as_c()) if shadow is not None else None
+    _check(lib.dk_decode_step(_ptr(q), B, T, Hq, Hkv, _ptr(lm), _dtype(lm), pool_strides(lm), C, d, k,
+                              float(scale), int(reduce), csh, _ptr(K), _ptr(V), _dtype(K), pool_strides(K),
+                              pool_strides(V), chunk, _ptr(topk_idx), _ptr(topk_score), _ptr(union_ids),
+                              _ptr(member), _ptr(count), _ptr(overlap), _ptr(out), _ptr(lse), _ptr(ws),
+                              0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+    return topk_idx, topk_score, union_ids, member, count, overlap, out, lse
+
+
 @_on_stream
 def sparse_decode_attn_noalloc(q, K, V, block_ids, member, count, chunk: int, scale: float,
                                pool_blocks: int | None = None, out=None, lse=None, want_lse=True, stream=None):
@@ -635,8 +678,16 @@ class DecodeStep:
         self.ws_attn = torch.empty(max(n, 1), dtype=torch.uint8, device=device)
         self.out = torch.empty(B, T, Hq, d, dtype=torch.float32, device=device)
         self.lse = torch.empty(B, T, Hq, dtype=torch.float32, device=device)
+        n = decode_step_workspace_size(B, Hkv, T, Hq, C, d, k, chunk, shadow is not None)
+        self.ws_step = torch.empty(max(n, 1), dtype=torch.uint8, device=device)
 
-    def run(self, q, lm, K, V, stream=None):
+    def run(self, q, lm, K, V, stream=None, fused=False):
+        """The two calls, or with fused=True the one dk_decode_step call (same results)."""
+        if fused:
+            decode_step(q, lm, K, V, self.chunk, self.k, self.scale, self.reduce, self.shadow, self.topk_idx,
+                        self.topk_score, self.union_ids, self.member, self.count, self.overlap, self.out,
+                        self.lse, self.ws_step, stream=stream)
+            return self.out, self.lse
         score_topk_union(q, lm, self.k, self.scale, self.reduce, self.topk_idx, self.topk_score,
                          self.union_ids, self.member, self.count, self.overlap, self.ws_topk,
                          shadow=self.shadow, stream=stream)

@@ -623,6 +623,61 @@ dk_status dk_sparse_decode_attn(const float* q, int B, int T, int Hq, int Hkv, c
     return e == hipSuccess ? DK_OK : hip_fail(e, fn);
 }
 
+size_t dk_decode_step_workspace_size(int B, int Hkv, int T, int Hq, int C, int d, int k, int chunk,
+                                     int with_shadow) {
+    if (B < 1 || Hkv < 1 || T < 1 || Hq < 1 || C < 1 || d < 1 || k < 1 || chunk < 1) return 0;
+    const size_t a = dk_score_topk_workspace_size(B, Hkv, T, C, k, with_shadow);
+    const size_t b = dk_attn_workspace_size(B, Hkv, T, Hq, d, T * k, chunk);
+    return a > b ? a : b;
+}
+
+dk_status dk_decode_step(const float* q, int B, int T, int Hq, int Hkv, const void* lm, dk_dtype lm_dtype,
+                         dk_strides ls, int C, int d, int k, float scale, dk_group_reduce reduce,
+                         const dk_landmark_shadow* shadow, const void* K, const void* V, dk_dtype kv_dtype,
+                         dk_strides ks, dk_strides vs, int chunk, int32_t* topk_idx, float* topk_score,
+                         int32_t* union_ids, uint8_t* member, int32_t* union_count, int32_t* overlap, float* out,
+                         float* lse, void* ws, size_t ws_bytes, void* stream) {
+    g_err.clear();
+    const char* fn = "dk_decode_step";
+    DK_REQUIRE(lm_dtype == DK_F32, DK_ERR_UNSUPPORTED, "%s: landmarks must be DK_F32", fn);
+    dk::TopkPlan tplan{};
+    // the two calls' checks, before anything is enqueued (the workspace serves them in turn)
+    dk_status s = check_score_topk(fn, q, B, T, Hq, lm, lm_dtype, ls, Hkv, C, d, k, scale, reduce, shadow, topk_idx,
+                                   ws, ws_bytes, &tplan);
+    if (s != DK_OK) return s;
+    DK_REQUIRE(union_ids && member && union_count, DK_ERR_INVALID_ARG,
+               "%s: union_ids, member, union_count must be non-NULL", fn);
+    s = check_union(fn, T, k, 0, false);
+    if (s != DK_OK) return s;
+    AttnCall c{};
+    s = check_attn(fn, q, B, T, Hq, Hkv, K, V, kv_dtype, ks, vs, d, d, chunk, union_ids, member, out, C, T * k,
+                   scale, &c);
+    if (s != DK_OK) return s;
+    DK_REQUIRE(ws_bytes >= c.ws_bytes && (c.ws_bytes == 0 || ws), DK_ERR_INVALID_ARG,
+               "%s: workspace needs %zu bytes (got %zu)", fn, c.ws_bytes > tplan.ws_bytes ? c.ws_bytes : tplan.ws_bytes,
+               ws_bytes);
+    const dk::UnionOut un{union_ids, member, union_count, overlap};
+    const hipStream_t st = (hipStream_t)stream;
+    // One kernel when every (b, g) is one block of each call: the shadow selection
+    // with its union in the block (k + 1 <= 256), the attention fast path with one
+    // range per (b, g) and no partials, and 512 threads per selection block.
+    const bool fused = shadow && reduce == DK_REDUCE_MEAN && T == 2 && Hq == 4 * Hkv && d == 128 && !c.latent &&
+                       dk::use_fast_path(kv_dtype, d, Hq / Hkv, T, chunk, ks, vs) && c.plan.splits == 1 &&
+                       c.plan.nparts == 1 && k + 1 <= 256 && (int64_t)B * Hkv > 256;
+    hipError_t e;
+    if (fused) {
+        e = dk::launch_step_fused(q, B, Hq, Hkv, C, k, scale, shadow, (const float*)lm, ls, K, V, ks, vs, chunk,
+                                  topk_idx, topk_score, un, out, lse, st);
+    } else {
+        e = dk::launch_score_topk(q, B, T, Hq, (const float*)lm, ls, Hkv, C, d, k, scale, reduce, shadow, topk_idx,
+                                  topk_score, ws, tplan, &un, st);
+        if (e == hipSuccess)
+            e = run_attn(c, q, B, T, Hq, Hkv, K, V, kv_dtype, ks, vs, d, chunk, union_ids, member, union_count,
+                         T * k, C, scale, out, lse, ws, st);
+    }
+    return e == hipSuccess ? DK_OK : hip_fail(e, fn);
+}
+
 dk_status dk_sparse_decode_attn_noalloc(const float* q, int B, int T, int Hq, int Hkv, const void* K,
                                         const void* V, dk_dtype kv_dtype, dk_strides ks, dk_strides vs, int dk,
                                         int dv, int chunk, const int32_t* block_ids, const uint8_t* member,

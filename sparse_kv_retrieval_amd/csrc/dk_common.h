@@ -244,6 +244,12 @@ struct UnionOut {
     int32_t* count;      // [B, Hkv]
     int32_t* overlap;    // [B, Hkv] or null
 };
+// One fused kernel for dk_decode_step (shadow scores, selection, union and the
+// attention fast path per (b, g)); T = 2, G = 4, d = 128, bf16 K/V, mean reduce.
+hipError_t launch_step_fused(const float* q, int B, int Hq, int Hkv, int C, int k, float scale,
+                             const dk_landmark_shadow* sh, const float* lm, dk_strides ls, const void* K,
+                             const void* V, dk_strides ks, dk_strides vs, int chunk, int32_t* topk_idx,
+                             float* topk_score, const UnionOut& un, float* out, float* lse, hipStream_t st);
 hipError_t launch_score_topk(const float* q, int B, int T, int Hq, const float* lm, dk_strides ls,
                              int Hkv, int C, int d, int k, float scale, dk_group_reduce reduce,
                              const dk_landmark_shadow* shadow, int32_t* topk_idx, float* topk_score,
@@ -340,6 +346,8 @@ struct AttnTail {
     const void* V_new;
 };
 AttnPlan plan_attn(int B, int Hkv, int T, int Hq, int dv, int N, int chunk, bool tail = false);
+// the attention fast path's shapes: bf16, d = 128, G = 4, T = 2, chunk a multiple of 32
+bool use_fast_path(dk_dtype dt, int D, int G, int T, int chunk, dk_strides ks, dk_strides vs);
 hipError_t launch_attention(const float* q, int B, int T, int Hq, int Hkv, const void* K,
                             const void* V, dk_dtype dt, dk_strides ks, dk_strides vs, int D,
                             int chunk, const int32_t* block_ids, const uint8_t* member,

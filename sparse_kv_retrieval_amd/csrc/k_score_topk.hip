@@ -23,6 +23,7 @@
 // T dot products; the max reduction keeps all G*T vectors.
 #include <type_traits>
 
+#include "dk_attn_fast.h"
 #include "dk_common.h"
 #include "dk_union_core.h"
 
@@ -525,23 +526,23 @@ __host__ __device__ inline size_t select_group_words(int C, int D, int nvec) {
     return (size_t)Cp + (size_t)(Cp > 256 ? Cp : 256) + (size_t)nvec * D + 256 + 16;
 }
 
-// KPT: shadow scores each pass-2 thread holds in registers (at least C / 256)
+// The work of one (b, g): the block's threads in LDS smem2 (T groups of
+// select_group_words).  KPT: shadow scores each pass-2 thread holds in registers
+// (at least C / 256).
 template <int D, int NQ, int T, bool MAXRED, int F, int KPT>
-__global__ __launch_bounds__(T * kThreads * F) void k_score_select(
-    const float* __restrict__ q, int Hq, const uint8_t* __restrict__ lm8, const float* __restrict__ chunk_scale,
-    const float* __restrict__ scale_max, const float* __restrict__ lm, dk_strides ls, int Hkv, int C, int k,
-    float scale, int32_t* __restrict__ topk_idx, float* __restrict__ topk_score, UnionOut un) {
+__device__ __forceinline__ void score_select_block(
+    uint32_t* smem2, int bg, const float* __restrict__ q, int Hq, const uint8_t* __restrict__ lm8,
+    const float* __restrict__ chunk_scale, const float* __restrict__ scale_max, const float* __restrict__ lm,
+    dk_strides ls, int Hkv, int C, int k, float scale, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_score, const UnionOut& un) {
     constexpr int NVEC = MAXRED ? NQ / T : 1;          // query vectors per group
     constexpr int NW = T * F * kThreads / kWave;       // waves of the block (pass 1 uses all)
-    extern __shared__ uint32_t smem2[];
     const int Cp = (C + 3) & ~3;
     const int cand_words = Cp > kThreads ? Cp : kThreads;
     const size_t gw = select_group_words(C, D, NVEC);
     auto qv_of = [&](int u) { return (float*)(smem2 + (size_t)u * gw + Cp + cand_words); };
     auto misc_of = [&](int u) { return (int*)(smem2 + (size_t)u * gw + gw - 6); };
 
-    int bg, unused;
-    xcd_unit(blockIdx.x, 1, gridDim.x, bg, unused);
     const int b = bg / Hkv, g = bg - b * Hkv;
     const int Gq = Hq / Hkv;
     const float SM = scale_max[bg];   // for pass 2, loaded early
@@ -949,6 +950,51 @@ __global__ __launch_bounds__(T * kThreads * F) void k_score_select(
     }
 }
 
+// One decode step of one layer for one (b, g) per block: the shadow scoring,
+// exact selection and union above, then the attention fast path over the union
+// the block has just written.  A block needs no other block's result, so the
+// blocks that finish their selection early stream their attention while the
+// others still score: the selection phase of one block overlaps the gathers of
+// another, and the attention launch and its start-up latency go away.
+struct StepArgs {
+    const float* q;
+    int Hq, Hkv, C, k;
+    float scale;
+    const uint8_t* lm8;
+    const float* chunk_scale;
+    const float* scale_max;
+    const float* lm;
+    dk_strides ls;
+    int32_t* topk_idx;
+    float* topk_score;
+    UnionOut un;
+    attn::AttnArgs a;   // block_ids / member / count are the union outputs
+};
+
+template <int KPT>
+__global__ __launch_bounds__(2 * kThreads) void k_step_fused(StepArgs s) {
+    extern __shared__ uint32_t smem2[];
+    int bg, unused;
+    xcd_unit(blockIdx.x, 1, gridDim.x, bg, unused);
+    score_select_block<128, 2, 2, false, 1, KPT>(smem2, bg, s.q, s.Hq, s.lm8, s.chunk_scale, s.scale_max, s.lm,
+                                                 s.ls, s.Hkv, s.C, s.k, s.scale, s.topk_idx, s.topk_score, s.un);
+    __syncthreads();   // the union this block wrote is visible to all its threads; LDS is free
+    if (threadIdx.x >= attn::kFastThreads) return;
+    attn::attn_fast_block<false>(s.a, *reinterpret_cast<attn::FastSmem*>(smem2), bg, 0);
+}
+
+template <int D, int NQ, int T, bool MAXRED, int F, int KPT>
+__global__ __launch_bounds__(T * kThreads * F) void k_score_select(
+    const float* __restrict__ q, int Hq, const uint8_t* __restrict__ lm8, const float* __restrict__ chunk_scale,
+    const float* __restrict__ scale_max, const float* __restrict__ lm, dk_strides ls, int Hkv, int C, int k,
+    float scale, int32_t* __restrict__ topk_idx, float* __restrict__ topk_score, UnionOut un) {
+    extern __shared__ uint32_t smem2[];
+    int bg, unused;
+    xcd_unit(blockIdx.x, 1, gridDim.x, bg, unused);
+    score_select_block<D, NQ, T, MAXRED, F, KPT>(smem2, bg, q, Hq, lm8, chunk_scale, scale_max, lm, ls, Hkv, C, k,
+                                                 scale, topk_idx, topk_score, un);
+}
+
 
 template <int D, int NQ, int T, bool MAXRED>
 hipError_t launch_split(const float* q, int B, int Hq, const float* lm, dk_strides ls, int Hkv,
@@ -1141,6 +1187,37 @@ hipError_t launch_score_topk(const float* q, int B, int T, int Hq, const float* 
     if (!un) return hipSuccess;
     return launch_union(topk_idx, B, Hkv, T, k, C, un->ids, un->member, un->count, un->overlap, nullptr,
                         st);
+}
+
+
+hipError_t launch_step_fused(const float* q, int B, int Hq, int Hkv, int C, int k, float scale,
+                             const dk_landmark_shadow* sh, const float* lm, dk_strides ls, const void* K,
+                             const void* V, dk_strides ks, dk_strides vs, int chunk, int32_t* topk_idx,
+                             float* topk_score, const UnionOut& un, float* out, float* lse, hipStream_t st) {
+    constexpr int T = 2;
+    StepArgs s{};
+    s.q = q; s.Hq = Hq; s.Hkv = Hkv; s.C = C; s.k = k; s.scale = scale;
+    s.lm8 = sh->lm8; s.chunk_scale = sh->chunk_scale; s.scale_max = sh->scale_max;
+    s.lm = lm; s.ls = ls; s.topk_idx = topk_idx; s.topk_score = topk_score; s.un = un;
+    attn::AttnArgs& a = s.a;
+    a.q = q; a.Hq = Hq; a.Hkv = Hkv; a.T = T; a.G = Hq / Hkv;
+    a.K = K; a.V = V; a.ks = ks; a.vs = vs; a.chunk = chunk;
+    a.block_ids = un.ids; a.member = un.member; a.count = un.count;
+    a.N = T * k; a.pool_blocks = C;
+    a.scale_log2 = scale * attn::kLog2e;
+    a.splits = 1; a.nparts = 1;
+    a.out = out; a.lse = lse;
+    const size_t lds_sel = (size_t)T * select_group_words(C, 128, 1) * 4;
+    const size_t lds = lds_sel > sizeof(attn::FastSmem) ? lds_sel : sizeof(attn::FastSmem);
+    const unsigned grid = (unsigned)((int64_t)B * Hkv);
+    const int per = (C + kThreads - 1) / kThreads;
+    if (per <= 4)
+        hipLaunchKernelGGL(k_step_fused<4>, dim3(grid), dim3(2 * kThreads), lds, st, s);
+    else if (per <= 16)
+        hipLaunchKernelGGL(k_step_fused<16>, dim3(grid), dim3(2 * kThreads), lds, st, s);
+    else
+        hipLaunchKernelGGL(k_step_fused<kShadowMaxC / kThreads>, dim3(grid), dim3(2 * kThreads), lds, st, s);
+    return hipGetLastError();
 }
 
 }  // namespace dk

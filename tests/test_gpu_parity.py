@@ -766,18 +766,19 @@ def test_step_tiny_full(dkb, shadow):
     check_step_sampled(dkb, w, q, K, V, st, [(0, 0)])
 
 
-@pytest.mark.parametrize("name,samples", [
-    ("llama8b_l32k", [(0, 0), (7, 3), (15, 7)]),
-    ("b64_l128k", [(0, 0), (37, 5), (63, 7)]),
+@pytest.mark.parametrize("name,samples,fused", [
+    ("llama8b_l32k", [(0, 0), (7, 3), (15, 7)], False),
+    ("b64_l128k", [(0, 0), (37, 5), (63, 7)], False),
+    ("b64_l128k", [(1, 1), (30, 6), (62, 0)], True),    # dk_decode_step: the bench's one fused kernel
 ])
-def test_step_full_size_sampled(dkb, name, samples):
+def test_step_full_size_sampled(dkb, name, samples, fused):
     """Full-size workload in the bench's launch configuration, oracle on sampled (b, g)."""
     w = WORKLOADS[name]
     q, K, V = make(w, 1)
     lm = dkb.build_landmarks(K, w.chunk)
     sh = dkb.build_landmark_shadow(lm)
     st = dkb.DecodeStep(w.B, w.T, w.Hq, w.Hkv, w.d, w.C, w.chunk, w.k, w.scale, "cuda", shadow=sh)
-    st.run(q, lm, K, V)
+    st.run(q, lm, K, V, fused=fused)
     torch.cuda.synchronize()
     near = check_step_sampled(dkb, w, q, K, V, st, samples)
     acc = st.overlap.float().mean().item() / w.k
@@ -795,6 +796,60 @@ def test_step_full_size_sampled(dkb, name, samples):
     print(f"{name}: attention of all {w.B * w.Hkv} (b, g) within {worst:.3e}")
     del K, V, lm
     torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------------------
+# dk_decode_step: score_topk_union and sparse_decode_attn in one call (one fused
+# kernel where the shapes allow it, else the two calls' kernels)
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,B,L,kw,shadow,reduce", [
+    ("b64_l128k", 40, 8192, {}, True, "mean"),             # fused: 320 (b, g)
+    ("b64_l128k", 33, 16384, dict(k=128), True, "mean"),   # fused: 264 (b, g), up to 256 union entries
+    ("b64_l128k", 40, 4096, dict(k=1), True, "mean"),      # fused, one chunk per query
+    ("b64_l128k", 40, 8192, {}, False, "mean"),            # fp32 landmarks: the two calls
+    ("b64_l128k", 40, 8192, {}, True, "max"),              # max reduction: the two calls
+    ("b64_l128k", 40, 8192, dict(T=1), True, "mean"),      # one query: the two calls
+    ("llama8b_l32k", 16, 8192, {}, True, "mean"),          # 128 (b, g): the two calls
+])
+def test_decode_step_equals_two_calls(dkb, name, B, L, kw, shadow, reduce):
+    """Every output of dk_decode_step equals the two calls' bit for bit, on two query
+    sets in turn through the same buffers (nothing of the first call carries over)."""
+    w = workload(name, B, L, **kw)
+    q, K, V = make(w, 31)
+    q2 = synth.make_queries(w, 32, device="cuda")
+    lm = dkb.build_landmarks(K, w.chunk)
+    sh = dkb.build_landmark_shadow(lm) if shadow else None
+    red = dkb.DK_REDUCE_MAX if reduce == "max" else dkb.DK_REDUCE_MEAN
+    two, one = (dkb.DecodeStep(w.B, w.T, w.Hq, w.Hkv, w.d, w.C, w.chunk, w.k, w.scale, "cuda", reduce=red, shadow=sh)
+                for _ in range(2))
+    print(f"case {name} B={B} L={L} {kw} shadow={shadow} {reduce}", flush=True)
+    for qq in (q2, q):
+        two.run(qq, lm, K, V)
+        one.run(qq, lm, K, V, fused=True)
+        torch.cuda.synchronize()
+        for out in ("topk_idx", "topk_score", "union_ids", "member", "count", "overlap", "out", "lse"):
+            assert torch.equal(getattr(two, out), getattr(one, out)), out
+
+
+def test_decode_step_fused_against_oracle(dkb):
+    """The fused kernel against the oracle: sampled selections (near-ties counted), the
+    union of every (b, g) from the GPU's sets, and attention of every (b, g)."""
+    w = workload("b64_l128k", 40, 8192)
+    q, K, V = make(w, 33)
+    lm = dkb.build_landmarks(K, w.chunk)
+    sh = dkb.build_landmark_shadow(lm)
+    st = dkb.DecodeStep(w.B, w.T, w.Hq, w.Hkv, w.d, w.C, w.chunk, w.k, w.scale, "cuda", shadow=sh)
+    st.run(q, lm, K, V, fused=True)
+    torch.cuda.synchronize()
+    near = check_step_sampled(dkb, w, q, K, V, st, [(0, 0), (17, 3), (39, 7)])
+    ru, rm, rc, ro = O.union_select(st.topk_idx.cpu().numpy())
+    np.testing.assert_array_equal(st.union_ids.cpu().numpy(), ru)
+    np.testing.assert_array_equal(st.member.cpu().numpy(), rm)
+    np.testing.assert_array_equal(st.count.cpu().numpy(), rc)
+    np.testing.assert_array_equal(st.overlap.cpu().numpy(), ro)
+    worst = check_attention_every_pair(w, q, K, V, st)
+    print(f"near-tie chunks {near}; attention of all {w.B * w.Hkv} (b, g) within {worst:.3e}", flush=True)
 
 
 # ----------------------------------------------------------------------------
