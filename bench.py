@@ -1052,10 +1052,12 @@ def run(args):
     accuracy = float(np.mean(overlap)) / w.k
 
     attn_call = "sparse_decode_attn_tail" if args.tail else "sparse_decode_attn"
-    # the step as one dk_decode_step call (one fused kernel at this shape) unless the
-    # tail rows or --two-calls ask for the separate calls
-    fused = not args.tail and not args.two_calls
+    # the step as one dk_decode_step call (one fused kernel at this shape; with tail
+    # rows the call runs the two calls' kernels) unless --two-calls asks for the
+    # separate calls
+    fused = not args.two_calls
     split_calls = ("score_topk_union", attn_call)
+    step_kernels = "the two calls' kernels, tail rows included" if args.tail else "one fused kernel"
     calls = ("decode_step",) if fused else split_calls
     if args.tail:
         # one tail and one pair of fresh rows, shared by the layers like the pool
@@ -1071,6 +1073,12 @@ def run(args):
         ws_tail = torch.empty(dkb.attn_tail_workspace_size(w.B, w.Hkv, w.T, w.Hq, w.d, w.T * w.k, w.chunk),
                               dtype=torch.uint8, device=dev)
         tail_rows = int(tail_len.sum().item())
+        ws_step = torch.empty(max(1, dkb.decode_step_workspace_size(w.B, w.Hkv, w.T, w.Hq, w.C, w.d, w.k, w.chunk,
+                                                                    shadow is not None, True)),
+                              dtype=torch.uint8, device=dev)
+        tail_kw = dict(K_tail=K_tail, V_tail=V_tail, tail_len=tail_len, K_new=K_new, V_new=V_new)
+    else:
+        ws_step, tail_kw = st.ws_step, {}
     use_events = not args.no_events
     call_ms = {c: 0.0 for c in calls + (split_calls if fused else ())}
 
@@ -1083,7 +1091,7 @@ def run(args):
                 e[0].record()
             if one_call:
                 dkb.decode_step(q, lm, K, V, w.chunk, w.k, w.scale, dkb.DK_REDUCE_MEAN, shadow, st.topk_idx, None,
-                                st.union_ids, st.member, st.count, st.overlap, st.out, st.lse, st.ws_step)
+                                st.union_ids, st.member, st.count, st.overlap, st.out, st.lse, ws_step, **tail_kw)
                 if e:
                     e[1].record()
                 continue
@@ -1182,7 +1190,7 @@ def run(args):
         + (w.Hkv * (tail_rows + w.B * w.T) * w.d * 2 * K.element_size() if args.tail else 0),
     }
     # the fused call: the selection's bytes (its union stays in the block) and the selected KV
-    per_call_bytes["decode_step"] = score_bytes + w.B * w.Hkv * w.T * w.k * 4 * 3 + sel_bytes_step / w.layers
+    per_call_bytes["decode_step"] = per_call_bytes["score_topk_union"] + per_call_bytes[attn_call]
     for c in calls + (split_calls if fused else ()):
         if not use_events:
             break
@@ -1204,7 +1212,8 @@ def run(args):
     roofline = None
     if dominant:
         kd = kernels[dominant]
-        traffic = measured_traffic(w.name, dominant)
+        # the counter summaries are of runs without tail rows
+        traffic = None if args.tail else measured_traffic(w.name, dominant)
         roofline = {"bound": "hbm", "kernel": dominant, "achieved": kd["GBps"], "peak": HBM_PEAK_GBPS,
                     "unit": "GB/s", "frac": round(kd["GBps"] / HBM_PEAK_GBPS, 4),
                     "traffic": None if traffic is None else int(traffic)}
@@ -1231,9 +1240,9 @@ def run(args):
         "ms_per_step_min": round(float(np.min(step_ms)), 4),
         "timing": "value and ms_per_step: event-free steps (one event per step boundary); kernels and "
                   "roofline: a second pass of the same steps with events around every call"
-                  + ("; the step is one dk_decode_step call per layer (one fused kernel), and a third pass "
-                     "times the same work as its two separate calls (score_topk_union, sparse_decode_attn: "
-                     "selected_kv_GBps is the selected KV over the separate attention call's time)"
+                  + (f"; the step is one dk_decode_step call per layer ({step_kernels}), "
+                     f"and a third pass times the same work as its two separate calls (score_topk_union, "
+                     f"{attn_call}: selected_kv_GBps is the selected KV over the separate attention call's time)"
                      if fused else ""),
         "step_call": "dk_decode_step" if fused else "dk_score_topk_union + " + ("dk_sparse_decode_attn_tail" if args.tail else "dk_sparse_decode_attn"),
         "ms_per_step_call_pass": None if call_pass_ms is None else round(call_pass_ms, 4),

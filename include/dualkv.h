@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define DK_ABI_VERSION 13
+#define DK_ABI_VERSION 14
 
 typedef enum {
     DK_OK = 0,
@@ -501,40 +501,6 @@ dk_status dk_sparse_decode_attn_noalloc(const float* q, int B, int T, int Hq, in
                                         float* out, float* lse, void* stream);
 
 /*
- * dk_decode_step - one layer's decode step in one call: dk_score_topk_union
- * followed by dk_sparse_decode_attn over the union it wrote.
- *
- * DualDecoder "4.1" (the index from the query and the landmarks), "4.2" and
- * "5.3" (attention over the retrieved chunks equals attention over the true
- * index), "5.2" and "6.4" (both tokens in one pass); Adaptive DHiSparse
- * Figure 3 (2) (each query attends over its own selection, each union chunk is
- * read once).
- *
- * The arguments are those of the two calls: q, B, T, Hq, Hkv, lm (DK_F32),
- * ls, C, d, k, scale, reduce and shadow as for dk_score_topk_union; K, V,
- * kv_dtype, ks, vs and chunk as for dk_sparse_decode_attn with dk = dv = d, the
- * union as its block_ids / member / count, N = T*k and pool_blocks = C.  The
- * outputs are both calls' outputs (topk_score and overlap may be NULL, lse may
- * be NULL) and equal theirs bit for bit.  ws: dk_decode_step_workspace_size
- * bytes (NULL when 0).  Errors are those of the two calls, checked before
- * anything is enqueued.
- *
- * With a shadow, the mean reduction, T = 2, G = 4, d = 128, bf16 K/V, chunk a
- * multiple of 32, k <= 128 and B*Hkv > 256, one kernel does both: each block
- * scores, selects and merges one (b, g), then attends over that union, so the
- * blocks that finish their selection early stream their attention while others
- * still select.  Other shapes run the two calls' kernels in turn.
- */
-size_t dk_decode_step_workspace_size(int B, int Hkv, int T, int Hq, int C, int d, int k, int chunk,
-                                     int with_shadow);
-dk_status dk_decode_step(const float* q, int B, int T, int Hq, int Hkv, const void* lm, dk_dtype lm_dtype,
-                         dk_strides ls, int C, int d, int k, float scale, dk_group_reduce reduce,
-                         const dk_landmark_shadow* shadow, const void* K, const void* V, dk_dtype kv_dtype,
-                         dk_strides ks, dk_strides vs, int chunk, int32_t* topk_idx, float* topk_score,
-                         int32_t* union_ids, uint8_t* member, int32_t* union_count, int32_t* overlap, float* out,
-                         float* lse, void* ws, size_t ws_bytes, void* stream);
-
-/*
  * dk_sparse_decode_attn_tail - dk_sparse_decode_attn plus the rows every query
  * attends besides its chunks.
  *
@@ -579,6 +545,44 @@ dk_status dk_sparse_decode_attn_tail(const float* q, int B, int T, int Hq, int H
                                      const int32_t* count, int N, int pool_blocks,
                                      const dk_attn_extra* extra, float scale,
                                      float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * dk_decode_step - one layer's decode step in one call: dk_score_topk_union
+ * followed by dk_sparse_decode_attn over the union it wrote.
+ *
+ * DualDecoder "4.1" (the index from the query and the landmarks), "4.2" and
+ * "5.3" (attention over the retrieved chunks equals attention over the true
+ * index), "5.2" and "6.4" (both tokens in one pass); Adaptive DHiSparse
+ * Figure 3 (2) (each query attends over its own selection, each union chunk is
+ * read once).
+ *
+ * The arguments are those of the two calls: q, B, T, Hq, Hkv, lm (DK_F32),
+ * ls, C, d, k, scale, reduce and shadow as for dk_score_topk_union; K, V,
+ * kv_dtype, ks, vs and chunk as for dk_sparse_decode_attn with dk = dv = d, the
+ * union as its block_ids / member / count, N = T*k and pool_blocks = C.  The
+ * outputs are both calls' outputs (topk_score and overlap may be NULL, lse may
+ * be NULL) and equal theirs bit for bit.  extra: NULL, or the tail rows and the
+ * step's own rows of dk_sparse_decode_attn_tail (which then replaces
+ * dk_sparse_decode_attn, with its causal rule).  ws:
+ * dk_decode_step_workspace_size bytes (with_tail: extra is given; NULL when 0).
+ * Errors are those of the two calls, checked before anything is enqueued.
+ *
+ * With a shadow, the mean reduction, T = 2, G = 4, d = 128, bf16 K/V, chunk a
+ * multiple of 32, k <= 128 and B*Hkv > 256, one kernel does both: each block
+ * scores, selects and merges one (b, g), then attends over that union, so the
+ * blocks that finish their selection early stream their attention while others
+ * still select.  Other shapes, and calls with extra, run the two calls' kernels
+ * in turn.
+ */
+size_t dk_decode_step_workspace_size(int B, int Hkv, int T, int Hq, int C, int d, int k, int chunk,
+                                     int with_shadow, int with_tail);
+dk_status dk_decode_step(const float* q, int B, int T, int Hq, int Hkv, const void* lm, dk_dtype lm_dtype,
+                         dk_strides ls, int C, int d, int k, float scale, dk_group_reduce reduce,
+                         const dk_landmark_shadow* shadow, const void* K, const void* V, dk_dtype kv_dtype,
+                         dk_strides ks, dk_strides vs, int chunk, const dk_attn_extra* extra,
+                         int32_t* topk_idx, float* topk_score,
+                         int32_t* union_ids, uint8_t* member, int32_t* union_count, int32_t* overlap, float* out,
+                         float* lse, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_PKG, "libdualkv.so")
 DK_OK, DK_ERR_INVALID_ARG, DK_ERR_UNSUPPORTED, DK_ERR_HIP = 0, 1, 2, 3
 DK_F32, DK_BF16 = 0, 1
 DK_REDUCE_MEAN, DK_REDUCE_MAX = 0, 1
-ABI_VERSION = 13
+ABI_VERSION = 14
 
 _STATUS = {0: "DK_OK", 1: "DK_ERR_INVALID_ARG", 2: "DK_ERR_UNSUPPORTED", 3: "DK_ERR_HIP"}
 
@@ -73,9 +73,10 @@ EXPORTS = [
                            ctypes.POINTER(dk_landmark_shadow), _P, _P, _P, _Z, _P]),
     ("dk_score_topk_union", _I, [_P, _I, _I, _I, _P, _I, _S, _I, _I, _I, _I, _F, _I,
                                  ctypes.POINTER(dk_landmark_shadow), _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
-    ("dk_decode_step_workspace_size", _Z, [_I, _I, _I, _I, _I, _I, _I, _I, _I]),
+    ("dk_decode_step_workspace_size", _Z, [_I, _I, _I, _I, _I, _I, _I, _I, _I, _I]),
     ("dk_decode_step", _I, [_P, _I, _I, _I, _I, _P, _I, _S, _I, _I, _I, _F, _I, ctypes.POINTER(dk_landmark_shadow),
-                            _P, _P, _I, _S, _S, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
+                            _P, _P, _I, _S, _S, _I, ctypes.POINTER(dk_attn_extra), _P, _P, _P, _P, _P, _P, _P, _P,
+                            _P, _Z, _P]),
     ("dk_capped_plan", _I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
     ("dk_union_select", _I, [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, ctypes.POINTER(dk_cache_plan), _P]),
     ("dk_gather_kv", _I, [_P, _P, _I, _S, _I, _I, _I, _I, _P, _P, _P, _I, _I, _P, _P, _S, _I, _I, _P]),
@@ -515,17 +516,37 @@ def sparse_decode_attn(q, K, V, block_ids, member, count, chunk: int, scale: flo
     return out, lse
 
 
-def decode_step_workspace_size(B, Hkv, T, Hq, C, d, k, chunk, with_shadow) -> int:
-    return int(lib.dk_decode_step_workspace_size(B, Hkv, T, Hq, C, d, k, chunk, int(bool(with_shadow))))
+def decode_step_workspace_size(B, Hkv, T, Hq, C, d, k, chunk, with_shadow, with_tail=False) -> int:
+    return int(lib.dk_decode_step_workspace_size(B, Hkv, T, Hq, C, d, k, chunk, int(bool(with_shadow)),
+                                                 int(bool(with_tail))))
+
+
+def _attn_extra(B, T, Hkv, dk, dv, K, K_tail, V_tail, tail_len, K_new, V_new) -> dk_attn_extra:
+    """The dk_attn_extra of the tail rows and the step's own rows, after shape checks."""
+    for name, t in (("K_tail", K_tail), ("V_tail", V_tail), ("K_new", K_new), ("V_new", V_new)):
+        if t is not None and t.dtype != K.dtype:
+            raise ValueError(f"{name} must have the pools' dtype")
+    if K_new is not None:
+        _need(K_new, K.dtype, (B, T, Hkv, dk), "K_new")
+        _need(V_new, K.dtype, (B, T, Hkv, dv), "V_new")
+    if tail_len is not None:
+        _need(tail_len, torch.int32, (B,), "tail_len")
+    zero = dk_strides(0, 0, 0)
+    return dk_attn_extra(_ptr(K_tail), _ptr(V_tail),
+                         pool_strides(K_tail) if K_tail is not None else zero,
+                         pool_strides(V_tail) if V_tail is not None else zero,
+                         _ptr(tail_len), K_tail.shape[2] if K_tail is not None else 0,
+                         _ptr(K_new), _ptr(V_new))
 
 
 @_on_stream
 def decode_step(q, lm, K, V, chunk: int, k: int, scale: float, reduce: int = DK_REDUCE_MEAN,
                 shadow: Shadow | None = None, topk_idx=None, topk_score=None, union_ids=None, member=None,
                 count=None, overlap=None, out=None, lse=None, ws=None, want_scores=False, want_lse=True,
-                stream=None):
+                K_tail=None, V_tail=None, tail_len=None, K_new=None, V_new=None, stream=None):
     """score_topk_union then sparse_decode_attn over its union, as one library call
-    (dk_decode_step: one fused kernel where the shapes allow it)."""
+    (dk_decode_step: one fused kernel where the shapes allow it).  With any of K_tail,
+    V_tail, K_new, V_new given, the attention is sparse_decode_attn_tail's."""
     B, T, Hq, d = q.shape
     _, Hkv, C, _ = lm.shape
     _need(q, torch.float32, (B, T, Hq, d), "q")
@@ -543,13 +564,16 @@ def decode_step(q, lm, K, V, chunk: int, k: int, scale: float, reduce: int = DK_
     out = torch.empty(B, T, Hq, d, dtype=torch.float32, device=dev) if out is None else out
     if lse is None and want_lse:
         lse = torch.empty(B, T, Hq, dtype=torch.float32, device=dev)
-    nbytes = decode_step_workspace_size(B, Hkv, T, Hq, C, d, k, chunk, shadow is not None)
+    with_tail = any(t is not None for t in (K_tail, V_tail, K_new, V_new))
+    extra = _attn_extra(B, T, Hkv, d, d, K, K_tail, V_tail, tail_len, K_new, V_new) if with_tail else None
+    nbytes = decode_step_workspace_size(B, Hkv, T, Hq, C, d, k, chunk, shadow is not None, with_tail)
     if ws is None and nbytes:
         ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     csh = ctypes.byref(shadow.as_c()) if shadow is not None else None
     _check(lib.dk_decode_step(_ptr(q), B, T, Hq, Hkv, _ptr(lm), _dtype(lm), pool_strides(lm), C, d, k,
                               float(scale), int(reduce), csh, _ptr(K), _ptr(V), _dtype(K), pool_strides(K),
-                              pool_strides(V), chunk, _ptr(topk_idx), _ptr(topk_score), _ptr(union_ids),
+                              pool_strides(V), chunk, ctypes.byref(extra) if extra is not None else None,
+                              _ptr(topk_idx), _ptr(topk_score), _ptr(union_ids),
                               _ptr(member), _ptr(count), _ptr(overlap), _ptr(out), _ptr(lse), _ptr(ws),
                               0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
     return topk_idx, topk_score, union_ids, member, count, overlap, out, lse
@@ -621,14 +645,7 @@ def sparse_decode_attn_tail(q, K, V, block_ids, member, count, chunk: int, scale
         _need(member, torch.uint8, (B, Hkv, N), "member")
     if count is not None:
         _need(count, torch.int32, (B, Hkv), "count")
-    for name, t in (("K_tail", K_tail), ("V_tail", V_tail), ("K_new", K_new), ("V_new", V_new)):
-        if t is not None and t.dtype != K.dtype:
-            raise ValueError(f"{name} must have the pools' dtype")
-    if K_new is not None:
-        _need(K_new, K.dtype, (B, T, Hkv, dk), "K_new")
-        _need(V_new, V.dtype, (B, T, Hkv, dv), "V_new")
-    if tail_len is not None:
-        _need(tail_len, torch.int32, (B,), "tail_len")
+    extra = _attn_extra(B, T, Hkv, dk, dv, K, K_tail, V_tail, tail_len, K_new, V_new)
     if out is None:
         out = torch.empty(B, T, Hq, dv, dtype=torch.float32, device=q.device)
     if lse is None:
@@ -638,12 +655,6 @@ def sparse_decode_attn_tail(q, K, V, block_ids, member, count, chunk: int, scale
     nbytes = attn_tail_workspace_size(B, Hkv, T, Hq, dv, N, chunk)
     if ws is None and nbytes:
         ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    zero = dk_strides(0, 0, 0)
-    extra = dk_attn_extra(_ptr(K_tail), _ptr(V_tail),
-                          pool_strides(K_tail) if K_tail is not None else zero,
-                          pool_strides(V_tail) if V_tail is not None else zero,
-                          _ptr(tail_len), K_tail.shape[2] if K_tail is not None else 0,
-                          _ptr(K_new), _ptr(V_new))
     _check(lib.dk_sparse_decode_attn_tail(_ptr(q), B, T, Hq, Hkv, _ptr(K), _ptr(V), _dtype(K),
                                           pool_strides(K), pool_strides(V), dk, dv, chunk, _ptr(block_ids),
                                           _ptr(member), _ptr(count), N, pool_blocks, ctypes.byref(extra),

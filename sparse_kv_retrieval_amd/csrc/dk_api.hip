@@ -304,6 +304,49 @@ hipError_t static_scratch(hipStream_t st, void** out) {
     return hipSuccess;
 }
 
+// Argument checks of the attention with tail and own rows (dk_sparse_decode_attn_tail,
+// dk_decode_step with an extra); `fn` names the entry point in the messages.
+dk_status check_attn_tail(const char* fn, const float* q, int B, int T, int Hq, int Hkv, const void* K,
+                          const void* V, dk_dtype kv_dtype, dk_strides ks, dk_strides vs, int dk, int dv,
+                          int chunk, const int32_t* block_ids, const uint8_t* member, int N, int pool_blocks,
+                          const dk_attn_extra* extra, float scale, const float* out, const void* ws,
+                          size_t ws_bytes, dk::AttnPlan* plan_out) {
+    const int esz = dtype_size(kv_dtype);
+    DK_REQUIRE(q && K && V && block_ids && out && extra, DK_ERR_INVALID_ARG,
+               "%s: q, K, V, block_ids, out, extra must be non-NULL", fn);
+    DK_REQUIRE(esz != 0, DK_ERR_INVALID_ARG, "%s: unknown kv_dtype %d", fn, (int)kv_dtype);
+    DK_REQUIRE(B >= 1 && Hq >= 1 && Hkv >= 1 && dk >= 1 && dv >= 1 && chunk >= 1 && N >= 1 &&
+                   pool_blocks >= 0,
+               DK_ERR_INVALID_ARG, "%s: sizes out of range", fn);
+    DK_REQUIRE(T == 1 || T == 2, DK_ERR_INVALID_ARG, "%s: T must be 1 or 2 (got %d)", fn, T);
+    DK_REQUIRE(Hq % Hkv == 0, DK_ERR_INVALID_ARG, "%s: Hq (%d) %% Hkv (%d) != 0", fn, Hq, Hkv);
+    DK_REQUIRE(member || T == 1, DK_ERR_INVALID_ARG, "%s: member is required when T == 2", fn);
+    DK_REQUIRE(std::isfinite(scale), DK_ERR_INVALID_ARG, "%s: scale must be finite", fn);
+    DK_REQUIRE(!extra->K_tail == !extra->V_tail, DK_ERR_INVALID_ARG,
+               "%s: K_tail and V_tail must both be given or both be NULL", fn);
+    DK_REQUIRE(!extra->K_new == !extra->V_new, DK_ERR_INVALID_ARG,
+               "%s: K_new and V_new must both be given or both be NULL", fn);
+    DK_REQUIRE(!extra->K_tail || (extra->tail_max >= 0 && extra->tail_k_s.b >= 0 && extra->tail_k_s.h >= 0 &&
+                                  extra->tail_k_s.t >= 0 && extra->tail_v_s.b >= 0 && extra->tail_v_s.h >= 0 &&
+                                  extra->tail_v_s.t >= 0),
+               DK_ERR_INVALID_ARG, "%s: tail_max and the tail strides must be >= 0", fn);
+    DK_REQUIRE(dk == dv && (dk == 64 || dk == 128), DK_ERR_UNSUPPORTED,
+               "%s: needs dk == dv in {64, 128} (got %d, %d)", fn, dk, dv);
+    DK_REQUIRE((Hq / Hkv) * T <= 16, DK_ERR_UNSUPPORTED, "%s: G*T must be <= 16", fn);
+    DK_REQUIRE(aligned16(q) && aligned16(out) && aligned16(K) && aligned16(V) && strides_ok(ks, esz) &&
+                   strides_ok(vs, esz) &&
+                   (!extra->K_tail || (aligned16(extra->K_tail) && aligned16(extra->V_tail) &&
+                                       strides_ok(extra->tail_k_s, esz) && strides_ok(extra->tail_v_s, esz))) &&
+                   (!extra->K_new || (aligned16(extra->K_new) && aligned16(extra->V_new))),
+               DK_ERR_UNSUPPORTED, "%s: q, out, K, V, the tail and new rows and their strides must be 16-byte aligned",
+               fn);
+    const dk::AttnPlan plan = dk::plan_attn(B, Hkv, T, Hq, dv, N, chunk, true);
+    DK_REQUIRE(ws_bytes >= plan.ws_bytes && (plan.ws_bytes == 0 || ws), DK_ERR_INVALID_ARG,
+               "%s: workspace needs %zu bytes (got %zu)", fn, plan.ws_bytes, ws_bytes);
+    *plan_out = plan;
+    return DK_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -624,17 +667,19 @@ dk_status dk_sparse_decode_attn(const float* q, int B, int T, int Hq, int Hkv, c
 }
 
 size_t dk_decode_step_workspace_size(int B, int Hkv, int T, int Hq, int C, int d, int k, int chunk,
-                                     int with_shadow) {
+                                     int with_shadow, int with_tail) {
     if (B < 1 || Hkv < 1 || T < 1 || Hq < 1 || C < 1 || d < 1 || k < 1 || chunk < 1) return 0;
     const size_t a = dk_score_topk_workspace_size(B, Hkv, T, C, k, with_shadow);
-    const size_t b = dk_attn_workspace_size(B, Hkv, T, Hq, d, T * k, chunk);
+    const size_t b = with_tail ? dk_attn_tail_workspace_size(B, Hkv, T, Hq, d, T * k, chunk)
+                               : dk_attn_workspace_size(B, Hkv, T, Hq, d, T * k, chunk);
     return a > b ? a : b;
 }
 
 dk_status dk_decode_step(const float* q, int B, int T, int Hq, int Hkv, const void* lm, dk_dtype lm_dtype,
                          dk_strides ls, int C, int d, int k, float scale, dk_group_reduce reduce,
                          const dk_landmark_shadow* shadow, const void* K, const void* V, dk_dtype kv_dtype,
-                         dk_strides ks, dk_strides vs, int chunk, int32_t* topk_idx, float* topk_score,
+                         dk_strides ks, dk_strides vs, int chunk, const dk_attn_extra* extra,
+                         int32_t* topk_idx, float* topk_score,
                          int32_t* union_ids, uint8_t* member, int32_t* union_count, int32_t* overlap, float* out,
                          float* lse, void* ws, size_t ws_bytes, void* stream) {
     g_err.clear();
@@ -650,20 +695,34 @@ dk_status dk_decode_step(const float* q, int B, int T, int Hq, int Hkv, const vo
     s = check_union(fn, T, k, 0, false);
     if (s != DK_OK) return s;
     AttnCall c{};
-    s = check_attn(fn, q, B, T, Hq, Hkv, K, V, kv_dtype, ks, vs, d, d, chunk, union_ids, member, out, C, T * k,
-                   scale, &c);
-    if (s != DK_OK) return s;
-    DK_REQUIRE(ws_bytes >= c.ws_bytes && (c.ws_bytes == 0 || ws), DK_ERR_INVALID_ARG,
-               "%s: workspace needs %zu bytes (got %zu)", fn, c.ws_bytes > tplan.ws_bytes ? c.ws_bytes : tplan.ws_bytes,
-               ws_bytes);
+    dk::AttnPlan tail_plan{};
+    if (extra) {
+        s = check_attn_tail(fn, q, B, T, Hq, Hkv, K, V, kv_dtype, ks, vs, d, d, chunk, union_ids, member, T * k, C,
+                            extra, scale, out, ws, ws_bytes, &tail_plan);
+        if (s != DK_OK) return s;
+        c.plan = tail_plan;
+    } else {
+        s = check_attn(fn, q, B, T, Hq, Hkv, K, V, kv_dtype, ks, vs, d, d, chunk, union_ids, member, out, C, T * k,
+                       scale, &c);
+        if (s != DK_OK) return s;
+        DK_REQUIRE(ws_bytes >= c.ws_bytes && (c.ws_bytes == 0 || ws), DK_ERR_INVALID_ARG,
+                   "%s: workspace needs %zu bytes (got %zu)", fn,
+                   c.ws_bytes > tplan.ws_bytes ? c.ws_bytes : tplan.ws_bytes, ws_bytes);
+    }
     const dk::UnionOut un{union_ids, member, union_count, overlap};
     const hipStream_t st = (hipStream_t)stream;
+    const dk::AttnTail tail = extra ? dk::AttnTail{extra->K_tail, extra->V_tail, extra->tail_k_s, extra->tail_v_s,
+                                                   extra->tail_len, extra->K_tail ? extra->tail_max : 0,
+                                                   extra->K_new, extra->V_new}
+                                    : dk::AttnTail{};
     // One kernel when every (b, g) is one block of each call: the shadow selection
     // with its union in the block (k + 1 <= 256), the attention fast path with one
-    // range per (b, g) and no partials, and 512 threads per selection block.
+    // range per (b, g) and no partials, and 512 threads per selection block.  Not
+    // with tail rows: their addressing takes the fused kernel past 128 registers, one
+    // block per CU instead of two (measured slower than the two calls' kernels).
     const bool fused = shadow && reduce == DK_REDUCE_MEAN && T == 2 && Hq == 4 * Hkv && d == 128 && !c.latent &&
                        dk::use_fast_path(kv_dtype, d, Hq / Hkv, T, chunk, ks, vs) && c.plan.splits == 1 &&
-                       c.plan.nparts == 1 && k + 1 <= 256 && (int64_t)B * Hkv > 256;
+                       c.plan.nparts == 1 && !extra && k + 1 <= 256 && (int64_t)B * Hkv > 256;
     hipError_t e;
     if (fused) {
         e = dk::launch_step_fused(q, B, Hq, Hkv, C, k, scale, shadow, (const float*)lm, ls, K, V, ks, vs, chunk,
@@ -671,7 +730,10 @@ dk_status dk_decode_step(const float* q, int B, int T, int Hq, int Hkv, const vo
     } else {
         e = dk::launch_score_topk(q, B, T, Hq, (const float*)lm, ls, Hkv, C, d, k, scale, reduce, shadow, topk_idx,
                                   topk_score, ws, tplan, &un, st);
-        if (e == hipSuccess)
+        if (e == hipSuccess && extra)
+            e = dk::launch_attention(q, B, T, Hq, Hkv, K, V, kv_dtype, ks, vs, d, chunk, union_ids, member,
+                                     union_count, T * k, C, scale, out, lse, ws, tail_plan, &tail, st);
+        else if (e == hipSuccess)
             e = run_attn(c, q, B, T, Hq, Hkv, K, V, kv_dtype, ks, vs, d, chunk, union_ids, member, union_count,
                          T * k, C, scale, out, lse, ws, st);
     }
@@ -717,38 +779,10 @@ dk_status dk_sparse_decode_attn_tail(const float* q, int B, int T, int Hq, int H
                                      void* ws, size_t ws_bytes, void* stream) {
     g_err.clear();
     const char* fn = "dk_sparse_decode_attn_tail";
-    const int esz = dtype_size(kv_dtype);
-    DK_REQUIRE(q && K && V && block_ids && out && extra, DK_ERR_INVALID_ARG,
-               "%s: q, K, V, block_ids, out, extra must be non-NULL", fn);
-    DK_REQUIRE(esz != 0, DK_ERR_INVALID_ARG, "%s: unknown kv_dtype %d", fn, (int)kv_dtype);
-    DK_REQUIRE(B >= 1 && Hq >= 1 && Hkv >= 1 && dk >= 1 && dv >= 1 && chunk >= 1 && N >= 1 &&
-                   pool_blocks >= 0,
-               DK_ERR_INVALID_ARG, "%s: sizes out of range", fn);
-    DK_REQUIRE(T == 1 || T == 2, DK_ERR_INVALID_ARG, "%s: T must be 1 or 2 (got %d)", fn, T);
-    DK_REQUIRE(Hq % Hkv == 0, DK_ERR_INVALID_ARG, "%s: Hq (%d) %% Hkv (%d) != 0", fn, Hq, Hkv);
-    DK_REQUIRE(member || T == 1, DK_ERR_INVALID_ARG, "%s: member is required when T == 2", fn);
-    DK_REQUIRE(std::isfinite(scale), DK_ERR_INVALID_ARG, "%s: scale must be finite", fn);
-    DK_REQUIRE(!extra->K_tail == !extra->V_tail, DK_ERR_INVALID_ARG,
-               "%s: K_tail and V_tail must both be given or both be NULL", fn);
-    DK_REQUIRE(!extra->K_new == !extra->V_new, DK_ERR_INVALID_ARG,
-               "%s: K_new and V_new must both be given or both be NULL", fn);
-    DK_REQUIRE(!extra->K_tail || (extra->tail_max >= 0 && extra->tail_k_s.b >= 0 && extra->tail_k_s.h >= 0 &&
-                                  extra->tail_k_s.t >= 0 && extra->tail_v_s.b >= 0 && extra->tail_v_s.h >= 0 &&
-                                  extra->tail_v_s.t >= 0),
-               DK_ERR_INVALID_ARG, "%s: tail_max and the tail strides must be >= 0", fn);
-    DK_REQUIRE(dk == dv && (dk == 64 || dk == 128), DK_ERR_UNSUPPORTED,
-               "%s: needs dk == dv in {64, 128} (got %d, %d)", fn, dk, dv);
-    DK_REQUIRE((Hq / Hkv) * T <= 16, DK_ERR_UNSUPPORTED, "%s: G*T must be <= 16", fn);
-    DK_REQUIRE(aligned16(q) && aligned16(out) && aligned16(K) && aligned16(V) && strides_ok(ks, esz) &&
-                   strides_ok(vs, esz) &&
-                   (!extra->K_tail || (aligned16(extra->K_tail) && aligned16(extra->V_tail) &&
-                                       strides_ok(extra->tail_k_s, esz) && strides_ok(extra->tail_v_s, esz))) &&
-                   (!extra->K_new || (aligned16(extra->K_new) && aligned16(extra->V_new))),
-               DK_ERR_UNSUPPORTED, "%s: q, out, K, V, the tail and new rows and their strides must be 16-byte aligned",
-               fn);
-    const dk::AttnPlan plan = dk::plan_attn(B, Hkv, T, Hq, dv, N, chunk, true);
-    DK_REQUIRE(ws_bytes >= plan.ws_bytes && (plan.ws_bytes == 0 || ws), DK_ERR_INVALID_ARG,
-               "%s: workspace needs %zu bytes (got %zu)", fn, plan.ws_bytes, ws_bytes);
+    dk::AttnPlan plan{};
+    dk_status s = check_attn_tail(fn, q, B, T, Hq, Hkv, K, V, kv_dtype, ks, vs, dk, dv, chunk, block_ids, member, N,
+                                  pool_blocks, extra, scale, out, ws, ws_bytes, &plan);
+    if (s != DK_OK) return s;
     const dk::AttnTail tail{extra->K_tail, extra->V_tail, extra->tail_k_s, extra->tail_v_s, extra->tail_len,
                             extra->K_tail ? extra->tail_max : 0, extra->K_new, extra->V_new};
     hipError_t e = dk::launch_attention(q, B, T, Hq, Hkv, K, V, kv_dtype, ks, vs, dk, chunk, block_ids,

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version():
-    assert lib.dk_abi_version() == 13
+    assert lib.dk_abi_version() == 14
 
 
 def err():
@@ -349,9 +349,11 @@ def test_capped_plan_rejects(kw, status):
 def decode_step(q=FAKE, B=64, T=2, Hq=32, Hkv=8, lm=FAKE, lmdt=0, ls=b.dk_strides(1 << 22, 1 << 19, 128), C=4096,
                 d=128, k=64, scale=0.088, reduce=0, shadow=None, K=FAKE, V=FAKE, kvdt=1,
                 ks=b.dk_strides(1 << 30, 1 << 27, 128), vs=b.dk_strides(1 << 30, 1 << 27, 128), chunk=32,
-                idx=FAKE, sc=FAKE, uid=FAKE, mem=FAKE, cnt=FAKE, ov=FAKE, out=FAKE, lse=FAKE, ws=FAKE, wsb=1 << 30):
+                idx=FAKE, sc=FAKE, uid=FAKE, mem=FAKE, cnt=FAKE, ov=FAKE, out=FAKE, lse=FAKE, ws=FAKE, wsb=1 << 30,
+                ex=None):
+    exp = ctypes.byref(ex) if ex is not None else None
     return lib.dk_decode_step(q, B, T, Hq, Hkv, lm, lmdt, ls, C, d, k, scale, reduce, shadow, K, V, kvdt, ks, vs,
-                              chunk, idx, sc, uid, mem, cnt, ov, out, lse, ws, wsb, None)
+                              chunk, exp, idx, sc, uid, mem, cnt, ov, out, lse, ws, wsb, None)
 
 
 def test_decode_step_workspace_size():
@@ -359,14 +361,21 @@ def test_decode_step_workspace_size():
     for B, Hkv, C, k, sh in [(64, 8, 4096, 64, 1), (16, 8, 1024, 64, 1), (16, 8, 1024, 64, 0), (2, 8, 512, 16, 0)]:
         want = max(lib.dk_score_topk_workspace_size(B, Hkv, 2, C, k, sh),
                    lib.dk_attn_workspace_size(B, Hkv, 2, 32, 128, 2 * k, 32))
-        assert lib.dk_decode_step_workspace_size(B, Hkv, 2, 32, C, 128, k, 32, sh) == want
-    assert lib.dk_decode_step_workspace_size(0, 8, 2, 32, 4096, 128, 64, 32, 1) == 0
+        assert lib.dk_decode_step_workspace_size(B, Hkv, 2, 32, C, 128, k, 32, sh, 0) == want
+        # with the tail rows the attention's share is the tail attention's size
+        want_t = max(lib.dk_score_topk_workspace_size(B, Hkv, 2, C, k, sh),
+                     lib.dk_attn_tail_workspace_size(B, Hkv, 2, 32, 128, 2 * k, 32))
+        assert lib.dk_decode_step_workspace_size(B, Hkv, 2, 32, C, 128, k, 32, sh, 1) == want_t
+    assert lib.dk_decode_step_workspace_size(0, 8, 2, 32, 4096, 128, 64, 32, 1, 0) == 0
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(q=NULL), 1), (dict(lmdt=1), 2), (dict(T=3), 1), (dict(uid=NULL), 1), (dict(cnt=NULL), 1),
     (dict(out=NULL), 1), (dict(K=NULL), 1), (dict(d=96), 2), (dict(k=0), 1), (dict(k=5000), 1),
     (dict(Hq=30), 1), (dict(chunk=0), 1), (dict(ws=NULL, wsb=0, B=16), 1),
+    # the tail attention's checks: a half-given pair, a negative tail length, misaligned rows
+    (dict(ex=extra(Vt=NULL)), 1), (dict(ex=extra(Kn=NULL)), 1), (dict(ex=extra(tmax=-1)), 1),
+    (dict(ex=extra(Kn=ctypes.c_void_p(0x1008))), 2),
 ])
 def test_decode_step_rejects(kw, status):
     assert decode_step(**kw) == status, err()

@@ -852,6 +852,87 @@ def test_decode_step_fused_against_oracle(dkb):
     print(f"near-tie chunks {near}; attention of all {w.B * w.Hkv} (b, g) within {worst:.3e}", flush=True)
 
 
+def tail_rows(w, tail_max, lens, fresh, seed):
+    """Tail pools [B, Hkv, tail_max, d], lengths and the step's own rows [B, T, Hkv, d] on the GPU."""
+    gen = torch.Generator().manual_seed(seed)
+    dt = synth.kv_torch_dtype(w)
+    Kt = Vt = Kn = Vn = tl = None
+    if tail_max:
+        Kt = torch.randn(w.B, w.Hkv, tail_max, w.d, generator=gen).to(dt).cuda()
+        Vt = torch.randn(w.B, w.Hkv, tail_max, w.d, generator=gen).to(dt).cuda()
+    if fresh:
+        Kn = torch.randn(w.B, w.T, w.Hkv, w.d, generator=gen).to(dt).cuda()
+        Vn = torch.randn(w.B, w.T, w.Hkv, w.d, generator=gen).to(dt).cuda()
+    if lens is not None:
+        tl = torch.randint(lens[0], lens[1] + 1, (w.B,), generator=gen, dtype=torch.int32).cuda()
+    return dict(K_tail=Kt, V_tail=Vt, tail_len=tl, K_new=Kn, V_new=Vn)
+
+
+@pytest.mark.parametrize("name,B,L,kw,tail_max,lens,fresh", [
+    ("b64_l128k", 40, 8192, {}, 96, (0, 96), True),           # ragged tails and own rows, one range per (b, g)
+    ("b64_l128k", 33, 16384, dict(k=128), 40, None, True),    # 256 union entries + full tails
+    ("b64_l128k", 40, 4096, {}, 0, None, True),               # own rows only
+    ("b64_l128k", 40, 4096, {}, 17, (5, 17), False),          # tail only
+    ("llama8b_l32k", 16, 8192, {}, 64, (0, 64), True),        # 128 (b, g): two ranges and their merge
+    ("b64_l128k", 40, 8192, dict(T=1), 33, (0, 33), True),    # one query: the generic kernels
+])
+def test_decode_step_tail_equals_two_calls(dkb, name, B, L, kw, tail_max, lens, fresh):
+    """dk_decode_step with the tail rows and the step's own rows equals dk_score_topk_union
+    followed by dk_sparse_decode_attn_tail bit for bit, on two query sets in turn (with
+    an extra the call runs those two calls' kernels, never the fused one)."""
+    w = workload(name, B, L, **kw)
+    q, K, V = make(w, 35)
+    q2 = synth.make_queries(w, 36, device="cuda")
+    lm = dkb.build_landmarks(K, w.chunk)
+    sh = dkb.build_landmark_shadow(lm)
+    extra = tail_rows(w, tail_max, lens, fresh, 35)
+    two = dkb.DecodeStep(w.B, w.T, w.Hq, w.Hkv, w.d, w.C, w.chunk, w.k, w.scale, "cuda", shadow=sh)
+    print(f"case {name} B={B} L={L} {kw} tail_max={tail_max} lens={lens} fresh={fresh}", flush=True)
+    for qq in (q2, q):
+        dkb.score_topk_union(qq, lm, w.k, w.scale, dkb.DK_REDUCE_MEAN, two.topk_idx, two.topk_score, two.union_ids,
+                             two.member, two.count, two.overlap, two.ws_topk, shadow=sh)
+        o2, l2 = dkb.sparse_decode_attn_tail(qq, K, V, two.union_ids, two.member, two.count, w.chunk, w.scale,
+                                             **extra)
+        got = dkb.decode_step(qq, lm, K, V, w.chunk, w.k, w.scale, dkb.DK_REDUCE_MEAN, sh, want_scores=True,
+                              **extra)
+        torch.cuda.synchronize()
+        ref = (two.topk_idx, two.topk_score, two.union_ids, two.member, two.count, two.overlap, o2, l2)
+        for nm, a, b in zip(("topk_idx", "topk_score", "union_ids", "member", "count", "overlap", "out", "lse"),
+                            ref, got):
+            assert torch.equal(a, b), nm
+
+
+def test_decode_step_tail_against_oracle(dkb):
+    """dk_decode_step with ragged tails and the step's own rows against the oracle's
+    attention with tail, on sampled requests, over the GPU's own selections."""
+    w = workload("b64_l128k", 40, 8192)
+    q, K, V = make(w, 37)
+    lm = dkb.build_landmarks(K, w.chunk)
+    sh = dkb.build_landmark_shadow(lm)
+    extra = tail_rows(w, 96, (0, 96), True, 37)
+    idx, _, uid, mem, cnt, ov, out, lse = dkb.decode_step(q, lm, K, V, w.chunk, w.k, w.scale, dkb.DK_REDUCE_MEAN,
+                                                          sh, **extra)
+    torch.cuda.synchronize()
+    f64 = lambda x: None if x is None else synth.to_numpy_f64(x)
+    tol = ATOL[w.kv_dtype]
+    tl = extra["tail_len"].cpu().numpy()
+    worst = 0.0
+    for b in (0, 13, 39):
+        sl = slice(b, b + 1)
+        sel = idx[sl].cpu().numpy().astype(np.int64)
+        ro_, rl_ = O.sparse_attention_tail(q[sl].cpu().numpy().astype(np.float64), f64(K[sl]), f64(V[sl]), sel,
+                                           w.chunk, w.scale, f64(extra["K_tail"][sl]), f64(extra["V_tail"][sl]),
+                                           tl[sl], f64(extra["K_new"][sl]), f64(extra["V_new"][sl]))
+        e = max(max_abs(out[sl].cpu().numpy(), ro_), max_abs(lse[sl].cpu().numpy(), rl_))
+        print(f"request {b} (tail {int(tl[b])} rows): max err {e:.3e}", flush=True)
+        assert e <= tol, (b, e)
+        worst = max(worst, e)
+    ru, rm, rc, ro = O.union_select(idx.cpu().numpy())
+    np.testing.assert_array_equal(uid.cpu().numpy(), ru)
+    np.testing.assert_array_equal(mem.cpu().numpy(), rm)
+    np.testing.assert_array_equal(cnt.cpu().numpy(), rc)
+
+
 # ----------------------------------------------------------------------------
 # host-resident pool: hot cache, misses copied from pinned host memory
 # ----------------------------------------------------------------------------
