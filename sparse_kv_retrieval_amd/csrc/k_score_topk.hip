@@ -980,6 +980,10 @@ __global__ __launch_bounds__(2 * kThreads) void k_step_fused(StepArgs s) {
                                                  s.ls, s.Hkv, s.C, s.k, s.scale, s.topk_idx, s.topk_score, s.un);
     __syncthreads();   // the union this block wrote is visible to all its threads; LDS is free
     if (threadIdx.x >= attn::kFastThreads) return;
+    // The CU's other block may still be selecting: its ALU work yields to these
+    // waves' loads and DMA issues, which keep HBM busy (measured: 4.71 -> 4.67 ms
+    // per 32-layer step at B = 64, L = 128K; the reverse order gains nothing).
+    __builtin_amdgcn_s_setprio(2);
     attn::attn_fast_block<false>(s.a, *reinterpret_cast<attn::FastSmem*>(smem2), bg, 0);
 }
 
